@@ -1,0 +1,138 @@
+"""ctypes binding of liblion_attn.so: the same entry points as include/lion_attn.h, taking torch
+tensors.  Argument marshalling only -- every step of the computation runs in the HIP kernels.
+PyTorch supplies device memory and the stream; outputs (and the workspace, if the caller passes
+none) are allocated with torch."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblion_attn.so")
+
+MASK_LIT, MASK_D, MASK_S = 0, 1, 2
+DTYPE_F32, DTYPE_BF16 = 0, 1
+FORM_FULL, FORM_CHUNK, FORM_BIRNN = 0, 1, 2
+_KINDS = {"lit": MASK_LIT, "d": MASK_D, "s": MASK_S}
+
+
+class LionError(RuntimeError):
+    """A nonzero status from the C ABI."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({lion_status_str(status)})")
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, fp, i, f, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    common = [vp, vp, vp, fp, i]
+    lib.lion_attn_full.argtypes = common + [f, i, i, i, i, i, vp, i, fp, vp]
+    lib.lion_attn_chunk.argtypes = common + [i, f, i, i, i, i, i, vp, i, fp, vp, sz, vp]
+    lib.lion_attn_birnn.argtypes = common + [f, i, i, i, i, i, vp, i, fp, vp, sz, vp]
+    for fn in ("lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_abi_version"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.lion_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.lion_attn_workspace_bytes.restype = sz
+    lib.lion_status_str.argtypes = [i]
+    lib.lion_status_str.restype = ctypes.c_char_p
+    lib.lion_attn_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def lion_status_str(status: int) -> str:
+    return library().lion_status_str(int(status)).decode()
+
+
+def lion_attn_abi_version() -> int:
+    return library().lion_attn_abi_version()
+
+
+def lion_attn_workspace_bytes(form: int, B: int, H: int, L: int, d: int, C: int = 0, dtype: int = DTYPE_BF16) -> int:
+    return int(library().lion_attn_workspace_bytes(form, B, H, L, d, C, dtype))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _prepare(q, k, v, mask_kind, y, y_dtype, den_out, stream):
+    import torch
+    kind = _KINDS[mask_kind] if isinstance(mask_kind, str) else int(mask_kind)
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, L, d = q.shape
+    dt = _dtype_code(q)
+    if y is None:
+        out_dtype = q.dtype if y_dtype is None else y_dtype
+        y = torch.empty((B, H, L, d), dtype=out_dtype, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sptr = ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return kind, B, H, L, d, dt, y, _dtype_code(y), sptr
+
+
+def lion_attn_full(q, k, v, log_lambda, mask_kind, eps: float = 1e-6, *, y=None, y_dtype=None, den_out=None,
+                   stream=None):
+    """Full form; returns y.  q, k, v: contiguous [B, H, L, d] bf16/fp32 cuda tensors."""
+    kind, B, H, L, d, dt, y, ydt, sptr = _prepare(q, k, v, mask_kind, y, y_dtype, den_out, stream)
+    rc = library().lion_attn_full(_ptr(q), _ptr(k), _ptr(v), _ptr(log_lambda), kind, float(eps), B, H, L, d, dt,
+                                  _ptr(y), ydt, _ptr(den_out), sptr)
+    if rc != 0:
+        raise LionError("lion_attn_full", rc)
+    return y
+
+
+def _workspace(form, B, H, L, d, C, dt, workspace, device):
+    import torch
+    need = lion_attn_workspace_bytes(form, B, H, L, d, C, dt)
+    if need == (1 << 64) - 1:
+        return None, 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, nbytes
+
+
+def lion_attn_chunk(q, k, v, log_lambda, mask_kind, C: int = 64, eps: float = 1e-6, *, y=None, y_dtype=None,
+                    den_out=None, workspace=None, stream=None):
+    """Chunkwise form with chunk size C; returns y."""
+    kind, B, H, L, d, dt, y, ydt, sptr = _prepare(q, k, v, mask_kind, y, y_dtype, den_out, stream)
+    ws, nbytes = _workspace(FORM_CHUNK, B, H, L, d, C, dt, workspace, q.device)
+    rc = library().lion_attn_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(log_lambda), kind, int(C), float(eps), B, H, L,
+                                   d, dt, _ptr(y), ydt, _ptr(den_out), _ptr(ws), nbytes, sptr)
+    if rc != 0:
+        raise LionError("lion_attn_chunk", rc)
+    return y
+
+
+def lion_attn_birnn(q, k, v, log_lambda, mask_kind, eps: float = 1e-6, *, y=None, y_dtype=None, den_out=None,
+                    workspace=None, stream=None):
+    """Bidirectional RNN form; returns y."""
+    kind, B, H, L, d, dt, y, ydt, sptr = _prepare(q, k, v, mask_kind, y, y_dtype, den_out, stream)
+    ws, nbytes = _workspace(FORM_BIRNN, B, H, L, d, 0, dt, workspace, q.device)
+    rc = library().lion_attn_birnn(_ptr(q), _ptr(k), _ptr(v), _ptr(log_lambda), kind, float(eps), B, H, L, d, dt,
+                                   _ptr(y), ydt, _ptr(den_out), _ptr(ws), nbytes, sptr)
+    if rc != 0:
+        raise LionError("lion_attn_birnn", rc)
+    return y

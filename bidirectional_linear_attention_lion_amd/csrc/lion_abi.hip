@@ -1,0 +1,133 @@
+// lion_abi.hip -- the extern "C" boundary of the LION attention library.
+//
+// Every argument is checked on the host before any HIP call; a rejected call touches no buffer
+// and enqueues nothing.  Valid calls are handed to the launchers of the three forms.
+#include <math.h>
+#include <stdint.h>
+
+#include "lion_attn.h"
+#include "lion_internal.h"
+
+namespace {
+
+constexpr long long kMaxL = 1 << 22;          // positions per sequence
+constexpr long long kMaxRows = 1LL << 31;     // B * H * L (row indices stay in int range)
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool d_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool c_supported(int C) { return C == 16 || C == 32 || C == 64 || C == 128 || C == 256; }
+
+// Shared checks of the three entry points; returns LION_OK or a negative status.
+int check_common(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, float eps,
+                 int B, int H, int L, int d, int dtype, const void *y, int y_dtype, const float *den_out) {
+    if (!q || !k || !v || !y) return LION_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LION_ERR_INVALID;
+    if (den_out && !aligned16(den_out)) return LION_ERR_INVALID;
+    if (mask_kind != LION_MASK_LIT && mask_kind != LION_MASK_D && mask_kind != LION_MASK_S) return LION_ERR_INVALID;
+    if (mask_kind == LION_MASK_LIT ? log_lambda != nullptr : log_lambda == nullptr) return LION_ERR_INVALID;
+    if (log_lambda && !aligned16(log_lambda)) return LION_ERR_INVALID;
+    if (!(eps >= 0.f) || !isfinite(eps)) return LION_ERR_INVALID;
+    if (B < 1 || H < 1 || L < 1 || d < 1) return LION_ERR_INVALID;
+    if ((long long)L > kMaxL || (long long)B * H * L > kMaxRows) return LION_ERR_INVALID;
+    if (dtype != LION_DTYPE_F32 && dtype != LION_DTYPE_BF16) return LION_ERR_INVALID;
+    if (y_dtype != LION_DTYPE_F32 && y_dtype != LION_DTYPE_BF16) return LION_ERR_INVALID;
+    if (!d_supported(d)) return LION_ERR_UNSUPPORTED;
+    if (dtype == LION_DTYPE_F32 && y_dtype != LION_DTYPE_F32) return LION_ERR_UNSUPPORTED;
+    return LION_OK;
+}
+
+lion::AttnArgs make_args(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind,
+                         float eps, int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out) {
+    lion::AttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_lambda = log_lambda;
+    a.kind = mask_kind;
+    a.eps = eps;
+    a.B = B;
+    a.H = H;
+    a.L = L;
+    a.d = d;
+    a.in_bf16 = dtype == LION_DTYPE_BF16;
+    a.y = y;
+    a.out_bf16 = y_dtype == LION_DTYPE_BF16;
+    a.den_out = den_out;
+    a.C = 0;
+    a.workspace = nullptr;
+    a.workspace_bytes = 0;
+    return a;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? LION_OK : LION_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int lion_attn_full(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, float eps,
+                   int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out, void *stream) {
+    int rc = check_common(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    if (rc != LION_OK) return rc;
+    lion::AttnArgs a = make_args(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    return status_of(lion::launch_full(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lion_attn_chunk(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, int C,
+                    float eps, int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_common(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    if (rc != LION_OK) return rc;
+    if (C < 1) return LION_ERR_INVALID;
+    if (!c_supported(C)) return LION_ERR_UNSUPPORTED;
+    const size_t need = lion::chunk_workspace_bytes(B, H, L, d, C);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return LION_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return LION_ERR_INVALID;
+    lion::AttnArgs a = make_args(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    a.C = C;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    return status_of(lion::launch_chunk(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lion_attn_birnn(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, float eps,
+                    int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    int rc = check_common(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    if (rc != LION_OK) return rc;
+    const size_t need = lion::birnn_workspace_bytes(B, H, L, d);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return LION_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return LION_ERR_INVALID;
+    lion::AttnArgs a = make_args(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    return status_of(lion::launch_birnn(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, int dtype) {
+    if (B < 1 || H < 1 || L < 1 || !d_supported(d) || (long long)L > kMaxL || (long long)B * H * L > kMaxRows)
+        return (size_t)-1;
+    if (dtype != LION_DTYPE_F32 && dtype != LION_DTYPE_BF16) return (size_t)-1;
+    switch (form) {
+    case LION_FORM_FULL: return 0;
+    case LION_FORM_CHUNK: return c_supported(C) ? lion::chunk_workspace_bytes(B, H, L, d, C) : (size_t)-1;
+    case LION_FORM_BIRNN: return lion::birnn_workspace_bytes(B, H, L, d);
+    default: return (size_t)-1;
+    }
+}
+
+const char *lion_status_str(int status) {
+    switch (status) {
+    case LION_OK: return "ok";
+    case LION_ERR_INVALID: return "invalid argument";
+    case LION_ERR_UNSUPPORTED: return "unsupported combination";
+    case LION_ERR_WORKSPACE: return "workspace too small";
+    case LION_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int lion_attn_abi_version(void) { return LION_ATTN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+/*
+ * lion_attn.h -- C ABI of the LION bidirectional masked linear attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * For every batch b and head h the library computes, from queries q, keys k and values v,
+ *
+ *     y_i = sum_j M_ij (phi(q_i) . phi(k_j)) v_j / ( sum_j M_ij (phi(q_i) . phi(k_j)) + eps )
+ *
+ * that is Y = SCALE(phi(Q) phi(K)^T (.) M) V with SCALE the row normalisation.  The mask M holds
+ * the products of per-token decays lambda between positions i and j, in either direction:
+ * M_ii = 1 and, for i < j, M_ij = M_ji = lambda_{i+1} * ... * lambda_j.
+ *
+ * Sources, all on the page "LION: A bidirectional framework that trains like a Transformer and
+ * infers like an RNN" (author-reviewer discussion) unless said otherwise:
+ *   - attention form Y = SCALE(QK^T (.) M)V and its equivalent bidirectional RNN: reply
+ *     "Concern 1", Theorem 3.3 Eq. 25 and Eq. 20-24;
+ *   - the RNN that keeps one vector y and one scalar c per token and direction: reply
+ *     "1: Recurrence Form of Linear Attention";
+ *   - chunking for parallel inference: reply "4: Practicality of Recurrent Inference", and the
+ *     blog page "LION Part IV - Results", section "LION Architecture Variants and Trade-offs";
+ *   - the three mask kinds LION-LIT (lambda = 1), LION-RETNET / LION-D (fixed per-head decay) and
+ *     LION-S (input-dependent lambda_i): reply "(3) ... two distinct methodological
+ *     contributions"; phi = elu()+1 for LIT and normalised silu for S: item 4, "Default
+ *     non-linearity".
+ *
+ * Three entry points compute the same Y by the three forms; results agree up to rounding.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   q, k, v      device pointers, contiguous row-major [B, H, L, d], element type `dtype`.
+ *   log_lambda   device pointer to fp32 log(lambda), every entry finite and <= 0:
+ *                  LION_MASK_LIT: must be NULL (lambda = 1);
+ *                  LION_MASK_D:   [H]        one decay per head;
+ *                  LION_MASK_S:   [B, H, L]  one decay per token (entry 0 of each row never enters).
+ *   mask_kind    LION_MASK_LIT / LION_MASK_D / LION_MASK_S; it also selects phi:
+ *                  LIT: phi(x) = elu(x) + 1;  D: phi(x) = x;  S: phi = silu(x) / ||silu(x)||_2 over the
+ *                  d channels of the token (an all-zero silu vector gives phi = 0).
+ *   eps          >= 0 and finite, added to every row sum.
+ *   B, H, L      >= 1;  d in {16, 32, 64, 128}.
+ *   dtype        LION_DTYPE_BF16 or LION_DTYPE_F32: element type of q, k, v.
+ *   y            device pointer, contiguous [B, H, L, d], element type `y_dtype`;
+ *                y_dtype is dtype, or LION_DTYPE_F32 when dtype is bf16 (an fp32 output keeps
+ *                the kernel's fp32 result unrounded).
+ *   den_out      NULL, or device pointer to fp32 [B, H, L] receiving each row sum + eps.
+ *   stream       a hipStream_t; NULL means the default stream.
+ * Every device pointer must be 16-byte aligned.
+ *
+ * Precision: bf16 inputs feed bf16 matrix-core products with fp32 accumulation; phi and the
+ * row-sum products are formed in fp32 and rounded to bf16 before the products that need them.
+ * fp32 inputs keep every step in fp32.  Row sums (denominators) are accumulated in fp32.
+ *
+ * Ownership and threading: the caller allocates and owns every buffer, workspace included.  The
+ * library allocates and frees nothing, never synchronises, keeps no mutable global state and is
+ * reentrant.  All work is enqueued on `stream`; outputs are valid once the stream reaches that
+ * point.  Input buffers are only read; y, den_out and the workspace are written.
+ *
+ * Errors: every entry point returns LION_OK (0) or a negative status.  Argument errors are found
+ * on the host before any HIP call and leave every buffer untouched:
+ *   LION_ERR_INVALID      a required pointer is NULL or misaligned, a size is out of range, eps is
+ *                         negative or not finite, an enum is unknown, or log_lambda is given for LIT
+ *                         / missing for D and S;
+ *   LION_ERR_UNSUPPORTED  a valid but unimplemented combination (d, C, dtype / y_dtype);
+ *   LION_ERR_WORKSPACE    the workspace is smaller than lion_attn_workspace_bytes() asks for;
+ *   LION_ERR_HIP          a HIP launch reported an error (hipGetLastError after the launch).
+ * Faults inside a kernel surface at the caller's next synchronisation.  No exception crosses the
+ * ABI.
+ */
+#ifndef LION_ATTN_H
+#define LION_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LION_ATTN_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define LION_API __attribute__((visibility("default")))
+#else
+#define LION_API
+#endif
+
+enum lion_mask_kind { LION_MASK_LIT = 0, LION_MASK_D = 1, LION_MASK_S = 2 };
+enum lion_dtype { LION_DTYPE_F32 = 0, LION_DTYPE_BF16 = 1 };
+enum lion_form { LION_FORM_FULL = 0, LION_FORM_CHUNK = 1, LION_FORM_BIRNN = 2 };
+enum lion_status {
+    LION_OK = 0,
+    LION_ERR_INVALID = -1,
+    LION_ERR_UNSUPPORTED = -2,
+    LION_ERR_WORKSPACE = -3,
+    LION_ERR_HIP = -4
+};
+
+/* Full (attention) form: the L x L masked score matrix is formed tile by tile on chip and never
+ * written out; the mask is generated from prefix sums of log(lambda) inside the kernel.
+ * Source: Theorem 3.3 Eq. 25, reply "Concern 1" (the form LION trains with).
+ * Needs no workspace. */
+LION_API int lion_attn_full(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, float eps,
+                   int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out, void *stream);
+
+/* Chunkwise form: masked attention inside chunks of C consecutive tokens plus forward and
+ * backward d x (d+1) states carried from chunk to chunk.  C in {16, 32, 64, 128, 256}; the last
+ * chunk may be partial.  Source: reply "4: Practicality of Recurrent Inference"; blog "LION Part
+ * IV - Results", "LION Chunk".
+ * workspace: device buffer of at least lion_attn_workspace_bytes(LION_FORM_CHUNK, ...) bytes
+ * (may be NULL when that is 0); its contents on entry do not matter and on exit are unspecified. */
+LION_API int lion_attn_chunk(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, int C,
+                    float eps, int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bidirectional RNN form: a forward and a backward recurrence over tokens with d x d matrix
+ * states, S_i = lambda_i S_{i-1} + phi(k_i) v_i^T (backward: S_i = lambda_{i+1} S_{i+1} + ...),
+ * keeping only a vector and a scalar per token and direction; the diagonal term is counted once.
+ * Source: Theorem 3.3 Eq. 20-24, reply "Concern 1"; reply "1: Recurrence Form of Linear
+ * Attention".
+ * workspace: as for lion_attn_chunk, sized by lion_attn_workspace_bytes(LION_FORM_BIRNN, ...). */
+LION_API int lion_attn_birnn(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, float eps,
+                    int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/* Workspace bytes `form` needs for these sizes (C is ignored except for LION_FORM_CHUNK).
+ * Returns 0 when no workspace is needed, and (size_t)-1 for arguments the form rejects. */
+LION_API size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, int dtype);
+
+/* Static, NUL-terminated description of a status code. */
+LION_API const char *lion_status_str(int status);
+
+/* LION_ATTN_ABI_VERSION of the built library. */
+LION_API int lion_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LION_ATTN_H */

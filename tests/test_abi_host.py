@@ -1,0 +1,130 @@
+"""The C ABI on the host (CPU only): the library loads, exports every symbol the header declares,
+and rejects every invalid argument with the documented status before any HIP call.
+
+Only argument combinations that validation must reject are passed here (with fake, aligned,
+non-null pointers); nothing in this file can reach a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bidirectional_linear_attention_lion_amd as lion
+from bidirectional_linear_attention_lion_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lion_attn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+P = 0x10000          # fake aligned device address: never dereferenced by the calls below
+MIS = 0x10008        # misaligned by 8 bytes
+SIZE_MAX = (1 << 64) - 1
+
+
+def header_symbols():
+    with open(HEADER) as fh:
+        text = fh.read()
+    return re.findall(r"LION_API\s+[\w\s\*]+?\b(lion_\w+)\s*\(", text)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = lion.library()
+    names = header_symbols()
+    assert set(names) == {"lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_workspace_bytes",
+                          "lion_status_str", "lion_attn_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert lion.lion_attn_abi_version() == 1
+
+
+def test_status_strings():
+    assert lion.lion_status_str(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert lion.lion_status_str(s) not in ("ok", "unknown status")
+    assert lion.lion_status_str(-99) == "unknown status"
+
+
+def full(q=P, k=P, v=P, ll=None, kind=0, eps=1e-6, B=2, H=3, L=17, d=64, dt=1, y=P, ydt=1, den=None):
+    return lion.library().lion_attn_full(q, k, v, ll, kind, eps, B, H, L, d, dt, y, ydt, den, None)
+
+
+def chunk(C=64, ws=None, wsb=0, **kw):
+    a = dict(q=P, k=P, v=P, ll=None, kind=0, eps=1e-6, B=2, H=3, L=17, d=64, dt=1, y=P, ydt=1, den=None)
+    a.update(kw)
+    return lion.library().lion_attn_chunk(a["q"], a["k"], a["v"], a["ll"], a["kind"], C, a["eps"], a["B"], a["H"],
+                                          a["L"], a["d"], a["dt"], a["y"], a["ydt"], a["den"], ws, wsb, None)
+
+
+def birnn(ws=None, wsb=0, **kw):
+    a = dict(q=P, k=P, v=P, ll=None, kind=0, eps=1e-6, B=2, H=3, L=17, d=64, dt=1, y=P, ydt=1, den=None)
+    a.update(kw)
+    return lion.library().lion_attn_birnn(a["q"], a["k"], a["v"], a["ll"], a["kind"], a["eps"], a["B"], a["H"],
+                                          a["L"], a["d"], a["dt"], a["y"], a["ydt"], a["den"], ws, wsb, None)
+
+
+INVALID_CASES = [
+    ("null q", dict(q=None)), ("null k", dict(k=None)), ("null v", dict(v=None)), ("null y", dict(y=None)),
+    ("misaligned q", dict(q=MIS)), ("misaligned y", dict(y=MIS)), ("misaligned den", dict(den=MIS)),
+    ("bad kind", dict(kind=3)), ("negative kind", dict(kind=-1)),
+    ("LIT with log_lambda", dict(kind=0, ll=P)), ("D without log_lambda", dict(kind=1, ll=None)),
+    ("S without log_lambda", dict(kind=2, ll=None)), ("misaligned log_lambda", dict(kind=1, ll=MIS)),
+    ("negative eps", dict(eps=-1e-3)), ("nan eps", dict(eps=float("nan"))), ("inf eps", dict(eps=float("inf"))),
+    ("B=0", dict(B=0)), ("H=0", dict(H=0)), ("L=0", dict(L=0)), ("d=0", dict(d=0)), ("L negative", dict(L=-5)),
+    ("L too large", dict(L=(1 << 22) + 1)), ("rows too many", dict(B=1 << 12, H=1 << 10, L=1 << 10)),
+    ("bad dtype", dict(dt=2)), ("bad y dtype", dict(ydt=7)),
+]
+UNSUPPORTED_CASES = [("d=48", dict(d=48)), ("d=256", dict(d=256)), ("d=8", dict(d=8)),
+                     ("f32 in, bf16 out", dict(dt=0, ydt=1))]
+
+
+@pytest.mark.parametrize("name,kw", INVALID_CASES, ids=[c[0] for c in INVALID_CASES])
+@pytest.mark.parametrize("entry", [full, chunk, birnn], ids=["full", "chunk", "birnn"])
+def test_invalid_arguments(entry, name, kw):
+    assert entry(**kw) == INVALID
+
+
+@pytest.mark.parametrize("name,kw", UNSUPPORTED_CASES, ids=[c[0] for c in UNSUPPORTED_CASES])
+@pytest.mark.parametrize("entry", [full, chunk, birnn], ids=["full", "chunk", "birnn"])
+def test_unsupported_combinations(entry, name, kw):
+    assert entry(**kw) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("C,status", [(0, INVALID), (-64, INVALID), (48, UNSUPPORTED), (512, UNSUPPORTED),
+                                      (8, UNSUPPORTED)])
+def test_chunk_size_checks(C, status):
+    assert chunk(C=C) == status
+
+
+def test_workspace_query():
+    wb = lion.lion_attn_workspace_bytes
+    assert wb(lion.FORM_FULL, 2, 3, 17, 64, 0, 1) == 0
+    for bad in [(lion.FORM_FULL, 0, 3, 17, 64, 0, 1), (lion.FORM_CHUNK, 2, 3, 17, 64, 48, 1),
+                (lion.FORM_BIRNN, 2, 3, 17, 48, 0, 1), (7, 2, 3, 17, 64, 64, 1), (lion.FORM_FULL, 2, 3, 17, 64, 0, 5)]:
+        assert wb(*bad) == SIZE_MAX, bad
+    for form in (lion.FORM_CHUNK, lion.FORM_BIRNN):
+        for L in (1, 197, 512, 4097):
+            n = wb(form, 8, 12, L, 64, 64, 1)
+            assert 0 <= n < (1 << 40)
+
+
+@pytest.mark.parametrize("form,entry", [(binding.FORM_CHUNK, chunk), (binding.FORM_BIRNN, birnn)])
+def test_workspace_too_small(form, entry):
+    """Sizes for which the form needs scratch memory must reject a missing or short workspace."""
+    for (B, H, L) in [(8, 12, 4097), (64, 12, 197), (1, 1, 100000)]:
+        need = lion.lion_attn_workspace_bytes(form, B, H, L, 64, 64, 1)
+        if need == 0:
+            continue
+        kw = dict(kind=1, ll=P, B=B, H=H, L=L)
+        assert entry(ws=None, wsb=need, **kw) == WORKSPACE
+        assert entry(ws=P, wsb=need - 1, **kw) == WORKSPACE
+        return
+    pytest.skip("form needs no workspace at any tested size")
+
+
+def test_binding_requires_built_library(monkeypatch, tmp_path):
+    """No fallback: a missing library is an error, not a silent CPU path."""
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError):
+        binding.library()

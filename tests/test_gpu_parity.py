@@ -1,0 +1,158 @@
+"""GPU parity of the three forms against the fp64 oracle (needs an MI355X; marked gpu).
+
+Every call goes through the C ABI (ctypes binding).  Inputs are the seeded synthetic workloads of
+``inputs.py``; the oracle consumes the exact values the device consumed.  Gates: see parity.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from bidirectional_linear_attention_lion_amd import inputs as lin
+from tests.gpu_util import oracle_full, oracle_rows, report, sample_rows, to_device
+from tests.parity import assert_parity, compare
+
+pytestmark = pytest.mark.gpu
+
+FORMS = ["full", "chunk", "birnn"]
+
+
+def run_form(form, q, k, v, ll, kind, eps, C=64, y_dtype=None):
+    import torch
+    import bidirectional_linear_attention_lion_amd as lion
+    B, H, L, d = q.shape
+    den = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    if form == "full":
+        y = lion.lion_attn_full(q, k, v, ll, kind, eps, y_dtype=y_dtype, den_out=den)
+    elif form == "chunk":
+        y = lion.lion_attn_chunk(q, k, v, ll, kind, C, eps, y_dtype=y_dtype, den_out=den)
+    else:
+        y = lion.lion_attn_birnn(q, k, v, ll, kind, eps, y_dtype=y_dtype, den_out=den)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), den.cpu().numpy().astype(np.float64)
+
+
+def _check(form, inp, eps, C=64, y_dtype=None, require_literal=None, tag=""):
+    import torch
+    wl = inp.wl
+    q, k, v, ll = to_device(inp)
+    out_dtype = "f32" if (y_dtype == torch.float32 or wl.dtype == "f32") else "bf16"
+    y, den = run_form(form, q, k, v, ll, wl.kind, eps, C=C, y_dtype=y_dtype)
+    yr, dr, an, ad = oracle_full(inp, eps)
+    rep = compare(y, yr, dr, an, ad, wl.dtype, out_dtype, wl.d, wl.L)
+    # the row sums the kernel used, against the exact ones, relative to the absolute-value sums
+    den_err = float(np.max(np.abs(den - dr.reshape(den.shape)) / (ad.reshape(den.shape) + 1e-30)))
+    report(f"[{form}{'' if form != 'chunk' else ' C=%d' % C}] {wl.name} B{wl.B} H{wl.H} L{wl.L} d{wl.d} "
+           f"{wl.dtype}->{out_dtype} kind={lin.KIND_NAME[wl.kind]} {tag}: {rep} den_relerr={den_err:.2e}")
+    if require_literal is None:
+        require_literal = wl.kind == lin.LIT or wl.name == "lion_s_unit"
+    assert_parity(rep, f"{form} {wl.name}", require_literal=require_literal)
+    u = 2.0 ** -8 if wl.dtype == "bf16" else (wl.d + wl.L) * 2.0 ** -24
+    assert den_err <= 3 * u, f"row sums off by {den_err:.3e} of their absolute sums"
+
+
+# ---- the five workloads at sizes the oracle finishes in seconds (full L and d, fewer B x H) ------
+REDUCED = {
+    "lion_s_unit": dict(),
+    "vit_tiny_lit": dict(B=2, H=3),
+    "vit_base_d": dict(B=2, H=12),
+    "bert_large_s": dict(B=2, H=4),
+    "hires_d": dict(B=1, H=2),
+}
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_workload_reduced(form, name):
+    wl = lin.WORKLOADS[name]
+    inp = lin.make_inputs(wl, **REDUCED[name])
+    chunks = wl.chunks if form == "chunk" else (64,)
+    for C in chunks:
+        _check(form, inp, wl.eps, C=C)
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("name", ["bert_large_s", "vit_base_d"])
+def test_workload_fp32_output(form, name):
+    import torch
+    wl = lin.WORKLOADS[name]
+    inp = lin.make_inputs(wl, **REDUCED[name])
+    _check(form, inp, wl.eps, y_dtype=torch.float32, tag="(fp32 y)")
+
+
+# ---- full sizes, in the launch configuration the bench times, checked on sampled rows ---------------
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("name", [n for n in lin.WORKLOADS if n != "lion_s_unit"])
+def test_workload_full_size_sampled(form, name):
+    wl = lin.WORKLOADS[name]
+    inp = lin.make_inputs(wl)
+    q, k, v, ll = to_device(inp)
+    rows = sample_rows(wl.B, wl.H, wl.L, 160, seed=7)
+    yr, dr, an, ad = oracle_rows(inp, wl.eps, rows)
+    for C in (wl.chunks if form == "chunk" else (64,)):
+        y, den = run_form(form, q, k, v, ll, wl.kind, wl.eps, C=C)
+        ys = y.reshape(-1, wl.d)[rows]
+        rep = compare(ys, yr, dr, an, ad, wl.dtype, "bf16", wl.d, wl.L)
+        report(f"[{form} C={C} full-size sampled] {wl.name}: {rep}")
+        assert_parity(rep, f"{form} {wl.name} full size", require_literal=wl.kind == lin.LIT)
+        assert np.all(np.isfinite(y)), "non-finite outputs"
+
+
+# ---- edge cases --------------------------------------------------------------------------------------
+EDGE_L = [1, 2, 3, 15, 16, 17, 31, 32, 33, 100]
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("kind", [lin.LIT, lin.D, lin.S])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_lengths(form, kind, dtype):
+    for L in EDGE_L:
+        inp = lin.random_inputs(2, 3, L, 64, kind, dtype=dtype, seed=100 + L)
+        _check(form, inp, 1e-6, C=16, tag=f"(edge L={L})")
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_head_dims(form, d, dtype):
+    for kind in (lin.LIT, lin.D, lin.S):
+        inp = lin.random_inputs(1, 2, 77, d, kind, dtype=dtype, seed=200 + d)
+        _check(form, inp, 1e-6, C=32, tag=f"(d={d})")
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_decay_to_zero_gives_v(form):
+    """log(lambda) = -1000: the mask is the identity, so y_i = v_i (eps = 0)."""
+    import torch
+    inp = lin.random_inputs(1, 2, 70, 32, lin.S, dtype="f32", seed=301)
+    q, k, v, _ = to_device(inp)
+    ll = torch.full((1, 2, 70), -1000.0, dtype=torch.float32, device="cuda")
+    y, _ = run_form(form, q, k, v, ll, lin.S, 0.0, C=16)
+    vv = v.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(y - vv)) <= 1e-4 * np.sqrt(np.mean(vv ** 2))
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_deterministic(form):
+    wl = lin.WORKLOADS["vit_base_d"]
+    inp = lin.make_inputs(wl, B=2, H=4)
+    q, k, v, ll = to_device(inp)
+    y1, d1 = run_form(form, q, k, v, ll, wl.kind, wl.eps)
+    y2, d2 = run_form(form, q, k, v, ll, wl.kind, wl.eps)
+    assert np.array_equal(y1, y2) and np.array_equal(d1, d2)
+
+
+def test_forms_agree_on_gpu():
+    """Full, chunk (several C) and RNN forms of the same inputs agree within their error bounds."""
+    wl = lin.WORKLOADS["bert_large_s"]
+    inp = lin.make_inputs(wl, B=1, H=4)
+    q, k, v, ll = to_device(inp)
+    yr, dr, an, ad = oracle_full(inp, wl.eps)
+    outs = {"full": run_form("full", q, k, v, ll, wl.kind, wl.eps)[0],
+            "birnn": run_form("birnn", q, k, v, ll, wl.kind, wl.eps)[0]}
+    for C in (16, 32, 64, 128, 256):
+        outs[f"chunk{C}"] = run_form("chunk", q, k, v, ll, wl.kind, wl.eps, C=C)[0]
+    for name, y in outs.items():
+        rep = compare(y, yr, dr, an, ad, "bf16", "bf16", wl.d, wl.L)
+        report(f"[agree] {name}: {rep}")
+        assert_parity(rep, name)
