@@ -1,0 +1,242 @@
+"""Throughput of LION bidirectional masked linear attention (forward) on one MI355X.
+
+One step = one forward pass of every form listed (full, chunk, bidirectional RNN by default) over
+one batch of the workload's synthetic inputs; each form writes the attention output of all B x L
+tokens (every head).  Input sets are rotated so that more than --rotate-gib of distinct buffers
+stream through HBM: the 256 MB last-level cache cannot hold them, so kernels read HBM, not cache.
+
+Prints one JSON line.  ``value`` is form-tokens per second: forms x B x L tokens per step over the
+step time (the harmonic mean of the per-form rates, which ``forms`` lists one by one).
+``roofline`` is for the kernel that takes the largest share of the step; ``cpu_baseline`` times
+the fp64 oracle on the host for the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LION attention fwd tokens/s per form (full/chunk/RNN) + % of MFMA or HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
+VALU_FP32_PEAK_TFLOPS = 157.3   # fp32 vector
+CSRC = os.path.join(ROOT, "bidirectional_linear_attention_lion_amd", "csrc")
+KERNEL_FILES = {"full": "lion_full.hip", "chunk": "lion_chunk.hip", "birnn": "lion_birnn.hip"}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="vit_tiny_lit")
+    ap.add_argument("--forms", default="full,chunk,birnn")
+    ap.add_argument("--chunk", type=int, default=None, help="chunk size C (default: the workload's first)")
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0,
+                    help="wall-time budget of the oracle sample (0 disables)")
+    return ap.parse_args()
+
+
+def kernel_hash(form: str) -> str:
+    h = hashlib.sha256()
+    for f in (KERNEL_FILES[form], "lion_device.h", "lion_mask.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(form: str, wl, C: int):
+    """Algorithmic bytes and flops of one launch (what the method must read, write and compute)."""
+    B, H, L, d = wl.B, wl.H, wl.L, wl.d
+    esz = 2 if wl.dtype == "bf16" else 4
+    nbytes = 4 * B * H * L * d * esz                      # read q, k, v; write y
+    if wl.kind == 2:
+        nbytes += 4 * B * H * L                           # per-token log(lambda)
+    elif wl.kind == 1:
+        nbytes += 4 * H
+    bh = B * H
+    if form == "full":
+        flops = bh * (4 * L * L * d + 2 * L * L)          # phi(Q)phi(K)^T, P V, mask and row sums
+    elif form == "chunk":
+        flops = bh * (4 * L * C * d + 8 * L * d * d + 2 * L * C)   # intra-chunk + state fold and use
+    else:
+        per_dir = (4 * d * d + 3 * d) if wl.kind == 0 else (5 * d * d + 4 * d)
+        flops = bh * L * 2 * per_dir                      # two recurrences: state update + q^T S, q.z
+    return nbytes, flops
+
+
+def bound_of(form: str) -> str:
+    return "alu" if form == "birnn" else "hbm"
+
+
+def read_traffic(form: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken on this kernel."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{form}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_h = re.search(r"kernel_source_sha256_16:\s*(\w+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_h or not m_b or m_h.group(1) != kernel_hash(form):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The fp64 oracle (the full-form definition) on the host: the whole workload if it fits the
+    budget, else as many leading batch entries as do; tokens/s over the sample."""
+    import oracle
+    from bidirectional_linear_attention_lion_amd import inputs as lin
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    inp1 = lin.make_inputs(wl, B=1)
+    t0 = time.perf_counter()
+    oracle.full(inp1.q, inp1.k, inp1.v, inp1.log_lambda_f64, wl.kind, wl.eps)
+    t1 = time.perf_counter() - t0
+    nb = int(max(1, min(wl.B, budget_s / max(t1, 1e-6))))
+    inp = lin.make_inputs(wl, B=nb) if nb > 1 else inp1
+    t0 = time.perf_counter()
+    oracle.full(inp.q, inp.k, inp.v, inp.log_lambda_f64, wl.kind, wl.eps)
+    dt = time.perf_counter() - t0
+    return {"value": nb * wl.L / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nb} of {wl.B} batch entries x {wl.H} heads x L={wl.L} (fp64 C oracle, "
+                      f"OpenMP over (batch, head)), {dt:.2f} s"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the (batch, head) problems are independent, see the design notes for sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bidirectional_linear_attention_lion_amd as lion
+    from bidirectional_linear_attention_lion_amd import inputs as lin
+
+    wl = lin.WORKLOADS[args.workload]
+    C = args.chunk or wl.chunks[0]
+    forms = [f for f in args.forms.split(",") if f]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    inp = lin.make_inputs(wl)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q0, k0, v0 = to_dev(inp.q_dev), to_dev(inp.k_dev), to_dev(inp.v_dev)
+    ll = None if inp.log_lambda is None else torch.from_numpy(inp.log_lambda).to(dev)
+    set_bytes = 4 * q0.numel() * q0.element_size()
+    nsets = max(2, int(np.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
+    sets = [(q0.clone(), k0.clone(), v0.clone(), torch.empty_like(q0)) for _ in range(nsets)]
+    del q0, k0, v0
+    ws = {}
+    for f, form_id in (("chunk", lion.FORM_CHUNK), ("birnn", lion.FORM_BIRNN)):
+        nb = lion.lion_attn_workspace_bytes(form_id, wl.B, wl.H, wl.L, wl.d, C, 1 if wl.dtype == "bf16" else 0)
+        ws[f] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+
+    def call(form, s):
+        q, k, v, y = sets[s % nsets]
+        if form == "full":
+            lion.lion_attn_full(q, k, v, ll, wl.kind, wl.eps, y=y, stream=stream)
+        elif form == "chunk":
+            lion.lion_attn_chunk(q, k, v, ll, wl.kind, C, wl.eps, y=y, workspace=ws["chunk"], stream=stream)
+        else:
+            lion.lion_attn_birnn(q, k, v, ll, wl.kind, wl.eps, y=y, workspace=ws["birnn"], stream=stream)
+
+    for s in range(args.warmup):
+        for f in forms:
+            call(f, s)
+    torch.cuda.synchronize()
+
+    ev = {f: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for f in forms}
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        for f in forms:
+            ev[f][s][0].record(stream)
+            call(f, args.warmup + s)
+            ev[f][s][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    tokens = wl.B * wl.L
+    per_form = {}
+    for f in forms:
+        ms = [a.elapsed_time(b) for a, b in ev[f]]
+        avg = float(np.mean(ms))
+        nbytes, flops = algorithmic(f, wl, C)
+        per_form[f] = {
+            "tokens_per_s": tokens / (avg * 1e-3),
+            "ms_avg": avg,
+            "ms_p10": float(np.percentile(ms, 10)),
+            "ms_p90": float(np.percentile(ms, 90)),
+            "alg_GBps": nbytes / (avg * 1e-3) / 1e9,
+            "alg_TFLOPs": flops / (avg * 1e-3) / 1e12,
+            "bound": bound_of(f),
+        }
+        if f == "chunk":
+            per_form[f]["C"] = C
+    dom = max(forms, key=lambda f: per_form[f]["ms_avg"])
+    nbytes, flops = algorithmic(dom, wl, C)
+    avg_s = per_form[dom]["ms_avg"] * 1e-3
+    if bound_of(dom) == "hbm":
+        achieved, peak, unit = nbytes / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = flops / avg_s / 1e12, VALU_FP32_PEAK_TFLOPS, "TFLOP/s"
+    traffic = read_traffic(dom, wl.name)
+    for f in forms:
+        pf = per_form[f]
+        pf["frac_of_roof"] = (pf["alg_GBps"] / HBM_PEAK_GBS) if pf["bound"] == "hbm" \
+            else (pf["alg_TFLOPs"] / VALU_FP32_PEAK_TFLOPS)
+        pf["frac_mfma_bf16"] = pf["alg_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS if f != "birnn" else None
+
+    out = {
+        "metric": METRIC,
+        "value": len(forms) * tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "L": wl.L, "d": wl.d,
+                   "mask": lin.KIND_NAME[wl.kind], "forms": forms, "C": C, "input_sets": nsets},
+        "forms": per_form,
+        "roofline": {"bound": bound_of(dom), "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak,
+                     "traffic": traffic},
+    }
+    if args.cpu_baseline_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_baseline_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,6 +17,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool d_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool c_supported(int C) { return C == 16 || C == 32 || C == 64 || C == 128 || C == 256; }
+// a chunk's query tiles must fit one pass of the chunk kernel's waves (256 rows, 128 for d = 128)
+bool c_supported_for(int C, int d) { return c_supported(C) && (d < 128 || C <= 128); }
 
 // Shared checks of the three entry points; returns LION_OK or a negative status.
 int check_common(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, float eps,
@@ -71,6 +73,7 @@ int lion_attn_full(const void *q, const void *k, const void *v, const float *log
     int rc = check_common(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
     if (rc != LION_OK) return rc;
     lion::AttnArgs a = make_args(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    if (!lion::plan_full(a).ok) return LION_ERR_UNSUPPORTED;
     return status_of(lion::launch_full(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -80,12 +83,13 @@ int lion_attn_chunk(const void *q, const void *k, const void *v, const float *lo
     int rc = check_common(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
     if (rc != LION_OK) return rc;
     if (C < 1) return LION_ERR_INVALID;
-    if (!c_supported(C)) return LION_ERR_UNSUPPORTED;
-    const size_t need = lion::chunk_workspace_bytes(B, H, L, d, C);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return LION_ERR_WORKSPACE;
+    if (!c_supported_for(C, d)) return LION_ERR_UNSUPPORTED;
     if (workspace && !aligned16(workspace)) return LION_ERR_INVALID;
     lion::AttnArgs a = make_args(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
     a.C = C;
+    const lion::Plan plan = lion::plan_chunk(a);
+    if (!plan.ok) return LION_ERR_UNSUPPORTED;
+    if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return LION_ERR_WORKSPACE;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
     return status_of(lion::launch_chunk(a, reinterpret_cast<hipStream_t>(stream)));
@@ -96,10 +100,11 @@ int lion_attn_birnn(const void *q, const void *k, const void *v, const float *lo
                     size_t workspace_bytes, void *stream) {
     int rc = check_common(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
     if (rc != LION_OK) return rc;
-    const size_t need = lion::birnn_workspace_bytes(B, H, L, d);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return LION_ERR_WORKSPACE;
     if (workspace && !aligned16(workspace)) return LION_ERR_INVALID;
     lion::AttnArgs a = make_args(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    const lion::Plan plan = lion::plan_birnn(a);
+    if (!plan.ok) return LION_ERR_UNSUPPORTED;
+    if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return LION_ERR_WORKSPACE;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
     return status_of(lion::launch_birnn(a, reinterpret_cast<hipStream_t>(stream)));
@@ -109,12 +114,22 @@ size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, in
     if (B < 1 || H < 1 || L < 1 || !d_supported(d) || (long long)L > kMaxL || (long long)B * H * L > kMaxRows)
         return (size_t)-1;
     if (dtype != LION_DTYPE_F32 && dtype != LION_DTYPE_BF16) return (size_t)-1;
+    // the plans depend on sizes, dtype and (for the full form's LDS) the mask kind; LION-S is the
+    // largest of the kinds, so it answers for all of them
+    lion::AttnArgs a = make_args(nullptr, nullptr, nullptr, nullptr, LION_MASK_S, 0.f, B, H, L, d, dtype, nullptr,
+                                 dtype, nullptr);
+    lion::Plan plan;
     switch (form) {
-    case LION_FORM_FULL: return 0;
-    case LION_FORM_CHUNK: return c_supported(C) ? lion::chunk_workspace_bytes(B, H, L, d, C) : (size_t)-1;
-    case LION_FORM_BIRNN: return lion::birnn_workspace_bytes(B, H, L, d);
+    case LION_FORM_FULL: plan = lion::plan_full(a); break;
+    case LION_FORM_CHUNK:
+        if (!c_supported_for(C, d)) return (size_t)-1;
+        a.C = C;
+        plan = lion::plan_chunk(a);
+        break;
+    case LION_FORM_BIRNN: plan = lion::plan_birnn(a); break;
     default: return (size_t)-1;
     }
+    return plan.ok ? plan.workspace : (size_t)-1;
 }
 
 const char *lion_status_str(int status) {

@@ -17,6 +17,7 @@
 
 #include "lion_device.h"
 #include "lion_internal.h"
+#include "lion_mask.h"
 
 namespace lion {
 namespace {
@@ -47,67 +48,6 @@ struct FullCfg {
     static constexpr int VROW = kKB + (BF16 ? 8 : 4);       // V^T tile row pitch (elements)
     using QFrag = std::conditional_t<BF16, bf16x8, float>;
 };
-
-// Exclusive scan of one double per thread over the workgroup (nt a multiple of 64, <= 1024).
-__device__ double block_excl_scan(double x, double *sh, int tid, int nt) {
-    sh[tid] = x;
-    __syncthreads();
-    if (tid < 64) {
-        const int per = nt / 64;
-        double local = 0.0;
-        for (int u = 0; u < per; ++u) local += sh[tid * per + u];
-        double incl = local;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            double t = __shfl_up(incl, o, 64);
-            if (tid >= o) incl += t;
-        }
-        double run = incl - local;
-        for (int u = 0; u < per; ++u) {
-            double t = sh[tid * per + u];
-            sh[tid * per + u] = run;
-            run += t;
-        }
-    }
-    __syncthreads();
-    double r = sh[tid];
-    __syncthreads();
-    return r;
-}
-
-// Mask exponent table E[0 .. nkb*32) for one (batch, head), relative to position t_ref.
-template <int KIND>
-__device__ void build_exponents(float *E, double *scan_sh, const float *ll, int bh, int H, int L, int Lpad,
-                                int t_ref, int tid, int nt) {
-    if constexpr (KIND == kMaskD) {
-        const float lg = ll[bh % H] * kLog2e;
-        for (int t = tid; t < Lpad; t += nt) E[t] = t < L ? (float)(t - t_ref) * lg : 0.f;
-        __syncthreads();
-    } else if constexpr (KIND == kMaskS) {
-        const float *row = ll + (size_t)bh * L;
-        const int seg = (L + nt - 1) / nt;
-        const int t0 = tid * seg, t1 = min(t0 + seg, L);
-        double s = 0.0;
-        for (int t = t0; t < t1; ++t) s += (double)row[t];
-        const double excl = block_excl_scan(s, scan_sh, tid, nt);
-        // A at t_ref, computed by the thread whose segment holds it
-        __shared__ double a_ref;
-        if (t_ref >= t0 && t_ref < t1) {
-            double a = excl;
-            for (int t = t0; t <= t_ref; ++t) a += (double)row[t];
-            a_ref = a;
-        }
-        __syncthreads();
-        const double ar = a_ref;
-        double a = excl;
-        for (int t = t0; t < t1; ++t) {
-            a += (double)row[t];
-            E[t] = (float)((a - ar) * 1.4426950408889634);
-        }
-        for (int t = L + tid; t < Lpad; t += nt) E[t] = 0.f;
-        __syncthreads();
-    }
-}
 
 template <int D, int KIND, int QT, bool BF16>
 __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
@@ -370,9 +310,41 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
     }
 }
 
+// Launch shape of the full form: query tiles per wave, waves per workgroup, workgroups per
+// (batch, head), and the LDS the kernel asks for.
+struct FullShape {
+    int qt, nw, nsb;
+    size_t lds;
+};
+
+FullShape full_shape(const AttnArgs &a) {
+    const int ntiles = (a.L + 15) / 16;
+    const long bhs = (long)a.B * a.H;
+    int qt = 1;
+    if (a.in_bf16) {
+        // largest tile count per wave that still gives >= 2 waves per SIMD (256 CUs x 4 SIMDs)
+        const int cand[3] = {a.d == 128 ? 2 : 4, 2, 1};
+        for (int c : cand) {
+            qt = c;
+            if (bhs * ((ntiles + c - 1) / c) >= 2048) break;
+        }
+    }
+    const int wtiles = (ntiles + qt - 1) / qt;      // waves needed per (batch, head)
+    FullShape sh;
+    sh.qt = qt;
+    sh.nw = wtiles < 8 ? wtiles : 8;
+    sh.nsb = (ntiles + sh.nw * qt - 1) / (sh.nw * qt);
+    const size_t esz = a.in_bf16 ? 2 : 4;
+    const int Lpad = ((a.L + kKB - 1) / kKB) * kKB;
+    size_t lds = (size_t)(kKB * (a.d + (a.in_bf16 ? 8 : 4)) + a.d * (kKB + (a.in_bf16 ? 8 : 4))) * esz;
+    if (a.kind != kMaskLit) lds += (size_t)Lpad * 4;
+    if (a.kind == kMaskS) lds += (size_t)sh.nw * 64 * 8;
+    sh.lds = lds;
+    return sh;
+}
+
 template <int D, int KIND, int QT, bool BF16>
-hipError_t launch_full_t(const AttnArgs &a, hipStream_t stream, int nw, int nsb) {
-    using C = FullCfg<D, BF16>;
+hipError_t launch_full_t(const AttnArgs &a, hipStream_t stream, const FullShape &sh) {
     FullParams p;
     p.q = a.q;
     p.k = a.k;
@@ -384,40 +356,25 @@ hipError_t launch_full_t(const AttnArgs &a, hipStream_t stream, int nw, int nsb)
     p.y = a.y;
     p.out_bf16 = a.out_bf16 ? 1 : 0;
     p.den_out = a.den_out;
-    p.nsb = nsb;
-    p.tiles_per_wg = nw * QT;
-    p.nblocks = a.B * a.H * nsb;
-    const int nt = nw * 64;
-    const int Lpad = ((a.L + kKB - 1) / kKB) * kKB;
-    size_t lds = (size_t)(kKB * C::KROW + D * C::VROW) * sizeof(typename C::T);
-    if (KIND != kMaskLit) lds += (size_t)Lpad * 4;
-    if (KIND == kMaskS) lds += (size_t)nt * 8;
-    hipLaunchKernelGGL((full_kernel<D, KIND, QT, BF16>), dim3(p.nblocks), dim3(nt), lds, stream, p);
+    p.nsb = sh.nsb;
+    p.tiles_per_wg = sh.nw * QT;
+    p.nblocks = a.B * a.H * sh.nsb;
+    if (sh.lds > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&full_kernel<D, KIND, QT, BF16>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh.lds);
+    hipLaunchKernelGGL((full_kernel<D, KIND, QT, BF16>), dim3(p.nblocks), dim3(sh.nw * 64), sh.lds, stream, p);
     return hipGetLastError();
 }
 
 template <int D, int KIND, bool BF16>
 hipError_t dispatch_qt(const AttnArgs &a, hipStream_t stream) {
-    const int ntiles = (a.L + 15) / 16;
-    const long bhs = (long)a.B * a.H;
-    int qt = 1;
-    if constexpr (BF16) {
-        // largest tile count per wave that still gives >= 2 waves per SIMD (256 CUs x 4 SIMDs)
-        const int cand[3] = {D == 128 ? 2 : 4, 2, 1};
-        for (int c : cand) {
-            qt = c;
-            if (bhs * ((ntiles + c - 1) / c) >= 2048) break;
-        }
-    }
-    const int wtiles = (ntiles + qt - 1) / qt;      // waves needed per (batch, head)
-    const int nw = wtiles < 8 ? wtiles : 8;
-    const int nsb = (ntiles + nw * qt - 1) / (nw * qt);
+    const FullShape sh = full_shape(a);
     if constexpr (BF16) {
         if constexpr (D != 128)
-            if (qt == 4) return launch_full_t<D, KIND, 4, BF16>(a, stream, nw, nsb);
-        if (qt == 2) return launch_full_t<D, KIND, 2, BF16>(a, stream, nw, nsb);
+            if (sh.qt == 4) return launch_full_t<D, KIND, 4, BF16>(a, stream, sh);
+        if (sh.qt == 2) return launch_full_t<D, KIND, 2, BF16>(a, stream, sh);
     }
-    return launch_full_t<D, KIND, 1, BF16>(a, stream, nw, nsb);
+    return launch_full_t<D, KIND, 1, BF16>(a, stream, sh);
 }
 
 template <int D, bool BF16>
@@ -440,6 +397,13 @@ hipError_t dispatch_d(const AttnArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+Plan plan_full(const AttnArgs &a) {
+    Plan p;
+    p.ok = full_shape(a).lds <= kLdsPerWorkgroup;
+    p.workspace = 0;
+    return p;
+}
 
 hipError_t launch_full(const AttnArgs &a, hipStream_t stream) {
     return a.in_bf16 ? dispatch_d<true>(a, stream) : dispatch_d<false>(a, stream);

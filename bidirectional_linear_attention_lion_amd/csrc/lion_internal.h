@@ -22,12 +22,22 @@ struct AttnArgs {
     size_t workspace_bytes;
 };
 
+// What a form needs for given sizes, decided on the host without any HIP call.
+struct Plan {
+    bool ok;            // false: the sizes exceed what the kernels support (e.g. LDS per workgroup)
+    size_t workspace;   // bytes of caller workspace the launch will use
+};
+
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;   // gfx950 LDS available to one workgroup
+
+Plan plan_full(const AttnArgs &a);
+Plan plan_chunk(const AttnArgs &a);
+Plan plan_birnn(const AttnArgs &a);
+
 // Each launcher enqueues its kernels on `stream` and returns hipSuccess or the launch error.
+// Callers check the form's plan first.
 hipError_t launch_full(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_chunk(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_birnn(const AttnArgs &a, hipStream_t stream);
-
-size_t chunk_workspace_bytes(int B, int H, int L, int d, int C);
-size_t birnn_workspace_bytes(int B, int H, int L, int d);
 
 }  // namespace lion

@@ -101,8 +101,8 @@ LION_API int lion_attn_full(const void *q, const void *k, const void *v, const f
                    int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out, void *stream);
 
 /* Chunkwise form: masked attention inside chunks of C consecutive tokens plus forward and
- * backward d x (d+1) states carried from chunk to chunk.  C in {16, 32, 64, 128, 256}; the last
- * chunk may be partial.  Source: reply "4: Practicality of Recurrent Inference"; blog "LION Part
+ * backward d x (d+1) states carried from chunk to chunk.  C in {16, 32, 64, 128, 256} (at most 128
+ * when d = 128; larger is LION_ERR_UNSUPPORTED); the last chunk may be partial.  Source: reply "4: Practicality of Recurrent Inference"; blog "LION Part
  * IV - Results", "LION Chunk".
  * workspace: device buffer of at least lion_attn_workspace_bytes(LION_FORM_CHUNK, ...) bytes
  * (may be NULL when that is 0); its contents on entry do not matter and on exit are unspecified. */

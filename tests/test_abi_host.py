@@ -96,6 +96,11 @@ def test_chunk_size_checks(C, status):
     assert chunk(C=C) == status
 
 
+def test_chunk_size_limit_for_d128():
+    assert chunk(C=256, d=128) == UNSUPPORTED
+    assert lion.lion_attn_workspace_bytes(lion.FORM_CHUNK, 1, 1, 100, 128, 256, 1) == SIZE_MAX
+
+
 def test_workspace_query():
     wb = lion.lion_attn_workspace_bytes
     assert wb(lion.FORM_FULL, 2, 3, 17, 64, 0, 1) == 0
