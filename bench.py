@@ -45,7 +45,30 @@ def parse_args():
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0,
                     help="wall-time budget of the oracle sample (0 disables)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the benchmark, run plain device copies of this many MiB (reference for "
+                         "HBM byte counters) and print their rate")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int, reps: int = 5):
+    """Device-to-device copies of a known size: reads and writes exactly mib MiB each."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    print(json.dumps({"copy_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4, "ms": ms,
+                      "GBps_read_plus_write": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def kernel_hash(form: str) -> str:
@@ -115,6 +138,9 @@ def cpu_baseline(wl, budget_s: float):
 
 def main():
     args = parse_args()
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               f"(the (batch, head) problems are independent, see the design notes for sharding)",
