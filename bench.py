@@ -1,8 +1,10 @@
 """Throughput of LION bidirectional masked linear attention (forward) on one MI355X.
 
-One step = one forward pass of every form listed (full, chunk, bidirectional RNN by default) over
-one batch of the workload's synthetic inputs; each form writes the attention output of all B x L
-tokens (every head).  Input sets are rotated so that more than --rotate-gib of distinct buffers
+One step = one forward pass of every form the workload is quoted with (for the default ViT-Tiny
+shaped LION-LIT workload: the full and the chunkwise form) over one batch of the workload's
+synthetic inputs; each form writes the attention output of all B x L tokens (every head).  The
+timed region runs the K steps form by form: K back-to-back launches of each form between one pair
+of HIP events on the launch stream, so each form's average launch duration is its events' span / K.  Input sets are rotated so that more than --rotate-gib of distinct buffers
 stream through HBM: the 256 MB last-level cache cannot hold them, so kernels read HBM, not cache.
 
 Prints one JSON line.  ``value`` is form-tokens per second: forms x B x L tokens per step over the
@@ -40,7 +42,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="vit_tiny_lit")
-    ap.add_argument("--forms", default="full,chunk,birnn")
+    ap.add_argument("--forms", default=None, help="comma-separated forms (default: the workload's)")
     ap.add_argument("--chunk", type=int, default=None, help="chunk size C (default: the workload's first)")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0,
@@ -69,6 +71,33 @@ def copy_calibration(mib: int, reps: int = 5):
     ms = t0.elapsed_time(t1) / reps
     print(json.dumps({"copy_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4, "ms": ms,
                       "GBps_read_plus_write": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
+
+
+def spin_cycles_for(seconds: float) -> int:
+    """Argument of torch.cuda._sleep that keeps the GPU busy for about `seconds`."""
+    import torch
+    n = 1 << 20
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    torch.cuda._sleep(n)
+    b.record()
+    torch.cuda.synchronize()
+    per_cycle = a.elapsed_time(b) * 1e-3 / n
+    return int(seconds / max(per_cycle, 1e-12))
+
+
+def host_seconds_per_call(call, forms, start):
+    """Host time to enqueue one launch (measured after warm-up, GPU work not waited for)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(5):
+        for f in forms:
+            call(f, start + s)
+    t = (time.perf_counter() - t0) / (5 * len(forms))
+    torch.cuda.synchronize()
+    return t
 
 
 def kernel_hash(form: str) -> str:
@@ -154,7 +183,7 @@ def main():
 
     wl = lin.WORKLOADS[args.workload]
     C = args.chunk or wl.chunks[0]
-    forms = [f for f in args.forms.split(",") if f]
+    forms = list(wl.forms) if args.forms is None else [f for f in args.forms.split(",") if f]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -192,17 +221,21 @@ def main():
             call(f, s)
     torch.cuda.synchronize()
 
-    ev = {f: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for f in forms}
+    ev = {f: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for f in forms}
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    # Hold the GPU in a spin kernel while the host enqueues every timed launch, so the kernels then run
+    # back to back and the events bracket kernel execution, not host submission time.
+    host_s = host_seconds_per_call(call, forms, args.warmup)
+    sleep_cycles = spin_cycles_for(1.5 * host_s * len(forms) * args.steps + 2e-3)
     torch.cuda.synchronize()
+    torch.cuda._sleep(sleep_cycles)
     t_start.record(stream)
-    for s in range(args.steps):
-        for f in forms:
-            ev[f][s][0].record(stream)
-            call(f, args.warmup + s)
-            ev[f][s][1].record(stream)
+    for f in forms:
+        ev[f][0].record(stream)
+        for s in range(args.steps):
+            call(f, args.warmup + 5 + s)
+        ev[f][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -211,14 +244,11 @@ def main():
     tokens = wl.B * wl.L
     per_form = {}
     for f in forms:
-        ms = [a.elapsed_time(b) for a, b in ev[f]]
-        avg = float(np.mean(ms))
+        avg = ev[f][0].elapsed_time(ev[f][1]) / args.steps
         nbytes, flops = algorithmic(f, wl, C)
         per_form[f] = {
             "tokens_per_s": tokens / (avg * 1e-3),
             "ms_avg": avg,
-            "ms_p10": float(np.percentile(ms, 10)),
-            "ms_p90": float(np.percentile(ms, 90)),
             "alg_GBps": nbytes / (avg * 1e-3) / 1e9,
             "alg_TFLOPs": flops / (avg * 1e-3) / 1e12,
             "bound": bound_of(f),
@@ -253,7 +283,8 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "L": wl.L, "d": wl.d,
-                   "mask": lin.KIND_NAME[wl.kind], "forms": forms, "C": C, "input_sets": nsets},
+                   "mask": lin.KIND_NAME[wl.kind], "forms": forms, "C": C, "input_sets": nsets,
+                   "host_us_per_launch": host_s * 1e6},
         "forms": per_form,
         "roofline": {"bound": bound_of(dom), "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak,

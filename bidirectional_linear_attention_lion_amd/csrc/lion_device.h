@@ -71,6 +71,13 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
     return x * per + (x < rem ? x : rem) + idx;
 }
 
+// Value known to be the same in every lane of the wave, kept in a scalar register (so branches on it
+// are scalar branches rather than exec-mask divergence).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uniform(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }

@@ -2,27 +2,32 @@
 //
 // Y = SCALE(phi(Q) phi(K)^T (.) M) V, the form LION trains with ("LION: A bidirectional framework
 // that trains like a Transformer and infers like an RNN", reply "Concern 1", Theorem 3.3 Eq. 25).
-// The L x L score matrix is never materialised: each workgroup owns a run of 16-row query tiles
-// of one (batch, head) and streams the keys in blocks of 32 through LDS.  Per block and query
-// tile a wave forms S^T = phi(K) phi(Q)^T with matrix-core tiles, applies the mask in registers,
-// accumulates the fp32 row sums, and feeds the masked scores back as the B operand of
-// O^T = V^T P^T without leaving registers.
+// The L x L score matrix is never materialised.  A workgroup (4 or 8 waves) owns a run of 16-row
+// query tiles of one (batch, head); each wave owns up to QT consecutive tiles.  Keys stream through
+// LDS in super-blocks of 64 (phi(K) row-major, V transposed), double-buffered: the global loads of
+// super-block s+1 are in flight while the waves compute on super-block s.  Per 32-key sub-block and
+// query tile a wave forms S^T = phi(K) phi(Q)^T on matrix cores, applies the mask in registers,
+// accumulates fp32 row sums, and feeds the masked scores back as the B operand of O^T = V^T P^T
+// (the D layout of the first product is the B layout of the second, so P never leaves registers).
 //
-// Mask: M_ij = exp(-|A_i - A_j|) with A the prefix sums of log(lambda) (the cumsum mask of the
-// pages' "P3: LION-S uses cumsum" reply), kept as a per-position exponent table E (base 2) in LDS:
-//   LIT: no mask;  D: E_t = (t - t_ref) log2(lambda_h);  S: E_t = (A_t - A_ref) log2(e) from an fp64
-//   prefix scan, so no fp32 cancellation builds up along long sequences.
-// Only non-positive exponents are exponentiated (exp2(-|E_i - E_j|)).
+// Mask (see lion_mask.h): M_ij = exp2(-|E_i - E_j|).  A sub-block whose keys all lie after a wave's
+// last query row r uses the separable form M_ij = exp2(E_r - E_i) * exp2(E_j - E_r) (both factors
+// <= 1): the row factor is computed once per query row, the column factor once per key and shared
+// by all the wave's tiles, so a score costs two multiplies instead of an exponential.  Keys wholly
+// before the first row r0 use exp2(E_i - E_r0) * exp2(E_r0 - E_j) likewise.  Only sub-blocks that
+// overlap the wave's rows pay one exponential per score.
 #include <type_traits>
 
 #include "lion_device.h"
 #include "lion_internal.h"
 #include "lion_mask.h"
+#include "lion_stage.h"
 
 namespace lion {
 namespace {
 
-constexpr int kKB = 32;  // keys per staged block (two 16-key halves of S^T)
+constexpr int kKB = 32;                       // keys per sub-block (two 16-key halves of S^T)
+constexpr size_t kStageBytes = 64 * 1024;     // K + V bytes of one stage (a double buffer halves it)
 
 struct FullParams {
     const void *q, *k, *v;
@@ -35,17 +40,16 @@ struct FullParams {
     int nsb;           // workgroups per (batch, head)
     int tiles_per_wg;  // 16-row query tiles per workgroup
     int nblocks;       // grid size
+    int sk;            // keys per stage (multiple of 32)
+    int nbuf;          // 1: the whole sequence is one stage; 2: double-buffered stages
 };
 
 template <int D, bool BF16>
 struct FullCfg {
     using T = std::conditional_t<BF16, __bf16, float>;
-    static constexpr int VEC = 16 / (int)sizeof(T);        // elements per 16-byte chunk
-    static constexpr int CPK = D / VEC;                     // chunks per key row
+    using RT = RowTile<D, T>;
     static constexpr int CPL = D / 4;                       // channels owned by each lane group
     static constexpr int NS = BF16 ? (CPL + 7) / 8 : CPL;   // score MFMA steps
-    static constexpr int KROW = D + (BF16 ? 8 : 4);         // K tile row pitch (elements)
-    static constexpr int VROW = kKB + (BF16 ? 8 : 4);       // V^T tile row pitch (elements)
     using QFrag = std::conditional_t<BF16, bf16x8, float>;
 };
 
@@ -53,14 +57,15 @@ template <int D, int KIND, int QT, bool BF16>
 __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
     using C = FullCfg<D, BF16>;
     using T = typename C::T;
+    using RT = typename C::RT;
     extern __shared__ __align__(16) unsigned char smem[];
 
-    const int tid = threadIdx.x, nt = blockDim.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, nt = blockDim.x, nw = nt >> 6;
+    const int lane = tid & 63, wave = uniform(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int L = p.L;
-    const int nkb = (L + kKB - 1) / kKB;
-    const int Lpad = nkb * kKB;
+    const int L = p.L, SK = p.sk;
+    const int nst = (L + SK - 1) / SK;
+    const int Lpad = nst * SK;
     const int ntiles = (L + 15) / 16;
 
     const int tile = xcd_tile(blockIdx.x, p.nblocks);
@@ -68,36 +73,47 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
     const int sb = tile % p.nsb;
     const int tile0 = sb * p.tiles_per_wg;                  // first query tile of this workgroup
     const int wtile0 = tile0 + wave * QT;                    // first query tile of this wave
+    const int wave_tiles = max(0, min(QT, ntiles - wtile0));
 
-    // LDS carve-up: [E table][fp64 scan scratch][K tile][V^T tile]
-    float *E = reinterpret_cast<float *>(smem);
-    double *scan_sh = reinterpret_cast<double *>(smem + (KIND == kMaskLit ? 0 : Lpad * 4));
-    unsigned char *tiles = smem + (KIND == kMaskLit ? 0 : Lpad * 4 + (KIND == kMaskS ? nt * 8 : 0));
-    T *Ks = reinterpret_cast<T *>(tiles);
-    T *Vt = Ks + kKB * C::KROW;
+    // LDS: [K stage buffers][V stage buffers][E table][fp64 scan scratch]
+    T *Kb = reinterpret_cast<T *>(smem);
+    T *Vb = Kb + (size_t)p.nbuf * SK * D;
+    float *E = reinterpret_cast<float *>(Vb + (size_t)p.nbuf * SK * D);
+    double *scan_sh = reinterpret_cast<double *>(E + (KIND == kMaskLit ? 0 : Lpad));
 
-    const size_t base = (size_t)bh * L;  // row offset of this (batch, head)
+    const size_t base = (size_t)bh * L;
     const T *qg = reinterpret_cast<const T *>(p.q) + base * D;
     const T *kg = reinterpret_cast<const T *>(p.k) + base * D;
     const T *vg = reinterpret_cast<const T *>(p.v) + base * D;
 
+    // stage 0 in flight while the prologue runs
+    stage_rows<D, T>(Kb, kg, 0, SK, L, wave, nw, lane);
+    stage_rows<D, T>(Vb, vg, 0, SK, L, wave, nw, lane);
+
     if constexpr (KIND != kMaskLit)
         build_exponents<KIND>(E, scan_sh, p.ll, bh, p.H, L, Lpad, min(tile0 * 16, L - 1), tid, nt);
 
-    // ---- query fragments: phi(q) for this wave's tiles (B operand of S^T = K Q^T) -------------
+    // ---- query fragments: phi(q) of this wave's tiles (B operand of S^T = K Q^T) -----------------
     typename C::QFrag qf[QT][C::NS];
     float Ei[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         const int i = (wtile0 + qt) * 16 + r;
+        const bool ok = i < L && qt < wave_tiles;
         float x[C::CPL];
-        if (i < L && wtile0 + qt < ntiles) {
-            const T *src = qg + (size_t)i * D + g * C::CPL;
+        const T *src = qg + (size_t)(ok ? i : 0) * D + g * C::CPL;
+        if constexpr (C::CPL * sizeof(T) % 16 == 0) {
 #pragma unroll
-            for (int c = 0; c < C::CPL; ++c) x[c] = (float)src[c];
+            for (int c = 0; c < C::CPL; c += RT::VEC) {
+                T tmp[RT::VEC];
+                const u32x4 raw = ld16(src + c);
+                __builtin_memcpy(tmp, &raw, 16);
+#pragma unroll
+                for (int e = 0; e < RT::VEC; ++e) x[c + e] = (float)tmp[e];
+            }
         } else {
 #pragma unroll
-            for (int c = 0; c < C::CPL; ++c) x[c] = 0.f;
+            for (int c = 0; c < C::CPL; ++c) x[c] = (float)src[c];
         }
         float ss = 0.f;
 #pragma unroll
@@ -105,31 +121,46 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
             x[c] = phi_pre<KIND>(x[c]);
             ss += x[c] * x[c];
         }
+        float sc = ok ? 1.f : 0.f;
         if constexpr (KIND == kMaskS) {
             ss += __shfl_xor(ss, 16, 64);
             ss += __shfl_xor(ss, 32, 64);
-            const float sc = inv_norm(ss);
-#pragma unroll
-            for (int c = 0; c < C::CPL; ++c) x[c] *= sc;
-        }
-        if (!(i < L)) {
-#pragma unroll
-            for (int c = 0; c < C::CPL; ++c) x[c] = 0.f;
+            sc *= inv_norm(ss);
         }
         if constexpr (BF16) {
 #pragma unroll
             for (int s = 0; s < C::NS; ++s) {
                 bf16x8 f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) f[e] = (8 * s + e < C::CPL) ? f2bf(x[8 * s + e]) : f2bf(0.f);
+                for (int e = 0; e < 8; ++e) f[e] = (8 * s + e < C::CPL) ? f2bf(x[8 * s + e] * sc) : f2bf(0.f);
                 qf[qt][s] = f;
             }
         } else {
 #pragma unroll
-            for (int s = 0; s < C::NS; ++s) qf[qt][s] = x[s];
+            for (int s = 0; s < C::NS; ++s) qf[qt][s] = x[s] * sc;
         }
         Ei[qt] = 0.f;
         if constexpr (KIND != kMaskLit) Ei[qt] = E[min(i, L - 1)];
+    }
+
+    // rows of this wave and the row factors of the separable mask (keys before / after the rows)
+    const int rw0 = wtile0 * 16;
+    const int rwl = min((wtile0 + wave_tiles) * 16, L) - 1;
+    float e_first = 0.f, e_last = 0.f;
+    if constexpr (KIND != kMaskLit) {
+        if (wave_tiles > 0) {
+            e_first = uniform(E[rw0]);
+            e_last = uniform(E[rwl]);
+        }
+    }
+    float rowf_b[QT], rowf_a[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        rowf_b[qt] = rowf_a[qt] = 1.f;
+        if constexpr (KIND != kMaskLit) {
+            rowf_b[qt] = fast_exp2(Ei[qt] - e_first);
+            rowf_a[qt] = fast_exp2(e_last - Ei[qt]);
+        }
     }
 
     f32x4 acc_o[QT][D / 16];
@@ -140,106 +171,146 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
 #pragma unroll
         for (int ct = 0; ct < D / 16; ++ct) acc_o[qt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int wave_tiles = max(0, min(QT, ntiles - wtile0));
 
-    for (int kb = 0; kb < nkb; ++kb) {
-        // ---- stage phi(K) (row-major) and V^T for keys kb*32 .. kb*32+31 -------------------------
-        const int total = kKB * C::CPK;
-        for (int c0 = 0; c0 < total; c0 += nt) {
-            const int c = c0 + tid;
-            const bool active = c < total;
-            const int kl = c / C::CPK, cc = (c % C::CPK) * C::VEC;
-            const int j = kb * kKB + kl;
-            float xk[C::VEC], xv[C::VEC];
-            if (active && j < L) {
-                const T *ks = kg + (size_t)j * D + cc;
-                const T *vs = vg + (size_t)j * D + cc;
+    for (int s = 0; s < nst; ++s) {
+        const int buf = p.nbuf == 1 ? 0 : (s & 1);
+        T *kbuf = Kb + (size_t)buf * SK * D;
+        const T *vbuf = Vb + (size_t)buf * SK * D;
+        wait_vm_all();
+        __syncthreads();                                     // stage s is in LDS; buffer s+1 is free
+        if (s + 1 < nst) {
+            const int nb = (s + 1) & 1;
+            stage_rows<D, T>(Kb + (size_t)nb * SK * D, kg, (s + 1) * SK, SK, L, wave, nw, lane);
+            stage_rows<D, T>(Vb + (size_t)nb * SK * D, vg, (s + 1) * SK, SK, L, wave, nw, lane);
+        }
+        // phi over the staged keys (in place); keys at or past L become zero rows
+        {
+            const int row_end = min(SK, L - s * SK);         // rows of real keys in this stage
+            const int nslot = SK * RT::CPK;
+            const int first = (KIND == kMaskD) ? row_end * RT::CPK : 0;   // identity phi: only padding
+            for (int sl0 = first - first % 64; sl0 < nslot; sl0 += nt) {
+                const int sl = sl0 + tid;
+                if (sl - lane >= nslot) break;                // wave-uniform: nslot is a multiple of 64
+                const bool mine = sl >= first && sl < nslot;
+                const int row = sl / RT::CPK;
+                T x[RT::VEC];
+                __builtin_memcpy(x, kbuf + (size_t)sl * RT::VEC, 16);
+                float f[RT::VEC], ss = 0.f;
 #pragma unroll
-                for (int e = 0; e < C::VEC; ++e) {
-                    xk[e] = (float)ks[e];
-                    xv[e] = (float)vs[e];
+                for (int e = 0; e < RT::VEC; ++e) {
+                    f[e] = phi_pre<KIND>((float)x[e]);
+                    ss += f[e] * f[e];
                 }
-            } else {
+                float scl = row < row_end ? 1.f : 0.f;
+                if constexpr (KIND == kMaskS) scl *= inv_norm(group_sum<RT::CPK>(ss));
 #pragma unroll
-                for (int e = 0; e < C::VEC; ++e) xk[e] = xv[e] = 0.f;
-            }
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < C::VEC; ++e) {
-                xk[e] = phi_pre<KIND>(xk[e]);
-                ss += xk[e] * xk[e];
-            }
-            if constexpr (KIND == kMaskS) {
-                ss = group_sum<C::CPK>(ss);
-                const float sc = inv_norm(ss);
-#pragma unroll
-                for (int e = 0; e < C::VEC; ++e) xk[e] *= sc;
-            }
-            if (active) {
-                const bool valid = j < L;
-#pragma unroll
-                for (int e = 0; e < C::VEC; ++e) {
-                    Ks[kl * C::KROW + cc + e] = (T)(valid ? xk[e] : 0.f);
-                    Vt[(cc + e) * C::VROW + kl] = (T)xv[e];
-                }
+                for (int e = 0; e < RT::VEC; ++e) x[e] = (T)(f[e] * scl);
+                if (mine) __builtin_memcpy(kbuf + (size_t)sl * RT::VEC, x, 16);
             }
         }
         __syncthreads();
+        if (wave_tiles == 0) continue;
 
-        if (wave_tiles > 0) {
-            // K fragments (A operand of S^T): row 16t + r, channels of lane group g
-            typename C::QFrag kf[2][C::NS];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const T *src = Ks + (16 * t + r) * C::KROW + g * C::CPL;
-                if constexpr (BF16) {
-#pragma unroll
-                    for (int s = 0; s < C::NS; ++s) {
-                        bf16x8 f;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) f[e] = (8 * s + e < C::CPL) ? src[8 * s + e] : f2bf(0.f);
-                        kf[t][s] = f;
-                    }
-                } else {
-#pragma unroll
-                    for (int s = 0; s < C::NS; ++s) kf[t][s] = src[s];
-                }
-            }
-            // mask exponents of the 8 keys this lane touches: 16t + 4g + e
-            float Ej[2][4];
+        for (int h = 0; h < SK / kKB; ++h) {
+            const int j0 = s * SK + h * kKB;
+            if (j0 >= L) break;
+            // region of this sub-block relative to the wave's rows (wave-uniform)
+            int region = 0;                                    // overlap: per-score exponentials
             if constexpr (KIND != kMaskLit) {
+                if (j0 + kKB - 1 < rw0) region = 1;            // every key before every row
+                else if (j0 > rwl) region = 2;                  // every key after every row
+            }
+            // K fragments (A operand of S^T): key row 16t + r of the sub-block, channels of group g
+            auto kelem = [&](int t, int col) { return kbuf + RT::off(h * kKB + 16 * t + r, col); };
+            bf16x8 kf[2][BF16 ? C::NS : 1];
+            if constexpr (BF16) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) Ej[t][e] = E[kb * kKB + 16 * t + 4 * g + e];
+                    for (int st = 0; st < C::NS; ++st) {
+                        if constexpr (C::CPL >= 8) {
+                            kf[t][st] = *reinterpret_cast<const bf16x8 *>(kelem(t, g * C::CPL + 8 * st));
+                        } else {
+                            const bf16x4 h4 = *reinterpret_cast<const bf16x4 *>(kelem(t, g * C::CPL));
+                            bf16x8 f;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                f[e] = h4[e];
+                                f[4 + e] = f2bf(0.f);
+                            }
+                            kf[t][st] = f;
+                        }
+                    }
+            }
+            // per-key mask data of the 8 keys this lane touches, j0 + 16t + 4g + e: the exponent in the
+            // overlap region, the column factor elsewhere
+            float mk[2][4];
+            if constexpr (KIND != kMaskLit) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const f32x4 e4 = *reinterpret_cast<const f32x4 *>(E + j0 + 16 * t + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        mk[t][e] = region == 0 ? e4[e] : fast_exp2(region == 1 ? e_first - e4[e] : e4[e] - e_last);
+                }
+            }
+            // V^T fragments (A operand of O^T += V^T P^T): keys j0 + 4g + e and j0 + 16 + 4g + e of
+            // value channel 16 ct + r, read transposed from the row-major value tile
+            bf16x8 vfr[BF16 ? D / 16 : 1];
+            if constexpr (BF16) {
+#pragma unroll
+                for (int ct = 0; ct < D / 16; ++ct) {
+                    const int row = h * kKB + 4 * g + (r >> 2), col = 16 * ct + 4 * (r & 3);
+                    const bf16x4 lo = read_tr_b16(vbuf + RT::off(row, col));
+                    const bf16x4 hi = read_tr_b16(vbuf + RT::off(row + 16, col));
+                    bf16x8 f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        f[e] = lo[e];
+                        f[4 + e] = hi[e];
+                    }
+                    vfr[ct] = f;
+                }
             }
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) {
                 if (qt >= wave_tiles) break;
-                f32x4 s_acc[2];
+                f32x4 sacc[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    s_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < C::NS; ++s) {
+                    for (int st = 0; st < C::NS; ++st) {
                         if constexpr (BF16)
-                            s_acc[t] = mfma_bf16(kf[t][s], qf[qt][s], s_acc[t]);
+                            sacc[t] = mfma_bf16(kf[t][st], qf[qt][st], sacc[t]);
                         else
-                            s_acc[t] = mfma_f32(kf[t][s], qf[qt][s], s_acc[t]);
+                            sacc[t] = mfma_f32(*kelem(t, g * C::CPL + st), qf[qt][st], sacc[t]);
                     }
                 }
-                // s_acc[t][e] = S[query r][key 16t + 4g + e]; mask, row-sum, feed to P V
+                // sacc[t][e] = S[query r][key j0 + 16t + 4g + e]; mask it (region is wave-uniform)
                 float pv[2][4];
+                if (KIND == kMaskLit) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) pv[t][e] = sacc[t][e];
+                } else if (region == 0) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            pv[t][e] = sacc[t][e] * fast_exp2(-__builtin_fabsf(Ei[qt] - mk[t][e]));
+                } else {
+                    const float rowf = region == 1 ? rowf_b[qt] : rowf_a[qt];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) pv[t][e] = (sacc[t][e] * rowf) * mk[t][e];
+                }
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float m = 1.f;
-                        if constexpr (KIND != kMaskLit) m = fast_exp2(-__builtin_fabsf(Ei[qt] - Ej[t][e]));
-                        const float pe = s_acc[t][e] * m;
-                        den[qt] += pe;
-                        pv[t][e] = pe;
-                    }
+                    for (int e = 0; e < 4; ++e) den[qt] += pv[t][e];
                 if constexpr (BF16) {
                     bf16x8 pf;
 #pragma unroll
@@ -248,30 +319,19 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
                         pf[4 + e] = f2bf(pv[1][e]);
                     }
 #pragma unroll
-                    for (int ct = 0; ct < D / 16; ++ct) {
-                        const T *vs = Vt + (16 * ct + r) * C::VROW + 4 * g;
-                        bf16x8 vf;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            vf[e] = vs[e];
-                            vf[4 + e] = vs[16 + e];
-                        }
-                        acc_o[qt][ct] = mfma_bf16(vf, pf, acc_o[qt][ct]);
-                    }
+                    for (int ct = 0; ct < D / 16; ++ct) acc_o[qt][ct] = mfma_bf16(vfr[ct], pf, acc_o[qt][ct]);
                 } else {
 #pragma unroll
-                    for (int ct = 0; ct < D / 16; ++ct) {
-                        const T *vs = Vt + (16 * ct + r) * C::VROW + 4 * g;
+                    for (int ct = 0; ct < D / 16; ++ct)
 #pragma unroll
                         for (int t = 0; t < 2; ++t)
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
-                                acc_o[qt][ct] = mfma_f32(vs[16 * t + e], pv[t][e], acc_o[qt][ct]);
-                    }
+                                acc_o[qt][ct] = mfma_f32(vbuf[RT::off(h * kKB + 16 * t + 4 * g + e, 16 * ct + r)],
+                                                         pv[t][e], acc_o[qt][ct]);
                 }
             }
         }
-        __syncthreads();
     }
 
     // ---- epilogue: full row sums, divide, store -------------------------------------------------
@@ -310,10 +370,10 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
     }
 }
 
-// Launch shape of the full form: query tiles per wave, waves per workgroup, workgroups per
-// (batch, head), and the LDS the kernel asks for.
+// Launch shape of the full form: query tiles per wave, waves per workgroup (4 or 8), workgroups per
+// (batch, head), keys per stage, stage buffers, and the LDS the kernel asks for.
 struct FullShape {
-    int qt, nw, nsb;
+    int qt, nw, nsb, sk, nbuf;
     size_t lds;
 };
 
@@ -323,20 +383,29 @@ FullShape full_shape(const AttnArgs &a) {
     int qt = 1;
     if (a.in_bf16) {
         // largest tile count per wave that still gives >= 2 waves per SIMD (256 CUs x 4 SIMDs)
-        const int cand[3] = {a.d == 128 ? 2 : 4, 2, 1};
+        const int cand[3] = {a.d == 128 ? 1 : 4, 2, 1};
         for (int c : cand) {
             qt = c;
             if (bhs * ((ntiles + c - 1) / c) >= 2048) break;
         }
     }
-    const int wtiles = (ntiles + qt - 1) / qt;      // waves needed per (batch, head)
+    const int wtiles = (ntiles + qt - 1) / qt;      // waves with query tiles per (batch, head)
     FullShape sh;
     sh.qt = qt;
-    sh.nw = wtiles < 8 ? wtiles : 8;
+    sh.nw = wtiles >= 6 ? 8 : 4;
     sh.nsb = (ntiles + sh.nw * qt - 1) / (sh.nw * qt);
     const size_t esz = a.in_bf16 ? 2 : 4;
-    const int Lpad = ((a.L + kKB - 1) / kKB) * kKB;
-    size_t lds = (size_t)(kKB * (a.d + (a.in_bf16 ? 8 : 4)) + a.d * (kKB + (a.in_bf16 ? 8 : 4))) * esz;
+    const size_t per_key = 2 * (size_t)a.d * esz;   // K and V bytes of one key
+    const int lr = ((a.L + kKB - 1) / kKB) * kKB;
+    if ((size_t)lr * per_key <= kStageBytes) {
+        sh.sk = lr;                                  // the whole sequence is one stage
+        sh.nbuf = 1;
+    } else {
+        sh.sk = (int)(kStageBytes / 2 / per_key);     // double-buffered stages
+        sh.nbuf = 2;
+    }
+    const int Lpad = ((a.L + sh.sk - 1) / sh.sk) * sh.sk;
+    size_t lds = (size_t)sh.nbuf * sh.sk * per_key;
     if (a.kind != kMaskLit) lds += (size_t)Lpad * 4;
     if (a.kind == kMaskS) lds += (size_t)sh.nw * 64 * 8;
     sh.lds = lds;
@@ -359,6 +428,8 @@ hipError_t launch_full_t(const AttnArgs &a, hipStream_t stream, const FullShape 
     p.nsb = sh.nsb;
     p.tiles_per_wg = sh.nw * QT;
     p.nblocks = a.B * a.H * sh.nsb;
+    p.sk = sh.sk;
+    p.nbuf = sh.nbuf;
     if (sh.lds > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&full_kernel<D, KIND, QT, BF16>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh.lds);
@@ -370,9 +441,10 @@ template <int D, int KIND, bool BF16>
 hipError_t dispatch_qt(const AttnArgs &a, hipStream_t stream) {
     const FullShape sh = full_shape(a);
     if constexpr (BF16) {
-        if constexpr (D != 128)
+        if constexpr (D != 128) {
             if (sh.qt == 4) return launch_full_t<D, KIND, 4, BF16>(a, stream, sh);
-        if (sh.qt == 2) return launch_full_t<D, KIND, 2, BF16>(a, stream, sh);
+            if (sh.qt == 2) return launch_full_t<D, KIND, 2, BF16>(a, stream, sh);
+        }
     }
     return launch_full_t<D, KIND, 1, BF16>(a, stream, sh);
 }

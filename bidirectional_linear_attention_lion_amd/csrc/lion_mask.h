@@ -5,7 +5,7 @@
 // (parallel scan)").  Kernels keep a per-position exponent table E_t = (A_t - A_ref) log2(e) in LDS
 // and only ever exponentiate non-positive differences of it.  For LION-S the prefix sums are taken
 // in fp64 (a workgroup-wide scan), so rounding does not accumulate along long sequences; LION-D's
-// table is the exact product (t - t_ref) log2(lambda_h).
+// table is the single product (t - t_ref) log2(lambda_h).
 #pragma once
 
 #include "lion_device.h"
@@ -39,13 +39,14 @@ __device__ __forceinline__ double block_excl_scan(double x, double *sh, int tid,
     return r;
 }
 
-// Mask exponent table E[0 .. nkb*32) for one (batch, head), relative to position t_ref.
+// Mask exponent table E[0 .. Lpad) for one (batch, head), relative to position t_ref; entries past
+// L - 1 repeat E[L - 1].
 template <int KIND>
 __device__ __forceinline__ void build_exponents(float *E, double *scan_sh, const float *ll, int bh, int H, int L, int Lpad,
                                 int t_ref, int tid, int nt) {
     if constexpr (KIND == kMaskD) {
         const float lg = ll[bh % H] * kLog2e;
-        for (int t = tid; t < Lpad; t += nt) E[t] = t < L ? (float)(t - t_ref) * lg : 0.f;
+        for (int t = tid; t < Lpad; t += nt) E[t] = (float)(min(t, L - 1) - t_ref) * lg;
         __syncthreads();
     } else if constexpr (KIND == kMaskS) {
         const float *row = ll + (size_t)bh * L;
@@ -68,7 +69,11 @@ __device__ __forceinline__ void build_exponents(float *E, double *scan_sh, const
             a += (double)row[t];
             E[t] = (float)((a - ar) * 1.4426950408889634);
         }
-        for (int t = L + tid; t < Lpad; t += nt) E[t] = 0.f;
+        __syncthreads();
+        // positions past the end repeat the last exponent, so every difference a kernel forms with
+        // them stays <= 0 where real positions' would
+        const float elast = E[L - 1];
+        for (int t = L + tid; t < Lpad; t += nt) E[t] = elast;
         __syncthreads();
     }
 }

@@ -6,13 +6,17 @@ rounds to bf16 where the workload asks for bf16, and forms log(lambda) by each w
 The result carries the exact values the device receives (``*_dev``) and their exact fp64 upcast
 (``*_f64``), so the oracle consumes precisely what the kernels consume.
 
-Recipes (draw order q -> k -> v -> decay inputs; fp32 draws; bf16 by round-to-nearest-even):
+Recipes (draw order q -> k -> v -> decay inputs; fp32 draws; bf16 by round-to-nearest-even), with
+the forms each is quoted with:
   lion_s_unit   B1  H1  L64   d16 fp32  LION-S:   log lam = log sigmoid(z + 2), z ~ N(0,1) [B,H,L]
-  vit_tiny_lit  B64 H3  L197  d64 bf16  LION-LIT: lambda = 1 (no decay input)
+                                                  full, chunk (C=16), RNN
+  vit_tiny_lit  B64 H3  L197  d64 bf16  LION-LIT: lambda = 1 (no decay input);  full, chunk (C=64)
   vit_base_d    B64 H12 L197  d64 bf16  LION-D:   log lam_h = log(1 - 2^(-5-h)), h = 0..H-1
+                                                  full, chunk (C=64), RNN
   bert_large_s  B32 H16 L512  d64 bf16  LION-S:   log lam = log sigmoid(x_i . w_h + 3),
                                                   x ~ N(0,1) [B,L,1024] shared by heads, w ~ N(0,1/1024) [H,1024]
-  hires_d       B8  H12 L4097 d64 bf16  LION-D:   per-head lambda as vit_base_d
+                                                  full, chunk (C=64)
+  hires_d       B8  H12 L4097 d64 bf16  LION-D:   per-head lambda as vit_base_d;  chunk (C=64/128/256), RNN
 
 The shapes stand in for the pages' workloads (ViT-Tiny at 224 px: 196 patches + cls; ViT-Base
 with 12 heads; BERT-Large with 16 heads at 512 tokens; a 1024 x 1024 image in 16-pixel patches
@@ -38,7 +42,7 @@ class Workload:
     dtype: str          # "f32" or "bf16": storage and MFMA input type of q, k, v, y
     kind: int           # LIT / D / S
     lam_recipe: str     # "none", "per_head", "sigmoid_noise", "sigmoid_proj"
-    forms: tuple
+    forms: tuple        # the forms the workload is quoted with (every form runs on every workload in tests)
     chunks: tuple = (64,)
     eps: float = 1e-6
     seed: int = 0
@@ -52,13 +56,13 @@ WORKLOADS = {
     "lion_s_unit": Workload("lion_s_unit", 1, 1, 64, 16, "f32", S, "sigmoid_noise",
                             ("full", "chunk", "birnn"), chunks=(16,), seed=1),
     "vit_tiny_lit": Workload("vit_tiny_lit", 64, 3, 197, 64, "bf16", LIT, "none",
-                             ("full", "chunk", "birnn"), chunks=(64,), seed=2),
+                             ("full", "chunk"), chunks=(64,), seed=2),
     "vit_base_d": Workload("vit_base_d", 64, 12, 197, 64, "bf16", D, "per_head",
                            ("full", "chunk", "birnn"), chunks=(64,), seed=3),
     "bert_large_s": Workload("bert_large_s", 32, 16, 512, 64, "bf16", S, "sigmoid_proj",
-                             ("full", "chunk", "birnn"), chunks=(64,), seed=4),
+                             ("full", "chunk"), chunks=(64,), seed=4),
     "hires_d": Workload("hires_d", 8, 12, 4097, 64, "bf16", D, "per_head",
-                        ("full", "chunk", "birnn"), chunks=(64, 128, 256), seed=5),
+                        ("chunk", "birnn"), chunks=(64, 128, 256), seed=5),
 }
 
 
