@@ -102,7 +102,7 @@ def host_seconds_per_call(call, forms, start):
 
 def kernel_hash(form: str) -> str:
     h = hashlib.sha256()
-    for f in (KERNEL_FILES[form], "lion_device.h", "lion_mask.h"):
+    for f in (KERNEL_FILES[form], "lion_device.h", "lion_mask.h", "lion_stage.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

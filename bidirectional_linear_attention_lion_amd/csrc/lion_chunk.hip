@@ -4,545 +4,690 @@
 // bidirectional framework that trains like a Transformer and infers like an RNN", reply
 // "4: Practicality of Recurrent Inference"; blog "LION Part IV - Results", "LION Chunk").  The
 // pages print no chunk equations; the ones used here follow from the mask M_ij = exp(-|A_i - A_j|)
-// (A = prefix sums of log(lambda)).  For chunk c = tokens s_c .. e_c and [v, 1] the value row with
-// the row-sum column appended:
-//   F_c = exp(A_{e_c} - A_{e_{c-1}}) F_{c-1} + sum_{j in c} exp(A_{e_c} - A_j) phi(k_j) [v_j, 1]^T
-//   G_c = exp(A_{e_c} - A_{e_{c-1}}) G_{c+1} + sum_{j in c} exp(A_j - A_{e_{c-1}}) phi(k_j) [v_j, 1]^T
+// (A = prefix sums of log(lambda)).  For chunk c = tokens s_c .. e_c, a_c = exp(A_{e_c} - A_{e_{c-1}})
+// its total decay, and [v, 1] the value row with the row-sum column appended:
+//   local states   Fl_c = sum_{j in c} exp(A_{e_c} - A_j)     phi(k_j) [v_j, 1]^T
+//                  Gl_c = sum_{j in c} exp(A_j - A_{e_{c-1}}) phi(k_j) [v_j, 1]^T
+//   carried states F_c = a_c F_{c-1} + Fl_c   (F_{-1} = 0),   G_c = a_c G_{c+1} + Gl_c   (G_n = 0)
 //   out_i = sum_{j in c} M_ij (phi(q_i).phi(k_j)) [v_j, 1]
 //           + exp(A_i - A_{e_{c-1}}) phi(q_i)^T F_{c-1} + exp(A_{e_c} - A_i) phi(q_i)^T G_{c+1}
 //   y_i = out_i[:d] / (out_i[d] + eps)
-// Every exponent is <= 0.
+// Every exponent is <= 0, and all of them are differences of prefix sums taken inside one chunk, so
+// no long-range prefix sum (and its rounding) is ever formed.
 //
-// One workgroup (8 waves) per (batch, head) sweeps the chunks twice, keeping the d x (d+1)
-// states on chip:
-//   backward pass, c = n-1 .. 1: park G_{c+1} (bf16 d x d plus the fp32 row-sum column), then fold
-//     chunk c into G;
-//   forward pass,  c = 0 .. n-1: intra-chunk masked attention on matrix cores (as in the full form),
-//     plus F_{c-1} and the parked G_{c+1} applied to the decayed queries, then fold chunk c into F.
-// Chunk states live in fp32 matrix-core accumulators spread over the 8 waves.  The fold multiplies
-// the weighted values (w_j v_j)^T by phi(K); the row-sum column rides along as two extra rows of
-// that operand holding w_j split into a bf16 high part and the bf16 rounding of the remainder, so
-// the row-sum state -- whose rounding error a nearly cancelling denominator amplifies -- keeps
-// about 2^-17 relative accuracy although the tiles are bf16.  Parked backward states stay in LDS
-// when they fit, else in the caller's workspace.
+// Three launches, each parallel over (batch, head, chunk):
+//   state: one workgroup per chunk stages the chunk's keys and values in LDS and folds them into Fl_c
+//          and Gl_c on the matrix cores;
+//   scan:  the carried states, elementwise over the d x (d+1) entries, sequential over the chunks of
+//          one (batch, head), in place over the local states;
+//   out:   one workgroup per chunk: intra-chunk masked attention (matrix-core tiles, mask in
+//          registers) plus F_{c-1} and G_{c+1} applied to the decayed queries.
+// A state is stored as its d x d value part in the input type plus its row-sum column in fp32.  A fold
+// multiplies phi(K)^T by the weighted values w_j v_j; the row-sum column rides along as two extra
+// columns of that operand holding w_j as a bf16 high part plus the bf16 rounding of the remainder,
+// so the row-sum state -- whose error a nearly cancelling denominator amplifies -- keeps about 2^-17
+// relative accuracy.  The value part is stored in the fold's own register layout: lane (r, g) of
+// tile (ct, nt) holds state[16 ct + r][16 nt + 4 g + e], which is exactly an A operand of the output
+// product when the contraction slots of group g are the key channels 16 nt + 4 g + e; the queries use
+// the same channel assignment, so neither side needs a transpose.
 #include <type_traits>
 
 #include "lion_device.h"
 #include "lion_internal.h"
-#include "lion_mask.h"
+#include "lion_stage.h"
 
 namespace lion {
 namespace {
 
-constexpr int kKB = 32;                // tokens per staged sub-block
-constexpr int kNW = 8;                 // waves per workgroup
-constexpr int kNT = kNW * 64;
-constexpr int kGLdsMax = 64 * 1024;    // parked backward states kept in LDS up to this many bytes
+constexpr int kKB = 32;   // keys per sub-block
+
+__host__ __device__ constexpr int cpad(int C) { return (C + kKB - 1) / kKB * kKB; }
+__host__ __device__ constexpr int state_waves(int d) { return d == 128 ? 8 : 4; }
 
 struct ChunkParams {
     const void *q, *k, *v;
     const float *ll;
     float eps;
-    int H, L, C;
+    int H, L, C, n;        // n: chunks per (batch, head)
     void *y;
     int out_bf16;
     float *den_out;
-    unsigned char *ws;   // parked states in global memory, or null when they live in LDS
+    unsigned char *fs;     // forward states, [B*H*n] slots
+    unsigned char *gs;     // backward states, [B*H*n] slots
+    float *tot;            // log2 of each chunk's total decay, [B*H*n]
 };
 
 template <int D, bool BF16>
 struct ChunkCfg {
     using T = std::conditional_t<BF16, __bf16, float>;
-    static constexpr int VEC = 16 / (int)sizeof(T);
-    static constexpr int CPK = D / VEC;
-    static constexpr int CPL = D / 4;
-    static constexpr int NS = BF16 ? (CPL + 7) / 8 : CPL;
-    static constexpr int KROW = D + (BF16 ? 8 : 4);      // row-major phi(K) sub-block pitch
-    static constexpr int TROW = kKB + (BF16 ? 8 : 4);    // transposed (token-contiguous) pitch
-    static constexpr int VR = D + 16;                     // weighted V^T rows: D values, w_hi, w_lo, zeros
-    static constexpr int SROW = D + (BF16 ? 8 : 4);      // state copy pitch (rows = value channel)
-    static constexpr int NCT = D / 16 + 1;                // state tiles along the value(+1) axis
-    static constexpr int NDT = D / 16;                    // state tiles along the key-channel axis
-    static constexpr int MAXT = (NCT * NDT + kNW - 1) / kNW;   // state tiles per wave
-    static constexpr int QT = D == 128 ? 1 : 2;           // query tiles per wave: C <= 16 * kNW * QT
+    using RT = RowTile<D, T>;
+    static constexpr int NDT = D / 16;                    // key-channel tiles
+    static constexpr int NCT = NDT + 1;                   // value tiles plus the weight tile
+    static constexpr int HW = NDT >= 2 ? 2 : 1;           // key-channel tiles per bf16 fragment
+    static constexpr int NP = NDT / HW;                   // bf16 fragments over the d channels
+    static constexpr int NQ = BF16 ? NP : D / 4;          // query fragments per tile
     using QFrag = std::conditional_t<BF16, bf16x8, float>;
-    static constexpr size_t GSLOT = (size_t)D * D * sizeof(T) + (size_t)D * 4;   // one parked state
+    static constexpr size_t VBYTES = (size_t)D * D * sizeof(T);
+    static constexpr size_t SLOT = (VBYTES + (size_t)D * 4 + 15) & ~(size_t)15;
 };
 
+// Element offset of lane `lane`'s four values of tile (ct, nt) in a state slot's value part.
 template <int D, bool BF16>
-__host__ __device__ size_t lds_fixed_bytes(int L) {
-    using C = ChunkCfg<D, BF16>;
-    using T = typename C::T;
-    const int Lpad = ((L + kKB - 1) / kKB) * kKB;
-    size_t b = (size_t)Lpad * 4 + kNT * 8;                 // exponent table + scan scratch
-    b += (size_t)kKB * C::KROW * sizeof(T);                // Ks
-    b += (size_t)D * C::TROW * sizeof(T);                  // Vt (plain, for P V)
-    b += (size_t)C::VR * C::TROW * sizeof(T);              // Vw (weighted, plus the two weight rows)
-    b += (size_t)D * C::TROW * sizeof(T);                  // Kt
-    b += (size_t)D * C::SROW * sizeof(T) + (size_t)D * 4;   // current F copy and its row-sum column
-    return (b + 15) & ~(size_t)15;
+__device__ __forceinline__ int slot_off(int ct, int nt, int lane) {
+    using Cf = ChunkCfg<D, BF16>;
+    return (((ct * Cf::NP + nt / Cf::HW) * 64 + lane) * Cf::HW + nt % Cf::HW) * 4;
 }
 
-// Parked backward states go to LDS when they are small and fit beside the fixed carve-up.
-template <int D, bool BF16>
-bool park_in_lds(int L, int Cc) {
-    const size_t park = (size_t)((L + Cc - 1) / Cc) * ChunkCfg<D, BF16>::GSLOT;
-    return park <= (size_t)kGLdsMax && lds_fixed_bytes<D, BF16>(L) + park <= kLdsPerWorkgroup;
+// Contraction channel of fp32 step s for lane group g: channels 16 nt + 4 g + e, s = 4 nt + e.
+__device__ __forceinline__ int f32_ch(int s, int g) { return 16 * (s / 4) + 4 * g + (s & 3); }
+
+// LION-S chunk-local exponents E[t] = sum_{u <= t} log2(lambda_{cs + u}) (fp64 scan), for t < rows;
+// entries past the chunk's last token repeat its total.  Needs rows <= threads; ends with a barrier.
+__device__ void chunk_exponents_s(float *E, double *wsum, const float *ll, int cn, int rows, int tid) {
+    double x = tid < cn ? (double)ll[tid] * 1.4426950408889634 : 0.0;
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) x += wsum[w];
+    if (tid < rows) E[tid] = (float)x;
+    __syncthreads();
 }
 
+// phi over `rows` staged key rows in place (LIT: elu + 1; S: silu, L2-normalised per row).
+template <int D, int KIND, typename T>
+__device__ __forceinline__ void phi_rows(T *kb, int rows, int tid, int nt) {
+    using RT = RowTile<D, T>;
+    const int nslot = rows * RT::CPK;
+    const int lane = tid & 63;
+    for (int sl0 = 0; sl0 < nslot; sl0 += nt) {
+        const int sl = sl0 + tid;
+        if (sl - lane >= nslot) break;   // whole wave past the end (nslot is a multiple of 64)
+        T x[RT::VEC];
+        __builtin_memcpy(x, kb + (size_t)sl * RT::VEC, 16);
+        float f[RT::VEC], ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < RT::VEC; ++e) {
+            f[e] = phi_pre<KIND>((float)x[e]);
+            ss += f[e] * f[e];
+        }
+        float scl = 1.f;
+        if constexpr (KIND == kMaskS) scl = inv_norm(group_sum<RT::CPK>(ss));
+#pragma unroll
+        for (int e = 0; e < RT::VEC; ++e) x[e] = (T)(f[e] * scl);
+        __builtin_memcpy(kb + (size_t)sl * RT::VEC, x, 16);
+    }
+}
+
+// V^T (or K^T) fragment of sub-block h, channel tile ct, from a row-major staged bf16 tile:
+// lane (r, g) gets rows h*32 + {4g + e, 16 + 4g + e} of column 16 ct + r.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16 *tile, int h, int ct, int r, int g) {
+    using RT = RowTile<D, __bf16>;
+    const int row = h * kKB + 4 * g + (r >> 2), col = 16 * ct + 4 * (r & 3);
+    const bf16x4 lo4 = read_tr_b16(tile + RT::off(row, col));
+    const bf16x4 hi4 = read_tr_b16(tile + RT::off(row + 16, col));
+    bf16x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[e] = lo4[e];
+        f[4 + e] = hi4[e];
+    }
+    return f;
+}
+
+// ================================ state kernel ========================================================
 template <int D, int KIND, bool BF16>
-__global__ void __launch_bounds__(kNT) chunk_kernel(ChunkParams p) {
+__global__ void __launch_bounds__(state_waves(D) * 64) chunk_state_kernel(ChunkParams p) {
     using Cf = ChunkCfg<D, BF16>;
     using T = typename Cf::T;
+    using RT = typename Cf::RT;
+    constexpr int NW = state_waves(D), NT = NW * 64;
+    constexpr int NDT = Cf::NDT, NCT = Cf::NCT;
+    constexpr bool kColOwn = NW == NDT;   // wave w owns key-channel tile nt = w; ct = u is static
+    constexpr int MAXT = (NCT * NDT + NW - 1) / NW;
     extern __shared__ __align__(16) unsigned char smem[];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int L = p.L, Cc = p.C;
-    const int n = (L + Cc - 1) / Cc;
-    const int Lpad = ((L + kKB - 1) / kKB) * kKB;
-    const int bh = blockIdx.x;
+    const int L = p.L, n = p.n;
+    const int bid = blockIdx.x, bh = bid / n, c = bid % n;
+    const int cs = c * p.C, cn = min(p.C, L - cs);
+    const int rows = cpad(cn);
+    const int cp = cpad(p.C);
+
+    T *Ks = reinterpret_cast<T *>(smem);
+    T *Vs = Ks + cp * D;
+    float *E = reinterpret_cast<float *>(Vs + cp * D);
+    double *wsum = reinterpret_cast<double *>(E + cp);
     const size_t base = (size_t)bh * L;
+    stage_rows<D, T>(Ks, reinterpret_cast<const T *>(p.k) + base * D, cs, rows, L, wave, NW, lane);
+    stage_rows<D, T>(Vs, reinterpret_cast<const T *>(p.v) + base * D, cs, rows, L, wave, NW, lane);
 
-    // ---- LDS carve-up ---------------------------------------------------------------------------------
-    unsigned char *sp = smem;
-    float *E = reinterpret_cast<float *>(sp);
-    sp += (size_t)Lpad * 4;
-    double *scan_sh = reinterpret_cast<double *>(sp);
-    sp += kNT * 8;
-    T *Ks = reinterpret_cast<T *>(sp);
-    sp += (size_t)kKB * Cf::KROW * sizeof(T);
-    T *Vt = reinterpret_cast<T *>(sp);
-    sp += (size_t)D * Cf::TROW * sizeof(T);
-    T *Vw = reinterpret_cast<T *>(sp);
-    sp += (size_t)Cf::VR * Cf::TROW * sizeof(T);
-    T *Kt = reinterpret_cast<T *>(sp);
-    sp += (size_t)D * Cf::TROW * sizeof(T);
-    T *Fs = reinterpret_cast<T *>(sp);
-    sp += (size_t)D * Cf::SROW * sizeof(T);
-    float *Fz = reinterpret_cast<float *>(sp);
-    sp = smem + lds_fixed_bytes<D, BF16>(L);
-    unsigned char *park = p.ws ? p.ws + (size_t)bh * n * Cf::GSLOT : sp;
-
-    const T *qg = reinterpret_cast<const T *>(p.q) + base * D;
-    const T *kg = reinterpret_cast<const T *>(p.k) + base * D;
-    const T *vg = reinterpret_cast<const T *>(p.v) + base * D;
-
-    if constexpr (KIND != kMaskLit) build_exponents<KIND>(E, scan_sh, p.ll, bh, p.H, L, Lpad, 0, tid, kNT);
+    float lgD = 0.f;
+    if constexpr (KIND == kMaskD) lgD = p.ll[bh % p.H] * kLog2e;
+    if constexpr (KIND == kMaskS) chunk_exponents_s(E, wsum, p.ll + base + cs, cn, rows, tid);
+    // exponent of local token t relative to A_{e_{c-1}}
     auto Ex = [&](int t) -> float {
         if constexpr (KIND == kMaskLit) return 0.f;
+        else if constexpr (KIND == kMaskD) return (float)(t + 1) * lgD;
         else return E[t];
     };
-
-    f32x4 st[Cf::MAXT];
-
-    // Stage, for the tokens [j0, j0 + 32) that lie in [cs, ce]: phi(K) row-major (if attend),
-    // phi(K)^T, V^T, and the weighted (w_j v_j)^T with the weight split w_hi + w_lo below it.
-    auto stage = [&](int j0, int cs, int ce, bool attend, bool fwd_weights) {
-        const int total = kKB * Cf::CPK;
-        const float eref = fwd_weights ? Ex(ce) : Ex(cs > 0 ? cs - 1 : 0);
-        for (int c0 = 0; c0 < total; c0 += kNT) {
-            const int c = c0 + tid;
-            const bool active = c < total;
-            const int kl = c / Cf::CPK, cc = (c % Cf::CPK) * Cf::VEC;
-            const int j = j0 + kl;
-            const bool valid = active && j >= cs && j <= ce;
-            float xk[Cf::VEC], xv[Cf::VEC];
-            if (valid) {
-                const T *ks = kg + (size_t)j * D + cc;
-                const T *vs = vg + (size_t)j * D + cc;
-#pragma unroll
-                for (int e = 0; e < Cf::VEC; ++e) {
-                    xk[e] = (float)ks[e];
-                    xv[e] = (float)vs[e];
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < Cf::VEC; ++e) xk[e] = xv[e] = 0.f;
-            }
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < Cf::VEC; ++e) {
-                xk[e] = phi_pre<KIND>(xk[e]);
-                ss += xk[e] * xk[e];
-            }
-            if constexpr (KIND == kMaskS) {
-                const float sc = inv_norm(group_sum<Cf::CPK>(ss));
-#pragma unroll
-                for (int e = 0; e < Cf::VEC; ++e) xk[e] *= sc;
-            }
-            // fold weight: forward exp(A_{e_c} - A_j), backward exp(A_j - A_{e_{c-1}}); both <= 1
-            float w = 1.f;
-            if constexpr (KIND != kMaskLit) {
-                if (valid) w = fast_exp2(fwd_weights ? eref - Ex(j) : Ex(j) - eref);
-            }
-            if (active) {
-                if (!valid) w = 0.f;
-#pragma unroll
-                for (int e = 0; e < Cf::VEC; ++e) {
-                    const float kv = valid ? xk[e] : 0.f;
-                    if (attend) {
-                        Ks[kl * Cf::KROW + cc + e] = (T)kv;
-                        Vt[(cc + e) * Cf::TROW + kl] = (T)xv[e];
-                    }
-                    Kt[(cc + e) * Cf::TROW + kl] = (T)kv;
-                    Vw[(cc + e) * Cf::TROW + kl] = (T)(w * xv[e]);
-                }
-                if (cc == 0) {
-                    const T whi = (T)w;
-                    Vw[D * Cf::TROW + kl] = whi;
-                    Vw[(D + 1) * Cf::TROW + kl] = (T)(w - (float)whi);
-#pragma unroll
-                    for (int z = 2; z < 16; ++z) Vw[(D + z) * Cf::TROW + kl] = (T)0.f;
-                }
-            }
-        }
-    };
-
-    // st += Vw (sub-block) x phi(K) (sub-block) for this wave's state tiles
-    auto fold = [&]() {
-#pragma unroll
-        for (int u = 0; u < Cf::MAXT; ++u) {
-            const int tt = wave + kNW * u;
-            if (tt >= Cf::NCT * Cf::NDT) break;
-            const int ct = tt / Cf::NDT, nt = tt % Cf::NDT;
-            const T *va = Vw + (16 * ct + r) * Cf::TROW + 4 * g;
-            const T *kb = Kt + (16 * nt + r) * Cf::TROW + 4 * g;
-            if constexpr (BF16) {
-                bf16x8 a, b;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[e] = va[e];
-                    a[4 + e] = va[16 + e];
-                    b[e] = kb[e];
-                    b[4 + e] = kb[16 + e];
-                }
-                st[u] = mfma_bf16(a, b, st[u]);
-            } else {
-#pragma unroll
-                for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) st[u] = mfma_f32(va[16 * t2 + e], kb[16 * t2 + e], st[u]);
-            }
-        }
-    };
-
-    auto scale_state = [&](float a) {
-#pragma unroll
-        for (int u = 0; u < Cf::MAXT; ++u) st[u] *= a;
-    };
-
-    // write this wave's state tiles into a state copy (rows = value channel, cols = key channel)
-    auto write_state = [&](T *dst, float *dz) {
-#pragma unroll
-        for (int u = 0; u < Cf::MAXT; ++u) {
-            const int tt = wave + kNW * u;
-            if (tt >= Cf::NCT * Cf::NDT) break;
-            const int ct = tt / Cf::NDT, nt = tt % Cf::NDT;
-            if (ct < D / 16) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dst[(16 * ct + 4 * g + e) * Cf::SROW + 16 * nt + r] = (T)st[u][e];
-            } else if (g == 0) {
-                dz[16 * nt + r] = st[u][0] + st[u][1];   // row-sum state = w_hi part + w_lo part
-            }
-        }
-    };
-
-    auto zero_state = [&]() {
-#pragma unroll
-        for (int u = 0; u < Cf::MAXT; ++u) st[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    };
-
-    // ================= backward pass: park G_{c+1} for c = n-1 .. 0, fold chunk c for c >= 1 ==========
-    zero_state();
-    for (int c = n - 1; c >= 0; --c) {
-        const int cs = c * Cc, ce = min(cs + Cc, L) - 1;
-        // park G_{c+1} (zero for the last chunk)
-        {
-            T *gs = reinterpret_cast<T *>(park + (size_t)c * Cf::GSLOT);
-            float *gz = reinterpret_cast<float *>(park + (size_t)c * Cf::GSLOT + (size_t)D * D * sizeof(T));
-#pragma unroll
-            for (int u = 0; u < Cf::MAXT; ++u) {
-                const int tt = wave + kNW * u;
-                if (tt >= Cf::NCT * Cf::NDT) break;
-                const int ct = tt / Cf::NDT, nt = tt % Cf::NDT;
-                if (ct < D / 16) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) gs[(16 * ct + 4 * g + e) * D + 16 * nt + r] = (T)st[u][e];
-                } else if (g == 0) {
-                    gz[16 * nt + r] = st[u][0] + st[u][1];
-                }
-            }
-        }
-        if (c == 0) break;
-        // G_c = exp(A_{e_c} - A_{e_{c-1}}) G_{c+1} + sum_j exp(A_j - A_{e_{c-1}}) k_j [v_j, 1]^T
-        if constexpr (KIND != kMaskLit) scale_state(fast_exp2(Ex(ce) - Ex(cs - 1)));
-        for (int j0 = cs - (cs % kKB); j0 <= ce; j0 += kKB) {
-            __syncthreads();
-            stage(j0, cs, ce, false, false);
-            __syncthreads();
-            fold();
-        }
-    }
-    if (p.ws) __threadfence();
+    wait_vm_all();
     __syncthreads();
-
-    // ================= forward pass ======================================================================
-    const int tiles_per_chunk = (Cc + 15) / 16;
-    zero_state();
-    for (int c = 0; c < n; ++c) {
-        const int cs = c * Cc, ce = min(cs + Cc, L) - 1;
-        const bool has_f = c > 0, has_g = c < n - 1;
-        // current F_{c-1} (this wave's tiles -> LDS copy); G_{c+1} is read from its parking slot
+    if constexpr (KIND != kMaskD) {
+        phi_rows<D, KIND, T>(Ks, rows, tid, NT);
         __syncthreads();
-        if (has_f) write_state(Fs, Fz);
-        const T *Gs = reinterpret_cast<const T *>(park + (size_t)c * Cf::GSLOT);
-        const float *Gz = reinterpret_cast<const float *>(park + (size_t)c * Cf::GSLOT + (size_t)D * D * sizeof(T));
-        // fold weights for F_c; the state registers are rescaled now, the LDS copy keeps F_{c-1}
-        if (has_f && KIND != kMaskLit) scale_state(fast_exp2(Ex(ce) - Ex(cs - 1)));
+    }
+    const float etot = Ex(cn - 1);
 
-        // ---- query fragments of this wave's tiles in chunk c ----------------------------------------
-        typename Cf::QFrag qf[Cf::QT][Cf::NS];
-        float Ei[Cf::QT];
-        int ntl = 0;
+    auto tile_of = [&](int u, int &ct, int &nt) -> bool {
+        if constexpr (kColOwn) {
+            ct = u;
+            nt = wave;
+            return u < NCT;
+        } else {
+            const int tt = wave + NW * u;
+            ct = tt / NDT;
+            nt = tt % NDT;
+            return tt < NCT * NDT;
+        }
+    };
+
+    f32x4 sf[MAXT], sg[MAXT];
 #pragma unroll
-        for (int qt = 0; qt < Cf::QT; ++qt) {
-            const int tl = wave + kNW * qt;
-            const int i = cs + tl * 16 + r;
-            const bool tile_ok = tl < tiles_per_chunk;
-            if (tile_ok) ntl = qt + 1;
-            const bool ok = tile_ok && i <= ce;
-            float xq[Cf::CPL];
-            float ssq = 0.f;
+    for (int u = 0; u < MAXT; ++u) sf[u] = sg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int h = 0; h < rows / kKB; ++h) {
+        // fold weights of the sub-block's tokens 4g + e and 16 + 4g + e; 0 past the chunk's end
+        float wf[2][4], wg[2][4];
 #pragma unroll
-            for (int cc = 0; cc < Cf::CPL; ++cc) {
-                float x = ok ? (float)qg[(size_t)i * D + g * Cf::CPL + cc] : 0.f;
-                x = phi_pre<KIND>(x);
-                xq[cc] = x;
-                ssq += x * x;
-            }
-            if constexpr (KIND == kMaskS) {
-                ssq += __shfl_xor(ssq, 16, 64);
-                ssq += __shfl_xor(ssq, 32, 64);
-                const float sc = inv_norm(ssq);
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int cc = 0; cc < Cf::CPL; ++cc) xq[cc] *= sc;
-            }
-            if (!ok) {
-#pragma unroll
-                for (int cc = 0; cc < Cf::CPL; ++cc) xq[cc] = 0.f;
-            }
-            if constexpr (BF16) {
-#pragma unroll
-                for (int s = 0; s < Cf::NS; ++s) {
-                    bf16x8 f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) f[e] = (8 * s + e < Cf::CPL) ? f2bf(xq[8 * s + e]) : f2bf(0.f);
-                    qf[qt][s] = f;
+            for (int e = 0; e < 4; ++e) {
+                const int j = h * kKB + 16 * t + 4 * g + e;
+                const float valid = j < cn ? 1.f : 0.f;
+                float a = valid, b = valid;
+                if constexpr (KIND != kMaskLit) {
+                    const float ej = Ex(j);
+                    a *= fast_exp2(fminf(etot - ej, 0.f));
+                    b *= fast_exp2(fminf(ej, 0.f));
                 }
-            } else {
-#pragma unroll
-                for (int s = 0; s < Cf::NS; ++s) qf[qt][s] = xq[s];
+                wf[t][e] = a;
+                wg[t][e] = b;
             }
-            Ei[qt] = Ex(ok ? i : cs);
-        }
-
-        f32x4 acc[Cf::QT][D / 16];
-        float den[Cf::QT];
+        bf16x8 kfr{};
+        if constexpr (BF16 && kColOwn) kfr = tr_frag<D>(Ks, h, wave, r, g);
 #pragma unroll
-        for (int qt = 0; qt < Cf::QT; ++qt) {
-            den[qt] = 0.f;
+        for (int u = 0; u < MAXT; ++u) {
+            int ct, nt;
+            if (!tile_of(u, ct, nt)) break;
+            if constexpr (BF16) {
+                const bf16x8 a = kColOwn ? kfr : tr_frag<D>(Ks, h, nt, r, g);
+                bf16x8 bf, bg;
+                if (ct < NDT) {
+                    const bf16x8 vv = tr_frag<D>(Vs, h, ct, r, g);
 #pragma unroll
-            for (int ct = 0; ct < D / 16; ++ct) acc[qt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-
-        // ---- intra-chunk attention and the fold of chunk c into F -------------------------------------
-        for (int j0 = cs - (cs % kKB); j0 <= ce; j0 += kKB) {
-            __syncthreads();
-            stage(j0, cs, ce, true, true);
-            __syncthreads();
-            if (c < n - 1) fold();
-            if (ntl == 0) continue;
-            typename Cf::QFrag kf[2][Cf::NS];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const T *src = Ks + (16 * t + r) * Cf::KROW + g * Cf::CPL;
-                if constexpr (BF16) {
-#pragma unroll
-                    for (int s = 0; s < Cf::NS; ++s) {
-                        bf16x8 f;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) f[e] = (8 * s + e < Cf::CPL) ? src[8 * s + e] : f2bf(0.f);
-                        kf[t][s] = f;
+                    for (int e = 0; e < 4; ++e) {
+                        bf[e] = f2bf(wf[0][e] * (float)vv[e]);
+                        bf[4 + e] = f2bf(wf[1][e] * (float)vv[4 + e]);
+                        bg[e] = f2bf(wg[0][e] * (float)vv[e]);
+                        bg[4 + e] = f2bf(wg[1][e] * (float)vv[4 + e]);
                     }
                 } else {
 #pragma unroll
-                    for (int s = 0; s < Cf::NS; ++s) kf[t][s] = src[s];
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const __bf16 fh = f2bf(wf[t][e]), gh = f2bf(wg[t][e]);
+                            const __bf16 fl = f2bf(wf[t][e] - (float)fh), gl = f2bf(wg[t][e] - (float)gh);
+                            bf[4 * t + e] = r == 0 ? fh : (r == 1 ? fl : f2bf(0.f));
+                            bg[4 * t + e] = r == 0 ? gh : (r == 1 ? gl : f2bf(0.f));
+                        }
                 }
-            }
-            float Ej[2][4];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = min(j0 + 16 * t + 4 * g + e, L - 1);
-                    Ej[t][e] = Ex(j);
-                }
-#pragma unroll
-            for (int qt = 0; qt < Cf::QT; ++qt) {
-                if (qt >= ntl) break;
-                f32x4 sa[2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    sa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < Cf::NS; ++s) {
-                        if constexpr (BF16)
-                            sa[t] = mfma_bf16(kf[t][s], qf[qt][s], sa[t]);
-                        else
-                            sa[t] = mfma_f32(kf[t][s], qf[qt][s], sa[t]);
-                    }
-                }
-                float pv[2][4];
+                sf[u] = mfma_bf16(a, bf, sf[u]);
+                sg[u] = mfma_bf16(a, bg, sg[u]);
+            } else {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float m = 1.f;
-                        if constexpr (KIND != kMaskLit) m = fast_exp2(-__builtin_fabsf(Ei[qt] - Ej[t][e]));
-                        const float pe = sa[t][e] * m;
-                        den[qt] += pe;
-                        pv[t][e] = pe;
+                        const int row = h * kKB + 16 * t + 4 * g + e;
+                        const float a = Ks[RT::off(row, 16 * nt + r)];
+                        const float vv = ct < NDT ? Vs[RT::off(row, 16 * ct + r)] : (r == 0 ? 1.f : 0.f);
+                        sf[u] = mfma_f32(a, wf[t][e] * vv, sf[u]);
+                        sg[u] = mfma_f32(a, wg[t][e] * vv, sg[u]);
                     }
+            }
+        }
+    }
+
+    // store: value tiles in register layout, the row-sum column (hi + lo columns) as fp32
+    const bool want_f = c < n - 1, want_g = c > 0;
+    unsigned char *fslot = p.fs + (size_t)bid * Cf::SLOT;
+    unsigned char *gslot = p.gs + (size_t)bid * Cf::SLOT;
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) {
+        int ct, nt;
+        if (!tile_of(u, ct, nt)) break;
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            if (which == 0 ? !want_f : !want_g) continue;
+            const f32x4 s = which == 0 ? sf[u] : sg[u];
+            unsigned char *slot = which == 0 ? fslot : gslot;
+            if (ct < NDT) {
+                T *dst = reinterpret_cast<T *>(slot) + slot_off<D, BF16>(ct, nt, lane);
                 if constexpr (BF16) {
-                    bf16x8 pf;
+                    bf16x4 o;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pf[e] = f2bf(pv[0][e]);
-                        pf[4 + e] = f2bf(pv[1][e]);
-                    }
-#pragma unroll
-                    for (int ct = 0; ct < D / 16; ++ct) {
-                        const T *vs = Vt + (16 * ct + r) * Cf::TROW + 4 * g;
-                        bf16x8 vf;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            vf[e] = vs[e];
-                            vf[4 + e] = vs[16 + e];
-                        }
-                        acc[qt][ct] = mfma_bf16(vf, pf, acc[qt][ct]);
-                    }
+                    for (int e = 0; e < 4; ++e) o[e] = f2bf(s[e]);
+                    *reinterpret_cast<bf16x4 *>(dst) = o;
                 } else {
-#pragma unroll
-                    for (int ct = 0; ct < D / 16; ++ct) {
-                        const T *vs = Vt + (16 * ct + r) * Cf::TROW + 4 * g;
-#pragma unroll
-                        for (int t = 0; t < 2; ++t)
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) acc[qt][ct] = mfma_f32(vs[16 * t + e], pv[t][e], acc[qt][ct]);
-                    }
+                    *reinterpret_cast<f32x4 *>(dst) = s;
                 }
+            } else {
+                f32x4 z;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) z[e] = s[e] + __shfl_xor(s[e], 1, 64);
+                if (r == 0) *reinterpret_cast<f32x4 *>(slot + Cf::VBYTES + (size_t)(16 * nt + 4 * g) * 4) = z;
             }
         }
+    }
+    if (tid == 0) p.tot[bid] = etot;
+}
 
-        // ---- inter-chunk terms: F_{c-1} and G_{c+1} applied to the decayed queries ---------------------
-        if (ntl > 0 && (has_f || has_g)) {
-#pragma unroll
-            for (int which = 0; which < 2; ++which) {
-                const bool use = which == 0 ? has_f : has_g;
-                if (!use) continue;
-                const T *Ss = which == 0 ? Fs : Gs;
-                const float *Sz = which == 0 ? Fz : Gz;
-                const int pitch = which == 0 ? Cf::SROW : D;
-#pragma unroll
-                for (int qt = 0; qt < Cf::QT; ++qt) {
-                    if (qt >= ntl) break;
-                    // decay from the chunk boundary to the query: exp(A_i - A_{e_{c-1}}) or exp(A_{e_c} - A_i)
-                    float dq = 1.f;
-                    if constexpr (KIND != kMaskLit)
-                        dq = which == 0 ? fast_exp2(Ei[qt] - Ex(cs - 1)) : fast_exp2(Ex(ce) - Ei[qt]);
-                    // the same rounded phi(q) the intra-chunk scores use
-                    float zdot = 0.f;
-                    typename Cf::QFrag qd[Cf::NS];
-                    if constexpr (BF16) {
-#pragma unroll
-                        for (int s = 0; s < Cf::NS; ++s) {
-                            bf16x8 f;
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const float x = (8 * s + e < Cf::CPL) ? (float)qf[qt][s][e] : 0.f;
-                                if (8 * s + e < Cf::CPL) zdot += x * Sz[g * Cf::CPL + 8 * s + e];
-                                f[e] = f2bf(dq * x);
-                            }
-                            qd[s] = f;
-                        }
-                    } else {
-#pragma unroll
-                        for (int s = 0; s < Cf::NS; ++s) {
-                            zdot += qf[qt][s] * Sz[g * Cf::CPL + s];
-                            qd[s] = dq * qf[qt][s];
-                        }
-                    }
-                    den[qt] += dq * zdot;
-#pragma unroll
-                    for (int ct = 0; ct < D / 16; ++ct) {
-                        const T *src = Ss + (16 * ct + r) * pitch + g * Cf::CPL;
-#pragma unroll
-                        for (int s = 0; s < Cf::NS; ++s) {
-                            if constexpr (BF16) {
-                                bf16x8 a;
-#pragma unroll
-                                for (int e = 0; e < 8; ++e) a[e] = (8 * s + e < Cf::CPL) ? src[8 * s + e] : f2bf(0.f);
-                                acc[qt][ct] = mfma_bf16(a, qd[s], acc[qt][ct]);
-                            } else {
-                                acc[qt][ct] = mfma_f32(src[s], qd[s], acc[qt][ct]);
-                            }
-                        }
-                    }
-                }
-            }
-        }
+// ================================ scan kernel =========================================================
+// One thread per 16-byte vector of a slot, sequential over the chunks of its (batch, head): forward
+// states F_c = a_c F_{c-1} + Fl_c for c = 0 .. n-2, backward G_c = a_c G_{c+1} + Gl_c for c = n-1 .. 1,
+// each written over the local state of the same chunk.  Loads run kU chunks ahead.
+constexpr int kScanThreads = 256;
+constexpr int kU = 4;
 
-        // ---- epilogue ----------------------------------------------------------------------------------
+template <int D, bool BF16>
+__host__ __device__ constexpr int scan_vectors() {
+    return (int)(ChunkCfg<D, BF16>::VBYTES / 16) + D / 4;
+}
+
+template <int D, bool BF16>
+__global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(ChunkParams p) {
+    using Cf = ChunkCfg<D, BF16>;
+    using T = typename Cf::T;
+    constexpr int NVV = (int)(Cf::VBYTES / 16);
+    constexpr int NV = scan_vectors<D, BF16>();
+    constexpr int NBLK = (NV + kScanThreads - 1) / kScanThreads;
+    constexpr int VEC = 16 / (int)sizeof(T);
+    const int n = p.n;
+    const int bid = blockIdx.x;
+    const int blk = bid % NBLK, dir = (bid / NBLK) & 1, bh = bid / (2 * NBLK);
+    const int vi = blk * kScanThreads + (int)threadIdx.x;
+    if (vi >= NV) return;   // this kernel has no barriers
+    const bool zpart = vi >= NVV;
+    const size_t off = zpart ? Cf::VBYTES + (size_t)(vi - NVV) * 16 : (size_t)vi * 16;
+    unsigned char *base = (dir == 0 ? p.fs : p.gs) + (size_t)bh * n * Cf::SLOT + off;
+    const float *tot = p.tot + (size_t)bh * n;
+    const int steps = n - 1;
+    auto chunk_of = [&](int k) { return dir == 0 ? k : n - 1 - k; };
+
+    u32x4 buf[kU];
 #pragma unroll
-        for (int qt = 0; qt < Cf::QT; ++qt) {
-            if (qt >= ntl) break;
-            float dsum = den[qt];
-            dsum += __shfl_xor(dsum, 16, 64);
-            dsum += __shfl_xor(dsum, 32, 64);
-            const float div = dsum + p.eps;
-            const int i = cs + (wave + kNW * qt) * 16 + r;
-            if (i <= ce) {
-                const float inv = 1.f / div;
-                const size_t row = base + i;
-                if (p.out_bf16) {
-                    __bf16 *yo = reinterpret_cast<__bf16 *>(p.y) + row * D;
+    for (int u = 0; u < kU; ++u)
+        if (u < steps) buf[u] = ld16(base + (size_t)chunk_of(u) * Cf::SLOT);
+    float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < steps; k0 += kU) {
 #pragma unroll
-                    for (int ct = 0; ct < D / 16; ++ct) {
-                        bf16x4 o;
+        for (int u = 0; u < kU; ++u) {
+            const int k = k0 + u;
+            if (k >= steps) break;
+            const int c = chunk_of(k);
+            const u32x4 x = buf[u];
+            if (k + kU < steps) buf[u] = ld16(base + (size_t)chunk_of(k + kU) * Cf::SLOT);
+            const float a = fast_exp2(tot[c]);
+            u32x4 o;
+            if (zpart || !BF16) {
+                // whole-vector reinterpretation (a bit_cast of one element of a u32x4 is not used:
+                // it has been seen to read element 0 for every index)
+                const f32x4 xf = __builtin_bit_cast(f32x4, x);
+                f32x4 of;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) o[e] = f2bf(acc[qt][ct][e] * inv);
-                        *reinterpret_cast<bf16x4 *>(yo + 16 * ct + 4 * g) = o;
-                    }
-                } else {
-                    float *yo = reinterpret_cast<float *>(p.y) + row * D;
-#pragma unroll
-                    for (int ct = 0; ct < D / 16; ++ct) {
-                        f32x4 o;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) o[e] = acc[qt][ct][e] * inv;
-                        *reinterpret_cast<f32x4 *>(yo + 16 * ct + 4 * g) = o;
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    run[i] = a * run[i] + xf[i];
+                    of[i] = run[i];
                 }
-                if (p.den_out && g == 0) p.den_out[row] = div;
+                o = __builtin_bit_cast(u32x4, of);
+            } else {
+                const bf16x8 xb = __builtin_bit_cast(bf16x8, x);
+                bf16x8 ob;
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    run[i] = a * run[i] + (float)xb[i];
+                    ob[i] = f2bf(run[i]);
+                }
+                o = __builtin_bit_cast(u32x4, ob);
             }
+            st16(base + (size_t)c * Cf::SLOT, o);
         }
     }
 }
 
+// ================================ output kernel =======================================================
+template <int D, int KIND, int NW, int QT, bool BF16>
+__global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
+    using Cf = ChunkCfg<D, BF16>;
+    using T = typename Cf::T;
+    using RT = typename Cf::RT;
+    using QFrag = typename Cf::QFrag;
+    constexpr int NT = NW * 64;
+    constexpr int NDT = Cf::NDT, NQ = Cf::NQ, HW = Cf::HW;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int L = p.L, n = p.n;
+    const int bid = blockIdx.x, bh = bid / n, c = bid % n;
+    const int cs = c * p.C, cn = min(p.C, L - cs);
+    const int rows = cpad(cn);
+    const int cp = cpad(p.C);
+    const int tiles = (cn + 15) / 16;
+
+    T *Ks = reinterpret_cast<T *>(smem);
+    T *Vs = Ks + cp * D;
+    float *E = reinterpret_cast<float *>(Vs + cp * D);
+    double *wsum = reinterpret_cast<double *>(E + cp);
+    const size_t base = (size_t)bh * L;
+    stage_rows<D, T>(Ks, reinterpret_cast<const T *>(p.k) + base * D, cs, rows, L, wave, NW, lane);
+    stage_rows<D, T>(Vs, reinterpret_cast<const T *>(p.v) + base * D, cs, rows, L, wave, NW, lane);
+
+    float lgD = 0.f;
+    if constexpr (KIND == kMaskD) lgD = p.ll[bh % p.H] * kLog2e;
+    if constexpr (KIND == kMaskS) chunk_exponents_s(E, wsum, p.ll + base + cs, cn, rows, tid);
+    auto Ex = [&](int t) -> float {
+        if constexpr (KIND == kMaskLit) return 0.f;
+        else if constexpr (KIND == kMaskD) return (float)(t + 1) * lgD;
+        else return E[t];
+    };
+    const float etot = Ex(cn - 1);
+
+    // ---- queries of this wave's tiles (channels in fragment order), phi, decay exponents ---------
+    QFrag qf[QT][NQ];
+    float Ei[QT], den[QT];
+    f32x4 acc[QT][NDT];
+    const T *qg = reinterpret_cast<const T *>(p.q) + base * D;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const int tl = wave + NW * qt;
+        const int il = 16 * tl + r;
+        const bool ok = tl < tiles && il < cn;
+        const T *src = qg + (size_t)(cs + min(il, cn - 1)) * D + 4 * g;
+        float x[NQ][8];
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+            if constexpr (BF16) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    if (hh < HW) {
+                        const bf16x4 v4 = *reinterpret_cast<const bf16x4 *>(src + 16 * (HW * s + hh));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[s][4 * hh + e] = phi_pre<KIND>((float)v4[e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[s][4 * hh + e] = 0.f;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += x[s][e] * x[s][e];
+            } else {
+                x[s][0] = phi_pre<KIND>((float)src[16 * (s / 4) + (s & 3)]);
+                ss += x[s][0] * x[s][0];
+            }
+        }
+        float sc = ok ? 1.f : 0.f;
+        if constexpr (KIND == kMaskS) {
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            sc *= inv_norm(ss);
+        }
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+            if constexpr (BF16) {
+                bf16x8 f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = f2bf(x[s][e] * sc);
+                qf[qt][s] = f;
+            } else {
+                qf[qt][s] = x[s][0] * sc;
+            }
+        }
+        Ei[qt] = Ex(ok ? il : 0);
+        den[qt] = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) acc[qt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // ---- inter-chunk terms: F_{c-1} on exp(A_i - A_{e_{c-1}}) q_i, G_{c+1} on exp(A_{e_c} - A_i) q_i ----
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        if (which == 0 ? c == 0 : c == n - 1) continue;
+        const unsigned char *slot = which == 0 ? p.fs + (size_t)(bid - 1) * Cf::SLOT
+                                               : p.gs + (size_t)(bid + 1) * Cf::SLOT;
+        const T *sv = reinterpret_cast<const T *>(slot);
+        const float *sz = reinterpret_cast<const float *>(slot + Cf::VBYTES);
+        f32x4 z4[NDT];
+#pragma unroll
+        for (int nt = 0; nt < NDT; ++nt) z4[nt] = *reinterpret_cast<const f32x4 *>(sz + 16 * nt + 4 * g);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            if (wave + NW * qt >= tiles) break;
+            float dq = 1.f;
+            if constexpr (KIND != kMaskLit) dq = which == 0 ? fast_exp2(Ei[qt]) : fast_exp2(etot - Ei[qt]);
+            float zdot = 0.f;
+            QFrag qd[NQ];
+#pragma unroll
+            for (int s = 0; s < NQ; ++s) {
+                if constexpr (BF16) {
+                    bf16x8 f;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const float xv = (float)qf[qt][s][k];
+                        if (k / 4 < HW) zdot += xv * z4[HW * s + k / 4][k & 3];
+                        f[k] = f2bf(dq * xv);
+                    }
+                    qd[s] = f;
+                } else {
+                    zdot += qf[qt][s] * z4[s / 4][s & 3];
+                    qd[s] = dq * qf[qt][s];
+                }
+            }
+            den[qt] += dq * zdot;
+#pragma unroll
+            for (int ct = 0; ct < NDT; ++ct) {
+                if constexpr (BF16) {
+#pragma unroll
+                    for (int s = 0; s < NQ; ++s) {
+                        const T *src = sv + slot_off<D, BF16>(ct, HW * s, lane);
+                        bf16x8 a;
+                        if constexpr (HW == 2) {
+                            a = *reinterpret_cast<const bf16x8 *>(src);
+                        } else {
+                            const bf16x4 h4 = *reinterpret_cast<const bf16x4 *>(src);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                a[e] = h4[e];
+                                a[4 + e] = f2bf(0.f);
+                            }
+                        }
+                        acc[qt][ct] = mfma_bf16(a, qd[s], acc[qt][ct]);
+                    }
+                } else {
+#pragma unroll
+                    for (int nt = 0; nt < NDT; ++nt) {
+                        const f32x4 a4 = *reinterpret_cast<const f32x4 *>(sv + slot_off<D, BF16>(ct, nt, lane));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[qt][ct] = mfma_f32(a4[e], qd[4 * nt + e], acc[qt][ct]);
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- intra-chunk masked attention -----------------------------------------------------------
+    wait_vm_all();
+    __syncthreads();
+    if constexpr (KIND != kMaskD) {
+        phi_rows<D, KIND, T>(Ks, rows, tid, NT);
+        __syncthreads();
+    }
+    for (int h = 0; h < rows / kKB; ++h) {
+        const int j0 = h * kKB;
+        const bool partial = j0 + kKB > cn;
+        if (wave >= tiles) break;
+        bf16x8 vfr[BF16 ? NDT : 1];
+        if constexpr (BF16) {
+#pragma unroll
+            for (int ct = 0; ct < NDT; ++ct) vfr[ct] = tr_frag<D>(Vs, h, ct, r, g);
+        }
+        QFrag kf[2][BF16 ? NQ : 1];
+        if constexpr (BF16) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int s = 0; s < NQ; ++s) {
+                    const int row = j0 + 16 * t + r;
+                    bf16x8 f;
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        if (hh < HW) {
+                            const bf16x4 v4 =
+                                *reinterpret_cast<const bf16x4 *>(Ks + RT::off(row, 16 * (HW * s + hh) + 4 * g));
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) f[4 * hh + e] = v4[e];
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) f[4 * hh + e] = f2bf(0.f);
+                        }
+                    }
+                    kf[t][s] = f;
+                }
+        }
+        float Ej[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ej[t][e] = Ex(j0 + 16 * t + 4 * g + e);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            if (wave + NW * qt >= tiles) break;
+            f32x4 sa[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                sa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < NQ; ++s) {
+                    if constexpr (BF16)
+                        sa[t] = mfma_bf16(kf[t][s], qf[qt][s], sa[t]);
+                    else
+                        sa[t] = mfma_f32(Ks[RT::off(j0 + 16 * t + r, f32_ch(s, g))], qf[qt][s], sa[t]);
+                }
+            }
+            float pv[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float pe = sa[t][e];
+                    if constexpr (KIND != kMaskLit) pe *= fast_exp2(-__builtin_fabsf(Ei[qt] - Ej[t][e]));
+                    if (partial) pe = j0 + 16 * t + 4 * g + e < cn ? pe : 0.f;
+                    den[qt] += pe;
+                    pv[t][e] = pe;
+                }
+            if constexpr (BF16) {
+                bf16x8 pf;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pf[e] = f2bf(pv[0][e]);
+                    pf[4 + e] = f2bf(pv[1][e]);
+                }
+#pragma unroll
+                for (int ct = 0; ct < NDT; ++ct) acc[qt][ct] = mfma_bf16(vfr[ct], pf, acc[qt][ct]);
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < NDT; ++ct)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[qt][ct] =
+                                mfma_f32(Vs[RT::off(j0 + 16 * t + 4 * g + e, 16 * ct + r)], pv[t][e], acc[qt][ct]);
+            }
+        }
+    }
+
+    // ---- epilogue ------------------------------------------------------------------------------
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const int tl = wave + NW * qt;
+        if (tl >= tiles) break;
+        float dsum = den[qt];
+        dsum += __shfl_xor(dsum, 16, 64);
+        dsum += __shfl_xor(dsum, 32, 64);
+        const float div = dsum + p.eps;
+        const int il = 16 * tl + r;
+        if (il < cn) {
+            const float inv = 1.f / div;
+            const size_t row = base + cs + il;
+            if (p.out_bf16) {
+                __bf16 *yo = reinterpret_cast<__bf16 *>(p.y) + row * D;
+#pragma unroll
+                for (int ct = 0; ct < NDT; ++ct) {
+                    bf16x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = f2bf(acc[qt][ct][e] * inv);
+                    *reinterpret_cast<bf16x4 *>(yo + 16 * ct + 4 * g) = o;
+                }
+            } else {
+                float *yo = reinterpret_cast<float *>(p.y) + row * D;
+#pragma unroll
+                for (int ct = 0; ct < NDT; ++ct) {
+                    f32x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = acc[qt][ct][e] * inv;
+                    *reinterpret_cast<f32x4 *>(yo + 16 * ct + 4 * g) = o;
+                }
+            }
+            if (p.den_out && g == 0) p.den_out[row] = div;
+        }
+    }
+}
+
+// ================================ host side ===========================================================
+template <int D, bool BF16>
+size_t chunk_lds(int C, int nw) {
+    const int cp = cpad(C);
+    return 2 * (size_t)cp * D * sizeof(typename ChunkCfg<D, BF16>::T) + (size_t)cp * 4 + (size_t)nw * 8;
+}
+
+template <typename K>
+void allow_lds(K *kernel, size_t lds) {
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+}
+
+template <int D, bool BF16>
+size_t workspace_t(const AttnArgs &a) {
+    const size_t n = (size_t)((a.L + a.C - 1) / a.C);
+    if (n < 2) return 0;   // one chunk: no states to carry
+    const size_t nb = (size_t)a.B * a.H * n;
+    return 2 * nb * ChunkCfg<D, BF16>::SLOT + ((nb * 4 + 15) & ~(size_t)15);
+}
+
 template <int D, int KIND, bool BF16>
 hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
+    using Cf = ChunkCfg<D, BF16>;
     ChunkParams p;
     p.q = a.q;
     p.k = a.k;
@@ -552,17 +697,34 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
     p.H = a.H;
     p.L = a.L;
     p.C = a.C;
+    p.n = (a.L + a.C - 1) / a.C;
     p.y = a.y;
     p.out_bf16 = a.out_bf16 ? 1 : 0;
     p.den_out = a.den_out;
-    const bool in_lds = park_in_lds<D, BF16>(a.L, a.C);
-    p.ws = in_lds ? nullptr : reinterpret_cast<unsigned char *>(a.workspace);
-    size_t lds = lds_fixed_bytes<D, BF16>(a.L);
-    if (in_lds) lds += (size_t)((a.L + a.C - 1) / a.C) * ChunkCfg<D, BF16>::GSLOT;
-    if (lds > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_kernel<D, KIND, BF16>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((chunk_kernel<D, KIND, BF16>), dim3(a.B * a.H), dim3(kNT), lds, stream, p);
+    const size_t nb = (size_t)a.B * a.H * p.n;
+    p.fs = p.gs = nullptr;
+    p.tot = nullptr;
+    if (p.n > 1) {
+        p.fs = reinterpret_cast<unsigned char *>(a.workspace);
+        p.gs = p.fs + nb * Cf::SLOT;
+        p.tot = reinterpret_cast<float *>(p.gs + nb * Cf::SLOT);
+        constexpr int NW1 = state_waves(D);
+        const size_t lds1 = chunk_lds<D, BF16>(a.C, NW1);
+        allow_lds(&chunk_state_kernel<D, KIND, BF16>, lds1);
+        hipLaunchKernelGGL((chunk_state_kernel<D, KIND, BF16>), dim3((unsigned)nb), dim3(NW1 * 64), lds1, stream, p);
+        constexpr int NBLK = (scan_vectors<D, BF16>() + kScanThreads - 1) / kScanThreads;
+        hipLaunchKernelGGL((chunk_scan_kernel<D, BF16>), dim3((unsigned)(a.B * a.H * 2 * NBLK)), dim3(kScanThreads), 0,
+                           stream, p);
+    }
+    // output workgroups: the chunk's C/16 query tiles over 4 waves (C <= 64) or 8 waves (C >= 128)
+    auto out = [&](auto kernel, int nw) {
+        const size_t lds = chunk_lds<D, BF16>(a.C, nw);
+        allow_lds(kernel, lds);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)nb), dim3(nw * 64), lds, stream, p);
+    };
+    if (a.C <= 64) out(&chunk_out_kernel<D, KIND, 4, 1, BF16>, 4);
+    else if (D == 128 || a.C <= 128) out(&chunk_out_kernel<D, KIND, 8, 1, BF16>, 8);
+    else out(&chunk_out_kernel<D, KIND, 8, (D == 128 ? 1 : 2), BF16>, 8);
     return hipGetLastError();
 }
 
@@ -588,10 +750,8 @@ hipError_t dispatch_d(const AttnArgs &a, hipStream_t stream) {
 template <int D, bool BF16>
 Plan plan_t(const AttnArgs &a) {
     Plan p;
-    p.ok = lds_fixed_bytes<D, BF16>(a.L) <= kLdsPerWorkgroup;
-    p.workspace = park_in_lds<D, BF16>(a.L, a.C)
-                      ? 0
-                      : (size_t)a.B * a.H * ((a.L + a.C - 1) / a.C) * ChunkCfg<D, BF16>::GSLOT;
+    p.ok = chunk_lds<D, BF16>(a.C, 8) <= kLdsPerWorkgroup;
+    p.workspace = workspace_t<D, BF16>(a);
     return p;
 }
 
