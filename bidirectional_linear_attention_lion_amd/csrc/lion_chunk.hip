@@ -68,7 +68,9 @@ struct ChunkCfg {
     static constexpr int NQ = BF16 ? NP : D / 4;          // query fragments per tile
     using QFrag = std::conditional_t<BF16, bf16x8, float>;
     static constexpr size_t VBYTES = (size_t)D * D * sizeof(T);
-    static constexpr size_t SLOT = (VBYTES + (size_t)D * 4 + 15) & ~(size_t)15;
+    // bf16 slots are whole KiB so a workgroup can copy one into LDS with 1 KiB direct loads
+    static constexpr size_t SLOT = BF16 ? (VBYTES + (size_t)D * 4 + 1023) & ~(size_t)1023
+                                        : (VBYTES + (size_t)D * 4 + 15) & ~(size_t)15;
 };
 
 // Element offset of lane `lane`'s four values of tile (ct, nt) in a state slot's value part.
@@ -138,6 +140,17 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16 *tile, int h, int ct, int
         f[4 + e] = hi4[e];
     }
     return f;
+}
+
+// LDS of the state and output kernels: keys, values, exponent table, scan scratch, and for the bf16
+// output kernel the two carried states.
+template <int D, bool BF16>
+__host__ __device__ size_t chunk_lds(int C, int nw, bool with_states) {
+    const int cp = cpad(C);
+    size_t b = 2 * (size_t)cp * D * sizeof(typename ChunkCfg<D, BF16>::T) + (size_t)cp * 4 + (size_t)nw * 8;
+    b = (b + 15) & ~(size_t)15;
+    if (BF16 && with_states) b += 2 * ChunkCfg<D, BF16>::SLOT;
+    return b;
 }
 
 // ================================ state kernel ========================================================
@@ -397,9 +410,16 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
     T *Vs = Ks + cp * D;
     float *E = reinterpret_cast<float *>(Vs + cp * D);
     double *wsum = reinterpret_cast<double *>(E + cp);
+    // bf16: the carried states F_{c-1} and G_{c+1} are copied into LDS beside the keys and values
+    unsigned char *Fsm = reinterpret_cast<unsigned char *>(smem) + chunk_lds<D, BF16>(p.C, NW, false);
+    unsigned char *Gsm = Fsm + Cf::SLOT;
     const size_t base = (size_t)bh * L;
     stage_rows<D, T>(Ks, reinterpret_cast<const T *>(p.k) + base * D, cs, rows, L, wave, NW, lane);
     stage_rows<D, T>(Vs, reinterpret_cast<const T *>(p.v) + base * D, cs, rows, L, wave, NW, lane);
+    if constexpr (BF16) {
+        if (c > 0) stage_flat(Fsm, p.fs + (size_t)(bid - 1) * Cf::SLOT, (int)(Cf::SLOT / 1024), wave, NW, lane);
+        if (c < n - 1) stage_flat(Gsm, p.gs + (size_t)(bid + 1) * Cf::SLOT, (int)(Cf::SLOT / 1024), wave, NW, lane);
+    }
 
     float lgD = 0.f;
     if constexpr (KIND == kMaskD) lgD = p.ll[bh % p.H] * kLog2e;
@@ -468,12 +488,16 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
         for (int ct = 0; ct < NDT; ++ct) acc[qt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    wait_vm_all();
+    __syncthreads();
+
     // ---- inter-chunk terms: F_{c-1} on exp(A_i - A_{e_{c-1}}) q_i, G_{c+1} on exp(A_{e_c} - A_i) q_i ----
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
         if (which == 0 ? c == 0 : c == n - 1) continue;
-        const unsigned char *slot = which == 0 ? p.fs + (size_t)(bid - 1) * Cf::SLOT
-                                               : p.gs + (size_t)(bid + 1) * Cf::SLOT;
+        const unsigned char *slot;
+        if constexpr (BF16) slot = which == 0 ? Fsm : Gsm;
+        else slot = which == 0 ? p.fs + (size_t)(bid - 1) * Cf::SLOT : p.gs + (size_t)(bid + 1) * Cf::SLOT;
         const T *sv = reinterpret_cast<const T *>(slot);
         const float *sz = reinterpret_cast<const float *>(slot + Cf::VBYTES);
         f32x4 z4[NDT];
@@ -535,8 +559,6 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
     }
 
     // ---- intra-chunk masked attention -----------------------------------------------------------
-    wait_vm_all();
-    __syncthreads();
     if constexpr (KIND != kMaskD) {
         phi_rows<D, KIND, T>(Ks, rows, tid, NT);
         __syncthreads();
@@ -663,12 +685,379 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
     }
 }
 
-// ================================ host side ===========================================================
-template <int D, bool BF16>
-size_t chunk_lds(int C, int nw) {
-    const int cp = cpad(C);
-    return 2 * (size_t)cp * D * sizeof(typename ChunkCfg<D, BF16>::T) + (size_t)cp * 4 + (size_t)nw * 8;
+// ================================ resident kernel =====================================================
+// Short sequences -- every key and value row of a (batch, head) fits in LDS and there are at most
+// kFuseChunks chunks: one workgroup of 16 waves per (batch, head), one launch, no workspace.  Waves
+// 4c .. 4c+3 fold chunk c into its local states Fl_c and Gl_c, which stay in LDS; then wave w computes
+// query tile w: its chunk's intra-chunk attention plus every other chunk's local state applied to the
+// query with the decay in between,
+//   F_{c-1} q = sum_{c' < c} exp(A_{e_{c-1}} - A_{e_{c'}}) Fl_{c'} q,
+//   G_{c+1} q = sum_{c' > c} exp(A_{e_{c'-1}} - A_{e_c}) Gl_{c'} q,
+// a direct sum over at most three states in place of the carried scan.
+constexpr int kFuseWaves = 16;
+constexpr int kFuseChunks = 4;
+constexpr int kFuseRows = 256;
+
+__host__ __device__ constexpr bool fused_ok(int L, int C, int d, bool bf16) {
+    return bf16 && d <= 64 && C % 64 == 0 && cpad(L) <= kFuseRows && (L + C - 1) / C <= kFuseChunks;
 }
+
+template <int D>
+__host__ __device__ constexpr size_t fused_lds() {
+    return 2 * (size_t)kFuseRows * D * 2 + 2 * kFuseChunks * ChunkCfg<D, true>::SLOT + (size_t)kFuseRows * 4 + 16 * 4 +
+           16 * 8;
+}
+
+// LION-S exponents relative to each chunk's start, E[t] = sum_{u = cs(t)}^{t} log2(lambda_u): one fp64 scan
+// over the sequence (threads 0 .. 255), differenced in fp64 at the chunk starts; positions past L - 1
+// get the last chunk's total.  Needs rows <= 256; all threads call it.
+__device__ void fused_exponents_s(float *E, double *sh, const float *ll, int L, int C, int rows, int tid) {
+    const int lane = tid & 63, wave = tid >> 6;
+    double x = tid < L ? (double)ll[tid] * 1.4426950408889634 : 0.0;
+    if (wave < 4) {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const double y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) sh[wave] = x;
+    }
+    __syncthreads();
+    if (wave < 4)
+        for (int w = 0; w < wave; ++w) x += sh[w];
+    if (tid == 0) sh[4] = 0.0;
+    if (tid < rows && (tid + 1) % C == 0 && (tid + 1) / C < kFuseChunks) sh[4 + (tid + 1) / C] = x;
+    __syncthreads();
+    if (tid < rows) E[tid] = (float)(x - sh[4 + tid / C]);
+    __syncthreads();
+}
+
+template <int D, int KIND>
+__global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParams p) {
+    using Cf = ChunkCfg<D, true>;
+    using T = __bf16;
+    using RT = typename Cf::RT;
+    constexpr int NT = kFuseWaves * 64;
+    constexpr int NDT = Cf::NDT, NCT = Cf::NCT, NQ = Cf::NQ, HW = Cf::HW;
+    constexpr bool kColOwn = NDT == 4;   // the 4 waves of a chunk own one key-channel tile each
+    constexpr int MAXT = (NCT * NDT + 3) / 4;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int L = p.L, C = p.C, n = p.n;
+    const int bh = blockIdx.x;
+    const int rows = cpad(L);
+    const size_t base = (size_t)bh * L;
+
+    // LDS: [K rows][V rows][Fl_0 Gl_0 Fl_1 Gl_1 ...][E][chunk totals][scan scratch]
+    T *Ks = reinterpret_cast<T *>(smem);
+    T *Vs = Ks + kFuseRows * D;
+    unsigned char *sl = reinterpret_cast<unsigned char *>(Vs + kFuseRows * D);
+    float *E = reinterpret_cast<float *>(sl + 2 * kFuseChunks * Cf::SLOT);
+    float *tot = E + kFuseRows;
+    double *sh = reinterpret_cast<double *>(tot + 16);
+    auto fslot = [&](int c) { return sl + (size_t)(2 * c) * Cf::SLOT; };
+    auto gslot = [&](int c) { return sl + (size_t)(2 * c + 1) * Cf::SLOT; };
+
+    stage_rows<D, T>(Ks, reinterpret_cast<const T *>(p.k) + base * D, 0, rows, L, wave, kFuseWaves, lane);
+    stage_rows<D, T>(Vs, reinterpret_cast<const T *>(p.v) + base * D, 0, rows, L, wave, kFuseWaves, lane);
+
+    // this wave's query tile (loaded now, used after the folds)
+    const int ntiles = (L + 15) / 16;
+    const int i = 16 * wave + r;
+    bf16x4 qraw[NQ][2];
+    {
+        const T *src = reinterpret_cast<const T *>(p.q) + (base + min(i, L - 1)) * D + 4 * g;
+#pragma unroll
+        for (int s = 0; s < NQ; ++s)
+#pragma unroll
+            for (int hh = 0; hh < HW; ++hh) qraw[s][hh] = *reinterpret_cast<const bf16x4 *>(src + 16 * (HW * s + hh));
+    }
+
+    float lgD = 0.f;
+    if constexpr (KIND == kMaskD) lgD = p.ll[bh % p.H] * kLog2e;
+    if constexpr (KIND == kMaskS) fused_exponents_s(E, sh, p.ll + base, L, C, rows, tid);
+    // exponent of token t of the chunk starting at cs, relative to the end of the chunk before it
+    auto Ex = [&](int t, int cs) -> float {
+        if constexpr (KIND == kMaskLit) return 0.f;
+        else if constexpr (KIND == kMaskD) return (float)(t - cs + 1) * lgD;
+        else return E[t];
+    };
+    wait_vm_all();
+    __syncthreads();
+    if constexpr (KIND != kMaskD) {
+        phi_rows<D, KIND, T>(Ks, rows, tid, NT);
+        __syncthreads();
+    }
+
+    // ---- fold: waves 4c .. 4c+3 -> Fl_c, Gl_c ---------------------------------------------------
+    if (wave < 4 * n) {
+        const int c = wave >> 2, k = wave & 3;
+        const int cs = c * C, cn = min(C, L - cs);
+        const float etot = Ex(cs + cn - 1, cs);
+        auto tile_of = [&](int u, int &ct, int &nt) -> bool {
+            if constexpr (kColOwn) {
+                ct = u;
+                nt = k;
+                return u < NCT;
+            } else {
+                const int tt = k + 4 * u;
+                ct = tt / NDT;
+                nt = tt % NDT;
+                return tt < NCT * NDT;
+            }
+        };
+        f32x4 sf[MAXT], sg[MAXT];
+#pragma unroll
+        for (int u = 0; u < MAXT; ++u) sf[u] = sg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h = cs / kKB; h < (cs + cpad(cn)) / kKB; ++h) {
+            float wf[2][4], wg[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = h * kKB + 16 * t + 4 * g + e;
+                    const float valid = j < cs + cn ? 1.f : 0.f;
+                    float a = valid, b = valid;
+                    if constexpr (KIND != kMaskLit) {
+                        const float ej = Ex(j, cs);
+                        a *= fast_exp2(fminf(etot - ej, 0.f));
+                        b *= fast_exp2(fminf(ej, 0.f));
+                    }
+                    wf[t][e] = a;
+                    wg[t][e] = b;
+                }
+            bf16x8 kfr{};
+            if constexpr (kColOwn) kfr = tr_frag<D>(Ks, h, k, r, g);
+#pragma unroll
+            for (int u = 0; u < MAXT; ++u) {
+                int ct, nt;
+                if (!tile_of(u, ct, nt)) break;
+                const bf16x8 a = kColOwn ? kfr : tr_frag<D>(Ks, h, nt, r, g);
+                bf16x8 bf, bg;
+                if (ct < NDT) {
+                    const bf16x8 vv = tr_frag<D>(Vs, h, ct, r, g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        bf[e] = f2bf(wf[0][e] * (float)vv[e]);
+                        bf[4 + e] = f2bf(wf[1][e] * (float)vv[4 + e]);
+                        bg[e] = f2bf(wg[0][e] * (float)vv[e]);
+                        bg[4 + e] = f2bf(wg[1][e] * (float)vv[4 + e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const __bf16 fh = f2bf(wf[t][e]), gh = f2bf(wg[t][e]);
+                            const __bf16 flo = f2bf(wf[t][e] - (float)fh), glo = f2bf(wg[t][e] - (float)gh);
+                            bf[4 * t + e] = r == 0 ? fh : (r == 1 ? flo : f2bf(0.f));
+                            bg[4 * t + e] = r == 0 ? gh : (r == 1 ? glo : f2bf(0.f));
+                        }
+                }
+                sf[u] = mfma_bf16(a, bf, sf[u]);
+                if constexpr (KIND != kMaskLit) sg[u] = mfma_bf16(a, bg, sg[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < MAXT; ++u) {
+            int ct, nt;
+            if (!tile_of(u, ct, nt)) break;
+#pragma unroll
+            for (int which = 0; which < (KIND == kMaskLit ? 1 : 2); ++which) {
+                // LIT: the two local states coincide; one copy in the forward slot serves both
+                if (KIND != kMaskLit && (which == 0 ? c == n - 1 : c == 0)) continue;
+                const f32x4 s = which == 0 ? sf[u] : sg[u];
+                unsigned char *slot = which == 0 ? fslot(c) : gslot(c);
+                if (ct < NDT) {
+                    bf16x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = f2bf(s[e]);
+                    *reinterpret_cast<bf16x4 *>(reinterpret_cast<T *>(slot) + slot_off<D, true>(ct, nt, lane)) = o;
+                } else {
+                    f32x4 z;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) z[e] = s[e] + __shfl_xor(s[e], 1, 64);
+                    if (r == 0) *reinterpret_cast<f32x4 *>(slot + Cf::VBYTES + (size_t)(16 * nt + 4 * g) * 4) = z;
+                }
+            }
+        }
+        if (k == 0 && lane == 0) tot[c] = etot;
+    }
+    __syncthreads();
+    if (wave >= ntiles) return;   // no barriers below
+
+    // ---- query tile `wave` of chunk c -----------------------------------------------------------
+    const int c = (16 * wave) / C;
+    const int cs = c * C, cn = min(C, L - cs);
+    const bool ok = i < cs + cn;
+    const float etot = tot[c];
+    bf16x8 qf[NQ];
+    float Ei, den = 0.f;
+    f32x4 acc[NDT];
+    {
+        float x[NQ][8];
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < NQ; ++s)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float xv = hh < HW ? phi_pre<KIND>((float)qraw[s][hh][e]) : 0.f;
+                    x[s][4 * hh + e] = xv;
+                    ss += xv * xv;
+                }
+        float sc = ok ? 1.f : 0.f;
+        if constexpr (KIND == kMaskS) {
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            sc *= inv_norm(ss);
+        }
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+            bf16x8 f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = f2bf(x[s][e] * sc);
+            qf[s] = f;
+        }
+        Ei = Ex(ok ? i : cs, cs);
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // other chunks' local states on the decayed query
+    for (int c2 = 0; c2 < n; ++c2) {
+        if (c2 == c) continue;
+        float ex = c2 < c ? Ei : etot - Ei;
+        for (int c3 = min(c, c2) + 1; c3 < max(c, c2); ++c3) ex += tot[c3];
+        const float dq = KIND == kMaskLit ? 1.f : fast_exp2(ex);
+        const unsigned char *slot = (c2 < c || KIND == kMaskLit) ? fslot(c2) : gslot(c2);
+        const T *sv = reinterpret_cast<const T *>(slot);
+        const float *sz = reinterpret_cast<const float *>(slot + Cf::VBYTES);
+        float zdot = 0.f;
+        bf16x8 qd[NQ];
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+            bf16x8 f;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (hh < HW) z4 = *reinterpret_cast<const f32x4 *>(sz + 16 * (HW * s + hh) + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float xv = (float)qf[s][4 * hh + e];
+                    zdot += xv * z4[e];
+                    f[4 * hh + e] = f2bf(dq * xv);
+                }
+            }
+            qd[s] = KIND == kMaskLit ? qf[s] : f;
+        }
+        den += dq * zdot;
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct)
+#pragma unroll
+            for (int s = 0; s < NQ; ++s) {
+                const T *src = sv + slot_off<D, true>(ct, HW * s, lane);
+                bf16x8 a;
+                if constexpr (HW == 2) {
+                    a = *reinterpret_cast<const bf16x8 *>(src);
+                } else {
+                    const bf16x4 h4 = *reinterpret_cast<const bf16x4 *>(src);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        a[e] = h4[e];
+                        a[4 + e] = f2bf(0.f);
+                    }
+                }
+                acc[ct] = mfma_bf16(a, qd[s], acc[ct]);
+            }
+    }
+
+    // intra-chunk attention over the chunk's keys
+    for (int h = cs / kKB; h < (cs + cpad(cn)) / kKB; ++h) {
+        const int j0 = h * kKB;
+        const bool partial = j0 + kKB > cs + cn;
+        bf16x8 vfr[NDT];
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) vfr[ct] = tr_frag<D>(Vs, h, ct, r, g);
+        bf16x8 kf[2][NQ];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int s = 0; s < NQ; ++s) {
+                const int row = j0 + 16 * t + r;
+                bf16x8 f;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    if (hh < HW) {
+                        const bf16x4 v4 =
+                            *reinterpret_cast<const bf16x4 *>(Ks + RT::off(row, 16 * (HW * s + hh) + 4 * g));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) f[4 * hh + e] = v4[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) f[4 * hh + e] = f2bf(0.f);
+                    }
+                }
+                kf[t][s] = f;
+            }
+        f32x4 sa[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            sa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NQ; ++s) sa[t] = mfma_bf16(kf[t][s], qf[s], sa[t]);
+        }
+        bf16x8 pf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 16 * t + 4 * g + e;
+                float pe = sa[t][e];
+                if constexpr (KIND != kMaskLit) pe *= fast_exp2(-__builtin_fabsf(Ei - Ex(j, cs)));
+                if (partial) pe = j < cs + cn ? pe : 0.f;
+                den += pe;
+                pf[4 * t + e] = f2bf(pe);
+            }
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) acc[ct] = mfma_bf16(vfr[ct], pf, acc[ct]);
+    }
+
+    // epilogue
+    den += __shfl_xor(den, 16, 64);
+    den += __shfl_xor(den, 32, 64);
+    const float div = den + p.eps;
+    if (ok) {
+        const float inv = 1.f / div;
+        const size_t row = base + i;
+        if (p.out_bf16) {
+            __bf16 *yo = reinterpret_cast<__bf16 *>(p.y) + row * D;
+#pragma unroll
+            for (int ct = 0; ct < NDT; ++ct) {
+                bf16x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = f2bf(acc[ct][e] * inv);
+                *reinterpret_cast<bf16x4 *>(yo + 16 * ct + 4 * g) = o;
+            }
+        } else {
+            float *yo = reinterpret_cast<float *>(p.y) + row * D;
+#pragma unroll
+            for (int ct = 0; ct < NDT; ++ct) {
+                f32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = acc[ct][e] * inv;
+                *reinterpret_cast<f32x4 *>(yo + 16 * ct + 4 * g) = o;
+            }
+        }
+        if (p.den_out && g == 0) p.den_out[row] = div;
+    }
+}
+
+// ================================ host side ===========================================================
+
 
 template <typename K>
 void allow_lds(K *kernel, size_t lds) {
@@ -680,7 +1069,7 @@ void allow_lds(K *kernel, size_t lds) {
 template <int D, bool BF16>
 size_t workspace_t(const AttnArgs &a) {
     const size_t n = (size_t)((a.L + a.C - 1) / a.C);
-    if (n < 2) return 0;   // one chunk: no states to carry
+    if (n < 2 || fused_ok(a.L, a.C, D, BF16)) return 0;   // one chunk, or states kept in LDS
     const size_t nb = (size_t)a.B * a.H * n;
     return 2 * nb * ChunkCfg<D, BF16>::SLOT + ((nb * 4 + 15) & ~(size_t)15);
 }
@@ -704,12 +1093,21 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
     const size_t nb = (size_t)a.B * a.H * p.n;
     p.fs = p.gs = nullptr;
     p.tot = nullptr;
+    if constexpr (BF16 && D <= 64) {
+        if (fused_ok(a.L, a.C, D, BF16)) {
+            constexpr size_t lds = fused_lds<D>();
+            allow_lds(&chunk_fused_kernel<D, KIND>, lds);
+            hipLaunchKernelGGL((chunk_fused_kernel<D, KIND>), dim3((unsigned)(a.B * a.H)), dim3(kFuseWaves * 64), lds,
+                               stream, p);
+            return hipGetLastError();
+        }
+    }
     if (p.n > 1) {
         p.fs = reinterpret_cast<unsigned char *>(a.workspace);
         p.gs = p.fs + nb * Cf::SLOT;
         p.tot = reinterpret_cast<float *>(p.gs + nb * Cf::SLOT);
         constexpr int NW1 = state_waves(D);
-        const size_t lds1 = chunk_lds<D, BF16>(a.C, NW1);
+        const size_t lds1 = chunk_lds<D, BF16>(a.C, NW1, false);
         allow_lds(&chunk_state_kernel<D, KIND, BF16>, lds1);
         hipLaunchKernelGGL((chunk_state_kernel<D, KIND, BF16>), dim3((unsigned)nb), dim3(NW1 * 64), lds1, stream, p);
         constexpr int NBLK = (scan_vectors<D, BF16>() + kScanThreads - 1) / kScanThreads;
@@ -718,7 +1116,7 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
     }
     // output workgroups: the chunk's C/16 query tiles over 4 waves (C <= 64) or 8 waves (C >= 128)
     auto out = [&](auto kernel, int nw) {
-        const size_t lds = chunk_lds<D, BF16>(a.C, nw);
+        const size_t lds = chunk_lds<D, BF16>(a.C, nw, true);
         allow_lds(kernel, lds);
         hipLaunchKernelGGL(kernel, dim3((unsigned)nb), dim3(nw * 64), lds, stream, p);
     };
@@ -750,7 +1148,7 @@ hipError_t dispatch_d(const AttnArgs &a, hipStream_t stream) {
 template <int D, bool BF16>
 Plan plan_t(const AttnArgs &a) {
     Plan p;
-    p.ok = chunk_lds<D, BF16>(a.C, 8) <= kLdsPerWorkgroup;
+    p.ok = chunk_lds<D, BF16>(a.C, 8, true) <= kLdsPerWorkgroup;
     p.workspace = workspace_t<D, BF16>(a);
     return p;
 }

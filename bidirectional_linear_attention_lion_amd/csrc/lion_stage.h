@@ -50,6 +50,15 @@ __device__ __forceinline__ void stage_rows(T *tile, const T *src, int row0, int 
     }
 }
 
+// Issue the direct loads of `kib` KiB starting at `src` (16-byte aligned) into LDS at `dst`; waves
+// share the 1 KiB load instructions round-robin.
+__device__ __forceinline__ void stage_flat(void *dst, const void *src, int kib, int wave, int nw, int lane) {
+    for (int i = wave; i < kib; i += nw)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const char *>(src) + (size_t)i * 1024 + lane * 16,
+                                         (__attribute__((address_space(3))) void *)(reinterpret_cast<char *>(dst) + i * 1024),
+                                         16, 0, 0);
+}
+
 // Wait for this wave's outstanding vector-memory loads (which includes its direct LDS loads):
 // s_waitcnt vmcnt(0) in the gfx9 encoding (vmcnt bits 3:0 and 15:14 = 0, expcnt 6:4 and lgkmcnt
 // 11:8 at their maxima, i.e. not waited on).
