@@ -8,16 +8,25 @@
 // with q, k after phi; the diagonal term appears in both recurrences and is counted once.  Only a
 // vector y and a scalar c per token and direction are kept (the pages' O(Ld + L) memory).
 //
-// One workgroup per (batch, head).  Its first half of waves runs the forward recurrence over
-// tokens 0, 1, ..., its second half the backward one over L-1, L-2, ...; both advance one token
-// per step.  During the first ceil(L/2) steps each direction parks its partial (y, c) of the
-// token it visits; after a barrier each direction meets tokens the other one has parked and
-// finishes them.  The parking buffer is LDS when it fits, else a global workspace.
+// Work split: one workgroup per (batch, head, group of CW value columns) -- columns of y never interact,
+// so groups need no communication -- with NR waves per direction.  A wave's lane is a value column c
+// of the group (lane % CW) in one of 64 / CW row slices (lane / CW); the lane holds RW rows of that
+// column of the d x d state in registers (RW = d CW / (64 NR)).  Per token and element the state update
+// and the output dot product are one v_fmac_f32 each: k_i and q_i reach every lane through the DPP
+// row_newbcast modifier (lane i of each 16-lane row broadcast to the row), folded into the
+// instruction.  The decay is taken out of the per-element work by carrying S' = S / Lambda_t, Lambda_t
+// the running product of the decays inside a 16-token block: S'_t = S'_{t-1} + (k_t / Lambda_t) v_t^T
+// and q^T S_t = Lambda_t q^T S'_t; S' is brought back to scale at every block start, and within a block
+// whenever Lambda would fall below 2^-60 (a decay of 0 simply resets the state).  The row-sum state z is
+// kept once per 16-lane row (lane i holding z_i); q.z is a 16-lane DPP sum, taken for the whole block
+// at its end.
 //
-// State layout: direction wave w owns value columns 16w .. 16w+15; lane (r = lane % 16,
-// g = lane / 16) holds S[rows g*D/4 .. g*D/4 + D/4 - 1][column 16w + r] in registers.  q^T S is a
-// per-lane partial dot plus a 4-lane reduction; the row-sum state z is spread one row per lane and
-// q.z is a full-wave reduction.
+// Tokens go in blocks of kT = 16 per direction.  A block's phi(q), phi(k), v, diagonal and scale
+// factors are staged in LDS from rows loaded during the previous block; the recurrences write per-slice
+// partials of y and q.z to LDS; then the partials are reduced: a token the other direction visited in
+// an earlier block is finished with the partial parked then, a token whose other visit comes in a later
+// block is parked (in the caller's workspace), and a token both directions visit within this block is
+// finished directly.  The first visitor removes the diagonal, so it is counted once.
 #include <type_traits>
 
 #include "lion_device.h"
@@ -26,8 +35,7 @@
 namespace lion {
 namespace {
 
-constexpr int kT = 16;                  // tokens staged per step block
-constexpr int kLdsBufMax = 64 * 1024;   // parking buffer kept in LDS up to this many bytes
+constexpr int kT = 16;   // tokens per block and direction
 
 struct RnnParams {
     const void *q, *k, *v;
@@ -37,225 +45,436 @@ struct RnnParams {
     void *y;
     int out_bf16;
     float *den_out;
-    float *ws;   // global parking buffer [B*H][L+1][D+1], or null when it lives in LDS
+    float *park;   // [B*H][groups][L][CW+1]: one direction's partial (y, c) of each token
 };
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+// ---- DPP broadcast fused multiply-adds ---------------------------------------------------------------
+// The DPP source (kb, qb) must not be written by a VALU instruction in the two instructions before a DPP
+// read; each block starts with s_nop 1 since the compiler does not track hazards inside inline asm.
+#define LION_BC_S(i) "v_fmac_f32_dpp %[s" #i "], %[kb], %[vj] row_newbcast:" #i " row_mask:0xf bank_mask:0xf\n\t"
+#define LION_BC_Y(i, a) "v_fmac_f32_dpp %[" a "], %[qb], %[s" #i "] row_newbcast:" #i " row_mask:0xf bank_mask:0xf\n\t"
+
+// S[i] += k_(row base + i) * vj for i < N, k broadcast from lane i of each 16-lane row of kb.
+template <int N>
+__device__ __forceinline__ void dpp_update(float *S, float kb, float vj);
+template <>
+__device__ __forceinline__ void dpp_update<16>(float *S, float kb, float vj) {
+    asm volatile("s_nop 1\n\t" LION_BC_S(0) LION_BC_S(1) LION_BC_S(2) LION_BC_S(3) LION_BC_S(4) LION_BC_S(5)
+                     LION_BC_S(6) LION_BC_S(7) LION_BC_S(8) LION_BC_S(9) LION_BC_S(10) LION_BC_S(11) LION_BC_S(12)
+                         LION_BC_S(13) LION_BC_S(14) LION_BC_S(15)
+                 : [s0] "+v"(S[0]), [s1] "+v"(S[1]), [s2] "+v"(S[2]), [s3] "+v"(S[3]), [s4] "+v"(S[4]),
+                   [s5] "+v"(S[5]), [s6] "+v"(S[6]), [s7] "+v"(S[7]), [s8] "+v"(S[8]), [s9] "+v"(S[9]),
+                   [s10] "+v"(S[10]), [s11] "+v"(S[11]), [s12] "+v"(S[12]), [s13] "+v"(S[13]), [s14] "+v"(S[14]),
+                   [s15] "+v"(S[15])
+                 : [kb] "v"(kb), [vj] "v"(vj));
+}
+template <>
+__device__ __forceinline__ void dpp_update<8>(float *S, float kb, float vj) {
+    asm volatile("s_nop 1\n\t" LION_BC_S(0) LION_BC_S(1) LION_BC_S(2) LION_BC_S(3) LION_BC_S(4) LION_BC_S(5)
+                     LION_BC_S(6) LION_BC_S(7)
+                 : [s0] "+v"(S[0]), [s1] "+v"(S[1]), [s2] "+v"(S[2]), [s3] "+v"(S[3]), [s4] "+v"(S[4]),
+                   [s5] "+v"(S[5]), [s6] "+v"(S[6]), [s7] "+v"(S[7])
+                 : [kb] "v"(kb), [vj] "v"(vj));
+}
+template <>
+__device__ __forceinline__ void dpp_update<4>(float *S, float kb, float vj) {
+    asm volatile("s_nop 1\n\t" LION_BC_S(0) LION_BC_S(1) LION_BC_S(2) LION_BC_S(3)
+                 : [s0] "+v"(S[0]), [s1] "+v"(S[1]), [s2] "+v"(S[2]), [s3] "+v"(S[3])
+                 : [kb] "v"(kb), [vj] "v"(vj));
+}
+template <>
+__device__ __forceinline__ void dpp_update<2>(float *S, float kb, float vj) {
+    asm volatile("s_nop 1\n\t" LION_BC_S(0) LION_BC_S(1)
+                 : [s0] "+v"(S[0]), [s1] "+v"(S[1])
+                 : [kb] "v"(kb), [vj] "v"(vj));
+}
+
+// y0 += q_i S[i] (even i), y1 += q_i S[i] (odd i) for i < N, q broadcast like k above.
+template <int N>
+__device__ __forceinline__ void dpp_dot(float &y0, float &y1, float qb, const float *S);
+template <>
+__device__ __forceinline__ void dpp_dot<16>(float &y0, float &y1, float qb, const float *S) {
+    asm volatile("s_nop 1\n\t" LION_BC_Y(0, "y0") LION_BC_Y(1, "y1") LION_BC_Y(2, "y0") LION_BC_Y(3, "y1")
+                     LION_BC_Y(4, "y0") LION_BC_Y(5, "y1") LION_BC_Y(6, "y0") LION_BC_Y(7, "y1") LION_BC_Y(8, "y0")
+                         LION_BC_Y(9, "y1") LION_BC_Y(10, "y0") LION_BC_Y(11, "y1") LION_BC_Y(12, "y0")
+                             LION_BC_Y(13, "y1") LION_BC_Y(14, "y0") LION_BC_Y(15, "y1")
+                 : [y0] "+v"(y0), [y1] "+v"(y1)
+                 : [qb] "v"(qb), [s0] "v"(S[0]), [s1] "v"(S[1]), [s2] "v"(S[2]), [s3] "v"(S[3]), [s4] "v"(S[4]),
+                   [s5] "v"(S[5]), [s6] "v"(S[6]), [s7] "v"(S[7]), [s8] "v"(S[8]), [s9] "v"(S[9]), [s10] "v"(S[10]),
+                   [s11] "v"(S[11]), [s12] "v"(S[12]), [s13] "v"(S[13]), [s14] "v"(S[14]), [s15] "v"(S[15]));
+}
+template <>
+__device__ __forceinline__ void dpp_dot<8>(float &y0, float &y1, float qb, const float *S) {
+    asm volatile("s_nop 1\n\t" LION_BC_Y(0, "y0") LION_BC_Y(1, "y1") LION_BC_Y(2, "y0") LION_BC_Y(3, "y1")
+                     LION_BC_Y(4, "y0") LION_BC_Y(5, "y1") LION_BC_Y(6, "y0") LION_BC_Y(7, "y1")
+                 : [y0] "+v"(y0), [y1] "+v"(y1)
+                 : [qb] "v"(qb), [s0] "v"(S[0]), [s1] "v"(S[1]), [s2] "v"(S[2]), [s3] "v"(S[3]), [s4] "v"(S[4]),
+                   [s5] "v"(S[5]), [s6] "v"(S[6]), [s7] "v"(S[7]));
+}
+template <>
+__device__ __forceinline__ void dpp_dot<4>(float &y0, float &y1, float qb, const float *S) {
+    asm volatile("s_nop 1\n\t" LION_BC_Y(0, "y0") LION_BC_Y(1, "y1") LION_BC_Y(2, "y0") LION_BC_Y(3, "y1")
+                 : [y0] "+v"(y0), [y1] "+v"(y1)
+                 : [qb] "v"(qb), [s0] "v"(S[0]), [s1] "v"(S[1]), [s2] "v"(S[2]), [s3] "v"(S[3]));
+}
+template <>
+__device__ __forceinline__ void dpp_dot<2>(float &y0, float &y1, float qb, const float *S) {
+    asm volatile("s_nop 1\n\t" LION_BC_Y(0, "y0") LION_BC_Y(1, "y1")
+                 : [y0] "+v"(y0), [y1] "+v"(y1)
+                 : [qb] "v"(qb), [s0] "v"(S[0]), [s1] "v"(S[1]));
+}
+#undef LION_BC_S
+#undef LION_BC_Y
+
+// Sum over the 16 lanes of each row (every lane receives its row's sum).
+__device__ __forceinline__ float row16_sum(float x) {
+    auto dpp = [](float v, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), decltype(ctrl)::value,
+                                                                     0xF, 0xF, true));
+    };
+    x += dpp(x, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+    x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+    x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+    x += dpp(x, std::integral_constant<int, 0x140>{});   // row_mirror
     return x;
 }
 
-__device__ __forceinline__ float load_coherent(const float *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
-template <int D, int KIND, bool BF16, bool LDSBUF>
-__global__ void __launch_bounds__(1024) birnn_kernel(RnnParams p) {
+template <int D, int CW, int NR>
+struct RnnShape {
+    static constexpr int NS = 64 / CW;              // row slices per wave
+    static constexpr int RW = D * CW / (64 * NR);   // state rows per lane
+    static constexpr int RB = RW < 16 ? RW : 16;    // rows per DPP block
+    static constexpr int KV = (RW + 15) / 16;       // DPP blocks per lane
+    static constexpr int NG = D / CW;               // column groups
+    static constexpr int NP = NR * NS;              // partials per column
+};
+
+template <int D, int KIND, int CW, int NR, bool BF16>
+__global__ void __launch_bounds__(2 * NR * 64) birnn_kernel(RnnParams p) {
     using T = std::conditional_t<BF16, __bf16, float>;
-    constexpr int NWD = D / 16;            // waves per direction
-    constexpr int NTD = NWD * 64;          // threads per direction
-    constexpr int RPL = D / 4;             // state rows per lane
-    constexpr int ZPL = (D + 63) / 64;     // z rows per lane
-    constexpr int TPT = D / 4;             // staging threads per token (4 channels each)
-    constexpr int DROW = D + 1;            // parking row: y[0..D-1], c
-    static_assert(NTD / TPT == kT, "one staging pass per block");
+    using Sh = RnnShape<D, CW, NR>;
+    constexpr int NS = Sh::NS, RW = Sh::RW, RB = Sh::RB, KV = Sh::KV, NG = Sh::NG, NP = Sh::NP;
+    constexpr int NTD = NR * 64;              // threads per direction
+    constexpr int TPT = D / 4;                // staging threads per token (4 channels each)
+    constexpr int PAIRS = kT * TPT;
+    constexpr int PPT = (PAIRS + NTD - 1) / NTD;
+    constexpr int QKS = kT * D + 16;          // q/k staging floats (padded: lanes past a slice read on)
+    constexpr int RITER = (kT * CW + NTD - 1) / NTD;
+    constexpr float kRenorm = 8.673617379884035e-19f;   // 2^-60
+    static_assert(RW >= 2 && RW <= 64 && RW % RB == 0, "rows per lane");
 
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
-    const int dir = tid / NTD;             // 0 forward, 1 backward
-    const int dt = tid % NTD;              // thread index within the direction
-    const int lane = tid & 63, dwave = dt >> 6;
-    const int r = lane & 15, g = lane >> 4;
-    const int col = 16 * dwave + r;
+    const int dir = uniform(tid / NTD);       // 0 forward, 1 backward
+    const int dt = tid % NTD;
+    const int lane = tid & 63;
+    const int rg = uniform(dt >> 6);          // wave within the direction
+    const int c = lane % CW, sub = lane / CW;
+    const int slice = rg * NS + sub;
+    const int rb = slice * RW;                // first state row of this lane
     const int L = p.L;
-    const int bh = blockIdx.x;
+    const int bid = blockIdx.x, bh = bid / NG, cg = bid % NG;
+    const int col = cg * CW + c;
     const size_t base = (size_t)bh * L;
 
-    // LDS: per direction [Qs T x D][Ks T x D][Vs T x D][dec T][diag T], then (optionally) parking buffer
-    constexpr int STAGE = kT * (3 * D + 2);
-    float *stage = reinterpret_cast<float *>(smem) + dir * STAGE;
-    float *Qs = stage, *Ks = Qs + kT * D, *Vs = Ks + kT * D, *dec = Vs + kT * D, *sdiag = dec + kT;
-    float *buf = LDSBUF ? reinterpret_cast<float *>(smem) + 2 * STAGE : p.ws + (size_t)bh * (L + 1) * DROW;
+    // LDS: per direction [Qs][Ks][Vs][diag][ksc][ysc][mult], then Yp[2][kT][NP][CW] and Cp[2][kT][NP]
+    constexpr int DIRF = 2 * QKS + kT * D + 4 * kT;
+    float *stg = reinterpret_cast<float *>(smem) + dir * DIRF;
+    float *Qs = stg, *Ks = Qs + QKS, *Vs = Ks + QKS, *sdiag = Vs + kT * D, *ksc = sdiag + kT, *ysc = ksc + kT,
+          *mult = ysc + kT;
+    float *Yp = reinterpret_cast<float *>(smem) + 2 * DIRF;
+    float *Cp = Yp + 2 * kT * NP * CW;
+    float *park = p.park + (size_t)bid * L * (CW + 1);
 
     const T *qg = reinterpret_cast<const T *>(p.q) + base * D;
     const T *kg = reinterpret_cast<const T *>(p.k) + base * D;
     const T *vg = reinterpret_cast<const T *>(p.v) + base * D;
     const float lg_head = (KIND == kMaskD) ? p.ll[bh % p.H] * kLog2e : 0.f;
-
-    float S[RPL];
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) S[i] = 0.f;
-    float z[ZPL];
-#pragma unroll
-    for (int u = 0; u < ZPL; ++u) z[u] = 0.f;
-
-    const int h = (L + 1) / 2;             // steps of the first phase
-    const bool odd = (L & 1) != 0;
-
-    // token visited at step s by this direction
     auto token_at = [&](int s) { return dir == 0 ? s : L - 1 - s; };
+    // decay applied before adding the token visited at step s: lambda_t forward, lambda_{t+1} backward
+    auto decay_at = [&](int s) -> float {
+        if constexpr (KIND == kMaskLit) return 1.f;
+        else if constexpr (KIND == kMaskD) return fast_exp2(lg_head);
+        else {
+            const int td = dir == 0 ? s : L - s;
+            return (s < L && td < L) ? fast_exp2(p.ll[base + td] * kLog2e) : 1.f;
+        }
+    };
+    const int nblk = (L + kT - 1) / kT;
 
-    for (int s0 = 0; s0 < L; s0 += kT) {
-        // ---- stage kT steps of this direction: phi(q), phi(k), v, decay, diagonal -----------------
-        {
-            const int tl = dt / TPT, c4 = (dt % TPT) * 4;
-            const int s = s0 + tl;
-            const bool valid = s < L;
-            const int t = valid ? token_at(s) : 0;
-            float xq[4], xk[4], xv[4];
+    // ---- staging: raw rows loaded during the previous block, then phi, diagonal, scale factors -----
+    using V4 = std::conditional_t<BF16, bf16x4, f32x4>;   // kept in the input type: no wait at load
+    V4 raw[PPT][3];
+    auto prefetch = [&](int b) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xq[e] = valid ? (float)qg[(size_t)t * D + c4 + e] : 0.f;
-                xk[e] = valid ? (float)kg[(size_t)t * D + c4 + e] : 0.f;
-                xv[e] = valid ? (float)vg[(size_t)t * D + c4 + e] : 0.f;
+        for (int u = 0; u < PPT; ++u) {
+            const int pr = dt + NTD * u;
+            const int tl = pr / TPT, c4 = (pr % TPT) * 4;
+            const size_t off = (size_t)token_at(min(b * kT + tl, L - 1)) * D + c4;
+            if (pr < PAIRS) {
+                raw[u][0] = *reinterpret_cast<const V4 *>(qg + off);
+                raw[u][1] = *reinterpret_cast<const V4 *>(kg + off);
+                raw[u][2] = *reinterpret_cast<const V4 *>(vg + off);
             }
-            float sq = 0.f, sk = 0.f;
+        }
+    };
+    auto stage = [&](int b) {
+#pragma unroll
+        for (int u = 0; u < PPT; ++u) {
+            const int pr0 = NTD * u;
+            if (pr0 + dt - lane >= PAIRS) break;   // whole wave past the end (PAIRS is a multiple of 64)
+            const int pr = pr0 + dt;
+            const int tl = pr / TPT, c4 = (pr % TPT) * 4;
+            const int s = b * kT + tl;
+            const bool valid = s < L;
+            float xq[4], xk[4], sq = 0.f, sk = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                xq[e] = phi_pre<KIND>(xq[e]);
-                xk[e] = phi_pre<KIND>(xk[e]);
+                xq[e] = phi_pre<KIND>((float)raw[u][0][e]);
+                xk[e] = phi_pre<KIND>((float)raw[u][1][e]);
                 sq += xq[e] * xq[e];
                 sk += xk[e] * xk[e];
             }
+            float fq = valid ? 1.f : 0.f, fk = fq;
             if constexpr (KIND == kMaskS) {
-                const float fq = inv_norm(group_sum<TPT>(sq)), fk = inv_norm(group_sum<TPT>(sk));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    xq[e] *= fq;
-                    xk[e] *= fk;
-                }
+                fq *= inv_norm(group_sum<TPT>(sq));
+                fk *= inv_norm(group_sum<TPT>(sk));
             }
             float dg = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dg += xq[e] * xk[e];
-            dg = group_sum<TPT>(dg);
-#pragma unroll
             for (int e = 0; e < 4; ++e) {
-                Qs[tl * D + c4 + e] = valid ? xq[e] : 0.f;
-                Ks[tl * D + c4 + e] = valid ? xk[e] : 0.f;
-                Vs[tl * D + c4 + e] = xv[e];
+                xq[e] *= fq;
+                xk[e] *= fk;
+                Qs[tl * D + c4 + e] = xq[e];
+                Ks[tl * D + c4 + e] = xk[e];
+                Vs[tl * D + c4 + e] = (float)raw[u][2][e];
+                dg += xq[e] * xk[e];
             }
-            if (dt % TPT == 0) {
-                sdiag[tl] = valid ? dg : 0.f;
-                // decay applied before adding token t: lambda_t forward, lambda_{t+1} backward
-                float dcy = 1.f;
-                if constexpr (KIND == kMaskD) dcy = fast_exp2(lg_head);
-                if constexpr (KIND == kMaskS) {
-                    const int td = dir == 0 ? t : t + 1;
-                    dcy = (valid && td < L) ? fast_exp2(p.ll[base + td] * kLog2e) : 1.f;
+            dg = group_sum<TPT>(dg);
+            if (c4 == 0) {
+                sdiag[tl] = dg;
+                if constexpr (KIND != kMaskLit) {
+                    // replay the block's scale sequence up to this token (every leader derives the same)
+                    float lam = 1.f, mu = 1.f;
+                    for (int u2 = 0; u2 <= tl; ++u2) {
+                        const float l2 = lam * decay_at(b * kT + u2);
+                        if (l2 < kRenorm) {
+                            mu = l2;
+                            lam = 1.f;
+                        } else {
+                            mu = 1.f;
+                            lam = l2;
+                        }
+                    }
+                    ksc[tl] = 1.f / lam;
+                    ysc[tl] = lam;
+                    mult[tl] = mu;
                 }
-                dec[tl] = dcy;
             }
         }
-        __syncthreads();
+    };
 
-        // ---- advance the recurrence kT steps -------------------------------------------------------
-        const int nsteps = min(kT, L - s0);
-        for (int tl = 0; tl < nsteps; ++tl) {
-            const int s = s0 + tl;
-            if (s == h) {
-                // phase change: everything parked in the first phase is visible from here on
-                if constexpr (!LDSBUF) __threadfence();
-                __syncthreads();
-            }
-            const int t = token_at(s);
-            const float dcy = dec[tl];
-            const float vc = Vs[tl * D + col];
-            const float *qr = Qs + tl * D + g * RPL;
-            const float *kr = Ks + tl * D + g * RPL;
-            float ypart = 0.f;
+    // ---- state: S'[i] = rows rb + i of column col; z' per 16-lane row (lane i%16 of block m: row 16m+i) --
+    float S[RW];
 #pragma unroll
-            for (int i = 0; i < RPL; ++i) {
-                S[i] = __builtin_fmaf(dcy, S[i], kr[i] * vc);
-                ypart = __builtin_fmaf(qr[i], S[i], ypart);
-            }
-            ypart += __shfl_xor(ypart, 16, 64);
-            ypart += __shfl_xor(ypart, 32, 64);
-            float cpart = 0.f;
+    for (int i = 0; i < RW; ++i) S[i] = 0.f;
+    float z[KV], zmask[KV];
 #pragma unroll
-            for (int u = 0; u < ZPL; ++u) {
-                const int zr = lane + 64 * u;
-                if (zr < D) {
-                    z[u] = __builtin_fmaf(dcy, z[u], Ks[tl * D + zr]);
-                    cpart = __builtin_fmaf(Qs[tl * D + zr], z[u], cpart);
-                }
-            }
-            const float cden = wave_sum(cpart);
-
-            if (s < h) {
-                // park this direction's partial; the parking side removes the diagonal, except the
-                // backward visit of the middle token of an odd L, which goes to the extra row L
-                const bool middle_b = odd && dir == 1 && s == h - 1;
-                const float dg = middle_b ? 0.f : sdiag[tl];
-                float *row = buf + (size_t)(middle_b ? L : t) * DROW;
-                if (g == 0) row[col] = ypart - dg * vc;
-                if (dwave == 0 && lane == 0) row[D] = cden - dg;
-            } else {
-                const float *row = buf + (size_t)t * DROW;
-                float yo, co;
-                if constexpr (LDSBUF) {
-                    yo = row[col];
-                    co = row[D];
-                } else {
-                    yo = load_coherent(row + col);
-                    co = load_coherent(row + D);
-                }
-                const float div = cden + co + p.eps;
-                const float out = (ypart + yo) / div;
-                if (g == 0) {
-                    if (p.out_bf16)
-                        reinterpret_cast<__bf16 *>(p.y)[(base + t) * D + col] = f2bf(out);
-                    else
-                        reinterpret_cast<float *>(p.y)[(base + t) * D + col] = out;
-                }
-                if (p.den_out && dwave == 0 && lane == 0) p.den_out[base + t] = div;
-            }
-        }
-        __syncthreads();
+    for (int m = 0; m < KV; ++m) {
+        z[m] = 0.f;
+        zmask[m] = 16 * m + (lane & 15) < RW ? 1.f : 0.f;
     }
+    float lam_end = 1.f;   // scale of S' at the end of the previous block
 
-    // ---- middle token of an odd L: both partials were parked in the first phase --------------------
-    if (odd) {
-        if (h >= L) {  // L == 1: the phase change above never ran
-            if constexpr (!LDSBUF) __threadfence();
-            __syncthreads();
+    prefetch(0);
+    stage(0);
+    __syncthreads();
+
+    for (int b = 0; b < nblk; ++b) {
+        const int s0 = b * kT;
+        const int nsteps = min(kT, L - s0);
+        // the next block's rows load while this block's recurrence runs (staged after the reduction).
+        // The previous reduction's stores are drained first: with stores still counted alongside the
+        // loads, the compiler would otherwise wait for the loads too before reusing a store's registers.
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        if (b + 1 < nblk) prefetch(b + 1);
+
+        // ---- recurrence over the block's tokens ------------------------------------------------------
+        if constexpr (KIND != kMaskLit) {
+#pragma unroll
+            for (int i = 0; i < RW; ++i) S[i] *= lam_end;
+#pragma unroll
+            for (int m = 0; m < KV; ++m) z[m] *= lam_end;
         }
-        if (dir == 0) {
-            const int m = h - 1;
-            const float *rf = buf + (size_t)m * DROW;
-            const float *rb = buf + (size_t)L * DROW;
-            float yf, yb, cf, cb;
-            if constexpr (LDSBUF) {
-                yf = rf[col]; yb = rb[col]; cf = rf[D]; cb = rb[D];
+        // per-token scalars of the block, one register each (lane t holds token t's value)
+        const float kscv = KIND != kMaskLit ? ksc[lane & 15] : 1.f;
+        const float yscv = KIND != kMaskLit ? ysc[lane & 15] : 1.f;
+        const float multv = KIND != kMaskLit ? mult[lane & 15] : 1.f;
+        const float diagv = sdiag[lane & 15];
+        auto lane_val = [](float v, int i) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i));
+        };
+        // this lane's k, q (rows rb + 16m + lane % 16) and v of token tl; loaded one token ahead
+        struct Tok {
+            float kb[KV], qb[KV], vj;
+        };
+        auto load_tok = [&](int tl) {
+            Tok x;
+            const float *qrow = Qs + tl * D + rb + (lane & 15);
+            const float *krow = Ks + tl * D + rb + (lane & 15);
+#pragma unroll
+            for (int m = 0; m < KV; ++m) {
+                x.kb[m] = krow[16 * m];
+                x.qb[m] = qrow[16 * m];
+            }
+            x.vj = Vs[tl * D + col];
+            return x;
+        };
+        float cpv[kT];
+        Tok cur = load_tok(0);
+#pragma unroll
+        for (int tl = 0; tl < kT; ++tl) {
+            cpv[tl] = 0.f;
+            if (tl >= nsteps) continue;
+            // (unconditional: the staging buffer always holds kT rows; rows past the block are unused)
+            Tok nxt;
+            if (tl + 1 < kT) nxt = load_tok(tl + 1);
+            float ks = 1.f, ys = 1.f;
+            if constexpr (KIND != kMaskLit) {
+                ks = lane_val(kscv, tl);
+                ys = lane_val(yscv, tl);
+                const float mu = lane_val(multv, tl);
+                if (mu != 1.f) {
+#pragma unroll
+                    for (int i = 0; i < RW; ++i) S[i] *= mu;
+#pragma unroll
+                    for (int m = 0; m < KV; ++m) z[m] *= mu;
+                }
+                if (tl == nsteps - 1) lam_end = ys;
+            }
+            float y0 = 0.f, y1 = 0.f, cp = 0.f;
+#pragma unroll
+            for (int m = 0; m < KV; ++m) {
+                const float kb = cur.kb[m] * ks, qb = cur.qb[m];
+                dpp_update<RB>(S + RB * m, kb, cur.vj);
+                dpp_dot<RB>(y0, y1, qb, S + RB * m);
+                z[m] += kb;
+                cp += zmask[m] * qb * z[m];
+            }
+            cpv[tl] = cp;
+            float y = (y0 + y1) * ys;
+            const int s = s0 + tl, sp = L - 1 - s;
+            if (slice == 0 && (s < sp || (s == sp && dir == 1))) y -= lane_val(diagv, tl) * cur.vj;   // first visitor
+            Yp[((dir * kT + tl) * NP + slice) * CW + c] = y;
+            if (tl + 1 < kT) cur = nxt;
+        }
+        // q.z partials of the block: 16 independent row sums, written by the first lane of each slice
+#pragma unroll
+        for (int tl = 0; tl < kT; ++tl) cpv[tl] = row16_sum(cpv[tl]);
+#pragma unroll
+        for (int tl = 0; tl < kT; ++tl) {
+            if (tl >= nsteps) break;
+            float cp = cpv[tl];
+            if constexpr (KIND != kMaskLit) cp *= lane_val(yscv, tl);
+            const int s = s0 + tl, sp = L - 1 - s;
+            if (slice == 0 && (s < sp || (s == sp && dir == 1))) cp -= lane_val(diagv, tl);
+            if (c == 0) Cp[(dir * kT + tl) * NP + slice] = cp;
+        }
+        __syncthreads();
+
+        // ---- reduce the partials: park, finish with a parked partial, or finish both directions ------
+        // (the parked partials this block needs are loaded first, all at once)
+        float pky[RITER], pkc[RITER];
+#pragma unroll
+        for (int it = 0; it < RITER; ++it) {
+            const int idx = dt + NTD * it;
+            pky[it] = pkc[it] = 0.f;
+            if (idx < nsteps * CW) {
+                const int tl = idx / CW, c2 = idx % CW;
+                const int s = s0 + tl;
+                if (L - 1 - s < s0) {
+                    const size_t row = (size_t)token_at(s) * (CW + 1);
+                    pky[it] = park[row + c2];
+                    pkc[it] = park[row + CW];
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < RITER; ++it) {
+            const int idx = dt + NTD * it;
+            if (idx >= nsteps * CW) break;
+            const int tl = idx / CW, c2 = idx % CW;
+            const int s = s0 + tl, sp = L - 1 - s;
+            const int t = token_at(s);
+            float y = 0.f, cs = 0.f;
+#pragma unroll
+            for (int g = 0; g < NP; ++g) {
+                y += Yp[((dir * kT + tl) * NP + g) * CW + c2];
+                cs += Cp[(dir * kT + tl) * NP + g];
+            }
+            float yo, co;
+            if (sp >= s0 + nsteps) {
+                park[(size_t)t * (CW + 1) + c2] = y;
+                if (c2 == 0) park[(size_t)t * (CW + 1) + CW] = cs;
+                continue;
+            } else if (sp < s0) {
+                yo = pky[it];
+                co = pkc[it];
             } else {
-                yf = load_coherent(rf + col); yb = load_coherent(rb + col);
-                cf = load_coherent(rf + D); cb = load_coherent(rb + D);
+                if (dir == 1) continue;
+                const int tp = sp - s0;
+                yo = 0.f;
+                co = 0.f;
+#pragma unroll
+                for (int g = 0; g < NP; ++g) {
+                    yo += Yp[((kT + tp) * NP + g) * CW + c2];
+                    co += Cp[(kT + tp) * NP + g];
+                }
             }
-            const float div = cf + cb + p.eps;
-            const float out = (yf + yb) / div;
-            if (g == 0) {
-                if (p.out_bf16)
-                    reinterpret_cast<__bf16 *>(p.y)[(base + m) * D + col] = f2bf(out);
-                else
-                    reinterpret_cast<float *>(p.y)[(base + m) * D + col] = out;
-            }
-            if (p.den_out && dwave == 0 && lane == 0) p.den_out[base + m] = div;
+            const float div = cs + co + p.eps;
+            const float out = (y + yo) / div;
+            const size_t o = (base + t) * D + cg * CW + c2;
+            if (p.out_bf16)
+                reinterpret_cast<__bf16 *>(p.y)[o] = f2bf(out);
+            else
+                reinterpret_cast<float *>(p.y)[o] = out;
+            if (p.den_out && cg == 0 && c2 == 0) p.den_out[base + t] = div;
         }
+        if (b + 1 < nblk) stage(b + 1);
+        __syncthreads();
     }
 }
+
+template <int D, int CW, int NR>
+constexpr size_t rnn_lds() {
+    using Sh = RnnShape<D, CW, NR>;
+    const size_t dirf = 2 * ((size_t)kT * D + 16) + (size_t)kT * D + 4 * kT;
+    return (2 * dirf + 2 * (size_t)kT * Sh::NP * CW + 2 * (size_t)kT * Sh::NP) * 4;
+}
+
+// Work splits (column group width, waves per direction) per head dimension, from the fewest waves
+// (least per-token overhead) to the most; the first giving at least 1.5 waves per SIMD is used (measured
+// on LION-D, d = 64: B64 H12 L197 runs best on 64 x 2, B8 H12 L4097 on 32 x 4).
+struct RnnSplit {
+    int cw, nr;
+};
+constexpr RnnSplit kSplit16[] = {{16, 1}, {16, 2}};
+constexpr RnnSplit kSplit32[] = {{32, 2}, {32, 4}, {16, 4}};
+constexpr RnnSplit kSplit64[] = {{64, 2}, {64, 4}, {32, 4}, {16, 4}};
+constexpr RnnSplit kSplit128[] = {{64, 4}, {32, 4}, {16, 4}};
 
 template <int D>
-size_t park_bytes(int L) {
-    return (size_t)(L + 1) * (D + 1) * 4;
+int rnn_split(int B, int H) {
+    const RnnSplit *sp = D == 16 ? kSplit16 : D == 32 ? kSplit32 : D == 64 ? kSplit64 : kSplit128;
+    const int n = D == 16 ? 2 : D == 32 ? 3 : D == 64 ? 4 : 3;
+    for (int i = 0; i < n; ++i)
+        if ((long)B * H * (D / sp[i].cw) * 2 * sp[i].nr >= 1536) return i;
+    return n - 1;
 }
 
-size_t park_bytes_rt(int L, int d) { return (size_t)(L + 1) * (d + 1) * 4; }
-
-bool park_in_lds(int L, int d) { return park_bytes_rt(L, d) <= (size_t)kLdsBufMax; }
-
-template <int D, int KIND, bool BF16>
-hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
+template <int D, int KIND, int CW, int NR, bool BF16>
+hipError_t launch_split(const AttnArgs &a, hipStream_t stream) {
     RnnParams p;
     p.q = a.q;
     p.k = a.k;
@@ -267,20 +486,35 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
     p.y = a.y;
     p.out_bf16 = a.out_bf16 ? 1 : 0;
     p.den_out = a.den_out;
-    p.ws = reinterpret_cast<float *>(a.workspace);
-    const int nt = 2 * (D / 16) * 64;
-    size_t lds = (size_t)2 * kT * (3 * D + 2) * 4;
-    const int grid = a.B * a.H;
-    if (park_in_lds(a.L, D)) {
-        lds += park_bytes<D>(a.L);
-        if (lds > 64 * 1024)
-            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&birnn_kernel<D, KIND, BF16, true>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL((birnn_kernel<D, KIND, BF16, true>), dim3(grid), dim3(nt), lds, stream, p);
-    } else {
-        hipLaunchKernelGGL((birnn_kernel<D, KIND, BF16, false>), dim3(grid), dim3(nt), lds, stream, p);
-    }
+    p.park = reinterpret_cast<float *>(a.workspace);
+    constexpr size_t lds = rnn_lds<D, CW, NR>();
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&birnn_kernel<D, KIND, CW, NR, BF16>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL((birnn_kernel<D, KIND, CW, NR, BF16>), dim3(a.B * a.H * (D / CW)), dim3(2 * NR * 64), lds,
+                       stream, p);
     return hipGetLastError();
+}
+
+template <int D, int KIND, bool BF16>
+hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
+    const int i = rnn_split<D>(a.B, a.H);
+    if constexpr (D == 16) {
+        return i == 0 ? launch_split<16, KIND, 16, 1, BF16>(a, stream) : launch_split<16, KIND, 16, 2, BF16>(a, stream);
+    } else if constexpr (D == 32) {
+        if (i == 0) return launch_split<32, KIND, 32, 2, BF16>(a, stream);
+        if (i == 1) return launch_split<32, KIND, 32, 4, BF16>(a, stream);
+        return launch_split<32, KIND, 16, 4, BF16>(a, stream);
+    } else if constexpr (D == 64) {
+        if (i == 0) return launch_split<64, KIND, 64, 2, BF16>(a, stream);
+        if (i == 1) return launch_split<64, KIND, 64, 4, BF16>(a, stream);
+        if (i == 2) return launch_split<64, KIND, 32, 4, BF16>(a, stream);
+        return launch_split<64, KIND, 16, 4, BF16>(a, stream);
+    } else {
+        if (i == 0) return launch_split<128, KIND, 64, 4, BF16>(a, stream);
+        if (i == 1) return launch_split<128, KIND, 32, 4, BF16>(a, stream);
+        return launch_split<128, KIND, 16, 4, BF16>(a, stream);
+    }
 }
 
 template <int D, bool BF16>
@@ -302,12 +536,23 @@ hipError_t dispatch_d(const AttnArgs &a, hipStream_t stream) {
     }
 }
 
+template <int D>
+size_t workspace_t(const AttnArgs &a) {
+    const RnnSplit sp = (D == 16 ? kSplit16 : D == 32 ? kSplit32 : D == 64 ? kSplit64 : kSplit128)[rnn_split<D>(a.B, a.H)];
+    return (size_t)a.B * a.H * (D / sp.cw) * a.L * (sp.cw + 1) * 4;
+}
+
 }  // namespace
 
 Plan plan_birnn(const AttnArgs &a) {
     Plan p;
-    p.ok = true;   // staging is at most 2 * 16 * (3 * 128 + 2) * 4 bytes; parking beyond 64 KiB goes to HBM
-    p.workspace = park_in_lds(a.L, a.d) ? 0 : (size_t)a.B * a.H * park_bytes_rt(a.L, a.d);
+    p.ok = rnn_lds<128, 64, 4>() <= kLdsPerWorkgroup;
+    switch (a.d) {
+    case 16: p.workspace = workspace_t<16>(a); break;
+    case 32: p.workspace = workspace_t<32>(a); break;
+    case 64: p.workspace = workspace_t<64>(a); break;
+    default: p.workspace = workspace_t<128>(a); break;
+    }
     return p;
 }
 
