@@ -3,9 +3,11 @@
 // Y = SCALE(phi(Q) phi(K)^T (.) M) V, the form LION trains with ("LION: A bidirectional framework
 // that trains like a Transformer and infers like an RNN", reply "Concern 1", Theorem 3.3 Eq. 25).
 // The L x L score matrix is never materialised.  A workgroup (4 or 8 waves) owns a run of 16-row
-// query tiles of one (batch, head); each wave owns up to QT consecutive tiles.  Keys stream through
-// LDS in super-blocks of 64 (phi(K) row-major, V transposed), double-buffered: the global loads of
-// super-block s+1 are in flight while the waves compute on super-block s.  Per 32-key sub-block and
+// query tiles of one (batch, head); each wave owns up to QT consecutive tiles.  Keys and values stream
+// through LDS as row-major stages loaded straight from global memory (the whole sequence as one stage
+// when it fits, else double-buffered stages whose loads are in flight while the waves compute on the
+// previous one); phi is applied to the staged keys in place, and V^T fragments are read from the
+// row-major value rows with ds_read_b64_tr_b16.  Per 32-key sub-block and
 // query tile a wave forms S^T = phi(K) phi(Q)^T on matrix cores, applies the mask in registers,
 // accumulates fp32 row sums, and feeds the masked scores back as the B operand of O^T = V^T P^T
 // (the D layout of the first product is the B layout of the second, so P never leaves registers).
