@@ -693,7 +693,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
 // query with the decay in between,
 //   F_{c-1} q = sum_{c' < c} exp(A_{e_{c-1}} - A_{e_{c'}}) Fl_{c'} q,
 //   G_{c+1} q = sum_{c' > c} exp(A_{e_{c'-1}} - A_{e_c}) Gl_{c'} q,
-// a direct sum over at most three states in place of the carried scan.
+// a direct sum over at most three states in place of the carried scan.  Keys pass through registers
+// on their way into LDS: phi is applied there and rows past L are zeroed, so padded keys add nothing to
+// any state, score or row sum and no later step masks them.
 constexpr int kFuseWaves = 16;
 constexpr int kFuseChunks = 4;
 constexpr int kFuseRows = 256;
@@ -702,9 +704,35 @@ __host__ __device__ constexpr bool fused_ok(int L, int C, int d, bool bf16) {
     return bf16 && d <= 64 && C % 64 == 0 && cpad(L) <= kFuseRows && (L + C - 1) / C <= kFuseChunks;
 }
 
+// Contraction fragments over the key channels: fragment s of lane (r, g) holds the eight consecutive
+// channels 32 s + 8 g .. 32 s + 8 g + 7 (d = 16: lanes g >= 2 hold zeros), so a query or key fragment
+// is one 16-byte read.  A state slot holds, per 16-wide value tile ct and fragment s, the A operand
+// state[16 ct + r][channels of (s, g)], followed by the row sums as a two-row A-operand tile (row 0
+// their bf16 high part, row 1 the bf16 rounding of the remainder).
+template <int D>
+struct Fuse {
+    static constexpr int NDT = D / 16;
+    static constexpr int NF = (D + 31) / 32;
+    static constexpr int VB = NDT * NF * 1024;
+    static constexpr int SLOT = VB + NF * 128;
+    // element offsets: fragment s of value tile ct as read by `lane`
+    __device__ static __forceinline__ int rd(int ct, int s, int lane) { return ((ct * NF + s) * 64 + lane) * 8; }
+    // where lane (r, g) of a fold tile (ct, nt), holding channels 16 nt + 4 g + e, writes its four values
+    __device__ static __forceinline__ int wr(int ct, int nt, int r, int g) {
+        return ((ct * NF + nt / 2) * 64 + (2 * (nt % 2) + g / 2) * 16 + r) * 8 + 4 * (g % 2);
+    }
+    // row-sum tile: row rr (0 or 1) of fragment s as read by group g, and where fold lane (rr, g) of tile nt writes
+    __device__ static __forceinline__ int zrd(int s, int rr, int g) { return ((s * 2 + rr) * 4 + g) * 8; }
+    __device__ static __forceinline__ int zwr(int nt, int rr, int g) {
+        return (((nt / 2) * 2 + rr) * 4 + 2 * (nt % 2) + g / 2) * 8 + 4 * (g % 2);
+    }
+    // whether group g's channels of a fragment exist (only d = 16 has empty groups)
+    __device__ static __forceinline__ bool has_ch(int g) { return 8 * g < D || D >= 32; }
+};
+
 template <int D>
 __host__ __device__ constexpr size_t fused_lds() {
-    return 2 * (size_t)kFuseRows * D * 2 + 2 * kFuseChunks * ChunkCfg<D, true>::SLOT + (size_t)kFuseRows * 4 + 16 * 4 +
+    return 2 * (size_t)kFuseRows * D * 2 + 2 * kFuseChunks * (size_t)Fuse<D>::SLOT + (size_t)kFuseRows * 4 + 16 * 4 +
            16 * 8;
 }
 
@@ -734,11 +762,11 @@ __device__ void fused_exponents_s(float *E, double *sh, const float *ll, int L, 
 
 template <int D, int KIND>
 __global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParams p) {
-    using Cf = ChunkCfg<D, true>;
+    using F = Fuse<D>;
     using T = __bf16;
-    using RT = typename Cf::RT;
+    using RT = RowTile<D, T>;
     constexpr int NT = kFuseWaves * 64;
-    constexpr int NDT = Cf::NDT, NCT = Cf::NCT, NQ = Cf::NQ, HW = Cf::HW;
+    constexpr int NDT = F::NDT, NCT = NDT + 1, NF = F::NF;
     constexpr bool kColOwn = NDT == 4;   // the 4 waves of a chunk own one key-channel tile each
     constexpr int MAXT = (NCT * NDT + 3) / 4;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -754,25 +782,32 @@ __global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParam
     T *Ks = reinterpret_cast<T *>(smem);
     T *Vs = Ks + kFuseRows * D;
     unsigned char *sl = reinterpret_cast<unsigned char *>(Vs + kFuseRows * D);
-    float *E = reinterpret_cast<float *>(sl + 2 * kFuseChunks * Cf::SLOT);
+    float *E = reinterpret_cast<float *>(sl + 2 * kFuseChunks * F::SLOT);
     float *tot = E + kFuseRows;
     double *sh = reinterpret_cast<double *>(tot + 16);
-    auto fslot = [&](int c) { return sl + (size_t)(2 * c) * Cf::SLOT; };
-    auto gslot = [&](int c) { return sl + (size_t)(2 * c + 1) * Cf::SLOT; };
+    auto fslot = [&](int c) { return sl + (size_t)(2 * c) * F::SLOT; };
+    auto gslot = [&](int c) { return sl + (size_t)(2 * c + 1) * F::SLOT; };
 
-    stage_rows<D, T>(Ks, reinterpret_cast<const T *>(p.k) + base * D, 0, rows, L, wave, kFuseWaves, lane);
+    // values straight to LDS, keys into registers
     stage_rows<D, T>(Vs, reinterpret_cast<const T *>(p.v) + base * D, 0, rows, L, wave, kFuseWaves, lane);
-
-    // this wave's query tile (loaded now, used after the folds)
+    constexpr int KPER = (kFuseRows * RT::CPK + NT - 1) / NT;   // 16-byte key chunks per thread
+    u32x4 kx[KPER];
+    {
+        const T *kg = reinterpret_cast<const T *>(p.k) + base * D;
+#pragma unroll
+        for (int u = 0; u < KPER; ++u) {
+            const int c16 = min(tid + u * NT, rows * RT::CPK - 1);
+            kx[u] = ld16(kg + (size_t)min(c16 / RT::CPK, L - 1) * D + (c16 % RT::CPK) * RT::VEC);
+        }
+    }
+    // this wave's query tile: row 16 wave + r, fragment s = channels 32 s + 8 g .. + 7
     const int ntiles = (L + 15) / 16;
     const int i = 16 * wave + r;
-    bf16x4 qraw[NQ][2];
+    u32x4 qraw[NF];
     {
-        const T *src = reinterpret_cast<const T *>(p.q) + (base + min(i, L - 1)) * D + 4 * g;
+        const T *src = reinterpret_cast<const T *>(p.q) + (base + min(i, L - 1)) * D;
 #pragma unroll
-        for (int s = 0; s < NQ; ++s)
-#pragma unroll
-            for (int hh = 0; hh < HW; ++hh) qraw[s][hh] = *reinterpret_cast<const bf16x4 *>(src + 16 * (HW * s + hh));
+        for (int s = 0; s < NF; ++s) qraw[s] = ld16(src + min(32 * s + 8 * g, D - 8));
     }
 
     float lgD = 0.f;
@@ -785,67 +820,86 @@ __global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParam
         else return E[t];
     };
     wait_vm_all();
-    __syncthreads();
-    if constexpr (KIND != kMaskD) {
-        phi_rows<D, KIND, T>(Ks, rows, tid, NT);
-        __syncthreads();
+    // phi on the keys (rows past L written as zeros); a row's chunks sit in consecutive lanes
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) {
+        const int c16 = tid + u * NT, row = c16 / RT::CPK;
+        u32x4 o;
+        if constexpr (KIND == kMaskD) {
+            o = row < L ? kx[u] : u32x4{0u, 0u, 0u, 0u};
+        } else {
+            const bf16x8 x = __builtin_bit_cast(bf16x8, kx[u]);
+            float f[8], ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                f[e] = phi_pre<KIND>((float)x[e]);
+                ss += f[e] * f[e];
+            }
+            float scl = row < L ? 1.f : 0.f;
+            if constexpr (KIND == kMaskS) scl *= inv_norm(group_sum<RT::CPK>(ss));
+            bf16x8 y;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = f2bf(f[e] * scl);
+            o = __builtin_bit_cast(u32x4, y);
+        }
+        if (c16 < rows * RT::CPK) st16(Ks + RT::off(row, (c16 % RT::CPK) * RT::VEC), o);
     }
+    __syncthreads();
 
     // ---- fold: waves 4c .. 4c+3 -> Fl_c, Gl_c ---------------------------------------------------
+    // A wave always uses one key-channel tile nt (A operand), so the per-key fold weights are applied
+    // once per sub-block to that fragment; the value fragments enter the products unweighted.  The
+    // row-sum tile instead takes the unweighted keys and the weights split as bf16 high part plus the
+    // bf16 rounding of the remainder (columns 0 and 1), which keeps the row sums at ~2^-17.
     if (wave < 4 * n) {
         const int c = wave >> 2, k = wave & 3;
         const int cs = c * C, cn = min(C, L - cs);
         const float etot = Ex(cs + cn - 1, cs);
-        auto tile_of = [&](int u, int &ct, int &nt) -> bool {
-            if constexpr (kColOwn) {
-                ct = u;
-                nt = k;
-                return u < NCT;
-            } else {
-                const int tt = k + 4 * u;
-                ct = tt / NDT;
-                nt = tt % NDT;
-                return tt < NCT * NDT;
-            }
-        };
+        const int nt = k % NDT;
+        auto ct_of = [&](int u) { return kColOwn ? u : (k + 4 * u) / NDT; };
+        auto has = [&](int u) { return kColOwn ? u < NCT : k + 4 * u < NCT * NDT; };
+        bf16x8 ones;   // LIT weight tile: weight 1 in column 0
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ones[e] = f2bf(r == 0 ? 1.f : 0.f);
         f32x4 sf[MAXT], sg[MAXT];
 #pragma unroll
         for (int u = 0; u < MAXT; ++u) sf[u] = sg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int h = cs / kKB; h < (cs + cpad(cn)) / kKB; ++h) {
             float wf[2][4], wg[2][4];
+            if constexpr (KIND != kMaskLit) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = h * kKB + 16 * t + 4 * g + e;
-                    const float valid = j < cs + cn ? 1.f : 0.f;
-                    float a = valid, b = valid;
-                    if constexpr (KIND != kMaskLit) {
-                        const float ej = Ex(j, cs);
-                        a *= fast_exp2(fminf(etot - ej, 0.f));
-                        b *= fast_exp2(fminf(ej, 0.f));
-                    }
-                    wf[t][e] = a;
-                    wg[t][e] = b;
-                }
-            bf16x8 kfr{};
-            if constexpr (kColOwn) kfr = tr_frag<D>(Ks, h, k, r, g);
-#pragma unroll
-            for (int u = 0; u < MAXT; ++u) {
-                int ct, nt;
-                if (!tile_of(u, ct, nt)) break;
-                const bf16x8 a = kColOwn ? kfr : tr_frag<D>(Ks, h, nt, r, g);
-                bf16x8 bf, bg;
-                if (ct < NDT) {
-                    const bf16x8 vv = tr_frag<D>(Vs, h, ct, r, g);
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        bf[e] = f2bf(wf[0][e] * (float)vv[e]);
-                        bf[4 + e] = f2bf(wf[1][e] * (float)vv[4 + e]);
-                        bg[e] = f2bf(wg[0][e] * (float)vv[e]);
-                        bg[4 + e] = f2bf(wg[1][e] * (float)vv[4 + e]);
+                        const float ej = Ex(h * kKB + 16 * t + 4 * g + e, cs);
+                        wf[t][e] = fast_exp2(fminf(etot - ej, 0.f));
+                        wg[t][e] = fast_exp2(fminf(ej, 0.f));
                     }
+            }
+            const bf16x8 kfr = tr_frag<D>(Ks, h, nt, r, g);
+            bf16x8 af = kfr, ag = kfr;
+            if constexpr (KIND != kMaskLit) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float kv = (float)kfr[4 * t + e];
+                        af[4 * t + e] = f2bf(wf[t][e] * kv);
+                        ag[4 * t + e] = f2bf(wg[t][e] * kv);
+                    }
+            }
+#pragma unroll
+            for (int u = 0; u < MAXT; ++u) {
+                if (!has(u)) break;
+                const int ct = ct_of(u);
+                if (ct < NDT) {
+                    const bf16x8 vv = tr_frag<D>(Vs, h, ct, r, g);
+                    sf[u] = mfma_bf16(af, vv, sf[u]);
+                    if constexpr (KIND != kMaskLit) sg[u] = mfma_bf16(ag, vv, sg[u]);
+                } else if constexpr (KIND == kMaskLit) {
+                    sf[u] = mfma_bf16(kfr, ones, sf[u]);
                 } else {
+                    bf16x8 bf, bg;
 #pragma unroll
                     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -855,31 +909,35 @@ __global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParam
                             bf[4 * t + e] = r == 0 ? fh : (r == 1 ? flo : f2bf(0.f));
                             bg[4 * t + e] = r == 0 ? gh : (r == 1 ? glo : f2bf(0.f));
                         }
+                    sf[u] = mfma_bf16(kfr, bf, sf[u]);
+                    sg[u] = mfma_bf16(kfr, bg, sg[u]);
                 }
-                sf[u] = mfma_bf16(a, bf, sf[u]);
-                if constexpr (KIND != kMaskLit) sg[u] = mfma_bf16(a, bg, sg[u]);
             }
         }
 #pragma unroll
         for (int u = 0; u < MAXT; ++u) {
-            int ct, nt;
-            if (!tile_of(u, ct, nt)) break;
+            if (!has(u)) break;
+            const int ct = ct_of(u);
 #pragma unroll
             for (int which = 0; which < (KIND == kMaskLit ? 1 : 2); ++which) {
                 // LIT: the two local states coincide; one copy in the forward slot serves both
                 if (KIND != kMaskLit && (which == 0 ? c == n - 1 : c == 0)) continue;
-                const f32x4 s = which == 0 ? sf[u] : sg[u];
-                unsigned char *slot = which == 0 ? fslot(c) : gslot(c);
+                const f32x4 sv = which == 0 ? sf[u] : sg[u];
+                T *slot = reinterpret_cast<T *>(which == 0 ? fslot(c) : gslot(c));
+                bf16x4 o;
                 if (ct < NDT) {
-                    bf16x4 o;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = f2bf(s[e]);
-                    *reinterpret_cast<bf16x4 *>(reinterpret_cast<T *>(slot) + slot_off<D, true>(ct, nt, lane)) = o;
+                    for (int e = 0; e < 4; ++e) o[e] = f2bf(sv[e]);
+                    *reinterpret_cast<bf16x4 *>(slot + F::wr(ct, nt, r, g)) = o;
                 } else {
-                    f32x4 z;
+                    // row sums z[16 nt + 4 g + e] = columns 0 + 1
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) z[e] = s[e] + __shfl_xor(s[e], 1, 64);
-                    if (r == 0) *reinterpret_cast<f32x4 *>(slot + Cf::VBYTES + (size_t)(16 * nt + 4 * g) * 4) = z;
+                    for (int e = 0; e < 4; ++e) {
+                        const float z = sv[e] + __shfl_xor(sv[e], 1, 64);
+                        const __bf16 zh = f2bf(z);
+                        o[e] = r == 0 ? zh : f2bf(z - (float)zh);
+                    }
+                    if (r < 2) *reinterpret_cast<bf16x4 *>(slot + F::VB / 2 + F::zwr(nt, r, g)) = o;
                 }
             }
         }
@@ -893,22 +951,22 @@ __global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParam
     const int cs = c * C, cn = min(C, L - cs);
     const bool ok = i < cs + cn;
     const float etot = tot[c];
-    bf16x8 qf[NQ];
+    bf16x8 qf[NF];
     float Ei, den = 0.f;
     f32x4 acc[NDT];
     {
-        float x[NQ][8];
+        float x[NF][8];
         float ss = 0.f;
 #pragma unroll
-        for (int s = 0; s < NQ; ++s)
+        for (int s = 0; s < NF; ++s) {
+            const bf16x8 qv = __builtin_bit_cast(bf16x8, qraw[s]);
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float xv = hh < HW ? phi_pre<KIND>((float)qraw[s][hh][e]) : 0.f;
-                    x[s][4 * hh + e] = xv;
-                    ss += xv * xv;
-                }
+            for (int e = 0; e < 8; ++e) {
+                const float xv = F::has_ch(g) ? phi_pre<KIND>((float)qv[e]) : 0.f;
+                x[s][e] = xv;
+                ss += xv * xv;
+            }
+        }
         float sc = ok ? 1.f : 0.f;
         if constexpr (KIND == kMaskS) {
             ss += __shfl_xor(ss, 16, 64);
@@ -916,7 +974,7 @@ __global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParam
             sc *= inv_norm(ss);
         }
 #pragma unroll
-        for (int s = 0; s < NQ; ++s) {
+        for (int s = 0; s < NF; ++s) {
             bf16x8 f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) f[e] = f2bf(x[s][e] * sc);
@@ -927,98 +985,83 @@ __global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParam
         for (int ct = 0; ct < NDT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // other chunks' local states on the decayed query
+    // other chunks' local states applied to the query; the decay between them scales the product
+    f32x4 accz = f32x4{0.f, 0.f, 0.f, 0.f};   // row sums: rows 0 (high part) and 1 (low part) of a tile
     for (int c2 = 0; c2 < n; ++c2) {
         if (c2 == c) continue;
         float ex = c2 < c ? Ei : etot - Ei;
         for (int c3 = min(c, c2) + 1; c3 < max(c, c2); ++c3) ex += tot[c3];
-        const float dq = KIND == kMaskLit ? 1.f : fast_exp2(ex);
-        const unsigned char *slot = (c2 < c || KIND == kMaskLit) ? fslot(c2) : gslot(c2);
-        const T *sv = reinterpret_cast<const T *>(slot);
-        const float *sz = reinterpret_cast<const float *>(slot + Cf::VBYTES);
-        float zdot = 0.f;
-        bf16x8 qd[NQ];
-#pragma unroll
-        for (int s = 0; s < NQ; ++s) {
-            bf16x8 f;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (hh < HW) z4 = *reinterpret_cast<const f32x4 *>(sz + 16 * (HW * s + hh) + 4 * g);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float xv = (float)qf[s][4 * hh + e];
-                    zdot += xv * z4[e];
-                    f[4 * hh + e] = f2bf(dq * xv);
-                }
-            }
-            qd[s] = KIND == kMaskLit ? qf[s] : f;
-        }
-        den += dq * zdot;
+        const T *sv = reinterpret_cast<const T *>((c2 < c || KIND == kMaskLit) ? fslot(c2) : gslot(c2));
+        // every LDS read of the slot is issued before the first product, so their latencies overlap
+        bf16x8 sa[NDT][NF], za[NF];
 #pragma unroll
         for (int ct = 0; ct < NDT; ++ct)
 #pragma unroll
-            for (int s = 0; s < NQ; ++s) {
-                const T *src = sv + slot_off<D, true>(ct, HW * s, lane);
-                bf16x8 a;
-                if constexpr (HW == 2) {
-                    a = *reinterpret_cast<const bf16x8 *>(src);
-                } else {
-                    const bf16x4 h4 = *reinterpret_cast<const bf16x4 *>(src);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        a[e] = h4[e];
-                        a[4 + e] = f2bf(0.f);
-                    }
-                }
-                acc[ct] = mfma_bf16(a, qd[s], acc[ct]);
+            for (int s = 0; s < NF; ++s) {
+                sa[ct][s] = bf16x8{};
+                if (F::has_ch(g)) sa[ct][s] = *reinterpret_cast<const bf16x8 *>(sv + F::rd(ct, s, lane));
             }
+#pragma unroll
+        for (int s = 0; s < NF; ++s) {
+            za[s] = bf16x8{};
+            if (r < 2 && F::has_ch(g)) za[s] = *reinterpret_cast<const bf16x8 *>(sv + F::VB / 2 + F::zrd(s, r, g));
+        }
+        if constexpr (KIND == kMaskLit) {
+#pragma unroll
+            for (int s = 0; s < NF; ++s) {
+#pragma unroll
+                for (int ct = 0; ct < NDT; ++ct) acc[ct] = mfma_bf16(sa[ct][s], qf[s], acc[ct]);
+                accz = mfma_bf16(za[s], qf[s], accz);
+            }
+        } else {
+            const float dq = fast_exp2(ex);
+            f32x4 tv[NDT], tz = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ct = 0; ct < NDT; ++ct) tv[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NF; ++s) {
+#pragma unroll
+                for (int ct = 0; ct < NDT; ++ct) tv[ct] = mfma_bf16(sa[ct][s], qf[s], tv[ct]);
+                tz = mfma_bf16(za[s], qf[s], tz);
+            }
+#pragma unroll
+            for (int ct = 0; ct < NDT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[ct][e] += dq * tv[ct][e];
+            accz[0] += dq * tz[0];
+            accz[1] += dq * tz[1];
+        }
     }
+    // rows 0 and 1 of the row-sum tile sit in lanes g = 0 (elements 0, 1); other lanes hold zeros
+    den += accz[0] + accz[1];
 
-    // intra-chunk attention over the chunk's keys
+    // intra-chunk attention over the chunk's keys (padded keys are zero rows: no mask needed)
     for (int h = cs / kKB; h < (cs + cpad(cn)) / kKB; ++h) {
         const int j0 = h * kKB;
-        const bool partial = j0 + kKB > cs + cn;
-        bf16x8 vfr[NDT];
+        bf16x8 vfr[NDT], kf[2][NF];
 #pragma unroll
         for (int ct = 0; ct < NDT; ++ct) vfr[ct] = tr_frag<D>(Vs, h, ct, r, g);
-        bf16x8 kf[2][NQ];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int s = 0; s < NQ; ++s) {
-                const int row = j0 + 16 * t + r;
-                bf16x8 f;
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    if (hh < HW) {
-                        const bf16x4 v4 =
-                            *reinterpret_cast<const bf16x4 *>(Ks + RT::off(row, 16 * (HW * s + hh) + 4 * g));
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) f[4 * hh + e] = v4[e];
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) f[4 * hh + e] = f2bf(0.f);
-                    }
-                }
-                kf[t][s] = f;
+            for (int s = 0; s < NF; ++s) {
+                kf[t][s] = bf16x8{};
+                if (F::has_ch(g)) kf[t][s] = *reinterpret_cast<const bf16x8 *>(Ks + RT::off(j0 + 16 * t + r, 32 * s + 8 * g));
             }
         f32x4 sa[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             sa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < NQ; ++s) sa[t] = mfma_bf16(kf[t][s], qf[s], sa[t]);
+            for (int s = 0; s < NF; ++s) sa[t] = mfma_bf16(kf[t][s], qf[s], sa[t]);
         }
         bf16x8 pf;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int j = j0 + 16 * t + 4 * g + e;
                 float pe = sa[t][e];
-                if constexpr (KIND != kMaskLit) pe *= fast_exp2(-__builtin_fabsf(Ei - Ex(j, cs)));
-                if (partial) pe = j < cs + cn ? pe : 0.f;
+                if constexpr (KIND != kMaskLit) pe *= fast_exp2(-__builtin_fabsf(Ei - Ex(j0 + 16 * t + 4 * g + e, cs)));
                 den += pe;
                 pf[4 * t + e] = f2bf(pe);
             }
