@@ -103,8 +103,19 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
         const int i = (wtile0 + qt) * 16 + r;
         const bool ok = i < L && qt < wave_tiles;
         float x[C::CPL];
-        const T *src = qg + (size_t)(ok ? i : 0) * D + g * C::CPL;
-        if constexpr (C::CPL * sizeof(T) % 16 == 0) {
+        const T *row = qg + (size_t)(ok ? i : 0) * D;
+        if constexpr (BF16 && C::CPL >= 8) {
+            // fragment st of lane group g: the eight channels of 16-byte chunk 4 st + g
+#pragma unroll
+            for (int st = 0; st < C::NS; ++st) {
+                T tmp[8];
+                const u32x4 raw = ld16(row + 8 * (4 * st + g));
+                __builtin_memcpy(tmp, &raw, 16);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[8 * st + e] = (float)tmp[e];
+            }
+        } else if constexpr (C::CPL * sizeof(T) % 16 == 0) {
+            const T *src = row + g * C::CPL;
 #pragma unroll
             for (int c = 0; c < C::CPL; c += RT::VEC) {
                 T tmp[RT::VEC];
@@ -114,6 +125,7 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
                 for (int e = 0; e < RT::VEC; ++e) x[c + e] = (float)tmp[e];
             }
         } else {
+            const T *src = row + g * C::CPL;
 #pragma unroll
             for (int c = 0; c < C::CPL; ++c) x[c] = (float)src[c];
         }
@@ -231,7 +243,7 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
 #pragma unroll
                     for (int st = 0; st < C::NS; ++st) {
                         if constexpr (C::CPL >= 8) {
-                            kf[t][st] = *reinterpret_cast<const bf16x8 *>(kelem(t, g * C::CPL + 8 * st));
+                            kf[t][st] = *reinterpret_cast<const bf16x8 *>(kelem(t, 8 * (4 * st + g)));
                         } else {
                             const bf16x4 h4 = *reinterpret_cast<const bf16x4 *>(kelem(t, g * C::CPL));
                             bf16x8 f;

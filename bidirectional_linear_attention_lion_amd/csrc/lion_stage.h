@@ -4,9 +4,9 @@
 // memory into LDS with global_load_lds_dwordx4 (16 bytes per lane, no VGPRs in between), so a
 // workgroup can have a whole stage of keys and values in flight at once.  One such load writes the
 // 64 lanes' 16-byte chunks to 64 consecutive 16-byte LDS slots; slot s of the tile holds chunk
-// (s % CPK) ^ swz(row) of row s / CPK, an XOR swizzle that keeps the 16-byte reads of 16 different
-// rows (matrix-core A/B fragments) on distinct banks.  Rows at or past L are loaded from row L - 1
-// (always in bounds); kernels zero or ignore them.
+// (s % CPK) ^ swz(row) of row s / CPK, an XOR swizzle that spreads the 16-byte reads of 16 different
+// rows (matrix-core A/B fragments) and the transposed reads over distinct banks.  Rows at or past L
+// are loaded from row L - 1 (always in bounds); kernels zero or ignore them.
 //
 // V^T fragments are read from the row-major value tile with ds_read_b64_tr_b16: lane a of a 16-lane
 // group addresses row 4g + a/4 (g = that group), columns 16 ct + 4 (a % 4) .. + 3, and receives the
@@ -24,7 +24,10 @@ template <int D, typename T>
 struct RowTile {
     static constexpr int VEC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
     static constexpr int CPK = D / VEC;                // chunks per row
-    __device__ static __forceinline__ int swz(int row) { return (row >> 1) & (CPK - 1); }
+    // eight 16-byte chunks per row (bf16 d = 64): row & 7, under which both the 16-row fragment reads
+    // (lane group g reading chunk 4 s + g) and the transposed reads below hit distinct banks (checked
+    // with the SQ_LDS_BANK_CONFLICT counter); other widths: (row >> 1) & (CPK - 1)
+    __device__ static __forceinline__ int swz(int row) { return CPK == 8 ? (row & 7) : (row >> 1) & (CPK - 1); }
     // element offset of (row, col) in the swizzled tile
     __device__ static __forceinline__ int off(int row, int col) {
         return row * D + (((col / VEC) ^ swz(row)) * VEC) + (col % VEC);
