@@ -151,7 +151,7 @@ struct RnnShape {
 };
 
 template <int D, int KIND, int CW, int NR, bool BF16>
-__global__ void __launch_bounds__(2 * NR * 64) birnn_kernel(RnnParams p) {
+__global__ void __launch_bounds__(2 * NR * 64) __attribute__((amdgpu_waves_per_eu(3))) birnn_kernel(RnnParams p) {
     using T = std::conditional_t<BF16, __bf16, float>;
     using Sh = RnnShape<D, CW, NR>;
     constexpr int NS = Sh::NS, RW = Sh::RW, RB = Sh::RB, KV = Sh::KV, NG = Sh::NG, NP = Sh::NP;
@@ -307,11 +307,11 @@ __global__ void __launch_bounds__(2 * NR * 64) birnn_kernel(RnnParams p) {
 #pragma unroll
             for (int m = 0; m < KV; ++m) z[m] *= lam_end;
         }
-        // per-token scalars of the block, one register each (lane t holds token t's value)
+        // per-token scalars of the block, one register each (lane t holds token t's value); the tokens
+        // where the state is renormalised, as a scalar bit mask
         const float kscv = KIND != kMaskLit ? ksc[lane & 15] : 1.f;
-        const float yscv = KIND != kMaskLit ? ysc[lane & 15] : 1.f;
         const float multv = KIND != kMaskLit ? mult[lane & 15] : 1.f;
-        const float diagv = sdiag[lane & 15];
+        const unsigned rmask = KIND != kMaskLit ? (unsigned)(__ballot(multv != 1.f) & 0xFFFFu) : 0u;
         auto lane_val = [](float v, int i) {
             return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i));
         };
@@ -340,18 +340,16 @@ __global__ void __launch_bounds__(2 * NR * 64) birnn_kernel(RnnParams p) {
             // (unconditional: the staging buffer always holds kT rows; rows past the block are unused)
             Tok nxt;
             if (tl + 1 < kT) nxt = load_tok(tl + 1);
-            float ks = 1.f, ys = 1.f;
+            float ks = 1.f;
             if constexpr (KIND != kMaskLit) {
                 ks = lane_val(kscv, tl);
-                ys = lane_val(yscv, tl);
-                const float mu = lane_val(multv, tl);
-                if (mu != 1.f) {
+                if (rmask & (1u << tl)) {
+                    const float mu = lane_val(multv, tl);
 #pragma unroll
                     for (int i = 0; i < RW; ++i) S[i] *= mu;
 #pragma unroll
                     for (int m = 0; m < KV; ++m) z[m] *= mu;
                 }
-                if (tl == nsteps - 1) lam_end = ys;
             }
             float y0 = 0.f, y1 = 0.f, cp = 0.f;
 #pragma unroll
@@ -362,24 +360,19 @@ __global__ void __launch_bounds__(2 * NR * 64) birnn_kernel(RnnParams p) {
                 z[m] += kb;
                 cp += zmask[m] * qb * z[m];
             }
+            // unscaled partials (q^T S' and q.z' of this slice); the scale and the diagonal are applied
+            // once per token in the reduction
             cpv[tl] = cp;
-            float y = (y0 + y1) * ys;
-            const int s = s0 + tl, sp = L - 1 - s;
-            if (slice == 0 && (s < sp || (s == sp && dir == 1))) y -= lane_val(diagv, tl) * cur.vj;   // first visitor
-            Yp[((dir * kT + tl) * NP + slice) * CW + c] = y;
+            Yp[((dir * kT + tl) * NP + slice) * CW + c] = y0 + y1;
             if (tl + 1 < kT) cur = nxt;
         }
+        if constexpr (KIND != kMaskLit) lam_end = ysc[nsteps - 1];
         // q.z partials of the block: 16 independent row sums, written by the first lane of each slice
 #pragma unroll
         for (int tl = 0; tl < kT; ++tl) cpv[tl] = row16_sum(cpv[tl]);
+        if (c == 0) {
 #pragma unroll
-        for (int tl = 0; tl < kT; ++tl) {
-            if (tl >= nsteps) break;
-            float cp = cpv[tl];
-            if constexpr (KIND != kMaskLit) cp *= lane_val(yscv, tl);
-            const int s = s0 + tl, sp = L - 1 - s;
-            if (slice == 0 && (s < sp || (s == sp && dir == 1))) cp -= lane_val(diagv, tl);
-            if (c == 0) Cp[(dir * kT + tl) * NP + slice] = cp;
+            for (int tl = 0; tl < kT; ++tl) Cp[(dir * kT + tl) * NP + slice] = cpv[tl];
         }
         __syncthreads();
 
@@ -413,6 +406,11 @@ __global__ void __launch_bounds__(2 * NR * 64) birnn_kernel(RnnParams p) {
                 y += Yp[((dir * kT + tl) * NP + g) * CW + c2];
                 cs += Cp[(dir * kT + tl) * NP + g];
             }
+            if constexpr (KIND != kMaskLit) {
+                const float ys = ysc[tl];
+                y *= ys;
+                cs *= ys;
+            }
             float yo, co;
             if (sp >= s0 + nsteps) {
                 park[(size_t)t * (CW + 1) + c2] = y;
@@ -431,9 +429,16 @@ __global__ void __launch_bounds__(2 * NR * 64) birnn_kernel(RnnParams p) {
                     yo += Yp[((kT + tp) * NP + g) * CW + c2];
                     co += Cp[(kT + tp) * NP + g];
                 }
+                if constexpr (KIND != kMaskLit) {
+                    const float ys = ysc[DIRF + tp];   // the backward direction's scale of that token
+                    yo *= ys;
+                    co *= ys;
+                }
             }
-            const float div = cs + co + p.eps;
-            const float out = (y + yo) / div;
+            // both visits included the diagonal term: remove it once
+            const float dg = sdiag[tl];
+            const float div = cs + co - dg + p.eps;
+            const float out = (y + yo - dg * Vs[tl * D + cg * CW + c2]) / div;
             const size_t o = (base + t) * D + cg * CW + c2;
             if (p.out_bf16)
                 reinterpret_cast<__bf16 *>(p.y)[o] = f2bf(out);

@@ -55,6 +55,7 @@ struct ChunkParams {
     unsigned char *fs;     // forward states, [B*H*n] slots
     unsigned char *gs;     // backward states, [B*H*n] slots
     float *tot;            // log2 of each chunk's total decay, [B*H*n]
+    int ng;                // resident path: row groups per (batch, head)
 };
 
 template <int D, bool BF16>
@@ -355,7 +356,7 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(ChunkParams p)
         for (int u = 0; u < kU; ++u) {
             const int k = k0 + u;
             if (k >= steps) break;
-            const int c = chunk_of(k);
+            const int c = uniform(chunk_of(k));   // scalar load of the total (see group_scan_kernel)
             const u32x4 x = buf[u];
             if (k + kU < steps) buf[u] = ld16(base + (size_t)chunk_of(k + kU) * Cf::SLOT);
             const float a = fast_exp2(tot[c]);
@@ -686,8 +687,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
 }
 
 // ================================ resident kernel =====================================================
-// Short sequences -- every key and value row of a (batch, head) fits in LDS and there are at most
-// kFuseChunks chunks: one workgroup of 16 waves per (batch, head), one launch, no workspace.  Waves
+// Short sequences -- every key and value row of a (batch, head) fits in LDS (at most 256 rows, so at
+// most 4 chunks): one workgroup of 16 waves per (batch, head), one launch, no workspace.  Waves
 // 4c .. 4c+3 fold chunk c into its local states Fl_c and Gl_c, which stay in LDS; then wave w computes
 // query tile w: its chunk's intra-chunk attention plus every other chunk's local state applied to the
 // query with the decay in between,
@@ -696,13 +697,21 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
 // a direct sum over at most three states in place of the carried scan.  Keys pass through registers
 // on their way into LDS: phi is applied there and rows past L are zeroed, so padded keys add nothing to
 // any state, score or row sum and no later step masks them.
-constexpr int kFuseWaves = 16;
-constexpr int kFuseChunks = 4;
-constexpr int kFuseRows = 256;
+//
+// Longer sequences with C = 64 are cut into row groups of whole chunks (128 rows) and take
+// three launches: a group-state kernel folds each group's keys straight into the group's own states
+// (forward relative to the group's last token, backward relative to the token before its first); a
+// scan over the groups turns these into carried states in place; and this kernel processes each group
+// as above (a 128-row group is one workgroup of 8 waves, two per CU), with the carried states of all
+// earlier and of all later groups as two more states applied to every query of the group.
+constexpr int kFuseRows = 256;    // one launch up to this many rows
+constexpr int kGroupRows = 128;   // row group of longer sequences (C = 64)
 
 __host__ __device__ constexpr bool fused_ok(int L, int C, int d, bool bf16) {
-    return bf16 && d <= 64 && C % 64 == 0 && cpad(L) <= kFuseRows && (L + C - 1) / C <= kFuseChunks;
+    return bf16 && d <= 64 && C % 64 == 0 && L >= 1 && (L <= kFuseRows || C == 64);
 }
+__host__ __device__ constexpr int fused_rows(int L, int C) { return L <= kFuseRows ? kFuseRows : kGroupRows; }
+__host__ __device__ constexpr int fused_groups(int L, int C) { return (L + fused_rows(L, C) - 1) / fused_rows(L, C); }
 
 // Contraction fragments over the key channels: fragment s of lane (r, g) holds the eight consecutive
 // channels 32 s + 8 g .. 32 s + 8 g + 7 (d = 16: lanes g >= 2 hold zeros), so a query or key fragment
@@ -715,6 +724,7 @@ struct Fuse {
     static constexpr int NF = (D + 31) / 32;
     static constexpr int VB = NDT * NF * 1024;
     static constexpr int SLOT = VB + NF * 128;
+    static constexpr int SLOTK = (SLOT + 1023) & ~1023;   // a group state in the workspace: whole KiB
     // element offsets: fragment s of value tile ct as read by `lane`
     __device__ static __forceinline__ int rd(int ct, int s, int lane) { return ((ct * NF + s) * 64 + lane) * 8; }
     // where lane (r, g) of a fold tile (ct, nt), holding channels 16 nt + 4 g + e, writes its four values
@@ -730,18 +740,27 @@ struct Fuse {
     __device__ static __forceinline__ bool has_ch(int g) { return 8 * g < D || D >= 32; }
 };
 
-template <int D>
-__host__ __device__ constexpr size_t fused_lds() {
-    return 2 * (size_t)kFuseRows * D * 2 + 2 * kFuseChunks * (size_t)Fuse<D>::SLOT + (size_t)kFuseRows * 4 + 16 * 4 +
-           16 * 8;
+// Chunk-local states a ROWS-row workgroup keeps in LDS: forward states of chunks 0 .. NCH-2 and
+// backward states of chunks 1 .. NCH-1 (the only ones ever read), NCH = ROWS / 64 the most chunks a
+// group holds; LIT: one state per chunk.
+template <int KIND, int ROWS>
+__host__ __device__ constexpr int fuse_slots() { return KIND == kMaskLit ? ROWS / 64 : 2 * (ROWS / 64) - 2; }
+
+// LDS of the resident kernel: [K rows][V rows][chunk states][incoming F, G][E][totals][scratch]
+template <int D, int KIND, int ROWS>
+__host__ __device__ constexpr size_t fused_lds(bool incoming) {
+    return 2 * (size_t)ROWS * D * 2 + (size_t)fuse_slots<KIND, ROWS>() * Fuse<D>::SLOT +
+           (incoming ? 2 * (size_t)Fuse<D>::SLOTK : 0) + (size_t)ROWS * 4 + 16 * 4 + 16 * 8;
 }
 
 // LION-S exponents relative to each chunk's start, E[t] = sum_{u = cs(t)}^{t} log2(lambda_u): one fp64 scan
 // over the sequence (threads 0 .. 255), differenced in fp64 at the chunk starts; positions past L - 1
-// get the last chunk's total.  Needs rows <= 256; all threads call it.
-__device__ void fused_exponents_s(float *E, double *sh, const float *ll, int L, int C, int rows, int tid) {
+// get the last chunk's total.  `llt` is thread tid's log(lambda) (0 past L), loaded by the caller ahead
+// of its other loads.  Needs rows <= 256; all threads call it.
+__device__ __forceinline__ float load_ll(const float *ll, int L, int tid) { return tid < L ? ll[tid] : 0.f; }
+__device__ void fused_exponents_s(float *E, double *sh, float llt, int L, int C, int rows, int tid) {
     const int lane = tid & 63, wave = tid >> 6;
-    double x = tid < L ? (double)ll[tid] * 1.4426950408889634 : 0.0;
+    double x = (double)llt * 1.4426950408889634;
     if (wave < 4) {
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -754,18 +773,18 @@ __device__ void fused_exponents_s(float *E, double *sh, const float *ll, int L, 
     if (wave < 4)
         for (int w = 0; w < wave; ++w) x += sh[w];
     if (tid == 0) sh[4] = 0.0;
-    if (tid < rows && (tid + 1) % C == 0 && (tid + 1) / C < kFuseChunks) sh[4 + (tid + 1) / C] = x;
+    if (tid < rows && (tid + 1) % C == 0 && (tid + 1) / C < 4) sh[4 + (tid + 1) / C] = x;
     __syncthreads();
     if (tid < rows) E[tid] = (float)(x - sh[4 + tid / C]);
     __syncthreads();
 }
 
-template <int D, int KIND>
-__global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParams p) {
+template <int D, int KIND, int ROWS>
+__global__ void __launch_bounds__(ROWS / 16 * 64) chunk_fused_kernel(ChunkParams p) {
     using F = Fuse<D>;
     using T = __bf16;
     using RT = RowTile<D, T>;
-    constexpr int NT = kFuseWaves * 64;
+    constexpr int NW = ROWS / 16, NT = NW * 64, NCH = ROWS / 64;
     constexpr int NDT = F::NDT, NCT = NDT + 1, NF = F::NF;
     constexpr bool kColOwn = NDT == 4;   // the 4 waves of a chunk own one key-channel tile each
     constexpr int MAXT = (NCT * NDT + 3) / 4;
@@ -773,24 +792,33 @@ __global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParam
 
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int L = p.L, C = p.C, n = p.n;
-    const int bh = blockIdx.x;
+    const int C = p.C, ng = p.ng;
+    const int bh = blockIdx.x / ng, gi = blockIdx.x % ng;   // (batch, head) and row group
+    const int L = min(ROWS, p.L - gi * ROWS);                 // rows of this group
+    const int n = (L + C - 1) / C;                           // chunks of this group
     const int rows = cpad(L);
-    const size_t base = (size_t)bh * L;
+    const size_t base = (size_t)bh * p.L + (size_t)gi * ROWS;
+    const bool has_fin = gi > 0, has_gin = gi + 1 < ng;
 
-    // LDS: [K rows][V rows][Fl_0 Gl_0 Fl_1 Gl_1 ...][E][chunk totals][scan scratch]
     T *Ks = reinterpret_cast<T *>(smem);
-    T *Vs = Ks + kFuseRows * D;
-    unsigned char *sl = reinterpret_cast<unsigned char *>(Vs + kFuseRows * D);
-    float *E = reinterpret_cast<float *>(sl + 2 * kFuseChunks * F::SLOT);
-    float *tot = E + kFuseRows;
+    T *Vs = Ks + ROWS * D;
+    unsigned char *sl = reinterpret_cast<unsigned char *>(Vs + ROWS * D);
+    unsigned char *fin = sl + fuse_slots<KIND, ROWS>() * F::SLOT;
+    unsigned char *gin = fin + F::SLOTK;
+    float *E = reinterpret_cast<float *>(fin + (ng > 1 ? 2 * F::SLOTK : 0));
+    float *tot = E + ROWS;
     double *sh = reinterpret_cast<double *>(tot + 16);
-    auto fslot = [&](int c) { return sl + (size_t)(2 * c) * F::SLOT; };
-    auto gslot = [&](int c) { return sl + (size_t)(2 * c + 1) * F::SLOT; };
+    // forward state of chunk c (c <= NCH - 2; LIT: any c), backward state of chunk c (c >= 1)
+    auto fslot = [&](int c) { return sl + (size_t)c * F::SLOT; };
+    auto gslot = [&](int c) { return sl + (size_t)(NCH - 2 + c) * F::SLOT; };
 
-    // values straight to LDS, keys into registers
-    stage_rows<D, T>(Vs, reinterpret_cast<const T *>(p.v) + base * D, 0, rows, L, wave, kFuseWaves, lane);
-    constexpr int KPER = (kFuseRows * RT::CPK + NT - 1) / NT;   // 16-byte key chunks per thread
+    // log(lambda) first (its wait does not wait for the bulk loads behind it); values straight to LDS,
+    // keys into registers; the carried states of the other groups straight to LDS
+    const float llt = KIND == kMaskS ? load_ll(p.ll + base, L, tid) : 0.f;
+    stage_rows<D, T>(Vs, reinterpret_cast<const T *>(p.v) + base * D, 0, rows, L, wave, NW, lane);
+    if (has_fin) stage_flat(fin, p.fs + (size_t)(blockIdx.x - 1) * F::SLOTK, F::SLOTK / 1024, wave, NW, lane);
+    if (has_gin) stage_flat(gin, p.gs + (size_t)(blockIdx.x + 1) * F::SLOTK, F::SLOTK / 1024, wave, NW, lane);
+    constexpr int KPER = (ROWS * RT::CPK + NT - 1) / NT;   // 16-byte key chunks per thread
     u32x4 kx[KPER];
     {
         const T *kg = reinterpret_cast<const T *>(p.k) + base * D;
@@ -812,7 +840,7 @@ __global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParam
 
     float lgD = 0.f;
     if constexpr (KIND == kMaskD) lgD = p.ll[bh % p.H] * kLog2e;
-    if constexpr (KIND == kMaskS) fused_exponents_s(E, sh, p.ll + base, L, C, rows, tid);
+    if constexpr (KIND == kMaskS) fused_exponents_s(E, sh, llt, L, C, rows, tid);
     // exponent of token t of the chunk starting at cs, relative to the end of the chunk before it
     auto Ex = [&](int t, int cs) -> float {
         if constexpr (KIND == kMaskLit) return 0.f;
@@ -920,7 +948,8 @@ __global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParam
             const int ct = ct_of(u);
 #pragma unroll
             for (int which = 0; which < (KIND == kMaskLit ? 1 : 2); ++which) {
-                // LIT: the two local states coincide; one copy in the forward slot serves both
+                // LIT: the two local states coincide; one copy in the forward slot serves both.  The last
+                // chunk's forward and the first chunk's backward state are never read.
                 if (KIND != kMaskLit && (which == 0 ? c == n - 1 : c == 0)) continue;
                 const f32x4 sv = which == 0 ? sf[u] : sg[u];
                 T *slot = reinterpret_cast<T *>(which == 0 ? fslot(c) : gslot(c));
@@ -987,11 +1016,13 @@ __global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParam
 
     // other chunks' local states applied to the query; the decay between them scales the product
     f32x4 accz = f32x4{0.f, 0.f, 0.f, 0.f};   // row sums: rows 0 (high part) and 1 (low part) of a tile
-    for (int c2 = 0; c2 < n; ++c2) {
+    // chunks -1 and n stand for the carried states of all earlier and all later groups
+    for (int c2 = has_fin ? -1 : 0; c2 < (has_gin ? n + 1 : n); ++c2) {
         if (c2 == c) continue;
         float ex = c2 < c ? Ei : etot - Ei;
         for (int c3 = min(c, c2) + 1; c3 < max(c, c2); ++c3) ex += tot[c3];
-        const T *sv = reinterpret_cast<const T *>((c2 < c || KIND == kMaskLit) ? fslot(c2) : gslot(c2));
+        const unsigned char *sb = c2 < 0 ? fin : c2 == n ? gin : (c2 < c || KIND == kMaskLit) ? fslot(c2) : gslot(c2);
+        const T *sv = reinterpret_cast<const T *>(sb);
         // every LDS read of the slot is issued before the first product, so their latencies overlap
         bf16x8 sa[NDT][NF], za[NF];
 #pragma unroll
@@ -1099,6 +1130,198 @@ __global__ void __launch_bounds__(kFuseWaves * 64) chunk_fused_kernel(ChunkParam
     }
 }
 
+// ================================ group states ========================================================
+// The own states of one row group (ROWS rows, whole chunks) of a long sequence, folded straight from the
+// group's keys and values: Fg = sum_j 2^(E_last - E_j) phi(k_j) [v_j, 1]^T (relative to the group's
+// last token) and Gg = sum_j 2^(E_j) phi(k_j) [v_j, 1]^T (relative to the token before its first),
+// E_j = log2 of the decay product from the group's first token through token j; both equal the decayed
+// sums of the group's chunk-local states.  Eight waves: wave (dir, nt) folds key-channel tile nt of one
+// direction over all the group's keys (LIT: one state, written as both).  The states go to the
+// workspace in the resident kernel's slot layout, with the group's log2 decay total.
+template <int D, int KIND, int ROWS>
+__global__ void __launch_bounds__(512) group_state_kernel(ChunkParams p) {
+    using F = Fuse<D>;
+    using T = __bf16;
+    using RT = RowTile<D, T>;
+    constexpr int NT = 512, NDT = F::NDT, NCT = NDT + 1;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int ng = p.ng, bh = blockIdx.x / ng, gi = blockIdx.x % ng;
+    const int L = min(ROWS, p.L - gi * ROWS);
+    const int rows = cpad(L);
+    const size_t base = (size_t)bh * p.L + (size_t)gi * ROWS;
+
+    T *Ks = reinterpret_cast<T *>(smem);
+    T *Vs = Ks + ROWS * D;
+    float *E = reinterpret_cast<float *>(Vs + ROWS * D);
+    double *sh = reinterpret_cast<double *>(E + ROWS);
+
+    const float llt = KIND == kMaskS ? load_ll(p.ll + base, L, tid) : 0.f;
+    stage_rows<D, T>(Vs, reinterpret_cast<const T *>(p.v) + base * D, 0, rows, L, wave, 8, lane);
+    constexpr int KPER = (ROWS * RT::CPK + NT - 1) / NT;
+    u32x4 kx[KPER];
+    {
+        const T *kg = reinterpret_cast<const T *>(p.k) + base * D;
+#pragma unroll
+        for (int u = 0; u < KPER; ++u) {
+            const int c16 = min(tid + u * NT, rows * RT::CPK - 1);
+            kx[u] = ld16(kg + (size_t)min(c16 / RT::CPK, L - 1) * D + (c16 % RT::CPK) * RT::VEC);
+        }
+    }
+    float lgD = 0.f;
+    if constexpr (KIND == kMaskD) lgD = p.ll[bh % p.H] * kLog2e;
+    if constexpr (KIND == kMaskS) fused_exponents_s(E, sh, llt, L, ROWS, rows, tid);   // one "chunk": the group
+    auto Ex = [&](int t) -> float {
+        if constexpr (KIND == kMaskLit) return 0.f;
+        else if constexpr (KIND == kMaskD) return (float)(t + 1) * lgD;
+        else return E[t];
+    };
+    wait_vm_all();
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) {
+        const int c16 = tid + u * NT, row = c16 / RT::CPK;
+        u32x4 o;
+        if constexpr (KIND == kMaskD) {
+            o = row < L ? kx[u] : u32x4{0u, 0u, 0u, 0u};
+        } else {
+            const bf16x8 x = __builtin_bit_cast(bf16x8, kx[u]);
+            float f[8], ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                f[e] = phi_pre<KIND>((float)x[e]);
+                ss += f[e] * f[e];
+            }
+            float scl = row < L ? 1.f : 0.f;
+            if constexpr (KIND == kMaskS) scl *= inv_norm(group_sum<RT::CPK>(ss));
+            bf16x8 y;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = f2bf(f[e] * scl);
+            o = __builtin_bit_cast(u32x4, y);
+        }
+        if (c16 < rows * RT::CPK) st16(Ks + RT::off(row, (c16 % RT::CPK) * RT::VEC), o);
+    }
+    __syncthreads();
+
+    const int nt = wave & 3, dir = wave >> 2;
+    if (nt < NDT && (KIND != kMaskLit || dir == 0)) {
+        const float etot = Ex(L - 1);
+        bf16x8 ones;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ones[e] = f2bf(r == 0 ? 1.f : 0.f);
+        f32x4 acc[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < rows / kKB; ++h) {
+            const bf16x8 kfr = tr_frag<D>(Ks, h, nt, r, g);
+            bf16x8 af = kfr, bw = ones;
+            if constexpr (KIND != kMaskLit) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float ej = Ex(h * kKB + 16 * t + 4 * g + e);
+                        const float w = fast_exp2(fminf(dir == 0 ? etot - ej : ej, 0.f));
+                        af[4 * t + e] = f2bf(w * (float)kfr[4 * t + e]);
+                        const __bf16 wh = f2bf(w);
+                        bw[4 * t + e] = r == 0 ? wh : (r == 1 ? f2bf(w - (float)wh) : f2bf(0.f));
+                    }
+            }
+#pragma unroll
+            for (int ct = 0; ct < NDT; ++ct) acc[ct] = mfma_bf16(af, tr_frag<D>(Vs, h, ct, r, g), acc[ct]);
+            acc[NDT] = mfma_bf16(kfr, bw, acc[NDT]);
+        }
+#pragma unroll
+        for (int dd = 0; dd < 2; ++dd) {
+            if (KIND != kMaskLit && dd != dir) continue;
+            T *dst = reinterpret_cast<T *>((dd == 0 ? p.fs : p.gs) + (size_t)blockIdx.x * F::SLOTK);
+#pragma unroll
+            for (int ct = 0; ct < NDT; ++ct) {
+                bf16x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = f2bf(acc[ct][e]);
+                *reinterpret_cast<bf16x4 *>(dst + F::wr(ct, nt, r, g)) = o;
+            }
+            bf16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float z = acc[NDT][e] + __shfl_xor(acc[NDT][e], 1, 64);
+                const __bf16 zh = f2bf(z);
+                o[e] = r == 0 ? zh : f2bf(z - (float)zh);
+            }
+            if (r < 2) *reinterpret_cast<bf16x4 *>(dst + F::VB / 2 + F::zwr(nt, r, g)) = o;
+        }
+    }
+    if (tid == 0) p.tot[blockIdx.x] = Ex(L - 1);
+}
+
+template <int D, int ROWS>
+__host__ __device__ constexpr size_t group_state_lds() {
+    return 2 * (size_t)ROWS * D * 2 + (size_t)ROWS * 4 + 16 * 8;
+}
+
+// ================================ group scan ==========================================================
+// Carried group states of the resident path, in place: F_g <- 2^t_g F_{g-1} + F_g for g = 1 .. ng-2 and
+// G_g <- 2^t_g G_{g+1} + G_g for g = ng-2 .. 1 (the last forward and first backward states are never
+// read), accumulated in fp32 -- the row sums from their high plus low parts, re-split when stored.
+// One wave per (batch, head, direction, 1 KiB piece of the value part), plus one for the 256 bytes of
+// row sums.  The wave copies its piece of kScanSeg groups straight into LDS, waits once, then walks
+// them in order: the sequential chain touches only LDS and never waits on a global load.
+constexpr int kScanSeg = 32;
+constexpr int kScanWave = 64;
+
+template <int D>
+__host__ __device__ constexpr int group_scan_waves() {
+    return Fuse<D>::VB / 1024 + 1;
+}
+
+template <int D>
+__global__ void __launch_bounds__(kScanWave) group_scan_kernel(ChunkParams p) {
+    using F = Fuse<D>;
+    constexpr int NWV = group_scan_waves<D>();
+    extern __shared__ __align__(16) unsigned char buf[];   // kScanSeg KiB
+    const int lane = threadIdx.x;
+    const int ng = p.ng;
+    const int pc = blockIdx.x % NWV, dir = (blockIdx.x / NWV) & 1, bh = blockIdx.x / (2 * NWV);
+    const bool zu = pc == NWV - 1;
+    // bytes this wave copies per group, and where they start in a state
+    const int pbytes = zu ? F::NF * 128 : 1024;
+    const int poff = zu ? F::VB : pc * 1024;
+    unsigned char *base = (dir == 0 ? p.fs : p.gs) + (size_t)bh * ng * F::SLOTK + poff;
+    const float *tg = p.tot + (size_t)bh * ng;
+    const int steps = ng - 1;
+    auto group_of = [&](int k) { return dir == 0 ? k : ng - 1 - k; };
+    // this lane's unit: a value piece (lane), or row sums (lanes < 2 NF * 4 / 2): high piece hi, low piece hi + 4
+    const bool active = zu ? lane < F::NF * 4 : true;
+    const int o_hi = zu ? ((lane / 4) * 8 + lane % 4) * 16 : lane * 16;
+    const int o_lo = zu ? o_hi + 64 : o_hi;
+
+    float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < steps; s0 += kScanSeg) {
+        const int ns = min(kScanSeg, steps - s0);
+        for (int k = 0; k < ns; ++k)
+            if (lane * 16 < pbytes) load_lds16(buf + k * 1024, base + (size_t)group_of(s0 + k) * F::SLOTK + lane * 16);
+        wait_vm_all();   // also drains the previous segment's stores
+        for (int k = 0; k < ns; ++k) {
+            const int gg = uniform(group_of(s0 + k));
+            const float a = fast_exp2(tg[gg]);
+            const bf16x8 xh = *reinterpret_cast<const bf16x8 *>(buf + k * 1024 + o_hi);
+            const bf16x8 xl = *reinterpret_cast<const bf16x8 *>(buf + k * 1024 + o_lo);
+            bf16x8 oh, ol;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                run[e] = a * run[e] + (float)xh[e] + (zu ? (float)xl[e] : 0.f);
+                oh[e] = f2bf(run[e]);
+                ol[e] = f2bf(run[e] - (float)oh[e]);
+            }
+            unsigned char *dst = base + (size_t)gg * F::SLOTK;
+            if (active) *reinterpret_cast<bf16x8 *>(dst + o_hi) = oh;
+            if (zu && active) *reinterpret_cast<bf16x8 *>(dst + o_lo) = ol;
+        }
+    }
+}
+
 // ================================ host side ===========================================================
 
 
@@ -1109,10 +1332,25 @@ void allow_lds(K *kernel, size_t lds) {
                                   (int)lds);
 }
 
+template <int D>
+void launch_group_scan(const ChunkParams &p, unsigned bhs, hipStream_t stream) {
+    hipLaunchKernelGGL((group_scan_kernel<D>), dim3(bhs * 2 * group_scan_waves<D>()), dim3(kScanWave),
+                       kScanSeg * 1024, stream, p);
+}
+
 template <int D, bool BF16>
 size_t workspace_t(const AttnArgs &a) {
+    if constexpr (BF16 && D <= 64) {
+        if (fused_ok(a.L, a.C, D, BF16)) {
+            // resident path: one launch (states in LDS), or group states and totals
+            const size_t ng = (size_t)fused_groups(a.L, a.C);
+            if (ng < 2) return 0;
+            const size_t nb = (size_t)a.B * a.H * ng;
+            return 2 * nb * Fuse<D>::SLOTK + ((nb * 4 + 15) & ~(size_t)15);
+        }
+    }
     const size_t n = (size_t)((a.L + a.C - 1) / a.C);
-    if (n < 2 || fused_ok(a.L, a.C, D, BF16)) return 0;   // one chunk, or states kept in LDS
+    if (n < 2) return 0;   // one chunk
     const size_t nb = (size_t)a.B * a.H * n;
     return 2 * nb * ChunkCfg<D, BF16>::SLOT + ((nb * 4 + 15) & ~(size_t)15);
 }
@@ -1136,12 +1374,32 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
     const size_t nb = (size_t)a.B * a.H * p.n;
     p.fs = p.gs = nullptr;
     p.tot = nullptr;
+    p.ng = 1;
     if constexpr (BF16 && D <= 64) {
         if (fused_ok(a.L, a.C, D, BF16)) {
-            constexpr size_t lds = fused_lds<D>();
-            allow_lds(&chunk_fused_kernel<D, KIND>, lds);
-            hipLaunchKernelGGL((chunk_fused_kernel<D, KIND>), dim3((unsigned)(a.B * a.H)), dim3(kFuseWaves * 64), lds,
-                               stream, p);
+            const int rows = fused_rows(a.L, a.C);
+            p.ng = fused_groups(a.L, a.C);
+            const unsigned grid = (unsigned)(a.B * a.H * p.ng);
+            if (p.ng > 1) {
+                const size_t ngt = (size_t)a.B * a.H * p.ng;
+                p.fs = reinterpret_cast<unsigned char *>(a.workspace);
+                p.gs = p.fs + ngt * Fuse<D>::SLOTK;
+                p.tot = reinterpret_cast<float *>(p.gs + ngt * Fuse<D>::SLOTK);
+            }
+            auto run = [&](auto rows_c) {
+                constexpr int ROWS = decltype(rows_c)::value;
+                if constexpr (ROWS == kGroupRows) {   // groups: states, scan, then outputs
+                    constexpr size_t lds1 = group_state_lds<D, ROWS>();
+                    allow_lds(&group_state_kernel<D, KIND, ROWS>, lds1);
+                    hipLaunchKernelGGL((group_state_kernel<D, KIND, ROWS>), dim3(grid), dim3(512), lds1, stream, p);
+                    if (p.ng > 2) launch_group_scan<D>(p, (unsigned)(a.B * a.H), stream);
+                }
+                const size_t lds = fused_lds<D, KIND, ROWS>(p.ng > 1);
+                allow_lds(&chunk_fused_kernel<D, KIND, ROWS>, lds);
+                hipLaunchKernelGGL((chunk_fused_kernel<D, KIND, ROWS>), dim3(grid), dim3(ROWS / 16 * 64), lds, stream, p);
+            };
+            if (rows == kGroupRows) run(std::integral_constant<int, kGroupRows>{});
+            else run(std::integral_constant<int, kFuseRows>{});
             return hipGetLastError();
         }
     }

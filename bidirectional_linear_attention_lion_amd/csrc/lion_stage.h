@@ -62,6 +62,12 @@ __device__ __forceinline__ void stage_flat(void *dst, const void *src, int kib, 
                                          16, 0, 0);
 }
 
+// One lane's 16 bytes at `src` into the LDS slot of its lane index: this wave's load writes lane i's
+// bytes to dst + 16 i (lanes that do not execute it leave their slots alone).
+__device__ __forceinline__ void load_lds16(void *dst, const void *src) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+
 // Wait for this wave's outstanding vector-memory loads (which includes its direct LDS loads):
 // s_waitcnt vmcnt(0) in the gfx9 encoding (vmcnt bits 3:0 and 15:14 = 0, expcnt 6:4 and lgkmcnt
 // 11:8 at their maxima, i.e. not waited on).

@@ -111,6 +111,39 @@ def test_edge_lengths(form, kind, dtype):
         _check(form, inp, 1e-6, C=16, tag=f"(edge L={L})")
 
 
+# chunk sizes that are multiples of 64 (bf16, d <= 64) run the resident kernel: one launch up to 256 rows,
+# row groups of 256 with carried group states beyond (ragged last groups, down to a single row)
+RESIDENT_L = [1, 63, 64, 65, 200, 256, 257, 300, 511, 512, 513, 777]
+
+
+@pytest.mark.parametrize("kind", [lin.LIT, lin.D, lin.S])
+@pytest.mark.parametrize("C", [64, 128, 256])
+def test_chunk_resident_lengths(kind, C):
+    for L in RESIDENT_L:
+        inp = lin.random_inputs(1, 2, L, 64, kind, dtype="bf16", seed=400 + L)
+        _check("chunk", inp, 1e-6, C=C, tag=f"(resident L={L})")
+
+
+@pytest.mark.parametrize("d", [16, 32])
+def test_chunk_resident_head_dims(d):
+    for kind in (lin.LIT, lin.D, lin.S):
+        for L in (100, 300, 600):
+            inp = lin.random_inputs(1, 2, L, d, kind, dtype="bf16", seed=500 + d + L)
+            _check("chunk", inp, 1e-6, C=64, tag=f"(resident d={d} L={L})")
+
+
+def test_chunk_resident_decay_to_zero():
+    """log(lambda) = -1000 across row groups: every carried state vanishes and y_i = v_i."""
+    import torch
+    inp = lin.random_inputs(1, 2, 600, 64, lin.S, dtype="bf16", seed=302)
+    q, k, v, _ = to_device(inp)
+    ll = torch.full((1, 2, 600), -1000.0, dtype=torch.float32, device="cuda")
+    y, _ = run_form("chunk", q, k, v, ll, lin.S, 0.0, C=64)
+    vv = v.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(y))
+    assert np.max(np.abs(y - vv)) <= 2e-2 * np.sqrt(np.mean(vv ** 2))
+
+
 @pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
