@@ -459,8 +459,10 @@ constexpr size_t rnn_lds() {
 }
 
 // Work splits (column group width, waves per direction) per head dimension, from the fewest waves
-// (least per-token overhead) to the most; the first giving at least 1.5 waves per SIMD is used (measured
-// on LION-D, d = 64: B64 H12 L197 runs best on 64 x 2, B8 H12 L4097 on 32 x 4).
+// (least per-token overhead) to the most; the first giving at least 1.5 waves per SIMD is used, or 3
+// per SIMD for splits with 32 state rows per lane (their register count allows no more than 3).
+// Measured at d = 64: B64 H12 L197 runs best on 64 x 2, B32 H16 L512 and B64 H3 L197 on 64 x 4,
+// B8 H12 L4097 on 32 x 4.
 struct RnnSplit {
     int cw, nr;
 };
@@ -473,8 +475,10 @@ template <int D>
 int rnn_split(int B, int H) {
     const RnnSplit *sp = D == 16 ? kSplit16 : D == 32 ? kSplit32 : D == 64 ? kSplit64 : kSplit128;
     const int n = D == 16 ? 2 : D == 32 ? 3 : D == 64 ? 4 : 3;
-    for (int i = 0; i < n; ++i)
-        if ((long)B * H * (D / sp[i].cw) * 2 * sp[i].nr >= 1536) return i;
+    for (int i = 0; i < n; ++i) {
+        const int rw = D * sp[i].cw / (64 * sp[i].nr);
+        if ((long)B * H * (D / sp[i].cw) * 2 * sp[i].nr >= (rw >= 32 ? 3072 : 1536)) return i;
+    }
     return n - 1;
 }
 
