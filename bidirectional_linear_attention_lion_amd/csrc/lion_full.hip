@@ -88,9 +88,20 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
     const T *kg = reinterpret_cast<const T *>(p.k) + base * D;
     const T *vg = reinterpret_cast<const T *>(p.v) + base * D;
 
-    // stage 0 in flight while the prologue runs
-    stage_rows<D, T>(Kb, kg, 0, SK, L, wave, nw, lane);
+    // stage 0 in flight while the prologue runs.  When the whole sequence is one stage (and its key
+    // chunks fit 4 per thread), keys come through registers and phi is applied on the way into LDS.
+    const bool kreg = BF16 && p.nbuf == 1 && SK * RT::CPK <= 4 * nt;
+    u32x4 kx[4];
     stage_rows<D, T>(Vb, vg, 0, SK, L, wave, nw, lane);
+    if (kreg) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c16 = min(tid + u * nt, SK * RT::CPK - 1);
+            kx[u] = ld16(kg + (size_t)min(c16 / RT::CPK, L - 1) * D + (c16 % RT::CPK) * RT::VEC);
+        }
+    } else {
+        stage_rows<D, T>(Kb, kg, 0, SK, L, wave, nw, lane);
+    }
 
     if constexpr (KIND != kMaskLit)
         build_exponents<KIND>(E, scan_sh, p.ll, bh, p.H, L, Lpad, min(tile0 * 16, L - 1), tid, nt);
@@ -186,10 +197,35 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
         for (int ct = 0; ct < D / 16; ++ct) acc_o[qt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    if (kreg) {
+        // phi on the keys held in registers (rows at or past L written as zeros); the single stage is
+        // then complete after one barrier
+        wait_vm_all();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c16 = tid + u * nt, row = c16 / RT::CPK;
+            T x[RT::VEC];
+            __builtin_memcpy(x, &kx[u], 16);
+            float f[RT::VEC], ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < RT::VEC; ++e) {
+                f[e] = phi_pre<KIND>((float)x[e]);
+                ss += f[e] * f[e];
+            }
+            float scl = row < L ? 1.f : 0.f;
+            if constexpr (KIND == kMaskS) scl *= inv_norm(group_sum<RT::CPK>(ss));
+#pragma unroll
+            for (int e = 0; e < RT::VEC; ++e) x[e] = (T)(f[e] * scl);
+            if (c16 < SK * RT::CPK) __builtin_memcpy(Kb + RT::off(row, (c16 % RT::CPK) * RT::VEC), x, 16);
+        }
+        __syncthreads();
+    }
+
     for (int s = 0; s < nst; ++s) {
         const int buf = p.nbuf == 1 ? 0 : (s & 1);
         T *kbuf = Kb + (size_t)buf * SK * D;
         const T *vbuf = Vb + (size_t)buf * SK * D;
+        if (!kreg) {
         wait_vm_all();
         __syncthreads();                                     // stage s is in LDS; buffer s+1 is free
         if (s + 1 < nst) {
@@ -223,6 +259,7 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
             }
         }
         __syncthreads();
+        }
         if (wave_tiles == 0) continue;
 
         for (int h = 0; h < SK / kKB; ++h) {
