@@ -451,6 +451,338 @@ __global__ void __launch_bounds__(2 * NR * 64) __attribute__((amdgpu_waves_per_e
     }
 }
 
+// ---- pipelined variant --------------------------------------------------------------------------------
+// For grids of at most one workgroup per CU.  kHelp more waves take the per-block work off the
+// recurrence waves: while these run block b, the helpers reduce block b-1 (park, finish, store) and
+// stage block b+1 (phi, diagonal, scales, from rows loaded one block earlier), so one barrier per block
+// separates the roles and the recurrence waves never touch global memory.  Staging is triple-buffered
+// (b+1 is written while b is read and b-1 is still needed by its reduction), partials double-buffered.
+constexpr int kHelp = 8;
+
+template <int D, int CW, int NR>
+constexpr size_t rnn_pipe_lds() {
+    using Sh = RnnShape<D, CW, NR>;
+    const size_t dirf = 2 * ((size_t)kT * D + 16) + (size_t)kT * D + 4 * kT;
+    const size_t psz = 2 * (size_t)kT * Sh::NP * CW + 2 * (size_t)kT * Sh::NP;
+    return (6 * dirf + 2 * psz) * 4;
+}
+
+template <int D, int KIND, int CW, int NR, bool BF16>
+__global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnParams p) {
+    using T = std::conditional_t<BF16, __bf16, float>;
+    using Sh = RnnShape<D, CW, NR>;
+    constexpr int NS = Sh::NS, RW = Sh::RW, RB = Sh::RB, KV = Sh::KV, NG = Sh::NG, NP = Sh::NP;
+    constexpr int NTD = NR * 64;               // recurrence threads per direction
+    constexpr int NRT = 2 * NTD;               // recurrence threads
+    constexpr int NHT = kHelp * 64;            // helper threads
+    constexpr int TPT = D / 4;                 // staging threads per token (4 channels each)
+    constexpr int PAIRS = 2 * kT * TPT;        // staging units of a block, both directions
+    constexpr int PPT = (PAIRS + NHT - 1) / NHT;
+    constexpr int QKS = kT * D + 16;
+    constexpr int DIRF = 2 * QKS + kT * D + 4 * kT;
+    constexpr int PSZ = 2 * kT * NP * CW + 2 * kT * NP;
+    constexpr int RITEMS = 2 * kT * CW;        // reduction units of a block, both directions
+    constexpr int RITER = (RITEMS + NHT - 1) / NHT;
+    constexpr float kRenorm = 8.673617379884035e-19f;   // 2^-60
+    static_assert(RW >= 2 && RW <= 64 && RW % RB == 0, "rows per lane");
+    static_assert(PAIRS % 64 == 0, "staging units per wave");
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    float *S0 = reinterpret_cast<float *>(smem);
+    // staging buffer of block b, direction d; partial buffer of block b
+    auto stg_of = [&](int b, int d) { return S0 + ((b % 3) * 2 + d) * DIRF; };
+    auto part_of = [&](int b) { return S0 + 6 * DIRF + (b & 1) * PSZ; };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const bool helper = uniform(tid) >= NRT;
+    const int L = p.L;
+    const int bid = blockIdx.x, bh = bid / NG, cg = bid % NG;
+    const size_t base = (size_t)bh * L;
+    float *park = p.park + (size_t)bid * L * (CW + 1);
+    const int nblk = (L + kT - 1) / kT;
+
+    if (helper) {
+        // ================= helper waves: staging and reductions =================================
+        const int ht = tid - NRT;
+        const T *qg = reinterpret_cast<const T *>(p.q) + base * D;
+        const T *kg = reinterpret_cast<const T *>(p.k) + base * D;
+        const T *vg = reinterpret_cast<const T *>(p.v) + base * D;
+        const float lg_head = (KIND == kMaskD) ? p.ll[bh % p.H] * kLog2e : 0.f;
+        auto token_at = [&](int d, int s) { return d == 0 ? s : L - 1 - s; };
+        auto decay_at = [&](int d, int s) -> float {
+            if constexpr (KIND == kMaskLit) return 1.f;
+            else if constexpr (KIND == kMaskD) return fast_exp2(lg_head);
+            else {
+                const int td = d == 0 ? s : L - s;
+                return (s < L && td < L) ? fast_exp2(p.ll[base + td] * kLog2e) : 1.f;
+            }
+        };
+        using V4 = std::conditional_t<BF16, bf16x4, f32x4>;
+        V4 raw[PPT][3];
+        auto prefetch = [&](int b) {
+#pragma unroll
+            for (int u = 0; u < PPT; ++u) {
+                const int pr = ht + NHT * u;
+                const int d = pr / (kT * TPT), tl = (pr % (kT * TPT)) / TPT, c4 = (pr % TPT) * 4;
+                const size_t off = (size_t)token_at(d, min(b * kT + tl, L - 1)) * D + c4;
+                if (pr < PAIRS) {
+                    raw[u][0] = *reinterpret_cast<const V4 *>(qg + off);
+                    raw[u][1] = *reinterpret_cast<const V4 *>(kg + off);
+                    raw[u][2] = *reinterpret_cast<const V4 *>(vg + off);
+                }
+            }
+        };
+        auto stage = [&](int b) {
+#pragma unroll
+            for (int u = 0; u < PPT; ++u) {
+                const int pr0 = NHT * u;
+                if (pr0 + ht - lane >= PAIRS) break;   // whole wave past the end
+                const int pr = pr0 + ht;
+                const int d = pr / (kT * TPT), tl = (pr % (kT * TPT)) / TPT, c4 = (pr % TPT) * 4;
+                float *st = stg_of(b, d);
+                float *Qs = st, *Ks = Qs + QKS, *Vs = Ks + QKS, *sdiag = Vs + kT * D, *ksc = sdiag + kT,
+                      *ysc = ksc + kT, *mult = ysc + kT;
+                const int s = b * kT + tl;
+                const bool valid = s < L;
+                float xq[4], xk[4], sq = 0.f, sk = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    xq[e] = phi_pre<KIND>((float)raw[u][0][e]);
+                    xk[e] = phi_pre<KIND>((float)raw[u][1][e]);
+                    sq += xq[e] * xq[e];
+                    sk += xk[e] * xk[e];
+                }
+                float fq = valid ? 1.f : 0.f, fk = fq;
+                if constexpr (KIND == kMaskS) {
+                    fq *= inv_norm(group_sum<TPT>(sq));
+                    fk *= inv_norm(group_sum<TPT>(sk));
+                }
+                float dg = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    xq[e] *= fq;
+                    xk[e] *= fk;
+                    Qs[tl * D + c4 + e] = xq[e];
+                    Ks[tl * D + c4 + e] = xk[e];
+                    Vs[tl * D + c4 + e] = (float)raw[u][2][e];
+                    dg += xq[e] * xk[e];
+                }
+                dg = group_sum<TPT>(dg);
+                if (c4 == 0) {
+                    sdiag[tl] = dg;
+                    if constexpr (KIND != kMaskLit) {
+                        // replay the block's scale sequence up to this token (every leader derives the same)
+                        float lam = 1.f, mu = 1.f;
+                        for (int u2 = 0; u2 <= tl; ++u2) {
+                            const float l2 = lam * decay_at(d, b * kT + u2);
+                            if (l2 < kRenorm) {
+                                mu = l2;
+                                lam = 1.f;
+                            } else {
+                                mu = 1.f;
+                                lam = l2;
+                            }
+                        }
+                        ksc[tl] = 1.f / lam;
+                        ysc[tl] = lam;
+                        mult[tl] = mu;
+                    }
+                }
+            }
+        };
+        // parked partials block b's reduction needs: those parked at least two iterations before the
+        // reduction (partner step < s0 - kT) are loaded an iteration ahead, the rest when reduced
+        float pky[RITER], pkc[RITER];
+        auto prefetch_park = [&](int b, bool ahead) {
+            const int s0 = b * kT, nsteps = min(kT, L - s0);
+#pragma unroll
+            for (int it = 0; it < RITER; ++it) {
+                const int idx = ht + NHT * it;
+                const int d = idx / (kT * CW), tl = (idx % (kT * CW)) / CW, c2 = idx % CW;
+                if (idx < RITEMS && tl < nsteps) {
+                    const int s = s0 + tl, sp = L - 1 - s;
+                    if (ahead ? sp < s0 - kT : (sp < s0 && sp >= s0 - kT)) {
+                        const size_t row = (size_t)token_at(d, s) * (CW + 1);
+                        pky[it] = park[row + c2];
+                        pkc[it] = park[row + CW];
+                    }
+                }
+            }
+        };
+        auto reduce = [&](int b) {
+            const int s0 = b * kT, nsteps = min(kT, L - s0);
+            const float *Yp = part_of(b), *Cp = Yp + 2 * kT * NP * CW;
+            prefetch_park(b, false);
+#pragma unroll
+            for (int it = 0; it < RITER; ++it) {
+                const int idx = ht + NHT * it;
+                const int d = idx / (kT * CW), tl = (idx % (kT * CW)) / CW, c2 = idx % CW;
+                if (idx >= RITEMS || tl >= nsteps) continue;
+                const float *st = stg_of(b, d);
+                const float *Vs = st + 2 * QKS, *sdiag = Vs + kT * D, *ysc = sdiag + 2 * kT;
+                const int s = s0 + tl, sp = L - 1 - s;
+                const int t = token_at(d, s);
+                float y = 0.f, cs = 0.f;
+#pragma unroll
+                for (int g = 0; g < NP; ++g) {
+                    y += Yp[((d * kT + tl) * NP + g) * CW + c2];
+                    cs += Cp[(d * kT + tl) * NP + g];
+                }
+                if constexpr (KIND != kMaskLit) {
+                    y *= ysc[tl];
+                    cs *= ysc[tl];
+                }
+                float yo, co;
+                if (sp >= s0 + nsteps) {
+                    park[(size_t)t * (CW + 1) + c2] = y;
+                    if (c2 == 0) park[(size_t)t * (CW + 1) + CW] = cs;
+                    continue;
+                } else if (sp < s0) {
+                    yo = pky[it];
+                    co = pkc[it];
+                } else {
+                    if (d == 1) continue;
+                    const int tp = sp - s0;
+                    yo = 0.f;
+                    co = 0.f;
+#pragma unroll
+                    for (int g = 0; g < NP; ++g) {
+                        yo += Yp[((kT + tp) * NP + g) * CW + c2];
+                        co += Cp[(kT + tp) * NP + g];
+                    }
+                    if constexpr (KIND != kMaskLit) {
+                        const float ys = stg_of(b, 1)[2 * QKS + kT * D + 2 * kT + tp];   // backward scale of that token
+                        yo *= ys;
+                        co *= ys;
+                    }
+                }
+                // both visits included the diagonal term: remove it once
+                const float dg = sdiag[tl];
+                const float div = cs + co - dg + p.eps;
+                const float out = (y + yo - dg * Vs[tl * D + cg * CW + c2]) / div;
+                const size_t o = (base + t) * D + cg * CW + c2;
+                if (p.out_bf16)
+                    reinterpret_cast<__bf16 *>(p.y)[o] = f2bf(out);
+                else
+                    reinterpret_cast<float *>(p.y)[o] = out;
+                if (p.den_out && cg == 0 && c2 == 0) p.den_out[base + t] = div;
+            }
+        };
+
+        prefetch(0);
+        stage(0);
+        if (1 < nblk) prefetch(1);
+        __syncthreads();
+        for (int it = 0; it <= nblk; ++it) {
+            if (it >= 1) reduce(it - 1);
+            if (it + 1 < nblk) {
+                stage(it + 1);
+                if (it + 2 < nblk) prefetch(it + 2);
+            }
+            if (it < nblk) prefetch_park(it, true);
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ================= recurrence waves ================================================================
+    const int dir = uniform(tid / NTD);        // 0 forward, 1 backward
+    const int dt = tid % NTD;
+    const int rg = uniform(dt >> 6);
+    const int c = lane % CW, sub = lane / CW;
+    const int slice = rg * NS + sub;
+    const int rb = slice * RW;
+    const int col = cg * CW + c;
+
+    float S[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) S[i] = 0.f;
+    float z[KV], zmask[KV];
+#pragma unroll
+    for (int m = 0; m < KV; ++m) {
+        z[m] = 0.f;
+        zmask[m] = 16 * m + (lane & 15) < RW ? 1.f : 0.f;
+    }
+    float lam_end = 1.f;
+    __syncthreads();   // block 0 staged
+    for (int it = 0; it <= nblk; ++it) {
+        if (it < nblk) {
+            const int b = it, s0 = b * kT, nsteps = min(kT, L - s0);
+            const float *st = stg_of(b, dir);
+            const float *Qs = st, *Ks = Qs + QKS, *Vs = Ks + QKS, *ksc = Vs + kT * D + kT, *ysc = ksc + kT,
+                        *mult = ysc + kT;
+            float *Yp = part_of(b), *Cp = Yp + 2 * kT * NP * CW;
+            if constexpr (KIND != kMaskLit) {
+#pragma unroll
+                for (int i = 0; i < RW; ++i) S[i] *= lam_end;
+#pragma unroll
+                for (int m = 0; m < KV; ++m) z[m] *= lam_end;
+            }
+            const float kscv = KIND != kMaskLit ? ksc[lane & 15] : 1.f;
+            const float multv = KIND != kMaskLit ? mult[lane & 15] : 1.f;
+            const unsigned rmask = KIND != kMaskLit ? (unsigned)(__ballot(multv != 1.f) & 0xFFFFu) : 0u;
+            auto lane_val = [](float v, int i) {
+                return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i));
+            };
+            struct Tok {
+                float kb[KV], qb[KV], vj;
+            };
+            auto load_tok = [&](int tl) {
+                Tok x;
+                const float *qrow = Qs + tl * D + rb + (lane & 15);
+                const float *krow = Ks + tl * D + rb + (lane & 15);
+#pragma unroll
+                for (int m = 0; m < KV; ++m) {
+                    x.kb[m] = krow[16 * m];
+                    x.qb[m] = qrow[16 * m];
+                }
+                x.vj = Vs[tl * D + col];
+                return x;
+            };
+            float cpv[kT];
+            Tok cur = load_tok(0);
+#pragma unroll
+            for (int tl = 0; tl < kT; ++tl) {
+                cpv[tl] = 0.f;
+                if (tl >= nsteps) continue;
+                Tok nxt;
+                if (tl + 1 < kT) nxt = load_tok(tl + 1);
+                float ks = 1.f;
+                if constexpr (KIND != kMaskLit) {
+                    ks = lane_val(kscv, tl);
+                    if (rmask & (1u << tl)) {
+                        const float mu = lane_val(multv, tl);
+#pragma unroll
+                        for (int i = 0; i < RW; ++i) S[i] *= mu;
+#pragma unroll
+                        for (int m = 0; m < KV; ++m) z[m] *= mu;
+                    }
+                }
+                float y0 = 0.f, y1 = 0.f, cp = 0.f;
+#pragma unroll
+                for (int m = 0; m < KV; ++m) {
+                    const float kb = cur.kb[m] * ks, qb = cur.qb[m];
+                    dpp_update<RB>(S + RB * m, kb, cur.vj);
+                    dpp_dot<RB>(y0, y1, qb, S + RB * m);
+                    z[m] += kb;
+                    cp += zmask[m] * qb * z[m];
+                }
+                cpv[tl] = cp;
+                Yp[((dir * kT + tl) * NP + slice) * CW + c] = y0 + y1;
+                if (tl + 1 < kT) cur = nxt;
+            }
+            if constexpr (KIND != kMaskLit) lam_end = ysc[nsteps - 1];
+#pragma unroll
+            for (int tl = 0; tl < kT; ++tl) cpv[tl] = row16_sum(cpv[tl]);
+            if (c == 0) {
+#pragma unroll
+                for (int tl = 0; tl < kT; ++tl) Cp[(dir * kT + tl) * NP + slice] = cpv[tl];
+            }
+        }
+        __syncthreads();
+    }
+}
+
 template <int D, int CW, int NR>
 constexpr size_t rnn_lds() {
     using Sh = RnnShape<D, CW, NR>;
@@ -496,12 +828,23 @@ hipError_t launch_split(const AttnArgs &a, hipStream_t stream) {
     p.out_bf16 = a.out_bf16 ? 1 : 0;
     p.den_out = a.den_out;
     p.park = reinterpret_cast<float *>(a.workspace);
+    const unsigned grid = (unsigned)(a.B * a.H * (D / CW));
+    constexpr size_t plds = rnn_pipe_lds<D, CW, NR>();
+    if constexpr (plds <= kLdsPerWorkgroup) {
+        if (grid <= 256) {   // one workgroup per CU: the pipelined variant
+            if (plds > 64 * 1024)
+                (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&birnn_pipe_kernel<D, KIND, CW, NR, BF16>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
+            hipLaunchKernelGGL((birnn_pipe_kernel<D, KIND, CW, NR, BF16>), dim3(grid), dim3((2 * NR + kHelp) * 64), plds,
+                               stream, p);
+            return hipGetLastError();
+        }
+    }
     constexpr size_t lds = rnn_lds<D, CW, NR>();
     if (lds > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&birnn_kernel<D, KIND, CW, NR, BF16>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((birnn_kernel<D, KIND, CW, NR, BF16>), dim3(a.B * a.H * (D / CW)), dim3(2 * NR * 64), lds,
-                       stream, p);
+    hipLaunchKernelGGL((birnn_kernel<D, KIND, CW, NR, BF16>), dim3(grid), dim3(2 * NR * 64), lds, stream, p);
     return hipGetLastError();
 }
 
