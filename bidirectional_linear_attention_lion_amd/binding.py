@@ -11,6 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liblion_attn.so")
 
 MASK_LIT, MASK_D, MASK_S = 0, 1, 2
+CAUSAL = 4   # OR-ed into a mask kind: the causal (unidirectional) variant
 DTYPE_F32, DTYPE_BF16 = 0, 1
 FORM_FULL, FORM_CHUNK, FORM_BIRNN = 0, 1, 2
 _KINDS = {"lit": MASK_LIT, "d": MASK_D, "s": MASK_S}

@@ -26,8 +26,10 @@ int check_common(const void *q, const void *k, const void *v, const float *log_l
     if (!q || !k || !v || !y) return LION_ERR_INVALID;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LION_ERR_INVALID;
     if (den_out && !aligned16(den_out)) return LION_ERR_INVALID;
-    if (mask_kind != LION_MASK_LIT && mask_kind != LION_MASK_D && mask_kind != LION_MASK_S) return LION_ERR_INVALID;
-    if (mask_kind == LION_MASK_LIT ? log_lambda != nullptr : log_lambda == nullptr) return LION_ERR_INVALID;
+    if (mask_kind & ~(3 | LION_CAUSAL)) return LION_ERR_INVALID;
+    const int kind = mask_kind & 3;
+    if (kind != LION_MASK_LIT && kind != LION_MASK_D && kind != LION_MASK_S) return LION_ERR_INVALID;
+    if (kind == LION_MASK_LIT ? log_lambda != nullptr : log_lambda == nullptr) return LION_ERR_INVALID;
     if (log_lambda && !aligned16(log_lambda)) return LION_ERR_INVALID;
     if (!(eps >= 0.f) || !isfinite(eps)) return LION_ERR_INVALID;
     if (B < 1 || H < 1 || L < 1 || d < 1) return LION_ERR_INVALID;
@@ -46,7 +48,8 @@ lion::AttnArgs make_args(const void *q, const void *k, const void *v, const floa
     a.k = k;
     a.v = v;
     a.log_lambda = log_lambda;
-    a.kind = mask_kind;
+    a.kind = mask_kind & 3;
+    a.causal = (mask_kind & LION_CAUSAL) != 0;
     a.eps = eps;
     a.B = B;
     a.H = H;

@@ -11,6 +11,7 @@ struct AttnArgs {
     const void *q, *k, *v;      // [B, H, L, d], bf16 or fp32
     const float *log_lambda;    // NULL (LIT), [H] (D), [B, H, L] (S)
     int kind;                   // 0 LIT, 1 D, 2 S
+    bool causal;                // keys after the query masked out (the forward recurrence alone)
     float eps;
     int B, H, L, d;
     bool in_bf16;               // element type of q, k, v

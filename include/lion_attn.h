@@ -32,7 +32,8 @@
  *                  LION_MASK_LIT: must be NULL (lambda = 1);
  *                  LION_MASK_D:   [H]        one decay per head;
  *                  LION_MASK_S:   [B, H, L]  one decay per token (entry 0 of each row never enters).
- *   mask_kind    LION_MASK_LIT / LION_MASK_D / LION_MASK_S; it also selects phi:
+ *   mask_kind    LION_MASK_LIT / LION_MASK_D / LION_MASK_S, optionally | LION_CAUSAL (keys after
+ *                the query are masked out); the kind also selects phi:
  *                  LIT: phi(x) = elu(x) + 1;  D: phi(x) = x;  S: phi = silu(x) / ||silu(x)||_2 over the
  *                  d channels of the token (an all-zero silu vector gives phi = 0).
  *   eps          >= 0 and finite, added to every row sum.
@@ -83,6 +84,11 @@ extern "C" {
 #endif
 
 enum lion_mask_kind { LION_MASK_LIT = 0, LION_MASK_D = 1, LION_MASK_S = 2 };
+/* OR-ed into mask_kind: the causal (unidirectional) variant, M_ij = 0 for j > i -- the forward
+ * recurrence S_i = lambda_i S_{i-1} + phi(k_i) v_i^T alone, causal linear attention (reply "1:
+ * Recurrence Form of Linear Attention", Eq. 4a-4c) with the kind's decay (LION-S 1D for
+ * single-directional generation: reply item 5, "Is this method limited to bidirectional models?"). */
+enum { LION_CAUSAL = 4 };
 enum lion_dtype { LION_DTYPE_F32 = 0, LION_DTYPE_BF16 = 1 };
 enum lion_form { LION_FORM_FULL = 0, LION_FORM_CHUNK = 1, LION_FORM_BIRNN = 2 };
 enum lion_status {

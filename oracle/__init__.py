@@ -22,6 +22,7 @@ SRC = os.path.join(HERE, "lion_oracle.c")
 LIB = os.path.join(HERE, "liblion_oracle.so")
 
 MASK_LIT, MASK_D, MASK_S = 0, 1, 2
+CAUSAL = 4   # OR-ed into a kind: keys after the query masked out (see lion_oracle.c)
 KIND_NAMES = {"lit": MASK_LIT, "d": MASK_D, "s": MASK_S}
 
 CFLAGS = ["-O2", "-fno-fast-math", "-fPIC", "-shared", "-fopenmp", "-std=c99", "-Wall", "-Wextra"]

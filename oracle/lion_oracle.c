@@ -33,6 +33,13 @@
  *   - the L2 normalisation of silu has no epsilon; an all-zero silu vector maps to phi = 0.
  *   - LION-D uses phi = identity.
  *
+ * The causal (unidirectional) variant, mask_kind | ORACLE_CAUSAL, keeps only the keys at or before
+ * the query: M_ij = 0 for j > i.  What remains is the forward recurrence alone -- causal linear
+ * attention S_i = S_{i-1} + k_i v_i^T, z_i = z_{i-1} + k_i, y_i = q_i^T S_i / q_i^T z_i [RB, reply "1:
+ * Recurrence Form of Linear Attention", Eq. 4a-4c] with the kind's decay, which the pages use for
+ * single-directional generation (LION-S 1D) [RB, item 5 "Is this method limited to bidirectional
+ * models?"].
+ *
  * All arithmetic is IEEE double; build with plain -O2 (no fast-math), so the order of every sum is
  * the loop order written here.
  */
@@ -43,6 +50,7 @@
 #define ORACLE_MASK_LIT 0
 #define ORACLE_MASK_D 1
 #define ORACLE_MASK_S 2
+#define ORACLE_CAUSAL 4
 
 #define ORACLE_OK 0
 #define ORACLE_EINVAL (-1)
@@ -76,13 +84,14 @@ static void phi_row(int kind, const double *x, int d, double *out)
 
 /* Row i of the mask from the per-token decays lam[0..L-1] of one (batch, head):
  *   M_ii = 1,   M_ij = lam[i+1] * ... * lam[j]   (j > i),   M_ij = lam[j+1] * ... * lam[i]   (j < i).
- * lam[0] never enters.  Built as running products walking outward from the diagonal. */
-static void mask_row(const double *lam, int L, int i, double *m)
+ * lam[0] never enters.  Built as running products walking outward from the diagonal.  Causal:
+ * M_ij = 0 for j > i. */
+static void mask_row(const double *lam, int L, int i, int causal, double *m)
 {
     int j;
     m[i] = 1.0;
     for (j = i + 1; j < L; ++j)
-        m[j] = m[j - 1] * lam[j];
+        m[j] = causal ? 0.0 : m[j - 1] * lam[j];
     for (j = i - 1; j >= 0; --j)
         m[j] = m[j + 1] * lam[j + 1];
 }
@@ -149,7 +158,7 @@ int lion_oracle_mask_f64(const double *lam, int L, double *M)
     if (!lam || !M || L < 1)
         return ORACLE_EINVAL;
     for (i = 0; i < L; ++i)
-        mask_row(lam, L, i, M + (size_t)i * L);
+        mask_row(lam, L, i, 0, M + (size_t)i * L);
     return ORACLE_OK;
 }
 
@@ -159,13 +168,11 @@ int lion_oracle_mask_f64(const double *lam, int L, double *M)
  *   absnum (nullable): [B, H, L, d]   absden (nullable): [B, H, L]
  * Independent (batch, head) problems are spread over OpenMP threads; each row's sums run in
  * index order. */
-int lion_oracle_attn_f64(const double *phq, const double *phk, const double *v, const double *lam, double eps, int B,
-                         int H, int L, int d, double *y, double *den, double *absnum, double *absden)
+static int attn_all(const double *phq, const double *phk, const double *v, const double *lam, double eps, int causal,
+                    int B, int H, int L, int d, double *y, double *den, double *absnum, double *absden)
 {
     long bh, nbh;
     int err = 0;
-    if (!phq || !phk || !v || !lam || !y || B < 1 || H < 1 || L < 1 || d < 1 || !(eps >= 0.0))
-        return ORACLE_EINVAL;
     nbh = (long)B * H;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
     for (bh = 0; bh < nbh; ++bh) {
@@ -179,7 +186,7 @@ int lion_oracle_attn_f64(const double *phq, const double *phk, const double *v, 
         } else {
             for (i = 0; i < L; ++i) {
                 size_t row = base + (size_t)i;
-                mask_row(lam + base, L, i, m);
+                mask_row(lam + base, L, i, causal, m);
                 attn_row(phq + row * d, phk + base * d, v + base * d, m, L, d, eps, num, anum, y + row * d,
                          den ? den + row : NULL, absnum ? absnum + row * d : NULL, absden ? absden + row : NULL);
             }
@@ -189,6 +196,14 @@ int lion_oracle_attn_f64(const double *phq, const double *phk, const double *v, 
         free(anum);
     }
     return err ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
+int lion_oracle_attn_f64(const double *phq, const double *phk, const double *v, const double *lam, double eps, int B,
+                         int H, int L, int d, double *y, double *den, double *absnum, double *absden)
+{
+    if (!phq || !phk || !v || !lam || !y || B < 1 || H < 1 || L < 1 || d < 1 || !(eps >= 0.0))
+        return ORACLE_EINVAL;
+    return attn_all(phq, phk, v, lam, eps, 0, B, H, L, d, y, den, absnum, absden);
 }
 
 /* Per-token decays of one (batch, head) from the log-decay argument as the GPU library takes it:
@@ -217,6 +232,8 @@ int lion_oracle_full_f64(const double *q, const double *k, const double *v, cons
     double *phq, *phk, *lam;
     long bh;
     int rc;
+    int causal = (mask_kind & ORACLE_CAUSAL) != 0;
+    mask_kind &= ~ORACLE_CAUSAL;
     if (!q || !k || !v || !y || B < 1 || H < 1 || L < 1 || d < 1 || !(eps >= 0.0) ||
         mask_kind < ORACLE_MASK_LIT || mask_kind > ORACLE_MASK_S || (mask_kind != ORACLE_MASK_LIT && !log_lambda))
         return ORACLE_EINVAL;
@@ -235,7 +252,7 @@ int lion_oracle_full_f64(const double *q, const double *k, const double *v, cons
     lion_oracle_phi_f64(mask_kind, k, (long)nt, d, phk);
     for (bh = 0; bh < (long)B * H; ++bh)
         decays(mask_kind, log_lambda, H, L, bh, lam + (size_t)bh * L);
-    rc = lion_oracle_attn_f64(phq, phk, v, lam, eps, B, H, L, d, y, den, absnum, absden);
+    rc = attn_all(phq, phk, v, lam, eps, causal, B, H, L, d, y, den, absnum, absden);
     free(phq);
     free(phk);
     free(lam);
@@ -251,6 +268,8 @@ int lion_oracle_rows_f64(const double *q, const double *k, const double *v, cons
 {
     long r;
     int err = 0;
+    int causal = (mask_kind & ORACLE_CAUSAL) != 0;
+    mask_kind &= ~ORACLE_CAUSAL;
     if (!q || !k || !v || !y || !rows || nrows < 0 || B < 1 || H < 1 || L < 1 || d < 1 || !(eps >= 0.0) ||
         mask_kind < ORACLE_MASK_LIT || mask_kind > ORACLE_MASK_S || (mask_kind != ORACLE_MASK_LIT && !log_lambda))
         return ORACLE_EINVAL;
@@ -275,7 +294,7 @@ int lion_oracle_rows_f64(const double *q, const double *k, const double *v, cons
                 phi_row(mask_kind, k + (base + j) * d, d, phk + (size_t)j * d);
             phi_row(mask_kind, q + (base + i) * d, d, phq);
             decays(mask_kind, log_lambda, H, L, bh, lam);
-            mask_row(lam, L, i, m);
+            mask_row(lam, L, i, causal, m);
             attn_row(phq, phk, v + base * d, m, L, d, eps, num, anum, y + (size_t)r * d, den ? den + r : NULL,
                      absnum ? absnum + (size_t)r * d : NULL, absden ? absden + r : NULL);
         }

@@ -335,6 +335,70 @@ def pin_abs_sums(lib):
     assert idx.size == L
 
 
+# ---------------------------------------------------------------------------------------------
+# the causal variant (keys after the query masked out) against the forward recurrence written out
+# here: causal linear attention S_i = S_{i-1} + k_i v_i^T, z_i = z_{i-1} + k_i, y_i = q_i^T S_i / q_i^T z_i
+# [RB, reply "1: Recurrence Form of Linear Attention", Eq. 4a-4c], with the decay lambda_i applied to
+# the carried state for LION-D and LION-S
+
+def _phi_ref(kind, x):
+    t = torch.from_numpy(x)
+    if kind == "lit":
+        return (F.elu(t, alpha=1.0) + 1.0).numpy()
+    if kind == "s":
+        return F.normalize(F.silu(t), p=2.0, dim=-1).numpy()
+    return x.copy()
+
+
+def _causal_recurrence(q, k, v, lam, eps):
+    L, d = q.shape
+    S = np.zeros((d, v.shape[1]))
+    z = np.zeros(d)
+    y = np.empty_like(v)
+    den = np.empty(L)
+    for i in range(L):
+        S = lam[i] * S + np.outer(k[i], v[i])
+        z = lam[i] * z + k[i]
+        den[i] = q[i] @ z + eps
+        y[i] = (q[i] @ S) / den[i]
+    return y, den
+
+
+def pin_causal_is_forward_recurrence(lib):
+    rng = np.random.default_rng(81)
+    B, H, L, d = 2, 2, 23, 5
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    for kind, ll in (("lit", None), ("d", np.log(rng.uniform(0.6, 0.99, H))),
+                     ("s", np.log(rng.uniform(0.3, 1.0, (B, H, L))))):
+        y, den = oracle.full(q, k, v, ll, oracle.KIND_NAMES[kind] | oracle.CAUSAL, 1e-6, lib_path=lib)
+        for b in range(B):
+            for h in range(H):
+                lam = np.ones(L) if kind == "lit" else np.exp(ll[h] if kind == "d" else ll[b, h]) * np.ones(L)
+                yr, dr = _causal_recurrence(_phi_ref(kind, q[b, h]), _phi_ref(kind, k[b, h]), v[b, h], lam, 1e-6)
+                _close(y[b, h], yr, 1e-12, f"causal {kind} b{b} h{h} vs forward recurrence")
+                _close(den[b, h], dr, 1e-12, f"causal {kind} den b{b} h{h}")
+
+
+def pin_causal_ends(lib):
+    """The last row sees every key either way; the first row sees only itself."""
+    rng = np.random.default_rng(82)
+    B, H, L, d = 1, 3, 17, 4
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    ll = np.log(rng.uniform(0.4, 1.0, (B, H, L)))
+    yc, dc = oracle.full(q, k, v, ll, oracle.MASK_S | oracle.CAUSAL, 1e-3, lib_path=lib)
+    yb, db = oracle.full(q, k, v, ll, oracle.MASK_S, 1e-3, lib_path=lib)
+    _close(yc[:, :, -1], yb[:, :, -1], 1e-14, "causal last row vs bidirectional")
+    pq, pk = _phi_ref("s", q[0]), _phi_ref("s", k[0])
+    s00 = np.einsum("hc,hc->h", pq[:, 0], pk[:, 0])
+    _close(yc[0, :, 0], v[0, :, 0] * (s00 / (s00 + 1e-3))[:, None], 1e-14, "causal first row")
+    # and the causal rows never depend on later keys: change the last key and value
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, -1] += 1.0
+    v2[:, :, -1] -= 2.0
+    y2, _ = oracle.full(q, k2, v2, ll, oracle.MASK_S | oracle.CAUSAL, 1e-3, lib_path=lib)
+    assert np.array_equal(y2[:, :, :-1], yc[:, :, :-1]), "causal rows depend on a later token"
+
+
 ALL_PINS = [
     pin_phi_lit_is_elu_plus_one,
     pin_phi_s_is_normalised_silu,
@@ -353,4 +417,6 @@ ALL_PINS = [
     pin_forms_equivalent,
     pin_rows_entry_matches_full,
     pin_abs_sums,
+    pin_causal_is_forward_recurrence,
+    pin_causal_ends,
 ]

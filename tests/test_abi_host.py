@@ -67,6 +67,8 @@ INVALID_CASES = [
     ("null q", dict(q=None)), ("null k", dict(k=None)), ("null v", dict(v=None)), ("null y", dict(y=None)),
     ("misaligned q", dict(q=MIS)), ("misaligned y", dict(y=MIS)), ("misaligned den", dict(den=MIS)),
     ("bad kind", dict(kind=3)), ("negative kind", dict(kind=-1)),
+    ("unknown flag bit", dict(kind=8)), ("causal bad kind", dict(kind=3 | 4)),
+    ("causal LIT with log_lambda", dict(kind=4, ll=P)), ("causal S without log_lambda", dict(kind=2 | 4, ll=None)),
     ("LIT with log_lambda", dict(kind=0, ll=P)), ("D without log_lambda", dict(kind=1, ll=None)),
     ("S without log_lambda", dict(kind=2, ll=None)), ("misaligned log_lambda", dict(kind=1, ll=MIS)),
     ("negative eps", dict(eps=-1e-3)), ("nan eps", dict(eps=float("nan"))), ("inf eps", dict(eps=float("inf"))),

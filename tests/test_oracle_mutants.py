@@ -15,7 +15,9 @@ import oracle
 from tests.oracle_pins import ALL_PINS
 
 MUTANTS = [
-    ("mask forward index shifted", "m[j] = m[j - 1] * lam[j];", "m[j] = m[j - 1] * lam[j - 1];"),
+    ("mask forward index shifted", "causal ? 0.0 : m[j - 1] * lam[j];", "causal ? 0.0 : m[j - 1] * lam[j - 1];"),
+    ("causal keeps later keys", "causal ? 0.0 : m[j - 1] * lam[j];", "m[j - 1] * lam[j];"),
+    ("causal masks earlier keys", "m[j] = m[j + 1] * lam[j + 1];", "m[j] = causal ? 0.0 : m[j + 1] * lam[j + 1];"),
     ("mask backward index shifted", "m[j] = m[j + 1] * lam[j + 1];", "m[j] = m[j + 1] * lam[j];"),
     ("mask diagonal not one", "m[i] = 1.0;", "m[i] = 0.5;"),
     ("eps dropped", "div = den + eps;", "div = den;"),
