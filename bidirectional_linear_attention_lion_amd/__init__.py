@@ -5,6 +5,7 @@ in ``include/lion_attn.h``); this package only marshals torch tensors into that 
 no CPU fallback: if the library is missing, every call raises.
 """
 from .binding import (  # noqa: F401
+    CAUSAL,
     FORM_BIRNN,
     FORM_CHUNK,
     FORM_FULL,

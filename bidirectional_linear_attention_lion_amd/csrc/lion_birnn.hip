@@ -27,6 +27,10 @@
 // an earlier block is finished with the partial parked then, a token whose other visit comes in a later
 // block is parked (in the caller's workspace), and a token both directions visit within this block is
 // finished directly.  The first visitor removes the diagonal, so it is counted once.
+//
+// Causal variant (keys after the query masked out): the forward recurrence alone, each token finished
+// from its own forward partial, y_t = q_t^T S^F_t / (q_t^T z^F_t + eps) -- its diagonal term is
+// counted once already, and nothing is parked.  The plain kernel then runs only the forward waves.
 #include <type_traits>
 
 #include "lion_device.h"
@@ -46,6 +50,7 @@ struct RnnParams {
     int out_bf16;
     float *den_out;
     float *park;   // [B*H][groups][L][CW+1]: one direction's partial (y, c) of each token
+    int causal;    // forward direction only
 };
 
 // ---- DPP broadcast fused multiply-adds ---------------------------------------------------------------
@@ -289,6 +294,9 @@ __global__ void __launch_bounds__(2 * NR * 64) __attribute__((amdgpu_waves_per_e
 
     prefetch(0);
     stage(0);
+    // the 16 floats after the last token's q and k rows, which lanes past the last slice read (and mask
+    // out by multiplying with zero), must hold finite values: zeros
+    if (dt < 32) stg[(dt < 16 ? 0 : QKS) + kT * D + (dt & 15)] = 0.f;
     __syncthreads();
 
     for (int b = 0; b < nblk; ++b) {
@@ -386,7 +394,7 @@ __global__ void __launch_bounds__(2 * NR * 64) __attribute__((amdgpu_waves_per_e
             if (idx < nsteps * CW) {
                 const int tl = idx / CW, c2 = idx % CW;
                 const int s = s0 + tl;
-                if (L - 1 - s < s0) {
+                if (!p.causal && L - 1 - s < s0) {
                     const size_t row = (size_t)token_at(s) * (CW + 1);
                     pky[it] = park[row + c2];
                     pkc[it] = park[row + CW];
@@ -411,8 +419,10 @@ __global__ void __launch_bounds__(2 * NR * 64) __attribute__((amdgpu_waves_per_e
                 y *= ys;
                 cs *= ys;
             }
-            float yo, co;
-            if (sp >= s0 + nsteps) {
+            float yo, co, dg = 0.f;
+            if (p.causal) {
+                yo = co = 0.f;                            // the forward visit alone
+            } else if (sp >= s0 + nsteps) {
                 park[(size_t)t * (CW + 1) + c2] = y;
                 if (c2 == 0) park[(size_t)t * (CW + 1) + CW] = cs;
                 continue;
@@ -436,7 +446,7 @@ __global__ void __launch_bounds__(2 * NR * 64) __attribute__((amdgpu_waves_per_e
                 }
             }
             // both visits included the diagonal term: remove it once
-            const float dg = sdiag[tl];
+            if (!p.causal) dg = sdiag[tl];
             const float div = cs + co - dg + p.eps;
             const float out = (y + yo - dg * Vs[tl * D + cg * CW + c2]) / div;
             const size_t o = (base + t) * D + cg * CW + c2;
@@ -525,7 +535,7 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                 const int pr = ht + NHT * u;
                 const int d = pr / (kT * TPT), tl = (pr % (kT * TPT)) / TPT, c4 = (pr % TPT) * 4;
                 const size_t off = (size_t)token_at(d, min(b * kT + tl, L - 1)) * D + c4;
-                if (pr < PAIRS) {
+                if (pr < PAIRS && !(p.causal && d == 1)) {
                     raw[u][0] = *reinterpret_cast<const V4 *>(qg + off);
                     raw[u][1] = *reinterpret_cast<const V4 *>(kg + off);
                     raw[u][2] = *reinterpret_cast<const V4 *>(vg + off);
@@ -539,6 +549,7 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                 if (pr0 + ht - lane >= PAIRS) break;   // whole wave past the end
                 const int pr = pr0 + ht;
                 const int d = pr / (kT * TPT), tl = (pr % (kT * TPT)) / TPT, c4 = (pr % TPT) * 4;
+                if (p.causal && d == 1) break;        // wave-uniform: kT * TPT is a multiple of 64
                 float *st = stg_of(b, d);
                 float *Qs = st, *Ks = Qs + QKS, *Vs = Ks + QKS, *sdiag = Vs + kT * D, *ksc = sdiag + kT,
                       *ysc = ksc + kT, *mult = ysc + kT;
@@ -599,7 +610,7 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
             for (int it = 0; it < RITER; ++it) {
                 const int idx = ht + NHT * it;
                 const int d = idx / (kT * CW), tl = (idx % (kT * CW)) / CW, c2 = idx % CW;
-                if (idx < RITEMS && tl < nsteps) {
+                if (idx < RITEMS && tl < nsteps && !p.causal) {
                     const int s = s0 + tl, sp = L - 1 - s;
                     if (ahead ? sp < s0 - kT : (sp < s0 && sp >= s0 - kT)) {
                         const size_t row = (size_t)token_at(d, s) * (CW + 1);
@@ -617,7 +628,7 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
             for (int it = 0; it < RITER; ++it) {
                 const int idx = ht + NHT * it;
                 const int d = idx / (kT * CW), tl = (idx % (kT * CW)) / CW, c2 = idx % CW;
-                if (idx >= RITEMS || tl >= nsteps) continue;
+                if (idx >= RITEMS || tl >= nsteps || (p.causal && d == 1)) continue;
                 const float *st = stg_of(b, d);
                 const float *Vs = st + 2 * QKS, *sdiag = Vs + kT * D, *ysc = sdiag + 2 * kT;
                 const int s = s0 + tl, sp = L - 1 - s;
@@ -632,8 +643,10 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                     y *= ysc[tl];
                     cs *= ysc[tl];
                 }
-                float yo, co;
-                if (sp >= s0 + nsteps) {
+                float yo, co, dg = 0.f;
+                if (p.causal) {
+                    yo = co = 0.f;                        // the forward visit alone
+                } else if (sp >= s0 + nsteps) {
                     park[(size_t)t * (CW + 1) + c2] = y;
                     if (c2 == 0) park[(size_t)t * (CW + 1) + CW] = cs;
                     continue;
@@ -657,7 +670,7 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                     }
                 }
                 // both visits included the diagonal term: remove it once
-                const float dg = sdiag[tl];
+                if (!p.causal) dg = sdiag[tl];
                 const float div = cs + co - dg + p.eps;
                 const float out = (y + yo - dg * Vs[tl * D + cg * CW + c2]) / div;
                 const size_t o = (base + t) * D + cg * CW + c2;
@@ -672,6 +685,9 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
         prefetch(0);
         stage(0);
         if (1 < nblk) prefetch(1);
+        // zeros after the last token's q and k rows of every staging buffer (read by lanes past the last
+        // slice, which multiply them by zero: they must be finite)
+        if (ht < 6 * 32) S0[(ht / 32) * DIRF + (ht % 32 < 16 ? 0 : QKS) + kT * D + (ht & 15)] = 0.f;
         __syncthreads();
         for (int it = 0; it <= nblk; ++it) {
             if (it >= 1) reduce(it - 1);
@@ -705,8 +721,9 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
     }
     float lam_end = 1.f;
     __syncthreads();   // block 0 staged
+    const bool active = !(p.causal && dir == 1);
     for (int it = 0; it <= nblk; ++it) {
-        if (it < nblk) {
+        if (it < nblk && active) {
             const int b = it, s0 = b * kT, nsteps = min(kT, L - s0);
             const float *st = stg_of(b, dir);
             const float *Qs = st, *Ks = Qs + QKS, *Vs = Ks + QKS, *ksc = Vs + kT * D + kT, *ysc = ksc + kT,
@@ -804,12 +821,12 @@ constexpr RnnSplit kSplit64[] = {{64, 2}, {64, 4}, {32, 4}, {16, 4}};
 constexpr RnnSplit kSplit128[] = {{64, 4}, {32, 4}, {16, 4}};
 
 template <int D>
-int rnn_split(int B, int H) {
+int rnn_split(int B, int H, int dirs) {
     const RnnSplit *sp = D == 16 ? kSplit16 : D == 32 ? kSplit32 : D == 64 ? kSplit64 : kSplit128;
     const int n = D == 16 ? 2 : D == 32 ? 3 : D == 64 ? 4 : 3;
     for (int i = 0; i < n; ++i) {
         const int rw = D * sp[i].cw / (64 * sp[i].nr);
-        if ((long)B * H * (D / sp[i].cw) * 2 * sp[i].nr >= (rw >= 32 ? 3072 : 1536)) return i;
+        if ((long)B * H * (D / sp[i].cw) * dirs * sp[i].nr >= (rw >= 32 ? 3072 : 1536)) return i;
     }
     return n - 1;
 }
@@ -828,6 +845,7 @@ hipError_t launch_split(const AttnArgs &a, hipStream_t stream) {
     p.out_bf16 = a.out_bf16 ? 1 : 0;
     p.den_out = a.den_out;
     p.park = reinterpret_cast<float *>(a.workspace);
+    p.causal = a.causal ? 1 : 0;
     const unsigned grid = (unsigned)(a.B * a.H * (D / CW));
     constexpr size_t plds = rnn_pipe_lds<D, CW, NR>();
     if constexpr (plds <= kLdsPerWorkgroup) {
@@ -844,13 +862,15 @@ hipError_t launch_split(const AttnArgs &a, hipStream_t stream) {
     if (lds > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&birnn_kernel<D, KIND, CW, NR, BF16>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((birnn_kernel<D, KIND, CW, NR, BF16>), dim3(grid), dim3(2 * NR * 64), lds, stream, p);
+    // causal: the forward waves alone (threads of the backward direction would have nothing to do)
+    hipLaunchKernelGGL((birnn_kernel<D, KIND, CW, NR, BF16>), dim3(grid), dim3((a.causal ? 1 : 2) * NR * 64), lds,
+                       stream, p);
     return hipGetLastError();
 }
 
 template <int D, int KIND, bool BF16>
 hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
-    const int i = rnn_split<D>(a.B, a.H);
+    const int i = rnn_split<D>(a.B, a.H, a.causal ? 1 : 2);
     if constexpr (D == 16) {
         return i == 0 ? launch_split<16, KIND, 16, 1, BF16>(a, stream) : launch_split<16, KIND, 16, 2, BF16>(a, stream);
     } else if constexpr (D == 32) {
@@ -890,7 +910,9 @@ hipError_t dispatch_d(const AttnArgs &a, hipStream_t stream) {
 
 template <int D>
 size_t workspace_t(const AttnArgs &a) {
-    const RnnSplit sp = (D == 16 ? kSplit16 : D == 32 ? kSplit32 : D == 64 ? kSplit64 : kSplit128)[rnn_split<D>(a.B, a.H)];
+    if (a.causal) return 0;   // nothing parked
+    const RnnSplit sp =
+        (D == 16 ? kSplit16 : D == 32 ? kSplit32 : D == 64 ? kSplit64 : kSplit128)[rnn_split<D>(a.B, a.H, 2)];
     return (size_t)a.B * a.H * (D / sp.cw) * a.L * (sp.cw + 1) * 4;
 }
 

@@ -15,6 +15,9 @@
 // Every exponent is <= 0, and all of them are differences of prefix sums taken inside one chunk, so
 // no long-range prefix sum (and its rounding) is ever formed.
 //
+// Causal variant (keys after the query masked out): only the forward states exist -- out_i keeps the
+// intra-chunk keys j <= i and the F_{c-1} term -- so no backward state is folded, scanned or applied.
+//
 // Three launches, each parallel over (batch, head, chunk):
 //   state: one workgroup per chunk stages the chunk's keys and values in LDS and folds them into Fl_c
 //          and Gl_c on the matrix cores;
@@ -56,6 +59,7 @@ struct ChunkParams {
     unsigned char *gs;     // backward states, [B*H*n] slots
     float *tot;            // log2 of each chunk's total decay, [B*H*n]
     int ng;                // resident path: row groups per (batch, head)
+    int causal;            // keys after the query masked out: forward states only
 };
 
 template <int D, bool BF16>
@@ -264,7 +268,7 @@ __global__ void __launch_bounds__(state_waves(D) * 64) chunk_state_kernel(ChunkP
                         }
                 }
                 sf[u] = mfma_bf16(a, bf, sf[u]);
-                sg[u] = mfma_bf16(a, bg, sg[u]);
+                if (!p.causal) sg[u] = mfma_bf16(a, bg, sg[u]);
             } else {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
@@ -274,14 +278,14 @@ __global__ void __launch_bounds__(state_waves(D) * 64) chunk_state_kernel(ChunkP
                         const float a = Ks[RT::off(row, 16 * nt + r)];
                         const float vv = ct < NDT ? Vs[RT::off(row, 16 * ct + r)] : (r == 0 ? 1.f : 0.f);
                         sf[u] = mfma_f32(a, wf[t][e] * vv, sf[u]);
-                        sg[u] = mfma_f32(a, wg[t][e] * vv, sg[u]);
+                        if (!p.causal) sg[u] = mfma_f32(a, wg[t][e] * vv, sg[u]);
                     }
             }
         }
     }
 
     // store: value tiles in register layout, the row-sum column (hi + lo columns) as fp32
-    const bool want_f = c < n - 1, want_g = c > 0;
+    const bool want_f = c < n - 1, want_g = c > 0 && !p.causal;
     unsigned char *fslot = p.fs + (size_t)bid * Cf::SLOT;
     unsigned char *gslot = p.gs + (size_t)bid * Cf::SLOT;
 #pragma unroll
@@ -338,7 +342,7 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(ChunkParams p)
     const int bid = blockIdx.x;
     const int blk = bid % NBLK, dir = (bid / NBLK) & 1, bh = bid / (2 * NBLK);
     const int vi = blk * kScanThreads + (int)threadIdx.x;
-    if (vi >= NV) return;   // this kernel has no barriers
+    if (vi >= NV || (p.causal && dir == 1)) return;   // this kernel has no barriers
     const bool zpart = vi >= NVV;
     const size_t off = zpart ? Cf::VBYTES + (size_t)(vi - NVV) * 16 : (size_t)vi * 16;
     unsigned char *base = (dir == 0 ? p.fs : p.gs) + (size_t)bh * n * Cf::SLOT + off;
@@ -419,7 +423,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
     stage_rows<D, T>(Vs, reinterpret_cast<const T *>(p.v) + base * D, cs, rows, L, wave, NW, lane);
     if constexpr (BF16) {
         if (c > 0) stage_flat(Fsm, p.fs + (size_t)(bid - 1) * Cf::SLOT, (int)(Cf::SLOT / 1024), wave, NW, lane);
-        if (c < n - 1) stage_flat(Gsm, p.gs + (size_t)(bid + 1) * Cf::SLOT, (int)(Cf::SLOT / 1024), wave, NW, lane);
+        if (c < n - 1 && !p.causal)
+            stage_flat(Gsm, p.gs + (size_t)(bid + 1) * Cf::SLOT, (int)(Cf::SLOT / 1024), wave, NW, lane);
     }
 
     float lgD = 0.f;
@@ -495,7 +500,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
     // ---- inter-chunk terms: F_{c-1} on exp(A_i - A_{e_{c-1}}) q_i, G_{c+1} on exp(A_{e_c} - A_i) q_i ----
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-        if (which == 0 ? c == 0 : c == n - 1) continue;
+        if (which == 0 ? c == 0 : (c == n - 1 || p.causal)) continue;
         const unsigned char *slot;
         if constexpr (BF16) slot = which == 0 ? Fsm : Gsm;
         else slot = which == 0 ? p.fs + (size_t)(bid - 1) * Cf::SLOT : p.gs + (size_t)(bid + 1) * Cf::SLOT;
@@ -564,10 +569,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
         phi_rows<D, KIND, T>(Ks, rows, tid, NT);
         __syncthreads();
     }
+    // causal: the last query row of this wave's tiles bounds the keys it needs
+    const int wlast = 16 * (wave + NW * ((tiles - 1 - wave) / NW)) + 15;
     for (int h = 0; h < rows / kKB; ++h) {
         const int j0 = h * kKB;
         const bool partial = j0 + kKB > cn;
         if (wave >= tiles) break;
+        if (p.causal && j0 > wlast) break;
         bf16x8 vfr[BF16 ? NDT : 1];
         if constexpr (BF16) {
 #pragma unroll
@@ -624,6 +632,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
                     float pe = sa[t][e];
                     if constexpr (KIND != kMaskLit) pe *= fast_exp2(-__builtin_fabsf(Ei[qt] - Ej[t][e]));
                     if (partial) pe = j0 + 16 * t + 4 * g + e < cn ? pe : 0.f;
+                    if (p.causal && j0 + 16 * t + 4 * g + e > 16 * (wave + NW * qt) + r) pe = 0.f;
                     den[qt] += pe;
                     pv[t][e] = pe;
                 }
@@ -798,7 +807,7 @@ __global__ void __launch_bounds__(ROWS / 16 * 64) chunk_fused_kernel(ChunkParams
     const int n = (L + C - 1) / C;                           // chunks of this group
     const int rows = cpad(L);
     const size_t base = (size_t)bh * p.L + (size_t)gi * ROWS;
-    const bool has_fin = gi > 0, has_gin = gi + 1 < ng;
+    const bool has_fin = gi > 0, has_gin = gi + 1 < ng && !p.causal;
 
     T *Ks = reinterpret_cast<T *>(smem);
     T *Vs = Ks + ROWS * D;
@@ -923,7 +932,7 @@ __global__ void __launch_bounds__(ROWS / 16 * 64) chunk_fused_kernel(ChunkParams
                 if (ct < NDT) {
                     const bf16x8 vv = tr_frag<D>(Vs, h, ct, r, g);
                     sf[u] = mfma_bf16(af, vv, sf[u]);
-                    if constexpr (KIND != kMaskLit) sg[u] = mfma_bf16(ag, vv, sg[u]);
+                    if (KIND != kMaskLit && !p.causal) sg[u] = mfma_bf16(ag, vv, sg[u]);
                 } else if constexpr (KIND == kMaskLit) {
                     sf[u] = mfma_bf16(kfr, ones, sf[u]);
                 } else {
@@ -938,7 +947,7 @@ __global__ void __launch_bounds__(ROWS / 16 * 64) chunk_fused_kernel(ChunkParams
                             bg[4 * t + e] = r == 0 ? gh : (r == 1 ? glo : f2bf(0.f));
                         }
                     sf[u] = mfma_bf16(kfr, bf, sf[u]);
-                    sg[u] = mfma_bf16(kfr, bg, sg[u]);
+                    if (!p.causal) sg[u] = mfma_bf16(kfr, bg, sg[u]);
                 }
             }
         }
@@ -950,7 +959,7 @@ __global__ void __launch_bounds__(ROWS / 16 * 64) chunk_fused_kernel(ChunkParams
             for (int which = 0; which < (KIND == kMaskLit ? 1 : 2); ++which) {
                 // LIT: the two local states coincide; one copy in the forward slot serves both.  The last
                 // chunk's forward and the first chunk's backward state are never read.
-                if (KIND != kMaskLit && (which == 0 ? c == n - 1 : c == 0)) continue;
+                if (KIND != kMaskLit && (which == 0 ? c == n - 1 : (c == 0 || p.causal))) continue;
                 const f32x4 sv = which == 0 ? sf[u] : sg[u];
                 T *slot = reinterpret_cast<T *>(which == 0 ? fslot(c) : gslot(c));
                 bf16x4 o;
@@ -1017,7 +1026,9 @@ __global__ void __launch_bounds__(ROWS / 16 * 64) chunk_fused_kernel(ChunkParams
     // other chunks' local states applied to the query; the decay between them scales the product
     f32x4 accz = f32x4{0.f, 0.f, 0.f, 0.f};   // row sums: rows 0 (high part) and 1 (low part) of a tile
     // chunks -1 and n stand for the carried states of all earlier and all later groups
-    for (int c2 = has_fin ? -1 : 0; c2 < (has_gin ? n + 1 : n); ++c2) {
+    // (causal: earlier chunks and groups only)
+    const int c2_end = p.causal ? c : (has_gin ? n + 1 : n);
+    for (int c2 = has_fin ? -1 : 0; c2 < c2_end; ++c2) {
         if (c2 == c) continue;
         float ex = c2 < c ? Ei : etot - Ei;
         for (int c3 = min(c, c2) + 1; c3 < max(c, c2); ++c3) ex += tot[c3];
@@ -1066,9 +1077,11 @@ __global__ void __launch_bounds__(ROWS / 16 * 64) chunk_fused_kernel(ChunkParams
     // rows 0 and 1 of the row-sum tile sit in lanes g = 0 (elements 0, 1); other lanes hold zeros
     den += accz[0] + accz[1];
 
-    // intra-chunk attention over the chunk's keys (padded keys are zero rows: no mask needed)
+    // intra-chunk attention over the chunk's keys (padded keys are zero rows: no mask needed; causal:
+    // keys after the query zeroed, sub-blocks wholly after the tile skipped)
     for (int h = cs / kKB; h < (cs + cpad(cn)) / kKB; ++h) {
         const int j0 = h * kKB;
+        if (p.causal && j0 > 16 * wave + 15) break;
         bf16x8 vfr[NDT], kf[2][NF];
 #pragma unroll
         for (int ct = 0; ct < NDT; ++ct) vfr[ct] = tr_frag<D>(Vs, h, ct, r, g);
@@ -1093,6 +1106,7 @@ __global__ void __launch_bounds__(ROWS / 16 * 64) chunk_fused_kernel(ChunkParams
             for (int e = 0; e < 4; ++e) {
                 float pe = sa[t][e];
                 if constexpr (KIND != kMaskLit) pe *= fast_exp2(-__builtin_fabsf(Ei - Ex(j0 + 16 * t + 4 * g + e, cs)));
+                if (p.causal && j0 + 16 * t + 4 * g + e > i) pe = 0.f;
                 den += pe;
                 pf[4 * t + e] = f2bf(pe);
             }
@@ -1205,7 +1219,7 @@ __global__ void __launch_bounds__(512) group_state_kernel(ChunkParams p) {
     __syncthreads();
 
     const int nt = wave & 3, dir = wave >> 2;
-    if (nt < NDT && (KIND != kMaskLit || dir == 0)) {
+    if (nt < NDT && (KIND != kMaskLit || dir == 0) && !(p.causal && dir == 1)) {
         const float etot = Ex(L - 1);
         bf16x8 ones;
 #pragma unroll
@@ -1234,7 +1248,7 @@ __global__ void __launch_bounds__(512) group_state_kernel(ChunkParams p) {
         }
 #pragma unroll
         for (int dd = 0; dd < 2; ++dd) {
-            if (KIND != kMaskLit && dd != dir) continue;
+            if ((KIND != kMaskLit && dd != dir) || (p.causal && dd == 1)) continue;
             T *dst = reinterpret_cast<T *>((dd == 0 ? p.fs : p.gs) + (size_t)blockIdx.x * F::SLOTK);
 #pragma unroll
             for (int ct = 0; ct < NDT; ++ct) {
@@ -1284,6 +1298,7 @@ __global__ void __launch_bounds__(kScanWave) group_scan_kernel(ChunkParams p) {
     const int lane = threadIdx.x;
     const int ng = p.ng;
     const int pc = blockIdx.x % NWV, dir = (blockIdx.x / NWV) & 1, bh = blockIdx.x / (2 * NWV);
+    if (p.causal && dir == 1) return;   // no barriers in this kernel
     const bool zu = pc == NWV - 1;
     // bytes this wave copies per group, and where they start in a state
     const int pbytes = zu ? F::NF * 128 : 1024;
@@ -1375,6 +1390,7 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
     p.fs = p.gs = nullptr;
     p.tot = nullptr;
     p.ng = 1;
+    p.causal = a.causal ? 1 : 0;
     if constexpr (BF16 && D <= 64) {
         if (fused_ok(a.L, a.C, D, BF16)) {
             const int rows = fused_rows(a.L, a.C);

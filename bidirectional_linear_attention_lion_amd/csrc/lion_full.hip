@@ -44,6 +44,7 @@ struct FullParams {
     int nblocks;       // grid size
     int sk;            // keys per stage (multiple of 32)
     int nbuf;          // 1: the whole sequence is one stage; 2: double-buffered stages
+    int causal;        // keys after the query masked out
 };
 
 template <int D, bool BF16>
@@ -221,14 +222,16 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
         __syncthreads();
     }
 
-    for (int s = 0; s < nst; ++s) {
+    // causal: stages wholly after the workgroup's last query row are never needed
+    const int nst_used = p.causal ? min(nst, (min((tile0 + p.tiles_per_wg) * 16, L) - 1) / SK + 1) : nst;
+    for (int s = 0; s < nst_used; ++s) {
         const int buf = p.nbuf == 1 ? 0 : (s & 1);
         T *kbuf = Kb + (size_t)buf * SK * D;
         const T *vbuf = Vb + (size_t)buf * SK * D;
         if (!kreg) {
         wait_vm_all();
         __syncthreads();                                     // stage s is in LDS; buffer s+1 is free
-        if (s + 1 < nst) {
+        if (s + 1 < nst_used) {
             const int nb = (s + 1) & 1;
             stage_rows<D, T>(Kb + (size_t)nb * SK * D, kg, (s + 1) * SK, SK, L, wave, nw, lane);
             stage_rows<D, T>(Vb + (size_t)nb * SK * D, vg, (s + 1) * SK, SK, L, wave, nw, lane);
@@ -265,9 +268,10 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
         for (int h = 0; h < SK / kKB; ++h) {
             const int j0 = s * SK + h * kKB;
             if (j0 >= L) break;
+            if (p.causal && j0 > rwl) break;                   // causal: no later keys
             // region of this sub-block relative to the wave's rows (wave-uniform)
             int region = 0;                                    // overlap: per-score exponentials
-            if constexpr (KIND != kMaskLit) {
+            if (KIND != kMaskLit || p.causal) {
                 if (j0 + kKB - 1 < rw0) region = 1;            // every key before every row
                 else if (j0 > rwl) region = 2;                  // every key after every row
             }
@@ -340,7 +344,7 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
                 }
                 // sacc[t][e] = S[query r][key j0 + 16t + 4g + e]; mask it (region is wave-uniform)
                 float pv[2][4];
-                if (KIND == kMaskLit) {
+                if constexpr (KIND == kMaskLit) {
 #pragma unroll
                     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -357,6 +361,15 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
                     for (int t = 0; t < 2; ++t)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) pv[t][e] = (sacc[t][e] * rowf) * mk[t][e];
+                }
+                if (p.causal && region == 0) {
+                    // keys after this lane's query row are masked out
+                    const int i = (wtile0 + qt) * 16 + r;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (j0 + 16 * t + 4 * g + e > i) pv[t][e] = 0.f;
                 }
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
@@ -481,6 +494,7 @@ hipError_t launch_full_t(const AttnArgs &a, hipStream_t stream, const FullShape 
     p.nblocks = a.B * a.H * sh.nsb;
     p.sk = sh.sk;
     p.nbuf = sh.nbuf;
+    p.causal = a.causal ? 1 : 0;
     if (sh.lds > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&full_kernel<D, KIND, QT, BF16>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh.lds);

@@ -19,12 +19,14 @@ def to_device(inp: "lin.Inputs"):
     return dev(inp.q_dev), dev(inp.k_dev), dev(inp.v_dev), ll
 
 
-def oracle_full(inp: "lin.Inputs", eps: float):
-    return oracle.full(inp.q, inp.k, inp.v, inp.log_lambda_f64, inp.wl.kind, eps, want_abs=True)
+def oracle_full(inp: "lin.Inputs", eps: float, causal: bool = False):
+    kind = inp.wl.kind | (oracle.CAUSAL if causal else 0)
+    return oracle.full(inp.q, inp.k, inp.v, inp.log_lambda_f64, kind, eps, want_abs=True)
 
 
-def oracle_rows(inp: "lin.Inputs", eps: float, rows):
-    return oracle.rows(inp.q, inp.k, inp.v, inp.log_lambda_f64, inp.wl.kind, eps, rows, want_abs=True)
+def oracle_rows(inp: "lin.Inputs", eps: float, rows, causal: bool = False):
+    kind = inp.wl.kind | (oracle.CAUSAL if causal else 0)
+    return oracle.rows(inp.q, inp.k, inp.v, inp.log_lambda_f64, kind, eps, rows, want_abs=True)
 
 
 def sample_rows(B, H, L, n, seed=0):

@@ -15,6 +15,11 @@ every result within beta of the exact one is as correct as any other an implemen
 arithmetic can give.  So Gate C is asserted everywhere, and Gate L on every row of the
 well-conditioned workloads (LION-LIT, whose positive phi makes kappa = 1, and the fp32 LION-S unit
 case) and on the well-conditioned rows (kappa_i <= 2) of all the others.
+
+Row scale (``row_scale=True``, the causal variant): a causal row i averages i + 1 values, so output
+magnitudes fall by up to sqrt(L) from the first rows to the last, while every rounding above is
+relative to the row's own terms.  There RMS(Y_ref) in both gates is taken per row, over its d
+channels, instead of over the whole output.
 """
 from __future__ import annotations
 
@@ -50,7 +55,8 @@ class ParityReport:
                 f"median={self.kappa_median:.3g} tol={self.tol:g}")
 
 
-def compare(y_gpu, y_ref, den_ref, absnum, absden, in_dtype: str, out_dtype: str, d: int, L: int) -> ParityReport:
+def compare(y_gpu, y_ref, den_ref, absnum, absden, in_dtype: str, out_dtype: str, d: int, L: int,
+            row_scale: bool = False) -> ParityReport:
     """All arrays are per-row views: y [..., d], den/absden [...]. Values fp64."""
     y_gpu = np.asarray(y_gpu, dtype=np.float64).reshape(-1, d)
     y_ref = np.asarray(y_ref, dtype=np.float64).reshape(-1, d)
@@ -59,14 +65,17 @@ def compare(y_gpu, y_ref, den_ref, absnum, absden, in_dtype: str, out_dtype: str
     ad = np.asarray(absden, dtype=np.float64).reshape(-1)
     tol = BF16_TOL if in_dtype == "bf16" else F32_TOL
     u, uo = unit_roundoff(in_dtype, d, L), out_roundoff(out_dtype)
-    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    if row_scale:
+        rms = np.sqrt(np.mean(y_ref ** 2, axis=1))[:, None]
+    else:
+        rms = float(np.sqrt(np.mean(y_ref ** 2)))
     err = np.abs(y_gpu - y_ref)
     if not np.all(np.isfinite(y_gpu)):
         err = np.where(np.isfinite(y_gpu), err, np.inf)
     absden_ = np.abs(den)
     beta = 3 * u * (an + np.abs(y_ref) * ad[:, None]) / absden_[:, None] + uo * np.abs(y_ref)
     gate_c = float(np.max(err / (tol * rms + beta)))
-    row_err = np.max(err, axis=1) / rms
+    row_err = np.max(err, axis=1) / (rms[:, 0] if row_scale else rms)
     kappa = ad / absden_
     well = kappa <= KAPPA_WELL
     gl_well = float(np.max(row_err[well])) if np.any(well) else 0.0

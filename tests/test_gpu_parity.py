@@ -32,14 +32,17 @@ def run_form(form, q, k, v, ll, kind, eps, C=64, y_dtype=None):
     return y.float().cpu().numpy().astype(np.float64), den.cpu().numpy().astype(np.float64)
 
 
-def _check(form, inp, eps, C=64, y_dtype=None, require_literal=None, tag=""):
+def _check(form, inp, eps, C=64, y_dtype=None, require_literal=None, tag="", causal=False):
     import torch
+    import bidirectional_linear_attention_lion_amd as lion
     wl = inp.wl
     q, k, v, ll = to_device(inp)
     out_dtype = "f32" if (y_dtype == torch.float32 or wl.dtype == "f32") else "bf16"
-    y, den = run_form(form, q, k, v, ll, wl.kind, eps, C=C, y_dtype=y_dtype)
-    yr, dr, an, ad = oracle_full(inp, eps)
-    rep = compare(y, yr, dr, an, ad, wl.dtype, out_dtype, wl.d, wl.L)
+    y, den = run_form(form, q, k, v, ll, wl.kind | (lion.CAUSAL if causal else 0), eps, C=C, y_dtype=y_dtype)
+    yr, dr, an, ad = oracle_full(inp, eps, causal=causal)
+    if causal:
+        tag = ("causal " + tag).strip()
+    rep = compare(y, yr, dr, an, ad, wl.dtype, out_dtype, wl.d, wl.L, row_scale=causal)
     # the row sums the kernel used, against the exact ones, relative to the absolute-value sums
     den_err = float(np.max(np.abs(den - dr.reshape(den.shape)) / (ad.reshape(den.shape) + 1e-30)))
     report(f"[{form}{'' if form != 'chunk' else ' C=%d' % C}] {wl.name} B{wl.B} H{wl.H} L{wl.L} d{wl.d} "
@@ -189,3 +192,55 @@ def test_forms_agree_on_gpu():
         rep = compare(y, yr, dr, an, ad, "bf16", "bf16", wl.d, wl.L)
         report(f"[agree] {name}: {rep}")
         assert_parity(rep, name)
+
+
+# ---- causal variant (mask kind | CAUSAL): keys after the query masked out -------------------------
+# Lengths span one tile, ragged tiles, several chunks, the resident kernel (C = 64, 128), its row groups
+# (L > 256 with C = 64) and the multi-launch chunk path (C = 16, fp32).
+CAUSAL_L = [1, 2, 17, 64, 65, 130, 256, 300, 600]
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("kind", [lin.LIT, lin.D, lin.S])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_causal_lengths(form, kind, dtype):
+    chunks = (16, 64, 128) if form == "chunk" else (64,)
+    for L in CAUSAL_L:
+        inp = lin.random_inputs(1, 3, L, 64, kind, dtype=dtype, seed=700 + L)
+        for C in chunks:
+            _check(form, inp, 1e-6, C=C, tag=f"(L={L})", causal=True)
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("d", [16, 32, 128])
+def test_causal_head_dims(form, d):
+    for kind in (lin.LIT, lin.D, lin.S):
+        for L in (100, 300):
+            inp = lin.random_inputs(1, 2, L, d, kind, dtype="bf16", seed=800 + d + L)
+            _check(form, inp, 1e-6, C=64, tag=f"(d={d} L={L})", causal=True)
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_causal_many_heads(form):
+    """B x H large enough for the RNN form's plain (forward waves only) kernel and many workgroups."""
+    for kind in (lin.LIT, lin.S):
+        inp = lin.random_inputs(16, 16, 64, 64, kind, dtype="bf16", seed=901 + kind)
+        _check(form, inp, 1e-6, C=64, tag="(B16 H16)", causal=True)
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("name", ["vit_base_d", "bert_large_s"])
+def test_causal_full_size_sampled(form, name):
+    import bidirectional_linear_attention_lion_amd as lion
+    wl = lin.WORKLOADS[name]
+    inp = lin.make_inputs(wl)
+    q, k, v, ll = to_device(inp)
+    rows = sample_rows(wl.B, wl.H, wl.L, 160, seed=11)
+    yr, dr, an, ad = oracle_rows(inp, wl.eps, rows, causal=True)
+    for C in (wl.chunks if form == "chunk" else (64,)):
+        y, den = run_form(form, q, k, v, ll, wl.kind | lion.CAUSAL, wl.eps, C=C)
+        ys = y.reshape(-1, wl.d)[rows]
+        rep = compare(ys, yr, dr, an, ad, wl.dtype, "bf16", wl.d, wl.L, row_scale=True)
+        report(f"[{form} C={C} causal full-size sampled] {wl.name}: {rep}")
+        assert_parity(rep, f"{form} {wl.name} causal full size", require_literal=wl.kind == lin.LIT)
+        assert np.all(np.isfinite(y)), "non-finite outputs"
