@@ -44,6 +44,8 @@ def parse_args():
     ap.add_argument("--workload", default="vit_tiny_lit")
     ap.add_argument("--forms", default=None, help="comma-separated forms (default: the workload's)")
     ap.add_argument("--chunk", type=int, default=None, help="chunk size C (default: the workload's first)")
+    ap.add_argument("--causal", action="store_true",
+                    help="the causal variant (keys after the query masked out) of the workload's mask")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0,
                     help="wall-time budget of the oracle sample (0 disables)")
@@ -108,8 +110,10 @@ def kernel_hash(form: str) -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic(form: str, wl, C: int):
-    """Algorithmic bytes and flops of one launch (what the method must read, write and compute)."""
+def algorithmic(form: str, wl, C: int, causal: bool = False):
+    """Algorithmic bytes and flops of one launch (what the method must read, write and compute).
+    Causal: the L (L + 1) / 2 query-key pairs of the lower triangle, the intra-chunk triangles plus
+    the forward states only, one recurrence."""
     B, H, L, d = wl.B, wl.H, wl.L, wl.d
     esz = 2 if wl.dtype == "bf16" else 4
     nbytes = 4 * B * H * L * d * esz                      # read q, k, v; write y
@@ -119,22 +123,24 @@ def algorithmic(form: str, wl, C: int):
         nbytes += 4 * H
     bh = B * H
     if form == "full":
-        flops = bh * (4 * L * L * d + 2 * L * L)          # phi(Q)phi(K)^T, P V, mask and row sums
+        pairs = L * (L + 1) / 2 if causal else L * L
+        flops = bh * (4 * pairs * d + 2 * pairs)          # phi(Q)phi(K)^T, P V, mask and row sums
     elif form == "chunk":
-        flops = bh * (4 * L * C * d + 8 * L * d * d + 2 * L * C)   # intra-chunk + state fold and use
+        cpairs = L * (C + 1) / 2 if causal else L * C
+        flops = bh * (4 * cpairs * d + (4 if causal else 8) * L * d * d + 2 * cpairs)   # intra-chunk + states
     else:
         per_dir = (4 * d * d + 3 * d) if wl.kind == 0 else (5 * d * d + 4 * d)
-        flops = bh * L * 2 * per_dir                      # two recurrences: state update + q^T S, q.z
+        flops = bh * L * (1 if causal else 2) * per_dir   # recurrences: state update + q^T S, q.z
     return nbytes, flops
 
 
-def bound_of(form: str, wl, C: int) -> str:
+def bound_of(form: str, wl, C: int, causal: bool = False) -> str:
     """The roof that binds a form on a workload: the RNN form is fp32 vector-ALU work; the full and
     chunk forms are matrix-core work, bound by HBM below the bf16 ridge (peak flops / peak bytes) and
     by the matrix cores above it."""
     if form == "birnn":
         return "alu"
-    nbytes, flops = algorithmic(form, wl, C)
+    nbytes, flops = algorithmic(form, wl, C, causal)
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     return "mfma" if flops / nbytes > ridge else "hbm"
 
@@ -144,9 +150,9 @@ def peak_of(bound: str):
             "alu": (VALU_FP32_PEAK_TFLOPS, "TFLOP/s")}[bound]
 
 
-def read_traffic(form: str, workload: str):
+def read_traffic(form: str, workload: str, causal: bool = False):
     """HBM bytes per launch from a committed counter summary, if it was taken on this kernel."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{form}_{workload}.txt")
+    path = os.path.join(ROOT, "profiles", f"traffic_{form}_{workload}{'_causal' if causal else ''}.txt")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -157,15 +163,16 @@ def read_traffic(form: str, workload: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(wl, budget_s: float):
+def cpu_baseline(wl, budget_s: float, causal: bool = False):
     """The fp64 oracle (the full-form definition) on the host: the whole workload if it fits the
     budget, else as many leading batch entries as do; tokens/s over the sample."""
     import oracle
     from bidirectional_linear_attention_lion_amd import inputs as lin
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    kind = wl.kind | (oracle.CAUSAL if causal else 0)
     inp1 = lin.make_inputs(wl, B=1)
     t0 = time.perf_counter()
-    oracle.full(inp1.q, inp1.k, inp1.v, inp1.log_lambda_f64, wl.kind, wl.eps)
+    oracle.full(inp1.q, inp1.k, inp1.v, inp1.log_lambda_f64, kind, wl.eps)
     t1 = time.perf_counter() - t0
     nb = int(max(1, min(wl.B, budget_s / max(t1, 1e-6))))
     inp = lin.make_inputs(wl, B=nb) if nb > 1 else inp1
@@ -173,7 +180,7 @@ def cpu_baseline(wl, budget_s: float):
     reps, dt = 0, 0.0
     while True:
         t0 = time.perf_counter()
-        oracle.full(inp.q, inp.k, inp.v, inp.log_lambda_f64, wl.kind, wl.eps)
+        oracle.full(inp.q, inp.k, inp.v, inp.log_lambda_f64, kind, wl.eps)
         dt += time.perf_counter() - t0
         reps += 1
         if dt >= 0.5 * budget_s or reps >= 50 or dt + dt / reps > budget_s:
@@ -201,6 +208,8 @@ def main():
 
     wl = lin.WORKLOADS[args.workload]
     C = args.chunk or wl.chunks[0]
+    causal = args.causal
+    kind = wl.kind | (lion.CAUSAL if causal else 0)
     forms = list(wl.forms) if args.forms is None else [f for f in args.forms.split(",") if f]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -228,11 +237,11 @@ def main():
     def call(form, s):
         q, k, v, y = sets[s % nsets]
         if form == "full":
-            lion.lion_attn_full(q, k, v, ll, wl.kind, wl.eps, y=y, stream=stream)
+            lion.lion_attn_full(q, k, v, ll, kind, wl.eps, y=y, stream=stream)
         elif form == "chunk":
-            lion.lion_attn_chunk(q, k, v, ll, wl.kind, C, wl.eps, y=y, workspace=ws["chunk"], stream=stream)
+            lion.lion_attn_chunk(q, k, v, ll, kind, C, wl.eps, y=y, workspace=ws["chunk"], stream=stream)
         else:
-            lion.lion_attn_birnn(q, k, v, ll, wl.kind, wl.eps, y=y, workspace=ws["birnn"], stream=stream)
+            lion.lion_attn_birnn(q, k, v, ll, kind, wl.eps, y=y, workspace=ws["birnn"], stream=stream)
 
     for s in range(args.warmup):
         for f in forms:
@@ -263,23 +272,23 @@ def main():
     per_form = {}
     for f in forms:
         avg = ev[f][0].elapsed_time(ev[f][1]) / args.steps
-        nbytes, flops = algorithmic(f, wl, C)
+        nbytes, flops = algorithmic(f, wl, C, causal)
         per_form[f] = {
             "tokens_per_s": tokens / (avg * 1e-3),
             "ms_avg": avg,
             "alg_GBps": nbytes / (avg * 1e-3) / 1e9,
             "alg_TFLOPs": flops / (avg * 1e-3) / 1e12,
-            "bound": bound_of(f, wl, C),
+            "bound": bound_of(f, wl, C, causal),
         }
         if f == "chunk":
             per_form[f]["C"] = C
     dom = max(forms, key=lambda f: per_form[f]["ms_avg"])
-    nbytes, flops = algorithmic(dom, wl, C)
+    nbytes, flops = algorithmic(dom, wl, C, causal)
     avg_s = per_form[dom]["ms_avg"] * 1e-3
-    dom_bound = bound_of(dom, wl, C)
+    dom_bound = bound_of(dom, wl, C, causal)
     peak, unit = peak_of(dom_bound)
     achieved = nbytes / avg_s / 1e9 if dom_bound == "hbm" else flops / avg_s / 1e12
-    traffic = read_traffic(dom, wl.name)
+    traffic = read_traffic(dom, wl.name, causal)
     for f in forms:
         pf = per_form[f]
         pk, _ = peak_of(pf["bound"])
@@ -300,7 +309,7 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "L": wl.L, "d": wl.d,
-                   "mask": lin.KIND_NAME[wl.kind], "forms": forms, "C": C, "input_sets": nsets,
+                   "mask": lin.KIND_NAME[wl.kind] + ("+causal" if causal else ""), "forms": forms, "C": C, "input_sets": nsets,
                    "host_us_per_launch": host_s * 1e6},
         "forms": per_form,
         "roofline": {"bound": dom_bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
@@ -308,7 +317,7 @@ def main():
                      "traffic": traffic},
     }
     if args.cpu_baseline_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_baseline_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_baseline_seconds, causal)
     print(json.dumps(out), flush=True)
 
 

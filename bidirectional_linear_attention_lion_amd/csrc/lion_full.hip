@@ -73,7 +73,8 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
 
     const int tile = xcd_tile(blockIdx.x, p.nblocks);
     const int bh = tile / p.nsb;
-    const int sb = tile % p.nsb;
+    // causal: workgroups of later rows (more keys) are dispatched first, so the light ones form the tail
+    const int sb = p.causal ? p.nsb - 1 - tile % p.nsb : tile % p.nsb;
     const int tile0 = sb * p.tiles_per_wg;                  // first query tile of this workgroup
     const int wtile0 = tile0 + wave * QT;                    // first query tile of this wave
     const int wave_tiles = max(0, min(QT, ntiles - wtile0));
