@@ -307,3 +307,183 @@ int lion_oracle_rows_f64(const double *q, const double *k, const double *v, cons
     }
     return err ? ORACLE_ENOMEM : ORACLE_OK;
 }
+
+/* ---- backward pass of the full form ------------------------------------------------------------------
+ * The pages train the attention form ("trains like a Transformer": [OR] abstract; [RB] reply "Concern
+ * 1", Theorem 3.3 Eq. 25), so the gradient of the definition above is what training needs.  Nothing on
+ * the pages spells it out; it is the chain rule applied to the definition, step by step, for a loss
+ * whose gradient with respect to y is dy:
+ *
+ *   s_ij = phi(q_i).phi(k_j)      p_ij = M_ij s_ij      den_i = sum_j p_ij + eps      y_i = sum_j p_ij v_j / den_i
+ *   g_i  = dy_i / den_i           delta_i = g_i . y_i
+ *   dp_ij = g_i . v_j - delta_i                         (through the numerator and through den_i)
+ *   dv_j = sum_i p_ij g_i
+ *   dphi(q_i) = sum_j M_ij dp_ij phi(k_j)               dphi(k_j) = sum_i M_ij dp_ij phi(q_i)
+ *   dq_i, dk_j = the Jacobian of phi at q_i, k_j (transposed) applied to those
+ *   dM_ij = dp_ij s_ij
+ *   M_ij = prod_{t = min(i,j)+1}^{max(i,j)} lambda_t, so d M_ij / d log(lambda_t) = M_ij for t in that
+ *   range: dlog(lambda_t) = sum over the pairs (i, j) whose range holds t of dM_ij M_ij.  The range sums
+ *   are taken with a difference array (add at min+1, subtract after max, then one running sum), the
+ *   standard exact way to add a value over an index range.
+ *   LION-D: every lambda_t of a head is exp(log_lambda[h]), so dlog_lambda[h] = the sum of those over
+ *   every batch entry and token.  Causal: M_ij = 0 for j > i is a constant, contributing nothing. */
+
+/* The Jacobian of phi at x, transposed, applied to g (one token's d channels).
+ *   LIT: d(elu(x)+1)/dx = 1 for x > 0, exp(x) otherwise.   D: identity.
+ *   S: phi = s / ||s|| with s = silu(x): dphi/ds = (I - phi phi^T) / ||s||, and
+ *      dsilu/dx = sigmoid(x) (1 + x (1 - sigmoid(x))).  ||s|| = 0 gives 0 (phi is 0 there). */
+static void phi_grad_row(int kind, const double *x, const double *g, int d, double *dx)
+{
+    int c;
+    if (kind == ORACLE_MASK_LIT) {
+        for (c = 0; c < d; ++c)
+            dx[c] = g[c] * (x[c] > 0.0 ? 1.0 : exp(x[c]));
+    } else if (kind == ORACLE_MASK_D) {
+        for (c = 0; c < d; ++c)
+            dx[c] = g[c];
+    } else {
+        double ss = 0.0, nrm, pg = 0.0;
+        for (c = 0; c < d; ++c) {
+            const double sv = x[c] / (1.0 + exp(-x[c]));
+            ss += sv * sv;
+        }
+        nrm = sqrt(ss);
+        for (c = 0; c < d; ++c) {
+            const double sv = x[c] / (1.0 + exp(-x[c]));
+            pg += (nrm > 0.0 ? sv / nrm : 0.0) * g[c];
+        }
+        for (c = 0; c < d; ++c) {
+            const double sig = 1.0 / (1.0 + exp(-x[c]));
+            const double ph = nrm > 0.0 ? x[c] * sig / nrm : 0.0;
+            dx[c] = nrm > 0.0 ? sig * (1.0 + x[c] * (1.0 - sig)) * (g[c] - ph * pg) / nrm : 0.0;
+        }
+    }
+}
+
+/* Gradients of the full definition.
+ *   q, k, v, dy: [B, H, L, d];  log_lambda as for lion_oracle_full_f64;  mask_kind may carry ORACLE_CAUSAL.
+ *   dq, dk, dv: [B, H, L, d];  dll: NULL for LIT, [H] for D, [B, H, L] for S (entry t = 0 is always 0:
+ *   lambda_0 never enters the mask). */
+int lion_oracle_full_bwd_f64(const double *q, const double *k, const double *v, const double *log_lambda,
+                             int mask_kind, double eps, int B, int H, int L, int d, const double *dy, double *dq,
+                             double *dk, double *dv, double *dll)
+{
+    long bh, nbh = (long)B * H;
+    int err = 0, kind, causal;
+    double *dll_tok;
+    causal = (mask_kind & ORACLE_CAUSAL) != 0;
+    kind = mask_kind & ~ORACLE_CAUSAL;
+    if (!q || !k || !v || !dy || !dq || !dk || !dv || B < 1 || H < 1 || L < 1 || d < 1 || !(eps >= 0.0) ||
+        kind < ORACLE_MASK_LIT || kind > ORACLE_MASK_S || (kind != ORACLE_MASK_LIT && (!log_lambda || !dll)))
+        return ORACLE_EINVAL;
+    dll_tok = (double *)calloc((size_t)nbh * L, sizeof(double));
+    if (!dll_tok)
+        return ORACLE_ENOMEM;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (bh = 0; bh < nbh; ++bh) {
+        size_t base = (size_t)bh * L;
+        double *phq = (double *)malloc(sizeof(double) * (size_t)L * d);
+        double *phk = (double *)malloc(sizeof(double) * (size_t)L * d);
+        double *dphq = (double *)calloc((size_t)L * d, sizeof(double));
+        double *dphk = (double *)calloc((size_t)L * d, sizeof(double));
+        double *lam = (double *)malloc(sizeof(double) * (size_t)L);
+        double *m = (double *)malloc(sizeof(double) * (size_t)L);
+        double *s = (double *)malloc(sizeof(double) * (size_t)L);
+        double *y = (double *)malloc(sizeof(double) * (size_t)d);
+        double *g = (double *)malloc(sizeof(double) * (size_t)d);
+        double *diff = (double *)calloc((size_t)L + 1, sizeof(double));
+        int i, j, c;
+        if (!phq || !phk || !dphq || !dphk || !lam || !m || !s || !y || !g || !diff) {
+            err |= 1;
+        } else {
+            for (j = 0; j < L; ++j) {
+                phi_row(kind, q + (base + j) * d, d, phq + (size_t)j * d);
+                phi_row(kind, k + (base + j) * d, d, phk + (size_t)j * d);
+            }
+            decays(kind, log_lambda, H, L, bh, lam);
+            for (c = 0; c < L * d; ++c)
+                dv[base * d + c] = 0.0;
+            for (i = 0; i < L; ++i) {
+                const double *pq = phq + (size_t)i * d;
+                const double *dyi = dy + (base + i) * d;
+                double den = 0.0, delta = 0.0;
+                mask_row(lam, L, i, causal, m);
+                /* forward row: scores, row sum, output */
+                for (c = 0; c < d; ++c)
+                    y[c] = 0.0;
+                for (j = 0; j < L; ++j) {
+                    double sc = 0.0;
+                    for (c = 0; c < d; ++c)
+                        sc += pq[c] * phk[(size_t)j * d + c];
+                    s[j] = sc;
+                    den += m[j] * sc;
+                    for (c = 0; c < d; ++c)
+                        y[c] += m[j] * sc * v[(base + j) * d + c];
+                }
+                den += eps;
+                for (c = 0; c < d; ++c) {
+                    y[c] /= den;
+                    g[c] = dyi[c] / den;
+                    delta += g[c] * y[c];
+                }
+                /* backward row */
+                for (j = 0; j < L; ++j) {
+                    double gv = 0.0, dp, ds;
+                    for (c = 0; c < d; ++c)
+                        gv += g[c] * v[(base + j) * d + c];
+                    dp = gv - delta;
+                    for (c = 0; c < d; ++c)
+                        dv[(base + j) * d + c] += m[j] * s[j] * g[c];
+                    ds = m[j] * dp;
+                    for (c = 0; c < d; ++c) {
+                        dphq[(size_t)i * d + c] += ds * phk[(size_t)j * d + c];
+                        dphk[(size_t)j * d + c] += ds * pq[c];
+                    }
+                    /* dlog(lambda_t) += dM_ij M_ij for min(i,j) < t <= max(i,j) */
+                    if (j != i) {
+                        const double w = dp * s[j] * m[j];
+                        const int lo = i < j ? i : j, hi = i < j ? j : i;
+                        diff[lo + 1] += w;
+                        diff[hi + 1] -= w;
+                    }
+                }
+            }
+            for (j = 0; j < L; ++j) {
+                phi_grad_row(kind, q + (base + j) * d, dphq + (size_t)j * d, d, dq + (base + j) * d);
+                phi_grad_row(kind, k + (base + j) * d, dphk + (size_t)j * d, d, dk + (base + j) * d);
+            }
+            {
+                double run = 0.0;
+                for (j = 0; j < L; ++j) {
+                    run += diff[j];
+                    dll_tok[base + j] = run;
+                }
+            }
+        }
+        free(phq);
+        free(phk);
+        free(dphq);
+        free(dphk);
+        free(lam);
+        free(m);
+        free(s);
+        free(y);
+        free(g);
+        free(diff);
+    }
+    if (!err && kind == ORACLE_MASK_S) {
+        memcpy(dll, dll_tok, sizeof(double) * (size_t)nbh * L);
+    } else if (!err && kind == ORACLE_MASK_D) {
+        int h, t;
+        long b2;
+        for (h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (b2 = 0; b2 < B; ++b2)
+                for (t = 0; t < L; ++t)
+                    acc += dll_tok[((size_t)b2 * H + h) * L + t];
+            dll[h] = acc;
+        }
+    }
+    free(dll_tok);
+    return err ? ORACLE_ENOMEM : ORACLE_OK;
+}

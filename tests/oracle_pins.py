@@ -399,7 +399,48 @@ def pin_causal_ends(lib):
     assert np.array_equal(y2[:, :, :-1], yc[:, :, :-1]), "causal rows depend on a later token"
 
 
+def pin_bwd_finite_differences(lib):
+    """The backward oracle against central differences of the (pinned) forward definition.
+
+    Loss = sum(y * R) for a fixed random R, so dL/dy = R.  Every element of q, k, v and log(lambda) is
+    perturbed by +-h; the forward oracle alone gives the slope.  Covers every kind, the causal variant,
+    LION-D's per-head decay shared by two batch entries, and eps."""
+    rng = np.random.default_rng(91)
+    B, H, L, d, eps, h = 2, 2, 6, 3, 0.05, 1e-6
+    for kind in (oracle.MASK_LIT, oracle.MASK_D, oracle.MASK_S, oracle.MASK_S | oracle.CAUSAL,
+                 oracle.MASK_D | oracle.CAUSAL):
+        q, k, v, R = (rng.standard_normal((B, H, L, d)) for _ in range(4))
+        base = kind & 3
+        ll = None if base == 0 else (np.log(rng.uniform(0.3, 0.95, (H,))) if base == 1
+                                     else np.log(rng.uniform(0.2, 1.0, (B, H, L))))
+        dq, dk, dv, dll = oracle.full_bwd(q, k, v, ll, kind, eps, R, lib_path=lib)
+
+        def loss(q_, k_, v_, ll_):
+            y, _ = oracle.full(q_, k_, v_, ll_, kind, eps, lib_path=lib)
+            return float(np.sum(y * R))
+
+        def fd(x, which):
+            g = np.empty_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [q, k, v, ll]
+                args_m = [q, k, v, ll]
+                args_p[which], args_m[which] = xp, xm
+                g[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            return g
+
+        for name, an, which in (("dq", dq, 0), ("dk", dk, 1), ("dv", dv, 2)):
+            num = fd([q, k, v][which], which)
+            _close(an, num, 1e-6 * max(1.0, float(np.max(np.abs(num)))), f"{name} kind={kind}")
+        if base:
+            num = fd(ll, 3)
+            _close(dll, num, 1e-6 * max(1.0, float(np.max(np.abs(num)))), f"dlog_lambda kind={kind}")
+
+
 ALL_PINS = [
+    pin_bwd_finite_differences,
     pin_phi_lit_is_elu_plus_one,
     pin_phi_s_is_normalised_silu,
     pin_phi_d_is_identity,

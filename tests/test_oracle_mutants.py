@@ -25,7 +25,8 @@ MUTANTS = [
     ("elu+1 loses the +1", "x[c] > 0.0 ? x[c] + 1.0 : exp(x[c])", "x[c] > 0.0 ? x[c] : exp(x[c])"),
     ("elu branch flipped", "x[c] > 0.0 ? x[c] + 1.0 : exp(x[c])", "x[c] < 0.0 ? x[c] + 1.0 : exp(x[c])"),
     ("silu sign", "out[c] = x[c] / (1.0 + exp(-x[c]));", "out[c] = x[c] / (1.0 + exp(x[c]));"),
-    ("norm without sqrt", "nrm = sqrt(ss);", "nrm = ss;"),
+    ("norm without sqrt", "nrm = sqrt(ss);\n        for (c = 0; c < d; ++c)\n            out[c]",
+     "nrm = ss;\n        for (c = 0; c < d; ++c)\n            out[c]"),
     ("score uses v for k", "s += phq_i[c] * kj[c];", "s += phq_i[c] * vj[c];"),
     ("numerator uses k for v", "num[c] += p * vj[c];", "num[c] += p * kj[c];"),
     ("row sum of |P|", "den += p;", "den += pa;"),
@@ -39,6 +40,15 @@ MUTANTS = [
      "phi_row(mask_kind, q + (base + j) * d, d, phk + (size_t)j * d);"),
     ("absolute score drops a factor", "sa += fabs(phq_i[c]) * fabs(kj[c]);", "sa += fabs(phq_i[c]);"),
     ("abs numerator without |v|", "anum[c] += pa * fabs(vj[c]);", "anum[c] += pa * vj[c];"),
+    ("bwd delta term dropped", "dp = gv - delta;", "dp = gv;"),
+    ("bwd dv without the mask", "dv[(base + j) * d + c] += m[j] * s[j] * g[c];", "dv[(base + j) * d + c] += s[j] * g[c];"),
+    ("bwd silu derivative wrong", "sig * (1.0 + x[c] * (1.0 - sig))", "sig * (1.0 + x[c] * sig)"),
+    ("bwd norm projection dropped", "(g[c] - ph * pg) / nrm", "g[c] / nrm"),
+    ("bwd elu derivative flat", "g[c] * (x[c] > 0.0 ? 1.0 : exp(x[c]))", "g[c] * 1.0"),
+    ("bwd decay range off by one", "diff[lo + 1] += w;", "diff[lo] += w;"),
+    ("bwd key grad from its own phi", "dphk[(size_t)j * d + c] += ds * pq[c];",
+     "dphk[(size_t)j * d + c] += ds * phk[(size_t)j * d + c];"),
+    ("bwd per-head decay from one batch entry", "for (b2 = 0; b2 < B; ++b2)", "for (b2 = 0; b2 < 1; ++b2)"),
 ]
 
 
