@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     FORM_BIRNN,
     FORM_CHUNK,
     FORM_FULL,
+    FORM_FULL_BWD,
     MASK_D,
     MASK_LIT,
     MASK_S,
@@ -17,6 +18,7 @@ from .binding import (  # noqa: F401
     lion_attn_birnn,
     lion_attn_chunk,
     lion_attn_full,
+    lion_attn_full_bwd,
     lion_attn_workspace_bytes,
     lion_status_str,
     library,

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(PKG, "liblion_attn.so")
 MASK_LIT, MASK_D, MASK_S = 0, 1, 2
 CAUSAL = 4   # OR-ed into a mask kind: the causal (unidirectional) variant
 DTYPE_F32, DTYPE_BF16 = 0, 1
-FORM_FULL, FORM_CHUNK, FORM_BIRNN = 0, 1, 2
+FORM_FULL, FORM_CHUNK, FORM_BIRNN, FORM_FULL_BWD = 0, 1, 2, 3
 _KINDS = {"lit": MASK_LIT, "d": MASK_D, "s": MASK_S}
 
 
@@ -41,7 +41,8 @@ def library() -> ctypes.CDLL:
     lib.lion_attn_full.argtypes = common + [f, i, i, i, i, i, vp, i, fp, vp]
     lib.lion_attn_chunk.argtypes = common + [i, f, i, i, i, i, i, vp, i, fp, vp, sz, vp]
     lib.lion_attn_birnn.argtypes = common + [f, i, i, i, i, i, vp, i, fp, vp, sz, vp]
-    for fn in ("lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_abi_version"):
+    lib.lion_attn_full_bwd.argtypes = common + [i, i, i, i, i, vp, fp, vp, vp, vp, vp, i, fp, vp, sz, vp]
+    for fn in ("lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_full_bwd", "lion_attn_abi_version"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.lion_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.lion_attn_workspace_bytes.restype = sz
@@ -137,3 +138,32 @@ def lion_attn_birnn(q, k, v, log_lambda, mask_kind, eps: float = 1e-6, *, y=None
     if rc != 0:
         raise LionError("lion_attn_birnn", rc)
     return y
+
+
+def lion_attn_full_bwd(q, k, v, log_lambda, mask_kind, y, den, dy, *, grad_dtype=None, dq=None, dk=None, dv=None,
+                       dlog_lambda=None, workspace=None, stream=None):
+    """Backward pass of the full form; returns (dq, dk, dv, dlog_lambda).
+
+    y and den are the forward call's output and den_out; dy the incoming gradient (bf16)."""
+    import torch
+    kind = _KINDS[mask_kind] if isinstance(mask_kind, str) else int(mask_kind)
+    B, H, L, d = q.shape
+    dt = _dtype_code(q)
+    gdt = q.dtype if grad_dtype is None else grad_dtype
+    dq = torch.empty((B, H, L, d), dtype=gdt, device=q.device) if dq is None else dq
+    dk = torch.empty((B, H, L, d), dtype=gdt, device=q.device) if dk is None else dk
+    dv = torch.empty((B, H, L, d), dtype=gdt, device=q.device) if dv is None else dv
+    base = kind & 3
+    if dlog_lambda is None and base != MASK_LIT:
+        shape = (H,) if base == MASK_D else (B, H, L)
+        dlog_lambda = torch.empty(shape, dtype=torch.float32, device=q.device)
+    ws, nbytes = _workspace(FORM_FULL_BWD, B, H, L, d, 0, dt, workspace, q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sptr = ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    rc = library().lion_attn_full_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_lambda), kind, B, H, L, d, dt, _ptr(y),
+                                      _ptr(den), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq),
+                                      _ptr(dlog_lambda), _ptr(ws), nbytes, sptr)
+    if rc != 0:
+        raise LionError("lion_attn_full_bwd", rc)
+    return dq, dk, dv, dlog_lambda

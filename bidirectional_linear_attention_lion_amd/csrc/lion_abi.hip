@@ -113,6 +113,47 @@ int lion_attn_birnn(const void *q, const void *k, const void *v, const float *lo
     return status_of(lion::launch_birnn(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int lion_attn_full_bwd(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, int B,
+                       int H, int L, int d, int dtype, const void *y, const float *den, const void *dy, void *dq,
+                       void *dk, void *dv, int grad_dtype, float *dlog_lambda, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    int rc = check_common(q, k, v, log_lambda, mask_kind, 0.f, B, H, L, d, dtype, y, dtype, nullptr);
+    if (rc != LION_OK) return rc;
+    if (!den || !dy || !dq || !dk || !dv) return LION_ERR_INVALID;
+    if (!aligned16(den) || !aligned16(dy) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return LION_ERR_INVALID;
+    const int kind = mask_kind & 3;
+    if (kind == LION_MASK_LIT ? dlog_lambda != nullptr : dlog_lambda == nullptr) return LION_ERR_INVALID;
+    if (dlog_lambda && !aligned16(dlog_lambda)) return LION_ERR_INVALID;
+    if (grad_dtype != LION_DTYPE_F32 && grad_dtype != LION_DTYPE_BF16) return LION_ERR_INVALID;
+    if (workspace && !aligned16(workspace)) return LION_ERR_INVALID;
+    if (dtype != LION_DTYPE_BF16) return LION_ERR_UNSUPPORTED;
+    lion::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.log_lambda = log_lambda;
+    a.kind = kind;
+    a.causal = (mask_kind & LION_CAUSAL) != 0;
+    a.B = B;
+    a.H = H;
+    a.L = L;
+    a.d = d;
+    a.y = y;
+    a.dy = dy;
+    a.den = den;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.g_bf16 = grad_dtype == LION_DTYPE_BF16;
+    a.dll = dlog_lambda;
+    const lion::Plan plan = lion::plan_full_bwd(a);
+    if (!plan.ok) return LION_ERR_UNSUPPORTED;
+    if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return LION_ERR_WORKSPACE;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    return status_of(lion::launch_full_bwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, int dtype) {
     if (B < 1 || H < 1 || L < 1 || !d_supported(d) || (long long)L > kMaxL || (long long)B * H * L > kMaxRows)
         return (size_t)-1;
@@ -130,6 +171,17 @@ size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, in
         plan = lion::plan_chunk(a);
         break;
     case LION_FORM_BIRNN: plan = lion::plan_birnn(a); break;
+    case LION_FORM_FULL_BWD: {
+        if (dtype != LION_DTYPE_BF16) return (size_t)-1;
+        lion::BwdArgs b{};
+        b.kind = LION_MASK_S;
+        b.B = B;
+        b.H = H;
+        b.L = L;
+        b.d = d;
+        plan = lion::plan_full_bwd(b);
+        break;
+    }
     default: return (size_t)-1;
     }
     return plan.ok ? plan.workspace : (size_t)-1;

@@ -1,0 +1,612 @@
+// lion_full_bwd.hip -- backward pass of the full (attention) form of LION.
+//
+// LION trains with the attention form ("LION: A bidirectional framework that trains like a Transformer
+// and infers like an RNN", OpenReview abstract; reply "Concern 1", Theorem 3.3 Eq. 25).  For
+//   s_ij = phi(q_i).phi(k_j),  p_ij = M_ij s_ij,  den_i = sum_j p_ij + eps,  y_i = sum_j p_ij v_j / den_i
+// and an incoming gradient dy, the chain rule gives (delta_i = dy_i.y_i / den_i)
+//   dp_ij = (dy_i.v_j) / den_i - delta_i
+//   dv_j  = sum_i (p_ij / den_i) dy_i
+//   dphi(q_i) = sum_j M_ij dp_ij phi(k_j),   dphi(k_j) = sum_i M_ij dp_ij phi(q_i)
+//   dq, dk  = the Jacobian of phi (transposed) applied to those
+// and, through M_ij = exp(A_max(i,j) - A_min(i,j)) with A the prefix sums of log(lambda),
+//   dA_t = sum over pairs with max(i,j) = t of w_ij - sum over pairs with min(i,j) = t of w_ij,
+//   w_ij = dp_ij p_ij,   dlog(lambda_u) = sum_{t >= u} dA_t   (u >= 1; lambda_0 never enters).
+//
+// Three launches, none of which forms an L x L matrix:
+//   dq:   a wave per 16-query tile streams the keys and values (LDS stages, as in the forward kernel):
+//         S^T = phi(K) phi(Q)^T and (dy v^T)^T = V dY^T on matrix cores, the masked dS^T in registers,
+//         then dphi(Q)^T += phi(K)^T dS^T (the D layout of the first products is the B layout of this
+//         one, as in the forward).  It also writes delta and the row half of dA.
+//   dk/dv: a wave per 16-key tile streams phi(Q) and dY the same way: S and dY V^T with keys as the
+//         column index, then dV^T += dY^T (P / den) and dphi(K)^T += phi(Q)^T dS, and the column half
+//         of dA.
+//   dlog(lambda): LION-S a reverse prefix sum of dA per (batch, head); LION-D sum_t t dA_t over every
+//         batch entry of a head.
+// Causal variant: M_ij = 0 for j > i (a constant), so those pairs are skipped or zeroed.
+#include <type_traits>
+
+#include "lion_device.h"
+#include "lion_internal.h"
+#include "lion_mask.h"
+#include "lion_stage.h"
+
+namespace lion {
+namespace {
+
+constexpr int kKB = 32;                       // rows per sub-block (two 16-row halves)
+constexpr size_t kStageBytes = 64 * 1024;     // bytes of the two streamed operands per stage
+
+struct BwdParams {
+    const __bf16 *q, *k, *v;
+    const float *ll;
+    int H, L;
+    const __bf16 *y, *dy;
+    const float *den;          // the forward's divisors (row sum + eps)
+    void *dq, *dk, *dv;
+    int g_bf16;                // gradients stored as bf16 (else fp32)
+    float *delta, *da_row, *da_col;   // workspace, [B*H*L] each
+    float *dll;
+    int nsb;                   // workgroups per (batch, head)
+    int nblocks;               // grid size
+    int sk;                    // rows per stage (multiple of 32)
+    int nbuf;                  // 1: the whole sequence is one stage; 2: double-buffered stages
+    int causal;
+};
+
+// phi over the rows of a staged tile, in place; rows at or past `row_end` become zero rows.
+template <int D, int KIND>
+__device__ __forceinline__ void phi_stage(__bf16 *tile, int rows, int row_end, int tid, int nt) {
+    using RT = RowTile<D, __bf16>;
+    const int nslot = rows * RT::CPK;
+    const int lane = tid & 63;
+    const int first = (KIND == kMaskD) ? row_end * RT::CPK : 0;   // identity phi: only the padding
+    for (int sl0 = first - first % 64; sl0 < nslot; sl0 += nt) {
+        const int sl = sl0 + tid;
+        if (sl - lane >= nslot) break;   // wave-uniform: nslot is a multiple of 64
+        const bool mine = sl >= first && sl < nslot;
+        const int row = sl / RT::CPK;
+        __bf16 x[8];
+        __builtin_memcpy(x, tile + (size_t)sl * 8, 16);
+        float f[8], ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            f[e] = phi_pre<KIND>((float)x[e]);
+            ss += f[e] * f[e];
+        }
+        float scl = row < row_end ? 1.f : 0.f;
+        if constexpr (KIND == kMaskS) scl *= inv_norm(group_sum<RT::CPK>(ss));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = f2bf(f[e] * scl);
+        if (mine) __builtin_memcpy(tile + (size_t)sl * 8, x, 16);
+    }
+}
+
+// B-operand fragments of one row (row index r of the wave's 16-row tile): fragment st of lane group g
+// holds the eight channels 8 (4 st + g) .. + 7, phi applied (scaled by `ok`) or raw.
+template <int D, int KIND, bool PHI>
+__device__ __forceinline__ void row_frags(const __bf16 *row, bool ok, bf16x8 *out) {
+    constexpr int NS = D / 32;
+    float x[NS][8], ss = 0.f;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        const int g = (threadIdx.x & 63) >> 4;
+        const bf16x8 raw = __builtin_bit_cast(bf16x8, ld16(row + 8 * (4 * st + g)));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x[st][e] = PHI ? phi_pre<KIND>((float)raw[e]) : (float)raw[e];
+            ss += x[st][e] * x[st][e];
+        }
+    }
+    float sc = ok ? 1.f : 0.f;
+    if constexpr (PHI && KIND == kMaskS) {
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        sc *= inv_norm(ss);
+    }
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        bf16x8 f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = f2bf(x[st][e] * sc);
+        out[st] = f;
+    }
+}
+
+// A-operand fragment of rows h*32 + {16 t + r} of a staged tile, channels 8 (4 st + g) .. + 7.
+template <int D>
+__device__ __forceinline__ bf16x8 rows_frag(const __bf16 *tile, int h, int t, int st, int r, int g) {
+    using RT = RowTile<D, __bf16>;
+    return *reinterpret_cast<const bf16x8 *>(tile + RT::off(h * kKB + 16 * t + r, 8 * (4 * st + g)));
+}
+
+// A-operand fragment of the transposed tile: lane (r, g) gets column 16 ct + r at rows h*32 + 4g + e
+// and h*32 + 16 + 4g + e (see lion_stage.h).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16 *tile, int h, int ct, int r, int g) {
+    using RT = RowTile<D, __bf16>;
+    const int row = h * kKB + 4 * g + (r >> 2), col = 16 * ct + 4 * (r & 3);
+    const bf16x4 lo = read_tr_b16(tile + RT::off(row, col));
+    const bf16x4 hi = read_tr_b16(tile + RT::off(row + 16, col));
+    bf16x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[e] = lo[e];
+        f[4 + e] = hi[e];
+    }
+    return f;
+}
+
+// The transposed Jacobian of phi at x (channels 16 ct + 4 g + e of one row, held by the four lanes of
+// the row) applied to dphi: LIT elu+1 -> 1 or exp(x); D identity; S normalised silu,
+// dx = silu'(x) (dphi - phi (phi.dphi)) / ||silu(x)||, silu'(x) = sig (1 + x (1 - sig)).
+template <int D, int KIND>
+__device__ __forceinline__ void phi_backward(const float (&x)[D / 16][4], f32x4 (&g4)[D / 16]) {
+    if constexpr (KIND == kMaskLit) {
+#pragma unroll
+        for (int ct = 0; ct < D / 16; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!(x[ct][e] > 0.f)) g4[ct][e] *= fast_exp2(x[ct][e] * kLog2e);
+    } else if constexpr (KIND == kMaskS) {
+        float sig[D / 16][4], sv[D / 16][4], ss = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < D / 16; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sig[ct][e] = __builtin_amdgcn_rcpf(1.f + fast_exp2(-x[ct][e] * kLog2e));
+                sv[ct][e] = x[ct][e] * sig[ct][e];
+                ss += sv[ct][e] * sv[ct][e];
+            }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        const float inv = inv_norm(ss);
+        float pg = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < D / 16; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pg += sv[ct][e] * inv * g4[ct][e];
+        pg += __shfl_xor(pg, 16, 64);
+        pg += __shfl_xor(pg, 32, 64);
+#pragma unroll
+        for (int ct = 0; ct < D / 16; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float ds = sig[ct][e] * (1.f + x[ct][e] * (1.f - sig[ct][e]));
+                g4[ct][e] = ds * (g4[ct][e] - sv[ct][e] * inv * pg) * inv;
+            }
+    }
+}
+
+// Store four gradient values of row `row`, channels 16 ct + 4 g .. + 3.
+__device__ __forceinline__ void store4(void *base, bool bf16, size_t off, f32x4 v) {
+    if (bf16) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = f2bf(v[e]);
+        *reinterpret_cast<bf16x4 *>(reinterpret_cast<__bf16 *>(base) + off) = o;
+    } else {
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(base) + off) = v;
+    }
+}
+
+// ================================ dq ==================================================================
+template <int D, int KIND>
+__global__ void __launch_bounds__(512) bwd_dq_kernel(BwdParams p) {
+    using T = __bf16;
+    constexpr int NS = D / 32, NCT = D / 16;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x, nt = blockDim.x, nw = nt >> 6;
+    const int lane = tid & 63, wave = uniform(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int L = p.L, SK = p.sk;
+    const int nst = (L + SK - 1) / SK;
+    const int Lpad = nst * SK;
+    const int ntiles = (L + 15) / 16;
+
+    const int tile = xcd_tile(blockIdx.x, p.nblocks);
+    const int bh = tile / p.nsb;
+    // causal: workgroups of later rows (more keys) first
+    const int sb = p.causal ? p.nsb - 1 - tile % p.nsb : tile % p.nsb;
+    const int wt = sb * nw + wave;                 // this wave's query tile
+    const bool active = wt < ntiles;
+
+    T *Kb = reinterpret_cast<T *>(smem);
+    T *Vb = Kb + (size_t)p.nbuf * SK * D;
+    float *E = reinterpret_cast<float *>(Vb + (size_t)p.nbuf * SK * D);
+    double *scan_sh = reinterpret_cast<double *>(E + (KIND == kMaskLit ? 0 : Lpad));
+
+    const size_t base = (size_t)bh * L;
+    const T *kg = p.k + base * D;
+    const T *vg = p.v + base * D;
+    stage_rows<D, T>(Kb, kg, 0, SK, L, wave, nw, lane);
+    stage_rows<D, T>(Vb, vg, 0, SK, L, wave, nw, lane);
+    if constexpr (KIND != kMaskLit)
+        build_exponents<KIND>(E, scan_sh, p.ll, bh, p.H, L, Lpad, min(sb * nw * 16, L - 1), tid, nt);
+
+    // this lane's query row i: phi(q), dy fragments; den, delta
+    const int i = wt * 16 + r;
+    const bool ok = active && i < L;
+    const int ic = min(i, L - 1);
+    bf16x8 qf[NS], dyf[NS];
+    row_frags<D, KIND, true>(p.q + (base + ic) * D, ok, qf);
+    row_frags<D, KIND, false>(p.dy + (base + ic) * D, ok, dyf);
+    float dot = 0.f;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        const bf16x8 yv = __builtin_bit_cast(bf16x8, ld16(p.y + (base + ic) * D + 8 * (4 * st + g)));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += (float)dyf[st][e] * (float)yv[e];
+    }
+    dot += __shfl_xor(dot, 16, 64);
+    dot += __shfl_xor(dot, 32, 64);
+    const float den_i = ok ? p.den[base + ic] : 1.f;
+    const float inv_den = 1.f / den_i;
+    const float delta_i = ok ? dot * inv_den : 0.f;
+    if (ok && g == 0) p.delta[base + i] = delta_i;
+    const float Ei = KIND != kMaskLit ? E[ic] : 0.f;
+    const int wlast = min((wt + 1) * 16, L) - 1;
+
+    f32x4 acc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float rowterm = 0.f;
+
+    // causal: stages wholly after the workgroup's last query row are never needed
+    const int nst_used = p.causal ? min(nst, (min((sb + 1) * nw * 16, L) - 1) / SK + 1) : nst;
+    for (int s = 0; s < nst_used; ++s) {
+        const int buf = p.nbuf == 1 ? 0 : (s & 1);
+        T *kbuf = Kb + (size_t)buf * SK * D;
+        const T *vbuf = Vb + (size_t)buf * SK * D;
+        wait_vm_all();
+        __syncthreads();                                   // stage s is in LDS; buffer s+1 is free
+        if (s + 1 < nst_used) {
+            const int nb = (s + 1) & 1;
+            stage_rows<D, T>(Kb + (size_t)nb * SK * D, kg, (s + 1) * SK, SK, L, wave, nw, lane);
+            stage_rows<D, T>(Vb + (size_t)nb * SK * D, vg, (s + 1) * SK, SK, L, wave, nw, lane);
+        }
+        phi_stage<D, KIND>(kbuf, SK, min(SK, L - s * SK), tid, nt);
+        __syncthreads();
+        if (!active) continue;
+
+        for (int h = 0; h < SK / kKB; ++h) {
+            const int j0 = s * SK + h * kKB;
+            if (j0 >= L) break;
+            if (p.causal && j0 > wlast) break;
+            f32x4 sacc[2], dpacc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    sacc[t] = mfma_bf16(rows_frag<D>(kbuf, h, t, st, r, g), qf[st], sacc[t]);
+                    dpacc[t] = mfma_bf16(rows_frag<D>(vbuf, h, t, st, r, g), dyf[st], dpacc[t]);
+                }
+            }
+            // element (t, e): key j = j0 + 16 t + 4 g + e, query i
+            bf16x8 dsf;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                f32x4 ej = f32x4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (KIND != kMaskLit) ej = *reinterpret_cast<const f32x4 *>(E + j0 + 16 * t + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = j0 + 16 * t + 4 * g + e;
+                    float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(Ei - ej[e])) : 1.f;
+                    if (p.causal && j > i) m = 0.f;
+                    const float dp = dpacc[t][e] * inv_den - delta_i;
+                    const float w = dp * (sacc[t][e] * m);
+                    rowterm += j < i ? w : (j > i ? -w : 0.f);
+                    dsf[4 * t + e] = f2bf(dp * m);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma_bf16(tr_frag<D>(kbuf, h, ct, r, g), dsf, acc[ct]);
+        }
+    }
+    if (!active) return;
+
+    // rows of dA (pairs where this row is the later / earlier index), then dq through phi
+    rowterm += __shfl_xor(rowterm, 16, 64);
+    rowterm += __shfl_xor(rowterm, 32, 64);
+    if (KIND != kMaskLit && ok && g == 0) p.da_row[base + i] = rowterm;
+    // acc[ct][e] = dphi(q_i) at channel 16 ct + 4 g + e
+    float x[NCT][4];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(p.q + (base + ic) * D + 16 * ct + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[ct][e] = (float)q4[e];
+    }
+    phi_backward<D, KIND>(x, acc);
+    if (ok) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) store4(p.dq, p.g_bf16, (base + i) * D + 16 * ct + 4 * g, acc[ct]);
+    }
+}
+
+// ================================ dk, dv ==============================================================
+template <int D, int KIND>
+__global__ void __launch_bounds__(512) bwd_dkv_kernel(BwdParams p) {
+    using T = __bf16;
+    constexpr int NS = D / 32, NCT = D / 16;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x, nt = blockDim.x, nw = nt >> 6;
+    const int lane = tid & 63, wave = uniform(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int L = p.L, SK = p.sk;
+    const int nst = (L + SK - 1) / SK;
+    const int Lpad = nst * SK;
+    const int ntiles = (L + 15) / 16;
+
+    const int tile = xcd_tile(blockIdx.x, p.nblocks);
+    const int bh = tile / p.nsb;
+    // causal: workgroups of earlier keys (more queries) first
+    const int sb = tile % p.nsb;
+    const int wt = sb * nw + wave;                 // this wave's key tile
+    const bool active = wt < ntiles;
+
+    // LDS: [phi(Q) stages][dY stages][E][den][delta][scan scratch]
+    T *Qb = reinterpret_cast<T *>(smem);
+    T *Gb = Qb + (size_t)p.nbuf * SK * D;
+    float *E = reinterpret_cast<float *>(Gb + (size_t)p.nbuf * SK * D);
+    float *denT = E + (KIND == kMaskLit ? 0 : Lpad);
+    float *dlT = denT + Lpad;
+    double *scan_sh = reinterpret_cast<double *>(dlT + Lpad);
+
+    const size_t base = (size_t)bh * L;
+    const T *qg = p.q + base * D;
+    const T *gg = p.dy + base * D;
+    // causal: stages wholly before the workgroup's first key row are never needed
+    const int s_begin = p.causal ? min(sb * nw * 16, L - 1) / SK : 0;
+    stage_rows<D, T>(Qb + (size_t)(p.nbuf == 1 ? 0 : (s_begin & 1)) * SK * D, qg, s_begin * SK, SK, L, wave, nw, lane);
+    stage_rows<D, T>(Gb + (size_t)(p.nbuf == 1 ? 0 : (s_begin & 1)) * SK * D, gg, s_begin * SK, SK, L, wave, nw, lane);
+    for (int t = tid; t < Lpad; t += nt) {
+        denT[t] = t < L ? p.den[base + t] : 1.f;
+        dlT[t] = t < L ? p.delta[base + t] : 0.f;
+    }
+    if constexpr (KIND != kMaskLit)
+        build_exponents<KIND>(E, scan_sh, p.ll, bh, p.H, L, Lpad, min(sb * nw * 16, L - 1), tid, nt);
+
+    // this lane's key row j: phi(k), v fragments
+    const int j = wt * 16 + r;
+    const bool ok = active && j < L;
+    const int jc = min(j, L - 1);
+    bf16x8 kf[NS], vf[NS];
+    row_frags<D, KIND, true>(p.k + (base + jc) * D, ok, kf);
+    row_frags<D, KIND, false>(p.v + (base + jc) * D, ok, vf);
+    __syncthreads();   // tables written (build_exponents ends with a barrier only for D and S)
+    const float Ej = KIND != kMaskLit ? E[jc] : 0.f;
+    const int wfirst = wt * 16;
+
+    f32x4 acck[NCT], accv[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acck[ct] = accv[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float colterm = 0.f;
+
+    for (int s = s_begin; s < nst; ++s) {
+        const int buf = p.nbuf == 1 ? 0 : (s & 1);
+        T *qbuf = Qb + (size_t)buf * SK * D;
+        const T *gbuf = Gb + (size_t)buf * SK * D;
+        wait_vm_all();
+        __syncthreads();
+        if (s + 1 < nst) {
+            const int nb = (s + 1) & 1;
+            stage_rows<D, T>(Qb + (size_t)nb * SK * D, qg, (s + 1) * SK, SK, L, wave, nw, lane);
+            stage_rows<D, T>(Gb + (size_t)nb * SK * D, gg, (s + 1) * SK, SK, L, wave, nw, lane);
+        }
+        phi_stage<D, KIND>(qbuf, SK, min(SK, L - s * SK), tid, nt);
+        __syncthreads();
+        if (!active) continue;
+
+        for (int h = 0; h < SK / kKB; ++h) {
+            const int i0 = s * SK + h * kKB;
+            if (i0 >= L) break;
+            if (p.causal && i0 + kKB - 1 < wfirst) continue;   // every query before every key
+            f32x4 sacc[2], dpacc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    sacc[t] = mfma_bf16(rows_frag<D>(qbuf, h, t, st, r, g), kf[st], sacc[t]);
+                    dpacc[t] = mfma_bf16(rows_frag<D>(gbuf, h, t, st, r, g), vf[st], dpacc[t]);
+                }
+            }
+            // element (t, e): query i = i0 + 16 t + 4 g + e, key j
+            bf16x8 pf, dsf;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int ib = i0 + 16 * t + 4 * g;
+                const f32x4 dn = *reinterpret_cast<const f32x4 *>(denT + ib);
+                const f32x4 dl = *reinterpret_cast<const f32x4 *>(dlT + ib);
+                f32x4 ei = f32x4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (KIND != kMaskLit) ei = *reinterpret_cast<const f32x4 *>(E + ib);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = ib + e;
+                    float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(ei[e] - Ej)) : 1.f;
+                    if (p.causal && j > i) m = 0.f;
+                    const float inv = __builtin_amdgcn_rcpf(dn[e]);
+                    const float pm = sacc[t][e] * m;
+                    const float dp = dpacc[t][e] * inv - dl[e];
+                    const float w = dp * pm;
+                    colterm += i < j ? w : (i > j ? -w : 0.f);
+                    pf[4 * t + e] = f2bf(pm * inv);
+                    dsf[4 * t + e] = f2bf(dp * m);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                accv[ct] = mfma_bf16(tr_frag<D>(gbuf, h, ct, r, g), pf, accv[ct]);
+                acck[ct] = mfma_bf16(tr_frag<D>(qbuf, h, ct, r, g), dsf, acck[ct]);
+            }
+        }
+    }
+    if (!active) return;
+
+    colterm += __shfl_xor(colterm, 16, 64);
+    colterm += __shfl_xor(colterm, 32, 64);
+    if (KIND != kMaskLit && ok && g == 0) p.da_col[base + j] = colterm;
+    float x[NCT][4];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(p.k + (base + jc) * D + 16 * ct + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[ct][e] = (float)k4[e];
+    }
+    phi_backward<D, KIND>(x, acck);
+    if (ok) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            store4(p.dk, p.g_bf16, (base + j) * D + 16 * ct + 4 * g, acck[ct]);
+            store4(p.dv, p.g_bf16, (base + j) * D + 16 * ct + 4 * g, accv[ct]);
+        }
+    }
+}
+
+// ================================ dlog(lambda) ========================================================
+constexpr int kDllThreads = 256;
+
+// LION-S: one workgroup per (batch, head): dll_u = sum_{t >= u} (da_row_t + da_col_t) for u >= 1 (fp64),
+// dll_0 = 0.
+__global__ void __launch_bounds__(kDllThreads) bwd_dll_s_kernel(BwdParams p) {
+    __shared__ double sh[kDllThreads];
+    __shared__ double total;
+    const int tid = threadIdx.x, L = p.L;
+    const size_t base = (size_t)blockIdx.x * L;
+    const int seg = (L + kDllThreads - 1) / kDllThreads;
+    const int t0 = tid * seg, t1 = min(t0 + seg, L);
+    double s = 0.0;
+    for (int t = t0; t < t1; ++t) s += (double)p.da_row[base + t] + (double)p.da_col[base + t];
+    const double excl = block_excl_scan(s, sh, tid, kDllThreads);
+    if (tid == kDllThreads - 1) total = excl + s;
+    __syncthreads();
+    double run = excl;   // sum of dA over u < t
+    for (int t = t0; t < t1; ++t) {
+        p.dll[base + t] = t == 0 ? 0.f : (float)(total - run);
+        run += (double)p.da_row[base + t] + (double)p.da_col[base + t];
+    }
+}
+
+// LION-D: one workgroup per head: dll_h = sum over batch entries and tokens of t (da_row_t + da_col_t).
+__global__ void __launch_bounds__(kDllThreads) bwd_dll_d_kernel(BwdParams p, int B) {
+    __shared__ double sh[kDllThreads];
+    const int tid = threadIdx.x, L = p.L, h = blockIdx.x;
+    double s = 0.0;
+    for (int b = 0; b < B; ++b) {
+        const size_t base = ((size_t)b * p.H + h) * L;
+        for (int t = tid; t < L; t += kDllThreads) s += (double)t * ((double)p.da_row[base + t] + (double)p.da_col[base + t]);
+    }
+    sh[tid] = s;
+    __syncthreads();
+    for (int o = kDllThreads / 2; o > 0; o >>= 1) {
+        if (tid < o) sh[tid] += sh[tid + o];
+        __syncthreads();
+    }
+    if (tid == 0) p.dll[h] = (float)sh[0];
+}
+
+// ================================ host side ===========================================================
+struct BwdShape {
+    int nw, nsb, sk, nbuf;
+    size_t lds_dq, lds_dkv;
+};
+
+BwdShape bwd_shape(const BwdArgs &a) {
+    const int ntiles = (a.L + 15) / 16;
+    BwdShape sh;
+    sh.nw = ntiles >= 6 ? 8 : 4;
+    sh.nsb = (ntiles + sh.nw - 1) / sh.nw;
+    const size_t per_row = 2 * (size_t)a.d * 2;      // two bf16 rows per streamed position
+    const int lr = ((a.L + kKB - 1) / kKB) * kKB;
+    if ((size_t)lr * per_row <= kStageBytes) {
+        sh.sk = lr;
+        sh.nbuf = 1;
+    } else {
+        sh.sk = (int)(kStageBytes / 2 / per_row);
+        sh.nbuf = 2;
+    }
+    const int Lpad = ((a.L + sh.sk - 1) / sh.sk) * sh.sk;
+    size_t lds = (size_t)sh.nbuf * sh.sk * per_row;
+    if (a.kind != kMaskLit) lds += (size_t)Lpad * 4;
+    const size_t scan = a.kind == kMaskS ? (size_t)sh.nw * 64 * 8 : 0;
+    sh.lds_dq = lds + scan;
+    sh.lds_dkv = lds + 2 * (size_t)Lpad * 4 + scan;
+    return sh;
+}
+
+template <typename K>
+void allow_lds(K *kernel, size_t lds) {
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+}
+
+template <int D, int KIND>
+hipError_t launch_t(const BwdArgs &a, hipStream_t stream) {
+    const BwdShape sh = bwd_shape(a);
+    BwdParams p;
+    p.q = reinterpret_cast<const __bf16 *>(a.q);
+    p.k = reinterpret_cast<const __bf16 *>(a.k);
+    p.v = reinterpret_cast<const __bf16 *>(a.v);
+    p.ll = a.log_lambda;
+    p.H = a.H;
+    p.L = a.L;
+    p.y = reinterpret_cast<const __bf16 *>(a.y);
+    p.dy = reinterpret_cast<const __bf16 *>(a.dy);
+    p.den = a.den;
+    p.dq = a.dq;
+    p.dk = a.dk;
+    p.dv = a.dv;
+    p.g_bf16 = a.g_bf16 ? 1 : 0;
+    const size_t n = (size_t)a.B * a.H * a.L;
+    p.delta = reinterpret_cast<float *>(a.workspace);
+    p.da_row = p.delta + n;
+    p.da_col = p.da_row + n;
+    p.dll = a.dll;
+    p.nsb = sh.nsb;
+    p.nblocks = a.B * a.H * sh.nsb;
+    p.sk = sh.sk;
+    p.nbuf = sh.nbuf;
+    p.causal = a.causal ? 1 : 0;
+    allow_lds(&bwd_dq_kernel<D, KIND>, sh.lds_dq);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, KIND>), dim3(p.nblocks), dim3(sh.nw * 64), sh.lds_dq, stream, p);
+    allow_lds(&bwd_dkv_kernel<D, KIND>, sh.lds_dkv);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, KIND>), dim3(p.nblocks), dim3(sh.nw * 64), sh.lds_dkv, stream, p);
+    if constexpr (KIND == kMaskS)
+        hipLaunchKernelGGL(bwd_dll_s_kernel, dim3(a.B * a.H), dim3(kDllThreads), 0, stream, p);
+    else if constexpr (KIND == kMaskD)
+        hipLaunchKernelGGL(bwd_dll_d_kernel, dim3(a.H), dim3(kDllThreads), 0, stream, p, a.B);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_kind(const BwdArgs &a, hipStream_t stream) {
+    switch (a.kind) {
+    case kMaskLit: return launch_t<D, kMaskLit>(a, stream);
+    case kMaskD: return launch_t<D, kMaskD>(a, stream);
+    default: return launch_t<D, kMaskS>(a, stream);
+    }
+}
+
+}  // namespace
+
+Plan plan_full_bwd(const BwdArgs &a) {
+    Plan p;
+    const BwdShape sh = bwd_shape(a);
+    p.ok = (a.d == 32 || a.d == 64 || a.d == 128) && sh.lds_dkv <= kLdsPerWorkgroup;
+    p.workspace = 3 * (size_t)a.B * a.H * a.L * 4;
+    return p;
+}
+
+hipError_t launch_full_bwd(const BwdArgs &a, hipStream_t stream) {
+    switch (a.d) {
+    case 32: return dispatch_kind<32>(a, stream);
+    case 64: return dispatch_kind<64>(a, stream);
+    default: return dispatch_kind<128>(a, stream);
+    }
+}
+
+}  // namespace lion

@@ -31,13 +31,31 @@ struct Plan {
 
 constexpr size_t kLdsPerWorkgroup = 160 * 1024;   // gfx950 LDS available to one workgroup
 
+// Arguments of the full form's backward pass, validated by the ABI layer (bf16 inputs).
+struct BwdArgs {
+    const void *q, *k, *v;      // [B, H, L, d] bf16
+    const float *log_lambda;    // NULL (LIT), [H] (D), [B, H, L] (S)
+    int kind;
+    bool causal;
+    int B, H, L, d;
+    const void *y, *dy;         // [B, H, L, d] bf16
+    const float *den;           // [B, H, L]: the forward's row sums + eps
+    void *dq, *dk, *dv;         // [B, H, L, d]
+    bool g_bf16;                // element type of dq, dk, dv
+    float *dll;                 // NULL (LIT), [H] (D), [B, H, L] (S)
+    void *workspace;
+    size_t workspace_bytes;
+};
+
 Plan plan_full(const AttnArgs &a);
+Plan plan_full_bwd(const BwdArgs &a);
 Plan plan_chunk(const AttnArgs &a);
 Plan plan_birnn(const AttnArgs &a);
 
 // Each launcher enqueues its kernels on `stream` and returns hipSuccess or the launch error.
 // Callers check the form's plan first.
 hipError_t launch_full(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_full_bwd(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_chunk(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_birnn(const AttnArgs &a, hipStream_t stream);
 

@@ -90,7 +90,7 @@ enum lion_mask_kind { LION_MASK_LIT = 0, LION_MASK_D = 1, LION_MASK_S = 2 };
  * single-directional generation: reply item 5, "Is this method limited to bidirectional models?"). */
 enum { LION_CAUSAL = 4 };
 enum lion_dtype { LION_DTYPE_F32 = 0, LION_DTYPE_BF16 = 1 };
-enum lion_form { LION_FORM_FULL = 0, LION_FORM_CHUNK = 1, LION_FORM_BIRNN = 2 };
+enum lion_form { LION_FORM_FULL = 0, LION_FORM_CHUNK = 1, LION_FORM_BIRNN = 2, LION_FORM_FULL_BWD = 3 };
 enum lion_status {
     LION_OK = 0,
     LION_ERR_INVALID = -1,
@@ -125,6 +125,29 @@ LION_API int lion_attn_chunk(const void *q, const void *k, const void *v, const 
 LION_API int lion_attn_birnn(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, float eps,
                     int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/* Backward pass of the full form: the gradients of y = lion_attn_full(q, k, v, log_lambda) for an
+ * incoming gradient dy, i.e. dq, dk, dv and d log_lambda.  LION trains with the attention form (the
+ * OpenReview abstract: "trains like a Transformer"; Theorem 3.3 Eq. 25, reply "Concern 1"); the pages
+ * print no backward formulas, so this is the chain rule of the definition above:
+ *   delta_i = dy_i . y_i / den_i,   dp_ij = dy_i . v_j / den_i - delta_i,   dv_j = sum_i M_ij s_ij dy_i / den_i,
+ *   dphi(q_i) = sum_j M_ij dp_ij phi(k_j),  dphi(k_j) = sum_i M_ij dp_ij phi(q_i),  then phi's Jacobian;
+ *   d log(lambda_u) = sum over pairs (i, j) with min(i,j) < u <= max(i,j) of dp_ij M_ij s_ij
+ *   (LION-D: summed over every batch entry and token of the head; LION-S: entry 0 is always 0).
+ * q, k, v, log_lambda, mask_kind (LION_CAUSAL allowed), B, H, L, d: as for the forward call.
+ *   dtype      must be LION_DTYPE_BF16 (q, k, v, y, dy); fp32 inputs are LION_ERR_UNSUPPORTED.
+ *   d          32, 64 or 128 (16 is LION_ERR_UNSUPPORTED).
+ *   y, den     the forward call's y (bf16) and den_out (fp32 [B, H, L], row sum + eps) for these inputs.
+ *   dy         bf16 [B, H, L, d].
+ *   dq, dk, dv written, [B, H, L, d] of type grad_dtype (bf16 or fp32).
+ *   dlog_lambda  written: NULL for LIT; fp32 [H] for D; fp32 [B, H, L] for S.
+ *   workspace  >= lion_attn_workspace_bytes(LION_FORM_FULL_BWD, ...) bytes (12 B H L); contents on
+ *              entry do not matter.
+ * Errors as for the forward entry points. */
+LION_API int lion_attn_full_bwd(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind,
+                                int B, int H, int L, int d, int dtype, const void *y, const float *den,
+                                const void *dy, void *dq, void *dk, void *dv, int grad_dtype, float *dlog_lambda,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes `form` needs for these sizes (C is ignored except for LION_FORM_CHUNK).
  * Returns 0 when no workspace is needed, and (size_t)-1 for arguments the form rejects. */

@@ -56,7 +56,7 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.lion_oracle_attn_f64.argtypes = [dp, dp, dp, dp, d_, i, i, i, i, dp, dp, dp, dp]
     lib.lion_oracle_full_f64.argtypes = [dp, dp, dp, dp, i, d_, i, i, i, i, dp, dp, dp, dp]
     lib.lion_oracle_rows_f64.argtypes = [dp, dp, dp, dp, i, d_, i, i, i, i, lp, ctypes.c_long, dp, dp, dp, dp]
-    lib.lion_oracle_full_bwd_f64.argtypes = [dp, dp, dp, dp, i, d_, i, i, i, i, dp, dp, dp, dp, dp]
+    lib.lion_oracle_full_bwd_f64.argtypes = [dp, dp, dp, dp, i, d_, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp, dp]
     for f in ("phi", "mask", "attn", "full", "rows", "full_bwd"):
         getattr(lib, f"lion_oracle_{f}_f64").restype = ctypes.c_int
     _libs[path] = lib
@@ -153,18 +153,26 @@ def rows(q, k, v, log_lambda, kind, eps, row_ids, want_abs=False, lib_path: str 
     return (y, den, an, ad) if want_abs else (y, den)
 
 
-def full_bwd(q, k, v, log_lambda, kind, eps, dy, lib_path: str = LIB):
+def full_bwd(q, k, v, log_lambda, kind, eps, dy, want_abs=False, lib_path: str = LIB):
     """Gradients of the full-form definition for a loss with dL/dy = dy.
 
-    Returns (dq, dk, dv, dll); dll is None (LIT), [H] (D) or [B, H, L] (S)."""
+    Returns (dq, dk, dv, dll), then (adq, adk, adv, adll) if want_abs (the absolute-value companions
+    of the condition-aware gate); dll is None (LIT), [H] (D) or [B, H, L] (S)."""
     q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
     ll = None if log_lambda is None else _f64(log_lambda)
     B, H, L, d = q.shape
     dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
     base = _kind(kind) & 3
     dll = None if base == 0 else (np.empty((H,)) if base == 1 else np.empty((B, H, L)))
+    adq = adk = adv = adll = None
+    if want_abs:
+        adq, adk, adv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+        adll = None if dll is None else np.empty_like(dll)
     rc = load(lib_path).lion_oracle_full_bwd_f64(_p(q), _p(k), _p(v), _p(ll), _kind(kind), float(eps), B, H, L, d,
-                                                 _p(dy), _p(dq), _p(dk), _p(dv), _p(dll))
+                                                 _p(dy), _p(dq), _p(dk), _p(dv), _p(dll), _p(adq), _p(adk), _p(adv),
+                                                 _p(adll))
     if rc != 0:
         raise ValueError(f"lion_oracle_full_bwd_f64 returned {rc}")
+    if want_abs:
+        return dq, dk, dv, dll, adq, adk, adv, adll
     return dq, dk, dv, dll

@@ -326,12 +326,56 @@ int lion_oracle_rows_f64(const double *q, const double *k, const double *v, cons
  *   are taken with a difference array (add at min+1, subtract after max, then one running sum), the
  *   standard exact way to add a value over an index range.
  *   LION-D: every lambda_t of a head is exp(log_lambda[h]), so dlog_lambda[h] = the sum of those over
- *   every batch entry and token.  Causal: M_ij = 0 for j > i is a constant, contributing nothing. */
+ *   every batch entry and token.  Causal: M_ij = 0 for j > i is a constant, contributing nothing.
+ *
+ * Optional absolute-value companions (for the condition-aware parity gate, like absnum/absden of the
+ * forward): the same steps with every term replaced by its magnitude and every difference by a sum.
+ * The divisor and y come from the forward, whose first-order error (relative u per term) is at most
+ * u sum_j pbar_ij for den_i and u (sum_j pbar_ij |v_j| + |y_i| sum_j pbar_ij) / |den_i| for y_i
+ * (pbar_ij = M_ij sum_c |phi(q_i)_c| |phi(k_j)_c|, aden_i = sum_j pbar_ij), so those enter as
+ *   ag_i = |dy_i| (|den_i| + aden_i) / den_i^2,   ay_i = |y_i| + (sum_j pbar_ij |v_j| + |y_i| aden_i) / |den_i|,
+ *   adelta_i = sum_c ag_ic ay_ic,   adp_ij = sum_c ag_ic |v_jc| + adelta_i,   adv_j = sum_i pbar_ij ag_i,
+ *   adphi(q_i) = sum_j M_ij adp_ij |phi(k_j)|,   adphi(k_j) = sum_i M_ij adp_ij |phi(q_i)|,
+ *   then phi's Jacobian in absolute values, and adlog(lambda_t) = the range sums of adp_ij pbar_ij.
+ * A relative error of u in every term (and in den and y as above) moves each gradient by at most about
+ * u times its companion: the first-order bound, as in the forward's gate. */
 
 /* The Jacobian of phi at x, transposed, applied to g (one token's d channels).
  *   LIT: d(elu(x)+1)/dx = 1 for x > 0, exp(x) otherwise.   D: identity.
  *   S: phi = s / ||s|| with s = silu(x): dphi/ds = (I - phi phi^T) / ||s||, and
  *      dsilu/dx = sigmoid(x) (1 + x (1 - sigmoid(x))).  ||s|| = 0 gives 0 (phi is 0 there). */
+static void phi_grad_row(int kind, const double *x, const double *g, int d, double *dx);
+
+/* |Jacobian of phi|^T applied to a non-negative vector a (the companion of phi_grad_row):
+ *   LIT |phi'| a;  D a;  S |silu'| (a + |phi| (|phi| . a)) / ||silu(x)||. */
+static void phi_grad_abs_row(int kind, const double *x, const double *a, int d, double *out)
+{
+    int c;
+    if (kind == ORACLE_MASK_LIT) {
+        for (c = 0; c < d; ++c)
+            out[c] = a[c] * (x[c] > 0.0 ? 1.0 : exp(x[c]));
+    } else if (kind == ORACLE_MASK_D) {
+        for (c = 0; c < d; ++c)
+            out[c] = a[c];
+    } else {
+        double ss = 0.0, nrm, pa = 0.0;
+        for (c = 0; c < d; ++c) {
+            const double sv = x[c] / (1.0 + exp(-x[c]));
+            ss += sv * sv;
+        }
+        nrm = sqrt(ss);
+        for (c = 0; c < d; ++c) {
+            const double sv = x[c] / (1.0 + exp(-x[c]));
+            pa += (nrm > 0.0 ? fabs(sv) / nrm : 0.0) * a[c];
+        }
+        for (c = 0; c < d; ++c) {
+            const double sig = 1.0 / (1.0 + exp(-x[c]));
+            const double ph = nrm > 0.0 ? fabs(x[c] * sig) / nrm : 0.0;
+            out[c] = nrm > 0.0 ? fabs(sig * (1.0 + x[c] * (1.0 - sig))) * (a[c] + ph * pa) / nrm : 0.0;
+        }
+    }
+}
+
 static void phi_grad_row(int kind, const double *x, const double *g, int d, double *dx)
 {
     int c;
@@ -366,19 +410,24 @@ static void phi_grad_row(int kind, const double *x, const double *g, int d, doub
  *   lambda_0 never enters the mask). */
 int lion_oracle_full_bwd_f64(const double *q, const double *k, const double *v, const double *log_lambda,
                              int mask_kind, double eps, int B, int H, int L, int d, const double *dy, double *dq,
-                             double *dk, double *dv, double *dll)
+                             double *dk, double *dv, double *dll, double *adq, double *adk, double *adv,
+                             double *adll)
 {
     long bh, nbh = (long)B * H;
-    int err = 0, kind, causal;
-    double *dll_tok;
+    int err = 0, kind, causal, want_abs = adq && adk && adv;
+    double *dll_tok, *adll_tok;
     causal = (mask_kind & ORACLE_CAUSAL) != 0;
     kind = mask_kind & ~ORACLE_CAUSAL;
     if (!q || !k || !v || !dy || !dq || !dk || !dv || B < 1 || H < 1 || L < 1 || d < 1 || !(eps >= 0.0) ||
         kind < ORACLE_MASK_LIT || kind > ORACLE_MASK_S || (kind != ORACLE_MASK_LIT && (!log_lambda || !dll)))
         return ORACLE_EINVAL;
     dll_tok = (double *)calloc((size_t)nbh * L, sizeof(double));
-    if (!dll_tok)
+    adll_tok = (double *)calloc((size_t)nbh * L, sizeof(double));
+    if (!dll_tok || !adll_tok) {
+        free(dll_tok);
+        free(adll_tok);
         return ORACLE_ENOMEM;
+    }
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
     for (bh = 0; bh < nbh; ++bh) {
         size_t base = (size_t)bh * L;
@@ -392,8 +441,14 @@ int lion_oracle_full_bwd_f64(const double *q, const double *k, const double *v, 
         double *y = (double *)malloc(sizeof(double) * (size_t)d);
         double *g = (double *)malloc(sizeof(double) * (size_t)d);
         double *diff = (double *)calloc((size_t)L + 1, sizeof(double));
+        double *aphq = (double *)calloc((size_t)L * d, sizeof(double));
+        double *aphk = (double *)calloc((size_t)L * d, sizeof(double));
+        double *adiff = (double *)calloc((size_t)L + 1, sizeof(double));
+        double *ag = (double *)malloc(sizeof(double) * (size_t)d);
+        double *apv = (double *)malloc(sizeof(double) * (size_t)d);
         int i, j, c;
-        if (!phq || !phk || !dphq || !dphk || !lam || !m || !s || !y || !g || !diff) {
+        if (!phq || !phk || !dphq || !dphk || !lam || !m || !s || !y || !g || !diff || !aphq || !aphk || !adiff ||
+            !ag || !apv) {
             err |= 1;
         } else {
             for (j = 0; j < L; ++j) {
@@ -401,8 +456,11 @@ int lion_oracle_full_bwd_f64(const double *q, const double *k, const double *v, 
                 phi_row(kind, k + (base + j) * d, d, phk + (size_t)j * d);
             }
             decays(kind, log_lambda, H, L, bh, lam);
-            for (c = 0; c < L * d; ++c)
+            for (c = 0; c < L * d; ++c) {
                 dv[base * d + c] = 0.0;
+                if (want_abs)
+                    adv[base * d + c] = 0.0;
+            }
             for (i = 0; i < L; ++i) {
                 const double *pq = phq + (size_t)i * d;
                 const double *dyi = dy + (base + i) * d;
@@ -425,6 +483,45 @@ int lion_oracle_full_bwd_f64(const double *q, const double *k, const double *v, 
                     y[c] /= den;
                     g[c] = dyi[c] / den;
                     delta += g[c] * y[c];
+                }
+                if (want_abs) {
+                    /* the absolute-value companion of this row (see the comment above) */
+                    double adelta = 0.0, aden = 0.0;
+                    for (c = 0; c < d; ++c)
+                        apv[c] = 0.0;
+                    for (j = 0; j < L; ++j) {
+                        double pbar = 0.0;
+                        for (c = 0; c < d; ++c)
+                            pbar += fabs(pq[c]) * fabs(phk[(size_t)j * d + c]);
+                        pbar *= m[j];
+                        aden += pbar;
+                        for (c = 0; c < d; ++c)
+                            apv[c] += pbar * fabs(v[(base + j) * d + c]);
+                    }
+                    for (c = 0; c < d; ++c) {
+                        const double ay = fabs(y[c]) + (apv[c] + fabs(y[c]) * aden) / fabs(den);
+                        ag[c] = fabs(dyi[c]) * (fabs(den) + aden) / (den * den);
+                        adelta += ag[c] * ay;
+                    }
+                    for (j = 0; j < L; ++j) {
+                        double agv = 0.0, pbar = 0.0, adp;
+                        for (c = 0; c < d; ++c) {
+                            agv += ag[c] * fabs(v[(base + j) * d + c]);
+                            pbar += fabs(pq[c]) * fabs(phk[(size_t)j * d + c]);
+                        }
+                        pbar *= m[j];
+                        adp = agv + adelta;
+                        for (c = 0; c < d; ++c) {
+                            adv[(base + j) * d + c] += pbar * ag[c];
+                            aphq[(size_t)i * d + c] += m[j] * adp * fabs(phk[(size_t)j * d + c]);
+                            aphk[(size_t)j * d + c] += m[j] * adp * fabs(pq[c]);
+                        }
+                        if (j != i) {
+                            const int lo = i < j ? i : j, hi = i < j ? j : i;
+                            adiff[lo + 1] += adp * pbar;
+                            adiff[hi + 1] -= adp * pbar;
+                        }
+                    }
                 }
                 /* backward row */
                 for (j = 0; j < L; ++j) {
@@ -451,12 +548,18 @@ int lion_oracle_full_bwd_f64(const double *q, const double *k, const double *v, 
             for (j = 0; j < L; ++j) {
                 phi_grad_row(kind, q + (base + j) * d, dphq + (size_t)j * d, d, dq + (base + j) * d);
                 phi_grad_row(kind, k + (base + j) * d, dphk + (size_t)j * d, d, dk + (base + j) * d);
+                if (want_abs) {
+                    phi_grad_abs_row(kind, q + (base + j) * d, aphq + (size_t)j * d, d, adq + (base + j) * d);
+                    phi_grad_abs_row(kind, k + (base + j) * d, aphk + (size_t)j * d, d, adk + (base + j) * d);
+                }
             }
             {
-                double run = 0.0;
+                double run = 0.0, arun = 0.0;
                 for (j = 0; j < L; ++j) {
                     run += diff[j];
                     dll_tok[base + j] = run;
+                    arun += adiff[j];
+                    adll_tok[base + j] = arun;
                 }
             }
         }
@@ -470,20 +573,32 @@ int lion_oracle_full_bwd_f64(const double *q, const double *k, const double *v, 
         free(y);
         free(g);
         free(diff);
+        free(aphq);
+        free(aphk);
+        free(adiff);
+        free(ag);
+        free(apv);
     }
     if (!err && kind == ORACLE_MASK_S) {
         memcpy(dll, dll_tok, sizeof(double) * (size_t)nbh * L);
+        if (adll)
+            memcpy(adll, adll_tok, sizeof(double) * (size_t)nbh * L);
     } else if (!err && kind == ORACLE_MASK_D) {
         int h, t;
         long b2;
         for (h = 0; h < H; ++h) {
-            double acc = 0.0;
+            double acc = 0.0, aacc = 0.0;
             for (b2 = 0; b2 < B; ++b2)
-                for (t = 0; t < L; ++t)
+                for (t = 0; t < L; ++t) {
                     acc += dll_tok[((size_t)b2 * H + h) * L + t];
+                    aacc += adll_tok[((size_t)b2 * H + h) * L + t];
+                }
             dll[h] = acc;
+            if (adll)
+                adll[h] = aacc;
         }
     }
     free(dll_tok);
+    free(adll_tok);
     return err ? ORACLE_ENOMEM : ORACLE_OK;
 }

@@ -439,8 +439,28 @@ def pin_bwd_finite_differences(lib):
             _close(dll, num, 1e-6 * max(1.0, float(np.max(np.abs(num)))), f"dlog_lambda kind={kind}")
 
 
+def pin_bwd_abs_companions(lib):
+    """The backward's absolute-value companions bound their gradients (triangle inequality) and do not
+    change when dy or v flip sign -- what makes them a bound on rounding, not another gradient."""
+    rng = np.random.default_rng(92)
+    B, H, L, d = 2, 2, 9, 4
+    for kind in (oracle.MASK_LIT, oracle.MASK_D, oracle.MASK_S, oracle.MASK_S | oracle.CAUSAL):
+        q, k, v, dy = (rng.standard_normal((B, H, L, d)) for _ in range(4))
+        base = kind & 3
+        ll = None if base == 0 else (np.log(rng.uniform(0.3, 0.95, (H,))) if base == 1
+                                     else np.log(rng.uniform(0.2, 1.0, (B, H, L))))
+        r = oracle.full_bwd(q, k, v, ll, kind, 1e-3, dy, want_abs=True, lib_path=lib)
+        r2 = oracle.full_bwd(q, k, -v, ll, kind, 1e-3, -dy, want_abs=True, lib_path=lib)
+        for name, gr, ab, ab2 in zip(("dq", "dk", "dv", "dll"), r[:4], r[4:], r2[4:]):
+            if gr is None:
+                continue
+            assert np.all(np.abs(gr) <= ab * (1 + 1e-12)), f"{name} companion does not bound it (kind={kind})"
+            _close(ab2, ab, 1e-13, f"{name} companion under sign flips (kind={kind})")
+
+
 ALL_PINS = [
     pin_bwd_finite_differences,
+    pin_bwd_abs_companions,
     pin_phi_lit_is_elu_plus_one,
     pin_phi_s_is_normalised_silu,
     pin_phi_d_is_identity,

@@ -31,8 +31,8 @@ def header_symbols():
 def test_library_exports_every_declared_symbol():
     lib = lion.library()
     names = header_symbols()
-    assert set(names) == {"lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_workspace_bytes",
-                          "lion_status_str", "lion_attn_abi_version"}
+    assert set(names) == {"lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_full_bwd",
+                          "lion_attn_workspace_bytes", "lion_status_str", "lion_attn_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     assert lion.lion_attn_abi_version() == 1
@@ -127,6 +127,40 @@ def test_workspace_too_small(form, entry):
         assert entry(ws=P, wsb=need - 1, **kw) == WORKSPACE
         return
     pytest.skip("form needs no workspace at any tested size")
+
+
+def bwd(ws=P, wsb=1 << 30, **kw):
+    a = dict(q=P, k=P, v=P, ll=None, kind=0, B=2, H=3, L=17, d=64, dt=1, y=P, den=P, dy=P, dq=P, dk=P, dv=P, gdt=0,
+             dll=None)
+    a.update(kw)
+    return lion.library().lion_attn_full_bwd(a["q"], a["k"], a["v"], a["ll"], a["kind"], a["B"], a["H"], a["L"],
+                                             a["d"], a["dt"], a["y"], a["den"], a["dy"], a["dq"], a["dk"], a["dv"],
+                                             a["gdt"], a["dll"], ws, wsb, None)
+
+
+BWD_INVALID = [
+    ("null q", dict(q=None)), ("null y", dict(y=None)), ("null den", dict(den=None)), ("null dy", dict(dy=None)),
+    ("null dq", dict(dq=None)), ("null dk", dict(dk=None)), ("null dv", dict(dv=None)),
+    ("misaligned dy", dict(dy=MIS)), ("misaligned dv", dict(dv=MIS)), ("misaligned den", dict(den=MIS)),
+    ("LIT with dlog_lambda", dict(dll=P)), ("S without dlog_lambda", dict(kind=2, ll=P, dll=None)),
+    ("D without log_lambda", dict(kind=1, ll=None, dll=P)), ("misaligned dlog_lambda", dict(kind=1, ll=P, dll=MIS)),
+    ("bad grad dtype", dict(gdt=3)), ("bad kind", dict(kind=3)), ("L=0", dict(L=0)), ("misaligned workspace", dict(ws=MIS)),
+]
+
+
+@pytest.mark.parametrize("name,kw", BWD_INVALID, ids=[c[0] for c in BWD_INVALID])
+def test_bwd_invalid_arguments(name, kw):
+    assert bwd(**kw) == INVALID
+
+
+def test_bwd_unsupported_and_workspace():
+    assert bwd(dt=0) == UNSUPPORTED                 # fp32 inputs
+    assert bwd(d=16) == UNSUPPORTED
+    need = lion.lion_attn_workspace_bytes(lion.FORM_FULL_BWD, 2, 3, 17, 64, 0, 1)
+    assert need == 12 * 2 * 3 * 17
+    assert lion.lion_attn_workspace_bytes(lion.FORM_FULL_BWD, 2, 3, 17, 64, 0, 0) == SIZE_MAX
+    assert bwd(ws=None, wsb=need) == WORKSPACE
+    assert bwd(ws=P, wsb=need - 1) == WORKSPACE
 
 
 def test_binding_requires_built_library(monkeypatch, tmp_path):
