@@ -42,7 +42,8 @@ MUTANTS = [
     ("abs numerator without |v|", "anum[c] += pa * fabs(vj[c]);", "anum[c] += pa * vj[c];"),
     ("bwd delta term dropped", "dp = gv - delta;", "dp = gv;"),
     ("bwd dv without the mask", "dv[(base + j) * d + c] += m[j] * s[j] * g[c];", "dv[(base + j) * d + c] += s[j] * g[c];"),
-    ("bwd silu derivative wrong", "sig * (1.0 + x[c] * (1.0 - sig))", "sig * (1.0 + x[c] * sig)"),
+    ("bwd silu derivative wrong", "dx[c] = nrm > 0.0 ? sig * (1.0 + x[c] * (1.0 - sig))",
+     "dx[c] = nrm > 0.0 ? sig * (1.0 + x[c] * sig)"),
     ("bwd norm projection dropped", "(g[c] - ph * pg) / nrm", "g[c] / nrm"),
     ("bwd elu derivative flat", "g[c] * (x[c] > 0.0 ? 1.0 : exp(x[c]))", "g[c] * 1.0"),
     ("bwd decay range off by one", "diff[lo + 1] += w;", "diff[lo] += w;"),
