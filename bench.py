@@ -33,7 +33,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
 VALU_FP32_PEAK_TFLOPS = 157.3   # fp32 vector
 CSRC = os.path.join(ROOT, "bidirectional_linear_attention_lion_amd", "csrc")
-KERNEL_FILES = {"full": "lion_full.hip", "chunk": "lion_chunk.hip", "birnn": "lion_birnn.hip"}
+KERNEL_FILES = {"full": "lion_full.hip", "chunk": "lion_chunk.hip", "birnn": "lion_birnn.hip",
+                "full_bwd": "lion_full_bwd.hip"}
 
 
 def parse_args():
@@ -42,7 +43,9 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="vit_tiny_lit")
-    ap.add_argument("--forms", default=None, help="comma-separated forms (default: the workload's)")
+    ap.add_argument("--forms", default=None,
+                    help="comma-separated forms (default: the workload's); full_bwd times the full form's backward "
+                         "pass (bf16 gradients; y, den and a random dy prepared beforehand)")
     ap.add_argument("--chunk", type=int, default=None, help="chunk size C (default: the workload's first)")
     ap.add_argument("--causal", action="store_true",
                     help="the causal variant (keys after the query masked out) of the workload's mask")
@@ -122,6 +125,16 @@ def algorithmic(form: str, wl, C: int, causal: bool = False):
     elif wl.kind == 1:
         nbytes += 4 * H
     bh = B * H
+    if form == "full_bwd":
+        # read q, k, v, y, dy and den (and log(lambda)); write dq, dk, dv (bf16) and dlog(lambda)
+        nbytes = 8 * B * H * L * d * esz + 4 * B * H * L
+        if wl.kind == 2:
+            nbytes += 4 * B * H * L
+        elif wl.kind == 1:
+            nbytes += 4 * H
+        pairs = L * (L + 1) / 2 if causal else L * L
+        # S, dY V^T, dV, dphi(Q), dphi(K): five L x L x d products; mask, dp, dS and dA per pair
+        return nbytes, bh * (10 * pairs * d + 8 * pairs)
     if form == "full":
         pairs = L * (L + 1) / 2 if causal else L * L
         flops = bh * (4 * pairs * d + 2 * pairs)          # phi(Q)phi(K)^T, P V, mask and row sums
@@ -230,7 +243,21 @@ def main():
     sets = [(q0.clone(), k0.clone(), v0.clone(), torch.empty_like(q0)) for _ in range(nsets)]
     del q0, k0, v0
     ws = {}
-    for f, form_id in (("chunk", lion.FORM_CHUNK), ("birnn", lion.FORM_BIRNN)):
+    bwd_sets = []
+    if "full_bwd" in forms:
+        if wl.dtype != "bf16":
+            raise SystemExit("bench.py: full_bwd needs bf16 inputs")
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(wl.seed)
+        for (q, k, v, _) in sets:
+            den = torch.empty((wl.B, wl.H, wl.L), dtype=torch.float32, device=dev)
+            yb = lion.lion_attn_full(q, k, v, ll, kind, wl.eps, den_out=den, stream=stream)
+            dy = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            grads = tuple(torch.empty_like(q) for _ in range(3))
+            dll = None if wl.kind == 0 else torch.empty(
+                (wl.H,) if wl.kind == 1 else (wl.B, wl.H, wl.L), dtype=torch.float32, device=dev)
+            bwd_sets.append((yb, den, dy, grads, dll))
+    for f, form_id in (("chunk", lion.FORM_CHUNK), ("birnn", lion.FORM_BIRNN), ("full_bwd", lion.FORM_FULL_BWD)):
         nb = lion.lion_attn_workspace_bytes(form_id, wl.B, wl.H, wl.L, wl.d, C, 1 if wl.dtype == "bf16" else 0)
         ws[f] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
 
@@ -238,6 +265,10 @@ def main():
         q, k, v, y = sets[s % nsets]
         if form == "full":
             lion.lion_attn_full(q, k, v, ll, kind, wl.eps, y=y, stream=stream)
+        elif form == "full_bwd":
+            yb, den, dy, (dq, dk, dv), dll = bwd_sets[s % nsets]
+            lion.lion_attn_full_bwd(q, k, v, ll, kind, yb, den, dy, dq=dq, dk=dk, dv=dv, dlog_lambda=dll,
+                                    workspace=ws["full_bwd"], stream=stream)
         elif form == "chunk":
             lion.lion_attn_chunk(q, k, v, ll, kind, C, wl.eps, y=y, workspace=ws["chunk"], stream=stream)
         else:
