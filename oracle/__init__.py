@@ -57,7 +57,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.lion_oracle_full_f64.argtypes = [dp, dp, dp, dp, i, d_, i, i, i, i, dp, dp, dp, dp]
     lib.lion_oracle_rows_f64.argtypes = [dp, dp, dp, dp, i, d_, i, i, i, i, lp, ctypes.c_long, dp, dp, dp, dp]
     lib.lion_oracle_full_bwd_f64.argtypes = [dp, dp, dp, dp, i, d_, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp, dp]
-    for f in ("phi", "mask", "attn", "full", "rows", "full_bwd"):
+    lib.lion_oracle_selectivity_f64.argtypes = [dp, dp, dp, i, i, i, i, i, dp, dp, dp, dp]
+    for f in ("phi", "mask", "attn", "full", "rows", "full_bwd", "selectivity"):
         getattr(lib, f"lion_oracle_{f}_f64").restype = ctypes.c_int
     _libs[path] = lib
     return lib
@@ -176,3 +177,21 @@ def full_bwd(q, k, v, log_lambda, kind, eps, dy, want_abs=False, lib_path: str =
     if want_abs:
         return dq, dk, dv, dll, adq, adk, adv, adll
     return dq, dk, dv, dll
+
+
+def selectivity(x, w, bias, k=None, lib_path: str = LIB):
+    """LION-S's decay and key scale from the layer input: x [B, L, Dm], w [H, Dm], bias [H], optional
+    k [B, H, L, d].  Returns (log_lambda [B, H, L], key_scale [B, H, L], k_out or None)."""
+    x, w, bias = _f64(x), _f64(w), _f64(bias)
+    B, L, Dm = x.shape
+    H = w.shape[0]
+    ll = np.empty((B, H, L))
+    ks = np.empty((B, H, L))
+    kk = None if k is None else _f64(k)
+    d = 0 if kk is None else kk.shape[-1]
+    ko = None if kk is None else np.empty_like(kk)
+    rc = load(lib_path).lion_oracle_selectivity_f64(_p(x), _p(w), _p(bias), B, L, H, Dm, d, _p(kk), _p(ll), _p(ks),
+                                                    _p(ko))
+    if rc != 0:
+        raise ValueError(f"lion_oracle_selectivity_f64 returned {rc}")
+    return ll, ks, ko

@@ -602,3 +602,45 @@ int lion_oracle_full_bwd_f64(const double *q, const double *k, const double *v, 
     free(adll_tok);
     return err ? ORACLE_ENOMEM : ORACLE_OK;
 }
+
+/* ---- selectivity prologue of LION-S ------------------------------------------------------------------
+ * LION-S takes an input-dependent decay lambda_i, the scalar version of Mamba-2's state matrix [RB,
+ * reply "1. Some equations/notations are not clear enough", Eq. 5a], and the pages derive its two
+ * coefficients from zero-order-hold discretisation: exp(a_i) multiplies the state and exp(a_i) - 1 scales
+ * the input on the key path [RB, reply "Concern 8"].  Reading (the pages print neither formula): per head
+ * h, a_i = log(lambda_i) = log sigmoid(x_i . w_h + b_h) for the layer input x_i, so lambda_i = exp(a_i);
+ * the key scale is exp(a_i) - 1 = lambda_i - 1 = -sigmoid(-(x_i . w_h + b_h)), applied to the raw key
+ * (the attention then takes the scaled key as its k).
+ *   x: [B, L, Dm];  w: [H, Dm];  bias: [H]
+ *   log_lambda: [B, H, L];  key_scale (nullable): [B, H, L];
+ *   k, k_out (both or neither): [B, H, L, d], k_out = key_scale * k. */
+int lion_oracle_selectivity_f64(const double *x, const double *w, const double *bias, int B, int L, int H, int Dm,
+                                int d, const double *k, double *log_lambda, double *key_scale, double *k_out)
+{
+    long b;
+    if (!x || !w || !bias || !log_lambda || B < 1 || L < 1 || H < 1 || Dm < 1 || (!k != !k_out) ||
+        (k && d < 1))
+        return ORACLE_EINVAL;
+    for (b = 0; b < B; ++b) {
+        int h, i, c;
+        for (h = 0; h < H; ++h)
+            for (i = 0; i < L; ++i) {
+                const double *xi = x + ((size_t)b * L + i) * Dm;
+                const size_t row = ((size_t)b * H + h) * L + i;
+                double z = bias[h], ll, ks;
+                for (c = 0; c < Dm; ++c)
+                    z += xi[c] * w[(size_t)h * Dm + c];
+                /* log sigmoid(z) = -log(1 + exp(-z)), written so that exp never overflows */
+                ll = z >= 0.0 ? -log1p(exp(-z)) : z - log1p(exp(z));
+                /* lambda - 1 = sigmoid(z) - 1 = -sigmoid(-z) */
+                ks = -1.0 / (1.0 + exp(z));
+                log_lambda[row] = ll;
+                if (key_scale)
+                    key_scale[row] = ks;
+                if (k)
+                    for (c = 0; c < d; ++c)
+                        k_out[row * d + c] = ks * k[row * d + c];
+            }
+    }
+    return ORACLE_OK;
+}

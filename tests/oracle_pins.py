@@ -458,9 +458,35 @@ def pin_bwd_abs_companions(lib):
             _close(ab2, ab, 1e-13, f"{name} companion under sign flips (kind={kind})")
 
 
+def pin_selectivity(lib):
+    """log(lambda) = log sigmoid(x . w_h + b_h) and the key scale lambda - 1, against scipy's log_expit
+    and expit on a numpy matmul, with closed-form values at z = 0 and the far tails."""
+    from scipy.special import expit, log_expit
+    rng = np.random.default_rng(93)
+    B, L, H, Dm, d = 2, 7, 3, 40, 5
+    x = rng.standard_normal((B, L, Dm))
+    w = rng.standard_normal((H, Dm)) / np.sqrt(Dm)
+    bias = np.array([3.0, -1.0, 0.0])
+    k = rng.standard_normal((B, H, L, d))
+    ll, ks, ko = oracle.selectivity(x, w, bias, k, lib_path=lib)
+    z = np.einsum("blc,hc->bhl", x, w) + bias[None, :, None]
+    _close(ll, log_expit(z), 1e-14, "log lambda vs log_expit")
+    _close(ks, expit(z) - 1.0, 1e-14, "key scale vs expit - 1")
+    _close(ko, ks[..., None] * k, 1e-15, "scaled keys")
+    # closed forms: z = 0 -> log(1/2), -1/2; z = +-40 -> -exp(-40), 40 + log... (no overflow, no underflow to 0)
+    xz = np.zeros((1, 3, 1))
+    wz = np.ones((1, 1))
+    for bb, ll_ref, ks_ref in ((0.0, -np.log(2.0), -0.5), (40.0, -np.exp(-40.0), -np.exp(-40.0)),
+                               (-40.0, -40.0 - np.log1p(np.exp(-40.0)), -1.0 / (1.0 + np.exp(-40.0)))):
+        l1, k1, _ = oracle.selectivity(xz, wz, np.array([bb]), lib_path=lib)
+        _close(l1, np.full_like(l1, ll_ref), 1e-15, f"log lambda at z = {bb}")
+        _close(k1, np.full_like(k1, ks_ref), 1e-15, f"key scale at z = {bb}")
+
+
 ALL_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_abs_companions,
+    pin_selectivity,
     pin_phi_lit_is_elu_plus_one,
     pin_phi_s_is_normalised_silu,
     pin_phi_d_is_identity,

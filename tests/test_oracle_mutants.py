@@ -50,6 +50,11 @@ MUTANTS = [
     ("bwd key grad from its own phi", "dphk[(size_t)j * d + c] += ds * pq[c];",
      "dphk[(size_t)j * d + c] += ds * phk[(size_t)j * d + c];"),
     ("bwd per-head decay from one batch entry", "for (b2 = 0; b2 < B; ++b2)", "for (b2 = 0; b2 < 1; ++b2)"),
+    ("selectivity bias dropped", "double z = bias[h], ll, ks;", "double z = 0.0, ll, ks;"),
+    ("selectivity log sigmoid sign", "ll = z >= 0.0 ? -log1p(exp(-z)) : z - log1p(exp(z));",
+     "ll = z >= 0.0 ? -log1p(exp(z)) : z - log1p(exp(z));"),
+    ("selectivity key scale is lambda", "ks = -1.0 / (1.0 + exp(z));", "ks = 1.0 / (1.0 + exp(-z));"),
+    ("selectivity weights of the wrong head", "z += xi[c] * w[(size_t)h * Dm + c];", "z += xi[c] * w[c];"),
 ]
 
 
