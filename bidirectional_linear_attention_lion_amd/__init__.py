@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     lion_attn_full,
     lion_attn_full_bwd,
     lion_attn_workspace_bytes,
+    lion_selectivity,
     lion_status_str,
     library,
 )

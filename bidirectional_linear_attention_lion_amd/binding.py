@@ -42,7 +42,9 @@ def library() -> ctypes.CDLL:
     lib.lion_attn_chunk.argtypes = common + [i, f, i, i, i, i, i, vp, i, fp, vp, sz, vp]
     lib.lion_attn_birnn.argtypes = common + [f, i, i, i, i, i, vp, i, fp, vp, sz, vp]
     lib.lion_attn_full_bwd.argtypes = common + [i, i, i, i, i, vp, fp, vp, vp, vp, vp, i, fp, vp, sz, vp]
-    for fn in ("lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_full_bwd", "lion_attn_abi_version"):
+    lib.lion_selectivity.argtypes = [vp, vp, fp, i, i, i, i, fp, fp, vp, vp, i, vp]
+    for fn in ("lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_full_bwd", "lion_selectivity",
+               "lion_attn_abi_version"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.lion_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.lion_attn_workspace_bytes.restype = sz
@@ -167,3 +169,28 @@ def lion_attn_full_bwd(q, k, v, log_lambda, mask_kind, y, den, dy, *, grad_dtype
     if rc != 0:
         raise LionError("lion_attn_full_bwd", rc)
     return dq, dk, dv, dlog_lambda
+
+
+def lion_selectivity(x, w, bias, *, k=None, k_out=None, want_key_scale=False, stream=None):
+    """LION-S decays from the layer input x [B, L, Dm] (bf16), w [H, Dm] (bf16), bias [H] (fp32).
+
+    Returns (log_lambda [B, H, L], key_scale or None, k_out or None); with k [B, H, L, d] the scaled keys
+    are written to k_out (allocated if not given; may be k itself)."""
+    import torch
+    B, L, Dm = x.shape
+    H = w.shape[0]
+    ll = torch.empty((B, H, L), dtype=torch.float32, device=x.device)
+    ks = torch.empty((B, H, L), dtype=torch.float32, device=x.device) if want_key_scale else None
+    d = 0
+    if k is not None:
+        d = k.shape[-1]
+        if k_out is None:
+            k_out = torch.empty_like(k)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    sptr = ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    rc = library().lion_selectivity(_ptr(x), _ptr(w), _ptr(bias), B, L, H, Dm, _ptr(ll), _ptr(ks), _ptr(k),
+                                    _ptr(k_out), d, sptr)
+    if rc != 0:
+        raise LionError("lion_selectivity", rc)
+    return ll, ks, k_out

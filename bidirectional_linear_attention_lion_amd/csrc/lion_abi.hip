@@ -154,6 +154,33 @@ int lion_attn_full_bwd(const void *q, const void *k, const void *v, const float 
     return status_of(lion::launch_full_bwd(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int lion_selectivity(const void *x, const void *w, const float *bias, int B, int L, int H, int Dm, float *log_lambda,
+                     float *key_scale, const void *k, void *k_out, int d, void *stream) {
+    if (!x || !w || !bias || !log_lambda) return LION_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(bias) || !aligned16(log_lambda)) return LION_ERR_INVALID;
+    if (key_scale && !aligned16(key_scale)) return LION_ERR_INVALID;
+    if (!k != !k_out) return LION_ERR_INVALID;
+    if (k && (!aligned16(k) || !aligned16(k_out) || d < 1)) return LION_ERR_INVALID;
+    if (B < 1 || L < 1 || H < 1 || Dm < 1) return LION_ERR_INVALID;
+    if ((long long)L > kMaxL || (long long)B * H * L > kMaxRows || (long long)B * L * Dm > (1LL << 40))
+        return LION_ERR_INVALID;
+    lion::SelArgs a;
+    a.x = x;
+    a.w = w;
+    a.bias = bias;
+    a.B = B;
+    a.L = L;
+    a.H = H;
+    a.Dm = Dm;
+    a.log_lambda = log_lambda;
+    a.key_scale = key_scale;
+    a.k = k;
+    a.k_out = k_out;
+    a.d = k ? d : 0;
+    if (!lion::plan_selectivity(a).ok) return LION_ERR_UNSUPPORTED;
+    return status_of(lion::launch_selectivity(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, int dtype) {
     if (B < 1 || H < 1 || L < 1 || !d_supported(d) || (long long)L > kMaxL || (long long)B * H * L > kMaxRows)
         return (size_t)-1;

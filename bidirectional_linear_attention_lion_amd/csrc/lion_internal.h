@@ -47,7 +47,20 @@ struct BwdArgs {
     size_t workspace_bytes;
 };
 
+// Arguments of the LION-S selectivity prologue, validated by the ABI layer.
+struct SelArgs {
+    const void *x, *w;          // [B, L, Dm], [H, Dm] bf16
+    const float *bias;          // [H]
+    int B, L, H, Dm;
+    float *log_lambda;          // [B, H, L]
+    float *key_scale;           // nullable [B, H, L]
+    const void *k;              // nullable [B, H, L, d] bf16
+    void *k_out;                // with k
+    int d;
+};
+
 Plan plan_full(const AttnArgs &a);
+Plan plan_selectivity(const SelArgs &a);
 Plan plan_full_bwd(const BwdArgs &a);
 Plan plan_chunk(const AttnArgs &a);
 Plan plan_birnn(const AttnArgs &a);
@@ -56,6 +69,7 @@ Plan plan_birnn(const AttnArgs &a);
 // Callers check the form's plan first.
 hipError_t launch_full(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_full_bwd(const BwdArgs &a, hipStream_t stream);
+hipError_t launch_selectivity(const SelArgs &a, hipStream_t stream);
 hipError_t launch_chunk(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_birnn(const AttnArgs &a, hipStream_t stream);
 

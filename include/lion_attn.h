@@ -149,6 +149,23 @@ LION_API int lion_attn_full_bwd(const void *q, const void *k, const void *v, con
                                 const void *dy, void *dq, void *dk, void *dv, int grad_dtype, float *dlog_lambda,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* LION-S selectivity prologue: the per-token decays from the layer input, as log(lambda) for the
+ * attention entry points, and the key-path input scale of zero-order-hold discretisation.  Sources:
+ * lambda_i input-dependent, the scalar version of Mamba-2's state matrix (reply "1. Some
+ * equations/notations are not clear enough", Eq. 5a); exp(a_i) on the state and exp(a_i) - 1 on the
+ * input (reply "Concern 8").  The pages print neither formula; reading: per head h,
+ *   z_i = x_i . w_h + b_h,  log_lambda = a_i = log sigmoid(z_i),  key_scale = exp(a_i) - 1 = -sigmoid(-z_i),
+ *   k_out = key_scale * k  (the raw key; pass k_out as the attention's k).
+ *   x          bf16 [B, L, Dm], the layer input shared by the heads;  w  bf16 [H, Dm];  bias  fp32 [H].
+ *   Dm         a multiple of 32 (else LION_ERR_UNSUPPORTED).
+ *   log_lambda written, fp32 [B, H, L].
+ *   key_scale  NULL, or written, fp32 [B, H, L].
+ *   k, k_out   both NULL, or bf16 [B, H, L, d] with d a multiple of 8 (else LION_ERR_UNSUPPORTED);
+ *              k_out may equal k (in place).
+ * Device pointers 16-byte aligned; errors as for the attention entry points; no workspace. */
+LION_API int lion_selectivity(const void *x, const void *w, const float *bias, int B, int L, int H, int Dm,
+                              float *log_lambda, float *key_scale, const void *k, void *k_out, int d, void *stream);
+
 /* Workspace bytes `form` needs for these sizes (C is ignored except for LION_FORM_CHUNK).
  * Returns 0 when no workspace is needed, and (size_t)-1 for arguments the form rejects. */
 LION_API size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, int dtype);

@@ -32,7 +32,8 @@ def test_library_exports_every_declared_symbol():
     lib = lion.library()
     names = header_symbols()
     assert set(names) == {"lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_full_bwd",
-                          "lion_attn_workspace_bytes", "lion_status_str", "lion_attn_abi_version"}
+                          "lion_selectivity", "lion_attn_workspace_bytes", "lion_status_str",
+                          "lion_attn_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     assert lion.lion_attn_abi_version() == 1
@@ -161,6 +162,28 @@ def test_bwd_unsupported_and_workspace():
     assert lion.lion_attn_workspace_bytes(lion.FORM_FULL_BWD, 2, 3, 17, 64, 0, 0) == SIZE_MAX
     assert bwd(ws=None, wsb=need) == WORKSPACE
     assert bwd(ws=P, wsb=need - 1) == WORKSPACE
+
+
+def sel(x=P, w=P, bias=P, B=2, L=17, H=3, Dm=64, ll=P, ks=None, k=None, ko=None, d=64):
+    return lion.library().lion_selectivity(x, w, bias, B, L, H, Dm, ll, ks, k, ko, d, None)
+
+
+SEL_INVALID = [
+    ("null x", dict(x=None)), ("null w", dict(w=None)), ("null bias", dict(bias=None)), ("null out", dict(ll=None)),
+    ("misaligned x", dict(x=MIS)), ("misaligned key scale", dict(ks=MIS)), ("k without k_out", dict(k=P)),
+    ("k_out without k", dict(ko=P)), ("misaligned k_out", dict(k=P, ko=MIS)), ("k with d=0", dict(k=P, ko=P, d=0)),
+    ("B=0", dict(B=0)), ("L=0", dict(L=0)), ("H=0", dict(H=0)), ("Dm=0", dict(Dm=0)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SEL_INVALID, ids=[c[0] for c in SEL_INVALID])
+def test_selectivity_invalid_arguments(name, kw):
+    assert sel(**kw) == INVALID
+
+
+def test_selectivity_unsupported():
+    assert sel(Dm=48) == UNSUPPORTED
+    assert sel(k=P, ko=P, d=12) == UNSUPPORTED
 
 
 def test_binding_requires_built_library(monkeypatch, tmp_path):
