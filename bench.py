@@ -34,7 +34,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
 VALU_FP32_PEAK_TFLOPS = 157.3   # fp32 vector
 CSRC = os.path.join(ROOT, "bidirectional_linear_attention_lion_amd", "csrc")
 KERNEL_FILES = {"full": "lion_full.hip", "chunk": "lion_chunk.hip", "birnn": "lion_birnn.hip",
-                "full_bwd": "lion_full_bwd.hip"}
+                "full_bwd": "lion_full_bwd.hip", "selectivity": "lion_selectivity.hip"}
+SEL_WIDTH = 1024   # layer-input width of the selectivity prologue (the BERT-Large-shaped recipe)
 
 
 def parse_args():
@@ -45,7 +46,8 @@ def parse_args():
     ap.add_argument("--workload", default="vit_tiny_lit")
     ap.add_argument("--forms", default=None,
                     help="comma-separated forms (default: the workload's); full_bwd times the full form's backward "
-                         "pass (bf16 gradients; y, den and a random dy prepared beforehand)")
+                         "pass (bf16 gradients; y, den and a random dy prepared beforehand); selectivity times "
+                         "the LION-S prologue (log lambda from a [B, L, 1024] layer input, keys scaled)")
     ap.add_argument("--chunk", type=int, default=None, help="chunk size C (default: the workload's first)")
     ap.add_argument("--causal", action="store_true",
                     help="the causal variant (keys after the query masked out) of the workload's mask")
@@ -125,6 +127,10 @@ def algorithmic(form: str, wl, C: int, causal: bool = False):
     elif wl.kind == 1:
         nbytes += 4 * H
     bh = B * H
+    if form == "selectivity":
+        # read x [B, L, 1024] and w, write log(lambda); read and write the keys
+        nbytes = B * L * SEL_WIDTH * 2 + H * SEL_WIDTH * 2 + 4 * H + 4 * B * H * L + 2 * B * H * L * d * 2
+        return nbytes, 2 * B * L * H * SEL_WIDTH + B * H * L * (d + 8)
     if form == "full_bwd":
         # read q, k, v, y, dy and den (and log(lambda)); write dq, dk, dv (bf16) and dlog(lambda)
         nbytes = 8 * B * H * L * d * esz + 4 * B * H * L
@@ -257,6 +263,17 @@ def main():
             dll = None if wl.kind == 0 else torch.empty(
                 (wl.H,) if wl.kind == 1 else (wl.B, wl.H, wl.L), dtype=torch.float32, device=dev)
             bwd_sets.append((yb, den, dy, grads, dll))
+    sel = None
+    if "selectivity" in forms:
+        if wl.dtype != "bf16":
+            raise SystemExit("bench.py: selectivity needs bf16 inputs")
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(wl.seed + 1)
+        # one layer input per input set, so x streams from HBM like the other operands
+        xs = [torch.randn((wl.B, wl.L, SEL_WIDTH), generator=gen, device=dev).to(torch.bfloat16) for _ in range(nsets)]
+        ws_ = (torch.randn((wl.H, SEL_WIDTH), generator=gen, device=dev) / SEL_WIDTH ** 0.5).to(torch.bfloat16)
+        bs = torch.full((wl.H,), 3.0, dtype=torch.float32, device=dev)
+        sel = (xs, ws_, bs)
     for f, form_id in (("chunk", lion.FORM_CHUNK), ("birnn", lion.FORM_BIRNN), ("full_bwd", lion.FORM_FULL_BWD)):
         nb = lion.lion_attn_workspace_bytes(form_id, wl.B, wl.H, wl.L, wl.d, C, 1 if wl.dtype == "bf16" else 0)
         ws[f] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
@@ -265,6 +282,8 @@ def main():
         q, k, v, y = sets[s % nsets]
         if form == "full":
             lion.lion_attn_full(q, k, v, ll, kind, wl.eps, y=y, stream=stream)
+        elif form == "selectivity":
+            lion.lion_selectivity(sel[0][s % nsets], sel[1], sel[2], k=k, k_out=y, stream=stream)
         elif form == "full_bwd":
             yb, den, dy, (dq, dk, dv), dll = bwd_sets[s % nsets]
             lion.lion_attn_full_bwd(q, k, v, ll, kind, yb, den, dy, dq=dq, dk=dk, dv=dv, dlog_lambda=dll,
