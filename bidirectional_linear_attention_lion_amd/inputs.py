@@ -145,3 +145,12 @@ def random_inputs(B, H, L, d, kind, dtype="bf16", seed=0, lam_recipe=None, eps=1
     wl = Workload(f"random_{KIND_NAME[kind]}", B, H, L, d, dtype, kind, recipe, ("full", "chunk", "birnn"),
                   eps=eps, seed=seed)
     return make_inputs(wl)
+
+
+def column_major_order(rows: int, cols: int, cls: bool = True) -> np.ndarray:
+    """Tokens of an image in column-major patch order: the class token (if any) first, then patch (r, c)
+    of the row-major grid -- token cls + r * cols + c -- listed column by column.  int32 [L]."""
+    off = 1 if cls else 0
+    grid = np.arange(rows * cols, dtype=np.int32).reshape(rows, cols) + off
+    head = np.zeros(off, dtype=np.int32)
+    return np.concatenate([head, grid.T.reshape(-1)]).astype(np.int32)

@@ -58,7 +58,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.lion_oracle_rows_f64.argtypes = [dp, dp, dp, dp, i, d_, i, i, i, i, lp, ctypes.c_long, dp, dp, dp, dp]
     lib.lion_oracle_full_bwd_f64.argtypes = [dp, dp, dp, dp, i, d_, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp, dp]
     lib.lion_oracle_selectivity_f64.argtypes = [dp, dp, dp, i, i, i, i, i, dp, dp, dp, dp]
-    for f in ("phi", "mask", "attn", "full", "rows", "full_bwd", "selectivity"):
+    lib.lion_oracle_full2_f64.argtypes = [dp, dp, dp, dp, i, d_, lp, i, i, i, i, dp, dp, dp, dp]
+    for f in ("phi", "mask", "attn", "full", "rows", "full_bwd", "selectivity", "full2"):
         getattr(lib, f"lion_oracle_{f}_f64").restype = ctypes.c_int
     _libs[path] = lib
     return lib
@@ -195,3 +196,22 @@ def selectivity(x, w, bias, k=None, lib_path: str = LIB):
     if rc != 0:
         raise ValueError(f"lion_oracle_selectivity_f64 returned {rc}")
     return ll, ks, ko
+
+
+def full2(q, k, v, log_lambda, kind, eps, order, want_abs=False, lib_path: str = LIB):
+    """The full definition with the average of two masks: the tokens' own order and ``order`` ([L], the
+    tokens listed in a second order).  Returns (y, den) or (y, den, absnum, absden)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    ll = None if log_lambda is None else _f64(log_lambda)
+    B, H, L, d = q.shape
+    o = np.ascontiguousarray(order, dtype=np.int64)
+    y = np.empty_like(q)
+    den = np.empty((B, H, L))
+    an = np.empty_like(q) if want_abs else None
+    ad = np.empty((B, H, L)) if want_abs else None
+    rc = load(lib_path).lion_oracle_full2_f64(_p(q), _p(k), _p(v), _p(ll), _kind(kind), float(eps),
+                                              o.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), B, H, L, d, _p(y),
+                                              _p(den), _p(an), _p(ad))
+    if rc != 0:
+        raise ValueError(f"lion_oracle_full2_f64 returned {rc}")
+    return (y, den, an, ad) if want_abs else (y, den)

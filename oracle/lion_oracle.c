@@ -644,3 +644,86 @@ int lion_oracle_selectivity_f64(const double *x, const double *w, const double *
     }
     return ORACLE_OK;
 }
+
+/* ---- two token orders, averaged masks (patch-reordered LION-D / LION-S) -------------------------------
+ * For images the pages average the masks of two patch orders instead of choosing one: M = (M_b + M_c) / 2
+ * [RB, reply "P2: Comparison against vision SSMs", item 1, Figure 7 b and c; "LION-D natural / LION-S
+ * natural" rows of the ImageNet table].  Reading (the figure is not on the pages): M_b is the mask of the
+ * tokens' own order and M_c the same product-of-decays mask taken along a second order of the same
+ * tokens, order[p] = the token at position p of it (for an image: the column-major raster of the patch
+ * grid); each token keeps its own decay, so (M_c)_ij multiplies the decays of the tokens strictly after
+ * min(pos(i), pos(j)) up to and including max(pos(i), pos(j)) in that order.
+ *   order: [L], a permutation of 0 .. L-1 shared by every (batch, head); other arguments as
+ *   lion_oracle_full_f64 (mask_kind LIT, D or S; no causal flag). */
+int lion_oracle_full2_f64(const double *q, const double *k, const double *v, const double *log_lambda, int mask_kind,
+                          double eps, const long *order, int B, int H, int L, int d, double *y, double *den,
+                          double *absnum, double *absden)
+{
+    long bh, nbh = (long)B * H;
+    int err = 0, i;
+    char *seen;
+    if (!q || !k || !v || !y || !order || B < 1 || H < 1 || L < 1 || d < 1 || !(eps >= 0.0) ||
+        mask_kind < ORACLE_MASK_LIT || mask_kind > ORACLE_MASK_S || (mask_kind != ORACLE_MASK_LIT && !log_lambda))
+        return ORACLE_EINVAL;
+    seen = (char *)calloc((size_t)L, 1);
+    if (!seen)
+        return ORACLE_ENOMEM;
+    for (i = 0; i < L; ++i) {
+        if (order[i] < 0 || order[i] >= L || seen[order[i]])
+            err = 1;
+        else
+            seen[order[i]] = 1;
+    }
+    free(seen);
+    if (err)
+        return ORACLE_EINVAL;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (bh = 0; bh < nbh; ++bh) {
+        size_t base = (size_t)bh * L;
+        double *phq = (double *)malloc(sizeof(double) * (size_t)L * d);
+        double *phk = (double *)malloc(sizeof(double) * (size_t)L * d);
+        double *lam = (double *)malloc(sizeof(double) * (size_t)L);
+        double *lamc = (double *)malloc(sizeof(double) * (size_t)L);
+        double *mb = (double *)malloc(sizeof(double) * (size_t)L);
+        double *mc = (double *)malloc(sizeof(double) * (size_t)L);
+        double *m = (double *)malloc(sizeof(double) * (size_t)L);
+        long *pos = (long *)malloc(sizeof(long) * (size_t)L);
+        double *num = (double *)malloc(sizeof(double) * (size_t)d);
+        double *anum = (double *)malloc(sizeof(double) * (size_t)d);
+        int j, p;
+        if (!phq || !phk || !lam || !lamc || !mb || !mc || !m || !pos || !num || !anum) {
+            err |= 1;
+        } else {
+            for (j = 0; j < L; ++j) {
+                phi_row(mask_kind, q + (base + j) * d, d, phq + (size_t)j * d);
+                phi_row(mask_kind, k + (base + j) * d, d, phk + (size_t)j * d);
+            }
+            decays(mask_kind, log_lambda, H, L, bh, lam);
+            /* the decays listed along the second order, and each token's position in it */
+            for (p = 0; p < L; ++p) {
+                lamc[p] = lam[order[p]];
+                pos[order[p]] = p;
+            }
+            for (i = 0; i < L; ++i) {
+                mask_row(lam, L, i, 0, mb);
+                mask_row(lamc, L, (int)pos[i], 0, mc);   /* indexed by position in the second order */
+                for (j = 0; j < L; ++j)
+                    m[j] = 0.5 * (mb[j] + mc[pos[j]]);
+                attn_row(phq + (size_t)i * d, phk, v + base * d, m, L, d, eps, num, anum, y + (base + i) * d,
+                         den ? den + base + i : NULL, absnum ? absnum + (base + i) * d : NULL,
+                         absden ? absden + base + i : NULL);
+            }
+        }
+        free(phq);
+        free(phk);
+        free(lam);
+        free(lamc);
+        free(mb);
+        free(mc);
+        free(m);
+        free(pos);
+        free(num);
+        free(anum);
+    }
+    return err ? ORACLE_ENOMEM : ORACLE_OK;
+}

@@ -483,10 +483,98 @@ def pin_selectivity(lib):
         _close(k1, np.full_like(k1, ks_ref), 1e-15, f"key scale at z = {bb}")
 
 
+def _brute_rational_two(q, k, v, lam, eps, order):
+    """Exact rational evaluation of the two-order mask (phi = identity): the decay products taken along
+    the tokens' own order and along ``order``, averaged."""
+    L, d = len(q), len(q[0])
+    pos = {t: p for p, t in enumerate(order)}
+    ys = []
+    for i in range(L):
+        num = [Fraction(0)] * d
+        den = Fraction(0)
+        for j in range(L):
+            mb = Fraction(1)
+            for t in range(min(i, j) + 1, max(i, j) + 1):
+                mb *= lam[t]
+            mc = Fraction(1)
+            for p in range(min(pos[i], pos[j]) + 1, max(pos[i], pos[j]) + 1):
+                mc *= lam[order[p]]
+            s = sum((q[i][c] * k[j][c] for c in range(d)), Fraction(0)) * (mb + mc) / 2
+            den += s
+            for c in range(d):
+                num[c] += s * v[j][c]
+        ys.append([n / (den + eps) for n in num])
+    return ys
+
+
+def pin_two_order_mask(lib):
+    """Averaged masks of two token orders: brute force on tiny inputs with arbitrary permutations
+    (per-token decays, LION-S), exact rationals for LION-D; the identity order (and, for LION-D, the
+    reversed order, which keeps every distance) reduce to the one-order definition; LIT is unchanged by
+    any order."""
+    rng = np.random.default_rng(94)
+    # LION-S: phi from the (separately pinned) phi routine, the two masks as explicit decay products
+    for trial in range(8):
+        L = int(rng.integers(1, 8))
+        d = int(rng.integers(1, 4))
+        q, k, v = (rng.standard_normal((1, 1, L, d)) for _ in range(3))
+        lam = rng.uniform(0.2, 1.0, L)
+        order = [int(t) for t in rng.permutation(L)]
+        pos = {t: p for p, t in enumerate(order)}
+        M = np.zeros((L, L))
+        for i in range(L):
+            for j in range(L):
+                mb = 1.0
+                for t in range(min(i, j) + 1, max(i, j) + 1):
+                    mb *= lam[t]
+                mc = 1.0
+                for p in range(min(pos[i], pos[j]) + 1, max(pos[i], pos[j]) + 1):
+                    mc *= lam[order[p]]
+                M[i, j] = 0.5 * (mb + mc)
+        phq = oracle.phi("s", q[0, 0], lib_path=lib)
+        phk = oracle.phi("s", k[0, 0], lib_path=lib)
+        P = M * (phq @ phk.T)
+        ref = (P @ v[0, 0]) / (P.sum(1) + 1e-3)[:, None]
+        y, _ = oracle.full2(q, k, v, np.log(lam)[None, None], "s", 1e-3, order, lib_path=lib)
+        _close(y[0, 0], ref, 1e-12, f"two-order mask, per-token decays, trial {trial}")
+    # kind D (phi = identity, one decay per head) against exact rationals
+    for trial in range(6):
+        L = int(rng.integers(2, 7))
+        d = 2
+        q = [[Fraction(int(rng.integers(1, 9)), 4) for _ in range(d)] for _ in range(L)]
+        k = [[Fraction(int(rng.integers(1, 9)), 8) for _ in range(d)] for _ in range(L)]
+        v = [[Fraction(int(rng.integers(-16, 17)), 2) for _ in range(d)] for _ in range(L)]
+        lam1 = Fraction(int(rng.integers(2, 16)), 16)
+        lam = [lam1] * L
+        order = [int(t) for t in rng.permutation(L)]
+        ys = _brute_rational_two(q, k, v, lam, Fraction(1, 512), order)
+        f = lambda a: np.array([[float(t) for t in r] for r in a])[None, None]
+        y, _ = oracle.full2(f(q), f(k), f(v), np.array([np.log(float(lam1))]), "d", 1 / 512, order, lib_path=lib)
+        _close(y[0, 0], np.array([[float(t) for t in r] for r in ys]), 1e-13, f"two-order D trial {trial}")
+    # reductions
+    B, H, L, d = 2, 2, 23, 5
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    ll_s = np.log(rng.uniform(0.3, 1.0, (B, H, L)))
+    ll_d = np.log(np.array([0.9, 0.6]))
+    ident = np.arange(L)
+    for kind, ll in (("s", ll_s), ("d", ll_d)):
+        y1, d1 = oracle.full(q, k, v, ll, kind, 1e-3, lib_path=lib)
+        y2, d2 = oracle.full2(q, k, v, ll, kind, 1e-3, ident, lib_path=lib)
+        _close(y2, y1, 1e-14, f"identity second order, kind {kind}")
+    yr, _ = oracle.full2(q, k, v, ll_d, "d", 1e-3, ident[::-1], lib_path=lib)
+    y1, _ = oracle.full(q, k, v, ll_d, "d", 1e-3, lib_path=lib)
+    _close(yr, y1, 1e-13, "reversed order keeps LION-D's distances")
+    perm = rng.permutation(L)
+    yl, _ = oracle.full2(q, k, v, None, "lit", 1e-3, perm, lib_path=lib)
+    y1, _ = oracle.full(q, k, v, None, "lit", 1e-3, lib_path=lib)
+    _close(yl, y1, 1e-14, "LIT under any order")
+
+
 ALL_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_abs_companions,
     pin_selectivity,
+    pin_two_order_mask,
     pin_phi_lit_is_elu_plus_one,
     pin_phi_s_is_normalised_silu,
     pin_phi_d_is_identity,

@@ -55,6 +55,9 @@ MUTANTS = [
      "ll = z >= 0.0 ? -log1p(exp(z)) : z - log1p(exp(z));"),
     ("selectivity key scale is lambda", "ks = -1.0 / (1.0 + exp(z));", "ks = 1.0 / (1.0 + exp(-z));"),
     ("selectivity weights of the wrong head", "z += xi[c] * w[(size_t)h * Dm + c];", "z += xi[c] * w[c];"),
+    ("two-order mask ignores the second order", "m[j] = 0.5 * (mb[j] + mc[pos[j]]);", "m[j] = 0.5 * (mb[j] + mb[j]);"),
+    ("two-order decays not permuted", "lamc[p] = lam[order[p]];", "lamc[p] = lam[p];"),
+    ("two-order key position not mapped", "m[j] = 0.5 * (mb[j] + mc[pos[j]]);", "m[j] = 0.5 * (mb[j] + mc[j]);"),
 ]
 
 
