@@ -695,8 +695,9 @@ int lion_oracle_full2_f64(const double *q, const double *k, const double *v, con
             err |= 1;
         } else {
             for (j = 0; j < L; ++j) {
-                phi_row(mask_kind, q + (base + j) * d, d, phq + (size_t)j * d);
-                phi_row(mask_kind, k + (base + j) * d, d, phk + (size_t)j * d);
+                const size_t tok = base + (size_t)j;
+                phi_row(mask_kind, q + tok * d, d, phq + (size_t)j * d);
+                phi_row(mask_kind, k + tok * d, d, phk + (size_t)j * d);
             }
             decays(mask_kind, log_lambda, H, L, bh, lam);
             /* the decays listed along the second order, and each token's position in it */
