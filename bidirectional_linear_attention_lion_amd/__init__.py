@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     lion_attn_birnn,
     lion_attn_chunk,
     lion_attn_full,
+    lion_attn_full2,
     lion_attn_full_bwd,
     lion_attn_workspace_bytes,
     lion_selectivity,

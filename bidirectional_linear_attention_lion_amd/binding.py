@@ -43,8 +43,9 @@ def library() -> ctypes.CDLL:
     lib.lion_attn_birnn.argtypes = common + [f, i, i, i, i, i, vp, i, fp, vp, sz, vp]
     lib.lion_attn_full_bwd.argtypes = common + [i, i, i, i, i, vp, fp, vp, vp, vp, vp, i, fp, vp, sz, vp]
     lib.lion_selectivity.argtypes = [vp, vp, fp, i, i, i, i, fp, fp, vp, vp, i, vp]
+    lib.lion_attn_full2.argtypes = common + [f, vp, i, i, i, i, i, vp, i, fp, vp]
     for fn in ("lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_full_bwd", "lion_selectivity",
-               "lion_attn_abi_version"):
+               "lion_attn_full2", "lion_attn_abi_version"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.lion_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.lion_attn_workspace_bytes.restype = sz
@@ -104,6 +105,17 @@ def lion_attn_full(q, k, v, log_lambda, mask_kind, eps: float = 1e-6, *, y=None,
                                   _ptr(y), ydt, _ptr(den_out), sptr)
     if rc != 0:
         raise LionError("lion_attn_full", rc)
+    return y
+
+
+def lion_attn_full2(q, k, v, log_lambda, mask_kind, order, eps: float = 1e-6, *, y=None, y_dtype=None,
+                    den_out=None, stream=None):
+    """Full form with the masks of the tokens' own order and of ``order`` (int32 cuda tensor [L]) averaged."""
+    kind, B, H, L, d, dt, y, ydt, sptr = _prepare(q, k, v, mask_kind, y, y_dtype, den_out, stream)
+    rc = library().lion_attn_full2(_ptr(q), _ptr(k), _ptr(v), _ptr(log_lambda), kind, float(eps), _ptr(order), B, H,
+                                   L, d, dt, _ptr(y), ydt, _ptr(den_out), sptr)
+    if rc != 0:
+        raise LionError("lion_attn_full2", rc)
     return y
 
 

@@ -59,6 +59,7 @@ lion::AttnArgs make_args(const void *q, const void *k, const void *v, const floa
     a.y = y;
     a.out_bf16 = y_dtype == LION_DTYPE_BF16;
     a.den_out = den_out;
+    a.order = nullptr;
     a.C = 0;
     a.workspace = nullptr;
     a.workspace_bytes = 0;
@@ -76,6 +77,19 @@ int lion_attn_full(const void *q, const void *k, const void *v, const float *log
     int rc = check_common(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
     if (rc != LION_OK) return rc;
     lion::AttnArgs a = make_args(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    if (!lion::plan_full(a).ok) return LION_ERR_UNSUPPORTED;
+    return status_of(lion::launch_full(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lion_attn_full2(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, float eps,
+                    const int *order, int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out,
+                    void *stream) {
+    int rc = check_common(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    if (rc != LION_OK) return rc;
+    if (!order || !aligned16(order)) return LION_ERR_INVALID;
+    if (mask_kind & LION_CAUSAL) return LION_ERR_UNSUPPORTED;
+    lion::AttnArgs a = make_args(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    a.order = order;
     if (!lion::plan_full(a).ok) return LION_ERR_UNSUPPORTED;
     return status_of(lion::launch_full(a, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -18,6 +18,12 @@
 // by all the wave's tiles, so a score costs two multiplies instead of an exponential.  Keys wholly
 // before the first row r0 use exp2(E_i - E_r0) * exp2(E_r0 - E_j) likewise.  Only sub-blocks that
 // overlap the wave's rows pay one exponential per score.
+//
+// Two token orders (patch-reordered LION-D / LION-S: the pages average the masks of two patch orders,
+// reply "P2: Comparison against vision SSMs", item 1): M = (M_b + M_c) / 2 with M_c the same mask along a
+// second order of the tokens.  Its exponents are a second table F_t = prefix sum of log(lambda) along that
+// order, at token t's position in it, so (M_c)_ij = exp2(-|F_i - F_j|); every score then pays two
+// exponentials (F is not monotone along the tokens' own order, so no separable shortcut applies).
 #include <type_traits>
 
 #include "lion_device.h"
@@ -45,7 +51,35 @@ struct FullParams {
     int sk;            // keys per stage (multiple of 32)
     int nbuf;          // 1: the whole sequence is one stage; 2: double-buffered stages
     int causal;        // keys after the query masked out
+    const int *order;  // two-order variant: the tokens listed in the second order [L]
 };
+
+// Second-order exponent table F[t] = log2 of the decay product along `order` up to token t's position
+// (LION-S: an fp64 scan of log(lambda) gathered in that order; LION-D: position * log2(lambda_h));
+// entries past L - 1 are 0.  Order entries are clamped to [0, L) (the caller guarantees a permutation).
+template <int KIND>
+__device__ void build_order_exponents(float *F, double *scan_sh, const float *ll, const int *order, int bh, int H,
+                                      int L, int Lpad, int tid, int nt) {
+    for (int t = L + tid; t < Lpad; t += nt) F[t] = 0.f;
+    if constexpr (KIND == kMaskD) {
+        const float lg = ll[bh % H] * kLog2e;
+        for (int p = tid; p < L; p += nt) F[min(max(order[p], 0), L - 1)] = (float)p * lg;
+        __syncthreads();
+    } else if constexpr (KIND == kMaskS) {
+        const float *row = ll + (size_t)bh * L;
+        const int seg = (L + nt - 1) / nt;
+        const int p0 = tid * seg, p1 = min(p0 + seg, L);
+        double s = 0.0;
+        for (int p = p0; p < p1; ++p) s += (double)row[min(max(order[p], 0), L - 1)];
+        double a = block_excl_scan(s, scan_sh, tid, nt);
+        for (int p = p0; p < p1; ++p) {
+            const int t = min(max(order[p], 0), L - 1);
+            a += (double)row[t];
+            F[t] = (float)(a * 1.4426950408889634);
+        }
+        __syncthreads();
+    }
+}
 
 template <int D, bool BF16>
 struct FullCfg {
@@ -56,7 +90,7 @@ struct FullCfg {
     using QFrag = std::conditional_t<BF16, bf16x8, float>;
 };
 
-template <int D, int KIND, int QT, bool BF16>
+template <int D, int KIND, int QT, bool BF16, bool TWO>
 __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
     using C = FullCfg<D, BF16>;
     using T = typename C::T;
@@ -83,7 +117,8 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
     T *Kb = reinterpret_cast<T *>(smem);
     T *Vb = Kb + (size_t)p.nbuf * SK * D;
     float *E = reinterpret_cast<float *>(Vb + (size_t)p.nbuf * SK * D);
-    double *scan_sh = reinterpret_cast<double *>(E + (KIND == kMaskLit ? 0 : Lpad));
+    float *F = E + Lpad;                                    // second-order exponents (TWO)
+    double *scan_sh = reinterpret_cast<double *>(E + (KIND == kMaskLit ? 0 : (TWO ? 2 : 1) * Lpad));
 
     const size_t base = (size_t)bh * L;
     const T *qg = reinterpret_cast<const T *>(p.q) + base * D;
@@ -107,10 +142,11 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
 
     if constexpr (KIND != kMaskLit)
         build_exponents<KIND>(E, scan_sh, p.ll, bh, p.H, L, Lpad, min(tile0 * 16, L - 1), tid, nt);
+    if constexpr (TWO) build_order_exponents<KIND>(F, scan_sh, p.ll, p.order, bh, p.H, L, Lpad, tid, nt);
 
     // ---- query fragments: phi(q) of this wave's tiles (B operand of S^T = K Q^T) -----------------
     typename C::QFrag qf[QT][C::NS];
-    float Ei[QT];
+    float Ei[QT], Fi[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         const int i = (wtile0 + qt) * 16 + r;
@@ -166,8 +202,9 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
 #pragma unroll
             for (int s = 0; s < C::NS; ++s) qf[qt][s] = x[s] * sc;
         }
-        Ei[qt] = 0.f;
+        Ei[qt] = Fi[qt] = 0.f;
         if constexpr (KIND != kMaskLit) Ei[qt] = E[min(i, L - 1)];
+        if constexpr (TWO) Fi[qt] = F[min(i, L - 1)];
     }
 
     // rows of this wave and the row factors of the separable mask (keys before / after the rows)
@@ -272,7 +309,7 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
             if (p.causal && j0 > rwl) break;                   // causal: no later keys
             // region of this sub-block relative to the wave's rows (wave-uniform)
             int region = 0;                                    // overlap: per-score exponentials
-            if (KIND != kMaskLit || p.causal) {
+            if (!TWO && (KIND != kMaskLit || p.causal)) {
                 if (j0 + kKB - 1 < rw0) region = 1;            // every key before every row
                 else if (j0 > rwl) region = 2;                  // every key after every row
             }
@@ -300,7 +337,15 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
             }
             // per-key mask data of the 8 keys this lane touches, j0 + 16t + 4g + e: the exponent in the
             // overlap region, the column factor elsewhere
-            float mk[2][4];
+            float mk[2][4], fk[2][4];
+            if constexpr (TWO) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const f32x4 f4 = *reinterpret_cast<const f32x4 *>(F + j0 + 16 * t + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) fk[t][e] = f4[e];
+                }
+            }
             if constexpr (KIND != kMaskLit) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -355,7 +400,9 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
                     for (int t = 0; t < 2; ++t)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            pv[t][e] = sacc[t][e] * fast_exp2(-__builtin_fabsf(Ei[qt] - mk[t][e]));
+                            pv[t][e] = TWO ? sacc[t][e] * (0.5f * (fast_exp2(-__builtin_fabsf(Ei[qt] - mk[t][e])) +
+                                                                   fast_exp2(-__builtin_fabsf(Fi[qt] - fk[t][e]))))
+                                           : sacc[t][e] * fast_exp2(-__builtin_fabsf(Ei[qt] - mk[t][e]));
                 } else {
                     const float rowf = region == 1 ? rowf_b[qt] : rowf_a[qt];
 #pragma unroll
@@ -443,6 +490,7 @@ struct FullShape {
 };
 
 FullShape full_shape(const AttnArgs &a) {
+    const bool two = a.order != nullptr && a.kind != kMaskLit;
     const int ntiles = (a.L + 15) / 16;
     const long bhs = (long)a.B * a.H;
     int qt = 1;
@@ -471,13 +519,13 @@ FullShape full_shape(const AttnArgs &a) {
     }
     const int Lpad = ((a.L + sh.sk - 1) / sh.sk) * sh.sk;
     size_t lds = (size_t)sh.nbuf * sh.sk * per_key;
-    if (a.kind != kMaskLit) lds += (size_t)Lpad * 4;
+    if (a.kind != kMaskLit) lds += (size_t)Lpad * 4 * (two ? 2 : 1);
     if (a.kind == kMaskS) lds += (size_t)sh.nw * 64 * 8;
     sh.lds = lds;
     return sh;
 }
 
-template <int D, int KIND, int QT, bool BF16>
+template <int D, int KIND, int QT, bool BF16, bool TWO>
 hipError_t launch_full_t(const AttnArgs &a, hipStream_t stream, const FullShape &sh) {
     FullParams p;
     p.q = a.q;
@@ -496,23 +544,33 @@ hipError_t launch_full_t(const AttnArgs &a, hipStream_t stream, const FullShape 
     p.sk = sh.sk;
     p.nbuf = sh.nbuf;
     p.causal = a.causal ? 1 : 0;
+    p.order = a.order;
     if (sh.lds > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&full_kernel<D, KIND, QT, BF16>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&full_kernel<D, KIND, QT, BF16, TWO>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh.lds);
-    hipLaunchKernelGGL((full_kernel<D, KIND, QT, BF16>), dim3(p.nblocks), dim3(sh.nw * 64), sh.lds, stream, p);
+    hipLaunchKernelGGL((full_kernel<D, KIND, QT, BF16, TWO>), dim3(p.nblocks), dim3(sh.nw * 64), sh.lds, stream, p);
     return hipGetLastError();
 }
 
-template <int D, int KIND, bool BF16>
-hipError_t dispatch_qt(const AttnArgs &a, hipStream_t stream) {
+template <int D, int KIND, bool BF16, bool TWO>
+hipError_t dispatch_qt2(const AttnArgs &a, hipStream_t stream) {
     const FullShape sh = full_shape(a);
     if constexpr (BF16) {
         if constexpr (D != 128) {
-            if (sh.qt == 4) return launch_full_t<D, KIND, 4, BF16>(a, stream, sh);
-            if (sh.qt == 2) return launch_full_t<D, KIND, 2, BF16>(a, stream, sh);
+            if (sh.qt == 4) return launch_full_t<D, KIND, 4, BF16, TWO>(a, stream, sh);
+            if (sh.qt == 2) return launch_full_t<D, KIND, 2, BF16, TWO>(a, stream, sh);
         }
     }
-    return launch_full_t<D, KIND, 1, BF16>(a, stream, sh);
+    return launch_full_t<D, KIND, 1, BF16, TWO>(a, stream, sh);
+}
+
+// the two-order variant exists for the kinds with a decay (LIT's mask is all ones in any order)
+template <int D, int KIND, bool BF16>
+hipError_t dispatch_qt(const AttnArgs &a, hipStream_t stream) {
+    if constexpr (KIND != kMaskLit) {
+        if (a.order) return dispatch_qt2<D, KIND, BF16, true>(a, stream);
+    }
+    return dispatch_qt2<D, KIND, BF16, false>(a, stream);
 }
 
 template <int D, bool BF16>

@@ -12,6 +12,7 @@ struct AttnArgs {
     const float *log_lambda;    // NULL (LIT), [H] (D), [B, H, L] (S)
     int kind;                   // 0 LIT, 1 D, 2 S
     bool causal;                // keys after the query masked out (the forward recurrence alone)
+    const int *order;           // full form only, nullable: a second token order [L] (averaged masks)
     float eps;
     int B, H, L, d;
     bool in_bf16;               // element type of q, k, v

@@ -106,6 +106,20 @@ enum lion_status {
 LION_API int lion_attn_full(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, float eps,
                    int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out, void *stream);
 
+/* Full form with the average of two masks, M = (M_b + M_c) / 2: M_b along the tokens' own order and
+ * M_c the same product-of-decays mask along a second order of the same tokens, each token keeping its
+ * own decay -- the patch-reordered vision models (LION-D and LION-S with "natural" patch orders) average
+ * the masks of two patch orders (reply "P2: Comparison against vision SSMs", item 1, Figure 7 b and c).
+ *   order   device int32 [L]: order[p] = the token at position p of the second order; must be a
+ *           permutation of 0 .. L-1 (not checked on the device: other contents give unspecified
+ *           results, never an out-of-bounds access).  For an image the column-major raster of the patch
+ *           grid (the class token first).
+ *   mask_kind  LIT, D or S; LION_CAUSAL is LION_ERR_UNSUPPORTED.  LIT's mask is all ones in any order.
+ * Other arguments as lion_attn_full; no workspace. */
+LION_API int lion_attn_full2(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind,
+                             float eps, const int *order, int B, int H, int L, int d, int dtype, void *y,
+                             int y_dtype, float *den_out, void *stream);
+
 /* Chunkwise form: masked attention inside chunks of C consecutive tokens plus forward and
  * backward d x (d+1) states carried from chunk to chunk.  C in {16, 32, 64, 128, 256} (at most 128
  * when d = 128; larger is LION_ERR_UNSUPPORTED); the last chunk may be partial.  Source: reply "4: Practicality of Recurrent Inference"; blog "LION Part

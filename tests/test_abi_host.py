@@ -31,9 +31,9 @@ def header_symbols():
 def test_library_exports_every_declared_symbol():
     lib = lion.library()
     names = header_symbols()
-    assert set(names) == {"lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_full_bwd",
-                          "lion_selectivity", "lion_attn_workspace_bytes", "lion_status_str",
-                          "lion_attn_abi_version"}
+    assert set(names) == {"lion_attn_full", "lion_attn_full2", "lion_attn_chunk", "lion_attn_birnn",
+                          "lion_attn_full_bwd", "lion_selectivity", "lion_attn_workspace_bytes",
+                          "lion_status_str", "lion_attn_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     assert lion.lion_attn_abi_version() == 1
@@ -162,6 +162,21 @@ def test_bwd_unsupported_and_workspace():
     assert lion.lion_attn_workspace_bytes(lion.FORM_FULL_BWD, 2, 3, 17, 64, 0, 0) == SIZE_MAX
     assert bwd(ws=None, wsb=need) == WORKSPACE
     assert bwd(ws=P, wsb=need - 1) == WORKSPACE
+
+
+def full2(order=P, **kw):
+    a = dict(q=P, k=P, v=P, ll=P, kind=1, eps=1e-6, B=2, H=3, L=17, d=64, dt=1, y=P, ydt=1, den=None)
+    a.update(kw)
+    return lion.library().lion_attn_full2(a["q"], a["k"], a["v"], a["ll"], a["kind"], a["eps"], order, a["B"],
+                                          a["H"], a["L"], a["d"], a["dt"], a["y"], a["ydt"], a["den"], None)
+
+
+def test_full2_arguments():
+    assert full2(order=None) == INVALID
+    assert full2(order=MIS) == INVALID
+    assert full2(q=None) == INVALID
+    assert full2(kind=1 | 4) == UNSUPPORTED
+    assert full2(d=48) == UNSUPPORTED
 
 
 def sel(x=P, w=P, bias=P, B=2, L=17, H=3, Dm=64, ll=P, ks=None, k=None, ko=None, d=64):
