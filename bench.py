@@ -34,7 +34,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
 VALU_FP32_PEAK_TFLOPS = 157.3   # fp32 vector
 CSRC = os.path.join(ROOT, "bidirectional_linear_attention_lion_amd", "csrc")
 KERNEL_FILES = {"full": "lion_full.hip", "chunk": "lion_chunk.hip", "birnn": "lion_birnn.hip",
-                "full_bwd": "lion_full_bwd.hip", "selectivity": "lion_selectivity.hip"}
+                "full_bwd": "lion_full_bwd.hip", "selectivity": "lion_selectivity.hip", "full2": "lion_full.hip"}
 SEL_WIDTH = 1024   # layer-input width of the selectivity prologue (the BERT-Large-shaped recipe)
 
 
@@ -47,7 +47,9 @@ def parse_args():
     ap.add_argument("--forms", default=None,
                     help="comma-separated forms (default: the workload's); full_bwd times the full form's backward "
                          "pass (bf16 gradients; y, den and a random dy prepared beforehand); selectivity times "
-                         "the LION-S prologue (log lambda from a [B, L, 1024] layer input, keys scaled)")
+                         "the LION-S prologue (log lambda from a [B, L, 1024] layer input, keys scaled); full2 the full "
+                         "form with the masks of the raster and the column-major patch order averaged (image "
+                         "workloads: L = 1 + n^2)")
     ap.add_argument("--chunk", type=int, default=None, help="chunk size C (default: the workload's first)")
     ap.add_argument("--causal", action="store_true",
                     help="the causal variant (keys after the query masked out) of the workload's mask")
@@ -141,6 +143,8 @@ def algorithmic(form: str, wl, C: int, causal: bool = False):
         pairs = L * (L + 1) / 2 if causal else L * L
         # S, dY V^T, dV, dphi(Q), dphi(K): five L x L x d products; mask, dp, dS and dA per pair
         return nbytes, bh * (10 * pairs * d + 8 * pairs)
+    if form == "full2":
+        return nbytes, bh * (4 * L * L * d + 4 * L * L)   # as the full form, two mask terms per score
     if form == "full":
         pairs = L * (L + 1) / 2 if causal else L * L
         flops = bh * (4 * pairs * d + 2 * pairs)          # phi(Q)phi(K)^T, P V, mask and row sums
@@ -263,6 +267,12 @@ def main():
             dll = None if wl.kind == 0 else torch.empty(
                 (wl.H,) if wl.kind == 1 else (wl.B, wl.H, wl.L), dtype=torch.float32, device=dev)
             bwd_sets.append((yb, den, dy, grads, dll))
+    order = None
+    if "full2" in forms:
+        side = int(round((wl.L - 1) ** 0.5))
+        if side * side + 1 != wl.L:
+            raise SystemExit("bench.py: full2 needs an image workload (L = 1 + n^2)")
+        order = torch.from_numpy(lin.column_major_order(side, side)).to(dev)
     sel = None
     if "selectivity" in forms:
         if wl.dtype != "bf16":
@@ -282,6 +292,8 @@ def main():
         q, k, v, y = sets[s % nsets]
         if form == "full":
             lion.lion_attn_full(q, k, v, ll, kind, wl.eps, y=y, stream=stream)
+        elif form == "full2":
+            lion.lion_attn_full2(q, k, v, ll, kind, order, wl.eps, y=y, stream=stream)
         elif form == "selectivity":
             lion.lion_selectivity(sel[0][s % nsets], sel[1], sel[2], k=k, k_out=y, stream=stream)
         elif form == "full_bwd":
