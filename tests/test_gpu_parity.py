@@ -147,6 +147,30 @@ def test_chunk_resident_decay_to_zero():
     assert np.max(np.abs(y - vv)) <= 2e-2 * np.sqrt(np.mean(vv ** 2))
 
 
+# the full form's resident kernel (bf16, d >= 32, keys and values of a (batch, head) in LDS, grids of at
+# most 256 workgroups): lengths at the 64-key round edges and at its length limit for each head width
+# (past it the streaming kernel takes over), more than 15 query tiles (two workgroups per (batch,
+# head)), causal, and grids just inside and just past the 256-workgroup limit
+RESIDENT_FULL = [(64, [63, 64, 65, 128, 192, 193, 224, 240, 241, 255, 256, 257]), (32, [447, 448, 449]),
+                 (128, [96, 127, 128, 129])]
+
+
+@pytest.mark.parametrize("kind", [lin.LIT, lin.D, lin.S])
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_resident_lengths(kind, causal):
+    for d, lengths in RESIDENT_FULL:
+        for L in lengths:
+            inp = lin.random_inputs(1, 3, L, d, kind, dtype="bf16", seed=700 + d + L)
+            _check("full", inp, 1e-6, tag=f"(resident d={d} L={L})", causal=causal)
+
+
+def test_full_resident_grid_limit():
+    for B, H in ((16, 16), (257, 1)):
+        for kind in (lin.LIT, lin.S):
+            inp = lin.random_inputs(B, H, 100, 64, kind, dtype="bf16", seed=800 + B)
+            _check("full", inp, 1e-6, tag=f"(grid B{B} H{H})")
+
+
 @pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
