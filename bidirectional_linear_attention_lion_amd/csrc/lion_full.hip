@@ -443,14 +443,75 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
     } else {
         stage_rows<D, T>(Kb, kg, 0, SK, L, wave, nw, lane);
     }
-    T xr[QT][C::CPL];
-    load_query<D, QT, BF16>(xr, qg, wtile0, wave_tiles, L, r, g);
 
     if constexpr (KIND != kMaskLit)
         build_exponents<KIND>(E, scan_sh, p.ll, bh, p.H, L, Lpad, min(tile0 * 16, L - 1), tid, nt);
     if constexpr (TWO) build_order_exponents<KIND>(F, scan_sh, p.ll, p.order, bh, p.H, L, Lpad, tid, nt);
 
-    // rows of this wave; phi(q) fragments, row exponents and factors
+    // ---- query fragments: phi(q) of this wave's tiles (B operand of S^T = K Q^T) -----------------
+    typename C::QFrag qf[QT][C::NS];
+    float Ei[QT], Fi[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const int i = (wtile0 + qt) * 16 + r;
+        const bool ok = i < L && qt < wave_tiles;
+        float x[C::CPL];
+        const T *row = qg + (size_t)(ok ? i : 0) * D;
+        if constexpr (BF16 && C::CPL >= 8) {
+            // fragment st of lane group g: the eight channels of 16-byte chunk 4 st + g
+#pragma unroll
+            for (int st = 0; st < C::NS; ++st) {
+                T tmp[8];
+                const u32x4 raw = ld16(row + 8 * (4 * st + g));
+                __builtin_memcpy(tmp, &raw, 16);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[8 * st + e] = (float)tmp[e];
+            }
+        } else if constexpr (C::CPL * sizeof(T) % 16 == 0) {
+            const T *src = row + g * C::CPL;
+#pragma unroll
+            for (int c = 0; c < C::CPL; c += RT::VEC) {
+                T tmp[RT::VEC];
+                const u32x4 raw = ld16(src + c);
+                __builtin_memcpy(tmp, &raw, 16);
+#pragma unroll
+                for (int e = 0; e < RT::VEC; ++e) x[c + e] = (float)tmp[e];
+            }
+        } else {
+            const T *src = row + g * C::CPL;
+#pragma unroll
+            for (int c = 0; c < C::CPL; ++c) x[c] = (float)src[c];
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < C::CPL; ++c) {
+            x[c] = phi_pre<KIND>(x[c]);
+            ss += x[c] * x[c];
+        }
+        float sc = ok ? 1.f : 0.f;
+        if constexpr (KIND == kMaskS) {
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            sc *= inv_norm(ss);
+        }
+        if constexpr (BF16) {
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s) {
+                bf16x8 f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = (8 * s + e < C::CPL) ? f2bf(x[8 * s + e] * sc) : f2bf(0.f);
+                qf[qt][s] = f;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s) qf[qt][s] = x[s] * sc;
+        }
+        Ei[qt] = Fi[qt] = 0.f;
+        if constexpr (KIND != kMaskLit) Ei[qt] = E[min(i, L - 1)];
+        if constexpr (TWO) Fi[qt] = F[min(i, L - 1)];
+    }
+
+    // rows of this wave and the row factors of the separable mask (keys before / after the rows)
     const int rw0 = wtile0 * 16;
     const int rwl = min((wtile0 + wave_tiles) * 16, L) - 1;
     float e_first = 0.f, e_last = 0.f;
@@ -460,9 +521,24 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
             e_last = uniform(E[rwl]);
         }
     }
-    FullWave<D, QT, BF16> w;
-    query_frags<D, KIND, QT, BF16>(w, xr, wtile0, wave_tiles, L, r);
-    wave_rows_init<D, KIND, QT, BF16, TWO>(w, E, F, wtile0, L, r, e_first, e_last);
+    float rowf_b[QT], rowf_a[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        rowf_b[qt] = rowf_a[qt] = 1.f;
+        if constexpr (KIND != kMaskLit) {
+            rowf_b[qt] = fast_exp2(Ei[qt] - e_first);
+            rowf_a[qt] = fast_exp2(e_last - Ei[qt]);
+        }
+    }
+
+    f32x4 acc_o[QT][D / 16];
+    float den[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        den[qt] = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < D / 16; ++ct) acc_o[qt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     if (kreg) {
         // phi on the keys held in registers (rows at or past L written as zeros); the single stage is
@@ -535,12 +611,179 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
             const int j0 = s * SK + h * kKB;
             if (j0 >= L) break;
             if (p.causal && j0 > rwl) break;                   // causal: no later keys
-            const int region = subblock_region<KIND, TWO>(j0, rw0, rwl, p.causal);
-            full_subblock<D, KIND, QT, BF16, TWO>(w, kbuf, vbuf, h * kKB, j0, E, F, region, e_first, e_last, wtile0,
-                                                  wave_tiles, p.causal, r, g);
+            // region of this sub-block relative to the wave's rows (wave-uniform)
+            int region = 0;                                    // overlap: per-score exponentials
+            if (!TWO && (KIND != kMaskLit || p.causal)) {
+                if (j0 + kKB - 1 < rw0) region = 1;            // every key before every row
+                else if (j0 > rwl) region = 2;                  // every key after every row
+            }
+            // K fragments (A operand of S^T): key row 16t + r of the sub-block, channels of group g
+            auto kelem = [&](int t, int col) { return kbuf + RT::off(h * kKB + 16 * t + r, col); };
+            bf16x8 kf[2][BF16 ? C::NS : 1];
+            if constexpr (BF16) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int st = 0; st < C::NS; ++st) {
+                        if constexpr (C::CPL >= 8) {
+                            kf[t][st] = *reinterpret_cast<const bf16x8 *>(kelem(t, 8 * (4 * st + g)));
+                        } else {
+                            const bf16x4 h4 = *reinterpret_cast<const bf16x4 *>(kelem(t, g * C::CPL));
+                            bf16x8 f;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                f[e] = h4[e];
+                                f[4 + e] = f2bf(0.f);
+                            }
+                            kf[t][st] = f;
+                        }
+                    }
+            }
+            // per-key mask data of the 8 keys this lane touches, j0 + 16t + 4g + e: the exponent in the
+            // overlap region, the column factor elsewhere
+            float mk[2][4], fk[2][4];
+            if constexpr (TWO) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const f32x4 f4 = *reinterpret_cast<const f32x4 *>(F + j0 + 16 * t + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) fk[t][e] = f4[e];
+                }
+            }
+            if constexpr (KIND != kMaskLit) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const f32x4 e4 = *reinterpret_cast<const f32x4 *>(E + j0 + 16 * t + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        mk[t][e] = region == 0 ? e4[e] : fast_exp2(region == 1 ? e_first - e4[e] : e4[e] - e_last);
+                }
+            }
+            // V^T fragments (A operand of O^T += V^T P^T): keys j0 + 4g + e and j0 + 16 + 4g + e of
+            // value channel 16 ct + r, read transposed from the row-major value tile
+            bf16x8 vfr[BF16 ? D / 16 : 1];
+            if constexpr (BF16) {
+#pragma unroll
+                for (int ct = 0; ct < D / 16; ++ct) {
+                    const int row = h * kKB + 4 * g + (r >> 2), col = 16 * ct + 4 * (r & 3);
+                    const bf16x4 lo = read_tr_b16(vbuf + RT::off(row, col));
+                    const bf16x4 hi = read_tr_b16(vbuf + RT::off(row + 16, col));
+                    bf16x8 f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        f[e] = lo[e];
+                        f[4 + e] = hi[e];
+                    }
+                    vfr[ct] = f;
+                }
+            }
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+                if (qt >= wave_tiles) break;
+                f32x4 sacc[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < C::NS; ++st) {
+                        if constexpr (BF16)
+                            sacc[t] = mfma_bf16(kf[t][st], qf[qt][st], sacc[t]);
+                        else
+                            sacc[t] = mfma_f32(*kelem(t, g * C::CPL + st), qf[qt][st], sacc[t]);
+                    }
+                }
+                // sacc[t][e] = S[query r][key j0 + 16t + 4g + e]; mask it (region is wave-uniform)
+                float pv[2][4];
+                if constexpr (KIND == kMaskLit) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) pv[t][e] = sacc[t][e];
+                } else if (region == 0) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            pv[t][e] = TWO ? sacc[t][e] * (0.5f * (fast_exp2(-__builtin_fabsf(Ei[qt] - mk[t][e])) +
+                                                                   fast_exp2(-__builtin_fabsf(Fi[qt] - fk[t][e]))))
+                                           : sacc[t][e] * fast_exp2(-__builtin_fabsf(Ei[qt] - mk[t][e]));
+                } else {
+                    const float rowf = region == 1 ? rowf_b[qt] : rowf_a[qt];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) pv[t][e] = (sacc[t][e] * rowf) * mk[t][e];
+                }
+                if (p.causal && region == 0) {
+                    // keys after this lane's query row are masked out
+                    const int i = (wtile0 + qt) * 16 + r;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (j0 + 16 * t + 4 * g + e > i) pv[t][e] = 0.f;
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) den[qt] += pv[t][e];
+                if constexpr (BF16) {
+                    bf16x8 pf;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        pf[e] = f2bf(pv[0][e]);
+                        pf[4 + e] = f2bf(pv[1][e]);
+                    }
+#pragma unroll
+                    for (int ct = 0; ct < D / 16; ++ct) acc_o[qt][ct] = mfma_bf16(vfr[ct], pf, acc_o[qt][ct]);
+                } else {
+#pragma unroll
+                    for (int ct = 0; ct < D / 16; ++ct)
+#pragma unroll
+                        for (int t = 0; t < 2; ++t)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                acc_o[qt][ct] = mfma_f32(vbuf[RT::off(h * kKB + 16 * t + 4 * g + e, 16 * ct + r)],
+                                                         pv[t][e], acc_o[qt][ct]);
+                }
+            }
         }
     }
-    full_epilogue<D, QT, BF16>(w, p, base, wtile0, wave_tiles, L, r, g);
+
+    // ---- epilogue: full row sums, divide, store -------------------------------------------------
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        if (qt >= wave_tiles) break;
+        float dsum = den[qt];
+        dsum += __shfl_xor(dsum, 16, 64);
+        dsum += __shfl_xor(dsum, 32, 64);
+        const float div = dsum + p.eps;
+        const int i = (wtile0 + qt) * 16 + r;
+        if (i < L) {
+            const float inv = 1.f / div;
+            const size_t row = base + i;
+            if (p.out_bf16) {
+                __bf16 *yo = reinterpret_cast<__bf16 *>(p.y) + row * D;
+#pragma unroll
+                for (int ct = 0; ct < D / 16; ++ct) {
+                    bf16x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = f2bf(acc_o[qt][ct][e] * inv);
+                    *reinterpret_cast<bf16x4 *>(yo + 16 * ct + 4 * g) = o;
+                }
+            } else {
+                float *yo = reinterpret_cast<float *>(p.y) + row * D;
+#pragma unroll
+                for (int ct = 0; ct < D / 16; ++ct) {
+                    f32x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = acc_o[qt][ct][e] * inv;
+                    *reinterpret_cast<f32x4 *>(yo + 16 * ct + 4 * g) = o;
+                }
+            }
+            if (p.den_out && g == 0) p.den_out[row] = div;
+        }
+    }
 }
 
 // Workgroup barrier that waits for this wave's LDS operations only.  (__syncthreads() also carries a
