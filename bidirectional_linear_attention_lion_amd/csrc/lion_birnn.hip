@@ -456,6 +456,10 @@ __global__ void __launch_bounds__(2 * NR * 64) __attribute__((amdgpu_waves_per_e
                 reinterpret_cast<float *>(p.y)[o] = out;
             if (p.den_out && cg == 0 && c2 == 0) p.den_out[base + t] = div;
         }
+        // staging overwrites the rows, diagonal and scales the reduction reads (its own direction's and,
+        // for tokens both directions visit in this block, the other direction's scales): every wave must
+        // be done reducing first
+        __syncthreads();
         if (b + 1 < nblk) stage(b + 1);
         __syncthreads();
     }
