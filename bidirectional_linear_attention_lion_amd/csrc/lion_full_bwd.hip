@@ -13,11 +13,11 @@
 //   w_ij = dp_ij p_ij,   dlog(lambda_u) = sum_{t >= u} dA_t   (u >= 1; lambda_0 never enters).
 //
 // Three launches, none of which forms an L x L matrix:
-//   dq:   a wave per 16-query tile streams the keys and values (LDS stages, as in the forward kernel):
+//   dq:   a wave per one or two 16-query tiles streams the keys and values (LDS stages, as in the forward kernel):
 //         S^T = phi(K) phi(Q)^T and (dy v^T)^T = V dY^T on matrix cores, the masked dS^T in registers,
 //         then dphi(Q)^T += phi(K)^T dS^T (the D layout of the first products is the B layout of this
 //         one, as in the forward).  It also writes delta and the row half of dA.
-//   dk/dv: a wave per 16-key tile streams phi(Q) and dY the same way: S and dY V^T with keys as the
+//   dk/dv: a wave per one or two 16-key tiles streams phi(Q) and dY the same way: S and dY V^T with keys as the
 //         column index, then dV^T += dY^T (P / den) and dphi(K)^T += phi(Q)^T dS, and the column half
 //         of dA.
 //   dlog(lambda): LION-S a reverse prefix sum of dA per (batch, head); LION-D sum_t t dA_t over every
@@ -190,7 +190,8 @@ __device__ __forceinline__ void store4(void *base, bool bf16, size_t off, f32x4 
 }
 
 // ================================ dq ==================================================================
-template <int D, int KIND>
+// TT query tiles per wave: the key/value fragments a sub-block reads from LDS serve all of them.
+template <int D, int KIND, int TT>
 __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdParams p) {
     using T = __bf16;
     constexpr int NS = D / 32, NCT = D / 16;
@@ -208,8 +209,8 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdParams p) {
     const int bh = tile / p.nsb;
     // causal: workgroups of later rows (more keys) first
     const int sb = p.causal ? p.nsb - 1 - tile % p.nsb : tile % p.nsb;
-    const int wt = sb * nw + wave;                 // this wave's query tile
-    const bool active = wt < ntiles;
+    const int wt0 = (sb * nw + wave) * TT;         // this wave's first query tile
+    const bool active = wt0 < ntiles;
 
     T *Kb = reinterpret_cast<T *>(smem);
     T *Vb = Kb + (size_t)p.nbuf * SK * D;
@@ -222,38 +223,44 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdParams p) {
     stage_rows<D, T>(Kb, kg, 0, SK, L, wave, nw, lane);
     stage_rows<D, T>(Vb, vg, 0, SK, L, wave, nw, lane);
     if constexpr (KIND != kMaskLit)
-        build_exponents<KIND>(E, scan_sh, p.ll, bh, p.H, L, Lpad, min(sb * nw * 16, L - 1), tid, nt);
+        build_exponents<KIND>(E, scan_sh, p.ll, bh, p.H, L, Lpad, min(sb * nw * TT * 16, L - 1), tid, nt);
 
-    // this lane's query row i: phi(q), dy fragments; den, delta
-    const int i = wt * 16 + r;
-    const bool ok = active && i < L;
-    const int ic = min(i, L - 1);
-    bf16x8 qf[NS], dyf[NS];
-    row_frags<D, KIND, true>(p.q + (base + ic) * D, ok, qf);
-    row_frags<D, KIND, false>(p.dy + (base + ic) * D, ok, dyf);
-    float dot = 0.f;
+    // this lane's query row i of each tile: phi(q), dy fragments; den, delta
+    int irow[TT];
+    bool ok[TT];
+    bf16x8 qf[TT][NS], dyf[TT][NS];
+    float inv_den[TT], delta_i[TT], Ei[TT], rowterm[TT];
+    f32x4 acc[TT][NCT];
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
-        const bf16x8 yv = __builtin_bit_cast(bf16x8, ld16(p.y + (base + ic) * D + 8 * (4 * st + g)));
+    for (int tt = 0; tt < TT; ++tt) {
+        const int i = (wt0 + tt) * 16 + r;
+        irow[tt] = i;
+        ok[tt] = active && i < L;
+        const int ic = min(i, L - 1);
+        row_frags<D, KIND, true>(p.q + (base + ic) * D, ok[tt], qf[tt]);
+        row_frags<D, KIND, false>(p.dy + (base + ic) * D, ok[tt], dyf[tt]);
+        float dot = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dot += (float)dyf[st][e] * (float)yv[e];
+        for (int st = 0; st < NS; ++st) {
+            const bf16x8 yv = __builtin_bit_cast(bf16x8, ld16(p.y + (base + ic) * D + 8 * (4 * st + g)));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot += (float)dyf[tt][st][e] * (float)yv[e];
+        }
+        dot += __shfl_xor(dot, 16, 64);
+        dot += __shfl_xor(dot, 32, 64);
+        const float den_i = ok[tt] ? p.den[base + ic] : 1.f;
+        inv_den[tt] = 1.f / den_i;
+        delta_i[tt] = ok[tt] ? dot * inv_den[tt] : 0.f;
+        if (ok[tt] && g == 0) p.delta[base + i] = delta_i[tt];
+        Ei[tt] = KIND != kMaskLit ? E[ic] : 0.f;
+        rowterm[tt] = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    dot += __shfl_xor(dot, 16, 64);
-    dot += __shfl_xor(dot, 32, 64);
-    const float den_i = ok ? p.den[base + ic] : 1.f;
-    const float inv_den = 1.f / den_i;
-    const float delta_i = ok ? dot * inv_den : 0.f;
-    if (ok && g == 0) p.delta[base + i] = delta_i;
-    const float Ei = KIND != kMaskLit ? E[ic] : 0.f;
-    const int wlast = min((wt + 1) * 16, L) - 1;
-
-    f32x4 acc[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rowterm = 0.f;
+    const int wlast = min((wt0 + TT) * 16, L) - 1;   // the wave's last query row
 
     // causal: stages wholly after the workgroup's last query row are never needed
-    const int nst_used = p.causal ? min(nst, (min((sb + 1) * nw * 16, L) - 1) / SK + 1) : nst;
+    const int nst_used = p.causal ? min(nst, (min((sb + 1) * nw * TT * 16, L) - 1) / SK + 1) : nst;
     for (int s = 0; s < nst_used; ++s) {
         const int buf = p.nbuf == 1 ? 0 : (s & 1);
         T *kbuf = Kb + (size_t)buf * SK * D;
@@ -273,60 +280,94 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdParams p) {
             const int j0 = s * SK + h * kKB;
             if (j0 >= L) break;
             if (p.causal && j0 > wlast) break;
-            f32x4 sacc[2], dpacc[2];
+            // fragments shared by the wave's tiles: key and value rows (A operands of S^T and of
+            // (dY V^T)^T), transposed keys (A operand of dphi(Q)^T), the keys' mask exponents.  With
+            // two tiles they are read once up front; with one, where they are used (fewer registers)
+            bf16x8 kr[2][NS], vr[2][NS], kt[NCT];
+            if constexpr (TT > 1) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int st = 0; st < NS; ++st) {
+                        kr[t][st] = rows_frag<D>(kbuf, h, t, st, r, g);
+                        vr[t][st] = rows_frag<D>(vbuf, h, t, st, r, g);
+                    }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) kt[ct] = tr_frag<D>(kbuf, h, ct, r, g);
+            }
+            auto krow = [&](int t, int st) { return TT > 1 ? kr[t][st] : rows_frag<D>(kbuf, h, t, st, r, g); };
+            auto vrow = [&](int t, int st) { return TT > 1 ? vr[t][st] : rows_frag<D>(vbuf, h, t, st, r, g); };
+            auto ktr = [&](int ct) { return TT > 1 ? kt[ct] : tr_frag<D>(kbuf, h, ct, r, g); };
+            f32x4 ej[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int st = 0; st < NS; ++st) {
-                    sacc[t] = mfma_bf16(rows_frag<D>(kbuf, h, t, st, r, g), qf[st], sacc[t]);
-                    dpacc[t] = mfma_bf16(rows_frag<D>(vbuf, h, t, st, r, g), dyf[st], dpacc[t]);
-                }
-            }
-            // element (t, e): key j = j0 + 16 t + 4 g + e, query i
-            bf16x8 dsf;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                f32x4 ej = f32x4{0.f, 0.f, 0.f, 0.f};
-                if constexpr (KIND != kMaskLit) ej = *reinterpret_cast<const f32x4 *>(E + j0 + 16 * t + 4 * g);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = j0 + 16 * t + 4 * g + e;
-                    float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(Ei - ej[e])) : 1.f;
-                    if (p.causal && j > i) m = 0.f;
-                    const float dp = dpacc[t][e] * inv_den - delta_i;
-                    const float w = dp * (sacc[t][e] * m);
-                    rowterm += j < i ? w : (j > i ? -w : 0.f);
-                    dsf[4 * t + e] = f2bf(dp * m);
-                }
+                ej[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (KIND != kMaskLit) ej[t] = *reinterpret_cast<const f32x4 *>(E + j0 + 16 * t + 4 * g);
             }
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma_bf16(tr_frag<D>(kbuf, h, ct, r, g), dsf, acc[ct]);
+            for (int tt = 0; tt < TT; ++tt) {
+                if (wt0 + tt >= ntiles) break;
+                f32x4 sacc[2], dpacc[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < NS; ++st) {
+                        sacc[t] = mfma_bf16(krow(t, st), qf[tt][st], sacc[t]);
+                        dpacc[t] = mfma_bf16(vrow(t, st), dyf[tt][st], dpacc[t]);
+                    }
+                }
+                // element (t, e): key j = j0 + 16 t + 4 g + e, query irow[tt]
+                const int i = irow[tt];
+                bf16x8 dsf;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = j0 + 16 * t + 4 * g + e;
+                        float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(Ei[tt] - ej[t][e])) : 1.f;
+                        if (p.causal && j > i) m = 0.f;
+                        const float dp = dpacc[t][e] * inv_den[tt] - delta_i[tt];
+                        const float w = dp * (sacc[t][e] * m);
+                        rowterm[tt] += j < i ? w : (j > i ? -w : 0.f);
+                        dsf[4 * t + e] = f2bf(dp * m);
+                    }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) acc[tt][ct] = mfma_bf16(ktr(ct), dsf, acc[tt][ct]);
+            }
         }
     }
     if (!active) return;
 
-    // rows of dA (pairs where this row is the later / earlier index), then dq through phi
-    rowterm += __shfl_xor(rowterm, 16, 64);
-    rowterm += __shfl_xor(rowterm, 32, 64);
-    if (KIND != kMaskLit && ok && g == 0) p.da_row[base + i] = rowterm;
-    // acc[ct][e] = dphi(q_i) at channel 16 ct + 4 g + e
-    float x[NCT][4];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(p.q + (base + ic) * D + 16 * ct + 4 * g);
+    for (int tt = 0; tt < TT; ++tt) {
+        // rows of dA (pairs where this row is the later / earlier index), then dq through phi
+        float rt = rowterm[tt];
+        rt += __shfl_xor(rt, 16, 64);
+        rt += __shfl_xor(rt, 32, 64);
+        const int i = irow[tt];
+        const int ic = min(i, L - 1);
+        if (KIND != kMaskLit && ok[tt] && g == 0) p.da_row[base + i] = rt;
+        // acc[tt][ct][e] = dphi(q_i) at channel 16 ct + 4 g + e
+        float x[NCT][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[ct][e] = (float)q4[e];
-    }
-    phi_backward<D, KIND>(x, acc);
-    if (ok) {
+        for (int ct = 0; ct < NCT; ++ct) {
+            const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(p.q + (base + ic) * D + 16 * ct + 4 * g);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) store4(p.dq, p.g_bf16, (base + i) * D + 16 * ct + 4 * g, acc[ct]);
+            for (int e = 0; e < 4; ++e) x[ct][e] = (float)q4[e];
+        }
+        phi_backward<D, KIND>(x, acc[tt]);
+        if (ok[tt]) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                store4(p.dq, p.g_bf16, (base + i) * D + 16 * ct + 4 * g, acc[tt][ct]);
+        }
     }
 }
 
 // ================================ dk, dv ==============================================================
-template <int D, int KIND>
+// TT key tiles per wave: the query and dY fragments a sub-block reads from LDS serve all of them.
+template <int D, int KIND, int TT>
 __global__ void __launch_bounds__(512) bwd_dkv_kernel(BwdParams p) {
     using T = __bf16;
     constexpr int NS = D / 32, NCT = D / 16;
@@ -344,8 +385,8 @@ __global__ void __launch_bounds__(512) bwd_dkv_kernel(BwdParams p) {
     const int bh = tile / p.nsb;
     // causal: workgroups of earlier keys (more queries) first
     const int sb = tile % p.nsb;
-    const int wt = sb * nw + wave;                 // this wave's key tile
-    const bool active = wt < ntiles;
+    const int wt0 = (sb * nw + wave) * TT;         // this wave's first key tile
+    const bool active = wt0 < ntiles;
 
     // LDS: [phi(Q) stages][dY stages][E][den][delta][scan scratch]
     T *Qb = reinterpret_cast<T *>(smem);
@@ -359,7 +400,7 @@ __global__ void __launch_bounds__(512) bwd_dkv_kernel(BwdParams p) {
     const T *qg = p.q + base * D;
     const T *gg = p.dy + base * D;
     // causal: stages wholly before the workgroup's first key row are never needed
-    const int s_begin = p.causal ? min(sb * nw * 16, L - 1) / SK : 0;
+    const int s_begin = p.causal ? min(sb * nw * TT * 16, L - 1) / SK : 0;
     stage_rows<D, T>(Qb + (size_t)(p.nbuf == 1 ? 0 : (s_begin & 1)) * SK * D, qg, s_begin * SK, SK, L, wave, nw, lane);
     stage_rows<D, T>(Gb + (size_t)(p.nbuf == 1 ? 0 : (s_begin & 1)) * SK * D, gg, s_begin * SK, SK, L, wave, nw, lane);
     for (int t = tid; t < Lpad; t += nt) {
@@ -367,23 +408,32 @@ __global__ void __launch_bounds__(512) bwd_dkv_kernel(BwdParams p) {
         dlT[t] = t < L ? p.delta[base + t] : 0.f;
     }
     if constexpr (KIND != kMaskLit)
-        build_exponents<KIND>(E, scan_sh, p.ll, bh, p.H, L, Lpad, min(sb * nw * 16, L - 1), tid, nt);
+        build_exponents<KIND>(E, scan_sh, p.ll, bh, p.H, L, Lpad, min(sb * nw * TT * 16, L - 1), tid, nt);
 
-    // this lane's key row j: phi(k), v fragments
-    const int j = wt * 16 + r;
-    const bool ok = active && j < L;
-    const int jc = min(j, L - 1);
-    bf16x8 kf[NS], vf[NS];
-    row_frags<D, KIND, true>(p.k + (base + jc) * D, ok, kf);
-    row_frags<D, KIND, false>(p.v + (base + jc) * D, ok, vf);
-    __syncthreads();   // tables written (build_exponents ends with a barrier only for D and S)
-    const float Ej = KIND != kMaskLit ? E[jc] : 0.f;
-    const int wfirst = wt * 16;
-
-    f32x4 acck[NCT], accv[NCT];
+    // this lane's key row j of each tile: phi(k), v fragments
+    int jrow[TT];
+    bool ok[TT];
+    bf16x8 kf[TT][NS], vf[TT][NS];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acck[ct] = accv[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float colterm = 0.f;
+    for (int tt = 0; tt < TT; ++tt) {
+        const int j = (wt0 + tt) * 16 + r;
+        jrow[tt] = j;
+        ok[tt] = active && j < L;
+        const int jc = min(j, L - 1);
+        row_frags<D, KIND, true>(p.k + (base + jc) * D, ok[tt], kf[tt]);
+        row_frags<D, KIND, false>(p.v + (base + jc) * D, ok[tt], vf[tt]);
+    }
+    __syncthreads();   // tables written (build_exponents ends with a barrier only for D and S)
+    float Ej[TT], colterm[TT];
+    f32x4 acck[TT][NCT], accv[TT][NCT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        Ej[tt] = KIND != kMaskLit ? E[min(jrow[tt], L - 1)] : 0.f;
+        colterm[tt] = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acck[tt][ct] = accv[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int wfirst = wt0 * 16;                     // the wave's first key row
 
     for (int s = s_begin; s < nst; ++s) {
         const int buf = p.nbuf == 1 ? 0 : (s & 1);
@@ -404,64 +454,114 @@ __global__ void __launch_bounds__(512) bwd_dkv_kernel(BwdParams p) {
             const int i0 = s * SK + h * kKB;
             if (i0 >= L) break;
             if (p.causal && i0 + kKB - 1 < wfirst) continue;   // every query before every key
-            f32x4 sacc[2], dpacc[2];
+            // fragments shared by the wave's tiles: phi(Q) and dY rows, their transposes (read once up
+            // front with two tiles, where they are used with one), and the queries' divisors, deltas
+            // and mask exponents
+            bf16x8 qr[2][NS], gr[2][NS], qt[NCT], gt[NCT];
+            if constexpr (TT > 1) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int st = 0; st < NS; ++st) {
-                    sacc[t] = mfma_bf16(rows_frag<D>(qbuf, h, t, st, r, g), kf[st], sacc[t]);
-                    dpacc[t] = mfma_bf16(rows_frag<D>(gbuf, h, t, st, r, g), vf[st], dpacc[t]);
+                    for (int st = 0; st < NS; ++st) {
+                        qr[t][st] = rows_frag<D>(qbuf, h, t, st, r, g);
+                        gr[t][st] = rows_frag<D>(gbuf, h, t, st, r, g);
+                    }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    gt[ct] = tr_frag<D>(gbuf, h, ct, r, g);
+                    qt[ct] = tr_frag<D>(qbuf, h, ct, r, g);
                 }
             }
-            // element (t, e): query i = i0 + 16 t + 4 g + e, key j
-            bf16x8 pf, dsf;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            auto qrow = [&](int t, int st) { return TT > 1 ? qr[t][st] : rows_frag<D>(qbuf, h, t, st, r, g); };
+            auto grow = [&](int t, int st) { return TT > 1 ? gr[t][st] : rows_frag<D>(gbuf, h, t, st, r, g); };
+            auto qtr = [&](int ct) { return TT > 1 ? qt[ct] : tr_frag<D>(qbuf, h, ct, r, g); };
+            auto gtr = [&](int ct) { return TT > 1 ? gt[ct] : tr_frag<D>(gbuf, h, ct, r, g); };
+            // the queries' 1/den, delta and mask exponents (elements 4 g + e of half t)
+            auto query_vals = [&](int t, f32x4 &inv, f32x4 &dl, f32x4 &ei) {
                 const int ib = i0 + 16 * t + 4 * g;
                 const f32x4 dn = *reinterpret_cast<const f32x4 *>(denT + ib);
-                const f32x4 dl = *reinterpret_cast<const f32x4 *>(dlT + ib);
-                f32x4 ei = f32x4{0.f, 0.f, 0.f, 0.f};
-                if constexpr (KIND != kMaskLit) ei = *reinterpret_cast<const f32x4 *>(E + ib);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = ib + e;
-                    float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(ei[e] - Ej)) : 1.f;
-                    if (p.causal && j > i) m = 0.f;
-                    const float inv = __builtin_amdgcn_rcpf(dn[e]);
-                    const float pm = sacc[t][e] * m;
-                    const float dp = dpacc[t][e] * inv - dl[e];
-                    const float w = dp * pm;
-                    colterm += i < j ? w : (i > j ? -w : 0.f);
-                    pf[4 * t + e] = f2bf(pm * inv);
-                    dsf[4 * t + e] = f2bf(dp * m);
-                }
+                for (int e = 0; e < 4; ++e) inv[e] = __builtin_amdgcn_rcpf(dn[e]);
+                dl = *reinterpret_cast<const f32x4 *>(dlT + ib);
+                ei = f32x4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (KIND != kMaskLit) ei = *reinterpret_cast<const f32x4 *>(E + ib);
+            };
+            f32x4 inv2[2], dl2[2], ei2[2];
+            if constexpr (TT > 1) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) query_vals(t, inv2[t], dl2[t], ei2[t]);
             }
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                accv[ct] = mfma_bf16(tr_frag<D>(gbuf, h, ct, r, g), pf, accv[ct]);
-                acck[ct] = mfma_bf16(tr_frag<D>(qbuf, h, ct, r, g), dsf, acck[ct]);
+            for (int tt = 0; tt < TT; ++tt) {
+                if (wt0 + tt >= ntiles) break;
+                f32x4 sacc[2], dpacc[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < NS; ++st) {
+                        sacc[t] = mfma_bf16(qrow(t, st), kf[tt][st], sacc[t]);
+                        dpacc[t] = mfma_bf16(grow(t, st), vf[tt][st], dpacc[t]);
+                    }
+                }
+                // element (t, e): query i = i0 + 16 t + 4 g + e, key jrow[tt]
+                const int j = jrow[tt];
+                bf16x8 pf, dsf;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    f32x4 inv, dl, ei;
+                    if constexpr (TT > 1) {
+                        inv = inv2[t];
+                        dl = dl2[t];
+                        ei = ei2[t];
+                    } else {
+                        query_vals(t, inv, dl, ei);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = i0 + 16 * t + 4 * g + e;
+                        float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(ei[e] - Ej[tt])) : 1.f;
+                        if (p.causal && j > i) m = 0.f;
+                        const float pm = sacc[t][e] * m;
+                        const float dp = dpacc[t][e] * inv[e] - dl[e];
+                        const float w = dp * pm;
+                        colterm[tt] += i < j ? w : (i > j ? -w : 0.f);
+                        pf[4 * t + e] = f2bf(pm * inv[e]);
+                        dsf[4 * t + e] = f2bf(dp * m);
+                    }
+                }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    accv[tt][ct] = mfma_bf16(gtr(ct), pf, accv[tt][ct]);
+                    acck[tt][ct] = mfma_bf16(qtr(ct), dsf, acck[tt][ct]);
+                }
             }
         }
     }
     if (!active) return;
 
-    colterm += __shfl_xor(colterm, 16, 64);
-    colterm += __shfl_xor(colterm, 32, 64);
-    if (KIND != kMaskLit && ok && g == 0) p.da_col[base + j] = colterm;
-    float x[NCT][4];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(p.k + (base + jc) * D + 16 * ct + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[ct][e] = (float)k4[e];
-    }
-    phi_backward<D, KIND>(x, acck);
-    if (ok) {
+    for (int tt = 0; tt < TT; ++tt) {
+        float ctm = colterm[tt];
+        ctm += __shfl_xor(ctm, 16, 64);
+        ctm += __shfl_xor(ctm, 32, 64);
+        const int j = jrow[tt];
+        const int jc = min(j, L - 1);
+        if (KIND != kMaskLit && ok[tt] && g == 0) p.da_col[base + j] = ctm;
+        float x[NCT][4];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            store4(p.dk, p.g_bf16, (base + j) * D + 16 * ct + 4 * g, acck[ct]);
-            store4(p.dv, p.g_bf16, (base + j) * D + 16 * ct + 4 * g, accv[ct]);
+            const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(p.k + (base + jc) * D + 16 * ct + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[ct][e] = (float)k4[e];
+        }
+        phi_backward<D, KIND>(x, acck[tt]);
+        if (ok[tt]) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                store4(p.dk, p.g_bf16, (base + j) * D + 16 * ct + 4 * g, acck[tt][ct]);
+                store4(p.dv, p.g_bf16, (base + j) * D + 16 * ct + 4 * g, accv[tt][ct]);
+            }
         }
     }
 }
@@ -510,7 +610,7 @@ __global__ void __launch_bounds__(kDllThreads) bwd_dll_d_kernel(BwdParams p, int
 
 // ================================ host side ===========================================================
 struct BwdShape {
-    int nw, nsb, sk, nbuf;
+    int tt, nw, nsb, sk, nbuf;
     size_t lds_dq, lds_dkv;
 };
 
@@ -518,7 +618,11 @@ BwdShape bwd_shape(const BwdArgs &a) {
     const int ntiles = (a.L + 15) / 16;
     BwdShape sh;
     sh.nw = ntiles >= 6 ? 8 : 4;
-    sh.nsb = (ntiles + sh.nw - 1) / sh.nw;
+    // two tiles per wave (the fragments a sub-block reads from LDS serve both) from 32 tiles on;
+    // shorter sequences keep one (B64 H12 L197: 125 vs 136 us; B32 H16 L512: 349 vs 336 us; B8 H12
+    // L4097: 3776 vs 2734 us); d = 128 keeps one (registers)
+    sh.tt = a.d != 128 && ntiles >= 32 ? 2 : 1;
+    sh.nsb = (ntiles + sh.tt * sh.nw - 1) / (sh.tt * sh.nw);
     const size_t per_row = 2 * (size_t)a.d * 2;      // two bf16 rows per streamed position
     const int lr = ((a.L + kKB - 1) / kKB) * kKB;
     if ((size_t)lr * per_row <= kStageBytes) {
@@ -542,6 +646,22 @@ void allow_lds(K *kernel, size_t lds) {
     if (lds > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
+}
+
+template <int D, int KIND, int TT>
+void launch_grad_t(const BwdShape &sh, const BwdParams &p, hipStream_t stream) {
+    allow_lds(&bwd_dq_kernel<D, KIND, TT>, sh.lds_dq);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, KIND, TT>), dim3(p.nblocks), dim3(sh.nw * 64), sh.lds_dq, stream, p);
+    allow_lds(&bwd_dkv_kernel<D, KIND, TT>, sh.lds_dkv);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, KIND, TT>), dim3(p.nblocks), dim3(sh.nw * 64), sh.lds_dkv, stream, p);
+}
+
+template <int D, int KIND>
+void launch_grad(const BwdShape &sh, const BwdParams &p, hipStream_t stream) {
+    if constexpr (D != 128) {
+        if (sh.tt == 2) return launch_grad_t<D, KIND, 2>(sh, p, stream);
+    }
+    launch_grad_t<D, KIND, 1>(sh, p, stream);
 }
 
 template <int D, int KIND>
@@ -571,10 +691,7 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t stream) {
     p.sk = sh.sk;
     p.nbuf = sh.nbuf;
     p.causal = a.causal ? 1 : 0;
-    allow_lds(&bwd_dq_kernel<D, KIND>, sh.lds_dq);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, KIND>), dim3(p.nblocks), dim3(sh.nw * 64), sh.lds_dq, stream, p);
-    allow_lds(&bwd_dkv_kernel<D, KIND>, sh.lds_dkv);
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, KIND>), dim3(p.nblocks), dim3(sh.nw * 64), sh.lds_dkv, stream, p);
+    launch_grad<D, KIND>(sh, p, stream);
     if constexpr (KIND == kMaskS)
         hipLaunchKernelGGL(bwd_dll_s_kernel, dim3(a.B * a.H), dim3(kDllThreads), 0, stream, p);
     else if constexpr (KIND == kMaskD)
