@@ -285,6 +285,8 @@ def main():
         bs = torch.full((wl.H,), 3.0, dtype=torch.float32, device=dev)
         sel = (xs, ws_, bs)
     for f, form_id in (("chunk", lion.FORM_CHUNK), ("birnn", lion.FORM_BIRNN), ("full_bwd", lion.FORM_FULL_BWD)):
+        if f not in forms:
+            continue
         nb = lion.lion_attn_workspace_bytes(form_id, wl.B, wl.H, wl.L, wl.d, C, 1 if wl.dtype == "bf16" else 0)
         ws[f] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
 
