@@ -393,7 +393,9 @@ __device__ __forceinline__ void full_epilogue(FullWave<D, QT, BF16> &w, const Fu
 }
 
 // Streaming kernel: any length, fp32 or bf16, one or two token orders.  Keys and values pass through
-// LDS as one stage or as double-buffered stages.
+// LDS as one stage or as double-buffered stages.  It keeps the sub-block arithmetic of the helpers above
+// written out in place: built from the helpers it compiled to fewer registers but measured 6-7% slower
+// (B64 H12 L197 D, 36.3 vs 33.8 us on one box).
 template <int D, int KIND, int QT, bool BF16, bool TWO>
 __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
     using C = FullCfg<D, BF16>;
