@@ -8,7 +8,9 @@ of HIP events on the launch stream, so each form's average launch duration is it
 stream through HBM: the 256 MB last-level cache cannot hold them, so kernels read HBM, not cache.
 
 Prints one JSON line.  ``value`` is form-tokens per second: forms x B x L tokens per step over the
-step time (the harmonic mean of the per-form rates, which ``forms`` lists one by one).
+step time (the harmonic mean of the per-form rates, which ``forms`` lists one by one).  After the timed
+region each form is launched K more times, each launch between its own pair of events, for the spread
+of single-launch durations (``forms[f]["launch_us"]``: p10, median, p90).
 ``roofline`` is for the kernel that takes the largest share of the step; ``cpu_baseline`` times
 the fp64 oracle on the host for the same workload.
 """
@@ -332,6 +334,19 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
+    # per-launch spread (outside the timed region): each launch between its own pair of events
+    spread = {}
+    for f in forms:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for s, (e0, e1) in enumerate(evs):
+            e0.record(stream)
+            call(f, args.warmup + 5 + args.steps + s)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+        spread[f] = {"p10": float(np.percentile(us, 10)), "p50": float(np.median(us)), "p90": float(np.percentile(us, 90))}
+
     tokens = wl.B * wl.L
     per_form = {}
     for f in forms:
@@ -346,6 +361,7 @@ def main():
         }
         if f == "chunk":
             per_form[f]["C"] = C
+        per_form[f]["launch_us"] = spread[f]
     dom = max(forms, key=lambda f: per_form[f]["ms_avg"])
     nbytes, flops = algorithmic(dom, wl, C, causal)
     avg_s = per_form[dom]["ms_avg"] * 1e-3
