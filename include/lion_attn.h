@@ -142,7 +142,7 @@ LION_API int lion_attn_birnn(const void *q, const void *k, const void *v, const 
 
 /* Backward pass of the full form: the gradients of y = lion_attn_full(q, k, v, log_lambda) for an
  * incoming gradient dy, i.e. dq, dk, dv and d log_lambda.  LION trains with the attention form (the
- * OpenReview abstract: "trains like a Transformer"; Theorem 3.3 Eq. 25, reply "Concern 1"); the pages
+ * OpenReview title and abstract; Theorem 3.3 Eq. 25, reply "Concern 1"); the pages
  * print no backward formulas, so this is the chain rule of the definition above:
  *   delta_i = dy_i . y_i / den_i,   dp_ij = dy_i . v_j / den_i - delta_i,   dv_j = sum_i M_ij s_ij dy_i / den_i,
  *   dphi(q_i) = sum_j M_ij dp_ij phi(k_j),  dphi(k_j) = sum_i M_ij dp_ij phi(q_i),  then phi's Jacobian;

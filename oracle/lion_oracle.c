@@ -309,8 +309,8 @@ int lion_oracle_rows_f64(const double *q, const double *k, const double *v, cons
 }
 
 /* ---- backward pass of the full form ------------------------------------------------------------------
- * The pages train the attention form ("trains like a Transformer": [OR] abstract; [RB] reply "Concern
- * 1", Theorem 3.3 Eq. 25), so the gradient of the definition above is what training needs.  Nothing on
+ * The pages train the attention form ([OR] abstract and title; [RB] reply "Concern 1", Theorem 3.3
+ * Eq. 25), so the gradient of the definition above is what training needs.  Nothing on
  * the pages spells it out; it is the chain rule applied to the definition, step by step, for a loss
  * whose gradient with respect to y is dy:
  *
