@@ -1,0 +1,80 @@
+"""Host logic of bench.py (no GPU): algorithmic bytes and flops per launch against hand counts, the
+choice of the binding roof, the traffic summaries' source check, and the one-GPU guard."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from bidirectional_linear_attention_lion_amd import inputs as lin
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_full_vit_tiny():
+    wl = lin.WORKLOADS["vit_tiny_lit"]            # B64 H3 L197 d64 bf16, LIT: no decay input
+    nbytes, flops = bench.algorithmic("full", wl, 64)
+    assert nbytes == 4 * 64 * 3 * 197 * 64 * 2    # q, k, v read, y written, bf16
+    bh, L, d = 64 * 3, 197, 64
+    assert flops == bh * (4 * L * L * d + 2 * L * L)
+
+
+def test_algorithmic_decay_inputs():
+    base = 4 * 32 * 16 * 512 * 64 * 2
+    assert bench.algorithmic("full", lin.WORKLOADS["bert_large_s"], 64)[0] == base + 4 * 32 * 16 * 512   # LION-S
+    wl = lin.WORKLOADS["vit_base_d"]
+    assert bench.algorithmic("full", wl, 64)[0] == 4 * 64 * 12 * 197 * 64 * 2 + 4 * 12                # LION-D
+
+
+def test_algorithmic_chunk_and_rnn():
+    wl = lin.WORKLOADS["vit_base_d"]
+    bh, L, d, C = 64 * 12, 197, 64, 64
+    assert bench.algorithmic("chunk", wl, C)[1] == bh * (4 * L * C * d + 8 * L * d * d + 2 * L * C)
+    # two recurrences per token: state update and q^T S, q.z (LION-D: 5 d^2 + 4 d each)
+    assert bench.algorithmic("birnn", wl, C)[1] == bh * L * 2 * (5 * d * d + 4 * d)
+    lit = lin.WORKLOADS["vit_tiny_lit"]
+    assert bench.algorithmic("birnn", lit, C)[1] == 64 * 3 * 197 * 2 * (4 * d * d + 3 * d)
+
+
+def test_algorithmic_causal_counts_the_lower_triangle():
+    wl = lin.WORKLOADS["hires_d"]
+    bh, L, d = 8 * 12, 4097, 64
+    pairs = L * (L + 1) / 2
+    assert bench.algorithmic("full", wl, 64, causal=True)[1] == bh * (4 * pairs * d + 2 * pairs)
+
+
+def test_binding_roof():
+    # below the bf16 ridge (312.5 flop/B) the full and chunk forms are HBM-bound, above it MFMA-bound;
+    # the RNN is vector-ALU work
+    assert bench.bound_of("full", lin.WORKLOADS["vit_tiny_lit"], 64) == "hbm"       # ~99 flop/B
+    assert bench.bound_of("full", lin.WORKLOADS["bert_large_s"], 64) == "hbm"       # ~256 flop/B
+    assert bench.bound_of("full", lin.WORKLOADS["hires_d"], 64) == "mfma"           # ~2065 flop/B
+    assert bench.bound_of("chunk", lin.WORKLOADS["hires_d"], 256) == "hbm"
+    assert bench.bound_of("birnn", lin.WORKLOADS["vit_base_d"], 64) == "alu"
+    assert bench.peak_of("hbm") == (8000.0, "GB/s")
+    assert bench.peak_of("mfma") == (2500.0, "TFLOP/s")
+    assert bench.peak_of("alu") == (157.3, "TFLOP/s")
+
+
+def test_traffic_summary_needs_the_current_source(tmp_path, monkeypatch):
+    # bench.py reports counter-measured traffic only from a summary taken on the current kernel source
+    current = bench.kernel_hash("full")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    path = prof / "traffic_full_vit_tiny_lit.txt"
+    path.write_text(f"kernel_source_sha256_16: {current}\nhbm_bytes_per_launch: 19472411\n")
+    assert bench.read_traffic("full", "vit_tiny_lit") == 19472411.0
+    path.write_text("kernel_source_sha256_16: 0000000000000000\nhbm_bytes_per_launch: 19472411\n")
+    assert bench.read_traffic("full", "vit_tiny_lit") is None
+    assert bench.read_traffic("chunk", "vit_tiny_lit") is None        # no summary at all
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
