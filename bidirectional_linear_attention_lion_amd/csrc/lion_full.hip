@@ -6,9 +6,10 @@
 // (batch, head); each wave owns up to QT consecutive tiles.  Keys and values pass through LDS as
 // row-major tiles loaded straight from global memory, and V^T fragments are read from the row-major
 // value rows with ds_read_b64_tr_b16.  Two kernels:
-//   - resident (bf16, d >= 32, keys and values of the whole sequence fit 64 KiB of LDS): eight waves
-//     issue every load of the workgroup at the start, in rounds, and compute on each round of keys as
-//     soon as it has landed, so matrix-core work overlaps the memory traffic;
+//   - resident (bf16, d >= 32, keys and values of the whole sequence within 64 KiB of LDS and at most
+//     448 rows, grids of at most 256 workgroups): one compute wave per query tile plus a loader wave
+//     that issues every key/value load of the workgroup at the start, in rounds; the compute waves
+//     work on each round of keys as soon as it has landed, so matrix-core work overlaps the loads;
 //   - streaming (everything else): the sequence as one stage, or double-buffered stages whose loads
 //     are in flight while the waves compute on the previous one.
 // phi is applied to the staged keys in place (or on the way into LDS).  Per 32-key sub-block and
