@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(PKG, "liblion_attn.so")
 MASK_LIT, MASK_D, MASK_S = 0, 1, 2
 CAUSAL = 4   # OR-ed into a mask kind: the causal (unidirectional) variant
 DTYPE_F32, DTYPE_BF16 = 0, 1
-FORM_FULL, FORM_CHUNK, FORM_BIRNN, FORM_FULL_BWD = 0, 1, 2, 3
+FORM_FULL, FORM_CHUNK, FORM_BIRNN, FORM_FULL_BWD, FORM_CHUNK_BWD = 0, 1, 2, 3, 4
 _KINDS = {"lit": MASK_LIT, "d": MASK_D, "s": MASK_S}
 
 
@@ -42,9 +42,11 @@ def library() -> ctypes.CDLL:
     lib.lion_attn_chunk.argtypes = common + [i, f, i, i, i, i, i, vp, i, fp, vp, sz, vp]
     lib.lion_attn_birnn.argtypes = common + [f, i, i, i, i, i, vp, i, fp, vp, sz, vp]
     lib.lion_attn_full_bwd.argtypes = common + [i, i, i, i, i, vp, fp, vp, vp, vp, vp, i, fp, vp, sz, vp]
+    lib.lion_attn_chunk_bwd.argtypes = common + [i, i, i, i, i, i, vp, fp, vp, vp, vp, vp, i, fp, vp, sz, vp]
     lib.lion_selectivity.argtypes = [vp, vp, fp, i, i, i, i, fp, fp, vp, vp, i, vp]
     lib.lion_attn_full2.argtypes = common + [f, vp, i, i, i, i, i, vp, i, fp, vp]
-    for fn in ("lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_full_bwd", "lion_selectivity",
+    for fn in ("lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_full_bwd", "lion_attn_chunk_bwd",
+               "lion_selectivity",
                "lion_attn_full2", "lion_attn_abi_version"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.lion_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
@@ -180,6 +182,35 @@ def lion_attn_full_bwd(q, k, v, log_lambda, mask_kind, y, den, dy, *, grad_dtype
                                       _ptr(dlog_lambda), _ptr(ws), nbytes, sptr)
     if rc != 0:
         raise LionError("lion_attn_full_bwd", rc)
+    return dq, dk, dv, dlog_lambda
+
+
+def lion_attn_chunk_bwd(q, k, v, log_lambda, mask_kind, C, y, den, dy, *, grad_dtype=None, dq=None, dk=None,
+                        dv=None, dlog_lambda=None, workspace=None, stream=None):
+    """Backward pass computed chunkwise (chunks of C tokens); returns (dq, dk, dv, dlog_lambda).
+
+    Same gradients and arguments as lion_attn_full_bwd, plus the chunk size C."""
+    import torch
+    kind = _KINDS[mask_kind] if isinstance(mask_kind, str) else int(mask_kind)
+    B, H, L, d = q.shape
+    dt = _dtype_code(q)
+    gdt = q.dtype if grad_dtype is None else grad_dtype
+    dq = torch.empty((B, H, L, d), dtype=gdt, device=q.device) if dq is None else dq
+    dk = torch.empty((B, H, L, d), dtype=gdt, device=q.device) if dk is None else dk
+    dv = torch.empty((B, H, L, d), dtype=gdt, device=q.device) if dv is None else dv
+    base = kind & 3
+    if dlog_lambda is None and base != MASK_LIT:
+        shape = (H,) if base == MASK_D else (B, H, L)
+        dlog_lambda = torch.empty(shape, dtype=torch.float32, device=q.device)
+    ws, nbytes = _workspace(FORM_CHUNK_BWD, B, H, L, d, C, dt, workspace, q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sptr = ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    rc = library().lion_attn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_lambda), kind, C, B, H, L, d, dt, _ptr(y),
+                                       _ptr(den), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(dq),
+                                       _ptr(dlog_lambda), _ptr(ws), nbytes, sptr)
+    if rc != 0:
+        raise LionError("lion_attn_chunk_bwd", rc)
     return dq, dk, dv, dlog_lambda
 
 

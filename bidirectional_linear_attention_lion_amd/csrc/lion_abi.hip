@@ -127,10 +127,14 @@ int lion_attn_birnn(const void *q, const void *k, const void *v, const float *lo
     return status_of(lion::launch_birnn(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int lion_attn_full_bwd(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, int B,
-                       int H, int L, int d, int dtype, const void *y, const float *den, const void *dy, void *dq,
-                       void *dk, void *dv, int grad_dtype, float *dlog_lambda, void *workspace, size_t workspace_bytes,
-                       void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two backward entry points; fills `a` (workspace excluded) on success.
+int bwd_args(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, int B, int H, int L,
+             int d, int dtype, const void *y, const float *den, const void *dy, void *dq, void *dk, void *dv,
+             int grad_dtype, float *dlog_lambda, const void *workspace, lion::BwdArgs &a) {
     int rc = check_common(q, k, v, log_lambda, mask_kind, 0.f, B, H, L, d, dtype, y, dtype, nullptr);
     if (rc != LION_OK) return rc;
     if (!den || !dy || !dq || !dk || !dv) return LION_ERR_INVALID;
@@ -141,7 +145,7 @@ int lion_attn_full_bwd(const void *q, const void *k, const void *v, const float 
     if (grad_dtype != LION_DTYPE_F32 && grad_dtype != LION_DTYPE_BF16) return LION_ERR_INVALID;
     if (workspace && !aligned16(workspace)) return LION_ERR_INVALID;
     if (dtype != LION_DTYPE_BF16) return LION_ERR_UNSUPPORTED;
-    lion::BwdArgs a;
+    a = lion::BwdArgs{};
     a.q = q;
     a.k = k;
     a.v = v;
@@ -160,12 +164,45 @@ int lion_attn_full_bwd(const void *q, const void *k, const void *v, const float 
     a.dv = dv;
     a.g_bf16 = grad_dtype == LION_DTYPE_BF16;
     a.dll = dlog_lambda;
+    return LION_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lion_attn_full_bwd(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, int B,
+                       int H, int L, int d, int dtype, const void *y, const float *den, const void *dy, void *dq,
+                       void *dk, void *dv, int grad_dtype, float *dlog_lambda, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    lion::BwdArgs a;
+    const int rc = bwd_args(q, k, v, log_lambda, mask_kind, B, H, L, d, dtype, y, den, dy, dq, dk, dv, grad_dtype,
+                            dlog_lambda, workspace, a);
+    if (rc != LION_OK) return rc;
     const lion::Plan plan = lion::plan_full_bwd(a);
     if (!plan.ok) return LION_ERR_UNSUPPORTED;
     if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return LION_ERR_WORKSPACE;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
     return status_of(lion::launch_full_bwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int lion_attn_chunk_bwd(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, int C,
+                        int B, int H, int L, int d, int dtype, const void *y, const float *den, const void *dy,
+                        void *dq, void *dk, void *dv, int grad_dtype, float *dlog_lambda, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    lion::BwdArgs a;
+    const int rc = bwd_args(q, k, v, log_lambda, mask_kind, B, H, L, d, dtype, y, den, dy, dq, dk, dv, grad_dtype,
+                            dlog_lambda, workspace, a);
+    if (rc != LION_OK) return rc;
+    if (!c_supported(C)) return LION_ERR_UNSUPPORTED;
+    a.C = C;
+    const lion::Plan plan = lion::plan_chunk_bwd(a);
+    if (!plan.ok) return LION_ERR_UNSUPPORTED;
+    if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return LION_ERR_WORKSPACE;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    return status_of(lion::launch_chunk_bwd(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int lion_selectivity(const void *x, const void *w, const float *bias, int B, int L, int H, int Dm, float *log_lambda,
@@ -221,6 +258,18 @@ size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, in
         b.L = L;
         b.d = d;
         plan = lion::plan_full_bwd(b);
+        break;
+    }
+    case LION_FORM_CHUNK_BWD: {
+        if (dtype != LION_DTYPE_BF16) return (size_t)-1;
+        lion::BwdArgs b{};
+        b.kind = LION_MASK_S;
+        b.B = B;
+        b.H = H;
+        b.L = L;
+        b.d = d;
+        b.C = C;
+        plan = lion::plan_chunk_bwd(b);
         break;
     }
     default: return (size_t)-1;

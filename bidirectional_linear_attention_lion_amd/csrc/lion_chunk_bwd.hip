@@ -1,0 +1,676 @@
+// lion_chunk_bwd.hip -- backward pass of the chunkwise form of LION.
+//
+// The gradients are those of the full form's backward (the chain rule of y = attention(q, k, v) with
+// LION's mask; LION trains with the attention form, OpenReview abstract and reply "Concern 1",
+// Theorem 3.3 Eq. 25), computed the way the chunkwise form computes y (reply "4: Practicality of
+// Recurrent Inference"; blog "LION Part IV - Results", "LION Chunk"): inside a chunk of C tokens
+// pair by pair, across chunks through d x (d+1) states, so the work per (batch, head) is
+// O(L C d + L d^2) rather than O(L^2 d).
+//
+// With u_i = [dy_i / den_i, -delta_i] (delta_i = dy_i.y_i / den_i) and w_j = [v_j, 1], the gradient of
+// the score of pair (i, j) is dp_ij = u_i.w_j, and
+//   dphi(q_i) = sum_j M_ij dp_ij phi(k_j)        = (sum_j M_ij phi(k_j) w_j^T) u_i
+//   dphi(k_j) = sum_i M_ij dp_ij phi(q_i)        = (sum_i M_ij phi(q_i) u_i^T) w_j
+//   dv_j      = sum_i M_ij s_ij dy_i / den_i     = (sum_i M_ij phi(q_i) u_i^T)[:, :d]^T phi(k_j)
+// so the keys' states are the forward pass's (phi(k) [v, 1]^T) and the queries' states are the same
+// construction over phi(q) u^T.  For a token t of chunk c (first token s, last e), the tokens of
+// earlier chunks enter through the state entering from the left, weighted by exp(A_t - A_{s-1}), and
+// those of later chunks through the state entering from the right, weighted by exp(A_e - A_t); both
+// exponents are sums of log(lambda) inside the chunk, so no prefix over the whole sequence is needed.
+// The mask's gradient splits the same way: with w_ij = dp_ij M_ij s_ij,
+//   dA_t = sum_{j<t} w_tj - sum_{j>t} w_tj  (row half) + sum_{i<t} w_it - sum_{i>t} w_it  (column half)
+// and the row half over earlier chunks is phi(q_t) . (left state) u_t, times the weight, etc.
+// dlog(lambda) then follows from dA as in the full form's backward (a reverse prefix sum for LION-S,
+// sum_t t dA_t for LION-D).
+//
+// Three launches plus the dlog(lambda) one:
+//   local: one workgroup per (batch, head, chunk) sums the chunk's four states (keys and queries, each
+//          weighted towards the chunk's right end and towards its left end) into the workspace;
+//   scan:  per (batch, head) and state element, replaces each chunk's local state by the state entering
+//          it (from the left for the first two, from the right for the other two);
+//   main:  one workgroup per chunk forms the pair matrices M dp, M s and the signed w in LDS, then
+//          dphi(q), dphi(k), dv and the dA halves from them and from the four entering states, applies
+//          phi's Jacobian and stores dq, dk, dv.
+// Everything is fp32 vector arithmetic on LDS tiles.
+// Causal variant (M_ij = 0 for j > i): pairs above the diagonal drop out, and so do the keys' states
+// entering from the right and the queries' states entering from the left (a key sees later queries).
+#include "lion_device.h"
+#include "lion_internal.h"
+
+namespace lion {
+namespace {
+
+constexpr int kThreads = 256;   // a 16 x 16 grid of threads
+
+struct CbParams {
+    const __bf16 *q, *k, *v, *y, *dy;
+    const float *den, *ll;
+    int H, L, nch, causal;
+    void *dq, *dk, *dv;
+    int g_bf16;
+    float *states;           // [B H][nch][4][D][D + 1]: key-left, query-left, key-right, query-right
+    float *tot;              // [B H][nch]: the chunk's sum of log(lambda), times log2(e)
+    float *da_row, *da_col;  // [B H L]
+};
+
+template <int D, int CT>
+struct CbCfg {
+    static constexpr int DP = D + 4;          // LDS row stride of token rows (floats)
+    static constexpr int CP = CT + 4;         // LDS row stride of the pair matrices
+    static constexpr int T = CT / 16;         // token rows per thread (rows grp, grp + 16, ...)
+    static constexpr int TA = D / 16;         // contiguous channels per thread
+    static constexpr int DS = D + 1;          // row stride of a state
+    static constexpr int DD = D * DS;         // floats per state
+    static constexpr int TOK = 4 * CT * DP + 2 * CT + 4;   // phi(q), phi(k), v, dy/den; -delta; cum; tot
+    static constexpr int MAT = 3 * CT * CP;
+    static constexpr int BUF = MAT > DD ? MAT : DD;
+    static constexpr size_t LDS = (size_t)(TOK + BUF) * 4;
+};
+
+size_t cbwd_lds(int d, int C) {
+    const int DP = d + 4, CP = C + 4, DD = d * (d + 1);
+    const int tok = 4 * C * DP + 2 * C + 4, mat = 3 * C * CP;
+    return (size_t)(tok + (mat > DD ? mat : DD)) * 4;
+}
+
+template <int N>
+__device__ __forceinline__ void lds_load(float (&x)[N], const float *p) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < N; e += 4) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(p + e);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[e + i] = t[i];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < N; ++e) x[e] = p[e];
+    }
+}
+
+// Stage the chunk's tokens into LDS as fp32 rows: phi(q), phi(k), v, u = dy / den, and -delta;
+// then the chunk's prefix sums of log(lambda) (log2 units, relative to the chunk start, inclusive).
+// Rows at or past n are zero; prefix sums past n repeat the last one.
+template <int D, int KIND, int CT>
+__device__ void stage_tokens(const CbParams &p, float *sm, int bh, int c, int n) {
+    using CF = CbCfg<D, CT>;
+    float *Qs = sm, *Ks = Qs + CT * CF::DP, *Vs = Ks + CT * CF::DP, *Us = Vs + CT * CF::DP;
+    float *nd = Us + CT * CF::DP, *cum = nd + CT;
+    const int tid = threadIdx.x;
+    constexpr int SPR = D / 8;          // 16-byte slots per row
+    constexpr int NSL = CT * SPR;       // a multiple of 64
+    const size_t row0 = (size_t)bh * p.L + (size_t)c * CT;
+    for (int sl0 = 0; sl0 < NSL; sl0 += kThreads) {
+        if (sl0 + (tid & ~63) >= NSL) break;   // whole waves
+        const int sl = sl0 + tid;
+        const int row = sl / SPR, cs = (sl % SPR) * 8;
+        const bool ok = row < n;
+        float fq[8], fk[8], fv[8], fu[8];
+        float ssq = 0.f, ssk = 0.f, part = 0.f, dinv = 0.f;
+        if (ok) {
+            const size_t g = (row0 + row) * D + cs;
+            const bf16x8 q8 = __builtin_bit_cast(bf16x8, ld16(p.q + g));
+            const bf16x8 k8 = __builtin_bit_cast(bf16x8, ld16(p.k + g));
+            const bf16x8 v8 = __builtin_bit_cast(bf16x8, ld16(p.v + g));
+            const bf16x8 y8 = __builtin_bit_cast(bf16x8, ld16(p.y + g));
+            const bf16x8 d8 = __builtin_bit_cast(bf16x8, ld16(p.dy + g));
+            dinv = 1.f / p.den[row0 + row];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                fq[e] = phi_pre<KIND>((float)q8[e]);
+                fk[e] = phi_pre<KIND>((float)k8[e]);
+                fv[e] = (float)v8[e];
+                fu[e] = (float)d8[e] * dinv;
+                ssq += fq[e] * fq[e];
+                ssk += fk[e] * fk[e];
+                part += (float)d8[e] * (float)y8[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) fq[e] = fk[e] = fv[e] = fu[e] = 0.f;
+        }
+        part = group_sum<SPR>(part);
+        if constexpr (KIND == kMaskS) {
+            const float sq = inv_norm(group_sum<SPR>(ssq)), sk = inv_norm(group_sum<SPR>(ssk));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                fq[e] *= sq;
+                fk[e] *= sk;
+            }
+        }
+        float *dst[4] = {Qs, Ks, Vs, Us};
+        const float *src[4] = {fq, fk, fv, fu};
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            f32x4 lo, hi;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lo[e] = src[a][e];
+                hi[e] = src[a][4 + e];
+            }
+            *reinterpret_cast<f32x4 *>(dst[a] + row * CF::DP + cs) = lo;
+            *reinterpret_cast<f32x4 *>(dst[a] + row * CF::DP + cs + 4) = hi;
+        }
+        if (sl % SPR == 0) nd[row] = ok ? -part * dinv : 0.f;
+    }
+    if (tid < 64) {
+        const int t = tid;
+        float c2 = 0.f, tot2 = 0.f;
+        if constexpr (KIND == kMaskD) {
+            const float lg = p.ll[bh % p.H] * kLog2e;
+            c2 = (float)(min(t, n - 1) + 1) * lg;
+            tot2 = (float)n * lg;
+        } else if constexpr (KIND == kMaskS) {
+            double x = t < n ? (double)p.ll[row0 + t] : 0.0;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const double up = __shfl_up(x, o, 64);
+                if (t >= o) x += up;
+            }
+            c2 = (float)(x * 1.4426950408889634);
+            tot2 = (float)(__shfl(x, 63, 64) * 1.4426950408889634);
+        }
+        if (t < CT) cum[t] = c2;
+        if (t == 0) cum[CT] = tot2;
+    }
+}
+
+// ================================ local states =======================================================
+// Thread (ti, tj) owns state rows ti TA .. + TA - 1 and columns tj TA .. + TA - 1, plus column D of
+// its rows (written by the tj = 0 threads).
+template <int D, int KIND, int CT>
+__global__ void __launch_bounds__(kThreads) cbwd_local_kernel(CbParams p) {
+    using CF = CbCfg<D, CT>;
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    const int bh = blockIdx.x / p.nch, c = blockIdx.x % p.nch;
+    const int n = min(CT, p.L - c * CT);
+    stage_tokens<D, KIND, CT>(p, sm, bh, c, n);
+    __syncthreads();
+    const float *Qs = sm, *Ks = Qs + CT * CF::DP, *Vs = Ks + CT * CF::DP, *Us = Vs + CT * CF::DP;
+    const float *nd = Us + CT * CF::DP, *cum = nd + CT;
+    const float tot2 = cum[CT];
+    const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
+    constexpr int TA = CF::TA;
+    float *out = p.states + ((size_t)bh * p.nch + c) * 4 * CF::DD;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {   // 0: keys with [v, 1]; 1: queries with [dy / den, -delta]
+        const float *X = pass == 0 ? Ks : Qs, *Y = pass == 0 ? Vs : Us;
+        float fw[TA][TA], bw[TA][TA], fz[TA], bz[TA];
+#pragma unroll
+        for (int e = 0; e < TA; ++e) {
+            fz[e] = bz[e] = 0.f;
+#pragma unroll
+            for (int e2 = 0; e2 < TA; ++e2) fw[e][e2] = bw[e][e2] = 0.f;
+        }
+        for (int j = 0; j < n; ++j) {
+            const float ef = KIND == kMaskLit ? 1.f : fast_exp2(tot2 - cum[j]);   // towards the right end
+            const float eb = KIND == kMaskLit ? 1.f : fast_exp2(cum[j]);          // towards the left end
+            const float last = pass == 0 ? 1.f : nd[j];
+            float x[TA], y[TA];
+            lds_load(x, X + j * CF::DP + ti * TA);
+            lds_load(y, Y + j * CF::DP + tj * TA);
+#pragma unroll
+            for (int e = 0; e < TA; ++e) {
+                const float xf = ef * x[e], xb = eb * x[e];
+                fz[e] += xf * last;
+                bz[e] += xb * last;
+#pragma unroll
+                for (int e2 = 0; e2 < TA; ++e2) {
+                    fw[e][e2] += xf * y[e2];
+                    bw[e][e2] += xb * y[e2];
+                }
+            }
+        }
+        float *dl = out + pass * CF::DD, *dr = out + (2 + pass) * CF::DD;
+        // causal: queries see earlier keys only, so the keys' states enter from the left and the
+        // queries' states from the right
+        const bool keep_l = !p.causal || pass == 0, keep_r = !p.causal || pass == 1;
+#pragma unroll
+        for (int e = 0; e < TA; ++e) {
+            const int a = ti * TA + e;
+#pragma unroll
+            for (int e2 = 0; e2 < TA; ++e2) {
+                if (keep_l) dl[a * CF::DS + tj * TA + e2] = fw[e][e2];
+                if (keep_r) dr[a * CF::DS + tj * TA + e2] = bw[e][e2];
+            }
+            if (tj == 0) {
+                if (keep_l) dl[a * CF::DS + D] = fz[e];
+                if (keep_r) dr[a * CF::DS + D] = bz[e];
+            }
+        }
+    }
+    if (tid == 0) p.tot[(size_t)bh * p.nch + c] = tot2;
+}
+
+// ================================ scan over chunks ====================================================
+// One thread per (batch, head, state element): the state entering chunk c from the left is
+// S_c = exp(tot_{c-1}) S_{c-1} + local_{c-1} (S_0 = 0); from the right, the mirror image.
+__global__ void __launch_bounds__(kThreads) cbwd_scan_kernel(CbParams p, int DD, int nbpb) {
+    const int bh = blockIdx.x / nbpb;
+    const int e = (blockIdx.x % nbpb) * kThreads + threadIdx.x;
+    if (e >= 4 * DD) return;
+    const int st = e / DD, off = e % DD;
+    if (p.causal && (st == 1 || st == 2)) return;   // query-left and key-right states are unused
+    const size_t stride = 4 * (size_t)DD;
+    float *base = p.states + (size_t)bh * p.nch * stride + (size_t)st * DD + off;
+    const float *tt = p.tot + (size_t)bh * p.nch;
+    const int nch = p.nch;
+    constexpr int kBatch = 8;
+    float run = 0.f;
+    if (st < 2) {
+        for (int c0 = 0; c0 < nch; c0 += kBatch) {
+            float x[kBatch], f[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int c = c0 + u;
+                x[u] = c < nch ? base[c * stride] : 0.f;
+                f[u] = c < nch ? fast_exp2(tt[c]) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int c = c0 + u;
+                if (c < nch) {
+                    base[c * stride] = run;
+                    run = f[u] * run + x[u];
+                }
+            }
+        }
+    } else {
+        for (int c0 = nch - 1; c0 >= 0; c0 -= kBatch) {
+            float x[kBatch], f[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int c = c0 - u;
+                x[u] = c >= 0 ? base[c * stride] : 0.f;
+                f[u] = c >= 0 ? fast_exp2(tt[c]) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int c = c0 - u;
+                if (c >= 0) {
+                    base[c * stride] = run;
+                    run = f[u] * run + x[u];
+                }
+            }
+        }
+    }
+}
+
+// ================================ main ===============================================================
+// The transposed Jacobian of phi at the raw inputs x (TA channels of one row; the 16 threads of a row
+// hold its D channels) applied to g in place.
+template <int TA, int KIND>
+__device__ __forceinline__ void phi_backward_row(const float (&x)[TA], float (&g)[TA]) {
+    if constexpr (KIND == kMaskLit) {
+#pragma unroll
+        for (int e = 0; e < TA; ++e)
+            if (!(x[e] > 0.f)) g[e] *= fast_exp2(x[e] * kLog2e);
+    } else if constexpr (KIND == kMaskS) {
+        float sig[TA], sv[TA], ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < TA; ++e) {
+            sig[e] = __builtin_amdgcn_rcpf(1.f + fast_exp2(-x[e] * kLog2e));
+            sv[e] = x[e] * sig[e];
+            ss += sv[e] * sv[e];
+        }
+        const float inv = inv_norm(group_sum<16>(ss));
+        float pg = 0.f;
+#pragma unroll
+        for (int e = 0; e < TA; ++e) pg += sv[e] * inv * g[e];
+        pg = group_sum<16>(pg);
+#pragma unroll
+        for (int e = 0; e < TA; ++e) {
+            const float ds = sig[e] * (1.f + x[e] * (1.f - sig[e]));
+            g[e] = ds * (g[e] - sv[e] * inv * pg) * inv;
+        }
+    }
+}
+
+template <int TA>
+__device__ __forceinline__ void load_raw(const __bf16 *src, float (&x)[TA]) {
+    __bf16 b[TA];
+    __builtin_memcpy(b, src, sizeof(b));
+#pragma unroll
+    for (int e = 0; e < TA; ++e) x[e] = (float)b[e];
+}
+
+template <int TA>
+__device__ __forceinline__ void store_row(void *base, bool bf16, size_t off, const float (&g)[TA]) {
+    if (bf16) {
+        __bf16 b[TA];
+#pragma unroll
+        for (int e = 0; e < TA; ++e) b[e] = f2bf(g[e]);
+        __builtin_memcpy(reinterpret_cast<__bf16 *>(base) + off, b, sizeof(b));
+    } else {
+        __builtin_memcpy(reinterpret_cast<float *>(base) + off, g, sizeof(g));
+    }
+}
+
+template <int D, int KIND, int CT>
+__global__ void __launch_bounds__(kThreads) cbwd_main_kernel(CbParams p) {
+    using CF = CbCfg<D, CT>;
+    constexpr int T = CF::T, TA = CF::TA, DP = CF::DP, CP = CF::CP, DS = CF::DS;
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    const int bh = blockIdx.x / p.nch, c = blockIdx.x % p.nch;
+    const int n = min(CT, p.L - c * CT);
+    stage_tokens<D, KIND, CT>(p, sm, bh, c, n);
+    __syncthreads();
+    const float *Qs = sm, *Ks = Qs + CT * DP, *Vs = Ks + CT * DP, *Us = Vs + CT * DP;
+    const float *nd = Us + CT * DP, *cum = nd + CT;
+    float *buf = sm + CF::TOK;
+    float *D1 = buf, *D2 = D1 + CT * CP, *SW = D2 + CT * CP;
+    const float tot2 = cum[CT];
+    const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
+    const bool causal = p.causal != 0;
+
+    // ---- pair matrices: D1 = M dp, D2 = M s, SW = sign(i - j) M dp s (rows ti + 16 r, columns tj + 16 r2)
+    {
+        float ax[T][T], as[T][T];
+#pragma unroll
+        for (int r = 0; r < T; ++r)
+#pragma unroll
+            for (int r2 = 0; r2 < T; ++r2) ax[r][r2] = as[r][r2] = 0.f;
+#pragma unroll 1
+        for (int a = 0; a < D; a += 4) {
+            f32x4 u[T], qq[T], vv[T], kk[T];
+#pragma unroll
+            for (int r = 0; r < T; ++r) {
+                u[r] = *reinterpret_cast<const f32x4 *>(Us + (ti + 16 * r) * DP + a);
+                qq[r] = *reinterpret_cast<const f32x4 *>(Qs + (ti + 16 * r) * DP + a);
+                vv[r] = *reinterpret_cast<const f32x4 *>(Vs + (tj + 16 * r) * DP + a);
+                kk[r] = *reinterpret_cast<const f32x4 *>(Ks + (tj + 16 * r) * DP + a);
+            }
+#pragma unroll
+            for (int r = 0; r < T; ++r)
+#pragma unroll
+                for (int r2 = 0; r2 < T; ++r2)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ax[r][r2] += u[r][e] * vv[r2][e];
+                        as[r][r2] += qq[r][e] * kk[r2][e];
+                    }
+        }
+#pragma unroll
+        for (int r = 0; r < T; ++r)
+#pragma unroll
+            for (int r2 = 0; r2 < T; ++r2) {
+                const int i = ti + 16 * r, j = tj + 16 * r2;
+                const bool ok = i < n && j < n && !(causal && j > i);
+                float m = 0.f;
+                if (ok) m = KIND == kMaskLit ? 1.f : fast_exp2(-fabsf(cum[i] - cum[j]));
+                const float dp = ax[r][r2] + nd[i];
+                const float sgn = j < i ? 1.f : (j > i ? -1.f : 0.f);
+                D1[i * CP + j] = m * dp;
+                D2[i * CP + j] = m * as[r][r2];
+                SW[i * CP + j] = sgn * m * dp * as[r][r2];
+            }
+    }
+    __syncthreads();
+
+    // ---- intra-chunk parts: rows t = ti + 16 r, channels ta TA .. + TA - 1 (ta = tj)
+    const int ta = tj, a0 = ta * TA;
+    float gq[T][TA], gk[T][TA], gv[T][TA], dar[T], dac[T];
+#pragma unroll
+    for (int r = 0; r < T; ++r) {
+        dar[r] = dac[r] = 0.f;
+#pragma unroll
+        for (int e = 0; e < TA; ++e) gq[r][e] = gk[r][e] = gv[r][e] = 0.f;
+    }
+#pragma unroll 2
+    for (int j = 0; j < n; ++j) {
+        float kv[TA], qv[TA], uv[TA];
+        lds_load(kv, Ks + j * DP + a0);
+        lds_load(qv, Qs + j * DP + a0);
+        lds_load(uv, Us + j * DP + a0);
+#pragma unroll
+        for (int r = 0; r < T; ++r) {
+            const int t = ti + 16 * r;
+            const float d1 = D1[t * CP + j], d1t = D1[j * CP + t], d2t = D2[j * CP + t];
+#pragma unroll
+            for (int e = 0; e < TA; ++e) {
+                gq[r][e] += d1 * kv[e];
+                gk[r][e] += d1t * qv[e];
+                gv[r][e] += d2t * uv[e];
+            }
+        }
+    }
+    if constexpr (KIND != kMaskLit) {
+#pragma unroll
+        for (int r = 0; r < T; ++r) {
+            const int t = ti + 16 * r;
+#pragma unroll
+            for (int jj = 0; jj < T; ++jj) {
+                const int j = ta + 16 * jj;
+                dar[r] += SW[t * CP + j];
+                dac[r] -= SW[j * CP + t];
+            }
+        }
+    }
+    __syncthreads();   // the pair matrices' space takes the states next
+
+    // ---- the four entering states
+    const int c_last = p.nch - 1;
+#pragma unroll 1
+    for (int st = 0; st < 4; ++st) {
+        const bool right = st >= 2, keys = (st & 1) == 0;
+        // zero states: nothing left of the first chunk or right of the last; causal, the keys' state
+        // from the right and the queries' state from the left
+        if ((right ? c == c_last : c == 0) || (causal && keys == right)) continue;
+        const float *src = p.states + (((size_t)bh * p.nch + c) * 4 + st) * CF::DD;
+        for (int e = tid * 4; e < CF::DD; e += kThreads * 4)
+            *reinterpret_cast<f32x4 *>(buf + e) = *reinterpret_cast<const f32x4 *>(src + e);
+        __syncthreads();
+        float f[T];
+#pragma unroll
+        for (int r = 0; r < T; ++r) {
+            const float ct = cum[ti + 16 * r];
+            f[r] = KIND == kMaskLit ? 1.f : fast_exp2(right ? tot2 - ct : ct);
+        }
+        const float sgn = right ? -1.f : 1.f;
+        const float *Xs = keys ? Us : Vs;   // the vector the state multiplies (u for keys, w for queries)
+        float o[T][TA];
+#pragma unroll
+        for (int r = 0; r < T; ++r)
+#pragma unroll
+            for (int e = 0; e < TA; ++e) o[r][e] = 0.f;
+#pragma unroll 1
+        for (int b = 0; b < D; b += 4) {
+            f32x4 xv[T];
+#pragma unroll
+            for (int r = 0; r < T; ++r) xv[r] = *reinterpret_cast<const f32x4 *>(Xs + (ti + 16 * r) * DP + b);
+#pragma unroll
+            for (int e = 0; e < TA; ++e) {
+                const float *srow = buf + (a0 + e) * DS + b;
+                const float s0 = srow[0], s1 = srow[1], s2 = srow[2], s3 = srow[3];
+#pragma unroll
+                for (int r = 0; r < T; ++r) o[r][e] += s0 * xv[r][0] + s1 * xv[r][1] + s2 * xv[r][2] + s3 * xv[r][3];
+            }
+        }
+        // column D: times -delta (keys' states) or 1 (queries' states)
+#pragma unroll
+        for (int r = 0; r < T; ++r) {
+            const float last = keys ? nd[ti + 16 * r] : 1.f;
+#pragma unroll
+            for (int e = 0; e < TA; ++e) o[r][e] += buf[(a0 + e) * DS + D] * last;
+        }
+        const float *Ps = keys ? Qs : Ks;   // the dA half dots the result with phi of the same token
+#pragma unroll
+        for (int r = 0; r < T; ++r) {
+            const int t = ti + 16 * r;
+            float pv[TA];
+            lds_load(pv, Ps + t * DP + a0);
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < TA; ++e) {
+                dot += pv[e] * o[r][e];
+                if (keys) gq[r][e] += f[r] * o[r][e];
+                else gk[r][e] += f[r] * o[r][e];
+            }
+            if (keys) dar[r] += sgn * f[r] * dot;
+            else dac[r] += sgn * f[r] * dot;
+        }
+        if (!keys) {   // dv: the state's first D columns, transposed, times phi(k_t)
+            float ov[T][TA];
+#pragma unroll
+            for (int r = 0; r < T; ++r)
+#pragma unroll
+                for (int e = 0; e < TA; ++e) ov[r][e] = 0.f;
+#pragma unroll 1
+            for (int a = 0; a < D; a += 4) {
+                f32x4 kv[T];
+#pragma unroll
+                for (int r = 0; r < T; ++r) kv[r] = *reinterpret_cast<const f32x4 *>(Ks + (ti + 16 * r) * DP + a);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    float srow[TA];
+#pragma unroll
+                    for (int e = 0; e < TA; ++e) srow[e] = buf[(a + u) * DS + a0 + e];
+#pragma unroll
+                    for (int r = 0; r < T; ++r)
+#pragma unroll
+                        for (int e = 0; e < TA; ++e) ov[r][e] += kv[r][u] * srow[e];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < T; ++r)
+#pragma unroll
+                for (int e = 0; e < TA; ++e) gv[r][e] += f[r] * ov[r][e];
+        }
+        __syncthreads();
+    }
+
+    // ---- phi's Jacobian, stores
+    const size_t row0 = (size_t)bh * p.L + (size_t)c * CT;
+    const bool gb = p.g_bf16 != 0;
+#pragma unroll
+    for (int r = 0; r < T; ++r) {
+        const int t = ti + 16 * r;
+        if (t >= n) break;   // the row's 16 threads agree; later r only grow
+        const size_t off = (row0 + t) * D + a0;
+        if constexpr (KIND != kMaskD) {
+            float xq[TA], xk[TA];
+            load_raw(p.q + off, xq);
+            load_raw(p.k + off, xk);
+            phi_backward_row<TA, KIND>(xq, gq[r]);
+            phi_backward_row<TA, KIND>(xk, gk[r]);
+        }
+        store_row(p.dq, gb, off, gq[r]);
+        store_row(p.dk, gb, off, gk[r]);
+        store_row(p.dv, gb, off, gv[r]);
+        if constexpr (KIND != kMaskLit) {
+            const float sr = group_sum<16>(dar[r]), sc = group_sum<16>(dac[r]);
+            if (ta == 0) {
+                p.da_row[row0 + t] = sr;
+                p.da_col[row0 + t] = sc;
+            }
+        }
+    }
+}
+
+// ================================ host side ===========================================================
+template <typename K>
+void allow_lds(K *kernel, size_t lds) {
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+}
+
+struct CbLayout {
+    size_t states, tot, da;   // float offsets into the workspace
+    size_t floats;
+};
+
+CbLayout cbwd_layout(int B, int H, int L, int d, int C) {
+    const size_t bh = (size_t)B * H, nch = (size_t)((L + C - 1) / C);
+    const size_t dd = (size_t)d * (d + 1);
+    CbLayout w;
+    w.states = 0;
+    w.tot = 4 * bh * nch * dd;
+    w.da = w.tot + ((bh * nch + 3) / 4) * 4;
+    w.floats = w.da + 2 * (((bh * L) + 3) / 4) * 4;
+    return w;
+}
+
+template <int D, int KIND, int CT>
+hipError_t launch_cbwd_t(const BwdArgs &a, hipStream_t stream) {
+    using CF = CbCfg<D, CT>;
+    const CbLayout w = cbwd_layout(a.B, a.H, a.L, a.d, CT);
+    float *ws = reinterpret_cast<float *>(a.workspace);
+    CbParams p;
+    p.q = reinterpret_cast<const __bf16 *>(a.q);
+    p.k = reinterpret_cast<const __bf16 *>(a.k);
+    p.v = reinterpret_cast<const __bf16 *>(a.v);
+    p.y = reinterpret_cast<const __bf16 *>(a.y);
+    p.dy = reinterpret_cast<const __bf16 *>(a.dy);
+    p.den = a.den;
+    p.ll = a.log_lambda;
+    p.H = a.H;
+    p.L = a.L;
+    p.nch = (a.L + CT - 1) / CT;
+    p.causal = a.causal ? 1 : 0;
+    p.dq = a.dq;
+    p.dk = a.dk;
+    p.dv = a.dv;
+    p.g_bf16 = a.g_bf16 ? 1 : 0;
+    p.states = ws + w.states;
+    p.tot = ws + w.tot;
+    const size_t n = (size_t)a.B * a.H * a.L;
+    p.da_row = ws + w.da;
+    p.da_col = p.da_row + ((n + 3) / 4) * 4;
+    const int nblk = a.B * a.H * p.nch;
+    if (p.nch > 1) {
+        allow_lds(&cbwd_local_kernel<D, KIND, CT>, CF::LDS);
+        hipLaunchKernelGGL((cbwd_local_kernel<D, KIND, CT>), dim3(nblk), dim3(kThreads), CF::LDS, stream, p);
+        const int nbpb = (4 * CF::DD + kThreads - 1) / kThreads;
+        hipLaunchKernelGGL(cbwd_scan_kernel, dim3(a.B * a.H * nbpb), dim3(kThreads), 0, stream, p, CF::DD, nbpb);
+    }
+    allow_lds(&cbwd_main_kernel<D, KIND, CT>, CF::LDS);
+    hipLaunchKernelGGL((cbwd_main_kernel<D, KIND, CT>), dim3(nblk), dim3(kThreads), CF::LDS, stream, p);
+    if (KIND != kMaskLit) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_dll(KIND, p.da_row, p.da_col, a.dll, a.B, a.H, a.L, stream);
+    }
+    return hipGetLastError();
+}
+
+template <int D, int KIND>
+hipError_t launch_cbwd_c(const BwdArgs &a, hipStream_t stream) {
+    switch (a.C) {
+    case 16: return launch_cbwd_t<D, KIND, 16>(a, stream);
+    case 32: return launch_cbwd_t<D, KIND, 32>(a, stream);
+    default:
+        if constexpr (D != 128) return launch_cbwd_t<D, KIND, 64>(a, stream);
+        return hipErrorInvalidValue;
+    }
+}
+
+template <int D>
+hipError_t launch_cbwd_kind(const BwdArgs &a, hipStream_t stream) {
+    switch (a.kind) {
+    case kMaskLit: return launch_cbwd_c<D, kMaskLit>(a, stream);
+    case kMaskD: return launch_cbwd_c<D, kMaskD>(a, stream);
+    default: return launch_cbwd_c<D, kMaskS>(a, stream);
+    }
+}
+
+}  // namespace
+
+Plan plan_chunk_bwd(const BwdArgs &a) {
+    Plan p;
+    const bool dims = a.d == 32 || a.d == 64 || a.d == 128;
+    const bool cs = a.C == 16 || a.C == 32 || a.C == 64;
+    p.ok = dims && cs && cbwd_lds(a.d, a.C) <= kLdsPerWorkgroup;
+    p.workspace = p.ok ? cbwd_layout(a.B, a.H, a.L, a.d, a.C).floats * 4 : 0;
+    return p;
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream) {
+    switch (a.d) {
+    case 32: return launch_cbwd_kind<32>(a, stream);
+    case 64: return launch_cbwd_kind<64>(a, stream);
+    default: return launch_cbwd_kind<128>(a, stream);
+    }
+}
+
+}  // namespace lion

@@ -718,6 +718,20 @@ Plan plan_full_bwd(const BwdArgs &a) {
     return p;
 }
 
+hipError_t launch_dll(int kind, float *da_row, float *da_col, float *dll, int B, int H, int L, hipStream_t stream) {
+    BwdParams p{};
+    p.H = H;
+    p.L = L;
+    p.da_row = da_row;
+    p.da_col = da_col;
+    p.dll = dll;
+    if (kind == kMaskS)
+        hipLaunchKernelGGL(bwd_dll_s_kernel, dim3(B * H), dim3(kDllThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(bwd_dll_d_kernel, dim3(H), dim3(kDllThreads), 0, stream, p, B);
+    return hipGetLastError();
+}
+
 hipError_t launch_full_bwd(const BwdArgs &a, hipStream_t stream) {
     switch (a.d) {
     case 32: return dispatch_kind<32>(a, stream);

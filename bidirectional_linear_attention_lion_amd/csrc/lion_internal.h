@@ -44,6 +44,7 @@ struct BwdArgs {
     void *dq, *dk, *dv;         // [B, H, L, d]
     bool g_bf16;                // element type of dq, dk, dv
     float *dll;                 // NULL (LIT), [H] (D), [B, H, L] (S)
+    int C;                      // chunk size (chunk form's backward only)
     void *workspace;
     size_t workspace_bytes;
 };
@@ -63,6 +64,7 @@ struct SelArgs {
 Plan plan_full(const AttnArgs &a);
 Plan plan_selectivity(const SelArgs &a);
 Plan plan_full_bwd(const BwdArgs &a);
+Plan plan_chunk_bwd(const BwdArgs &a);
 Plan plan_chunk(const AttnArgs &a);
 Plan plan_birnn(const AttnArgs &a);
 
@@ -70,6 +72,10 @@ Plan plan_birnn(const AttnArgs &a);
 // Callers check the form's plan first.
 hipError_t launch_full(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_full_bwd(const BwdArgs &a, hipStream_t stream);
+hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream);
+// dlog(lambda) from the two halves of dA ([B, H, L] each): LION-S a reverse prefix sum per (batch,
+// head), LION-D sum_t t dA_t per head over the batch.  kind is 1 (D) or 2 (S).
+hipError_t launch_dll(int kind, float *da_row, float *da_col, float *dll, int B, int H, int L, hipStream_t stream);
 hipError_t launch_selectivity(const SelArgs &a, hipStream_t stream);
 hipError_t launch_chunk(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_birnn(const AttnArgs &a, hipStream_t stream);

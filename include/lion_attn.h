@@ -90,7 +90,8 @@ enum lion_mask_kind { LION_MASK_LIT = 0, LION_MASK_D = 1, LION_MASK_S = 2 };
  * single-directional generation: reply item 5, "Is this method limited to bidirectional models?"). */
 enum { LION_CAUSAL = 4 };
 enum lion_dtype { LION_DTYPE_F32 = 0, LION_DTYPE_BF16 = 1 };
-enum lion_form { LION_FORM_FULL = 0, LION_FORM_CHUNK = 1, LION_FORM_BIRNN = 2, LION_FORM_FULL_BWD = 3 };
+enum lion_form { LION_FORM_FULL = 0, LION_FORM_CHUNK = 1, LION_FORM_BIRNN = 2, LION_FORM_FULL_BWD = 3,
+                 LION_FORM_CHUNK_BWD = 4 };
 enum lion_status {
     LION_OK = 0,
     LION_ERR_INVALID = -1,
@@ -163,6 +164,22 @@ LION_API int lion_attn_full_bwd(const void *q, const void *k, const void *v, con
                                 const void *dy, void *dq, void *dk, void *dv, int grad_dtype, float *dlog_lambda,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* Backward pass computed the chunkwise way: the same gradients as lion_attn_full_bwd (same formulas),
+ * with pairs inside a chunk of C tokens formed directly and the rest of the sequence entering through
+ * d x (d+1) states per chunk boundary (the keys' states of the chunkwise forward, and the same
+ * construction over phi(q) and [dy / den, -delta]), so the work grows as L C d + L d^2 rather than
+ * L^2 d.  Sources: as for lion_attn_full_bwd, and the chunkwise form of lion_attn_chunk (reply
+ * "4: Practicality of Recurrent Inference"; blog "LION Part IV - Results", "LION Chunk").
+ *   C          16, 32 or 64 (at most 32 when d = 128); other values are LION_ERR_UNSUPPORTED.
+ *   every other argument as for lion_attn_full_bwd; y and den may come from any forward form.
+ *   workspace  >= lion_attn_workspace_bytes(LION_FORM_CHUNK_BWD, ..., C, ...) bytes: four fp32
+ *              d x (d+1) states per chunk and (batch, head), plus 8 B H L; contents on entry do not matter.
+ * Errors as for the forward entry points. */
+LION_API int lion_attn_chunk_bwd(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind,
+                                 int C, int B, int H, int L, int d, int dtype, const void *y, const float *den,
+                                 const void *dy, void *dq, void *dk, void *dv, int grad_dtype, float *dlog_lambda,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
 /* LION-S selectivity prologue: the per-token decays from the layer input, as log(lambda) for the
  * attention entry points, and the key-path input scale of zero-order-hold discretisation.  Sources:
  * lambda_i input-dependent, the scalar version of Mamba-2's state matrix (reply "1. Some
@@ -180,7 +197,8 @@ LION_API int lion_attn_full_bwd(const void *q, const void *k, const void *v, con
 LION_API int lion_selectivity(const void *x, const void *w, const float *bias, int B, int L, int H, int Dm,
                               float *log_lambda, float *key_scale, const void *k, void *k_out, int d, void *stream);
 
-/* Workspace bytes `form` needs for these sizes (C is ignored except for LION_FORM_CHUNK).
+/* Workspace bytes `form` needs for these sizes (C is ignored except for LION_FORM_CHUNK and
+ * LION_FORM_CHUNK_BWD).
  * Returns 0 when no workspace is needed, and (size_t)-1 for arguments the form rejects. */
 LION_API size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, int dtype);
 

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     lib = lion.library()
     names = header_symbols()
     assert set(names) == {"lion_attn_full", "lion_attn_full2", "lion_attn_chunk", "lion_attn_birnn",
-                          "lion_attn_full_bwd", "lion_selectivity", "lion_attn_workspace_bytes",
+                          "lion_attn_full_bwd", "lion_attn_chunk_bwd", "lion_selectivity", "lion_attn_workspace_bytes",
                           "lion_status_str", "lion_attn_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -162,6 +162,38 @@ def test_bwd_unsupported_and_workspace():
     assert lion.lion_attn_workspace_bytes(lion.FORM_FULL_BWD, 2, 3, 17, 64, 0, 0) == SIZE_MAX
     assert bwd(ws=None, wsb=need) == WORKSPACE
     assert bwd(ws=P, wsb=need - 1) == WORKSPACE
+
+
+def cbwd(C=64, ws=P, wsb=1 << 30, **kw):
+    a = dict(q=P, k=P, v=P, ll=None, kind=0, B=2, H=3, L=17, d=64, dt=1, y=P, den=P, dy=P, dq=P, dk=P, dv=P, gdt=0,
+             dll=None)
+    a.update(kw)
+    return lion.library().lion_attn_chunk_bwd(a["q"], a["k"], a["v"], a["ll"], a["kind"], C, a["B"], a["H"], a["L"],
+                                              a["d"], a["dt"], a["y"], a["den"], a["dy"], a["dq"], a["dk"], a["dv"],
+                                              a["gdt"], a["dll"], ws, wsb, None)
+
+
+@pytest.mark.parametrize("name,kw", BWD_INVALID, ids=[c[0] for c in BWD_INVALID])
+def test_chunk_bwd_invalid_arguments(name, kw):
+    assert cbwd(**kw) == INVALID
+
+
+def test_chunk_bwd_unsupported_and_workspace():
+    assert cbwd(dt=0) == UNSUPPORTED                 # fp32 inputs
+    assert cbwd(d=16) == UNSUPPORTED
+    for C in (8, 128, 256, 0):
+        assert cbwd(C=C) == UNSUPPORTED
+    assert cbwd(C=64, d=128) == UNSUPPORTED          # LDS: at most 32 tokens per chunk at d = 128
+    assert lion.lion_attn_workspace_bytes(lion.FORM_CHUNK_BWD, 2, 3, 17, 128, 64, 1) == SIZE_MAX
+    assert lion.lion_attn_workspace_bytes(lion.FORM_CHUNK_BWD, 2, 3, 17, 64, 64, 0) == SIZE_MAX
+    # four d x (d+1) fp32 states per chunk and (batch, head), the chunks' decay totals, two dA halves
+    B, H, L, d, C = 2, 3, 150, 64, 32
+    nch = (L + C - 1) // C
+    want = 4 * (4 * B * H * nch * d * (d + 1) + ((B * H * nch + 3) // 4) * 4 + 2 * ((B * H * L + 3) // 4) * 4)
+    need = lion.lion_attn_workspace_bytes(lion.FORM_CHUNK_BWD, B, H, L, d, C, 1)
+    assert need == want
+    assert cbwd(C=C, B=B, H=H, L=L, ws=None, wsb=need) == WORKSPACE
+    assert cbwd(C=C, B=B, H=H, L=L, ws=P, wsb=need - 1) == WORKSPACE
 
 
 def full2(order=P, **kw):

@@ -44,7 +44,8 @@ def _dev(bits):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def run_case(B, H, L, d, kind, causal=False, positive=True, seed=0, eps=1e-6, tag=""):
+def run_case(B, H, L, d, kind, causal=False, positive=True, seed=0, eps=1e-6, tag="", C=None):
+    """One case through the C ABI against the oracle; C given: the chunkwise backward with chunks of C."""
     import torch
     import bidirectional_linear_attention_lion_amd as lion
     rng = np.random.default_rng(seed)
@@ -59,7 +60,10 @@ def run_case(B, H, L, d, kind, causal=False, positive=True, seed=0, eps=1e-6, ta
     qd, kd, vd, gd = _dev(qb), _dev(kb), _dev(vb), _dev(gb)
     den = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
     y = lion.lion_attn_full(qd, kd, vd, ll, mk, eps, den_out=den)
-    dq, dk, dv, dll = lion.lion_attn_full_bwd(qd, kd, vd, ll, mk, y, den, gd, grad_dtype=torch.float32)
+    if C is None:
+        dq, dk, dv, dll = lion.lion_attn_full_bwd(qd, kd, vd, ll, mk, y, den, gd, grad_dtype=torch.float32)
+    else:
+        dq, dk, dv, dll = lion.lion_attn_chunk_bwd(qd, kd, vd, ll, mk, C, y, den, gd, grad_dtype=torch.float32)
     torch.cuda.synchronize()
     got = {"dq": dq, "dk": dk, "dv": dv, "dll": dll}
     res = oracle.full_bwd(q, k, v, None if ll32 is None else ll32.astype(np.float64),
@@ -79,7 +83,8 @@ def run_case(B, H, L, d, kind, causal=False, positive=True, seed=0, eps=1e-6, ta
         # a zero bound (an exactly zero gradient, e.g. dlog(lambda) at L = 1) admits only a zero error
         ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
         gates[name] = float(np.max(ratio))
-    report(f"[bwd] B{B} H{H} L{L} d{d} kind={lin.KIND_NAME[kind]}{' causal' if causal else ''} "
+    form = "bwd" if C is None else f"chunk_bwd C{C}"
+    report(f"[{form}] B{B} H{H} L{L} d{d} kind={lin.KIND_NAME[kind]}{' causal' if causal else ''} "
            f"{'positive' if positive else 'signed'} {tag}: literal "
            + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + " | gate "
            + " ".join(f"{n}={e:.3f}" for n, e in gates.items()))
