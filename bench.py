@@ -36,7 +36,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
 VALU_FP32_PEAK_TFLOPS = 157.3   # fp32 vector
 CSRC = os.path.join(ROOT, "bidirectional_linear_attention_lion_amd", "csrc")
 KERNEL_FILES = {"full": "lion_full.hip", "chunk": "lion_chunk.hip", "birnn": "lion_birnn.hip",
-                "full_bwd": "lion_full_bwd.hip", "selectivity": "lion_selectivity.hip", "full2": "lion_full.hip"}
+                "full_bwd": "lion_full_bwd.hip", "chunk_bwd": "lion_chunk_bwd.hip", "selectivity": "lion_selectivity.hip",
+                "full2": "lion_full.hip"}
 SEL_WIDTH = 1024   # layer-input width of the selectivity prologue (the BERT-Large-shaped recipe)
 
 
@@ -48,7 +49,8 @@ def parse_args():
     ap.add_argument("--workload", default="vit_tiny_lit")
     ap.add_argument("--forms", default=None,
                     help="comma-separated forms (default: the workload's); full_bwd times the full form's backward "
-                         "pass (bf16 gradients; y, den and a random dy prepared beforehand); selectivity times "
+                         "pass (bf16 gradients; y, den and a random dy prepared beforehand), chunk_bwd the same "
+                         "gradients computed chunkwise (chunks of --chunk tokens, default 32, at most 64); selectivity times "
                          "the LION-S prologue (log lambda from a [B, L, 1024] layer input, keys scaled); full2 the full "
                          "form with the masks of the raster and the column-major patch order averaged (image "
                          "workloads: L = 1 + n^2)")
@@ -145,6 +147,17 @@ def algorithmic(form: str, wl, C: int, causal: bool = False):
         pairs = L * (L + 1) / 2 if causal else L * L
         # S, dY V^T, dV, dphi(Q), dphi(K): five L x L x d products; mask, dp, dS and dA per pair
         return nbytes, bh * (10 * pairs * d + 8 * pairs)
+    if form == "chunk_bwd":
+        nbytes = 8 * B * H * L * d * esz + 4 * B * H * L
+        if wl.kind == 2:
+            nbytes += 4 * B * H * L
+        elif wl.kind == 1:
+            nbytes += 4 * H
+        cpairs = L * (C + 1) / 2 if causal else L * C
+        # the five products inside chunks; per token, the chunk's states summed (four d x (d+1), two
+        # when causal) and applied (dphi(q), dphi(k) and dv from them)
+        per_tok = (10 if causal else 20) * d * d
+        return nbytes, bh * (10 * cpairs * d + 8 * cpairs + L * per_tok)
     if form == "full2":
         return nbytes, bh * (4 * L * L * d + 4 * L * L)   # as the full form, two mask terms per score
     if form == "full":
@@ -163,7 +176,7 @@ def bound_of(form: str, wl, C: int, causal: bool = False) -> str:
     """The roof that binds a form on a workload: the RNN form is fp32 vector-ALU work; the full and
     chunk forms are matrix-core work, bound by HBM below the bf16 ridge (peak flops / peak bytes) and
     by the matrix cores above it."""
-    if form == "birnn":
+    if form in ("birnn", "chunk_bwd"):
         return "alu"
     nbytes, flops = algorithmic(form, wl, C, causal)
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -233,6 +246,10 @@ def main():
 
     wl = lin.WORKLOADS[args.workload]
     C = args.chunk or wl.chunks[0]
+    CB = min(args.chunk, 64) if args.chunk else 32   # the chunkwise backward's chunk size
+
+    def form_c(f):
+        return CB if f == "chunk_bwd" else C
     causal = args.causal
     kind = wl.kind | (lion.CAUSAL if causal else 0)
     forms = list(wl.forms) if args.forms is None else [f for f in args.forms.split(",") if f]
@@ -256,9 +273,9 @@ def main():
     del q0, k0, v0
     ws = {}
     bwd_sets = []
-    if "full_bwd" in forms:
+    if "full_bwd" in forms or "chunk_bwd" in forms:
         if wl.dtype != "bf16":
-            raise SystemExit("bench.py: full_bwd needs bf16 inputs")
+            raise SystemExit("bench.py: full_bwd and chunk_bwd need bf16 inputs")
         gen = torch.Generator(device=dev)
         gen.manual_seed(wl.seed)
         for (q, k, v, _) in sets:
@@ -286,10 +303,12 @@ def main():
         ws_ = (torch.randn((wl.H, SEL_WIDTH), generator=gen, device=dev) / SEL_WIDTH ** 0.5).to(torch.bfloat16)
         bs = torch.full((wl.H,), 3.0, dtype=torch.float32, device=dev)
         sel = (xs, ws_, bs)
-    for f, form_id in (("chunk", lion.FORM_CHUNK), ("birnn", lion.FORM_BIRNN), ("full_bwd", lion.FORM_FULL_BWD)):
+    for f, form_id in (("chunk", lion.FORM_CHUNK), ("birnn", lion.FORM_BIRNN), ("full_bwd", lion.FORM_FULL_BWD),
+                       ("chunk_bwd", lion.FORM_CHUNK_BWD)):
         if f not in forms:
             continue
-        nb = lion.lion_attn_workspace_bytes(form_id, wl.B, wl.H, wl.L, wl.d, C, 1 if wl.dtype == "bf16" else 0)
+        cf = CB if f == "chunk_bwd" else C
+        nb = lion.lion_attn_workspace_bytes(form_id, wl.B, wl.H, wl.L, wl.d, cf, 1 if wl.dtype == "bf16" else 0)
         ws[f] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
 
     def call(form, s):
@@ -304,6 +323,10 @@ def main():
             yb, den, dy, (dq, dk, dv), dll = bwd_sets[s % nsets]
             lion.lion_attn_full_bwd(q, k, v, ll, kind, yb, den, dy, dq=dq, dk=dk, dv=dv, dlog_lambda=dll,
                                     workspace=ws["full_bwd"], stream=stream)
+        elif form == "chunk_bwd":
+            yb, den, dy, (dq, dk, dv), dll = bwd_sets[s % nsets]
+            lion.lion_attn_chunk_bwd(q, k, v, ll, kind, CB, yb, den, dy, dq=dq, dk=dk, dv=dv,
+                                     dlog_lambda=dll, workspace=ws["chunk_bwd"], stream=stream)
         elif form == "chunk":
             lion.lion_attn_chunk(q, k, v, ll, kind, C, wl.eps, y=y, workspace=ws["chunk"], stream=stream)
         else:
@@ -351,21 +374,23 @@ def main():
     per_form = {}
     for f in forms:
         avg = ev[f][0].elapsed_time(ev[f][1]) / args.steps
-        nbytes, flops = algorithmic(f, wl, C, causal)
+        nbytes, flops = algorithmic(f, wl, form_c(f), causal)
         per_form[f] = {
             "tokens_per_s": tokens / (avg * 1e-3),
             "ms_avg": avg,
             "alg_GBps": nbytes / (avg * 1e-3) / 1e9,
             "alg_TFLOPs": flops / (avg * 1e-3) / 1e12,
-            "bound": bound_of(f, wl, C, causal),
+            "bound": bound_of(f, wl, form_c(f), causal),
         }
         if f == "chunk":
             per_form[f]["C"] = C
+        elif f == "chunk_bwd":
+            per_form[f]["C"] = CB
         per_form[f]["launch_us"] = spread[f]
     dom = max(forms, key=lambda f: per_form[f]["ms_avg"])
-    nbytes, flops = algorithmic(dom, wl, C, causal)
+    nbytes, flops = algorithmic(dom, wl, form_c(dom), causal)
     avg_s = per_form[dom]["ms_avg"] * 1e-3
-    dom_bound = bound_of(dom, wl, C, causal)
+    dom_bound = bound_of(dom, wl, form_c(dom), causal)
     peak, unit = peak_of(dom_bound)
     achieved = nbytes / avg_s / 1e9 if dom_bound == "hbm" else flops / avg_s / 1e12
     traffic = read_traffic(dom, wl.name, causal)

@@ -23,7 +23,8 @@
 // dlog(lambda) then follows from dA as in the full form's backward (a reverse prefix sum for LION-S,
 // sum_t t dA_t for LION-D).
 //
-// Three launches plus the dlog(lambda) one:
+// Three launches plus the dlog(lambda) one (states are stored with rows padded to 16 bytes, so every
+// read of them is a 16-byte one):
 //   local: one workgroup per (batch, head, chunk) sums the chunk's four states (keys and queries, each
 //          weighted towards the chunk's right end and towards its left end) into the workspace;
 //   scan:  per (batch, head) and state element, replaces each chunk's local state by the state entering
@@ -48,7 +49,7 @@ struct CbParams {
     int H, L, nch, causal;
     void *dq, *dk, *dv;
     int g_bf16;
-    float *states;           // [B H][nch][4][D][D + 1]: key-left, query-left, key-right, query-right
+    float *states;           // [B H][nch][4][D][D + 4] (D + 1 used): key-left, query-left, key-right, query-right
     float *tot;              // [B H][nch]: the chunk's sum of log(lambda), times log2(e)
     float *da_row, *da_col;  // [B H L]
 };
@@ -59,16 +60,17 @@ struct CbCfg {
     static constexpr int CP = CT + 4;         // LDS row stride of the pair matrices
     static constexpr int T = CT / 16;         // token rows per thread (rows grp, grp + 16, ...)
     static constexpr int TA = D / 16;         // contiguous channels per thread
-    static constexpr int DS = D + 1;          // row stride of a state
+    static constexpr int DS = D + 4;          // row stride of a state: D + 1 columns, padded to 16 bytes
     static constexpr int DD = D * DS;         // floats per state
     static constexpr int TOK = 4 * CT * DP + 2 * CT + 4;   // phi(q), phi(k), v, dy/den; -delta; cum; tot
     static constexpr int MAT = 3 * CT * CP;
     static constexpr int BUF = MAT > DD ? MAT : DD;
     static constexpr size_t LDS = (size_t)(TOK + BUF) * 4;
+    static constexpr size_t LDS_LOCAL = (size_t)TOK * 4;   // the local-state kernel stages tokens only
 };
 
 size_t cbwd_lds(int d, int C) {
-    const int DP = d + 4, CP = C + 4, DD = d * (d + 1);
+    const int DP = d + 4, CP = C + 4, DD = d * (d + 4);
     const int tok = 4 * C * DP + 2 * C + 4, mat = 3 * C * CP;
     return (size_t)(tok + (mat > DD ? mat : DD)) * 4;
 }
@@ -234,6 +236,11 @@ __global__ void __launch_bounds__(kThreads) cbwd_local_kernel(CbParams p) {
                 if (keep_r) dr[a * CF::DS + tj * TA + e2] = bw[e][e2];
             }
             if (tj == 0) {
+#pragma unroll
+                for (int pad = 1; pad < 4; ++pad) {   // keep the padding finite for the scan
+                    if (keep_l) dl[a * CF::DS + D + pad] = 0.f;
+                    if (keep_r) dr[a * CF::DS + D + pad] = 0.f;
+                }
                 if (keep_l) dl[a * CF::DS + D] = fz[e];
                 if (keep_r) dr[a * CF::DS + D] = bz[e];
             }
@@ -480,10 +487,10 @@ __global__ void __launch_bounds__(kThreads) cbwd_main_kernel(CbParams p) {
             for (int r = 0; r < T; ++r) xv[r] = *reinterpret_cast<const f32x4 *>(Xs + (ti + 16 * r) * DP + b);
 #pragma unroll
             for (int e = 0; e < TA; ++e) {
-                const float *srow = buf + (a0 + e) * DS + b;
-                const float s0 = srow[0], s1 = srow[1], s2 = srow[2], s3 = srow[3];
+                const f32x4 sv = *reinterpret_cast<const f32x4 *>(buf + (a0 + e) * DS + b);
 #pragma unroll
-                for (int r = 0; r < T; ++r) o[r][e] += s0 * xv[r][0] + s1 * xv[r][1] + s2 * xv[r][2] + s3 * xv[r][3];
+                for (int r = 0; r < T; ++r)
+                    o[r][e] += sv[0] * xv[r][0] + sv[1] * xv[r][1] + sv[2] * xv[r][2] + sv[3] * xv[r][3];
             }
         }
         // column D: times -delta (keys' states) or 1 (queries' states)
@@ -523,8 +530,7 @@ __global__ void __launch_bounds__(kThreads) cbwd_main_kernel(CbParams p) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     float srow[TA];
-#pragma unroll
-                    for (int e = 0; e < TA; ++e) srow[e] = buf[(a + u) * DS + a0 + e];
+                    lds_load(srow, buf + (a + u) * DS + a0);
 #pragma unroll
                     for (int r = 0; r < T; ++r)
 #pragma unroll
@@ -582,7 +588,7 @@ struct CbLayout {
 
 CbLayout cbwd_layout(int B, int H, int L, int d, int C) {
     const size_t bh = (size_t)B * H, nch = (size_t)((L + C - 1) / C);
-    const size_t dd = (size_t)d * (d + 1);
+    const size_t dd = (size_t)d * (d + 4);
     CbLayout w;
     w.states = 0;
     w.tot = 4 * bh * nch * dd;
@@ -619,8 +625,8 @@ hipError_t launch_cbwd_t(const BwdArgs &a, hipStream_t stream) {
     p.da_col = p.da_row + ((n + 3) / 4) * 4;
     const int nblk = a.B * a.H * p.nch;
     if (p.nch > 1) {
-        allow_lds(&cbwd_local_kernel<D, KIND, CT>, CF::LDS);
-        hipLaunchKernelGGL((cbwd_local_kernel<D, KIND, CT>), dim3(nblk), dim3(kThreads), CF::LDS, stream, p);
+        allow_lds(&cbwd_local_kernel<D, KIND, CT>, CF::LDS_LOCAL);
+        hipLaunchKernelGGL((cbwd_local_kernel<D, KIND, CT>), dim3(nblk), dim3(kThreads), CF::LDS_LOCAL, stream, p);
         const int nbpb = (4 * CF::DD + kThreads - 1) / kThreads;
         hipLaunchKernelGGL(cbwd_scan_kernel, dim3(a.B * a.H * nbpb), dim3(kThreads), 0, stream, p, CF::DD, nbpb);
     }

@@ -173,7 +173,8 @@ LION_API int lion_attn_full_bwd(const void *q, const void *k, const void *v, con
  *   C          16, 32 or 64 (at most 32 when d = 128); other values are LION_ERR_UNSUPPORTED.
  *   every other argument as for lion_attn_full_bwd; y and den may come from any forward form.
  *   workspace  >= lion_attn_workspace_bytes(LION_FORM_CHUNK_BWD, ..., C, ...) bytes: four fp32
- *              d x (d+1) states per chunk and (batch, head), plus 8 B H L; contents on entry do not matter.
+ *              d x (d+1) states (rows padded to d + 4) per chunk and (batch, head), plus 8 B H L;
+ *              contents on entry do not matter.
  * Errors as for the forward entry points. */
 LION_API int lion_attn_chunk_bwd(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind,
                                  int C, int B, int H, int L, int d, int dtype, const void *y, const float *den,

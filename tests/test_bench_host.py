@@ -39,6 +39,15 @@ def test_algorithmic_chunk_and_rnn():
     assert bench.algorithmic("birnn", lit, C)[1] == 64 * 3 * 197 * 2 * (4 * d * d + 3 * d)
 
 
+def test_algorithmic_chunk_bwd():
+    wl = lin.WORKLOADS["hires_d"]                 # B8 H12 L4097 d64, LION-D
+    bh, L, d = 8 * 12, 4097, 64
+    nbytes, flops = bench.algorithmic("chunk_bwd", wl, 32)
+    assert nbytes == 8 * bh * L * d * 2 + 4 * bh * L + 4 * 12
+    assert flops == bh * (10 * L * 32 * d + 8 * L * 32 + L * 20 * d * d)
+    assert bench.bound_of("chunk_bwd", wl, 64) == "alu"
+
+
 def test_algorithmic_causal_counts_the_lower_triangle():
     wl = lin.WORKLOADS["hires_d"]
     bh, L, d = 8 * 12, 4097, 64
