@@ -42,6 +42,7 @@ namespace lion {
 namespace {
 
 constexpr int kThreads = 256;   // a 16 x 16 grid of threads
+constexpr int kWalkMinPairs = 256;   // (batch, head) pairs from which one walk per pair fills the chip
 
 struct CbParams {
     const __bf16 *q, *k, *v, *y, *dy;
@@ -63,16 +64,16 @@ struct CbCfg {
     static constexpr int DS = D + 4;          // row stride of a state: D + 1 columns, padded to 16 bytes
     static constexpr int DD = D * DS;         // floats per state
     static constexpr int TOK = 4 * CT * DP + 2 * CT + 4;   // phi(q), phi(k), v, dy/den; -delta; cum; tot
-    static constexpr int MAT = 3 * CT * CP;
+    static constexpr int MAT = 2 * CT * CP;
     static constexpr int BUF = MAT > DD ? MAT : DD;
-    static constexpr size_t LDS = (size_t)(TOK + BUF) * 4;
+    static constexpr size_t LDS = (size_t)(TOK + BUF + 2 * CT) * 4;
     static constexpr size_t LDS_LOCAL = (size_t)TOK * 4;   // the local-state kernel stages tokens only
 };
 
 size_t cbwd_lds(int d, int C) {
     const int DP = d + 4, CP = C + 4, DD = d * (d + 4);
-    const int tok = 4 * C * DP + 2 * C + 4, mat = 3 * C * CP;
-    return (size_t)(tok + (mat > DD ? mat : DD)) * 4;
+    const int tok = 4 * C * DP + 2 * C + 4, mat = 2 * C * CP;
+    return (size_t)(tok + (mat > DD ? mat : DD) + 2 * C) * 4;
 }
 
 template <int N>
@@ -249,6 +250,97 @@ __global__ void __launch_bounds__(kThreads) cbwd_local_kernel(CbParams p) {
     if (tid == 0) p.tot[(size_t)bh * p.nch + c] = tot2;
 }
 
+// ================================ entering states by one sequential walk ==============================
+// One workgroup per (batch, head) walks the chunks left to right (keys' and queries' states entering from
+// the left) and then right to left (entering from the right), carrying the running states in registers:
+// each entering state is written once and no scan pass is needed.  Used when the (batch, head) pairs
+// alone fill the chip.  Thread ownership as in cbwd_local_kernel.
+template <int D, int KIND, int CT>
+__global__ void __launch_bounds__(kThreads) cbwd_walk_kernel(CbParams p) {
+    using CF = CbCfg<D, CT>;
+    constexpr int TA = CF::TA;
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    const int bh = blockIdx.x;
+    const float *Qs = sm, *Ks = Qs + CT * CF::DP, *Vs = Ks + CT * CF::DP, *Us = Vs + CT * CF::DP;
+    const float *nd = Us + CT * CF::DP, *cum = nd + CT;
+    const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
+#pragma unroll 1
+    for (int dir = 0; dir < 2; ++dir) {   // 0: from the left, 1: from the right
+        // causal: only the keys' state from the left and the queries' state from the right are used
+        const bool want_k = !p.causal || dir == 0, want_q = !p.causal || dir == 1;
+        float sk[TA][TA], sq[TA][TA], zk[TA], zq[TA];
+#pragma unroll
+        for (int e = 0; e < TA; ++e) {
+            zk[e] = zq[e] = 0.f;
+#pragma unroll
+            for (int e2 = 0; e2 < TA; ++e2) sk[e][e2] = sq[e][e2] = 0.f;
+        }
+#pragma unroll 1
+        for (int step = 0; step < p.nch; ++step) {
+            const int c = dir == 0 ? step : p.nch - 1 - step;
+            const int n = min(CT, p.L - c * CT);
+            stage_tokens<D, KIND, CT>(p, sm, bh, c, n);
+            __syncthreads();
+            // the state entering chunk c is the running sum so far
+            float *out = p.states + ((size_t)bh * p.nch + c) * 4 * CF::DD;
+            float *ok_ = out + (2 * dir) * CF::DD, *oq = out + (2 * dir + 1) * CF::DD;
+#pragma unroll
+            for (int e = 0; e < TA; ++e) {
+                const int a = ti * TA + e;
+#pragma unroll
+                for (int e2 = 0; e2 < TA; ++e2) {
+                    if (want_k) ok_[a * CF::DS + tj * TA + e2] = sk[e][e2];
+                    if (want_q) oq[a * CF::DS + tj * TA + e2] = sq[e][e2];
+                }
+                if (tj == 0) {
+#pragma unroll
+                    for (int pad = 1; pad < 4; ++pad) {
+                        if (want_k) ok_[a * CF::DS + D + pad] = 0.f;
+                        if (want_q) oq[a * CF::DS + D + pad] = 0.f;
+                    }
+                    if (want_k) ok_[a * CF::DS + D] = zk[e];
+                    if (want_q) oq[a * CF::DS + D] = zq[e];
+                }
+            }
+            // then decay it across the chunk and add the chunk's own tokens, weighted towards the
+            // chunk's far end (right end from the left, left end from the right)
+            const float tot2 = cum[CT];
+            const float dec = KIND == kMaskLit ? 1.f : fast_exp2(tot2);
+#pragma unroll
+            for (int e = 0; e < TA; ++e) {
+                zk[e] *= dec;
+                zq[e] *= dec;
+#pragma unroll
+                for (int e2 = 0; e2 < TA; ++e2) {
+                    sk[e][e2] *= dec;
+                    sq[e][e2] *= dec;
+                }
+            }
+            for (int j = 0; j < n; ++j) {
+                const float wgt = KIND == kMaskLit ? 1.f : fast_exp2(dir == 0 ? tot2 - cum[j] : cum[j]);
+                float xk[TA], xq[TA], yv[TA], yu[TA];
+                lds_load(xk, Ks + j * CF::DP + ti * TA);
+                lds_load(xq, Qs + j * CF::DP + ti * TA);
+                lds_load(yv, Vs + j * CF::DP + tj * TA);
+                lds_load(yu, Us + j * CF::DP + tj * TA);
+                const float ndj = nd[j];
+#pragma unroll
+                for (int e = 0; e < TA; ++e) {
+                    const float kx = wgt * xk[e], qx = wgt * xq[e];
+                    zk[e] += kx;
+                    zq[e] += qx * ndj;
+#pragma unroll
+                    for (int e2 = 0; e2 < TA; ++e2) {
+                        sk[e][e2] += kx * yv[e2];
+                        sq[e][e2] += qx * yu[e2];
+                    }
+                }
+            }
+            __syncthreads();   // before the next chunk's tokens overwrite these
+        }
+    }
+}
+
 // ================================ scan over chunks ====================================================
 // One thread per (batch, head, state element): the state entering chunk c from the left is
 // S_c = exp(tot_{c-1}) S_{c-1} + local_{c-1} (S_0 = 0); from the right, the mirror image.
@@ -353,104 +445,79 @@ __device__ __forceinline__ void store_row(void *base, bool bf16, size_t off, con
     }
 }
 
+// The pair and state products run on the matrix cores in fp32 (v_mfma_f32_16x16x4f32: lane 16 g + r
+// supplies A[r][k0 + g] and B[k0 + g][r] and receives D[4 g + e][r]); every operand is read from the
+// fp32 LDS tiles, so the inputs keep their fp32 values.  Wave w takes 16 x 16 tiles w, w + 4, ...
 template <int D, int KIND, int CT>
 __global__ void __launch_bounds__(kThreads) cbwd_main_kernel(CbParams p) {
     using CF = CbCfg<D, CT>;
     constexpr int T = CF::T, TA = CF::TA, DP = CF::DP, CP = CF::CP, DS = CF::DS;
+    constexpr int NT = CT / 16, NA = D / 16;
+    constexpr int NOUT = (NT * NA + 3) / 4;   // output tiles per wave
     extern __shared__ __attribute__((aligned(16))) float sm[];
     const int bh = blockIdx.x / p.nch, c = blockIdx.x % p.nch;
     const int n = min(CT, p.L - c * CT);
-    stage_tokens<D, KIND, CT>(p, sm, bh, c, n);
-    __syncthreads();
-    const float *Qs = sm, *Ks = Qs + CT * DP, *Vs = Ks + CT * DP, *Us = Vs + CT * DP;
+    float *Qs = sm, *Ks = Qs + CT * DP, *Vs = Ks + CT * DP, *Us = Vs + CT * DP;
     const float *nd = Us + CT * DP, *cum = nd + CT;
     float *buf = sm + CF::TOK;
-    float *D1 = buf, *D2 = D1 + CT * CP, *SW = D2 + CT * CP;
+    float *D1 = buf, *D2 = D1 + CT * CP;
+    float *dar = sm + CF::TOK + CF::BUF, *dac = dar + CT;   // dA halves of the chunk's tokens
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+    for (int t = tid; t < 2 * CT; t += kThreads) dar[t] = 0.f;
+    stage_tokens<D, KIND, CT>(p, sm, bh, c, n);
+    __syncthreads();
     const float tot2 = cum[CT];
-    const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
     const bool causal = p.causal != 0;
 
-    // ---- pair matrices: D1 = M dp, D2 = M s, SW = sign(i - j) M dp s (rows ti + 16 r, columns tj + 16 r2)
-    {
-        float ax[T][T], as[T][T];
-#pragma unroll
-        for (int r = 0; r < T; ++r)
-#pragma unroll
-            for (int r2 = 0; r2 < T; ++r2) ax[r][r2] = as[r][r2] = 0.f;
-#pragma unroll 1
-        for (int a = 0; a < D; a += 4) {
-            f32x4 u[T], qq[T], vv[T], kk[T];
-#pragma unroll
-            for (int r = 0; r < T; ++r) {
-                u[r] = *reinterpret_cast<const f32x4 *>(Us + (ti + 16 * r) * DP + a);
-                qq[r] = *reinterpret_cast<const f32x4 *>(Qs + (ti + 16 * r) * DP + a);
-                vv[r] = *reinterpret_cast<const f32x4 *>(Vs + (tj + 16 * r) * DP + a);
-                kk[r] = *reinterpret_cast<const f32x4 *>(Ks + (tj + 16 * r) * DP + a);
-            }
-#pragma unroll
-            for (int r = 0; r < T; ++r)
-#pragma unroll
-                for (int r2 = 0; r2 < T; ++r2)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        ax[r][r2] += u[r][e] * vv[r2][e];
-                        as[r][r2] += qq[r][e] * kk[r2][e];
-                    }
+    // ---- pair matrices D1 = M dp and D2 = M s; the dA sums of sign(i - j) M dp s straight from them
+    for (int tile = w; tile < NT * NT; tile += 4) {
+        const int ti = tile / NT, tj = tile % NT;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f}, s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int k0 = 0; k0 < D; k0 += 4) {
+            x = mfma_f32(Us[(16 * ti + r) * DP + k0 + g], Vs[(16 * tj + r) * DP + k0 + g], x);
+            s = mfma_f32(Qs[(16 * ti + r) * DP + k0 + g], Ks[(16 * tj + r) * DP + k0 + g], s);
         }
+        const int j = 16 * tj + r;
+        float csum = 0.f;
 #pragma unroll
-        for (int r = 0; r < T; ++r)
-#pragma unroll
-            for (int r2 = 0; r2 < T; ++r2) {
-                const int i = ti + 16 * r, j = tj + 16 * r2;
-                const bool ok = i < n && j < n && !(causal && j > i);
-                float m = 0.f;
-                if (ok) m = KIND == kMaskLit ? 1.f : fast_exp2(-fabsf(cum[i] - cum[j]));
-                const float dp = ax[r][r2] + nd[i];
-                const float sgn = j < i ? 1.f : (j > i ? -1.f : 0.f);
-                D1[i * CP + j] = m * dp;
-                D2[i * CP + j] = m * as[r][r2];
-                SW[i * CP + j] = sgn * m * dp * as[r][r2];
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * ti + 4 * g + e;
+            const bool ok = i < n && j < n && !(causal && j > i);
+            float m = 0.f;
+            if (ok) m = KIND == kMaskLit ? 1.f : fast_exp2(-fabsf(cum[i] - cum[j]));
+            const float dp = x[e] + nd[i];
+            D1[i * CP + j] = m * dp;
+            D2[i * CP + j] = m * s[e];
+            if constexpr (KIND != kMaskLit) {
+                const float sw = (j < i ? 1.f : (j > i ? -1.f : 0.f)) * m * dp * s[e];
+                const float rs = group_sum<16>(sw);           // over this tile's 16 columns
+                if (r == 0) atomicAdd(&dar[i], rs);
+                csum -= sw;
             }
+        }
+        if constexpr (KIND != kMaskLit) {
+            csum += __shfl_xor(csum, 16, 64);
+            csum += __shfl_xor(csum, 32, 64);                // over this tile's 16 rows
+            if (g == 0) atomicAdd(&dac[j], csum);
+        }
     }
     __syncthreads();
 
-    // ---- intra-chunk parts: rows t = ti + 16 r, channels ta TA .. + TA - 1 (ta = tj)
-    const int ta = tj, a0 = ta * TA;
-    float gq[T][TA], gk[T][TA], gv[T][TA], dar[T], dac[T];
+    // ---- intra-chunk parts of the output tiles (rows t = 16 tt + 4 g + e, channels 16 ta + r)
+    f32x4 aq[NOUT], ak[NOUT], av[NOUT];
 #pragma unroll
-    for (int r = 0; r < T; ++r) {
-        dar[r] = dac[r] = 0.f;
-#pragma unroll
-        for (int e = 0; e < TA; ++e) gq[r][e] = gk[r][e] = gv[r][e] = 0.f;
-    }
-#pragma unroll 2
-    for (int j = 0; j < n; ++j) {
-        float kv[TA], qv[TA], uv[TA];
-        lds_load(kv, Ks + j * DP + a0);
-        lds_load(qv, Qs + j * DP + a0);
-        lds_load(uv, Us + j * DP + a0);
-#pragma unroll
-        for (int r = 0; r < T; ++r) {
-            const int t = ti + 16 * r;
-            const float d1 = D1[t * CP + j], d1t = D1[j * CP + t], d2t = D2[j * CP + t];
-#pragma unroll
-            for (int e = 0; e < TA; ++e) {
-                gq[r][e] += d1 * kv[e];
-                gk[r][e] += d1t * qv[e];
-                gv[r][e] += d2t * uv[e];
-            }
-        }
-    }
-    if constexpr (KIND != kMaskLit) {
-#pragma unroll
-        for (int r = 0; r < T; ++r) {
-            const int t = ti + 16 * r;
-#pragma unroll
-            for (int jj = 0; jj < T; ++jj) {
-                const int j = ta + 16 * jj;
-                dar[r] += SW[t * CP + j];
-                dac[r] -= SW[j * CP + t];
-            }
+    for (int u = 0; u < NOUT; ++u) {
+        aq[u] = ak[u] = av[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile = w + 4 * u;
+        if (tile >= NT * NA) break;
+        const int tt = tile / NA, ta = tile % NA;
+#pragma unroll 4
+        for (int j0 = 0; j0 < CT; j0 += 4) {
+            const int jr = j0 + g;
+            aq[u] = mfma_f32(D1[(16 * tt + r) * CP + jr], Ks[jr * DP + 16 * ta + r], aq[u]);
+            ak[u] = mfma_f32(D1[jr * CP + 16 * tt + r], Qs[jr * DP + 16 * ta + r], ak[u]);
+            av[u] = mfma_f32(D2[jr * CP + 16 * tt + r], Us[jr * DP + 16 * ta + r], av[u]);
         }
     }
     __syncthreads();   // the pair matrices' space takes the states next
@@ -467,107 +534,94 @@ __global__ void __launch_bounds__(kThreads) cbwd_main_kernel(CbParams p) {
         for (int e = tid * 4; e < CF::DD; e += kThreads * 4)
             *reinterpret_cast<f32x4 *>(buf + e) = *reinterpret_cast<const f32x4 *>(src + e);
         __syncthreads();
-        float f[T];
-#pragma unroll
-        for (int r = 0; r < T; ++r) {
-            const float ct = cum[ti + 16 * r];
-            f[r] = KIND == kMaskLit ? 1.f : fast_exp2(right ? tot2 - ct : ct);
-        }
         const float sgn = right ? -1.f : 1.f;
-        const float *Xs = keys ? Us : Vs;   // the vector the state multiplies (u for keys, w for queries)
-        float o[T][TA];
-#pragma unroll
-        for (int r = 0; r < T; ++r)
-#pragma unroll
-            for (int e = 0; e < TA; ++e) o[r][e] = 0.f;
-#pragma unroll 1
-        for (int b = 0; b < D; b += 4) {
-            f32x4 xv[T];
-#pragma unroll
-            for (int r = 0; r < T; ++r) xv[r] = *reinterpret_cast<const f32x4 *>(Xs + (ti + 16 * r) * DP + b);
-#pragma unroll
-            for (int e = 0; e < TA; ++e) {
-                const f32x4 sv = *reinterpret_cast<const f32x4 *>(buf + (a0 + e) * DS + b);
-#pragma unroll
-                for (int r = 0; r < T; ++r)
-                    o[r][e] += sv[0] * xv[r][0] + sv[1] * xv[r][1] + sv[2] * xv[r][2] + sv[3] * xv[r][3];
-            }
-        }
-        // column D: times -delta (keys' states) or 1 (queries' states)
-#pragma unroll
-        for (int r = 0; r < T; ++r) {
-            const float last = keys ? nd[ti + 16 * r] : 1.f;
-#pragma unroll
-            for (int e = 0; e < TA; ++e) o[r][e] += buf[(a0 + e) * DS + D] * last;
-        }
+        const float *Xs = keys ? Us : Vs;   // what the state multiplies: u (keys' states), w (queries')
         const float *Ps = keys ? Qs : Ks;   // the dA half dots the result with phi of the same token
 #pragma unroll
-        for (int r = 0; r < T; ++r) {
-            const int t = ti + 16 * r;
-            float pv[TA];
-            lds_load(pv, Ps + t * DP + a0);
-            float dot = 0.f;
+        for (int u = 0; u < NOUT; ++u) {
+            const int tile = w + 4 * u;
+            if (tile >= NT * NA) break;
+            const int tt = tile / NA, ta = tile % NA, a = 16 * ta + r;
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int b0 = 0; b0 < D; b0 += 4)
+                o = mfma_f32(Xs[(16 * tt + r) * DP + b0 + g], buf[a * DS + b0 + g], o);
+            const float last = buf[a * DS + D];
+            float part[4];
 #pragma unroll
-            for (int e = 0; e < TA; ++e) {
-                dot += pv[e] * o[r][e];
-                if (keys) gq[r][e] += f[r] * o[r][e];
-                else gk[r][e] += f[r] * o[r][e];
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * tt + 4 * g + e;
+                const float f = KIND == kMaskLit ? 1.f : fast_exp2(right ? tot2 - cum[t] : cum[t]);
+                const float oe = o[e] + last * (keys ? nd[t] : 1.f);
+                if (keys) aq[u][e] += f * oe;
+                else ak[u][e] += f * oe;
+                part[e] = sgn * f * Ps[t * DP + a] * oe;
             }
-            if (keys) dar[r] += sgn * f[r] * dot;
-            else dac[r] += sgn * f[r] * dot;
-        }
-        if (!keys) {   // dv: the state's first D columns, transposed, times phi(k_t)
-            float ov[T][TA];
+            if constexpr (KIND != kMaskLit) {
 #pragma unroll
-            for (int r = 0; r < T; ++r)
-#pragma unroll
-                for (int e = 0; e < TA; ++e) ov[r][e] = 0.f;
-#pragma unroll 1
-            for (int a = 0; a < D; a += 4) {
-                f32x4 kv[T];
-#pragma unroll
-                for (int r = 0; r < T; ++r) kv[r] = *reinterpret_cast<const f32x4 *>(Ks + (ti + 16 * r) * DP + a);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    float srow[TA];
-                    lds_load(srow, buf + (a + u) * DS + a0);
-#pragma unroll
-                    for (int r = 0; r < T; ++r)
-#pragma unroll
-                        for (int e = 0; e < TA; ++e) ov[r][e] += kv[r][u] * srow[e];
+                for (int e = 0; e < 4; ++e) {
+                    const float ps = group_sum<16>(part[e]);   // over this tile's 16 channels
+                    if (r == 0) atomicAdd(keys ? &dar[16 * tt + 4 * g + e] : &dac[16 * tt + 4 * g + e], ps);
                 }
             }
+            if (!keys) {   // dv: the state's first D columns, transposed, times phi(k_t)
+                f32x4 ov = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+                for (int a0 = 0; a0 < D; a0 += 4)
+                    ov = mfma_f32(Ks[(16 * tt + r) * DP + a0 + g], buf[(a0 + g) * DS + 16 * ta + r], ov);
 #pragma unroll
-            for (int r = 0; r < T; ++r)
-#pragma unroll
-                for (int e = 0; e < TA; ++e) gv[r][e] += f[r] * ov[r][e];
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * tt + 4 * g + e;
+                    const float f = KIND == kMaskLit ? 1.f : fast_exp2(right ? tot2 - cum[t] : cum[t]);
+                    av[u][e] += f * ov[e];
+                }
+            }
         }
         __syncthreads();
     }
 
-    // ---- phi's Jacobian, stores
+    // ---- the outputs into the token tiles (no longer read), then phi's Jacobian and the stores with
+    // thread (ti, ta) owning rows ti + 16 r and channels ta TA .. + TA - 1
+#pragma unroll
+    for (int u = 0; u < NOUT; ++u) {
+        const int tile = w + 4 * u;
+        if (tile >= NT * NA) break;
+        const int tt = tile / NA, ta = tile % NA;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int at = (16 * tt + 4 * g + e) * DP + 16 * ta + r;
+            Qs[at] = aq[u][e];
+            Ks[at] = ak[u][e];
+            Vs[at] = av[u][e];
+        }
+    }
+    __syncthreads();
+    const int ti = tid >> 4, ta = tid & 15, a0 = ta * TA;
     const size_t row0 = (size_t)bh * p.L + (size_t)c * CT;
     const bool gb = p.g_bf16 != 0;
 #pragma unroll
-    for (int r = 0; r < T; ++r) {
-        const int t = ti + 16 * r;
-        if (t >= n) break;   // the row's 16 threads agree; later r only grow
+    for (int rr = 0; rr < T; ++rr) {
+        const int t = ti + 16 * rr;
+        if (t >= n) break;   // the row's 16 threads agree; later rr only grow
         const size_t off = (row0 + t) * D + a0;
+        float gq[TA], gk[TA], gv[TA];
+        lds_load(gq, Qs + t * DP + a0);
+        lds_load(gk, Ks + t * DP + a0);
+        lds_load(gv, Vs + t * DP + a0);
         if constexpr (KIND != kMaskD) {
             float xq[TA], xk[TA];
             load_raw(p.q + off, xq);
             load_raw(p.k + off, xk);
-            phi_backward_row<TA, KIND>(xq, gq[r]);
-            phi_backward_row<TA, KIND>(xk, gk[r]);
+            phi_backward_row<TA, KIND>(xq, gq);
+            phi_backward_row<TA, KIND>(xk, gk);
         }
-        store_row(p.dq, gb, off, gq[r]);
-        store_row(p.dk, gb, off, gk[r]);
-        store_row(p.dv, gb, off, gv[r]);
+        store_row(p.dq, gb, off, gq);
+        store_row(p.dk, gb, off, gk);
+        store_row(p.dv, gb, off, gv);
         if constexpr (KIND != kMaskLit) {
-            const float sr = group_sum<16>(dar[r]), sc = group_sum<16>(dac[r]);
             if (ta == 0) {
-                p.da_row[row0 + t] = sr;
-                p.da_col[row0 + t] = sc;
+                p.da_row[row0 + t] = dar[t];
+                p.da_col[row0 + t] = dac[t];
             }
         }
     }
@@ -624,7 +678,10 @@ hipError_t launch_cbwd_t(const BwdArgs &a, hipStream_t stream) {
     p.da_row = ws + w.da;
     p.da_col = p.da_row + ((n + 3) / 4) * 4;
     const int nblk = a.B * a.H * p.nch;
-    if (p.nch > 1) {
+    if (p.nch > 1 && a.B * a.H >= kWalkMinPairs) {
+        allow_lds(&cbwd_walk_kernel<D, KIND, CT>, CF::LDS_LOCAL);
+        hipLaunchKernelGGL((cbwd_walk_kernel<D, KIND, CT>), dim3(a.B * a.H), dim3(kThreads), CF::LDS_LOCAL, stream, p);
+    } else if (p.nch > 1) {
         allow_lds(&cbwd_local_kernel<D, KIND, CT>, CF::LDS_LOCAL);
         hipLaunchKernelGGL((cbwd_local_kernel<D, KIND, CT>), dim3(nblk), dim3(kThreads), CF::LDS_LOCAL, stream, p);
         const int nbpb = (4 * CF::DD + kThreads - 1) / kThreads;
