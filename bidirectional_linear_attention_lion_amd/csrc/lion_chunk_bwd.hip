@@ -23,16 +23,14 @@
 // dlog(lambda) then follows from dA as in the full form's backward (a reverse prefix sum for LION-S,
 // sum_t t dA_t for LION-D).
 //
-// Three launches plus the dlog(lambda) one (states are stored with rows padded to 16 bytes, so every
-// read of them is a 16-byte one):
-//   local: one workgroup per (batch, head, chunk) sums the chunk's four states (keys and queries, each
-//          weighted towards the chunk's right end and towards its left end) into the workspace;
-//   scan:  per (batch, head) and state element, replaces each chunk's local state by the state entering
-//          it (from the left for the first two, from the right for the other two);
-//   main:  one workgroup per chunk forms the pair matrices M dp, M s and the signed w in LDS, then
-//          dphi(q), dphi(k), dv and the dA halves from them and from the four entering states, applies
-//          phi's Jacobian and stores dq, dk, dv.
-// Everything is fp32 vector arithmetic on LDS tiles.
+// Two launches plus the dlog(lambda) one (states are stored with rows padded to 16 bytes):
+//   walk:  one workgroup per (batch, head, direction, keys or queries) walks the chunks in order,
+//          writing the state entering each chunk and then adding that chunk's tokens to its running
+//          state in registers (fp32 vector arithmetic);
+//   main:  one workgroup per chunk forms the pair matrices M dp and M s in LDS (and the dA sums of
+//          sign(i - j) M dp s), then dphi(q), dphi(k), dv and the rest of the dA halves from them and
+//          from the four entering states, on the matrix cores in fp32; applies phi's Jacobian and
+//          stores dq, dk, dv.
 // Causal variant (M_ij = 0 for j > i): pairs above the diagonal drop out, and so do the keys' states
 // entering from the right and the queries' states entering from the left (a key sees later queries).
 #include "lion_device.h"
@@ -42,7 +40,6 @@ namespace lion {
 namespace {
 
 constexpr int kThreads = 256;   // a 16 x 16 grid of threads
-constexpr int kWalkMinPairs = 256;   // (batch, head) pairs from which one walk per pair fills the chip
 
 struct CbParams {
     const __bf16 *q, *k, *v, *y, *dy;
@@ -51,7 +48,6 @@ struct CbParams {
     void *dq, *dk, *dv;
     int g_bf16;
     float *states;           // [B H][nch][4][D][D + 4] (D + 1 used): key-left, query-left, key-right, query-right
-    float *tot;              // [B H][nch]: the chunk's sum of log(lambda), times log2(e)
     float *da_row, *da_col;  // [B H L]
 };
 
@@ -63,11 +59,11 @@ struct CbCfg {
     static constexpr int TA = D / 16;         // contiguous channels per thread
     static constexpr int DS = D + 4;          // row stride of a state: D + 1 columns, padded to 16 bytes
     static constexpr int DD = D * DS;         // floats per state
-    static constexpr int TOK = 4 * CT * DP + 2 * CT + 4;   // phi(q), phi(k), v, dy/den; -delta; cum; tot
+    static constexpr int TOK = 4 * CT * DP + 2 * CT + 4;   // phi(q), phi(k), v, dy/den; -delta; cum, chunk total
     static constexpr int MAT = 2 * CT * CP;
     static constexpr int BUF = MAT > DD ? MAT : DD;
     static constexpr size_t LDS = (size_t)(TOK + BUF + 2 * CT) * 4;
-    static constexpr size_t LDS_LOCAL = (size_t)TOK * 4;   // the local-state kernel stages tokens only
+    static constexpr size_t LDS_WALK = (size_t)TOK * 4;   // the walks stage tokens only
 };
 
 size_t cbwd_lds(int d, int C) {
@@ -94,8 +90,10 @@ __device__ __forceinline__ void lds_load(float (&x)[N], const float *p) {
 // Stage the chunk's tokens into LDS as fp32 rows: phi(q), phi(k), v, u = dy / den, and -delta;
 // then the chunk's prefix sums of log(lambda) (log2 units, relative to the chunk start, inclusive).
 // Rows at or past n are zero; prefix sums past n repeat the last one.
-template <int D, int KIND, int CT>
+// WHICH: 0 everything, 1 the keys' rows only (phi(k), v), 2 the queries' only (phi(q), u, -delta).
+template <int D, int KIND, int CT, int WHICH = 0>
 __device__ void stage_tokens(const CbParams &p, float *sm, int bh, int c, int n) {
+    constexpr bool LQ = WHICH != 1, LK = WHICH != 2;
     using CF = CbCfg<D, CT>;
     float *Qs = sm, *Ks = Qs + CT * CF::DP, *Vs = Ks + CT * CF::DP, *Us = Vs + CT * CF::DP;
     float *nd = Us + CT * CF::DP, *cum = nd + CT;
@@ -108,33 +106,41 @@ __device__ void stage_tokens(const CbParams &p, float *sm, int bh, int c, int n)
         const int sl = sl0 + tid;
         const int row = sl / SPR, cs = (sl % SPR) * 8;
         const bool ok = row < n;
-        float fq[8], fk[8], fv[8], fu[8];
+        float fq[8] = {}, fk[8] = {}, fv[8] = {}, fu[8] = {};
         float ssq = 0.f, ssk = 0.f, part = 0.f, dinv = 0.f;
         if (ok) {
             const size_t g = (row0 + row) * D + cs;
-            const bf16x8 q8 = __builtin_bit_cast(bf16x8, ld16(p.q + g));
-            const bf16x8 k8 = __builtin_bit_cast(bf16x8, ld16(p.k + g));
-            const bf16x8 v8 = __builtin_bit_cast(bf16x8, ld16(p.v + g));
-            const bf16x8 y8 = __builtin_bit_cast(bf16x8, ld16(p.y + g));
-            const bf16x8 d8 = __builtin_bit_cast(bf16x8, ld16(p.dy + g));
-            dinv = 1.f / p.den[row0 + row];
+            if constexpr (LQ) {
+                const bf16x8 q8 = __builtin_bit_cast(bf16x8, ld16(p.q + g));
+                const bf16x8 y8 = __builtin_bit_cast(bf16x8, ld16(p.y + g));
+                const bf16x8 d8 = __builtin_bit_cast(bf16x8, ld16(p.dy + g));
+                dinv = 1.f / p.den[row0 + row];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                fq[e] = phi_pre<KIND>((float)q8[e]);
-                fk[e] = phi_pre<KIND>((float)k8[e]);
-                fv[e] = (float)v8[e];
-                fu[e] = (float)d8[e] * dinv;
-                ssq += fq[e] * fq[e];
-                ssk += fk[e] * fk[e];
-                part += (float)d8[e] * (float)y8[e];
+                for (int e = 0; e < 8; ++e) {
+                    fq[e] = phi_pre<KIND>((float)q8[e]);
+                    fu[e] = (float)d8[e] * dinv;
+                    ssq += fq[e] * fq[e];
+                    part += (float)d8[e] * (float)y8[e];
+                }
+            }
+            if constexpr (LK) {
+                const bf16x8 k8 = __builtin_bit_cast(bf16x8, ld16(p.k + g));
+                const bf16x8 v8 = __builtin_bit_cast(bf16x8, ld16(p.v + g));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    fk[e] = phi_pre<KIND>((float)k8[e]);
+                    fv[e] = (float)v8[e];
+                    ssk += fk[e] * fk[e];
+                }
             }
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) fq[e] = fk[e] = fv[e] = fu[e] = 0.f;
         }
-        part = group_sum<SPR>(part);
+        if constexpr (LQ) part = group_sum<SPR>(part);
         if constexpr (KIND == kMaskS) {
-            const float sq = inv_norm(group_sum<SPR>(ssq)), sk = inv_norm(group_sum<SPR>(ssk));
+            const float sq = LQ ? inv_norm(group_sum<SPR>(ssq)) : 0.f;
+            const float sk = LK ? inv_norm(group_sum<SPR>(ssk)) : 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 fq[e] *= sq;
@@ -145,6 +151,7 @@ __device__ void stage_tokens(const CbParams &p, float *sm, int bh, int c, int n)
         const float *src[4] = {fq, fk, fv, fu};
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
+            if ((a == 0 || a == 3) ? !LQ : !LK) continue;
             f32x4 lo, hi;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -154,7 +161,7 @@ __device__ void stage_tokens(const CbParams &p, float *sm, int bh, int c, int n)
             *reinterpret_cast<f32x4 *>(dst[a] + row * CF::DP + cs) = lo;
             *reinterpret_cast<f32x4 *>(dst[a] + row * CF::DP + cs + 4) = hi;
         }
-        if (sl % SPR == 0) nd[row] = ok ? -part * dinv : 0.f;
+        if (LQ && sl % SPR == 0) nd[row] = ok ? -part * dinv : 0.f;
     }
     if (tid < 64) {
         const int t = tid;
@@ -178,221 +185,89 @@ __device__ void stage_tokens(const CbParams &p, float *sm, int bh, int c, int n)
     }
 }
 
-// ================================ local states =======================================================
-// Thread (ti, tj) owns state rows ti TA .. + TA - 1 and columns tj TA .. + TA - 1, plus column D of
-// its rows (written by the tj = 0 threads).
-template <int D, int KIND, int CT>
-__global__ void __launch_bounds__(kThreads) cbwd_local_kernel(CbParams p) {
+// ================================ entering states by sequential walks ================================
+// One workgroup per (batch, head, direction, keys or queries) walks the chunks -- left to right for the
+// states entering from the left, right to left for those entering from the right -- carrying its
+// running state in registers, so each entering state is written once.  Causal runs only the keys'
+// walk from the left and the queries' walk from the right.  Thread (ti, tj) of the 16 x 16 grid owns
+// state rows ti TA .. + TA - 1 and columns tj TA .. + TA - 1, plus column D of its rows (written by
+// the tj = 0 threads).  (Splitting a walk over two workgroups by rows measured slower where the
+// pairs already fill the chip: the second workgroup stages the same tokens again.)
+template <int D, int KIND, int CT, int WHICH>
+__device__ void walk(const CbParams &p, float *sm, int bh, int dir) {
     using CF = CbCfg<D, CT>;
-    extern __shared__ __attribute__((aligned(16))) float sm[];
-    const int bh = blockIdx.x / p.nch, c = blockIdx.x % p.nch;
-    const int n = min(CT, p.L - c * CT);
-    stage_tokens<D, KIND, CT>(p, sm, bh, c, n);
-    __syncthreads();
+    constexpr int TA = CF::TA, RA = TA;
+    constexpr bool KEYS = WHICH == 1;
     const float *Qs = sm, *Ks = Qs + CT * CF::DP, *Vs = Ks + CT * CF::DP, *Us = Vs + CT * CF::DP;
     const float *nd = Us + CT * CF::DP, *cum = nd + CT;
-    const float tot2 = cum[CT];
+    const float *X = KEYS ? Ks : Qs, *Y = KEYS ? Vs : Us;
     const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
-    constexpr int TA = CF::TA;
-    float *out = p.states + ((size_t)bh * p.nch + c) * 4 * CF::DD;
+    const int st = 2 * dir + (KEYS ? 0 : 1);
+    const int a0 = ti * RA;
+    float sx[RA][TA], zx[RA];
+#pragma unroll
+    for (int e = 0; e < RA; ++e) {
+        zx[e] = 0.f;
+#pragma unroll
+        for (int e2 = 0; e2 < TA; ++e2) sx[e][e2] = 0.f;
+    }
 #pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {   // 0: keys with [v, 1]; 1: queries with [dy / den, -delta]
-        const float *X = pass == 0 ? Ks : Qs, *Y = pass == 0 ? Vs : Us;
-        float fw[TA][TA], bw[TA][TA], fz[TA], bz[TA];
+    for (int step = 0; step < p.nch; ++step) {
+        const int c = dir == 0 ? step : p.nch - 1 - step;
+        const int n = min(CT, p.L - c * CT);
+        stage_tokens<D, KIND, CT, WHICH>(p, sm, bh, c, n);
+        __syncthreads();
+        // the state entering chunk c is the running sum so far
+        float *out = p.states + (((size_t)bh * p.nch + c) * 4 + st) * CF::DD;
 #pragma unroll
-        for (int e = 0; e < TA; ++e) {
-            fz[e] = bz[e] = 0.f;
+        for (int e = 0; e < RA; ++e) {
+            const int a = a0 + e;
 #pragma unroll
-            for (int e2 = 0; e2 < TA; ++e2) fw[e][e2] = bw[e][e2] = 0.f;
-        }
-        for (int j = 0; j < n; ++j) {
-            const float ef = KIND == kMaskLit ? 1.f : fast_exp2(tot2 - cum[j]);   // towards the right end
-            const float eb = KIND == kMaskLit ? 1.f : fast_exp2(cum[j]);          // towards the left end
-            const float last = pass == 0 ? 1.f : nd[j];
-            float x[TA], y[TA];
-            lds_load(x, X + j * CF::DP + ti * TA);
-            lds_load(y, Y + j * CF::DP + tj * TA);
-#pragma unroll
-            for (int e = 0; e < TA; ++e) {
-                const float xf = ef * x[e], xb = eb * x[e];
-                fz[e] += xf * last;
-                bz[e] += xb * last;
-#pragma unroll
-                for (int e2 = 0; e2 < TA; ++e2) {
-                    fw[e][e2] += xf * y[e2];
-                    bw[e][e2] += xb * y[e2];
-                }
-            }
-        }
-        float *dl = out + pass * CF::DD, *dr = out + (2 + pass) * CF::DD;
-        // causal: queries see earlier keys only, so the keys' states enter from the left and the
-        // queries' states from the right
-        const bool keep_l = !p.causal || pass == 0, keep_r = !p.causal || pass == 1;
-#pragma unroll
-        for (int e = 0; e < TA; ++e) {
-            const int a = ti * TA + e;
-#pragma unroll
-            for (int e2 = 0; e2 < TA; ++e2) {
-                if (keep_l) dl[a * CF::DS + tj * TA + e2] = fw[e][e2];
-                if (keep_r) dr[a * CF::DS + tj * TA + e2] = bw[e][e2];
-            }
+            for (int e2 = 0; e2 < TA; ++e2) out[a * CF::DS + tj * TA + e2] = sx[e][e2];
             if (tj == 0) {
 #pragma unroll
-                for (int pad = 1; pad < 4; ++pad) {   // keep the padding finite for the scan
-                    if (keep_l) dl[a * CF::DS + D + pad] = 0.f;
-                    if (keep_r) dr[a * CF::DS + D + pad] = 0.f;
-                }
-                if (keep_l) dl[a * CF::DS + D] = fz[e];
-                if (keep_r) dr[a * CF::DS + D] = bz[e];
+                for (int pad = 1; pad < 4; ++pad) out[a * CF::DS + D + pad] = 0.f;
+                out[a * CF::DS + D] = zx[e];
             }
         }
+        // then decay it across the chunk and add the chunk's own tokens, weighted towards the chunk's
+        // far end (its right end walking from the left, its left end walking from the right)
+        const float tot2 = cum[CT];
+        const float dec = KIND == kMaskLit ? 1.f : fast_exp2(tot2);
+#pragma unroll
+        for (int e = 0; e < RA; ++e) {
+            zx[e] *= dec;
+#pragma unroll
+            for (int e2 = 0; e2 < TA; ++e2) sx[e][e2] *= dec;
+        }
+        for (int j = 0; j < n; ++j) {
+            const float wgt = KIND == kMaskLit ? 1.f : fast_exp2(dir == 0 ? tot2 - cum[j] : cum[j]);
+            const float last = KEYS ? 1.f : nd[j];
+            float x[RA], y[TA];
+            lds_load(x, X + j * CF::DP + a0);
+            lds_load(y, Y + j * CF::DP + tj * TA);
+#pragma unroll
+            for (int e = 0; e < RA; ++e) {
+                const float xw = wgt * x[e];
+                zx[e] += xw * last;
+#pragma unroll
+                for (int e2 = 0; e2 < TA; ++e2) sx[e][e2] += xw * y[e2];
+            }
+        }
+        __syncthreads();   // before the next chunk's tokens overwrite these
     }
-    if (tid == 0) p.tot[(size_t)bh * p.nch + c] = tot2;
 }
 
-// ================================ entering states by one sequential walk ==============================
-// One workgroup per (batch, head) walks the chunks left to right (keys' and queries' states entering from
-// the left) and then right to left (entering from the right), carrying the running states in registers:
-// each entering state is written once and no scan pass is needed.  Used when the (batch, head) pairs
-// alone fill the chip.  Thread ownership as in cbwd_local_kernel.
 template <int D, int KIND, int CT>
 __global__ void __launch_bounds__(kThreads) cbwd_walk_kernel(CbParams p) {
-    using CF = CbCfg<D, CT>;
-    constexpr int TA = CF::TA;
     extern __shared__ __attribute__((aligned(16))) float sm[];
-    const int bh = blockIdx.x;
-    const float *Qs = sm, *Ks = Qs + CT * CF::DP, *Vs = Ks + CT * CF::DP, *Us = Vs + CT * CF::DP;
-    const float *nd = Us + CT * CF::DP, *cum = nd + CT;
-    const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
-#pragma unroll 1
-    for (int dir = 0; dir < 2; ++dir) {   // 0: from the left, 1: from the right
-        // causal: only the keys' state from the left and the queries' state from the right are used
-        const bool want_k = !p.causal || dir == 0, want_q = !p.causal || dir == 1;
-        float sk[TA][TA], sq[TA][TA], zk[TA], zq[TA];
-#pragma unroll
-        for (int e = 0; e < TA; ++e) {
-            zk[e] = zq[e] = 0.f;
-#pragma unroll
-            for (int e2 = 0; e2 < TA; ++e2) sk[e][e2] = sq[e][e2] = 0.f;
-        }
-#pragma unroll 1
-        for (int step = 0; step < p.nch; ++step) {
-            const int c = dir == 0 ? step : p.nch - 1 - step;
-            const int n = min(CT, p.L - c * CT);
-            stage_tokens<D, KIND, CT>(p, sm, bh, c, n);
-            __syncthreads();
-            // the state entering chunk c is the running sum so far
-            float *out = p.states + ((size_t)bh * p.nch + c) * 4 * CF::DD;
-            float *ok_ = out + (2 * dir) * CF::DD, *oq = out + (2 * dir + 1) * CF::DD;
-#pragma unroll
-            for (int e = 0; e < TA; ++e) {
-                const int a = ti * TA + e;
-#pragma unroll
-                for (int e2 = 0; e2 < TA; ++e2) {
-                    if (want_k) ok_[a * CF::DS + tj * TA + e2] = sk[e][e2];
-                    if (want_q) oq[a * CF::DS + tj * TA + e2] = sq[e][e2];
-                }
-                if (tj == 0) {
-#pragma unroll
-                    for (int pad = 1; pad < 4; ++pad) {
-                        if (want_k) ok_[a * CF::DS + D + pad] = 0.f;
-                        if (want_q) oq[a * CF::DS + D + pad] = 0.f;
-                    }
-                    if (want_k) ok_[a * CF::DS + D] = zk[e];
-                    if (want_q) oq[a * CF::DS + D] = zq[e];
-                }
-            }
-            // then decay it across the chunk and add the chunk's own tokens, weighted towards the
-            // chunk's far end (right end from the left, left end from the right)
-            const float tot2 = cum[CT];
-            const float dec = KIND == kMaskLit ? 1.f : fast_exp2(tot2);
-#pragma unroll
-            for (int e = 0; e < TA; ++e) {
-                zk[e] *= dec;
-                zq[e] *= dec;
-#pragma unroll
-                for (int e2 = 0; e2 < TA; ++e2) {
-                    sk[e][e2] *= dec;
-                    sq[e][e2] *= dec;
-                }
-            }
-            for (int j = 0; j < n; ++j) {
-                const float wgt = KIND == kMaskLit ? 1.f : fast_exp2(dir == 0 ? tot2 - cum[j] : cum[j]);
-                float xk[TA], xq[TA], yv[TA], yu[TA];
-                lds_load(xk, Ks + j * CF::DP + ti * TA);
-                lds_load(xq, Qs + j * CF::DP + ti * TA);
-                lds_load(yv, Vs + j * CF::DP + tj * TA);
-                lds_load(yu, Us + j * CF::DP + tj * TA);
-                const float ndj = nd[j];
-#pragma unroll
-                for (int e = 0; e < TA; ++e) {
-                    const float kx = wgt * xk[e], qx = wgt * xq[e];
-                    zk[e] += kx;
-                    zq[e] += qx * ndj;
-#pragma unroll
-                    for (int e2 = 0; e2 < TA; ++e2) {
-                        sk[e][e2] += kx * yv[e2];
-                        sq[e][e2] += qx * yu[e2];
-                    }
-                }
-            }
-            __syncthreads();   // before the next chunk's tokens overwrite these
-        }
-    }
-}
-
-// ================================ scan over chunks ====================================================
-// One thread per (batch, head, state element): the state entering chunk c from the left is
-// S_c = exp(tot_{c-1}) S_{c-1} + local_{c-1} (S_0 = 0); from the right, the mirror image.
-__global__ void __launch_bounds__(kThreads) cbwd_scan_kernel(CbParams p, int DD, int nbpb) {
-    const int bh = blockIdx.x / nbpb;
-    const int e = (blockIdx.x % nbpb) * kThreads + threadIdx.x;
-    if (e >= 4 * DD) return;
-    const int st = e / DD, off = e % DD;
-    if (p.causal && (st == 1 || st == 2)) return;   // query-left and key-right states are unused
-    const size_t stride = 4 * (size_t)DD;
-    float *base = p.states + (size_t)bh * p.nch * stride + (size_t)st * DD + off;
-    const float *tt = p.tot + (size_t)bh * p.nch;
-    const int nch = p.nch;
-    constexpr int kBatch = 8;
-    float run = 0.f;
-    if (st < 2) {
-        for (int c0 = 0; c0 < nch; c0 += kBatch) {
-            float x[kBatch], f[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int c = c0 + u;
-                x[u] = c < nch ? base[c * stride] : 0.f;
-                f[u] = c < nch ? fast_exp2(tt[c]) : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int c = c0 + u;
-                if (c < nch) {
-                    base[c * stride] = run;
-                    run = f[u] * run + x[u];
-                }
-            }
-        }
-    } else {
-        for (int c0 = nch - 1; c0 >= 0; c0 -= kBatch) {
-            float x[kBatch], f[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int c = c0 - u;
-                x[u] = c >= 0 ? base[c * stride] : 0.f;
-                f[u] = c >= 0 ? fast_exp2(tt[c]) : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int c = c0 - u;
-                if (c >= 0) {
-                    base[c * stride] = run;
-                    run = f[u] * run + x[u];
-                }
-            }
-        }
-    }
+    const int ns = p.causal ? 2 : 4;
+    const int bh = blockIdx.x / ns, s = blockIdx.x % ns;
+    // causal: s = 0 keys from the left, s = 1 queries from the right; else s = 2 dir + (queries)
+    const int dir = p.causal ? s : s >> 1;
+    const bool keys = p.causal ? s == 0 : (s & 1) == 0;
+    if (keys) walk<D, KIND, CT, 1>(p, sm, bh, dir);
+    else walk<D, KIND, CT, 2>(p, sm, bh, dir);
 }
 
 // ================================ main ===============================================================
@@ -636,7 +511,7 @@ void allow_lds(K *kernel, size_t lds) {
 }
 
 struct CbLayout {
-    size_t states, tot, da;   // float offsets into the workspace
+    size_t states, da;   // float offsets into the workspace
     size_t floats;
 };
 
@@ -645,8 +520,7 @@ CbLayout cbwd_layout(int B, int H, int L, int d, int C) {
     const size_t dd = (size_t)d * (d + 4);
     CbLayout w;
     w.states = 0;
-    w.tot = 4 * bh * nch * dd;
-    w.da = w.tot + ((bh * nch + 3) / 4) * 4;
+    w.da = 4 * bh * nch * dd;
     w.floats = w.da + 2 * (((bh * L) + 3) / 4) * 4;
     return w;
 }
@@ -673,19 +547,14 @@ hipError_t launch_cbwd_t(const BwdArgs &a, hipStream_t stream) {
     p.dv = a.dv;
     p.g_bf16 = a.g_bf16 ? 1 : 0;
     p.states = ws + w.states;
-    p.tot = ws + w.tot;
     const size_t n = (size_t)a.B * a.H * a.L;
     p.da_row = ws + w.da;
     p.da_col = p.da_row + ((n + 3) / 4) * 4;
     const int nblk = a.B * a.H * p.nch;
-    if (p.nch > 1 && a.B * a.H >= kWalkMinPairs) {
-        allow_lds(&cbwd_walk_kernel<D, KIND, CT>, CF::LDS_LOCAL);
-        hipLaunchKernelGGL((cbwd_walk_kernel<D, KIND, CT>), dim3(a.B * a.H), dim3(kThreads), CF::LDS_LOCAL, stream, p);
-    } else if (p.nch > 1) {
-        allow_lds(&cbwd_local_kernel<D, KIND, CT>, CF::LDS_LOCAL);
-        hipLaunchKernelGGL((cbwd_local_kernel<D, KIND, CT>), dim3(nblk), dim3(kThreads), CF::LDS_LOCAL, stream, p);
-        const int nbpb = (4 * CF::DD + kThreads - 1) / kThreads;
-        hipLaunchKernelGGL(cbwd_scan_kernel, dim3(a.B * a.H * nbpb), dim3(kThreads), 0, stream, p, CF::DD, nbpb);
+    if (p.nch > 1) {
+        allow_lds(&cbwd_walk_kernel<D, KIND, CT>, CF::LDS_WALK);
+        hipLaunchKernelGGL((cbwd_walk_kernel<D, KIND, CT>), dim3(a.B * a.H * (a.causal ? 2 : 4)), dim3(kThreads),
+                           CF::LDS_WALK, stream, p);
     }
     allow_lds(&cbwd_main_kernel<D, KIND, CT>, CF::LDS);
     hipLaunchKernelGGL((cbwd_main_kernel<D, KIND, CT>), dim3(nblk), dim3(kThreads), CF::LDS, stream, p);

@@ -186,11 +186,10 @@ def test_chunk_bwd_unsupported_and_workspace():
     assert cbwd(C=64, d=128) == UNSUPPORTED          # LDS: at most 32 tokens per chunk at d = 128
     assert lion.lion_attn_workspace_bytes(lion.FORM_CHUNK_BWD, 2, 3, 17, 128, 64, 1) == SIZE_MAX
     assert lion.lion_attn_workspace_bytes(lion.FORM_CHUNK_BWD, 2, 3, 17, 64, 64, 0) == SIZE_MAX
-    # four d x (d+1) fp32 states (rows padded to d + 4) per chunk and (batch, head), the chunks' decay
-    # totals, two dA halves
+    # four d x (d+1) fp32 states (rows padded to d + 4) per chunk and (batch, head), two dA halves
     B, H, L, d, C = 2, 3, 150, 64, 32
     nch = (L + C - 1) // C
-    want = 4 * (4 * B * H * nch * d * (d + 4) + ((B * H * nch + 3) // 4) * 4 + 2 * ((B * H * L + 3) // 4) * 4)
+    want = 4 * (4 * B * H * nch * d * (d + 4) + 2 * ((B * H * L + 3) // 4) * 4)
     need = lion.lion_attn_workspace_bytes(lion.FORM_CHUNK_BWD, B, H, L, d, C, 1)
     assert need == want
     assert cbwd(C=C, B=B, H=H, L=L, ws=None, wsb=need) == WORKSPACE

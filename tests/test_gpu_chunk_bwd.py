@@ -5,8 +5,7 @@ The chunkwise backward computes the same gradients as the full form's backward, 
 same reference (``oracle.full_bwd``, pinned by finite differences of the forward definition) and the
 same condition-aware gate (``tests.test_gpu_bwd.run_case``).  The cases span one chunk, several chunks
 with a ragged last one, every supported chunk size and head dimension, the causal variant (no states
-entering from the right), signed inputs, one long sequence at the high-resolution length, and 256 (batch, head) pairs (where
-the entering states come from one walk per pair rather than from per-chunk sums and a scan).
+entering from the right), signed inputs, one long sequence at the high-resolution length, and 256 (batch, head) pairs.
 """
 from __future__ import annotations
 
@@ -55,7 +54,6 @@ def test_chunk_bwd_long_sequence():
 
 @pytest.mark.parametrize("kind", [lin.LIT, lin.D, lin.S])
 def test_chunk_bwd_many_pairs(kind):
-    # 256 (batch, head) pairs: the entering states come from one sequential walk per pair instead of
-    # per-chunk sums and a scan
+    # 256 (batch, head) pairs, 1024 walks and 1280 chunk workgroups in flight at once
     run_case(16, 16, 150, 64, kind, seed=4500, C=32)
     run_case(16, 16, 100, 64, kind, causal=True, positive=False, seed=4501, C=32)
