@@ -87,55 +87,86 @@ __device__ __forceinline__ void lds_load(float (&x)[N], const float *p) {
     }
 }
 
-// Stage the chunk's tokens into LDS as fp32 rows: phi(q), phi(k), v, u = dy / den, and -delta;
-// then the chunk's prefix sums of log(lambda) (log2 units, relative to the chunk start, inclusive).
-// Rows at or past n are zero; prefix sums past n repeat the last one.
+// Staging is split in two so a walk can issue the next chunk's loads before working on the current
+// one: tok_load reads the chunk's rows into registers, tok_commit applies phi, forms u and -delta,
+// writes the LDS rows and the prefix sums.
 // WHICH: 0 everything, 1 the keys' rows only (phi(k), v), 2 the queries' only (phi(q), u, -delta).
-template <int D, int KIND, int CT, int WHICH = 0>
-__device__ void stage_tokens(const CbParams &p, float *sm, int bh, int c, int n) {
+template <int D, int CT>
+struct TokRegs {
+    static constexpr int SPR = D / 8;                 // 16-byte slots per row
+    static constexpr int NSL = CT * SPR;              // a multiple of 64
+    static constexpr int NIT = (NSL + kThreads - 1) / kThreads;
+    bf16x8 q[NIT], k[NIT], v[NIT], y[NIT], d[NIT];
+    float den[NIT];
+    float ll;
+};
+
+template <int D, int KIND, int CT, int WHICH>
+__device__ __forceinline__ void tok_load(const CbParams &p, int bh, int c, int n, TokRegs<D, CT> &R) {
+    constexpr bool LQ = WHICH != 1, LK = WHICH != 2;
+    using TR = TokRegs<D, CT>;
+    const int tid = threadIdx.x;
+    const size_t row0 = (size_t)bh * p.L + (size_t)c * CT;
+#pragma unroll
+    for (int it = 0; it < TR::NIT; ++it) {
+        const int sl = it * kThreads + tid;
+        const int row = sl / TR::SPR, cs = (sl % TR::SPR) * 8;
+        if (sl < TR::NSL && row < n) {
+            const size_t g = (row0 + row) * D + cs;
+            if constexpr (LQ) {
+                R.q[it] = __builtin_bit_cast(bf16x8, ld16(p.q + g));
+                R.y[it] = __builtin_bit_cast(bf16x8, ld16(p.y + g));
+                R.d[it] = __builtin_bit_cast(bf16x8, ld16(p.dy + g));
+                R.den[it] = p.den[row0 + row];
+            }
+            if constexpr (LK) {
+                R.k[it] = __builtin_bit_cast(bf16x8, ld16(p.k + g));
+                R.v[it] = __builtin_bit_cast(bf16x8, ld16(p.v + g));
+            }
+        }
+    }
+    if constexpr (KIND == kMaskS)
+        if (tid < 64) R.ll = tid < n ? p.ll[row0 + tid] : 0.f;
+}
+
+// Rows at or past n are zero; prefix sums (log2 units, relative to the chunk start, inclusive) past n
+// repeat the last one; cum[CT] is the chunk's total.
+template <int D, int KIND, int CT, int WHICH>
+__device__ __forceinline__ void tok_commit(const CbParams &p, float *sm, int bh, int n, const TokRegs<D, CT> &R) {
     constexpr bool LQ = WHICH != 1, LK = WHICH != 2;
     using CF = CbCfg<D, CT>;
+    using TR = TokRegs<D, CT>;
+    constexpr int SPR = TR::SPR;
     float *Qs = sm, *Ks = Qs + CT * CF::DP, *Vs = Ks + CT * CF::DP, *Us = Vs + CT * CF::DP;
     float *nd = Us + CT * CF::DP, *cum = nd + CT;
     const int tid = threadIdx.x;
-    constexpr int SPR = D / 8;          // 16-byte slots per row
-    constexpr int NSL = CT * SPR;       // a multiple of 64
-    const size_t row0 = (size_t)bh * p.L + (size_t)c * CT;
-    for (int sl0 = 0; sl0 < NSL; sl0 += kThreads) {
-        if (sl0 + (tid & ~63) >= NSL) break;   // whole waves
-        const int sl = sl0 + tid;
+#pragma unroll
+    for (int it = 0; it < TR::NIT; ++it) {
+        if (it * kThreads + (tid & ~63) >= TR::NSL) break;   // whole waves
+        const int sl = it * kThreads + tid;
         const int row = sl / SPR, cs = (sl % SPR) * 8;
         const bool ok = row < n;
         float fq[8] = {}, fk[8] = {}, fv[8] = {}, fu[8] = {};
         float ssq = 0.f, ssk = 0.f, part = 0.f, dinv = 0.f;
         if (ok) {
-            const size_t g = (row0 + row) * D + cs;
             if constexpr (LQ) {
-                const bf16x8 q8 = __builtin_bit_cast(bf16x8, ld16(p.q + g));
-                const bf16x8 y8 = __builtin_bit_cast(bf16x8, ld16(p.y + g));
-                const bf16x8 d8 = __builtin_bit_cast(bf16x8, ld16(p.dy + g));
-                dinv = 1.f / p.den[row0 + row];
+                dinv = 1.f / R.den[it];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    fq[e] = phi_pre<KIND>((float)q8[e]);
-                    fu[e] = (float)d8[e] * dinv;
+                    fq[e] = phi_pre<KIND>((float)R.q[it][e]);
+                    fu[e] = (float)R.d[it][e] * dinv;
                     ssq += fq[e] * fq[e];
-                    part += (float)d8[e] * (float)y8[e];
+                    part += (float)R.d[it][e] * (float)R.y[it][e];
                 }
             }
             if constexpr (LK) {
-                const bf16x8 k8 = __builtin_bit_cast(bf16x8, ld16(p.k + g));
-                const bf16x8 v8 = __builtin_bit_cast(bf16x8, ld16(p.v + g));
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    fk[e] = phi_pre<KIND>((float)k8[e]);
-                    fv[e] = (float)v8[e];
+                    fk[e] = phi_pre<KIND>((float)R.k[it][e]);
+                    fv[e] = (float)R.v[it][e];
                     ssk += fk[e] * fk[e];
                 }
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) fq[e] = fk[e] = fv[e] = fu[e] = 0.f;
         }
         if constexpr (LQ) part = group_sum<SPR>(part);
         if constexpr (KIND == kMaskS) {
@@ -171,7 +202,7 @@ __device__ void stage_tokens(const CbParams &p, float *sm, int bh, int c, int n)
             c2 = (float)(min(t, n - 1) + 1) * lg;
             tot2 = (float)n * lg;
         } else if constexpr (KIND == kMaskS) {
-            double x = t < n ? (double)p.ll[row0 + t] : 0.0;
+            double x = (double)R.ll;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const double up = __shfl_up(x, o, 64);
@@ -183,6 +214,13 @@ __device__ void stage_tokens(const CbParams &p, float *sm, int bh, int c, int n)
         if (t < CT) cum[t] = c2;
         if (t == 0) cum[CT] = tot2;
     }
+}
+
+template <int D, int KIND, int CT, int WHICH = 0>
+__device__ void stage_tokens(const CbParams &p, float *sm, int bh, int c, int n) {
+    TokRegs<D, CT> R;
+    tok_load<D, KIND, CT, WHICH>(p, bh, c, n, R);
+    tok_commit<D, KIND, CT, WHICH>(p, sm, bh, n, R);
 }
 
 // ================================ entering states by sequential walks ================================
@@ -211,12 +249,22 @@ __device__ void walk(const CbParams &p, float *sm, int bh, int dir) {
 #pragma unroll
         for (int e2 = 0; e2 < TA; ++e2) sx[e][e2] = 0.f;
     }
+    TokRegs<D, CT> R;
+    {
+        const int c = dir == 0 ? 0 : p.nch - 1;
+        const int n = min(CT, p.L - c * CT);
+        tok_load<D, KIND, CT, WHICH>(p, bh, c, n, R);
+        tok_commit<D, KIND, CT, WHICH>(p, sm, bh, n, R);
+        __syncthreads();
+    }
 #pragma unroll 1
     for (int step = 0; step < p.nch; ++step) {
         const int c = dir == 0 ? step : p.nch - 1 - step;
         const int n = min(CT, p.L - c * CT);
-        stage_tokens<D, KIND, CT, WHICH>(p, sm, bh, c, n);
-        __syncthreads();
+        const int cn = dir == 0 ? c + 1 : c - 1;             // the next chunk of the walk
+        const int nn = min(CT, p.L - cn * CT);
+        const bool more = step + 1 < p.nch;
+        if (more) tok_load<D, KIND, CT, WHICH>(p, bh, cn, nn, R);   // in flight while this chunk is summed
         // the state entering chunk c is the running sum so far
         float *out = p.states + (((size_t)bh * p.nch + c) * 4 + st) * CF::DD;
 #pragma unroll
@@ -240,6 +288,7 @@ __device__ void walk(const CbParams &p, float *sm, int bh, int dir) {
 #pragma unroll
             for (int e2 = 0; e2 < TA; ++e2) sx[e][e2] *= dec;
         }
+#pragma unroll 8
         for (int j = 0; j < n; ++j) {
             const float wgt = KIND == kMaskLit ? 1.f : fast_exp2(dir == 0 ? tot2 - cum[j] : cum[j]);
             const float last = KEYS ? 1.f : nd[j];
@@ -255,6 +304,10 @@ __device__ void walk(const CbParams &p, float *sm, int bh, int dir) {
             }
         }
         __syncthreads();   // before the next chunk's tokens overwrite these
+        if (more) {
+            tok_commit<D, KIND, CT, WHICH>(p, sm, bh, nn, R);
+            __syncthreads();
+        }
     }
 }
 
