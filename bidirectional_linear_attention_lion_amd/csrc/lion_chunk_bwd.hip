@@ -227,28 +227,24 @@ __device__ void stage_tokens(const CbParams &p, float *sm, int bh, int c, int n)
 // One workgroup per (batch, head, direction, keys or queries) walks the chunks -- left to right for the
 // states entering from the left, right to left for those entering from the right -- carrying its
 // running state in registers, so each entering state is written once.  Causal runs only the keys'
-// walk from the left and the queries' walk from the right.  Thread (ti, tj) of the 16 x 16 grid owns
-// state rows ti TA .. + TA - 1 and columns tj TA .. + TA - 1, plus column D of its rows (written by
-// the tj = 0 threads).  (Splitting a walk over two workgroups by rows measured slower where the
-// pairs already fill the chip: the second workgroup stages the same tokens again.)
+// walk from the left and the queries' walk from the right.  The running state's first D columns live
+// in matrix-core accumulators (16 x 16 tiles spread over the four waves), column D in thread a of the
+// first D threads.  (Splitting a walk over two workgroups by rows measured slower where the pairs
+// already fill the chip: the second workgroup stages the same tokens again.)
 template <int D, int KIND, int CT, int WHICH>
 __device__ void walk(const CbParams &p, float *sm, int bh, int dir) {
     using CF = CbCfg<D, CT>;
-    constexpr int TA = CF::TA, RA = TA;
+    constexpr int NA = D / 16, NTW = NA * NA / 4;   // 16 x 16 state tiles, per wave
     constexpr bool KEYS = WHICH == 1;
     const float *Qs = sm, *Ks = Qs + CT * CF::DP, *Vs = Ks + CT * CF::DP, *Us = Vs + CT * CF::DP;
     const float *nd = Us + CT * CF::DP, *cum = nd + CT;
     const float *X = KEYS ? Ks : Qs, *Y = KEYS ? Vs : Us;
-    const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int st = 2 * dir + (KEYS ? 0 : 1);
-    const int a0 = ti * RA;
-    float sx[RA][TA], zx[RA];
+    f32x4 acc[NTW];   // state rows 16 ta + 4 g + e, column 16 tb + r of tile w + 4 u = NA ta + tb
 #pragma unroll
-    for (int e = 0; e < RA; ++e) {
-        zx[e] = 0.f;
-#pragma unroll
-        for (int e2 = 0; e2 < TA; ++e2) sx[e][e2] = 0.f;
-    }
+    for (int u = 0; u < NTW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float z = 0.f;    // column D of row tid (tid < D)
     TokRegs<D, CT> R;
     {
         const int c = dir == 0 ? 0 : p.nch - 1;
@@ -268,39 +264,40 @@ __device__ void walk(const CbParams &p, float *sm, int bh, int dir) {
         // the state entering chunk c is the running sum so far
         float *out = p.states + (((size_t)bh * p.nch + c) * 4 + st) * CF::DD;
 #pragma unroll
-        for (int e = 0; e < RA; ++e) {
-            const int a = a0 + e;
+        for (int u = 0; u < NTW; ++u) {
+            const int tile = w + 4 * u, ta = tile / NA, tb = tile % NA;
 #pragma unroll
-            for (int e2 = 0; e2 < TA; ++e2) out[a * CF::DS + tj * TA + e2] = sx[e][e2];
-            if (tj == 0) {
+            for (int e = 0; e < 4; ++e) out[(16 * ta + 4 * g + e) * CF::DS + 16 * tb + r] = acc[u][e];
+        }
+        if (tid < D) {
+            out[tid * CF::DS + D] = z;
 #pragma unroll
-                for (int pad = 1; pad < 4; ++pad) out[a * CF::DS + D + pad] = 0.f;
-                out[a * CF::DS + D] = zx[e];
-            }
+            for (int pad = 1; pad < 4; ++pad) out[tid * CF::DS + D + pad] = 0.f;
         }
         // then decay it across the chunk and add the chunk's own tokens, weighted towards the chunk's
-        // far end (its right end walking from the left, its left end walking from the right)
+        // far end (its right end walking from the left, its left end walking from the right), on the
+        // matrix cores: state[a][b] += sum_j (w_j x_j[a]) y_j[b]
         const float tot2 = cum[CT];
         const float dec = KIND == kMaskLit ? 1.f : fast_exp2(tot2);
 #pragma unroll
-        for (int e = 0; e < RA; ++e) {
-            zx[e] *= dec;
+        for (int u = 0; u < NTW; ++u)
 #pragma unroll
-            for (int e2 = 0; e2 < TA; ++e2) sx[e][e2] *= dec;
+            for (int e = 0; e < 4; ++e) acc[u][e] *= dec;
+        z *= dec;
+#pragma unroll 2
+        for (int k0 = 0; k0 < CT; k0 += 4) {
+            const int j = k0 + g;   // rows past n are zero
+            const float wj = KIND == kMaskLit ? 1.f : fast_exp2(dir == 0 ? tot2 - cum[j] : cum[j]);
+#pragma unroll
+            for (int u = 0; u < NTW; ++u) {
+                const int tile = w + 4 * u, ta = tile / NA, tb = tile % NA;
+                acc[u] = mfma_f32(wj * X[j * CF::DP + 16 * ta + r], Y[j * CF::DP + 16 * tb + r], acc[u]);
+            }
         }
-#pragma unroll 8
-        for (int j = 0; j < n; ++j) {
-            const float wgt = KIND == kMaskLit ? 1.f : fast_exp2(dir == 0 ? tot2 - cum[j] : cum[j]);
-            const float last = KEYS ? 1.f : nd[j];
-            float x[RA], y[TA];
-            lds_load(x, X + j * CF::DP + a0);
-            lds_load(y, Y + j * CF::DP + tj * TA);
-#pragma unroll
-            for (int e = 0; e < RA; ++e) {
-                const float xw = wgt * x[e];
-                zx[e] += xw * last;
-#pragma unroll
-                for (int e2 = 0; e2 < TA; ++e2) sx[e][e2] += xw * y[e2];
+        if (tid < D) {
+            for (int j = 0; j < n; ++j) {
+                const float wj = KIND == kMaskLit ? 1.f : fast_exp2(dir == 0 ? tot2 - cum[j] : cum[j]);
+                z += wj * X[j * CF::DP + tid] * (KEYS ? 1.f : nd[j]);
             }
         }
         __syncthreads();   // before the next chunk's tokens overwrite these
