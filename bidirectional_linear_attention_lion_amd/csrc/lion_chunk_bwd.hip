@@ -26,7 +26,7 @@
 // Two launches plus the dlog(lambda) one (states are stored with rows padded to 16 bytes):
 //   walk:  one workgroup per (batch, head, direction, keys or queries) walks the chunks in order,
 //          writing the state entering each chunk and then adding that chunk's tokens to its running
-//          state in registers (fp32 vector arithmetic);
+//          state (fp32 matrix cores, the state in accumulators);
 //   main:  one workgroup per chunk forms the pair matrices M dp and M s in LDS (and the dA sums of
 //          sign(i - j) M dp s), then dphi(q), dphi(k), dv and the rest of the dA halves from them and
 //          from the four entering states, on the matrix cores in fp32; applies phi's Jacobian and
