@@ -429,6 +429,28 @@ __global__ void __launch_bounds__(kThreads) cbwd_main_kernel(CbParams p) {
     }
     __syncthreads();
 
+    // ---- the entering states this chunk needs (zero: nothing left of the first chunk or right of
+    // the last; causal, the keys' state from the right and the queries' state from the left), each
+    // loaded into registers while the previous work runs
+    int sts[4], nst = 0;
+    {
+        const int c_last = p.nch - 1;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const bool right = st >= 2, keys = (st & 1) == 0;
+            if (!((right ? c == c_last : c == 0) || (causal && keys == right))) sts[nst++] = st;
+        }
+    }
+    constexpr int NV = (CF::DD / 4 + kThreads - 1) / kThreads;   // 16-byte pieces of a state per thread
+    f32x4 sreg[NV];
+    auto load_state = [&](int st) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(p.states + (((size_t)bh * p.nch + c) * 4 + st) * CF::DD);
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            if (v * kThreads + tid < CF::DD / 4) sreg[v] = src[v * kThreads + tid];
+    };
+    if (nst > 0) load_state(sts[0]);
+
     // ---- intra-chunk parts of the output tiles (rows t = 16 tt + 4 g + e, channels 16 ta + r)
     f32x4 aq[NOUT], ak[NOUT], av[NOUT];
 #pragma unroll
@@ -447,18 +469,16 @@ __global__ void __launch_bounds__(kThreads) cbwd_main_kernel(CbParams p) {
     }
     __syncthreads();   // the pair matrices' space takes the states next
 
-    // ---- the four entering states
-    const int c_last = p.nch - 1;
+    // ---- apply the entering states
 #pragma unroll 1
-    for (int st = 0; st < 4; ++st) {
+    for (int k = 0; k < nst; ++k) {
+        const int st = sts[k];
         const bool right = st >= 2, keys = (st & 1) == 0;
-        // zero states: nothing left of the first chunk or right of the last; causal, the keys' state
-        // from the right and the queries' state from the left
-        if ((right ? c == c_last : c == 0) || (causal && keys == right)) continue;
-        const float *src = p.states + (((size_t)bh * p.nch + c) * 4 + st) * CF::DD;
-        for (int e = tid * 4; e < CF::DD; e += kThreads * 4)
-            *reinterpret_cast<f32x4 *>(buf + e) = *reinterpret_cast<const f32x4 *>(src + e);
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            if (v * kThreads + tid < CF::DD / 4) reinterpret_cast<f32x4 *>(buf)[v * kThreads + tid] = sreg[v];
         __syncthreads();
+        if (k + 1 < nst) load_state(sts[k + 1]);
         const float sgn = right ? -1.f : 1.f;
         const float *Xs = keys ? Us : Vs;   // what the state multiplies: u (keys' states), w (queries')
         const float *Ps = keys ? Qs : Ks;   // the dA half dots the result with phi of the same token
