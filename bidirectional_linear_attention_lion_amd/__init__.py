@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     FORM_BIRNN,
     FORM_CHUNK,
     FORM_FULL,
+    FORM_CHUNK2,
     FORM_CHUNK_BWD,
     FORM_FULL_BWD,
     MASK_D,
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     lion_attn_full2,
     lion_attn_full_bwd,
     lion_attn_chunk_bwd,
+    lion_attn_chunk2,
     lion_attn_workspace_bytes,
     lion_selectivity,
     lion_status_str,

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(PKG, "liblion_attn.so")
 MASK_LIT, MASK_D, MASK_S = 0, 1, 2
 CAUSAL = 4   # OR-ed into a mask kind: the causal (unidirectional) variant
 DTYPE_F32, DTYPE_BF16 = 0, 1
-FORM_FULL, FORM_CHUNK, FORM_BIRNN, FORM_FULL_BWD, FORM_CHUNK_BWD = 0, 1, 2, 3, 4
+FORM_FULL, FORM_CHUNK, FORM_BIRNN, FORM_FULL_BWD, FORM_CHUNK_BWD, FORM_CHUNK2 = 0, 1, 2, 3, 4, 5
 _KINDS = {"lit": MASK_LIT, "d": MASK_D, "s": MASK_S}
 
 
@@ -45,9 +45,10 @@ def library() -> ctypes.CDLL:
     lib.lion_attn_chunk_bwd.argtypes = common + [i, i, i, i, i, i, vp, fp, vp, vp, vp, vp, i, fp, vp, sz, vp]
     lib.lion_selectivity.argtypes = [vp, vp, fp, i, i, i, i, fp, fp, vp, vp, i, vp]
     lib.lion_attn_full2.argtypes = common + [f, vp, i, i, i, i, i, vp, i, fp, vp]
+    lib.lion_attn_chunk2.argtypes = common + [i, f, vp, i, i, i, i, i, vp, i, fp, vp, sz, vp]
     for fn in ("lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_full_bwd", "lion_attn_chunk_bwd",
                "lion_selectivity",
-               "lion_attn_full2", "lion_attn_abi_version"):
+               "lion_attn_full2", "lion_attn_chunk2", "lion_attn_abi_version"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.lion_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.lion_attn_workspace_bytes.restype = sz
@@ -118,6 +119,19 @@ def lion_attn_full2(q, k, v, log_lambda, mask_kind, order, eps: float = 1e-6, *,
                                    L, d, dt, _ptr(y), ydt, _ptr(den_out), sptr)
     if rc != 0:
         raise LionError("lion_attn_full2", rc)
+    return y
+
+
+def lion_attn_chunk2(q, k, v, log_lambda, mask_kind, order, C: int = 64, eps: float = 1e-6, *, y=None, y_dtype=None,
+                     den_out=None, workspace=None, stream=None):
+    """Chunkwise form with the masks of the tokens' own order and of ``order`` (int32 cuda tensor [L])
+    averaged (the definition of lion_attn_full2)."""
+    kind, B, H, L, d, dt, y, ydt, sptr = _prepare(q, k, v, mask_kind, y, y_dtype, den_out, stream)
+    ws, nbytes = _workspace(FORM_CHUNK2, B, H, L, d, C, dt, workspace, q.device)
+    rc = library().lion_attn_chunk2(_ptr(q), _ptr(k), _ptr(v), _ptr(log_lambda), kind, C, float(eps), _ptr(order), B,
+                                    H, L, d, dt, _ptr(y), ydt, _ptr(den_out), _ptr(ws), nbytes, sptr)
+    if rc != 0:
+        raise LionError("lion_attn_chunk2", rc)
     return y
 
 

@@ -112,6 +112,27 @@ int lion_attn_chunk(const void *q, const void *k, const void *v, const float *lo
     return status_of(lion::launch_chunk(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int lion_attn_chunk2(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, int C,
+                     float eps, const int *order, int B, int H, int L, int d, int dtype, void *y, int y_dtype,
+                     float *den_out, void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_common(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    if (rc != LION_OK) return rc;
+    if (!order || !aligned16(order)) return LION_ERR_INVALID;
+    if (C < 1) return LION_ERR_INVALID;
+    if (workspace && !aligned16(workspace)) return LION_ERR_INVALID;
+    if (mask_kind & LION_CAUSAL) return LION_ERR_UNSUPPORTED;
+    if (!c_supported_for(C, d)) return LION_ERR_UNSUPPORTED;
+    lion::AttnArgs a = make_args(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    a.C = C;
+    a.order = order;
+    const lion::Plan plan = lion::plan_chunk2(a);
+    if (!plan.ok) return LION_ERR_UNSUPPORTED;
+    if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return LION_ERR_WORKSPACE;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    return status_of(lion::launch_chunk2(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int lion_attn_birnn(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, float eps,
                     int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out, void *workspace,
                     size_t workspace_bytes, void *stream) {
@@ -249,6 +270,11 @@ size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, in
         plan = lion::plan_chunk(a);
         break;
     case LION_FORM_BIRNN: plan = lion::plan_birnn(a); break;
+    case LION_FORM_CHUNK2:
+        if (!c_supported_for(C, d)) return (size_t)-1;
+        a.C = C;
+        plan = lion::plan_chunk2(a);
+        break;
     case LION_FORM_FULL_BWD: {
         if (dtype != LION_DTYPE_BF16) return (size_t)-1;
         lion::BwdArgs b{};

@@ -66,6 +66,7 @@ Plan plan_selectivity(const SelArgs &a);
 Plan plan_full_bwd(const BwdArgs &a);
 Plan plan_chunk_bwd(const BwdArgs &a);
 Plan plan_chunk(const AttnArgs &a);
+Plan plan_chunk2(const AttnArgs &a);
 Plan plan_birnn(const AttnArgs &a);
 
 // Each launcher enqueues its kernels on `stream` and returns hipSuccess or the launch error.
@@ -78,6 +79,7 @@ hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_dll(int kind, float *da_row, float *da_col, float *dll, int B, int H, int L, hipStream_t stream);
 hipError_t launch_selectivity(const SelArgs &a, hipStream_t stream);
 hipError_t launch_chunk(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_chunk2(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_birnn(const AttnArgs &a, hipStream_t stream);
 
 }  // namespace lion

@@ -91,7 +91,7 @@ enum lion_mask_kind { LION_MASK_LIT = 0, LION_MASK_D = 1, LION_MASK_S = 2 };
 enum { LION_CAUSAL = 4 };
 enum lion_dtype { LION_DTYPE_F32 = 0, LION_DTYPE_BF16 = 1 };
 enum lion_form { LION_FORM_FULL = 0, LION_FORM_CHUNK = 1, LION_FORM_BIRNN = 2, LION_FORM_FULL_BWD = 3,
-                 LION_FORM_CHUNK_BWD = 4 };
+                 LION_FORM_CHUNK_BWD = 4, LION_FORM_CHUNK2 = 5 };
 enum lion_status {
     LION_OK = 0,
     LION_ERR_INVALID = -1,
@@ -130,6 +130,20 @@ LION_API int lion_attn_full2(const void *q, const void *k, const void *v, const 
 LION_API int lion_attn_chunk(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, int C,
                     float eps, int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Chunkwise form with the two-order averaged mask of lion_attn_full2 (same definition, same order
+ * argument; reply "P2: Comparison against vision SSMs", item 1, Figure 7 b and c).  The attention is
+ * linear in the mask, so this runs the chunkwise form in the tokens' own order and in the second
+ * order (q, k, v and LION-S's log(lambda) rearranged into it in the workspace) with fp32 results and
+ * combines y = (y_b den_b + y_c den_c) / (den_b + den_c).
+ *   order      device int32 [L], as for lion_attn_full2.
+ *   C          as for lion_attn_chunk.  LION_CAUSAL is LION_ERR_UNSUPPORTED.
+ *   workspace  >= lion_attn_workspace_bytes(LION_FORM_CHUNK2, ..., C, dtype) bytes: the rearranged
+ *              inputs, two fp32 outputs and row sums, and the chunkwise form's own workspace.
+ * den_out, when given, receives the averaged mask's row sums + eps (as lion_attn_full2's). */
+LION_API int lion_attn_chunk2(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind,
+                              int C, float eps, const int *order, int B, int H, int L, int d, int dtype, void *y,
+                              int y_dtype, float *den_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bidirectional RNN form: a forward and a backward recurrence over tokens with d x d matrix
  * states, S_i = lambda_i S_{i-1} + phi(k_i) v_i^T (backward: S_i = lambda_{i+1} S_{i+1} + ...),
@@ -198,8 +212,8 @@ LION_API int lion_attn_chunk_bwd(const void *q, const void *k, const void *v, co
 LION_API int lion_selectivity(const void *x, const void *w, const float *bias, int B, int L, int H, int Dm,
                               float *log_lambda, float *key_scale, const void *k, void *k_out, int d, void *stream);
 
-/* Workspace bytes `form` needs for these sizes (C is ignored except for LION_FORM_CHUNK and
- * LION_FORM_CHUNK_BWD).
+/* Workspace bytes `form` needs for these sizes (C is ignored except for LION_FORM_CHUNK,
+ * LION_FORM_CHUNK_BWD and LION_FORM_CHUNK2).
  * Returns 0 when no workspace is needed, and (size_t)-1 for arguments the form rejects. */
 LION_API size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, int dtype);
 

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     lib = lion.library()
     names = header_symbols()
     assert set(names) == {"lion_attn_full", "lion_attn_full2", "lion_attn_chunk", "lion_attn_birnn",
-                          "lion_attn_full_bwd", "lion_attn_chunk_bwd", "lion_selectivity", "lion_attn_workspace_bytes",
+                          "lion_attn_full_bwd", "lion_attn_chunk_bwd", "lion_attn_chunk2", "lion_selectivity", "lion_attn_workspace_bytes",
                           "lion_status_str", "lion_attn_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -194,6 +194,27 @@ def test_chunk_bwd_unsupported_and_workspace():
     assert need == want
     assert cbwd(C=C, B=B, H=H, L=L, ws=None, wsb=need) == WORKSPACE
     assert cbwd(C=C, B=B, H=H, L=L, ws=P, wsb=need - 1) == WORKSPACE
+
+
+def chunk2(order=P, C=64, ws=P, wsb=1 << 40, **kw):
+    a = dict(q=P, k=P, v=P, ll=P, kind=1, eps=1e-6, B=2, H=3, L=17, d=64, dt=1, y=P, ydt=1, den=None)
+    a.update(kw)
+    return lion.library().lion_attn_chunk2(a["q"], a["k"], a["v"], a["ll"], a["kind"], C, a["eps"], order, a["B"],
+                                           a["H"], a["L"], a["d"], a["dt"], a["y"], a["ydt"], a["den"], ws, wsb, None)
+
+
+def test_chunk2_arguments():
+    assert chunk2(order=None) == INVALID
+    assert chunk2(order=MIS) == INVALID
+    assert chunk2(q=None) == INVALID
+    assert chunk2(ws=MIS) == INVALID
+    assert chunk2(kind=1 | 4) == UNSUPPORTED
+    assert chunk2(C=48) == UNSUPPORTED
+    need = lion.lion_attn_workspace_bytes(lion.FORM_CHUNK2, 2, 3, 17, 64, 64, 1)
+    assert need != SIZE_MAX and need > 2 * 3 * 17 * 64 * (3 * 2 + 2 * 4)
+    # the size query answers for LION-S (the largest: its rearranged log(lambda) too)
+    assert chunk2(kind=2, ws=None, wsb=need) == WORKSPACE
+    assert chunk2(kind=2, ws=P, wsb=need - 1) == WORKSPACE
 
 
 def full2(order=P, **kw):
