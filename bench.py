@@ -37,7 +37,7 @@ VALU_FP32_PEAK_TFLOPS = 157.3   # fp32 vector
 CSRC = os.path.join(ROOT, "bidirectional_linear_attention_lion_amd", "csrc")
 KERNEL_FILES = {"full": "lion_full.hip", "chunk": "lion_chunk.hip", "birnn": "lion_birnn.hip",
                 "full_bwd": "lion_full_bwd.hip", "chunk_bwd": "lion_chunk_bwd.hip", "selectivity": "lion_selectivity.hip",
-                "full2": "lion_full.hip"}
+                "full2": "lion_full.hip", "chunk2": "lion_chunk2.hip"}
 SEL_WIDTH = 1024   # layer-input width of the selectivity prologue (the BERT-Large-shaped recipe)
 
 
@@ -53,7 +53,7 @@ def parse_args():
                          "gradients computed chunkwise (chunks of --chunk tokens, default 32, at most 64); selectivity times "
                          "the LION-S prologue (log lambda from a [B, L, 1024] layer input, keys scaled); full2 the full "
                          "form with the masks of the raster and the column-major patch order averaged (image "
-                         "workloads: L = 1 + n^2)")
+                         "workloads: L = 1 + n^2), chunk2 the same averaged masks in the chunkwise form")
     ap.add_argument("--chunk", type=int, default=None, help="chunk size C (default: the workload's first)")
     ap.add_argument("--causal", action="store_true",
                     help="the causal variant (keys after the query masked out) of the workload's mask")
@@ -160,6 +160,10 @@ def algorithmic(form: str, wl, C: int, causal: bool = False):
         return nbytes, bh * (10 * cpairs * d + 8 * cpairs + L * per_tok)
     if form == "full2":
         return nbytes, bh * (4 * L * L * d + 4 * L * L)   # as the full form, two mask terms per score
+    if form == "chunk2":
+        # the chunkwise form's work once per order; bytes are the method's (the rearranged copies of
+        # q, k, v and the fp32 partial results are this implementation's own traffic)
+        return nbytes, 2 * bh * (4 * L * C * d + 8 * L * d * d + 2 * L * C)
     if form == "full":
         pairs = L * (L + 1) / 2 if causal else L * L
         flops = bh * (4 * pairs * d + 2 * pairs)          # phi(Q)phi(K)^T, P V, mask and row sums
@@ -287,10 +291,10 @@ def main():
                 (wl.H,) if wl.kind == 1 else (wl.B, wl.H, wl.L), dtype=torch.float32, device=dev)
             bwd_sets.append((yb, den, dy, grads, dll))
     order = None
-    if "full2" in forms:
+    if "full2" in forms or "chunk2" in forms:
         side = int(round((wl.L - 1) ** 0.5))
         if side * side + 1 != wl.L:
-            raise SystemExit("bench.py: full2 needs an image workload (L = 1 + n^2)")
+            raise SystemExit("bench.py: full2 and chunk2 need an image workload (L = 1 + n^2)")
         order = torch.from_numpy(lin.column_major_order(side, side)).to(dev)
     sel = None
     if "selectivity" in forms:
@@ -304,7 +308,7 @@ def main():
         bs = torch.full((wl.H,), 3.0, dtype=torch.float32, device=dev)
         sel = (xs, ws_, bs)
     for f, form_id in (("chunk", lion.FORM_CHUNK), ("birnn", lion.FORM_BIRNN), ("full_bwd", lion.FORM_FULL_BWD),
-                       ("chunk_bwd", lion.FORM_CHUNK_BWD)):
+                       ("chunk_bwd", lion.FORM_CHUNK_BWD), ("chunk2", lion.FORM_CHUNK2)):
         if f not in forms:
             continue
         cf = CB if f == "chunk_bwd" else C
@@ -317,6 +321,8 @@ def main():
             lion.lion_attn_full(q, k, v, ll, kind, wl.eps, y=y, stream=stream)
         elif form == "full2":
             lion.lion_attn_full2(q, k, v, ll, kind, order, wl.eps, y=y, stream=stream)
+        elif form == "chunk2":
+            lion.lion_attn_chunk2(q, k, v, ll, kind, order, C, wl.eps, y=y, workspace=ws["chunk2"], stream=stream)
         elif form == "selectivity":
             lion.lion_selectivity(sel[0][s % nsets], sel[1], sel[2], k=k, k_out=y, stream=stream)
         elif form == "full_bwd":

@@ -112,6 +112,13 @@ hipError_t launch_chunk2(const AttnArgs &a, hipStream_t stream) {
     const Plan inner_plan = plan_chunk(inner_args(a));
     const C2Layout w = c2_layout(a, inner_plan.workspace);
     char *ws = reinterpret_cast<char *>(a.workspace);
+    if (a.kind == kMaskLit) {   // the mask is all ones in any order: the one-order form is the answer
+        AttnArgs b = a;
+        b.order = nullptr;
+        b.workspace = inner_plan.workspace ? ws + w.inner : nullptr;
+        b.workspace_bytes = inner_plan.workspace;
+        return launch_chunk(b, stream);
+    }
     const size_t rows = (size_t)a.B * a.H * a.L;
     const int esz = a.in_bf16 ? 2 : 4;
     const int pieces = a.d * esz / 16;
