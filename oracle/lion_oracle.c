@@ -660,7 +660,7 @@ int lion_oracle_full2_f64(const double *q, const double *k, const double *v, con
                           double *absnum, double *absden)
 {
     long bh, nbh = (long)B * H;
-    int err = 0, i;
+    int err = 0, t;
     char *seen;
     if (!q || !k || !v || !y || !order || B < 1 || H < 1 || L < 1 || d < 1 || !(eps >= 0.0) ||
         mask_kind < ORACLE_MASK_LIT || mask_kind > ORACLE_MASK_S || (mask_kind != ORACLE_MASK_LIT && !log_lambda))
@@ -668,11 +668,11 @@ int lion_oracle_full2_f64(const double *q, const double *k, const double *v, con
     seen = (char *)calloc((size_t)L, 1);
     if (!seen)
         return ORACLE_ENOMEM;
-    for (i = 0; i < L; ++i) {
-        if (order[i] < 0 || order[i] >= L || seen[order[i]])
+    for (t = 0; t < L; ++t) {
+        if (order[t] < 0 || order[t] >= L || seen[order[t]])
             err = 1;
         else
-            seen[order[i]] = 1;
+            seen[order[t]] = 1;
     }
     free(seen);
     if (err)
@@ -690,7 +690,7 @@ int lion_oracle_full2_f64(const double *q, const double *k, const double *v, con
         long *pos = (long *)malloc(sizeof(long) * (size_t)L);
         double *num = (double *)malloc(sizeof(double) * (size_t)d);
         double *anum = (double *)malloc(sizeof(double) * (size_t)d);
-        int j, p;
+        int i, j, p;   /* private to this (batch, head) */
         if (!phq || !phk || !lam || !lamc || !mb || !mc || !m || !pos || !num || !anum) {
             err |= 1;
         } else {
