@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     MASK_D,
     MASK_LIT,
     MASK_S,
+    LionArgumentError,
     LionError,
     lion_attn_abi_version,
     lion_attn_birnn,
