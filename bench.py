@@ -1,18 +1,28 @@
 """Throughput of LION bidirectional masked linear attention (forward) on one MI355X.
 
-One step = one forward pass of every form the workload is quoted with (for the default ViT-Tiny
-shaped LION-LIT workload: the full and the chunkwise form) over one batch of the workload's
-synthetic inputs; each form writes the attention output of all B x L tokens (every head).  The
-timed region runs the K steps form by form: K back-to-back launches of each form between one pair
-of HIP events on the launch stream, so each form's average launch duration is its events' span / K.  Input sets are rotated so that more than --rotate-gib of distinct buffers
-stream through HBM: the 256 MB last-level cache cannot hold them, so kernels read HBM, not cache.
+Default workload: the high-resolution LION-D inference shape (a 1024 x 1024 image in 16-pixel patches
+plus the class token: B8 H12 L4097 d64, bf16), the largest configuration that fits one GPU, with every
+form it is quoted with: the chunkwise form at C = 64, 128 and 256, the bidirectional RNN, and the full
+form as the memory-bound reference.  Form keys: ``full``, ``chunk<C>`` (``chunk`` alone means the
+workload's chunk sizes, or --chunk), ``birnn``; and, off the default, ``full_bwd``, ``chunk_bwd<C>``,
+``selectivity``, ``full2``, ``chunk2_<C>``.
 
-Prints one JSON line.  ``value`` is form-tokens per second: forms x B x L tokens per step over the
-step time (the harmonic mean of the per-form rates, which ``forms`` lists one by one).  After the timed
-region each form is launched K more times, each launch between its own pair of events, for the spread
-of single-launch durations (``forms[f]["launch_us"]``: p10, median, p90).
-``roofline`` is for the kernel that takes the largest share of the step; ``cpu_baseline`` times
-the fp64 oracle on the host for the same workload.
+One step = one call of every form over one batch of the workload's synthetic inputs; each call writes
+the attention output of all B x L tokens (every head).  The timed region runs the K steps form by form:
+K back-to-back calls of each form between one pair of HIP events on the launch stream, so each form's
+average call duration is its events' span / K.  Input sets are rotated so that more than --rotate-gib
+of distinct buffers stream through HBM: the 256 MB last-level cache cannot hold them, so kernels read
+HBM, not cache.
+
+Prints one JSON line:
+  value         tokens/s (B x L per call) of the fastest forward form of the step -- the form a user
+                would run this workload with (``config.value_form`` names it; the pages find the
+                chunkwise form the fastest at inference).  Each form's own rate is in ``forms``.
+  ms_per_step   the step (every form once); ``step_tokens_per_s`` = B x L / ms_per_step.
+  forms         per form: tokens/s, average call time, algorithmic GB/s and TFLOP/s, the binding roof
+                and the fraction of it, memory (inputs + output + workspace), single-call spread.
+  roofline      for the form with the largest share of the step (the dominant kernel).
+  cpu_baseline  the fp64 oracle on the host, on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -39,6 +49,43 @@ KERNEL_FILES = {"full": "lion_full.hip", "chunk": "lion_chunk.hip", "birnn": "li
                 "full_bwd": "lion_full_bwd.hip", "chunk_bwd": "lion_chunk_bwd.hip", "selectivity": "lion_selectivity.hip",
                 "full2": "lion_full.hip", "chunk2": "lion_chunk2.hip"}
 SEL_WIDTH = 1024   # layer-input width of the selectivity prologue (the BERT-Large-shaped recipe)
+FORWARD_FORMS = ("full", "chunk", "birnn", "full2", "chunk2")
+
+
+def split_form(key: str, default_c: int = 64):
+    """Form key -> (form, C): ``chunk128`` -> ("chunk", 128), ``chunk_bwd32``, ``chunk2_128`` (two orders);
+    chunkwise keys without a size take default_c (chunk_bwd: 32)."""
+    for form, pat in (("chunk2", r"chunk2(?:_(\d+))?"), ("chunk_bwd", r"chunk_bwd(\d*)"), ("chunk", r"chunk(\d*)")):
+        m = re.fullmatch(pat, key)
+        if m:
+            c = m.group(1)
+            return form, int(c) if c else (32 if form == "chunk_bwd" else default_c)
+    if key in ("full", "full2", "full_bwd", "birnn", "selectivity"):
+        return key, default_c
+    raise SystemExit(f"bench.py: unknown form key {key!r}")
+
+
+def default_forms(wl, chunk=None):
+    """The workload's forms, the chunkwise one at each of its chunk sizes (or at ``chunk``); the
+    4097-token workload adds the full form as the memory-bound reference."""
+    keys = []
+    for f in wl.forms:
+        if f == "chunk":
+            keys += [f"chunk{c}" for c in ((chunk,) if chunk else wl.chunks)]
+        else:
+            keys.append(f)
+    if wl.L > 2048 and "full" not in keys:
+        keys.append("full")
+    return keys
+
+
+def memory_bytes(form: str, wl, C: int, workspace_bytes: int) -> dict:
+    """Device memory a call touches: inputs, output and workspace (the full form never forms the L x L
+    score or mask matrix; the pages' PyTorch full form does)."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    io = 4 * wl.B * wl.H * wl.L * wl.d * esz
+    io += {0: 0, 1: 4 * wl.H, 2: 4 * wl.B * wl.H * wl.L}[wl.kind]
+    return {"io_MB": io / 1e6, "workspace_MB": workspace_bytes / 1e6, "total_MB": (io + workspace_bytes) / 1e6}
 
 
 def parse_args():
@@ -46,15 +93,18 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="vit_tiny_lit")
+    ap.add_argument("--workload", default="hires_d")
     ap.add_argument("--forms", default=None,
-                    help="comma-separated forms (default: the workload's); full_bwd times the full form's backward "
-                         "pass (bf16 gradients; y, den and a random dy prepared beforehand), chunk_bwd the same "
-                         "gradients computed chunkwise (chunks of --chunk tokens, default 32, at most 64); selectivity times "
-                         "the LION-S prologue (log lambda from a [B, L, 1024] layer input, keys scaled); full2 the full "
-                         "form with the masks of the raster and the column-major patch order averaged (image "
-                         "workloads: L = 1 + n^2), chunk2 the same averaged masks in the chunkwise form")
-    ap.add_argument("--chunk", type=int, default=None, help="chunk size C (default: the workload's first)")
+                    help="comma-separated form keys (default: the workload's forms, the chunkwise form at each of "
+                         "its chunk sizes; the 4097-token workload adds the full form as a reference): full, "
+                         "chunk<C>, birnn; full_bwd (the full form's backward pass, bf16 gradients; y, den and a "
+                         "random dy prepared beforehand), chunk_bwd<C> (the same gradients computed chunkwise, C "
+                         "<= 64, default 32), selectivity (the LION-S prologue: log lambda from a [B, L, 1024] "
+                         "layer input, keys scaled), full2 / chunk2 (the masks of the raster and the "
+                         "column-major patch order averaged; image workloads, L = 1 + n^2; the chunkwise one is keyed "
+                         "chunk2_<C>)")
+    ap.add_argument("--chunk", type=int, default=None,
+                    help="chunk size C for form keys given without one (default: the workload's chunk sizes)")
     ap.add_argument("--causal", action="store_true",
                     help="the causal variant (keys after the query masked out) of the workload's mask")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
@@ -192,9 +242,11 @@ def peak_of(bound: str):
             "alu": (VALU_FP32_PEAK_TFLOPS, "TFLOP/s")}[bound]
 
 
-def read_traffic(form: str, workload: str, causal: bool = False):
-    """HBM bytes per launch from a committed counter summary, if it was taken on this kernel."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{form}_{workload}{'_causal' if causal else ''}.txt")
+def read_traffic(key: str, workload: str, causal: bool = False):
+    """HBM bytes per call of form key ``key`` from a committed counter summary, if it was taken on
+    the current kernel source."""
+    form = split_form(key)[0]
+    path = os.path.join(ROOT, "profiles", f"traffic_{key}_{workload}{'_causal' if causal else ''}.txt")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -249,20 +301,27 @@ def main():
     from bidirectional_linear_attention_lion_amd import inputs as lin
 
     wl = lin.WORKLOADS[args.workload]
-    C = args.chunk or wl.chunks[0]
-    CB = min(args.chunk, 64) if args.chunk else 32   # the chunkwise backward's chunk size
-
-    def form_c(f):
-        return CB if f == "chunk_bwd" else C
+    keys = default_forms(wl, args.chunk) if args.forms is None else [f for f in args.forms.split(",") if f]
+    if args.forms is not None and args.chunk is None:
+        # a key without a size takes each of the workload's chunk sizes
+        expanded = []
+        for key in keys:
+            form, c = split_form(key)
+            if form == "chunk" and key == form:
+                expanded += [f"chunk{cc}" for cc in wl.chunks]
+            elif form == "chunk2" and key == form:
+                expanded += [f"chunk2_{cc}" for cc in wl.chunks]
+            else:
+                expanded.append(key)
+        keys = expanded
+    spec = {key: split_form(key, args.chunk or wl.chunks[0]) for key in keys}
     causal = args.causal
     kind = wl.kind | (lion.CAUSAL if causal else 0)
-    forms = list(wl.forms) if args.forms is None else [f for f in args.forms.split(",") if f]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
     inp = lin.make_inputs(wl)
-    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
     def to_dev(a):
         if a.dtype == np.uint16:
@@ -275,9 +334,9 @@ def main():
     nsets = max(2, int(np.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
     sets = [(q0.clone(), k0.clone(), v0.clone(), torch.empty_like(q0)) for _ in range(nsets)]
     del q0, k0, v0
-    ws = {}
+    forms_used = {f for f, _ in spec.values()}
     bwd_sets = []
-    if "full_bwd" in forms or "chunk_bwd" in forms:
+    if forms_used & {"full_bwd", "chunk_bwd"}:
         if wl.dtype != "bf16":
             raise SystemExit("bench.py: full_bwd and chunk_bwd need bf16 inputs")
         gen = torch.Generator(device=dev)
@@ -291,13 +350,13 @@ def main():
                 (wl.H,) if wl.kind == 1 else (wl.B, wl.H, wl.L), dtype=torch.float32, device=dev)
             bwd_sets.append((yb, den, dy, grads, dll))
     order = None
-    if "full2" in forms or "chunk2" in forms:
+    if forms_used & {"full2", "chunk2"}:
         side = int(round((wl.L - 1) ** 0.5))
         if side * side + 1 != wl.L:
             raise SystemExit("bench.py: full2 and chunk2 need an image workload (L = 1 + n^2)")
         order = torch.from_numpy(lin.column_major_order(side, side)).to(dev)
     sel = None
-    if "selectivity" in forms:
+    if "selectivity" in forms_used:
         if wl.dtype != "bf16":
             raise SystemExit("bench.py: selectivity needs bf16 inputs")
         gen = torch.Generator(device=dev)
@@ -307,108 +366,121 @@ def main():
         ws_ = (torch.randn((wl.H, SEL_WIDTH), generator=gen, device=dev) / SEL_WIDTH ** 0.5).to(torch.bfloat16)
         bs = torch.full((wl.H,), 3.0, dtype=torch.float32, device=dev)
         sel = (xs, ws_, bs)
-    for f, form_id in (("chunk", lion.FORM_CHUNK), ("birnn", lion.FORM_BIRNN), ("full_bwd", lion.FORM_FULL_BWD),
-                       ("chunk_bwd", lion.FORM_CHUNK_BWD), ("chunk2", lion.FORM_CHUNK2)):
-        if f not in forms:
-            continue
-        cf = CB if f == "chunk_bwd" else C
-        nb = lion.lion_attn_workspace_bytes(form_id, wl.B, wl.H, wl.L, wl.d, cf, 1 if wl.dtype == "bf16" else 0)
-        ws[f] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    form_ids = {"chunk": lion.FORM_CHUNK, "birnn": lion.FORM_BIRNN, "full_bwd": lion.FORM_FULL_BWD,
+                "chunk_bwd": lion.FORM_CHUNK_BWD, "chunk2": lion.FORM_CHUNK2}
+    ws, ws_bytes = {}, {}
+    for key, (f, C) in spec.items():
+        nb = 0
+        if f in form_ids:
+            nb = lion.lion_attn_workspace_bytes(form_ids[f], wl.B, wl.H, wl.L, wl.d, C,
+                                                1 if wl.dtype == "bf16" else 0)
+            if nb == (1 << 64) - 1:
+                raise SystemExit(f"bench.py: form {key} does not support this workload")
+            ws[key] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+        ws_bytes[key] = nb
 
-    def call(form, s):
+    def call(key, s):
+        f, C = spec[key]
         q, k, v, y = sets[s % nsets]
-        if form == "full":
+        if f == "full":
             lion.lion_attn_full(q, k, v, ll, kind, wl.eps, y=y, stream=stream)
-        elif form == "full2":
+        elif f == "full2":
             lion.lion_attn_full2(q, k, v, ll, kind, order, wl.eps, y=y, stream=stream)
-        elif form == "chunk2":
-            lion.lion_attn_chunk2(q, k, v, ll, kind, order, C, wl.eps, y=y, workspace=ws["chunk2"], stream=stream)
-        elif form == "selectivity":
+        elif f == "chunk2":
+            lion.lion_attn_chunk2(q, k, v, ll, kind, order, C, wl.eps, y=y, workspace=ws[key], stream=stream)
+        elif f == "selectivity":
             lion.lion_selectivity(sel[0][s % nsets], sel[1], sel[2], k=k, k_out=y, stream=stream)
-        elif form == "full_bwd":
+        elif f == "full_bwd":
             yb, den, dy, (dq, dk, dv), dll = bwd_sets[s % nsets]
             lion.lion_attn_full_bwd(q, k, v, ll, kind, yb, den, dy, dq=dq, dk=dk, dv=dv, dlog_lambda=dll,
-                                    workspace=ws["full_bwd"], stream=stream)
-        elif form == "chunk_bwd":
+                                    workspace=ws[key], stream=stream)
+        elif f == "chunk_bwd":
             yb, den, dy, (dq, dk, dv), dll = bwd_sets[s % nsets]
-            lion.lion_attn_chunk_bwd(q, k, v, ll, kind, CB, yb, den, dy, dq=dq, dk=dk, dv=dv,
-                                     dlog_lambda=dll, workspace=ws["chunk_bwd"], stream=stream)
-        elif form == "chunk":
-            lion.lion_attn_chunk(q, k, v, ll, kind, C, wl.eps, y=y, workspace=ws["chunk"], stream=stream)
+            lion.lion_attn_chunk_bwd(q, k, v, ll, kind, C, yb, den, dy, dq=dq, dk=dk, dv=dv,
+                                     dlog_lambda=dll, workspace=ws[key], stream=stream)
+        elif f == "chunk":
+            lion.lion_attn_chunk(q, k, v, ll, kind, C, wl.eps, y=y, workspace=ws[key], stream=stream)
         else:
-            lion.lion_attn_birnn(q, k, v, ll, kind, wl.eps, y=y, workspace=ws["birnn"], stream=stream)
+            lion.lion_attn_birnn(q, k, v, ll, kind, wl.eps, y=y, workspace=ws[key], stream=stream)
 
     for s in range(args.warmup):
-        for f in forms:
-            call(f, s)
+        for key in keys:
+            call(key, s)
     torch.cuda.synchronize()
 
-    ev = {f: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for f in forms}
+    ev = {key: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for key in keys}
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     # Hold the GPU in a spin kernel while the host enqueues every timed launch, so the kernels then run
     # back to back and the events bracket kernel execution, not host submission time.
-    host_s = host_seconds_per_call(call, forms, args.warmup)
-    sleep_cycles = spin_cycles_for(1.5 * host_s * len(forms) * args.steps + 2e-3)
+    host_s = host_seconds_per_call(call, keys, args.warmup)
+    sleep_cycles = spin_cycles_for(1.5 * host_s * len(keys) * args.steps + 2e-3)
     torch.cuda.synchronize()
     torch.cuda._sleep(sleep_cycles)
     t_start.record(stream)
-    for f in forms:
-        ev[f][0].record(stream)
+    for key in keys:
+        ev[key][0].record(stream)
         for s in range(args.steps):
-            call(f, args.warmup + 5 + s)
-        ev[f][1].record(stream)
+            call(key, args.warmup + 5 + s)
+        ev[key][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    print(f"bench.py: timed {args.steps} steps of {','.join(keys)} on {wl.name}: {ms_per_step:.4f} ms/step",
+          file=sys.stderr, flush=True)
 
-    # per-launch spread (outside the timed region): each launch between its own pair of events
+    # per-call spread (outside the timed region): each call between its own pair of events
     spread = {}
-    for f in forms:
+    for key in keys:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         torch.cuda.synchronize()
         for s, (e0, e1) in enumerate(evs):
             e0.record(stream)
-            call(f, args.warmup + 5 + args.steps + s)
+            call(key, args.warmup + 5 + args.steps + s)
             e1.record(stream)
         torch.cuda.synchronize()
         us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
-        spread[f] = {"p10": float(np.percentile(us, 10)), "p50": float(np.median(us)), "p90": float(np.percentile(us, 90))}
+        spread[key] = {"p10": float(np.percentile(us, 10)), "p50": float(np.median(us)),
+                       "p90": float(np.percentile(us, 90))}
 
     tokens = wl.B * wl.L
     per_form = {}
-    for f in forms:
-        avg = ev[f][0].elapsed_time(ev[f][1]) / args.steps
-        nbytes, flops = algorithmic(f, wl, form_c(f), causal)
-        per_form[f] = {
+    for key in keys:
+        f, C = spec[key]
+        avg = ev[key][0].elapsed_time(ev[key][1]) / args.steps
+        nbytes, flops = algorithmic(f, wl, C, causal)
+        bound = bound_of(f, wl, C, causal)
+        pk, _ = peak_of(bound)
+        gbps, tflops = nbytes / (avg * 1e-3) / 1e9, flops / (avg * 1e-3) / 1e12
+        per_form[key] = {
             "tokens_per_s": tokens / (avg * 1e-3),
             "ms_avg": avg,
-            "alg_GBps": nbytes / (avg * 1e-3) / 1e9,
-            "alg_TFLOPs": flops / (avg * 1e-3) / 1e12,
-            "bound": bound_of(f, wl, form_c(f), causal),
+            "alg_GBps": gbps,
+            "alg_TFLOPs": tflops,
+            "bound": bound,
+            "frac_of_roof": (gbps if bound == "hbm" else tflops) / pk,
+            "frac_hbm": gbps / HBM_PEAK_GBS,
+            "frac_mfma_bf16": tflops / MFMA_BF16_PEAK_TFLOPS if f not in ("birnn", "chunk_bwd") else None,
+            "memory": memory_bytes(f, wl, C, ws_bytes[key]),
+            "launch_us": spread[key],
         }
-        if f == "chunk":
-            per_form[f]["C"] = C
-        elif f == "chunk_bwd":
-            per_form[f]["C"] = CB
-        per_form[f]["launch_us"] = spread[f]
-    dom = max(forms, key=lambda f: per_form[f]["ms_avg"])
-    nbytes, flops = algorithmic(dom, wl, form_c(dom), causal)
+        if f in ("chunk", "chunk2", "chunk_bwd"):
+            per_form[key]["C"] = C
+    fwd = [key for key in keys if spec[key][0] in FORWARD_FORMS] or keys
+    best = max(fwd, key=lambda key: per_form[key]["tokens_per_s"])
+    dom = max(keys, key=lambda key: per_form[key]["ms_avg"])
+    f_dom, c_dom = spec[dom]
+    nbytes, flops = algorithmic(f_dom, wl, c_dom, causal)
     avg_s = per_form[dom]["ms_avg"] * 1e-3
-    dom_bound = bound_of(dom, wl, form_c(dom), causal)
+    dom_bound = per_form[dom]["bound"]
     peak, unit = peak_of(dom_bound)
     achieved = nbytes / avg_s / 1e9 if dom_bound == "hbm" else flops / avg_s / 1e12
     traffic = read_traffic(dom, wl.name, causal)
-    for f in forms:
-        pf = per_form[f]
-        pk, _ = peak_of(pf["bound"])
-        pf["frac_of_roof"] = (pf["alg_GBps"] if pf["bound"] == "hbm" else pf["alg_TFLOPs"]) / pk
-        pf["frac_mfma_bf16"] = pf["alg_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS if f != "birnn" else None
 
     out = {
         "metric": METRIC,
-        "value": len(forms) * tokens / (ms_per_step * 1e-3),
+        "value": per_form[best]["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -420,12 +492,12 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "L": wl.L, "d": wl.d,
-                   "mask": lin.KIND_NAME[wl.kind] + ("+causal" if causal else ""), "forms": forms, "C": C, "input_sets": nsets,
-                   "host_us_per_launch": host_s * 1e6},
+                   "mask": lin.KIND_NAME[wl.kind] + ("+causal" if causal else ""), "forms": keys,
+                   "value_form": best, "input_sets": nsets, "host_us_per_launch": host_s * 1e6},
+        "step_tokens_per_s": tokens / (ms_per_step * 1e-3),
         "forms": per_form,
         "roofline": {"bound": dom_bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
-                     "frac": achieved / peak,
-                     "traffic": traffic},
+                     "frac": achieved / peak, "traffic": traffic},
     }
     if args.cpu_baseline_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_baseline_seconds, causal)

@@ -87,3 +87,32 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_form_keys_and_default_forms():
+    assert bench.split_form("chunk128") == ("chunk", 128)
+    assert bench.split_form("chunk", 64) == ("chunk", 64)
+    assert bench.split_form("chunk_bwd") == ("chunk_bwd", 32)
+    assert bench.split_form("birnn") == ("birnn", 64)
+    with pytest.raises(SystemExit):
+        bench.split_form("birnn64")
+    with pytest.raises(SystemExit):
+        bench.split_form("attention")
+    # the 4097-token workload: the chunkwise form at each chunk size, the RNN, the full form as reference
+    assert bench.default_forms(lin.WORKLOADS["hires_d"]) == ["chunk64", "chunk128", "chunk256", "birnn", "full"]
+    assert bench.default_forms(lin.WORKLOADS["vit_tiny_lit"]) == ["full", "chunk64"]
+    assert bench.default_forms(lin.WORKLOADS["hires_d"], chunk=128) == ["chunk128", "birnn", "full"]
+
+
+def test_memory_counts_inputs_output_and_workspace():
+    wl = lin.WORKLOADS["hires_d"]
+    m = bench.memory_bytes("chunk", wl, 128, 1_000_000)
+    io = 4 * 8 * 12 * 4097 * 64 * 2 + 4 * 12
+    assert m["io_MB"] == io / 1e6 and m["workspace_MB"] == 1.0 and m["total_MB"] == (io + 1e6) / 1e6
+
+
+def test_two_order_chunk_keys_do_not_swallow_the_chunk_size():
+    assert bench.split_form("chunk256") == ("chunk", 256)
+    assert bench.split_form("chunk2_128") == ("chunk2", 128)
+    assert bench.split_form("chunk2", 64) == ("chunk2", 64)
+    assert bench.split_form("chunk_bwd64") == ("chunk_bwd", 64)
