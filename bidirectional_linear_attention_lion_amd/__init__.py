@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     lion_attn_full_bwd,
     lion_attn_chunk_bwd,
     lion_attn_chunk2,
+    lion_attn_chunk_noalloc,
     lion_attn_workspace_bytes,
     lion_selectivity,
     lion_status_str,

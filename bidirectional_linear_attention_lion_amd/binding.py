@@ -46,9 +46,10 @@ def library() -> ctypes.CDLL:
     lib.lion_selectivity.argtypes = [vp, vp, fp, i, i, i, i, fp, fp, vp, vp, i, vp]
     lib.lion_attn_full2.argtypes = common + [f, vp, i, i, i, i, i, vp, i, fp, vp]
     lib.lion_attn_chunk2.argtypes = common + [i, f, vp, i, i, i, i, i, vp, i, fp, vp, sz, vp]
+    lib.lion_attn_chunk_noalloc.argtypes = common + [i, f, i, i, i, i, i, vp, i, fp, vp]
     for fn in ("lion_attn_full", "lion_attn_chunk", "lion_attn_birnn", "lion_attn_full_bwd", "lion_attn_chunk_bwd",
                "lion_selectivity",
-               "lion_attn_full2", "lion_attn_chunk2", "lion_attn_abi_version"):
+               "lion_attn_full2", "lion_attn_chunk2", "lion_attn_chunk_noalloc", "lion_attn_abi_version"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.lion_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.lion_attn_workspace_bytes.restype = sz
@@ -243,6 +244,17 @@ def lion_attn_chunk(q, k, v, log_lambda, mask_kind, C: int = 64, eps: float = 1e
     ws, nbytes = _workspace(FORM_CHUNK, B, H, L, d, int(C), dt, workspace, q.device)
     _call("lion_attn_chunk", _ptr(q), _ptr(k), _ptr(v), _ptr(log_lambda), kind, int(C), float(eps), B, H, L,
           d, dt, _ptr(y), ydt, _ptr(den_out), _ptr(ws), nbytes, sptr)
+    return y
+
+
+def lion_attn_chunk_noalloc(q, k, v, log_lambda, mask_kind, C: int = 64, eps: float = 1e-6, *, y=None, y_dtype=None,
+                            den_out=None, stream=None):
+    """Chunkwise form whose scratch is the library's built-in per-GPU array (no workspace argument; the
+    library allocates nothing).  Pass ``y`` to allocate nothing here either; calls overlapping in time on
+    one GPU race for the array."""
+    kind, B, H, L, d, dt, y, ydt, sptr = _prepare(q, k, v, log_lambda, mask_kind, y, y_dtype, den_out, stream)
+    _call("lion_attn_chunk_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(log_lambda), kind, int(C), float(eps), B, H, L,
+          d, dt, _ptr(y), ydt, _ptr(den_out), sptr)
     return y
 
 

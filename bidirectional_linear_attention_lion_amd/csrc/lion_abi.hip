@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "lion_attn.h"
 #include "lion_internal.h"
 
@@ -131,6 +133,65 @@ int lion_attn_chunk2(const void *q, const void *k, const void *v, const float *l
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
     return status_of(lion::launch_chunk2(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of lion_attn_chunk_noalloc: one copy per GPU, allocated with the code object and held until
+// the process ends.  In host code `scratch` names a host-side stand-in; the device address of each
+// GPU's copy comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kNoallocScratchBytes = LION_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void *scratch_ptr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device (nullptr and an error if it cannot be had).
+void *device_scratch(int *status) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *status = LION_ERR_HIP;
+        return nullptr;
+    }
+    std::call_once(scratch_once[dev], [dev] {
+        void *ptr = nullptr;
+        scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    if (scratch_err[dev] != hipSuccess || !scratch_ptr[dev]) {
+        *status = LION_ERR_HIP;
+        return nullptr;
+    }
+    *status = LION_OK;
+    return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int lion_attn_chunk_noalloc(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, int C,
+                            float eps, int B, int H, int L, int d, int dtype, void *y, int y_dtype, float *den_out,
+                            void *stream) {
+    int rc = check_common(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    if (rc != LION_OK) return rc;
+    if (C < 1) return LION_ERR_INVALID;
+    if (!c_supported_for(C, d)) return LION_ERR_UNSUPPORTED;
+    lion::AttnArgs a = make_args(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
+    a.C = C;
+    const lion::Plan plan = lion::plan_chunk(a);
+    if (!plan.ok) return LION_ERR_UNSUPPORTED;
+    if (plan.workspace > kNoallocScratchBytes) return LION_ERR_WORKSPACE;   // beyond the built-in scratch
+    if (plan.workspace > 0) {
+        a.workspace = device_scratch(&rc);
+        if (rc != LION_OK) return rc;
+        a.workspace_bytes = kNoallocScratchBytes;
+    }
+    return status_of(lion::launch_chunk(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int lion_attn_birnn(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind, float eps,

@@ -51,8 +51,9 @@
  * fp32 inputs keep every step in fp32.  Row sums (denominators) are accumulated in fp32.
  *
  * Ownership and threading: the caller allocates and owns every buffer, workspace included.  The
- * library allocates and frees nothing, never synchronises, keeps no mutable global state and is
- * reentrant.  All work is enqueued on `stream`; outputs are valid once the stream reaches that
+ * library allocates and frees nothing, never synchronises, and is reentrant; its one piece of global
+ * state is the scratch array of lion_attn_chunk_noalloc (one copy per GPU) and that array's per-device
+ * address.  All work is enqueued on `stream`; outputs are valid once the stream reaches that
  * point.  Input buffers are only read; y, den_out and the workspace are written.
  *
  * Errors: every entry point returns LION_OK (0) or a negative status.  Argument errors are found
@@ -144,6 +145,23 @@ LION_API int lion_attn_chunk(const void *q, const void *k, const void *v, const 
 LION_API int lion_attn_chunk2(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind,
                               int C, float eps, const int *order, int B, int H, int L, int d, int dtype, void *y,
                               int y_dtype, float *den_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Chunkwise form without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * kernels and results as lion_attn_chunk; the scratch lion_attn_chunk would take from the caller's
+ * workspace comes instead from a file-scope device array of LION_NOALLOC_SCRATCH_BYTES held by each GPU
+ * the library runs on until the process ends.  The call allocates and frees nothing (its first call on
+ * a device looks up that device's copy of the array).
+ *   Sizes whose workspace (lion_attn_workspace_bytes(LION_FORM_CHUNK, ...)) exceeds
+ *   LION_NOALLOC_SCRATCH_BYTES return LION_ERR_WORKSPACE before any HIP call.
+ *   Calls on one GPU share its array: calls that overlap in time on one GPU (other streams, other host
+ *   threads) race and give unspecified results; calls ordered on one stream are safe.  The chunkwise
+ *   kernels read nothing of the scratch they did not write in the same call.
+ * Errors as for lion_attn_chunk; LION_ERR_HIP also when the device copy of the array cannot be found. */
+#define LION_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+LION_API int lion_attn_chunk_noalloc(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind,
+                                     int C, float eps, int B, int H, int L, int d, int dtype, void *y, int y_dtype,
+                                     float *den_out, void *stream);
 
 /* Bidirectional RNN form: a forward and a backward recurrence over tokens with d x d matrix
  * states, S_i = lambda_i S_{i-1} + phi(k_i) v_i^T (backward: S_i = lambda_{i+1} S_{i+1} + ...),

@@ -33,6 +33,7 @@ def test_library_exports_every_declared_symbol():
     names = header_symbols()
     assert set(names) == {"lion_attn_full", "lion_attn_full2", "lion_attn_chunk", "lion_attn_birnn",
                           "lion_attn_full_bwd", "lion_attn_chunk_bwd", "lion_attn_chunk2", "lion_selectivity", "lion_attn_workspace_bytes",
+                          "lion_attn_chunk_noalloc",
                           "lion_status_str", "lion_attn_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -81,16 +82,42 @@ UNSUPPORTED_CASES = [("d=48", dict(d=48)), ("d=256", dict(d=256)), ("d=8", dict(
                      ("f32 in, bf16 out", dict(dt=0, ydt=1))]
 
 
+def chunk_noalloc(C=64, **kw):
+    a = dict(q=P, k=P, v=P, ll=None, kind=0, eps=1e-6, B=2, H=3, L=17, d=64, dt=1, y=P, ydt=1, den=None)
+    a.update(kw)
+    return lion.library().lion_attn_chunk_noalloc(a["q"], a["k"], a["v"], a["ll"], a["kind"], C, a["eps"], a["B"],
+                                                  a["H"], a["L"], a["d"], a["dt"], a["y"], a["ydt"], a["den"], None)
+
+
+ENTRIES = [full, chunk, birnn, chunk_noalloc]
+ENTRY_IDS = ["full", "chunk", "birnn", "chunk_noalloc"]
+
+
 @pytest.mark.parametrize("name,kw", INVALID_CASES, ids=[c[0] for c in INVALID_CASES])
-@pytest.mark.parametrize("entry", [full, chunk, birnn], ids=["full", "chunk", "birnn"])
+@pytest.mark.parametrize("entry", ENTRIES, ids=ENTRY_IDS)
 def test_invalid_arguments(entry, name, kw):
     assert entry(**kw) == INVALID
 
 
 @pytest.mark.parametrize("name,kw", UNSUPPORTED_CASES, ids=[c[0] for c in UNSUPPORTED_CASES])
-@pytest.mark.parametrize("entry", [full, chunk, birnn], ids=["full", "chunk", "birnn"])
+@pytest.mark.parametrize("entry", ENTRIES, ids=ENTRY_IDS)
 def test_unsupported_combinations(entry, name, kw):
     assert entry(**kw) == UNSUPPORTED
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    """The no-allocation chunkwise entry point serves sizes whose workspace fits its built-in array and
+    rejects larger ones (before any HIP call) with LION_ERR_WORKSPACE."""
+    cap = 64 << 20
+    sizes = [(8, 12, 4097, 16), (8, 12, 4097, 32), (64, 12, 197, 16), (32, 16, 512, 16), (16, 12, 4097, 64)]
+    seen_reject = False
+    for (B, H, L, C) in sizes:
+        need = lion.lion_attn_workspace_bytes(lion.FORM_CHUNK, B, H, L, 64, C, 1)
+        if need > cap:
+            seen_reject = True
+            assert chunk_noalloc(C=C, B=B, H=H, L=L, kind=1, ll=P) == WORKSPACE, (B, H, L, C)
+    assert seen_reject
+    assert chunk_noalloc(C=48) == UNSUPPORTED and chunk_noalloc(C=0) == INVALID
 
 
 @pytest.mark.parametrize("C,status", [(0, INVALID), (-64, INVALID), (48, UNSUPPORTED), (512, UNSUPPORTED),
