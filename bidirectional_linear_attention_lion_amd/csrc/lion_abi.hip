@@ -318,8 +318,8 @@ size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, in
     if (B < 1 || H < 1 || L < 1 || !d_supported(d) || (long long)L > kMaxL || (long long)B * H * L > kMaxRows)
         return (size_t)-1;
     if (dtype != LION_DTYPE_F32 && dtype != LION_DTYPE_BF16) return (size_t)-1;
-    // the plans depend on sizes, dtype and (for the full form's LDS) the mask kind; LION-S is the
-    // largest of the kinds, so it answers for all of them
+    // the plans depend on sizes, dtype and the mask kind: LION-S is the largest of the kinds for the
+    // full and chunkwise forms (LDS), and the RNN form's answer is the largest over the kinds
     lion::AttnArgs a = make_args(nullptr, nullptr, nullptr, nullptr, LION_MASK_S, 0.f, B, H, L, d, dtype, nullptr,
                                  dtype, nullptr);
     lion::Plan plan;
@@ -330,7 +330,16 @@ size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, in
         a.C = C;
         plan = lion::plan_chunk(a);
         break;
-    case LION_FORM_BIRNN: plan = lion::plan_birnn(a); break;
+    case LION_FORM_BIRNN: {
+        plan = lion::plan_birnn(a);
+        for (int kind : {LION_MASK_LIT, LION_MASK_D}) {
+            a.kind = kind;
+            const lion::Plan pk = lion::plan_birnn(a);
+            plan.ok = plan.ok && pk.ok;
+            if (pk.workspace > plan.workspace) plan.workspace = pk.workspace;
+        }
+        break;
+    }
     case LION_FORM_CHUNK2:
         if (!c_supported_for(C, d)) return (size_t)-1;
         a.C = C;

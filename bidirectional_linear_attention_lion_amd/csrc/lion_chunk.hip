@@ -238,37 +238,48 @@ __global__ void __launch_bounds__(state_waves(D) * 64) chunk_state_kernel(ChunkP
                 wf[t][e] = a;
                 wg[t][e] = b;
             }
-        bf16x8 kfr{};
-        if constexpr (BF16 && kColOwn) kfr = tr_frag<D>(Ks, h, wave, r, g);
+        // bf16: the fold weights multiply the key fragment (A operand), once per sub-block, rather than
+        // every value tile's B operand: A = bf16(w k) for the value tiles; the row-sum column takes
+        // A_hi + A_lo (the bf16 rounding of the remainder) against a column of ones, so the row sums keep
+        // ~2^-17 relative accuracy (a nearly cancelling denominator amplifies their error)
+        bf16x8 af_hi{}, af_lo{}, ag_hi{}, ag_lo{};
+        auto weighted = [&](const bf16x8 &kf, const float (&w)[2][4], bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = w[t][e] * (float)kf[4 * t + e];
+                    const __bf16 xh = f2bf(x);
+                    hi[4 * t + e] = xh;
+                    lo[4 * t + e] = f2bf(x - (float)xh);
+                }
+        };
+        if constexpr (BF16 && kColOwn) {
+            const bf16x8 kfr = tr_frag<D>(Ks, h, wave, r, g);
+            weighted(kfr, wf, af_hi, af_lo);
+            if (!p.causal) weighted(kfr, wg, ag_hi, ag_lo);
+        }
+        bf16x8 ones;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ones[e] = f2bf(r == 0 ? 1.f : 0.f);
 #pragma unroll
         for (int u = 0; u < MAXT; ++u) {
             int ct, nt;
             if (!tile_of(u, ct, nt)) break;
             if constexpr (BF16) {
-                const bf16x8 a = kColOwn ? kfr : tr_frag<D>(Ks, h, nt, r, g);
-                bf16x8 bf, bg;
+                if constexpr (!kColOwn) {
+                    const bf16x8 kfr = tr_frag<D>(Ks, h, nt, r, g);
+                    weighted(kfr, wf, af_hi, af_lo);
+                    if (!p.causal) weighted(kfr, wg, ag_hi, ag_lo);
+                }
                 if (ct < NDT) {
                     const bf16x8 vv = tr_frag<D>(Vs, h, ct, r, g);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        bf[e] = f2bf(wf[0][e] * (float)vv[e]);
-                        bf[4 + e] = f2bf(wf[1][e] * (float)vv[4 + e]);
-                        bg[e] = f2bf(wg[0][e] * (float)vv[e]);
-                        bg[4 + e] = f2bf(wg[1][e] * (float)vv[4 + e]);
-                    }
+                    sf[u] = mfma_bf16(af_hi, vv, sf[u]);
+                    if (!p.causal) sg[u] = mfma_bf16(ag_hi, vv, sg[u]);
                 } else {
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const __bf16 fh = f2bf(wf[t][e]), gh = f2bf(wg[t][e]);
-                            const __bf16 fl = f2bf(wf[t][e] - (float)fh), gl = f2bf(wg[t][e] - (float)gh);
-                            bf[4 * t + e] = r == 0 ? fh : (r == 1 ? fl : f2bf(0.f));
-                            bg[4 * t + e] = r == 0 ? gh : (r == 1 ? gl : f2bf(0.f));
-                        }
+                    sf[u] = mfma_bf16(af_lo, ones, mfma_bf16(af_hi, ones, sf[u]));
+                    if (!p.causal) sg[u] = mfma_bf16(ag_lo, ones, mfma_bf16(ag_hi, ones, sg[u]));
                 }
-                sf[u] = mfma_bf16(a, bf, sf[u]);
-                if (!p.causal) sg[u] = mfma_bf16(a, bg, sg[u]);
             } else {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
@@ -321,7 +332,8 @@ __global__ void __launch_bounds__(state_waves(D) * 64) chunk_state_kernel(ChunkP
 // ================================ scan kernel =========================================================
 // One thread per 16-byte vector of a slot, sequential over the chunks of its (batch, head): forward
 // states F_c = a_c F_{c-1} + Fl_c for c = 0 .. n-2, backward G_c = a_c G_{c+1} + Gl_c for c = n-1 .. 1,
-// each written over the local state of the same chunk.  Loads run kU chunks ahead.
+// each written over the local state of the same chunk.  Loads run kU chunks ahead (16 measured slower
+// than 4 on B8 H12 L4097, C = 128: 34 against 26 us).
 constexpr int kScanThreads = 256;
 constexpr int kU = 4;
 
@@ -631,11 +643,27 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
                 for (int e = 0; e < 4; ++e) {
                     float pe = sa[t][e];
                     if constexpr (KIND != kMaskLit) pe *= fast_exp2(-__builtin_fabsf(Ei[qt] - Ej[t][e]));
-                    if (partial) pe = j0 + 16 * t + 4 * g + e < cn ? pe : 0.f;
-                    if (p.causal && j0 + 16 * t + 4 * g + e > 16 * (wave + NW * qt) + r) pe = 0.f;
-                    den[qt] += pe;
                     pv[t][e] = pe;
                 }
+            // keys past the chunk's end, and (causal) keys after the query: both rare, so the masking is
+            // behind wave-uniform branches
+            if (partial) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pv[t][e] = j0 + 16 * t + 4 * g + e < cn ? pv[t][e] : 0.f;
+            }
+            if (p.causal && j0 + kKB - 1 > 16 * (wave + NW * qt)) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (j0 + 16 * t + 4 * g + e > 16 * (wave + NW * qt) + r) pv[t][e] = 0.f;
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) den[qt] += pv[t][e];
             if constexpr (BF16) {
                 bf16x8 pf;
 #pragma unroll
