@@ -107,6 +107,9 @@ def parse_args():
                     help="chunk size C for form keys given without one (default: the workload's chunk sizes)")
     ap.add_argument("--causal", action="store_true",
                     help="the causal variant (keys after the query masked out) of the workload's mask")
+    ap.add_argument("--fp32-arith", action="store_true",
+                    help="fp32 arithmetic throughout for the bf16 inputs (LION_FP32_ARITH; full and chunkwise "
+                         "forms), fp32 outputs")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0,
                     help="wall-time budget of the oracle sample (0 disables)")
@@ -317,6 +320,10 @@ def main():
     spec = {key: split_form(key, args.chunk or wl.chunks[0]) for key in keys}
     causal = args.causal
     kind = wl.kind | (lion.CAUSAL if causal else 0)
+    if args.fp32_arith:
+        if wl.dtype != "bf16" or any(f not in ("full", "chunk", "birnn") for f, _ in spec.values()):
+            raise SystemExit("bench.py: --fp32-arith applies to the full, chunkwise and RNN forms of bf16 workloads")
+        kind |= lion.FP32_ARITH
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -332,7 +339,8 @@ def main():
     ll = None if inp.log_lambda is None else torch.from_numpy(inp.log_lambda).to(dev)
     set_bytes = 4 * q0.numel() * q0.element_size()
     nsets = max(2, int(np.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
-    sets = [(q0.clone(), k0.clone(), v0.clone(), torch.empty_like(q0)) for _ in range(nsets)]
+    ydt = torch.float32 if args.fp32_arith else q0.dtype
+    sets = [(q0.clone(), k0.clone(), v0.clone(), torch.empty(q0.shape, dtype=ydt, device=dev)) for _ in range(nsets)]
     del q0, k0, v0
     forms_used = {f for f, _ in spec.values()}
     bwd_sets = []
@@ -492,7 +500,8 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "L": wl.L, "d": wl.d,
-                   "mask": lin.KIND_NAME[wl.kind] + ("+causal" if causal else ""), "forms": keys,
+                   "mask": lin.KIND_NAME[wl.kind] + ("+causal" if causal else "") + ("+fp32arith" if args.fp32_arith else ""),
+                   "forms": keys,
                    "value_form": best, "input_sets": nsets, "host_us_per_launch": host_s * 1e6},
         "step_tokens_per_s": tokens / (ms_per_step * 1e-3),
         "forms": per_form,

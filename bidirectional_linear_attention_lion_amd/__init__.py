@@ -6,6 +6,7 @@ no CPU fallback: if the library is missing, every call raises.
 """
 from .binding import (  # noqa: F401
     CAUSAL,
+    FP32_ARITH,
     FORM_BIRNN,
     FORM_CHUNK,
     FORM_FULL,

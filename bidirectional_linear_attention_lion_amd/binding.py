@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(PKG, "liblion_attn.so")
 
 MASK_LIT, MASK_D, MASK_S = 0, 1, 2
 CAUSAL = 4   # OR-ed into a mask kind: the causal (unidirectional) variant
+FP32_ARITH = 8   # OR-ed into a mask kind: fp32 arithmetic throughout for bf16 inputs (full and chunk forms)
 DTYPE_F32, DTYPE_BF16 = 0, 1
 FORM_FULL, FORM_CHUNK, FORM_BIRNN, FORM_FULL_BWD, FORM_CHUNK_BWD, FORM_CHUNK2 = 0, 1, 2, 3, 4, 5
 _KINDS = {"lit": MASK_LIT, "d": MASK_D, "s": MASK_S}
@@ -146,7 +147,7 @@ def _check_attn_inputs(q, k, v, log_lambda, kind):
     _tensor("q", q, (B, H, L, d), (q.dtype,))
     _tensor("k", k, (B, H, L, d), (q.dtype,), q.device)
     _tensor("v", v, (B, H, L, d), (q.dtype,), q.device)
-    if kind < 0 or (kind & ~(3 | CAUSAL)) or (kind & 3) == 3:
+    if kind < 0 or (kind & ~(3 | CAUSAL | FP32_ARITH)) or (kind & 3) == 3:
         raise LionArgumentError(f"unknown mask kind {kind}")
     want = _decay_shape(kind, B, H, L)
     if want is None:

@@ -28,7 +28,7 @@ int check_common(const void *q, const void *k, const void *v, const float *log_l
     if (!q || !k || !v || !y) return LION_ERR_INVALID;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y)) return LION_ERR_INVALID;
     if (den_out && !aligned16(den_out)) return LION_ERR_INVALID;
-    if (mask_kind & ~(3 | LION_CAUSAL)) return LION_ERR_INVALID;
+    if (mask_kind & ~(3 | LION_CAUSAL | LION_FP32_ARITH)) return LION_ERR_INVALID;
     const int kind = mask_kind & 3;
     if (kind != LION_MASK_LIT && kind != LION_MASK_D && kind != LION_MASK_S) return LION_ERR_INVALID;
     if (kind == LION_MASK_LIT ? log_lambda != nullptr : log_lambda == nullptr) return LION_ERR_INVALID;
@@ -58,6 +58,7 @@ lion::AttnArgs make_args(const void *q, const void *k, const void *v, const floa
     a.L = L;
     a.d = d;
     a.in_bf16 = dtype == LION_DTYPE_BF16;
+    a.fp32c = !a.in_bf16 || (mask_kind & LION_FP32_ARITH) != 0;
     a.y = y;
     a.out_bf16 = y_dtype == LION_DTYPE_BF16;
     a.den_out = den_out;
@@ -89,7 +90,7 @@ int lion_attn_full2(const void *q, const void *k, const void *v, const float *lo
     int rc = check_common(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
     if (rc != LION_OK) return rc;
     if (!order || !aligned16(order)) return LION_ERR_INVALID;
-    if (mask_kind & LION_CAUSAL) return LION_ERR_UNSUPPORTED;
+    if (mask_kind & (LION_CAUSAL | LION_FP32_ARITH)) return LION_ERR_UNSUPPORTED;
     lion::AttnArgs a = make_args(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
     a.order = order;
     if (!lion::plan_full(a).ok) return LION_ERR_UNSUPPORTED;
@@ -122,7 +123,7 @@ int lion_attn_chunk2(const void *q, const void *k, const void *v, const float *l
     if (!order || !aligned16(order)) return LION_ERR_INVALID;
     if (C < 1) return LION_ERR_INVALID;
     if (workspace && !aligned16(workspace)) return LION_ERR_INVALID;
-    if (mask_kind & LION_CAUSAL) return LION_ERR_UNSUPPORTED;
+    if (mask_kind & (LION_CAUSAL | LION_FP32_ARITH)) return LION_ERR_UNSUPPORTED;
     if (!c_supported_for(C, d)) return LION_ERR_UNSUPPORTED;
     lion::AttnArgs a = make_args(q, k, v, log_lambda, mask_kind, eps, B, H, L, d, dtype, y, y_dtype, den_out);
     a.C = C;
@@ -220,6 +221,7 @@ int bwd_args(const void *q, const void *k, const void *v, const float *log_lambd
     int rc = check_common(q, k, v, log_lambda, mask_kind, 0.f, B, H, L, d, dtype, y, dtype, nullptr);
     if (rc != LION_OK) return rc;
     if (!den || !dy || !dq || !dk || !dv) return LION_ERR_INVALID;
+    if (mask_kind & LION_FP32_ARITH) return LION_ERR_UNSUPPORTED;
     if (!aligned16(den) || !aligned16(dy) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return LION_ERR_INVALID;
     const int kind = mask_kind & 3;
     if (kind == LION_MASK_LIT ? dlog_lambda != nullptr : dlog_lambda == nullptr) return LION_ERR_INVALID;
@@ -325,11 +327,19 @@ size_t lion_attn_workspace_bytes(int form, int B, int H, int L, int d, int C, in
     lion::Plan plan;
     switch (form) {
     case LION_FORM_FULL: plan = lion::plan_full(a); break;
-    case LION_FORM_CHUNK:
+    case LION_FORM_CHUNK: {
         if (!c_supported_for(C, d)) return (size_t)-1;
         a.C = C;
         plan = lion::plan_chunk(a);
+        if (a.in_bf16) {   // bf16 inputs may ask for fp32 arithmetic, whose states are fp32
+            a.fp32c = true;
+            const lion::Plan pf = lion::plan_chunk(a);
+            plan.ok = plan.ok && pf.ok;
+            if (pf.workspace > plan.workspace) plan.workspace = pf.workspace;
+            a.fp32c = false;
+        }
         break;
+    }
     case LION_FORM_BIRNN: {
         plan = lion::plan_birnn(a);
         for (int kind : {LION_MASK_LIT, LION_MASK_D}) {

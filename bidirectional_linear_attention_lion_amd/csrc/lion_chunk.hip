@@ -158,8 +158,18 @@ __host__ __device__ size_t chunk_lds(int C, int nw, bool with_states) {
     return b;
 }
 
+// Rows of keys or values into a chunk kernel's tile: direct loads, or (bf16 inputs of fp32 arithmetic,
+// INB with T = float) converted exactly through registers.
+template <int D, typename T, bool INB>
+__device__ __forceinline__ void stage_input(T *tile, const void *src, int row0, int nrows, int L, int tid, int nt) {
+    if constexpr (INB && !std::is_same_v<T, __bf16>)
+        stage_rows_cvt<D>(tile, reinterpret_cast<const __bf16 *>(src), row0, nrows, L, tid, nt);
+    else
+        stage_rows<D, T>(tile, reinterpret_cast<const T *>(src), row0, nrows, L, uniform(tid >> 6), nt >> 6, tid & 63);
+}
+
 // ================================ state kernel ========================================================
-template <int D, int KIND, bool BF16>
+template <int D, int KIND, bool BF16, bool INB = BF16>
 __global__ void __launch_bounds__(state_waves(D) * 64) chunk_state_kernel(ChunkParams p) {
     using Cf = ChunkCfg<D, BF16>;
     using T = typename Cf::T;
@@ -183,8 +193,9 @@ __global__ void __launch_bounds__(state_waves(D) * 64) chunk_state_kernel(ChunkP
     float *E = reinterpret_cast<float *>(Vs + cp * D);
     double *wsum = reinterpret_cast<double *>(E + cp);
     const size_t base = (size_t)bh * L;
-    stage_rows<D, T>(Ks, reinterpret_cast<const T *>(p.k) + base * D, cs, rows, L, wave, NW, lane);
-    stage_rows<D, T>(Vs, reinterpret_cast<const T *>(p.v) + base * D, cs, rows, L, wave, NW, lane);
+    using TI = std::conditional_t<INB, __bf16, T>;
+    stage_input<D, T, INB>(Ks, reinterpret_cast<const TI *>(p.k) + base * D, cs, rows, L, tid, NT);
+    stage_input<D, T, INB>(Vs, reinterpret_cast<const TI *>(p.v) + base * D, cs, rows, L, tid, NT);
 
     float lgD = 0.f;
     if constexpr (KIND == kMaskD) lgD = p.ll[bh % p.H] * kLog2e;
@@ -404,7 +415,7 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(ChunkParams p)
 }
 
 // ================================ output kernel =======================================================
-template <int D, int KIND, int NW, int QT, bool BF16>
+template <int D, int KIND, int NW, int QT, bool BF16, bool INB = BF16>
 __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
     using Cf = ChunkCfg<D, BF16>;
     using T = typename Cf::T;
@@ -431,8 +442,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
     unsigned char *Fsm = reinterpret_cast<unsigned char *>(smem) + chunk_lds<D, BF16>(p.C, NW, false);
     unsigned char *Gsm = Fsm + Cf::SLOT;
     const size_t base = (size_t)bh * L;
-    stage_rows<D, T>(Ks, reinterpret_cast<const T *>(p.k) + base * D, cs, rows, L, wave, NW, lane);
-    stage_rows<D, T>(Vs, reinterpret_cast<const T *>(p.v) + base * D, cs, rows, L, wave, NW, lane);
+    using TI = std::conditional_t<INB, __bf16, T>;
+    stage_input<D, T, INB>(Ks, reinterpret_cast<const TI *>(p.k) + base * D, cs, rows, L, tid, NT);
+    stage_input<D, T, INB>(Vs, reinterpret_cast<const TI *>(p.v) + base * D, cs, rows, L, tid, NT);
     if constexpr (BF16) {
         if (c > 0) stage_flat(Fsm, p.fs + (size_t)(bid - 1) * Cf::SLOT, (int)(Cf::SLOT / 1024), wave, NW, lane);
         if (c < n - 1 && !p.causal)
@@ -453,13 +465,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_out_kernel(ChunkParams p) {
     QFrag qf[QT][NQ];
     float Ei[QT], den[QT];
     f32x4 acc[QT][NDT];
-    const T *qg = reinterpret_cast<const T *>(p.q) + base * D;
+    const TI *qg = reinterpret_cast<const TI *>(p.q) + base * D;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         const int tl = wave + NW * qt;
         const int il = 16 * tl + r;
         const bool ok = tl < tiles && il < cn;
-        const T *src = qg + (size_t)(cs + min(il, cn - 1)) * D + 4 * g;
+        const TI *src = qg + (size_t)(cs + min(il, cn - 1)) * D + 4 * g;
         float x[NQ][8];
         float ss = 0.f;
 #pragma unroll
@@ -1398,7 +1410,7 @@ size_t workspace_t(const AttnArgs &a) {
     return 2 * nb * ChunkCfg<D, BF16>::SLOT + ((nb * 4 + 15) & ~(size_t)15);
 }
 
-template <int D, int KIND, bool BF16>
+template <int D, int KIND, bool BF16, bool INB = BF16>
 hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
     using Cf = ChunkCfg<D, BF16>;
     ChunkParams p;
@@ -1453,8 +1465,9 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
         p.tot = reinterpret_cast<float *>(p.gs + nb * Cf::SLOT);
         constexpr int NW1 = state_waves(D);
         const size_t lds1 = chunk_lds<D, BF16>(a.C, NW1, false);
-        allow_lds(&chunk_state_kernel<D, KIND, BF16>, lds1);
-        hipLaunchKernelGGL((chunk_state_kernel<D, KIND, BF16>), dim3((unsigned)nb), dim3(NW1 * 64), lds1, stream, p);
+        allow_lds(&chunk_state_kernel<D, KIND, BF16, INB>, lds1);
+        hipLaunchKernelGGL((chunk_state_kernel<D, KIND, BF16, INB>), dim3((unsigned)nb), dim3(NW1 * 64), lds1, stream,
+                           p);
         constexpr int NBLK = (scan_vectors<D, BF16>() + kScanThreads - 1) / kScanThreads;
         hipLaunchKernelGGL((chunk_scan_kernel<D, BF16>), dim3((unsigned)(a.B * a.H * 2 * NBLK)), dim3(kScanThreads), 0,
                            stream, p);
@@ -1465,28 +1478,29 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
         allow_lds(kernel, lds);
         hipLaunchKernelGGL(kernel, dim3((unsigned)nb), dim3(nw * 64), lds, stream, p);
     };
-    if (a.C <= 64) out(&chunk_out_kernel<D, KIND, 4, 1, BF16>, 4);
-    else if (D == 128 || a.C <= 128) out(&chunk_out_kernel<D, KIND, 8, 1, BF16>, 8);
-    else out(&chunk_out_kernel<D, KIND, 8, (D == 128 ? 1 : 2), BF16>, 8);
+    if (a.C <= 64) out(&chunk_out_kernel<D, KIND, 4, 1, BF16, INB>, 4);
+    else if (D == 128 || a.C <= 128) out(&chunk_out_kernel<D, KIND, 8, 1, BF16, INB>, 8);
+    else out(&chunk_out_kernel<D, KIND, 8, (D == 128 ? 1 : 2), BF16, INB>, 8);
     return hipGetLastError();
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool INB>
 hipError_t dispatch_kind(const AttnArgs &a, hipStream_t stream) {
     switch (a.kind) {
-    case kMaskLit: return launch_t<D, kMaskLit, BF16>(a, stream);
-    case kMaskD: return launch_t<D, kMaskD, BF16>(a, stream);
-    default: return launch_t<D, kMaskS, BF16>(a, stream);
+    case kMaskLit: return launch_t<D, kMaskLit, BF16, INB>(a, stream);
+    case kMaskD: return launch_t<D, kMaskD, BF16, INB>(a, stream);
+    default: return launch_t<D, kMaskS, BF16, INB>(a, stream);
     }
 }
 
-template <bool BF16>
+// BF16: bf16 arithmetic; INB: bf16 inputs (with BF16 false: upcast exactly for fp32 arithmetic)
+template <bool BF16, bool INB>
 hipError_t dispatch_d(const AttnArgs &a, hipStream_t stream) {
     switch (a.d) {
-    case 16: return dispatch_kind<16, BF16>(a, stream);
-    case 32: return dispatch_kind<32, BF16>(a, stream);
-    case 64: return dispatch_kind<64, BF16>(a, stream);
-    default: return dispatch_kind<128, BF16>(a, stream);
+    case 16: return dispatch_kind<16, BF16, INB>(a, stream);
+    case 32: return dispatch_kind<32, BF16, INB>(a, stream);
+    case 64: return dispatch_kind<64, BF16, INB>(a, stream);
+    default: return dispatch_kind<128, BF16, INB>(a, stream);
     }
 }
 
@@ -1501,16 +1515,18 @@ Plan plan_t(const AttnArgs &a) {
 }  // namespace
 
 Plan plan_chunk(const AttnArgs &a) {
+    const bool bf16c = !a.fp32c;   // the arithmetic sets the tiles and states
     switch (a.d) {
-    case 16: return a.in_bf16 ? plan_t<16, true>(a) : plan_t<16, false>(a);
-    case 32: return a.in_bf16 ? plan_t<32, true>(a) : plan_t<32, false>(a);
-    case 64: return a.in_bf16 ? plan_t<64, true>(a) : plan_t<64, false>(a);
-    default: return a.in_bf16 ? plan_t<128, true>(a) : plan_t<128, false>(a);
+    case 16: return bf16c ? plan_t<16, true>(a) : plan_t<16, false>(a);
+    case 32: return bf16c ? plan_t<32, true>(a) : plan_t<32, false>(a);
+    case 64: return bf16c ? plan_t<64, true>(a) : plan_t<64, false>(a);
+    default: return bf16c ? plan_t<128, true>(a) : plan_t<128, false>(a);
     }
 }
 
 hipError_t launch_chunk(const AttnArgs &a, hipStream_t stream) {
-    return a.in_bf16 ? dispatch_d<true>(a, stream) : dispatch_d<false>(a, stream);
+    if (!a.fp32c) return dispatch_d<true, true>(a, stream);
+    return a.in_bf16 ? dispatch_d<false, true>(a, stream) : dispatch_d<false, false>(a, stream);
 }
 
 }  // namespace lion

@@ -397,11 +397,13 @@ __device__ __forceinline__ void full_epilogue(FullWave<D, QT, BF16> &w, const Fu
 // LDS as one stage or as double-buffered stages.  It keeps the sub-block arithmetic of the helpers above
 // written out in place: built from the helpers it compiled to fewer registers but measured 6-7% slower
 // (B64 H12 L197 D, 36.3 vs 33.8 us on one box).
-template <int D, int KIND, int QT, bool BF16, bool TWO>
+template <int D, int KIND, int QT, bool BF16, bool TWO, bool INB = BF16>
 __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
     using C = FullCfg<D, BF16>;
-    using T = typename C::T;
+    using T = typename C::T;                               // compute and LDS type
+    using TI = std::conditional_t<INB, __bf16, T>;        // input type (bf16 inputs of fp32 arithmetic)
     using RT = typename C::RT;
+    static_assert(!BF16 || INB, "bf16 arithmetic takes bf16 inputs");
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x, nt = blockDim.x, nw = nt >> 6;
@@ -428,15 +430,23 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
     double *scan_sh = reinterpret_cast<double *>(E + (KIND == kMaskLit ? 0 : (TWO ? 2 : 1) * Lpad));
 
     const size_t base = (size_t)bh * L;
-    const T *qg = reinterpret_cast<const T *>(p.q) + base * D;
-    const T *kg = reinterpret_cast<const T *>(p.k) + base * D;
-    const T *vg = reinterpret_cast<const T *>(p.v) + base * D;
+    const TI *qg = reinterpret_cast<const TI *>(p.q) + base * D;
+    const TI *kg = reinterpret_cast<const TI *>(p.k) + base * D;
+    const TI *vg = reinterpret_cast<const TI *>(p.v) + base * D;
+    // rows of keys or values into a stage buffer: direct loads, or (bf16 inputs of fp32 arithmetic)
+    // converted through registers
+    auto stage = [&](T *tile, const TI *src, int row0) {
+        if constexpr (!BF16 && INB)
+            stage_rows_cvt<D>(tile, src, row0, SK, L, tid, nt);
+        else
+            stage_rows<D, T>(tile, src, row0, SK, L, wave, nw, lane);
+    };
 
     // stage 0 in flight while the prologue runs.  When the whole sequence is one stage (and its key
     // chunks fit 4 per thread), keys come through registers and phi is applied on the way into LDS.
     const bool kreg = BF16 && p.nbuf == 1 && SK * RT::CPK <= 4 * nt;
     u32x4 kx[4];
-    stage_rows<D, T>(Vb, vg, 0, SK, L, wave, nw, lane);
+    stage(Vb, vg, 0);
     if (kreg) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -444,7 +454,7 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
             kx[u] = ld16(kg + (size_t)min(c16 / RT::CPK, L - 1) * D + (c16 % RT::CPK) * RT::VEC);
         }
     } else {
-        stage_rows<D, T>(Kb, kg, 0, SK, L, wave, nw, lane);
+        stage(Kb, kg, 0);
     }
 
     if constexpr (KIND != kMaskLit)
@@ -459,8 +469,12 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
         const int i = (wtile0 + qt) * 16 + r;
         const bool ok = i < L && qt < wave_tiles;
         float x[C::CPL];
-        const T *row = qg + (size_t)(ok ? i : 0) * D;
-        if constexpr (BF16 && C::CPL >= 8) {
+        const TI *row = qg + (size_t)(ok ? i : 0) * D;
+        if constexpr (!BF16 && INB) {
+            const TI *src = row + g * C::CPL;
+#pragma unroll
+            for (int c = 0; c < C::CPL; ++c) x[c] = (float)src[c];
+        } else if constexpr (BF16 && C::CPL >= 8) {
             // fragment st of lane group g: the eight channels of 16-byte chunk 4 st + g
 #pragma unroll
             for (int st = 0; st < C::NS; ++st) {
@@ -578,8 +592,8 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
         __syncthreads();                                     // stage s is in LDS; buffer s+1 is free
         if (s + 1 < nst_used) {
             const int nb = (s + 1) & 1;
-            stage_rows<D, T>(Kb + (size_t)nb * SK * D, kg, (s + 1) * SK, SK, L, wave, nw, lane);
-            stage_rows<D, T>(Vb + (size_t)nb * SK * D, vg, (s + 1) * SK, SK, L, wave, nw, lane);
+            stage(Kb + (size_t)nb * SK * D, kg, (s + 1) * SK);
+            stage(Vb + (size_t)nb * SK * D, vg, (s + 1) * SK);
         }
         // phi over the staged keys (in place); keys at or past L become zero rows
         {
@@ -1025,7 +1039,8 @@ FullShape full_shape(const AttnArgs &a) {
     const bool two = a.order != nullptr && a.kind != kMaskLit;
     const int ntiles = (a.L + 15) / 16;
     const long bhs = (long)a.B * a.H;
-    const size_t esz = a.in_bf16 ? 2 : 4;
+    const bool bf16c = !a.fp32c;                     // bf16 arithmetic
+    const size_t esz = bf16c ? 2 : 4;                // staged K and V elements
     const size_t per_key = 2 * (size_t)a.d * esz;   // K and V bytes of one key
     const int lr = ((a.L + kKB - 1) / kKB) * kKB;
     FullShape sh;
@@ -1033,7 +1048,7 @@ FullShape full_shape(const AttnArgs &a) {
     // on the chip at once; larger grids overlap workgroups' loads with others' compute in the streaming
     // kernel (measured: B64 H3 L197 10.7 vs 12.1 us; B64 H12 L197 37.7 vs 33.5 us)
     const int nsb_res = (ntiles + 14) / 15;
-    sh.resident = a.in_bf16 && a.d >= 32 && !two && (size_t)lr * per_key <= kStageBytes && lr <= 448 &&
+    sh.resident = bf16c && a.d >= 32 && !two && (size_t)lr * per_key <= kStageBytes && lr <= 448 &&
                   bhs * nsb_res <= kResidentMaxGrid;
     if (sh.resident) {
         // one compute wave per query tile plus the loader; the compute waves also cover the staged rows
@@ -1051,7 +1066,7 @@ FullShape full_shape(const AttnArgs &a) {
         return sh;
     }
     int qt = 1;
-    if (a.in_bf16) {
+    if (bf16c) {
         // largest tile count per wave that still gives >= 2 waves per SIMD (256 CUs x 4 SIMDs)
         const int cand[3] = {a.d == 128 ? 1 : 4, 2, 1};
         for (int c : cand) {
@@ -1110,52 +1125,54 @@ hipError_t launch_kernel(K kernel, const FullParams &p, const FullShape &sh, hip
     return hipGetLastError();
 }
 
-template <int D, int KIND, int QT, bool BF16, bool TWO>
+template <int D, int KIND, int QT, bool BF16, bool TWO, bool INB>
 hipError_t launch_full_t(const AttnArgs &a, hipStream_t stream, const FullShape &sh) {
     const FullParams p = full_params(a, sh);
     if constexpr (BF16 && !TWO && D >= 32 && QT == 1) {
         if (sh.resident) return launch_kernel(&full_resident_kernel<D, KIND, QT>, p, sh, stream);
     }
-    return launch_kernel(&full_kernel<D, KIND, QT, BF16, TWO>, p, sh, stream);
+    return launch_kernel(&full_kernel<D, KIND, QT, BF16, TWO, INB>, p, sh, stream);
 }
 
-template <int D, int KIND, bool BF16, bool TWO>
+template <int D, int KIND, bool BF16, bool TWO, bool INB>
 hipError_t dispatch_qt2(const AttnArgs &a, hipStream_t stream) {
     const FullShape sh = full_shape(a);
     if constexpr (BF16) {
         if constexpr (D != 128) {
-            if (sh.qt == 4) return launch_full_t<D, KIND, 4, BF16, TWO>(a, stream, sh);
-            if (sh.qt == 2) return launch_full_t<D, KIND, 2, BF16, TWO>(a, stream, sh);
+            if (sh.qt == 4) return launch_full_t<D, KIND, 4, BF16, TWO, INB>(a, stream, sh);
+            if (sh.qt == 2) return launch_full_t<D, KIND, 2, BF16, TWO, INB>(a, stream, sh);
         }
     }
-    return launch_full_t<D, KIND, 1, BF16, TWO>(a, stream, sh);
+    return launch_full_t<D, KIND, 1, BF16, TWO, INB>(a, stream, sh);
 }
 
-// the two-order variant exists for the kinds with a decay (LIT's mask is all ones in any order)
-template <int D, int KIND, bool BF16>
+// the two-order variant exists for the kinds with a decay (LIT's mask is all ones in any order), in
+// the input type's own arithmetic
+template <int D, int KIND, bool BF16, bool INB>
 hipError_t dispatch_qt(const AttnArgs &a, hipStream_t stream) {
-    if constexpr (KIND != kMaskLit) {
-        if (a.order) return dispatch_qt2<D, KIND, BF16, true>(a, stream);
+    if constexpr (KIND != kMaskLit && BF16 == INB) {
+        if (a.order) return dispatch_qt2<D, KIND, BF16, true, INB>(a, stream);
     }
-    return dispatch_qt2<D, KIND, BF16, false>(a, stream);
+    return dispatch_qt2<D, KIND, BF16, false, INB>(a, stream);
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool INB>
 hipError_t dispatch_kind(const AttnArgs &a, hipStream_t stream) {
     switch (a.kind) {
-    case kMaskLit: return dispatch_qt<D, kMaskLit, BF16>(a, stream);
-    case kMaskD: return dispatch_qt<D, kMaskD, BF16>(a, stream);
-    default: return dispatch_qt<D, kMaskS, BF16>(a, stream);
+    case kMaskLit: return dispatch_qt<D, kMaskLit, BF16, INB>(a, stream);
+    case kMaskD: return dispatch_qt<D, kMaskD, BF16, INB>(a, stream);
+    default: return dispatch_qt<D, kMaskS, BF16, INB>(a, stream);
     }
 }
 
-template <bool BF16>
+// BF16: bf16 arithmetic; INB: bf16 inputs (with BF16 false: upcast exactly for fp32 arithmetic)
+template <bool BF16, bool INB>
 hipError_t dispatch_d(const AttnArgs &a, hipStream_t stream) {
     switch (a.d) {
-    case 16: return dispatch_kind<16, BF16>(a, stream);
-    case 32: return dispatch_kind<32, BF16>(a, stream);
-    case 64: return dispatch_kind<64, BF16>(a, stream);
-    default: return dispatch_kind<128, BF16>(a, stream);
+    case 16: return dispatch_kind<16, BF16, INB>(a, stream);
+    case 32: return dispatch_kind<32, BF16, INB>(a, stream);
+    case 64: return dispatch_kind<64, BF16, INB>(a, stream);
+    default: return dispatch_kind<128, BF16, INB>(a, stream);
     }
 }
 
@@ -1169,7 +1186,8 @@ Plan plan_full(const AttnArgs &a) {
 }
 
 hipError_t launch_full(const AttnArgs &a, hipStream_t stream) {
-    return a.in_bf16 ? dispatch_d<true>(a, stream) : dispatch_d<false>(a, stream);
+    if (!a.fp32c) return dispatch_d<true, true>(a, stream);
+    return a.in_bf16 ? dispatch_d<false, true>(a, stream) : dispatch_d<false, false>(a, stream);
 }
 
 }  // namespace lion

@@ -16,6 +16,7 @@ struct AttnArgs {
     float eps;
     int B, H, L, d;
     bool in_bf16;               // element type of q, k, v
+    bool fp32c;                 // compute in fp32: fp32 inputs, or bf16 inputs upcast exactly (LION_FP32_ARITH)
     void *y;                    // [B, H, L, d]
     bool out_bf16;              // element type of y
     float *den_out;             // nullable [B, H, L]

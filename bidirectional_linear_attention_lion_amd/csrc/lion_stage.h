@@ -53,6 +53,28 @@ __device__ __forceinline__ void stage_rows(T *tile, const T *src, int row0, int 
     }
 }
 
+// bf16 rows [row0, row0 + nrows) of a row-major [L][D] array into an fp32 tile (RowTile<D, float>
+// layout), converted exactly on the way: each thread loads 16 bytes (eight bf16 values) and writes them
+// as two 16-byte fp32 chunks.  Unlike stage_rows this passes through VGPRs, so the caller's barrier
+// after it also completes the copy.  Rows at or past L are loaded from row L - 1, as above.
+template <int D>
+__device__ __forceinline__ void stage_rows_cvt(float *tile, const __bf16 *src, int row0, int nrows, int L, int tid,
+                                               int nt) {
+    using RT = RowTile<D, float>;
+    constexpr int C8 = D / 8;   // 16-byte bf16 chunks per row
+    for (int i = tid; i < nrows * C8; i += nt) {
+        const int row = i / C8, c8 = i % C8;
+        const int grow = min(row0 + row, L - 1);
+        const u32x4 raw = ld16(src + (size_t)grow * D + 8 * c8);
+        // whole-vector operations (element-wise bit_casts of vector elements have miscompiled)
+        const u32x4 ev = raw << 16, od = raw & 0xFFFF0000u;   // even and odd elements as fp32 bits
+        const u32x4 lo = __builtin_shufflevector(ev, od, 0, 4, 1, 5);
+        const u32x4 hi = __builtin_shufflevector(ev, od, 2, 6, 3, 7);
+        *reinterpret_cast<u32x4 *>(tile + RT::off(row, 8 * c8)) = lo;
+        *reinterpret_cast<u32x4 *>(tile + RT::off(row, 8 * c8 + 4)) = hi;
+    }
+}
+
 // Issue the direct loads of `kib` KiB starting at `src` (16-byte aligned) into LDS at `dst`; waves
 // share the 1 KiB load instructions round-robin.
 __device__ __forceinline__ void stage_flat(void *dst, const void *src, int kib, int wave, int nw, int lane) {

@@ -33,7 +33,7 @@
  *                  LION_MASK_D:   [H]        one decay per head;
  *                  LION_MASK_S:   [B, H, L]  one decay per token (entry 0 of each row never enters).
  *   mask_kind    LION_MASK_LIT / LION_MASK_D / LION_MASK_S, optionally | LION_CAUSAL (keys after
- *                the query are masked out); the kind also selects phi:
+ *                the query are masked out) and | LION_FP32_ARITH; the kind also selects phi:
  *                  LIT: phi(x) = elu(x) + 1;  D: phi(x) = x;  S: phi = silu(x) / ||silu(x)||_2 over the
  *                  d channels of the token (an all-zero silu vector gives phi = 0).
  *   eps          >= 0 and finite, added to every row sum.
@@ -48,7 +48,8 @@
  *
  * Precision: bf16 inputs feed bf16 matrix-core products with fp32 accumulation; phi and the
  * row-sum products are formed in fp32 and rounded to bf16 before the products that need them.
- * fp32 inputs keep every step in fp32.  Row sums (denominators) are accumulated in fp32.
+ * fp32 inputs, and bf16 inputs with LION_FP32_ARITH, keep every step in fp32.  Row sums (denominators)
+ * are accumulated in fp32.
  *
  * Ownership and threading: the caller allocates and owns every buffer, workspace included.  The
  * library allocates and frees nothing, never synchronises, and is reentrant; its one piece of global
@@ -90,6 +91,14 @@ enum lion_mask_kind { LION_MASK_LIT = 0, LION_MASK_D = 1, LION_MASK_S = 2 };
  * Recurrence Form of Linear Attention", Eq. 4a-4c) with the kind's decay (LION-S 1D for
  * single-directional generation: reply item 5, "Is this method limited to bidirectional models?"). */
 enum { LION_CAUSAL = 4 };
+/* OR-ed into mask_kind (full, chunkwise and RNN forms): fp32 arithmetic throughout for bf16 inputs.  The
+ * inputs are upcast exactly as they are staged, and phi, the scores, the masked scores, the carried
+ * states and the products run in fp32 (fp32 matrix cores), as for fp32 inputs, instead of being rounded
+ * to bf16 for the bf16 matrix cores.  For rows whose denominator nearly cancels (LION-S with normalised
+ * silu: condition numbers in the thousands), where bf16 rounding is amplified by the condition number;
+ * pair it with an fp32 y.  Slower (fp32 matrix-core peak is 1/16 of bf16).  The RNN form computes in fp32
+ * already and ignores it; the two-order and backward entry points return LION_ERR_UNSUPPORTED. */
+enum { LION_FP32_ARITH = 8 };
 enum lion_dtype { LION_DTYPE_F32 = 0, LION_DTYPE_BF16 = 1 };
 enum lion_form { LION_FORM_FULL = 0, LION_FORM_CHUNK = 1, LION_FORM_BIRNN = 2, LION_FORM_FULL_BWD = 3,
                  LION_FORM_CHUNK_BWD = 4, LION_FORM_CHUNK2 = 5 };

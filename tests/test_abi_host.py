@@ -69,7 +69,7 @@ INVALID_CASES = [
     ("null q", dict(q=None)), ("null k", dict(k=None)), ("null v", dict(v=None)), ("null y", dict(y=None)),
     ("misaligned q", dict(q=MIS)), ("misaligned y", dict(y=MIS)), ("misaligned den", dict(den=MIS)),
     ("bad kind", dict(kind=3)), ("negative kind", dict(kind=-1)),
-    ("unknown flag bit", dict(kind=8)), ("causal bad kind", dict(kind=3 | 4)),
+    ("unknown flag bit", dict(kind=16)), ("causal bad kind", dict(kind=3 | 4)),
     ("causal LIT with log_lambda", dict(kind=4, ll=P)), ("causal S without log_lambda", dict(kind=2 | 4, ll=None)),
     ("LIT with log_lambda", dict(kind=0, ll=P)), ("D without log_lambda", dict(kind=1, ll=None)),
     ("S without log_lambda", dict(kind=2, ll=None)), ("misaligned log_lambda", dict(kind=1, ll=MIS)),
@@ -150,7 +150,8 @@ def test_workspace_too_small(form, entry):
         need = lion.lion_attn_workspace_bytes(form, B, H, L, 64, 64, 1)
         if need == 0:
             continue
-        kw = dict(kind=1, ll=P, B=B, H=H, L=L)
+        # the query answers for every way the form can run; fp32 arithmetic (flag 8) needs the most
+        kw = dict(kind=1 | 8, ll=P, B=B, H=H, L=L)
         assert entry(ws=None, wsb=need, **kw) == WORKSPACE
         assert entry(ws=P, wsb=need - 1, **kw) == WORKSPACE
         return
@@ -184,6 +185,7 @@ def test_bwd_invalid_arguments(name, kw):
 def test_bwd_unsupported_and_workspace():
     assert bwd(dt=0) == UNSUPPORTED                 # fp32 inputs
     assert bwd(d=16) == UNSUPPORTED
+    assert bwd(kind=0 | 8) == UNSUPPORTED           # fp32 arithmetic: forward only
     need = lion.lion_attn_workspace_bytes(lion.FORM_FULL_BWD, 2, 3, 17, 64, 0, 1)
     assert need == 12 * 2 * 3 * 17
     assert lion.lion_attn_workspace_bytes(lion.FORM_FULL_BWD, 2, 3, 17, 64, 0, 0) == SIZE_MAX
@@ -287,3 +289,18 @@ def test_binding_requires_built_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError):
         binding.library()
+
+
+def test_fp32_arith_flag():
+    """LION_FP32_ARITH is accepted by the full, chunkwise and RNN forms and refused (unsupported) by the
+    two-order forms; the chunkwise workspace query covers the fp32 states it needs."""
+    F = 8
+    lib = lion.library()
+    for C in (64, 128):
+        for L in (197, 4097):
+            wf = lion.lion_attn_workspace_bytes(lion.FORM_CHUNK, 2, 3, L, 64, C, 1)
+            w32 = lion.lion_attn_workspace_bytes(lion.FORM_CHUNK, 2, 3, L, 64, C, 0)
+            assert wf >= w32, (C, L, wf, w32)   # bf16 inputs may take fp32 states
+    assert lib.lion_attn_full2(P, P, P, P, 1 | F, 1e-6, P, 2, 3, 17, 64, 1, P, 0, None, None) == UNSUPPORTED
+    assert lib.lion_attn_chunk2(P, P, P, P, 1 | F, 64, 1e-6, P, 2, 3, 17, 64, 1, P, 0, None, None, 0, None) == UNSUPPORTED
+    assert full(kind=3 | F) == INVALID and full(kind=16 | F) == INVALID
