@@ -343,10 +343,9 @@ __global__ void __launch_bounds__(state_waves(D) * 64) chunk_state_kernel(ChunkP
 // ================================ scan kernel =========================================================
 // One thread per 16-byte vector of a slot, sequential over the chunks of its (batch, head): forward
 // states F_c = a_c F_{c-1} + Fl_c for c = 0 .. n-2, backward G_c = a_c G_{c+1} + Gl_c for c = n-1 .. 1,
-// each written over the local state of the same chunk.  Loads run kU chunks ahead (16 measured slower
-// than 4 on B8 H12 L4097, C = 128: 34 against 26 us).
+// each written over the local state of the same chunk.  Loads run kU chunks ahead.
 constexpr int kScanThreads = 256;
-constexpr int kU = 4;
+constexpr int kU = 8;
 
 template <int D, bool BF16>
 __host__ __device__ constexpr int scan_vectors() {
@@ -373,20 +372,29 @@ __global__ void __launch_bounds__(kScanThreads) chunk_scan_kernel(ChunkParams p)
     const int steps = n - 1;
     auto chunk_of = [&](int k) { return dir == 0 ? k : n - 1 - k; };
 
+    // each chunk's total is loaded with its state vector, kU chunks ahead: vector-memory waits count in
+    // issue order, so a total loaded just before its use would also wait for every prefetched vector
+    // (loads past the last step reread the last step's chunk, so that every load is unconditional and
+    // lands straight in its buffer)
+    auto chunk_at = [&](int k) { return chunk_of(min(k, steps - 1)); };
     u32x4 buf[kU];
+    float tb[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
-        if (u < steps) buf[u] = ld16(base + (size_t)chunk_of(u) * Cf::SLOT);
+    for (int u = 0; u < kU; ++u) {
+        buf[u] = ld16(base + (size_t)chunk_at(u) * Cf::SLOT);
+        tb[u] = tot[chunk_at(u)];
+    }
     float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < steps; k0 += kU) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int k = k0 + u;
             if (k >= steps) break;
-            const int c = uniform(chunk_of(k));   // scalar load of the total (see group_scan_kernel)
+            const int c = chunk_of(k);
             const u32x4 x = buf[u];
-            if (k + kU < steps) buf[u] = ld16(base + (size_t)chunk_of(k + kU) * Cf::SLOT);
-            const float a = fast_exp2(tot[c]);
+            const float a = fast_exp2(tb[u]);
+            buf[u] = ld16(base + (size_t)chunk_at(k + kU) * Cf::SLOT);
+            tb[u] = tot[chunk_at(k + kU)];
             u32x4 o;
             if (zpart || !BF16) {
                 // whole-vector reinterpretation (a bit_cast of one element of a u32x4 is not used:
@@ -1357,10 +1365,12 @@ __global__ void __launch_bounds__(kScanWave) group_scan_kernel(ChunkParams p) {
         const int ns = min(kScanSeg, steps - s0);
         for (int k = 0; k < ns; ++k)
             if (lane * 16 < pbytes) load_lds16(buf + k * 1024, base + (size_t)group_of(s0 + k) * F::SLOTK + lane * 16);
+        // the segment's totals, lane k holding step k's (read back with readlane: no wait inside the chain)
+        const float tgl = lane < ns ? tg[group_of(s0 + lane)] : 0.f;
         wait_vm_all();   // also drains the previous segment's stores
         for (int k = 0; k < ns; ++k) {
             const int gg = uniform(group_of(s0 + k));
-            const float a = fast_exp2(tg[gg]);
+            const float a = fast_exp2(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tgl), k)));
             const bf16x8 xh = *reinterpret_cast<const bf16x8 *>(buf + k * 1024 + o_hi);
             const bf16x8 xl = *reinterpret_cast<const bf16x8 *>(buf + k * 1024 + o_lo);
             bf16x8 oh, ol;
