@@ -152,7 +152,9 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16 *tile, int h, int ct, int
 template <int D, bool BF16>
 __host__ __device__ size_t chunk_lds(int C, int nw, bool with_states) {
     const int cp = cpad(C);
-    size_t b = 2 * (size_t)cp * D * sizeof(typename ChunkCfg<D, BF16>::T) + (size_t)cp * 4 + (size_t)nw * 8;
+    // keys, values, exponents, scan scratch, and the state kernel's fold-weight table (2 per key)
+    size_t b = 2 * (size_t)cp * D * sizeof(typename ChunkCfg<D, BF16>::T) + (size_t)cp * 4 + (size_t)nw * 8 +
+               (size_t)cp * 8;
     b = (b + 15) & ~(size_t)15;
     if (BF16 && with_states) b += 2 * ChunkCfg<D, BF16>::SLOT;
     return b;
@@ -213,6 +215,24 @@ __global__ void __launch_bounds__(state_waves(D) * 64) chunk_state_kernel(ChunkP
         __syncthreads();
     }
     const float etot = Ex(cn - 1);
+    // bf16: the fold weights of every key of the chunk, once per workgroup (0 past the chunk's end); the
+    // sub-block loop reads them back four at a time instead of recomputing them in every lane
+    float *Wf = reinterpret_cast<float *>(wsum + NW), *Wg = Wf + cp;
+    if constexpr (BF16) {
+        for (int j = tid; j < cp; j += NT) {
+            float a = j < cn ? 1.f : 0.f, b = a;
+            if constexpr (KIND != kMaskLit) {
+                if (j < cn) {
+                    const float ej = Ex(j);
+                    a = fast_exp2(fminf(etot - ej, 0.f));
+                    b = fast_exp2(fminf(ej, 0.f));
+                }
+            }
+            Wf[j] = a;
+            Wg[j] = b;
+        }
+        __syncthreads();
+    }
 
     auto tile_of = [&](int u, int &ct, int &nt) -> bool {
         if constexpr (kColOwn) {
@@ -228,68 +248,84 @@ __global__ void __launch_bounds__(state_waves(D) * 64) chunk_state_kernel(ChunkP
     };
 
     f32x4 sf[MAXT], sg[MAXT];
+    float zf[MAXT], zg[MAXT];   // bf16: this lane's part of the row sums of the weight tile
 #pragma unroll
-    for (int u = 0; u < MAXT; ++u) sf[u] = sg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < MAXT; ++u) {
+        sf[u] = sg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        zf[u] = zg[u] = 0.f;
+    }
 
     for (int h = 0; h < rows / kKB; ++h) {
         // fold weights of the sub-block's tokens 4g + e and 16 + 4g + e; 0 past the chunk's end
         float wf[2][4], wg[2][4];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t) {
+            if constexpr (BF16) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4 *>(Wf + h * kKB + 16 * t + 4 * g);
+                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(Wg + h * kKB + 16 * t + 4 * g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = h * kKB + 16 * t + 4 * g + e;
-                const float valid = j < cn ? 1.f : 0.f;
-                float a = valid, b = valid;
-                if constexpr (KIND != kMaskLit) {
-                    const float ej = Ex(j);
-                    a *= fast_exp2(fminf(etot - ej, 0.f));
-                    b *= fast_exp2(fminf(ej, 0.f));
+                for (int e = 0; e < 4; ++e) {
+                    wf[t][e] = a4[e];
+                    wg[t][e] = b4[e];
                 }
-                wf[t][e] = a;
-                wg[t][e] = b;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = h * kKB + 16 * t + 4 * g + e;
+                    const float valid = j < cn ? 1.f : 0.f;
+                    float a = valid, b = valid;
+                    if constexpr (KIND != kMaskLit) {
+                        const float ej = Ex(j);
+                        a *= fast_exp2(fminf(etot - ej, 0.f));
+                        b *= fast_exp2(fminf(ej, 0.f));
+                    }
+                    wf[t][e] = a;
+                    wg[t][e] = b;
+                }
             }
+        }
         // bf16: the fold weights multiply the key fragment (A operand), once per sub-block, rather than
-        // every value tile's B operand: A = bf16(w k) for the value tiles; the row-sum column takes
-        // A_hi + A_lo (the bf16 rounding of the remainder) against a column of ones, so the row sums keep
-        // ~2^-17 relative accuracy (a nearly cancelling denominator amplifies their error)
-        bf16x8 af_hi{}, af_lo{}, ag_hi{}, ag_lo{};
-        auto weighted = [&](const bf16x8 &kf, const float (&w)[2][4], bf16x8 &hi, bf16x8 &lo) {
+        // every value tile's B operand: A = bf16(w k) for the value tiles.  The row sums (the weight
+        // tile) are accumulated in fp32 on the vector ALU from the same fragment, w times the exact key:
+        // a nearly cancelling denominator amplifies their error, so they get no bf16 rounding at all
+        bf16x8 af{}, ag{};
+        auto weighted = [&](const bf16x8 &kf, const float (&w)[2][4], bf16x8 &hi) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x = w[t][e] * (float)kf[4 * t + e];
-                    const __bf16 xh = f2bf(x);
-                    hi[4 * t + e] = xh;
-                    lo[4 * t + e] = f2bf(x - (float)xh);
-                }
+                for (int e = 0; e < 4; ++e) hi[4 * t + e] = f2bf(w[t][e] * (float)kf[4 * t + e]);
         };
-        if constexpr (BF16 && kColOwn) {
-            const bf16x8 kfr = tr_frag<D>(Ks, h, wave, r, g);
-            weighted(kfr, wf, af_hi, af_lo);
-            if (!p.causal) weighted(kfr, wg, ag_hi, ag_lo);
-        }
-        bf16x8 ones;
+        auto rowsum = [&](const bf16x8 &kf, const float (&w)[2][4], float &z) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ones[e] = f2bf(r == 0 ? 1.f : 0.f);
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) z = fmaf(w[t][e], (float)kf[4 * t + e], z);
+        };
+        bf16x8 kfr{};
+        if constexpr (BF16 && kColOwn) {
+            kfr = tr_frag<D>(Ks, h, wave, r, g);
+            weighted(kfr, wf, af);
+            if (!p.causal) weighted(kfr, wg, ag);
+        }
 #pragma unroll
         for (int u = 0; u < MAXT; ++u) {
             int ct, nt;
             if (!tile_of(u, ct, nt)) break;
             if constexpr (BF16) {
                 if constexpr (!kColOwn) {
-                    const bf16x8 kfr = tr_frag<D>(Ks, h, nt, r, g);
-                    weighted(kfr, wf, af_hi, af_lo);
-                    if (!p.causal) weighted(kfr, wg, ag_hi, ag_lo);
+                    kfr = tr_frag<D>(Ks, h, nt, r, g);
+                    if (ct < NDT) {
+                        weighted(kfr, wf, af);
+                        if (!p.causal) weighted(kfr, wg, ag);
+                    }
                 }
                 if (ct < NDT) {
                     const bf16x8 vv = tr_frag<D>(Vs, h, ct, r, g);
-                    sf[u] = mfma_bf16(af_hi, vv, sf[u]);
-                    if (!p.causal) sg[u] = mfma_bf16(ag_hi, vv, sg[u]);
+                    sf[u] = mfma_bf16(af, vv, sf[u]);
+                    if (!p.causal) sg[u] = mfma_bf16(ag, vv, sg[u]);
                 } else {
-                    sf[u] = mfma_bf16(af_lo, ones, mfma_bf16(af_hi, ones, sf[u]));
-                    if (!p.causal) sg[u] = mfma_bf16(ag_lo, ones, mfma_bf16(ag_hi, ones, sg[u]));
+                    rowsum(kfr, wf, zf[u]);
+                    if (!p.causal) rowsum(kfr, wg, zg[u]);
                 }
             } else {
 #pragma unroll
@@ -306,7 +342,7 @@ __global__ void __launch_bounds__(state_waves(D) * 64) chunk_state_kernel(ChunkP
         }
     }
 
-    // store: value tiles in register layout, the row-sum column (hi + lo columns) as fp32
+    // store: value tiles in register layout, the row sums as fp32
     const bool want_f = c < n - 1, want_g = c > 0 && !p.causal;
     unsigned char *fslot = p.fs + (size_t)bid * Cf::SLOT;
     unsigned char *gslot = p.gs + (size_t)bid * Cf::SLOT;
@@ -329,6 +365,13 @@ __global__ void __launch_bounds__(state_waves(D) * 64) chunk_state_kernel(ChunkP
                 } else {
                     *reinterpret_cast<f32x4 *>(dst) = s;
                 }
+            } else if constexpr (BF16) {
+                // lane (r, g) summed key channel 16 nt + r over its keys 4g + e, 16 + 4g + e of every
+                // sub-block: the four lane groups' parts added
+                float z = which == 0 ? zf[u] : zg[u];
+                z += __shfl_xor(z, 16, 64);
+                z += __shfl_xor(z, 32, 64);
+                if (g == 0) *reinterpret_cast<float *>(slot + Cf::VBYTES + (size_t)(16 * nt + r) * 4) = z;
             } else {
                 f32x4 z;
 #pragma unroll
