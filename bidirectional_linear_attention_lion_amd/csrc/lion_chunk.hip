@@ -1307,36 +1307,49 @@ __global__ void __launch_bounds__(512) group_state_kernel(ChunkParams p) {
         }
         if (c16 < rows * RT::CPK) st16(Ks + RT::off(row, (c16 % RT::CPK) * RT::VEC), o);
     }
-    __syncthreads();
+
+    // fold weights of every row, both directions, once per workgroup (forward relative to the group's
+    // last token, backward to the token before its first); the sub-block loop reads them four at a time
+    float *W = reinterpret_cast<float *>(sh + 16);   // [2][ROWS]
+    if constexpr (KIND != kMaskLit) {
+        const float etot = Ex(L - 1);
+        for (int j = tid; j < rows; j += NT) {
+            const float ej = Ex(j);
+            W[j] = fast_exp2(fminf(etot - ej, 0.f));
+            W[ROWS + j] = fast_exp2(fminf(ej, 0.f));
+        }
+    }
+    __syncthreads();   // keys (phi applied) and the weight table in LDS
 
     const int nt = wave & 3, dir = wave >> 2;
     if (nt < NDT && (KIND != kMaskLit || dir == 0) && !(p.causal && dir == 1)) {
-        const float etot = Ex(L - 1);
-        bf16x8 ones;
+        f32x4 acc[NDT];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ones[e] = f2bf(r == 0 ? 1.f : 0.f);
-        f32x4 acc[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < NDT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float zs = 0.f;   // row sums of key channel 16 nt + r over this lane's keys, fp32
         for (int h = 0; h < rows / kKB; ++h) {
             const bf16x8 kfr = tr_frag<D>(Ks, h, nt, r, g);
-            bf16x8 af = kfr, bw = ones;
+            bf16x8 af = kfr;
             if constexpr (KIND != kMaskLit) {
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < 2; ++t) {
+                    const f32x4 w4 = *reinterpret_cast<const f32x4 *>(W + dir * ROWS + h * kKB + 16 * t + 4 * g);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float ej = Ex(h * kKB + 16 * t + 4 * g + e);
-                        const float w = fast_exp2(fminf(dir == 0 ? etot - ej : ej, 0.f));
-                        af[4 * t + e] = f2bf(w * (float)kfr[4 * t + e]);
-                        const __bf16 wh = f2bf(w);
-                        bw[4 * t + e] = r == 0 ? wh : (r == 1 ? f2bf(w - (float)wh) : f2bf(0.f));
+                        const float k = (float)kfr[4 * t + e];
+                        af[4 * t + e] = f2bf(w4[e] * k);
+                        zs = fmaf(w4[e], k, zs);
                     }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) zs += (float)kfr[e];
             }
 #pragma unroll
             for (int ct = 0; ct < NDT; ++ct) acc[ct] = mfma_bf16(af, tr_frag<D>(Vs, h, ct, r, g), acc[ct]);
-            acc[NDT] = mfma_bf16(kfr, bw, acc[NDT]);
         }
+        zs += __shfl_xor(zs, 16, 64);
+        zs += __shfl_xor(zs, 32, 64);
 #pragma unroll
         for (int dd = 0; dd < 2; ++dd) {
             if ((KIND != kMaskLit && dd != dir) || (p.causal && dd == 1)) continue;
@@ -1348,10 +1361,12 @@ __global__ void __launch_bounds__(512) group_state_kernel(ChunkParams p) {
                 for (int e = 0; e < 4; ++e) o[e] = f2bf(acc[ct][e]);
                 *reinterpret_cast<bf16x4 *>(dst + F::wr(ct, nt, r, g)) = o;
             }
+            // the row-sum tile: row 0 the bf16 high parts, row 1 the bf16 rounding of the remainders, of key
+            // channels 16 nt + 4 g' + e held by fold lane (rr, g'): gather lane (r = 4 g' + e)'s sum
             bf16x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float z = acc[NDT][e] + __shfl_xor(acc[NDT][e], 1, 64);
+                const float z = __shfl(zs, 4 * g + e, 64);
                 const __bf16 zh = f2bf(z);
                 o[e] = r == 0 ? zh : f2bf(z - (float)zh);
             }
@@ -1363,7 +1378,7 @@ __global__ void __launch_bounds__(512) group_state_kernel(ChunkParams p) {
 
 template <int D, int ROWS>
 __host__ __device__ constexpr size_t group_state_lds() {
-    return 2 * (size_t)ROWS * D * 2 + (size_t)ROWS * 4 + 16 * 8;
+    return 2 * (size_t)ROWS * D * 2 + (size_t)ROWS * 4 + 16 * 8 + 2 * (size_t)ROWS * 4;   // + fold-weight table
 }
 
 // ================================ group scan ==========================================================
