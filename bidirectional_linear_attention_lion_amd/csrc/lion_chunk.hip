@@ -850,7 +850,8 @@ __host__ __device__ constexpr int fuse_slots() { return KIND == kMaskLit ? ROWS 
 template <int D, int KIND, int ROWS>
 __host__ __device__ constexpr size_t fused_lds(bool incoming) {
     return 2 * (size_t)ROWS * D * 2 + (size_t)fuse_slots<KIND, ROWS>() * Fuse<D>::SLOT +
-           (incoming ? 2 * (size_t)Fuse<D>::SLOTK : 0) + (size_t)ROWS * 4 + 16 * 4 + 16 * 8;
+           (incoming ? 2 * (size_t)Fuse<D>::SLOTK : 0) + (size_t)ROWS * 4 + 16 * 4 + 16 * 8 +
+           2 * (size_t)ROWS * 4;   // + the fold-weight table
 }
 
 // LION-S exponents relative to each chunk's start, E[t] = sum_{u = cs(t)}^{t} log2(lambda_u): one fp64 scan
@@ -972,13 +973,24 @@ __global__ void __launch_bounds__(ROWS / 16 * 64) chunk_fused_kernel(ChunkParams
         }
         if (c16 < rows * RT::CPK) st16(Ks + RT::off(row, (c16 % RT::CPK) * RT::VEC), o);
     }
+    // fold weights of every row of the group, forward and backward relative to its own chunk, once per
+    // workgroup; the fold reads them four at a time
+    float *W = reinterpret_cast<float *>(sh + 16);   // [2][ROWS]
+    if constexpr (KIND != kMaskLit) {
+        for (int t = tid; t < rows; t += NT) {
+            const int ccs = (t / C) * C, ccn = min(C, L - ccs);
+            const float ej = Ex(t, ccs);
+            W[t] = fast_exp2(fminf(Ex(ccs + ccn - 1, ccs) - ej, 0.f));
+            W[ROWS + t] = fast_exp2(fminf(ej, 0.f));
+        }
+    }
     __syncthreads();
 
     // ---- fold: waves 4c .. 4c+3 -> Fl_c, Gl_c ---------------------------------------------------
     // A wave always uses one key-channel tile nt (A operand), so the per-key fold weights are applied
     // once per sub-block to that fragment; the value fragments enter the products unweighted.  The
-    // row-sum tile instead takes the unweighted keys and the weights split as bf16 high part plus the
-    // bf16 rounding of the remainder (columns 0 and 1), which keeps the row sums at ~2^-17.
+    // row sums are accumulated in fp32 on the vector ALU, w times the exact key, and stored as a bf16
+    // high part plus the bf16 rounding of the remainder (~2^-17).
     if (wave < 4 * n) {
         const int c = wave >> 2, k = wave & 3;
         const int cs = c * C, cn = min(C, L - cs);
@@ -986,23 +998,23 @@ __global__ void __launch_bounds__(ROWS / 16 * 64) chunk_fused_kernel(ChunkParams
         const int nt = k % NDT;
         auto ct_of = [&](int u) { return kColOwn ? u : (k + 4 * u) / NDT; };
         auto has = [&](int u) { return kColOwn ? u < NCT : k + 4 * u < NCT * NDT; };
-        bf16x8 ones;   // LIT weight tile: weight 1 in column 0
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ones[e] = f2bf(r == 0 ? 1.f : 0.f);
         f32x4 sf[MAXT], sg[MAXT];
 #pragma unroll
         for (int u = 0; u < MAXT; ++u) sf[u] = sg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float zf = 0.f, zg = 0.f;   // row sums of key channel 16 nt + r over this lane's keys
         for (int h = cs / kKB; h < (cs + cpad(cn)) / kKB; ++h) {
             float wf[2][4], wg[2][4];
             if constexpr (KIND != kMaskLit) {
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < 2; ++t) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4 *>(W + h * kKB + 16 * t + 4 * g);
+                    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(W + ROWS + h * kKB + 16 * t + 4 * g);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float ej = Ex(h * kKB + 16 * t + 4 * g + e, cs);
-                        wf[t][e] = fast_exp2(fminf(etot - ej, 0.f));
-                        wg[t][e] = fast_exp2(fminf(ej, 0.f));
+                        wf[t][e] = a4[e];
+                        wg[t][e] = b4[e];
                     }
+                }
             }
             const bf16x8 kfr = tr_frag<D>(Ks, h, nt, r, g);
             bf16x8 af = kfr, ag = kfr;
@@ -1024,21 +1036,17 @@ __global__ void __launch_bounds__(ROWS / 16 * 64) chunk_fused_kernel(ChunkParams
                     const bf16x8 vv = tr_frag<D>(Vs, h, ct, r, g);
                     sf[u] = mfma_bf16(af, vv, sf[u]);
                     if (KIND != kMaskLit && !p.causal) sg[u] = mfma_bf16(ag, vv, sg[u]);
-                } else if constexpr (KIND == kMaskLit) {
-                    sf[u] = mfma_bf16(kfr, ones, sf[u]);
                 } else {
-                    bf16x8 bf, bg;
 #pragma unroll
-                    for (int t = 0; t < 2; ++t)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const __bf16 fh = f2bf(wf[t][e]), gh = f2bf(wg[t][e]);
-                            const __bf16 flo = f2bf(wf[t][e] - (float)fh), glo = f2bf(wg[t][e] - (float)gh);
-                            bf[4 * t + e] = r == 0 ? fh : (r == 1 ? flo : f2bf(0.f));
-                            bg[4 * t + e] = r == 0 ? gh : (r == 1 ? glo : f2bf(0.f));
+                    for (int e = 0; e < 8; ++e) {
+                        const float kv = (float)kfr[e];
+                        if constexpr (KIND == kMaskLit) {
+                            zf += kv;
+                        } else {
+                            zf = fmaf(wf[e / 4][e % 4], kv, zf);
+                            zg = fmaf(wg[e / 4][e % 4], kv, zg);
                         }
-                    sf[u] = mfma_bf16(kfr, bf, sf[u]);
-                    if (!p.causal) sg[u] = mfma_bf16(kfr, bg, sg[u]);
+                    }
                 }
             }
         }
@@ -1059,10 +1067,14 @@ __global__ void __launch_bounds__(ROWS / 16 * 64) chunk_fused_kernel(ChunkParams
                     for (int e = 0; e < 4; ++e) o[e] = f2bf(sv[e]);
                     *reinterpret_cast<bf16x4 *>(slot + F::wr(ct, nt, r, g)) = o;
                 } else {
-                    // row sums z[16 nt + 4 g + e] = columns 0 + 1
+                    // row sums z[16 nt + 4 g + e]: this lane's part summed over the four lane groups, then
+                    // gathered from the lane holding channel 16 nt + 4 g + e
+                    float zs = which == 0 ? zf : zg;
+                    zs += __shfl_xor(zs, 16, 64);
+                    zs += __shfl_xor(zs, 32, 64);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float z = sv[e] + __shfl_xor(sv[e], 1, 64);
+                        const float z = __shfl(zs, 4 * g + e, 64);
                         const __bf16 zh = f2bf(z);
                         o[e] = r == 0 ? zh : f2bf(z - (float)zh);
                     }
@@ -1248,7 +1260,7 @@ __global__ void __launch_bounds__(512) group_state_kernel(ChunkParams p) {
     using F = Fuse<D>;
     using T = __bf16;
     using RT = RowTile<D, T>;
-    constexpr int NT = 512, NDT = F::NDT, NCT = NDT + 1;
+    constexpr int NT = 512, NDT = F::NDT;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
