@@ -1552,14 +1552,17 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((chunk_scan_kernel<D, BF16>), dim3((unsigned)(a.B * a.H * 2 * NBLK)), dim3(kScanThreads), 0,
                            stream, p);
     }
-    // output workgroups: the chunk's C/16 query tiles over 4 waves (C <= 64) or 8 waves (C >= 128)
+    // output workgroups: the chunk's C/16 query tiles over 4 waves (C <= 64: one tile each; C = 128: two
+    // tiles each, which share every key and value fragment read -- 53 against 55 us on B8 H12 L4097 for
+    // 8 waves of one tile) or 8 waves (C >= 256, or d = 128)
     auto out = [&](auto kernel, int nw) {
         const size_t lds = chunk_lds<D, BF16>(a.C, nw, true);
         allow_lds(kernel, lds);
         hipLaunchKernelGGL(kernel, dim3((unsigned)nb), dim3(nw * 64), lds, stream, p);
     };
     if (a.C <= 64) out(&chunk_out_kernel<D, KIND, 4, 1, BF16, INB>, 4);
-    else if (D == 128 || a.C <= 128) out(&chunk_out_kernel<D, KIND, 8, 1, BF16, INB>, 8);
+    else if (D == 128) out(&chunk_out_kernel<D, KIND, 8, 1, BF16, INB>, 8);
+    else if (a.C <= 128) out(&chunk_out_kernel<D, KIND, 4, 2, BF16, INB>, 4);
     else out(&chunk_out_kernel<D, KIND, 8, (D == 128 ? 1 : 2), BF16, INB>, 8);
     return hipGetLastError();
 }
