@@ -128,6 +128,42 @@ __device__ __forceinline__ void dpp_dot<2>(float &y0, float &y1, float qb, const
                  : [y0] "+v"(y0), [y1] "+v"(y1)
                  : [qb] "v"(qb), [s0] "v"(S[0]), [s1] "v"(S[1]));
 }
+// As dpp_dot, but y0 and y1 start at the first two products (no accumulator to clear).
+#define LION_BC_Y0(i, a) "v_mul_f32_dpp %[" a "], %[qb], %[s" #i "] row_newbcast:" #i " row_mask:0xf bank_mask:0xf\n\t"
+template <int N>
+__device__ __forceinline__ void dpp_dot_first(float &y0, float &y1, float qb, const float *S);
+template <>
+__device__ __forceinline__ void dpp_dot_first<16>(float &y0, float &y1, float qb, const float *S) {
+    asm volatile("s_nop 1\n\t" LION_BC_Y0(0, "y0") LION_BC_Y0(1, "y1") LION_BC_Y(2, "y0") LION_BC_Y(3, "y1")
+                     LION_BC_Y(4, "y0") LION_BC_Y(5, "y1") LION_BC_Y(6, "y0") LION_BC_Y(7, "y1") LION_BC_Y(8, "y0")
+                         LION_BC_Y(9, "y1") LION_BC_Y(10, "y0") LION_BC_Y(11, "y1") LION_BC_Y(12, "y0")
+                             LION_BC_Y(13, "y1") LION_BC_Y(14, "y0") LION_BC_Y(15, "y1")
+                 : [y0] "=&v"(y0), [y1] "=&v"(y1)
+                 : [qb] "v"(qb), [s0] "v"(S[0]), [s1] "v"(S[1]), [s2] "v"(S[2]), [s3] "v"(S[3]), [s4] "v"(S[4]),
+                   [s5] "v"(S[5]), [s6] "v"(S[6]), [s7] "v"(S[7]), [s8] "v"(S[8]), [s9] "v"(S[9]), [s10] "v"(S[10]),
+                   [s11] "v"(S[11]), [s12] "v"(S[12]), [s13] "v"(S[13]), [s14] "v"(S[14]), [s15] "v"(S[15]));
+}
+template <>
+__device__ __forceinline__ void dpp_dot_first<8>(float &y0, float &y1, float qb, const float *S) {
+    asm volatile("s_nop 1\n\t" LION_BC_Y0(0, "y0") LION_BC_Y0(1, "y1") LION_BC_Y(2, "y0") LION_BC_Y(3, "y1")
+                     LION_BC_Y(4, "y0") LION_BC_Y(5, "y1") LION_BC_Y(6, "y0") LION_BC_Y(7, "y1")
+                 : [y0] "=&v"(y0), [y1] "=&v"(y1)
+                 : [qb] "v"(qb), [s0] "v"(S[0]), [s1] "v"(S[1]), [s2] "v"(S[2]), [s3] "v"(S[3]), [s4] "v"(S[4]),
+                   [s5] "v"(S[5]), [s6] "v"(S[6]), [s7] "v"(S[7]));
+}
+template <>
+__device__ __forceinline__ void dpp_dot_first<4>(float &y0, float &y1, float qb, const float *S) {
+    asm volatile("s_nop 1\n\t" LION_BC_Y0(0, "y0") LION_BC_Y0(1, "y1") LION_BC_Y(2, "y0") LION_BC_Y(3, "y1")
+                 : [y0] "=&v"(y0), [y1] "=&v"(y1)
+                 : [qb] "v"(qb), [s0] "v"(S[0]), [s1] "v"(S[1]), [s2] "v"(S[2]), [s3] "v"(S[3]));
+}
+template <>
+__device__ __forceinline__ void dpp_dot_first<2>(float &y0, float &y1, float qb, const float *S) {
+    asm volatile("s_nop 1\n\t" LION_BC_Y0(0, "y0") LION_BC_Y0(1, "y1")
+                 : [y0] "=&v"(y0), [y1] "=&v"(y1)
+                 : [qb] "v"(qb), [s0] "v"(S[0]), [s1] "v"(S[1]));
+}
+#undef LION_BC_Y0
 #undef LION_BC_S
 #undef LION_BC_Y
 
@@ -467,24 +503,43 @@ __global__ void __launch_bounds__(2 * NR * 64) __attribute__((amdgpu_waves_per_e
 
 // ---- pipelined variant --------------------------------------------------------------------------------
 // For grids of at most one workgroup per CU.  kHelp more waves take the per-block work off the
-// recurrence waves: while these run block b, the helpers reduce block b-1 (park, finish, store) and
-// stage block b+1 (phi, diagonal, scales, from rows loaded one block earlier), so one barrier per block
-// separates the roles and the recurrence waves never touch global memory.  Staging is triple-buffered
-// (b+1 is written while b is read and b-1 is still needed by its reduction), partials double-buffered.
+// recurrence waves, which then run nothing per token but the DPP products and the store of their
+// partial: while they run block b, the helpers reduce block b-1 (park, finish, store), stage block b+1
+// (phi, diagonal, k already divided by its scale Lambda_t, from rows loaded one block earlier), carry the
+// row-sum states z of both directions through block b (one helper wave per direction, lane i holding
+// z_i) and derive the scale factors of block b+2 (one helper wave).  One barrier per block separates the
+// roles and the recurrence waves never touch global memory.  Staging is triple-buffered (b+1 is written
+// while b is read and b-1 is still needed by its reduction), partials double-buffered, scale factors in
+// a ring of four blocks (b-1 reduced, b running, b+1 staged, b+2 written).
 constexpr int kHelp = 8;
 
 template <int D, int CW, int NR>
-constexpr size_t rnn_pipe_lds() {
+struct PipeLayout {
     using Sh = RnnShape<D, CW, NR>;
-    const size_t dirf = 2 * ((size_t)kT * D + 16) + (size_t)kT * D + 4 * kT;
-    const size_t psz = 2 * (size_t)kT * Sh::NP * CW + 2 * (size_t)kT * Sh::NP;
-    return (6 * dirf + 2 * psz) * 4;
+    static constexpr int QKS = kT * D + 16;              // q or k rows of a block, then 16 zero floats
+    static constexpr int DIRF = 2 * QKS + kT * D + kT;   // q, k / Lambda, v, diagonal of one direction
+    static constexpr int YP = 2 * kT * Sh::NP * CW;      // per-slice partials q^T S' of a block
+    static constexpr int PSZ = YP + 2 * kT;              // then q . z' per token and direction
+    static constexpr int RING = 3 * 2 * kT;              // [k scale, y scale, multiplier][direction][token]
+    static constexpr int ZST = 68;                       // row stride of the q . z transposition
+    // offsets in floats: partials first, so a token's partial is an immediate offset from a per-block base
+    static constexpr int PART = 0;
+    static constexpr int STG = PART + 2 * PSZ;
+    static constexpr int RNG = STG + 6 * DIRF;
+    static constexpr int ZT = RNG + 4 * RING;
+    static constexpr int TOTAL = ZT + 2 * kT * ZST;
+};
+
+template <int D, int CW, int NR>
+constexpr size_t rnn_pipe_lds() {
+    return (size_t)PipeLayout<D, CW, NR>::TOTAL * 4;
 }
 
 template <int D, int KIND, int CW, int NR, bool BF16>
 __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnParams p) {
     using T = std::conditional_t<BF16, __bf16, float>;
     using Sh = RnnShape<D, CW, NR>;
+    using Ly = PipeLayout<D, CW, NR>;
     constexpr int NS = Sh::NS, RW = Sh::RW, RB = Sh::RB, KV = Sh::KV, NG = Sh::NG, NP = Sh::NP;
     constexpr int NTD = NR * 64;               // recurrence threads per direction
     constexpr int NRT = 2 * NTD;               // recurrence threads
@@ -492,20 +547,19 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
     constexpr int TPT = D / 4;                 // staging threads per token (4 channels each)
     constexpr int PAIRS = 2 * kT * TPT;        // staging units of a block, both directions
     constexpr int PPT = (PAIRS + NHT - 1) / NHT;
-    constexpr int QKS = kT * D + 16;
-    constexpr int DIRF = 2 * QKS + kT * D + 4 * kT;
-    constexpr int PSZ = 2 * kT * NP * CW + 2 * kT * NP;
+    constexpr int QKS = Ly::QKS, DIRF = Ly::DIRF, PSZ = Ly::PSZ, YP = Ly::YP;
     constexpr int RITEMS = 2 * kT * CW;        // reduction units of a block, both directions
     constexpr int RITER = (RITEMS + NHT - 1) / NHT;
     constexpr float kRenorm = 8.673617379884035e-19f;   // 2^-60
     static_assert(RW >= 2 && RW <= 64 && RW % RB == 0, "rows per lane");
     static_assert(PAIRS % 64 == 0, "staging units per wave");
+    static_assert(kHelp >= 3, "two z waves and a scale wave");
 
     extern __shared__ __align__(16) unsigned char smem[];
     float *S0 = reinterpret_cast<float *>(smem);
-    // staging buffer of block b, direction d; partial buffer of block b
-    auto stg_of = [&](int b, int d) { return S0 + ((b % 3) * 2 + d) * DIRF; };
-    auto part_of = [&](int b) { return S0 + 6 * DIRF + (b & 1) * PSZ; };
+    auto part_of = [&](int b) { return S0 + Ly::PART + (b & 1) * PSZ; };
+    auto stg_of = [&](int b, int d) { return S0 + Ly::STG + ((b % 3) * 2 + d) * DIRF; };
+    auto ring_of = [&](int b) { return S0 + Ly::RNG + (b & 3) * Ly::RING; };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const bool helper = uniform(tid) >= NRT;
@@ -516,21 +570,72 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
     const int nblk = (L + kT - 1) / kT;
 
     if (helper) {
-        // ================= helper waves: staging and reductions =================================
+        // ================= helper waves =================================================================
         const int ht = tid - NRT;
+        const int hw = uniform(ht >> 6);
         const T *qg = reinterpret_cast<const T *>(p.q) + base * D;
         const T *kg = reinterpret_cast<const T *>(p.k) + base * D;
         const T *vg = reinterpret_cast<const T *>(p.v) + base * D;
         const float lg_head = (KIND == kMaskD) ? p.ll[bh % p.H] * kLog2e : 0.f;
         auto token_at = [&](int d, int s) { return d == 0 ? s : L - 1 - s; };
-        auto decay_at = [&](int d, int s) -> float {
-            if constexpr (KIND == kMaskLit) return 1.f;
-            else if constexpr (KIND == kMaskD) return fast_exp2(lg_head);
-            else {
-                const int td = d == 0 ? s : L - s;
-                return (s < L && td < L) ? fast_exp2(p.ll[base + td] * kLog2e) : 1.f;
+
+        // Scale factors of block b, both directions (lanes 0-15 forward, 16-31 backward; the upper half
+        // of the wave repeats them).  Inside a block the running product Lambda of the decays starts at 1;
+        // where it would fall below 2^-60 the state is multiplied by that product instead and Lambda
+        // restarts at 1.  Per token: 1 / Lambda (k scale), Lambda (y scale), the multiplier (1 if none).
+        auto scales = [&](int b) {
+            const int d = (lane >> 4) & 1, tl = lane & 15;
+            const int s = b * kT + tl;
+            float lg = 0.f;   // log2 of the decay applied at this step
+            if (s < L && !(p.causal && d == 1)) {
+                if constexpr (KIND == kMaskD) lg = lg_head;
+                else lg = (d == 0 || s > 0) ? p.ll[base + (d == 0 ? s : L - s)] * kLog2e : 0.f;
+            }
+            // Usual case: the block's running product stays above 2^-59 in both directions, so no
+            // multiplier is needed and Lambda_t = 2^(prefix sum of the log decays), summed within each
+            // 16-lane row by four DPP row shifts.
+            auto shr = [](float x, auto ctrl) {   // row_shr by ctrl - 0x110 lanes, 0 shifted in
+                return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                             decltype(ctrl)::value, 0xF, 0xF, false));
+            };
+            float ps = lg;
+            ps += shr(ps, std::integral_constant<int, 0x111>{});
+            ps += shr(ps, std::integral_constant<int, 0x112>{});
+            ps += shr(ps, std::integral_constant<int, 0x114>{});
+            ps += shr(ps, std::integral_constant<int, 0x118>{});
+            if (!__any(lane < 32 && ps < -59.f)) {
+                if (lane < 32) {
+                    float *rg = ring_of(b);
+                    rg[d * kT + tl] = fast_exp2(-ps);
+                    rg[(2 + d) * kT + tl] = fast_exp2(ps);
+                    rg[(4 + d) * kT + tl] = 1.f;
+                }
+                return;
+            }
+            // otherwise the products step by step, restarting where they would fall below 2^-60
+            const float dec = fast_exp2(lg);
+            float lam = 1.f, ys = 1.f, mu_t = 1.f;
+#pragma unroll
+            for (int u = 0; u < kT; ++u) {
+                const int i0 = __builtin_amdgcn_readlane(__builtin_bit_cast(int, dec), u);
+                const int i1 = __builtin_amdgcn_readlane(__builtin_bit_cast(int, dec), kT + u);
+                const float l2 = lam * __builtin_bit_cast(float, d == 0 ? i0 : i1);
+                const bool rn = l2 < kRenorm;
+                const float mu = rn ? l2 : 1.f;
+                lam = rn ? 1.f : l2;
+                if (u == tl) {
+                    ys = lam;
+                    mu_t = mu;
+                }
+            }
+            if (lane < 32) {
+                float *rg = ring_of(b);
+                rg[d * kT + tl] = 1.f / ys;
+                rg[(2 + d) * kT + tl] = ys;
+                rg[(4 + d) * kT + tl] = mu_t;
             }
         };
+
         using V4 = std::conditional_t<BF16, bf16x4, f32x4>;
         V4 raw[PPT][3];
         auto prefetch = [&](int b) {
@@ -546,6 +651,10 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                 }
             }
         };
+        auto tok_sum = [](float x) {
+            if constexpr (TPT == 16) return row16_sum(x);
+            else return group_sum<TPT>(x);
+        };
         auto stage = [&](int b) {
 #pragma unroll
             for (int u = 0; u < PPT; ++u) {
@@ -555,56 +664,96 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                 const int d = pr / (kT * TPT), tl = (pr % (kT * TPT)) / TPT, c4 = (pr % TPT) * 4;
                 if (p.causal && d == 1) break;        // wave-uniform: kT * TPT is a multiple of 64
                 float *st = stg_of(b, d);
-                float *Qs = st, *Ks = Qs + QKS, *Vs = Ks + QKS, *sdiag = Vs + kT * D, *ksc = sdiag + kT,
-                      *ysc = ksc + kT, *mult = ysc + kT;
+                float *Qs = st, *Ks = Qs + QKS, *Vs = Ks + QKS, *sdiag = Vs + kT * D;
                 const int s = b * kT + tl;
                 const bool valid = s < L;
-                float xq[4], xk[4], sq = 0.f, sk = 0.f;
+                f32x4 xq, xk, xv;
+                float sq = 0.f, sk = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     xq[e] = phi_pre<KIND>((float)raw[u][0][e]);
                     xk[e] = phi_pre<KIND>((float)raw[u][1][e]);
+                    xv[e] = (float)raw[u][2][e];
                     sq += xq[e] * xq[e];
                     sk += xk[e] * xk[e];
                 }
                 float fq = valid ? 1.f : 0.f, fk = fq;
                 if constexpr (KIND == kMaskS) {
-                    fq *= inv_norm(group_sum<TPT>(sq));
-                    fk *= inv_norm(group_sum<TPT>(sk));
+                    fq *= inv_norm(tok_sum(sq));
+                    fk *= inv_norm(tok_sum(sk));
                 }
+                const float ks = KIND != kMaskLit ? ring_of(b)[d * kT + tl] : 1.f;
                 float dg = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     xq[e] *= fq;
                     xk[e] *= fk;
-                    Qs[tl * D + c4 + e] = xq[e];
-                    Ks[tl * D + c4 + e] = xk[e];
-                    Vs[tl * D + c4 + e] = (float)raw[u][2][e];
                     dg += xq[e] * xk[e];
+                    xk[e] *= ks;
                 }
-                dg = group_sum<TPT>(dg);
-                if (c4 == 0) {
-                    sdiag[tl] = dg;
-                    if constexpr (KIND != kMaskLit) {
-                        // replay the block's scale sequence up to this token (every leader derives the same)
-                        float lam = 1.f, mu = 1.f;
-                        for (int u2 = 0; u2 <= tl; ++u2) {
-                            const float l2 = lam * decay_at(d, b * kT + u2);
-                            if (l2 < kRenorm) {
-                                mu = l2;
-                                lam = 1.f;
-                            } else {
-                                mu = 1.f;
-                                lam = l2;
-                            }
-                        }
-                        ksc[tl] = 1.f / lam;
-                        ysc[tl] = lam;
-                        mult[tl] = mu;
-                    }
-                }
+                *reinterpret_cast<f32x4 *>(Qs + tl * D + c4) = xq;
+                *reinterpret_cast<f32x4 *>(Ks + tl * D + c4) = xk;
+                *reinterpret_cast<f32x4 *>(Vs + tl * D + c4) = xv;
+                dg = tok_sum(dg);
+                if (c4 == 0) sdiag[tl] = dg;
             }
         };
+
+        // Row-sum state of one direction through block b (helper wave d): z' = z' m_t + k_t / Lambda_t per
+        // token, lane i holding z'_i (and z'_(i+64) for d = 128); the 16 products q_t . z'_t are summed
+        // over the lanes by a transposition through LDS and written beside the block's partials.
+        constexpr int ZR = D > 64 ? D / 64 : 1;
+        float zr[ZR], zlam = 1.f;
+#pragma unroll
+        for (int j = 0; j < ZR; ++j) zr[j] = 0.f;
+        auto zsum = [&](int b, int d) {
+            const int s0 = b * kT, nsteps = min(kT, L - s0);
+            const float *st = stg_of(b, d);
+            const float *Qs = st, *Ks = Qs + QKS;
+            const float *mult = ring_of(b) + (4 + d) * kT;
+            float *zt = S0 + Ly::ZT + d * kT * Ly::ZST;
+            if constexpr (KIND != kMaskLit) {
+#pragma unroll
+                for (int j = 0; j < ZR; ++j) zr[j] *= zlam;
+            }
+            // Every token of the block, with no branch between them, and the products kept in registers
+            // until all are done: the loads of all tokens can be in flight together.  Tokens past the end
+            // are staged with k = q = 0 and multiplier 1, so they leave z' as it is.
+            float xs[kT];
+#pragma unroll
+            for (int tl = 0; tl < kT; ++tl) {
+                float x = 0.f;
+                const float mu = KIND != kMaskLit ? mult[tl] : 1.f;
+#pragma unroll
+                for (int j = 0; j < ZR; ++j) {
+                    const int r = lane + 64 * j;
+                    if (r < D) {
+                        zr[j] = fmaf(zr[j], mu, Ks[tl * D + r]);
+                        x = fmaf(Qs[tl * D + r], zr[j], x);
+                    }
+                }
+                xs[tl] = x;
+            }
+#pragma unroll
+            for (int tl = 0; tl < kT; ++tl) zt[tl * Ly::ZST + lane] = xs[tl];
+            // the same wave reads what its lanes wrote: LDS keeps a wave's accesses in order
+            __builtin_amdgcn_wave_barrier();
+            asm volatile("" ::: "memory");
+            const int t = lane >> 2, part = lane & 3;
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(zt + t * Ly::ZST + part * 16);
+            float v = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 a = src[j];
+                v += (a[0] + a[1]) + (a[2] + a[3]);
+            }
+            v += __shfl_xor(v, 1, 64);
+            v += __shfl_xor(v, 2, 64);
+            if (part == 0) part_of(b)[YP + d * kT + t] = v;
+            if constexpr (KIND != kMaskLit) zlam = ring_of(b)[(2 + d) * kT + nsteps - 1];
+            asm volatile("" ::: "memory");
+        };
+
         // parked partials block b's reduction needs: those parked at least two iterations before the
         // reduction (partner step < s0 - kT) are loaded an iteration ahead, the rest when reduced
         float pky[RITER], pkc[RITER];
@@ -626,7 +775,8 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
         };
         auto reduce = [&](int b) {
             const int s0 = b * kT, nsteps = min(kT, L - s0);
-            const float *Yp = part_of(b), *Cp = Yp + 2 * kT * NP * CW;
+            const float *Yp = part_of(b), *Cp = Yp + YP;
+            const float *ysc = ring_of(b) + 2 * kT;   // [direction][token]
             prefetch_park(b, false);
 #pragma unroll
             for (int it = 0; it < RITER; ++it) {
@@ -634,18 +784,16 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                 const int d = idx / (kT * CW), tl = (idx % (kT * CW)) / CW, c2 = idx % CW;
                 if (idx >= RITEMS || tl >= nsteps || (p.causal && d == 1)) continue;
                 const float *st = stg_of(b, d);
-                const float *Vs = st + 2 * QKS, *sdiag = Vs + kT * D, *ysc = sdiag + 2 * kT;
+                const float *Vs = st + 2 * QKS, *sdiag = Vs + kT * D;
                 const int s = s0 + tl, sp = L - 1 - s;
                 const int t = token_at(d, s);
-                float y = 0.f, cs = 0.f;
+                float y = 0.f;
 #pragma unroll
-                for (int g = 0; g < NP; ++g) {
-                    y += Yp[((d * kT + tl) * NP + g) * CW + c2];
-                    cs += Cp[(d * kT + tl) * NP + g];
-                }
+                for (int g = 0; g < NP; ++g) y += Yp[((d * kT + tl) * NP + g) * CW + c2];
+                float cs = Cp[d * kT + tl];
                 if constexpr (KIND != kMaskLit) {
-                    y *= ysc[tl];
-                    cs *= ysc[tl];
+                    y *= ysc[d * kT + tl];
+                    cs *= ysc[d * kT + tl];
                 }
                 float yo, co, dg = 0.f;
                 if (p.causal) {
@@ -661,22 +809,18 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                     if (d == 1) continue;
                     const int tp = sp - s0;
                     yo = 0.f;
-                    co = 0.f;
 #pragma unroll
-                    for (int g = 0; g < NP; ++g) {
-                        yo += Yp[((kT + tp) * NP + g) * CW + c2];
-                        co += Cp[(kT + tp) * NP + g];
-                    }
+                    for (int g = 0; g < NP; ++g) yo += Yp[((kT + tp) * NP + g) * CW + c2];
+                    co = Cp[kT + tp];
                     if constexpr (KIND != kMaskLit) {
-                        const float ys = stg_of(b, 1)[2 * QKS + kT * D + 2 * kT + tp];   // backward scale of that token
-                        yo *= ys;
-                        co *= ys;
+                        yo *= ysc[kT + tp];   // backward scale of that token
+                        co *= ysc[kT + tp];
                     }
                 }
                 // both visits included the diagonal term: remove it once
                 if (!p.causal) dg = sdiag[tl];
                 const float div = cs + co - dg + p.eps;
-                const float out = (y + yo - dg * Vs[tl * D + cg * CW + c2]) / div;
+                const float out = (y + yo - dg * Vs[tl * D + cg * CW + c2]) * __builtin_amdgcn_rcpf(div);
                 const size_t o = (base + t) * D + cg * CW + c2;
                 if (p.out_bf16)
                     reinterpret_cast<__bf16 *>(p.y)[o] = f2bf(out);
@@ -686,12 +830,18 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
             }
         };
 
+        const bool scale_wave = KIND != kMaskLit && hw == kHelp - 1;
+        if (scale_wave) {
+            scales(0);
+            if (1 < nblk) scales(1);
+        }
+        __syncthreads();   // scale factors of blocks 0 and 1
         prefetch(0);
         stage(0);
         if (1 < nblk) prefetch(1);
-        // zeros after the last token's q and k rows of every staging buffer (read by lanes past the last
-        // slice, which multiply them by zero: they must be finite)
-        if (ht < 6 * 32) S0[(ht / 32) * DIRF + (ht % 32 < 16 ? 0 : QKS) + kT * D + (ht & 15)] = 0.f;
+        // zeros after the last token's q and k rows of every staging buffer (read, never used, by lanes
+        // past the last row slice)
+        if (ht < 6 * 32) S0[Ly::STG + (ht / 32) * DIRF + (ht % 32 < 16 ? 0 : QKS) + kT * D + (ht & 15)] = 0.f;
         __syncthreads();
         for (int it = 0; it <= nblk; ++it) {
             if (it >= 1) reduce(it - 1);
@@ -699,6 +849,8 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                 stage(it + 1);
                 if (it + 2 < nblk) prefetch(it + 2);
             }
+            if (it < nblk && hw < 2 && !(p.causal && hw == 1)) zsum(it, hw);
+            if (scale_wave && it + 2 < nblk) scales(it + 2);
             if (it < nblk) prefetch_park(it, true);
             __syncthreads();
         }
@@ -717,34 +869,23 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
     float S[RW];
 #pragma unroll
     for (int i = 0; i < RW; ++i) S[i] = 0.f;
-    float z[KV], zmask[KV];
-#pragma unroll
-    for (int m = 0; m < KV; ++m) {
-        z[m] = 0.f;
-        zmask[m] = 16 * m + (lane & 15) < RW ? 1.f : 0.f;
-    }
     float lam_end = 1.f;
+    __syncthreads();   // scale factors of blocks 0 and 1
     __syncthreads();   // block 0 staged
     const bool active = !(p.causal && dir == 1);
     for (int it = 0; it <= nblk; ++it) {
         if (it < nblk && active) {
             const int b = it, s0 = b * kT, nsteps = min(kT, L - s0);
             const float *st = stg_of(b, dir);
-            const float *Qs = st, *Ks = Qs + QKS, *Vs = Ks + QKS, *ksc = Vs + kT * D + kT, *ysc = ksc + kT,
-                        *mult = ysc + kT;
-            float *Yp = part_of(b), *Cp = Yp + 2 * kT * NP * CW;
+            const float *Qs = st, *Ks = Qs + QKS, *Vs = Ks + QKS;
+            const float *ysc = ring_of(b) + (2 + dir) * kT, *mult = ysc + 2 * kT;
+            float *yp = part_of(b) + (dir * kT * NP + slice) * CW + c;
             if constexpr (KIND != kMaskLit) {
 #pragma unroll
                 for (int i = 0; i < RW; ++i) S[i] *= lam_end;
-#pragma unroll
-                for (int m = 0; m < KV; ++m) z[m] *= lam_end;
             }
-            const float kscv = KIND != kMaskLit ? ksc[lane & 15] : 1.f;
             const float multv = KIND != kMaskLit ? mult[lane & 15] : 1.f;
             const unsigned rmask = KIND != kMaskLit ? (unsigned)(__ballot(multv != 1.f) & 0xFFFFu) : 0u;
-            auto lane_val = [](float v, int i) {
-                return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i));
-            };
             struct Tok {
                 float kb[KV], qb[KV], vj;
             };
@@ -760,45 +901,30 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                 x.vj = Vs[tl * D + col];
                 return x;
             };
-            float cpv[kT];
+            // every token of the block, past the end included: those are staged with k = q = 0 and
+            // multiplier 1, so they leave the state as it is, and their partials are never read
             Tok cur = load_tok(0);
 #pragma unroll
             for (int tl = 0; tl < kT; ++tl) {
-                cpv[tl] = 0.f;
-                if (tl >= nsteps) continue;
                 Tok nxt;
                 if (tl + 1 < kT) nxt = load_tok(tl + 1);
-                float ks = 1.f;
-                if constexpr (KIND != kMaskLit) {
-                    ks = lane_val(kscv, tl);
-                    if (rmask & (1u << tl)) {
-                        const float mu = lane_val(multv, tl);
+                if (KIND != kMaskLit && (rmask & (1u << tl))) {
+                    const float mu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, multv), tl));
 #pragma unroll
-                        for (int i = 0; i < RW; ++i) S[i] *= mu;
-#pragma unroll
-                        for (int m = 0; m < KV; ++m) z[m] *= mu;
-                    }
+                    for (int i = 0; i < RW; ++i) S[i] *= mu;
                 }
-                float y0 = 0.f, y1 = 0.f, cp = 0.f;
+                float y0, y1;
+                dpp_update<RB>(S, cur.kb[0], cur.vj);
+                dpp_dot_first<RB>(y0, y1, cur.qb[0], S);
 #pragma unroll
-                for (int m = 0; m < KV; ++m) {
-                    const float kb = cur.kb[m] * ks, qb = cur.qb[m];
-                    dpp_update<RB>(S + RB * m, kb, cur.vj);
-                    dpp_dot<RB>(y0, y1, qb, S + RB * m);
-                    z[m] += kb;
-                    cp += zmask[m] * qb * z[m];
+                for (int m = 1; m < KV; ++m) {
+                    dpp_update<RB>(S + RB * m, cur.kb[m], cur.vj);
+                    dpp_dot<RB>(y0, y1, cur.qb[m], S + RB * m);
                 }
-                cpv[tl] = cp;
-                Yp[((dir * kT + tl) * NP + slice) * CW + c] = y0 + y1;
+                yp[tl * NP * CW] = y0 + y1;
                 if (tl + 1 < kT) cur = nxt;
             }
             if constexpr (KIND != kMaskLit) lam_end = ysc[nsteps - 1];
-#pragma unroll
-            for (int tl = 0; tl < kT; ++tl) cpv[tl] = row16_sum(cpv[tl]);
-            if (c == 0) {
-#pragma unroll
-                for (int tl = 0; tl < kT; ++tl) Cp[(dir * kT + tl) * NP + slice] = cpv[tl];
-            }
         }
         __syncthreads();
     }
