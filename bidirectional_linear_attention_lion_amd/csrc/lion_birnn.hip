@@ -553,7 +553,10 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
     constexpr float kRenorm = 8.673617379884035e-19f;   // 2^-60
     static_assert(RW >= 2 && RW <= 64 && RW % RB == 0, "rows per lane");
     static_assert(PAIRS % 64 == 0, "staging units per wave");
-    static_assert(kHelp >= 3, "two z waves and a scale wave");
+    static_assert(kHelp >= 3, "two z waves and at least one reducing wave");
+    // state update on the matrix cores (see the recurrence waves), not for fp32 inputs with 16 or more
+    // rows per lane (registers)
+    constexpr bool kMatrixUpdate = RW % 4 == 0 && (BF16 || RW < 16);
 
     extern __shared__ __align__(16) unsigned char smem[];
     float *S0 = reinterpret_cast<float *>(smem);
@@ -571,6 +574,9 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
 
     if (helper) {
         // ================= helper waves =================================================================
+        // Their work per block is the longer path (the recurrence waves wait at the barrier), so they
+        // take the issue slots first where both are ready.
+        __builtin_amdgcn_s_setprio(1);
         const int ht = tid - NRT;
         const int hw = uniform(ht >> 6);
         const T *qg = reinterpret_cast<const T *>(p.q) + base * D;
@@ -719,20 +725,37 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
             // Every token of the block, with no branch between them, and the products kept in registers
             // until all are done: the loads of all tokens can be in flight together.  Tokens past the end
             // are staged with k = q = 0 and multiplier 1, so they leave z' as it is.
+            // Loads of half a block at a time (a quarter with fp32 inputs) issued before any use (the compiler otherwise waits for
+            // each token's loads in turn).
+            constexpr int kH = BF16 ? kT / 2 : kT / 4;   // (fewer at a time with fp32 inputs: registers)
             float xs[kT];
 #pragma unroll
-            for (int tl = 0; tl < kT; ++tl) {
-                float x = 0.f;
-                const float mu = KIND != kMaskLit ? mult[tl] : 1.f;
+            for (int h = 0; h < kT / kH; ++h) {
+                float kz[kH][ZR], qz[kH][ZR], mz[kH];
 #pragma unroll
-                for (int j = 0; j < ZR; ++j) {
-                    const int r = lane + 64 * j;
-                    if (r < D) {
-                        zr[j] = fmaf(zr[j], mu, Ks[tl * D + r]);
-                        x = fmaf(Qs[tl * D + r], zr[j], x);
+                for (int u = 0; u < kH; ++u) {
+                    const int tl = h * kH + u;
+                    mz[u] = KIND != kMaskLit ? mult[tl] : 1.f;
+#pragma unroll
+                    for (int j = 0; j < ZR; ++j) {
+                        const int r = min(lane + 64 * j, D - 1);
+                        kz[u][j] = Ks[tl * D + r];
+                        qz[u][j] = Qs[tl * D + r];
                     }
                 }
-                xs[tl] = x;
+                asm volatile("" ::: "memory");   // keep the loads above
+#pragma unroll
+                for (int u = 0; u < kH; ++u) {
+                    float x = 0.f;
+#pragma unroll
+                    for (int j = 0; j < ZR; ++j) {
+                        if (lane + 64 * j < D) {
+                            zr[j] = fmaf(zr[j], mz[u], kz[u][j]);
+                            x = fmaf(qz[u][j], zr[j], x);
+                        }
+                    }
+                    xs[h * kH + u] = x;
+                }
             }
 #pragma unroll
             for (int tl = 0; tl < kT; ++tl) zt[tl * Ly::ZST + lane] = xs[tl];
@@ -778,24 +801,44 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
             const float *Yp = part_of(b), *Cp = Yp + YP;
             const float *ysc = ring_of(b) + 2 * kT;   // [direction][token]
             prefetch_park(b, false);
+            // Every item's LDS operands first (indices past the end clamped: read, never used), then the
+            // arithmetic, so the block's reduction waits for LDS once rather than once per partial.
+            // items loaded together (registers: one at a time for fp32 inputs with four or more items)
+            constexpr int kPair = (RITER < 2 || (!BF16 && RITER > 2)) ? 1 : 2;
 #pragma unroll
-            for (int it = 0; it < RITER; ++it) {
+            for (int i0 = 0; i0 < RITER; i0 += kPair) {
+            float pp[kPair][NP], csl[kPair], scl[kPair], dgl[kPair], vl[kPair];
+#pragma unroll
+            for (int j = 0; j < kPair; ++j) {
+                const int it = i0 + j;
+                const int ic = min(ht + NHT * it, RITEMS - 1);
+                const int d = ic / (kT * CW), tl = (ic % (kT * CW)) / CW, c2 = ic % CW;
+#pragma unroll
+                for (int g = 0; g < NP; ++g) pp[j][g] = Yp[((d * kT + tl) * NP + g) * CW + c2];
+                csl[j] = Cp[d * kT + tl];
+                scl[j] = KIND != kMaskLit ? ysc[d * kT + tl] : 1.f;
+                const float *Vs = stg_of(b, d) + 2 * QKS;
+                dgl[j] = Vs[kT * D + tl];
+                vl[j] = Vs[tl * D + cg * CW + c2];
+            }
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < kPair; ++j) {
+                const int it = i0 + j;
                 const int idx = ht + NHT * it;
                 const int d = idx / (kT * CW), tl = (idx % (kT * CW)) / CW, c2 = idx % CW;
                 if (idx >= RITEMS || tl >= nsteps || (p.causal && d == 1)) continue;
-                const float *st = stg_of(b, d);
-                const float *Vs = st + 2 * QKS, *sdiag = Vs + kT * D;
                 const int s = s0 + tl, sp = L - 1 - s;
                 const int t = token_at(d, s);
-                float y = 0.f;
+                float ps[NP];
 #pragma unroll
-                for (int g = 0; g < NP; ++g) y += Yp[((d * kT + tl) * NP + g) * CW + c2];
-                float cs = Cp[d * kT + tl];
-                if constexpr (KIND != kMaskLit) {
-                    y *= ysc[d * kT + tl];
-                    cs *= ysc[d * kT + tl];
-                }
-                float yo, co, dg = 0.f;
+                for (int g = 0; g < NP; ++g) ps[g] = pp[j][g];
+#pragma unroll
+                for (int w = 1; w < NP; w <<= 1)
+#pragma unroll
+                    for (int g = 0; g + w < NP; g += 2 * w) ps[g] += ps[g + w];
+                float y = ps[0] * scl[j], cs = csl[j] * scl[j];
+                float yo, co;
                 if (p.causal) {
                     yo = co = 0.f;                        // the forward visit alone
                 } else if (sp >= s0 + nsteps) {
@@ -817,10 +860,14 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                         co *= ysc[kT + tp];
                     }
                 }
-                // both visits included the diagonal term: remove it once
-                if (!p.causal) dg = sdiag[tl];
-                const float div = cs + co - dg + p.eps;
-                const float out = (y + yo - dg * Vs[tl * D + cg * CW + c2]) * __builtin_amdgcn_rcpf(div);
+                // q . z' of both visits includes the diagonal term q_t . k_t: remove it once.  With the
+                // update on the matrix cores the partials q^T S' leave (q_t . k_t) v_t out: add it once;
+                // otherwise both visits include it: remove it once
+                const float dg = dgl[j];
+                const float dgc = p.causal ? 0.f : dg;
+                const float dgy = kMatrixUpdate ? dg : -dgc;
+                const float div = cs + co - dgc + p.eps;
+                const float out = (y + yo + dgy * vl[j]) * __builtin_amdgcn_rcpf(div);
                 const size_t o = (base + t) * D + cg * CW + c2;
                 if (p.out_bf16)
                     reinterpret_cast<__bf16 *>(p.y)[o] = f2bf(out);
@@ -828,8 +875,11 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                     reinterpret_cast<float *>(p.y)[o] = out;
                 if (p.den_out && cg == 0 && c2 == 0) p.den_out[base + t] = div;
             }
+            }
         };
 
+        // all helper waves stage and reduce; waves 0 and 1 also carry the row-sum states, the last one the
+        // scale factors (each on a SIMD of its own)
         const bool scale_wave = KIND != kMaskLit && hw == kHelp - 1;
         if (scale_wave) {
             scales(0);
@@ -866,9 +916,19 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
     const int rb = slice * RW;
     const int col = cg * CW + c;
 
-    float S[RW];
+    // State rows rb .. rb+RW-1 of column col, as RW/4 vectors: with a multiple of 4 rows per lane the
+    // update S' += (k / Lambda) v^T runs on the matrix cores, v_mfma_f32_4x4x1f32 being 16 independent
+    // 4 x 4 outer products per wave (output register r of lane l is row r of the 4-lane group's block:
+    // the k of that row comes from lane 4 (l / 4) + r, the v from lane l itself).  The state is then
+    // double-buffered: token t's product writes one copy while its dot product q^T S reads the other,
+    // S'_(t-1), written a token earlier, so the vector units never wait for the matrix cores; the
+    // diagonal term (q_t . k_t) v_t this leaves out is added in the reduction.  Otherwise (2 rows per
+    // lane, or fp32 inputs with 16 or more) the update is DPP FMAs in place and the dot product reads S'_t.
+    constexpr bool kMU = kMatrixUpdate;
+    constexpr int NM = (RW + 3) / 4;
+    f32x4 Sa[NM], Sb[NM];
 #pragma unroll
-    for (int i = 0; i < RW; ++i) S[i] = 0.f;
+    for (int m = 0; m < NM; ++m) Sa[m] = Sb[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     float lam_end = 1.f;
     __syncthreads();   // scale factors of blocks 0 and 1
     __syncthreads();   // block 0 staged
@@ -882,12 +942,12 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
             float *yp = part_of(b) + (dir * kT * NP + slice) * CW + c;
             if constexpr (KIND != kMaskLit) {
 #pragma unroll
-                for (int i = 0; i < RW; ++i) S[i] *= lam_end;
+                for (int m = 0; m < NM; ++m) Sa[m] *= lam_end;
             }
             const float multv = KIND != kMaskLit ? mult[lane & 15] : 1.f;
             const unsigned rmask = KIND != kMaskLit ? (unsigned)(__ballot(multv != 1.f) & 0xFFFFu) : 0u;
             struct Tok {
-                float kb[KV], qb[KV], vj;
+                float ka[kMU ? NM : 1], kb[KV], qb[KV], vj;
             };
             auto load_tok = [&](int tl) {
                 Tok x;
@@ -895,35 +955,74 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                 const float *krow = Ks + tl * D + rb + (lane & 15);
 #pragma unroll
                 for (int m = 0; m < KV; ++m) {
-                    x.kb[m] = krow[16 * m];
+                    if constexpr (!kMU) x.kb[m] = krow[16 * m];
                     x.qb[m] = qrow[16 * m];
+                }
+                if constexpr (kMU) {
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) x.ka[m] = Ks[tl * D + rb + 4 * m + (lane & 3)];
                 }
                 x.vj = Vs[tl * D + col];
                 return x;
             };
-            // every token of the block, past the end included: those are staged with k = q = 0 and
-            // multiplier 1, so they leave the state as it is, and their partials are never read
-            Tok cur = load_tok(0);
-#pragma unroll
-            for (int tl = 0; tl < kT; ++tl) {
-                Tok nxt;
-                if (tl + 1 < kT) nxt = load_tok(tl + 1);
+            // one token: rs holds S'_(t-1) on entry; the update goes to ws (the other copy) with the
+            // matrix cores, or to rs itself with DPP FMAs
+            auto step = [&](int tl, const Tok &x, f32x4 (&rs)[NM], f32x4 (&ws)[NM]) {
                 if (KIND != kMaskLit && (rmask & (1u << tl))) {
                     const float mu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, multv), tl));
 #pragma unroll
-                    for (int i = 0; i < RW; ++i) S[i] *= mu;
+                    for (int m = 0; m < NM; ++m) rs[m] *= mu;
                 }
                 float y0, y1;
-                dpp_update<RB>(S, cur.kb[0], cur.vj);
-                dpp_dot_first<RB>(y0, y1, cur.qb[0], S);
+                if constexpr (kMU) {
 #pragma unroll
-                for (int m = 1; m < KV; ++m) {
-                    dpp_update<RB>(S + RB * m, cur.kb[m], cur.vj);
-                    dpp_dot<RB>(y0, y1, cur.qb[m], S + RB * m);
+                    for (int m = 0; m < NM; ++m) {
+                        ws[m] = __builtin_amdgcn_mfma_f32_4x4x1f32(x.ka[m], x.vj, rs[m], 0, 0, 0);
+                        // issue this token's product before its dot product (an empty asm statement
+                        // taking its result keeps the compiler from moving it below the asm dot): the
+                        // dot then reads rs, written by the product issued a whole token earlier, far
+                        // more than the 4 wait states a vector read of that result needs
+                        asm volatile("" ::"v"(ws[m]));
+                    }
+                    float sr[RW];
+#pragma unroll
+                    for (int i = 0; i < RW; ++i) sr[i] = rs[i / 4][i % 4];
+                    dpp_dot_first<RB>(y0, y1, x.qb[0], sr);
+#pragma unroll
+                    for (int m = 1; m < KV; ++m) dpp_dot<RB>(y0, y1, x.qb[m], sr + RB * m);
+                } else {
+                    float sr[RW];
+#pragma unroll
+                    for (int i = 0; i < RW; ++i) sr[i] = rs[i / 4][i % 4];
+                    dpp_update<RB>(sr, x.kb[0], x.vj);
+                    dpp_dot_first<RB>(y0, y1, x.qb[0], sr);
+#pragma unroll
+                    for (int m = 1; m < KV; ++m) {
+                        dpp_update<RB>(sr + RB * m, x.kb[m], x.vj);
+                        dpp_dot<RB>(y0, y1, x.qb[m], sr + RB * m);
+                    }
+#pragma unroll
+                    for (int i = 0; i < RW; ++i) rs[i / 4][i % 4] = sr[i];
                 }
                 yp[tl * NP * CW] = y0 + y1;
-                if (tl + 1 < kT) cur = nxt;
+            };
+            // every token of the block, past the end included: those are staged with k = q = 0 and
+            // multiplier 1, so they leave the state as it is, and their partials are never read
+            // a token's operands are loaded one token ahead (measured: deeper is slower)
+            constexpr int kAhead = 1;
+            Tok tk[kAhead + 1];
+#pragma unroll
+            for (int u = 0; u < kAhead; ++u) tk[u] = load_tok(u);
+#pragma unroll
+            for (int tl = 0; tl < kT; ++tl) {
+                if (tl + kAhead < kT) tk[(tl + kAhead) % (kAhead + 1)] = load_tok(tl + kAhead);
+                const Tok &cur = tk[tl % (kAhead + 1)];
+                if (!kMU || (tl & 1) == 0)
+                    step(tl, cur, Sa, Sb);
+                else
+                    step(tl, cur, Sb, Sa);
             }
+            // kT is even: after the block the state is in Sa again
             if constexpr (KIND != kMaskLit) lam_end = ysc[nsteps - 1];
         }
         __syncthreads();
