@@ -725,9 +725,9 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
             // Every token of the block, with no branch between them, and the products kept in registers
             // until all are done: the loads of all tokens can be in flight together.  Tokens past the end
             // are staged with k = q = 0 and multiplier 1, so they leave z' as it is.
-            // Loads of half a block at a time (a quarter with fp32 inputs) issued before any use (the compiler otherwise waits for
-            // each token's loads in turn).
-            constexpr int kH = BF16 ? kT / 2 : kT / 4;   // (fewer at a time with fp32 inputs: registers)
+            // The block's loads (or a part at a time) issued before any use (the compiler
+            // otherwise waits for each token's loads in turn).
+            constexpr int kH = !BF16 ? kT / 4 : RW >= 16 ? kT / 2 : kT;   // (fewer at a time where registers are short)
             float xs[kT];
 #pragma unroll
             for (int h = 0; h < kT / kH; ++h) {
@@ -770,8 +770,13 @@ __global__ void __launch_bounds__((2 * NR + kHelp) * 64) birnn_pipe_kernel(RnnPa
                 const f32x4 a = src[j];
                 v += (a[0] + a[1]) + (a[2] + a[3]);
             }
-            v += __shfl_xor(v, 1, 64);
-            v += __shfl_xor(v, 2, 64);
+            // sum over the 4 lanes of a token (DPP quad permutations: no LDS round trip)
+            auto qp = [](float x, auto ctrl) {
+                return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                             decltype(ctrl)::value, 0xF, 0xF, true));
+            };
+            v += qp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+            v += qp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
             if (part == 0) part_of(b)[YP + d * kT + t] = v;
             if constexpr (KIND != kMaskLit) zlam = ring_of(b)[(2 + d) * kT + nsteps - 1];
             asm volatile("" ::: "memory");
