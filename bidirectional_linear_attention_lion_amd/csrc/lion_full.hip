@@ -397,6 +397,17 @@ __device__ __forceinline__ void full_epilogue(FullWave<D, QT, BF16> &w, const Fu
 // LDS as one stage or as double-buffered stages.  It keeps the sub-block arithmetic of the helpers above
 // written out in place: built from the helpers it compiled to fewer registers but measured 6-7% slower
 // (B64 H12 L197 D, 36.3 vs 33.8 us on one box).
+// Lane i of the lane's 16-lane row (DPP row_newbcast; the multiply that uses it takes it as a DPP operand).
+__device__ __forceinline__ float row_bcast(float x, int i) {
+    switch (i) {
+#define LION_RB(I) \
+    case I: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + I, 0xF, 0xF, false));
+    LION_RB(0) LION_RB(1) LION_RB(2) LION_RB(3) LION_RB(4) LION_RB(5) LION_RB(6) LION_RB(7)
+#undef LION_RB
+    default: return x;
+    }
+}
+
 template <int D, int KIND, int QT, bool BF16, bool TWO, bool INB = BF16>
 __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
     using C = FullCfg<D, BF16>;
@@ -656,9 +667,11 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
                         }
                     }
             }
-            // per-key mask data of the 8 keys this lane touches, j0 + 16t + 4g + e: the exponent in the
-            // overlap region, the column factor elsewhere
-            float mk[2][4], fk[2][4];
+            // per-key mask data of the 8 keys this lane touches, j0 + 16t + 4g + e: the exponents in the
+            // overlap region.  Elsewhere the column factor of a key is the same for the 16 lanes of a row
+            // (one lane group g): lane r < 8 of the row computes that of key j0 + 16 (r / 4) + 4g + r % 4,
+            // and the mask multiply takes it from that lane with a DPP row broadcast.
+            float mk[2][4], fk[2][4], mkl = 1.f;
             if constexpr (TWO) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -668,12 +681,16 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
                 }
             }
             if constexpr (KIND != kMaskLit) {
+                if (region == 0) {
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const f32x4 e4 = *reinterpret_cast<const f32x4 *>(E + j0 + 16 * t + 4 * g);
+                    for (int t = 0; t < 2; ++t) {
+                        const f32x4 e4 = *reinterpret_cast<const f32x4 *>(E + j0 + 16 * t + 4 * g);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        mk[t][e] = region == 0 ? e4[e] : fast_exp2(region == 1 ? e_first - e4[e] : e4[e] - e_last);
+                        for (int e = 0; e < 4; ++e) mk[t][e] = e4[e];
+                    }
+                } else {
+                    const float ej = E[j0 + 16 * ((r >> 2) & 1) + 4 * g + (r & 3)];
+                    mkl = fast_exp2(region == 1 ? e_first - ej : ej - e_last);
                 }
             }
             // V^T fragments (A operand of O^T += V^T P^T): keys j0 + 4g + e and j0 + 16 + 4g + e of
@@ -729,7 +746,7 @@ __global__ void __launch_bounds__(512) full_kernel(FullParams p) {
 #pragma unroll
                     for (int t = 0; t < 2; ++t)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) pv[t][e] = (sacc[t][e] * rowf) * mk[t][e];
+                        for (int e = 0; e < 4; ++e) pv[t][e] = row_bcast(mkl, 4 * t + e) * (sacc[t][e] * rowf);
                 }
                 if (p.causal && region == 0) {
                     // keys after this lane's query row are masked out
