@@ -191,6 +191,18 @@ __device__ __forceinline__ void store4(void *base, bool bf16, size_t off, f32x4 
 
 // ================================ dq ==================================================================
 // TT query tiles per wave: the key/value fragments a sub-block reads from LDS serve all of them.
+// Lane i (< 8) of the lane's 16-lane row (DPP row_newbcast; a multiply that uses it takes it as a DPP
+// operand).
+__device__ __forceinline__ float bwd_bcast16(float x, int i) {
+    switch (i) {
+#define LION_RB(I) \
+    case I: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + I, 0xF, 0xF, false));
+    LION_RB(0) LION_RB(1) LION_RB(2) LION_RB(3) LION_RB(4) LION_RB(5) LION_RB(6) LION_RB(7)
+#undef LION_RB
+    default: return x;
+    }
+}
+
 template <int D, int KIND, int TT>
 __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdParams p) {
     using T = __bf16;
@@ -258,6 +270,20 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdParams p) {
         for (int ct = 0; ct < NCT; ++ct) acc[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int wlast = min((wt0 + TT) * 16, L) - 1;   // the wave's last query row
+    // Separable mask for 32-key sub-blocks wholly before or after the wave's rows (first row w0, last
+    // wlast; the exponents decrease along the sequence): M_ij = exp2(E_i - E_w0) exp2(E_w0 - E_j) for
+    // keys before, exp2(E_wl - E_i) exp2(E_j - E_wl) for keys after, every factor at most 1.  The row
+    // factor is per tile; a key's column factor is the same for the 16 lanes of a row, so lane r < 8
+    // computes that of key j0 + 16 (r / 4) + 4g + r % 4 and the others take it by DPP row broadcast.
+    const int w0 = wt0 * 16;
+    const float e_first = KIND != kMaskLit && active ? uniform(E[min(w0, L - 1)]) : 0.f;
+    const float e_last = KIND != kMaskLit && active ? uniform(E[max(wlast, 0)]) : 0.f;
+    float rowf_b[TT], rowf_a[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        rowf_b[tt] = KIND != kMaskLit ? fast_exp2(Ei[tt] - e_first) : 1.f;
+        rowf_a[tt] = KIND != kMaskLit ? fast_exp2(e_last - Ei[tt]) : 1.f;
+    }
 
     // causal: stages wholly after the workgroup's last query row are never needed
     const int nst_used = p.causal ? min(nst, (min((sb + 1) * nw * TT * 16, L) - 1) / SK + 1) : nst;
@@ -298,11 +324,21 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdParams p) {
             auto krow = [&](int t, int st) { return TT > 1 ? kr[t][st] : rows_frag<D>(kbuf, h, t, st, r, g); };
             auto vrow = [&](int t, int st) { return TT > 1 ? vr[t][st] : rows_frag<D>(vbuf, h, t, st, r, g); };
             auto ktr = [&](int ct) { return TT > 1 ? kt[ct] : tr_frag<D>(kbuf, h, ct, r, g); };
+            // region of this sub-block relative to the wave's rows (wave-uniform): 0 overlap, 1 every key
+            // before every row, 2 every key after every row
+            const int region = j0 + kKB - 1 < w0 ? 1 : j0 > wlast ? 2 : 0;
             f32x4 ej[2];
+            float cl = 1.f;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                ej[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if constexpr (KIND != kMaskLit) ej[t] = *reinterpret_cast<const f32x4 *>(E + j0 + 16 * t + 4 * g);
+            for (int t = 0; t < 2; ++t) ej[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (KIND != kMaskLit) {
+                if (region == 0) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) ej[t] = *reinterpret_cast<const f32x4 *>(E + j0 + 16 * t + 4 * g);
+                } else {
+                    const float e = E[j0 + 16 * ((r >> 2) & 1) + 4 * g + (r & 3)];
+                    cl = fast_exp2(region == 1 ? e_first - e : e - e_last);
+                }
             }
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) {
@@ -320,18 +356,34 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdParams p) {
                 // element (t, e): key j = j0 + 16 t + 4 g + e, query irow[tt]
                 const int i = irow[tt];
                 bf16x8 dsf;
+                if (region == 0) {
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                    for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int j = j0 + 16 * t + 4 * g + e;
-                        float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(Ei[tt] - ej[t][e])) : 1.f;
-                        if (p.causal && j > i) m = 0.f;
-                        const float dp = dpacc[t][e] * inv_den[tt] - delta_i[tt];
-                        const float w = dp * (sacc[t][e] * m);
-                        rowterm[tt] += j < i ? w : (j > i ? -w : 0.f);
-                        dsf[4 * t + e] = f2bf(dp * m);
-                    }
+                        for (int e = 0; e < 4; ++e) {
+                            const int j = j0 + 16 * t + 4 * g + e;
+                            float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(Ei[tt] - ej[t][e])) : 1.f;
+                            if (p.causal && j > i) m = 0.f;
+                            const float dp = dpacc[t][e] * inv_den[tt] - delta_i[tt];
+                            const float w = dp * (sacc[t][e] * m);
+                            rowterm[tt] += j < i ? w : (j > i ? -w : 0.f);
+                            dsf[4 * t + e] = f2bf(dp * m);
+                        }
+                } else {
+                    // every key on one side of the row (keys after the rows never reach here when causal)
+                    const float rowf = region == 1 ? rowf_b[tt] : rowf_a[tt];
+                    float wsum = 0.f;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float m = KIND != kMaskLit ? bwd_bcast16(cl, 4 * t + e) * rowf : 1.f;
+                            const float dp = dpacc[t][e] * inv_den[tt] - delta_i[tt];
+                            wsum += dp * (sacc[t][e] * m);
+                            dsf[4 * t + e] = f2bf(dp * m);
+                        }
+                    rowterm[tt] += region == 1 ? wsum : -wsum;
+                }
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) acc[tt][ct] = mfma_bf16(ktr(ct), dsf, acc[tt][ct]);
             }
@@ -434,6 +486,14 @@ __global__ void __launch_bounds__(512) bwd_dkv_kernel(BwdParams p) {
         for (int ct = 0; ct < NCT; ++ct) acck[tt][ct] = accv[tt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int wfirst = wt0 * 16;                     // the wave's first key row
+    const int wlast = min((wt0 + TT) * 16, L) - 1;   // and its last
+    // Separable mask for 32-query sub-blocks wholly before or after the wave's keys (the exponents
+    // decrease along the sequence): M_ij = exp2(E_j - E_wf) exp2(E_wf - E_i) for queries before,
+    // exp2(E_wl - E_j) exp2(E_i - E_wl) for queries after, every factor at most 1.  The key factor is per
+    // tile (formed per sub-block: registers); lane r < 8 computes the factor of query
+    // i0 + 16 (r / 4) + 4g + r % 4 and the row's other lanes take it by DPP row broadcast.
+    const float e_first = KIND != kMaskLit && active ? uniform(E[min(wfirst, L - 1)]) : 0.f;
+    const float e_last = KIND != kMaskLit && active ? uniform(E[max(wlast, 0)]) : 0.f;
 
     for (int s = s_begin; s < nst; ++s) {
         const int buf = p.nbuf == 1 ? 0 : (s & 1);
@@ -476,7 +536,18 @@ __global__ void __launch_bounds__(512) bwd_dkv_kernel(BwdParams p) {
             auto grow = [&](int t, int st) { return TT > 1 ? gr[t][st] : rows_frag<D>(gbuf, h, t, st, r, g); };
             auto qtr = [&](int ct) { return TT > 1 ? qt[ct] : tr_frag<D>(qbuf, h, ct, r, g); };
             auto gtr = [&](int ct) { return TT > 1 ? gt[ct] : tr_frag<D>(gbuf, h, ct, r, g); };
-            // the queries' 1/den, delta and mask exponents (elements 4 g + e of half t)
+            // region of this sub-block relative to the wave's keys (wave-uniform): 0 overlap, 1 every query
+            // before every key (never reached when causal), 2 every query after every key
+            const int region = i0 + kKB - 1 < wfirst ? 1 : i0 > wlast ? 2 : 0;
+            float cl = 1.f;
+            if constexpr (KIND != kMaskLit) {
+                if (region != 0) {
+                    const float e = E[i0 + 16 * ((r >> 2) & 1) + 4 * g + (r & 3)];
+                    cl = fast_exp2(region == 1 ? e_first - e : e - e_last);
+                }
+            }
+            // the queries' 1/den, delta and mask exponents (elements 4 g + e of half t; the exponents only
+            // where the sub-block overlaps the wave's keys)
             auto query_vals = [&](int t, f32x4 &inv, f32x4 &dl, f32x4 &ei) {
                 const int ib = i0 + 16 * t + 4 * g;
                 const f32x4 dn = *reinterpret_cast<const f32x4 *>(denT + ib);
@@ -484,7 +555,8 @@ __global__ void __launch_bounds__(512) bwd_dkv_kernel(BwdParams p) {
                 for (int e = 0; e < 4; ++e) inv[e] = __builtin_amdgcn_rcpf(dn[e]);
                 dl = *reinterpret_cast<const f32x4 *>(dlT + ib);
                 ei = f32x4{0.f, 0.f, 0.f, 0.f};
-                if constexpr (KIND != kMaskLit) ei = *reinterpret_cast<const f32x4 *>(E + ib);
+                if constexpr (KIND != kMaskLit)
+                    if (region == 0) ei = *reinterpret_cast<const f32x4 *>(E + ib);
             };
             f32x4 inv2[2], dl2[2], ei2[2];
             if constexpr (TT > 1) {
@@ -507,6 +579,9 @@ __global__ void __launch_bounds__(512) bwd_dkv_kernel(BwdParams p) {
                 // element (t, e): query i = i0 + 16 t + 4 g + e, key jrow[tt]
                 const int j = jrow[tt];
                 bf16x8 pf, dsf;
+                float wsum = 0.f;
+                const float keyf = KIND != kMaskLit && region != 0
+                                       ? fast_exp2(region == 1 ? Ej[tt] - e_first : e_last - Ej[tt]) : 1.f;
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     f32x4 inv, dl, ei;
@@ -517,19 +592,32 @@ __global__ void __launch_bounds__(512) bwd_dkv_kernel(BwdParams p) {
                     } else {
                         query_vals(t, inv, dl, ei);
                     }
+                    if (region == 0) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = i0 + 16 * t + 4 * g + e;
-                        float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(ei[e] - Ej[tt])) : 1.f;
-                        if (p.causal && j > i) m = 0.f;
-                        const float pm = sacc[t][e] * m;
-                        const float dp = dpacc[t][e] * inv[e] - dl[e];
-                        const float w = dp * pm;
-                        colterm[tt] += i < j ? w : (i > j ? -w : 0.f);
-                        pf[4 * t + e] = f2bf(pm * inv[e]);
-                        dsf[4 * t + e] = f2bf(dp * m);
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = i0 + 16 * t + 4 * g + e;
+                            float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(ei[e] - Ej[tt])) : 1.f;
+                            if (p.causal && j > i) m = 0.f;
+                            const float pm = sacc[t][e] * m;
+                            const float dp = dpacc[t][e] * inv[e] - dl[e];
+                            const float w = dp * pm;
+                            colterm[tt] += i < j ? w : (i > j ? -w : 0.f);
+                            pf[4 * t + e] = f2bf(pm * inv[e]);
+                            dsf[4 * t + e] = f2bf(dp * m);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float m = KIND != kMaskLit ? bwd_bcast16(cl, 4 * t + e) * keyf : 1.f;
+                            const float pm = sacc[t][e] * m;
+                            const float dp = dpacc[t][e] * inv[e] - dl[e];
+                            wsum += dp * pm;
+                            pf[4 * t + e] = f2bf(pm * inv[e]);
+                            dsf[4 * t + e] = f2bf(dp * m);
+                        }
                     }
                 }
+                if (region != 0) colterm[tt] += region == 1 ? wsum : -wsum;
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
                     accv[tt][ct] = mfma_bf16(gtr(ct), pf, accv[tt][ct]);
