@@ -678,22 +678,39 @@ __global__ void __launch_bounds__(kDllThreads) bwd_dll_s_kernel(BwdParams p) {
     }
 }
 
-// LION-D: one workgroup per head: dll_h = sum over batch entries and tokens of t (da_row_t + da_col_t).
-__global__ void __launch_bounds__(kDllThreads) bwd_dll_d_kernel(BwdParams p, int B) {
+// LION-D: dll_h = sum over batch entries and tokens of t (da_row_t + da_col_t), in two launches so the
+// token sums spread over every (batch, head) rather than one workgroup per head.  The first forms the
+// fp64 sum of one (batch, head) row and leaves it as two floats (hi, lo) in element 0 of its da_row and
+// da_col rows (token 0 contributes nothing, and every read of the row precedes the barriers of the
+// reduction); the second adds a head's B partials.
+__global__ void __launch_bounds__(kDllThreads) bwd_dll_d_rows_kernel(BwdParams p) {
     __shared__ double sh[kDllThreads];
-    const int tid = threadIdx.x, L = p.L, h = blockIdx.x;
+    const int tid = threadIdx.x, L = p.L;
+    const size_t base = (size_t)blockIdx.x * L;
     double s = 0.0;
-    for (int b = 0; b < B; ++b) {
-        const size_t base = ((size_t)b * p.H + h) * L;
-        for (int t = tid; t < L; t += kDllThreads) s += (double)t * ((double)p.da_row[base + t] + (double)p.da_col[base + t]);
-    }
+    for (int t = tid; t < L; t += kDllThreads) s += (double)t * ((double)p.da_row[base + t] + (double)p.da_col[base + t]);
     sh[tid] = s;
     __syncthreads();
     for (int o = kDllThreads / 2; o > 0; o >>= 1) {
         if (tid < o) sh[tid] += sh[tid + o];
         __syncthreads();
     }
-    if (tid == 0) p.dll[h] = (float)sh[0];
+    if (tid == 0) {
+        const float hi = (float)sh[0];
+        p.da_row[base] = hi;
+        p.da_col[base] = (float)(sh[0] - (double)hi);
+    }
+}
+
+__global__ void __launch_bounds__(64) bwd_dll_d_kernel(BwdParams p, int B) {
+    const int h = blockIdx.x * 64 + threadIdx.x;
+    if (h >= p.H) return;
+    double s = 0.0;
+    for (int b = 0; b < B; ++b) {
+        const size_t base = ((size_t)b * p.H + h) * p.L;
+        s += (double)p.da_row[base] + (double)p.da_col[base];
+    }
+    p.dll[h] = (float)s;
 }
 
 // ================================ host side ===========================================================
@@ -780,10 +797,11 @@ hipError_t launch_t(const BwdArgs &a, hipStream_t stream) {
     p.nbuf = sh.nbuf;
     p.causal = a.causal ? 1 : 0;
     launch_grad<D, KIND>(sh, p, stream);
-    if constexpr (KIND == kMaskS)
-        hipLaunchKernelGGL(bwd_dll_s_kernel, dim3(a.B * a.H), dim3(kDllThreads), 0, stream, p);
-    else if constexpr (KIND == kMaskD)
-        hipLaunchKernelGGL(bwd_dll_d_kernel, dim3(a.H), dim3(kDllThreads), 0, stream, p, a.B);
+    if constexpr (KIND != kMaskLit) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_dll(KIND, p.da_row, p.da_col, p.dll, a.B, a.H, a.L, stream);
+    }
     return hipGetLastError();
 }
 
@@ -815,8 +833,10 @@ hipError_t launch_dll(int kind, float *da_row, float *da_col, float *dll, int B,
     p.dll = dll;
     if (kind == kMaskS)
         hipLaunchKernelGGL(bwd_dll_s_kernel, dim3(B * H), dim3(kDllThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(bwd_dll_d_kernel, dim3(H), dim3(kDllThreads), 0, stream, p, B);
+    else {
+        hipLaunchKernelGGL(bwd_dll_d_rows_kernel, dim3(B * H), dim3(kDllThreads), 0, stream, p);
+        hipLaunchKernelGGL(bwd_dll_d_kernel, dim3((H + 63) / 64), dim3(64), 0, stream, p, B);
+    }
     return hipGetLastError();
 }
 
