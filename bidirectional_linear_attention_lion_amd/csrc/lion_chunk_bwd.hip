@@ -638,13 +638,7 @@ hipError_t launch_cbwd_t(const BwdArgs &a, hipStream_t stream) {
 
 template <int D, int KIND>
 hipError_t launch_cbwd_c(const BwdArgs &a, hipStream_t stream) {
-    switch (a.C) {
-    case 16: return launch_cbwd_t<D, KIND, 16>(a, stream);
-    case 32: return launch_cbwd_t<D, KIND, 32>(a, stream);
-    default:
-        if constexpr (D != 128) return launch_cbwd_t<D, KIND, 64>(a, stream);
-        return hipErrorInvalidValue;
-    }
+    return a.C == 16 ? launch_cbwd_t<D, KIND, 16>(a, stream) : launch_cbwd_t<D, KIND, 32>(a, stream);
 }
 
 template <int D>
@@ -658,16 +652,19 @@ hipError_t launch_cbwd_kind(const BwdArgs &a, hipStream_t stream) {
 
 }  // namespace
 
+// Chunks of 64 and 128 run on the bf16 matrix-core kernels (lion_chunk_bwd_mfma.hip); 16 and 32 here.
 Plan plan_chunk_bwd(const BwdArgs &a) {
+    if (a.C >= 64) return plan_chunk_bwd_mfma(a);
     Plan p;
     const bool dims = a.d == 32 || a.d == 64 || a.d == 128;
-    const bool cs = a.C == 16 || a.C == 32 || a.C == 64;
+    const bool cs = a.C == 16 || a.C == 32;
     p.ok = dims && cs && cbwd_lds(a.d, a.C) <= kLdsPerWorkgroup;
     p.workspace = p.ok ? cbwd_layout(a.B, a.H, a.L, a.d, a.C).floats * 4 : 0;
     return p;
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream) {
+    if (a.C >= 64) return launch_chunk_bwd_mfma(a, stream);
     switch (a.d) {
     case 32: return launch_cbwd_kind<32>(a, stream);
     case 64: return launch_cbwd_kind<64>(a, stream);

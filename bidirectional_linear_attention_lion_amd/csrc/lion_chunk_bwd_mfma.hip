@@ -1,0 +1,690 @@
+// lion_chunk_bwd_mfma.hip -- backward pass of the chunkwise form for chunks of 64 and 128 tokens, every
+// product on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16).
+//
+// The gradients and their chunkwise split are those of lion_chunk_bwd.hip (the chain rule of the
+// attention form, OpenReview abstract and reply "Concern 1", Theorem 3.3 Eq. 25, organised like the
+// chunkwise form, reply "4: Practicality of Recurrent Inference"; blog "LION Part IV - Results", "LION
+// Chunk"): pairs inside a chunk formed directly, the rest of the sequence through the four states
+// entering each chunk,
+//   keys'    F = sum_j w_j phi(k_j) [v_j, 1]^T,   queries'  G = sum_i w_i phi(q_i) [dy_i / den_i, -delta_i]^T,
+// from the left and from the right.  Operands are rounded to bf16 as in the full form's backward
+// (phi(q), phi(k), the masked dS and P / den), and so are the states' d x d blocks; sums are fp32.
+//
+//   walk: a workgroup per (batch, head, direction, keys or queries) walks the chunks in order.  Its
+//         running state is fp32 in matrix-core accumulators; each chunk's tokens are staged as bf16
+//         with their weight folded in (X' = w_j phi(k_j), or w_i phi(q_i) / den_i), so the update is
+//         S^T <- e^{tot} S^T + Y^T X' with Y = v or dy (the last column, 1 or -dy.y, enters as a 17th
+//         row tile holding it as a bf16 hi/lo pair).  The state entering each chunk is written as bf16
+//         d x d rows plus its last column in fp32.
+//   main: a workgroup of C / 16 waves per chunk; wave w owns query tile w and key tile w.  The pair part
+//         is the full form's backward restricted to the chunk: S^T and dP^T against the chunk's keys,
+//         then dphi(Q)^T += phi(K)^T dS^T; S and dP against its queries, then dV^T += dY^T (P / den) and
+//         dphi(K)^T += phi(Q)^T dS.  The entering states, staged into the space of the value and dy
+//         tiles, then add (f the weight from the chunk's near end to the token)
+//           dphi(q_i) += f_i (F dy_i / den_i - F_d delta_i),   dphi(k_j) += f_j (G v_j + G_d),
+//           dv_j += f_j G^T phi(k_j)
+//         and the dA halves phi(q_i).(that) and phi(k_j).(that), plus from the left, minus from the right.
+// Causal variant: pairs above the diagonal drop out, and so do the keys' state from the right and the
+// queries' state from the left.
+#include "lion_device.h"
+#include "lion_internal.h"
+#include "lion_stage.h"
+#include "lion_bwd_tiles.h"
+
+namespace lion {
+namespace {
+
+constexpr int kWalkThreads = 256;
+
+struct MbParams {
+    const __bf16 *q, *k, *v, *y, *dy;
+    const float *den, *ll;
+    int H, L, nch, causal;
+    void *dq, *dk, *dv;
+    int g_bf16;
+    __bf16 *st;                // [B H][nch][4][D][D]: key-left, query-left, key-right, query-right
+    float *stz;                // [B H][nch][4][D]: the states' last column
+    float *da_row, *da_col;    // [B H L]
+};
+
+// Inclusive prefix sums of the chunk's log decays in log2 units relative to the chunk start (cum[t],
+// repeating the last one past n) and the chunk's total (cum[CT]); run by one whole wave.  LION-S reads
+// the decays from ll_row (n of them), LION-D forms them from the head's log(lambda).
+template <int KIND, int CT>
+__device__ __forceinline__ void chunk_cum(float *cum, const float *ll, const float *ll_row, int h, int n, int lane) {
+    if constexpr (KIND == kMaskD) {
+        const float lg = ll[h] * kLog2e;
+        for (int t = lane; t < CT; t += 64) cum[t] = (float)(min(t, n - 1) + 1) * lg;
+        if (lane == 0) cum[CT] = (float)n * lg;
+    } else if constexpr (KIND == kMaskS) {
+        constexpr int R = CT / 64;   // consecutive tokens per lane
+        double x[R], s = 0.0;
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const int t = lane * R + k;
+            s += t < n ? (double)ll_row[t] : 0.0;
+            x[k] = s;
+        }
+        double incl = s;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const double up = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += up;
+        }
+        const double excl = incl - s;
+#pragma unroll
+        for (int k = 0; k < R; ++k) cum[lane * R + k] = (float)((excl + x[k]) * 1.4426950408889634);
+        const double tot = __shfl(incl, 63, 64);
+        if (lane == 0) cum[CT] = (float)(tot * 1.4426950408889634);
+    } else {
+        for (int t = lane; t <= CT; t += 64) cum[t] = 0.f;
+    }
+}
+
+// ================================ walk ===============================================================
+template <int D, int CT, bool KEYS>
+struct WalkRegs {
+    static constexpr int SPR = D / 8;                     // 16-byte slots per row
+    static constexpr int NIT = CT * SPR / kWalkThreads;   // slots per thread
+    bf16x8 x[NIT], y[NIT], z[KEYS ? 1 : NIT];             // keys: k, v; queries: q, dy, y
+    float den[KEYS ? 1 : NIT];
+};
+
+template <int D, int CT, bool KEYS>
+__device__ __forceinline__ void walk_load(const MbParams &p, int bh, int c, int n, WalkRegs<D, CT, KEYS> &R) {
+    using WR = WalkRegs<D, CT, KEYS>;
+    const int tid = threadIdx.x;
+    const size_t row0 = (size_t)bh * p.L + (size_t)c * CT;
+#pragma unroll
+    for (int it = 0; it < WR::NIT; ++it) {
+        const int sl = it * kWalkThreads + tid;
+        const int row = sl / WR::SPR, cs = (sl % WR::SPR) * 8;
+        if (row < n) {
+            const size_t g = (row0 + row) * D + cs;
+            if constexpr (KEYS) {
+                R.x[it] = __builtin_bit_cast(bf16x8, ld16(p.k + g));
+                R.y[it] = __builtin_bit_cast(bf16x8, ld16(p.v + g));
+            } else {
+                R.x[it] = __builtin_bit_cast(bf16x8, ld16(p.q + g));
+                R.y[it] = __builtin_bit_cast(bf16x8, ld16(p.dy + g));
+                R.z[it] = __builtin_bit_cast(bf16x8, ld16(p.y + g));
+                R.den[it] = p.den[row0 + row];
+            }
+        }
+    }
+}
+
+// The chunk's rows into the LDS tiles: Xt = w phi(x) (/ den for queries), Yt = v or dy (rows at or past n
+// zero), cz = the last column's entries (queries: -dy.y; keys: unused).  Two barriers inside: the prefix
+// sums first (wave 0), then the rows.
+template <int D, int KIND, int CT, bool KEYS>
+__device__ __forceinline__ void walk_commit(const MbParams &p, __bf16 *Xt, __bf16 *Yt, float *cum, float *cz, int bh,
+                                            int c, int n, int dir, const WalkRegs<D, CT, KEYS> &R) {
+    using WR = WalkRegs<D, CT, KEYS>;
+    using RT = RowTile<D, __bf16>;
+    constexpr int SPR = WR::SPR;
+    const int tid = threadIdx.x;
+    if (tid < 64)
+        chunk_cum<KIND, CT>(cum, p.ll, KIND == kMaskS ? p.ll + (size_t)bh * p.L + (size_t)c * CT : nullptr, bh % p.H, n,
+                            tid);
+    __syncthreads();
+    const float tot = cum[CT];
+#pragma unroll
+    for (int it = 0; it < WR::NIT; ++it) {
+        const int sl = it * kWalkThreads + tid;
+        const int row = sl / SPR, cs = (sl % SPR) * 8;
+        const bool ok = row < n;
+        float fx[8], ss = 0.f, part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            fx[e] = ok ? phi_pre<KIND>((float)R.x[it][e]) : 0.f;
+            ss += fx[e] * fx[e];
+            if constexpr (!KEYS) part += ok ? (float)R.y[it][e] * (float)R.z[it][e] : 0.f;
+        }
+        float scl = 1.f;
+        if constexpr (KIND == kMaskS) scl = inv_norm(group_sum<SPR>(ss));
+        if constexpr (KIND != kMaskLit) scl *= fast_exp2(dir == 0 ? tot - cum[row] : cum[row]);
+        if constexpr (!KEYS) {
+            part = group_sum<SPR>(part);
+            if (ok) scl *= __builtin_amdgcn_rcpf(R.den[it]);
+            if (sl % SPR == 0) cz[row] = ok ? -part : 0.f;
+        }
+        bf16x8 xo, yo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            xo[e] = f2bf(fx[e] * scl);
+            yo[e] = ok ? R.y[it][e] : f2bf(0.f);
+        }
+        *reinterpret_cast<bf16x8 *>(Xt + RT::off(row, cs)) = xo;
+        *reinterpret_cast<bf16x8 *>(Yt + RT::off(row, cs)) = yo;
+    }
+}
+
+// State tiles: 16 x 16 tiles (tb, ta) of S^T, tb < NA + 1 (the last one holds the last column in its
+// first two rows), ta < NA; wave w takes tiles w, w + 4, ... with ta = tile % NA, tb = tile / NA.
+template <int D, int KIND, int CT, bool KEYS>
+__device__ void walk(const MbParams &p, unsigned char *smem, int bh, int dir) {
+    using RT = RowTile<D, __bf16>;
+    constexpr int NA = D / 16, NT = NA * (NA + 1), NU = (NT + 3) / 4;
+    __bf16 *Xt = reinterpret_cast<__bf16 *>(smem);
+    __bf16 *Yt = Xt + CT * D;
+    float *cum = reinterpret_cast<float *>(Yt + CT * D);
+    float *cz = cum + CT + 4;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const int st = 2 * dir + (KEYS ? 0 : 1);
+    f32x4 acc[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    WalkRegs<D, CT, KEYS> R;
+    {
+        const int c = dir == 0 ? 0 : p.nch - 1;
+        const int n = min(CT, p.L - c * CT);
+        walk_load<D, CT, KEYS>(p, bh, c, n, R);
+        walk_commit<D, KIND, CT, KEYS>(p, Xt, Yt, cum, cz, bh, c, n, dir, R);
+        __syncthreads();
+    }
+#pragma unroll 1
+    for (int step = 0; step < p.nch; ++step) {
+        const int c = dir == 0 ? step : p.nch - 1 - step;
+        const int cn = dir == 0 ? c + 1 : c - 1;
+        const int nn = min(CT, p.L - cn * CT);
+        const bool more = step + 1 < p.nch;
+        if (more) walk_load<D, CT, KEYS>(p, bh, cn, nn, R);   // in flight while this chunk is summed
+        // the state entering chunk c is the running sum so far
+        const size_t so = ((size_t)bh * p.nch + c) * 4 + st;
+        __bf16 *sd = p.st + so * D * D;
+        float *zd = p.stz + so * D;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int tile = w + 4 * u;
+            if (tile >= NT) break;
+            const int ta = tile % NA, tb = tile / NA, a = 16 * ta + r;
+            if (tb < NA) {
+                bf16x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = f2bf(acc[u][e]);
+                *reinterpret_cast<bf16x4 *>(sd + a * D + 16 * tb + 4 * g) = o;
+            } else if (g == 0) {
+                zd[a] = acc[u][0] + acc[u][1];
+            }
+        }
+        // decay across the chunk, then add its tokens: S^T[b][a] += sum_j Y_j[b] X'_j[a]
+        const float dec = KIND == kMaskLit ? 1.f : fast_exp2(cum[CT]);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) acc[u] *= dec;
+#pragma unroll
+        for (int h = 0; h < CT / kKB; ++h) {
+            // the last column's tile: row 0 the hi part, row 1 the lo part (keys: 1), at the tokens of
+            // the transposed fragments' slots (4 g + e and 16 + 4 g + e of the sub-block)
+            bf16x8 zf;
+            if constexpr (KEYS) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) zf[e] = f2bf(r == 0 ? 1.f : 0.f);
+            } else {
+                const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cz + h * kKB + 4 * g);
+                const f32x4 c1 = *reinterpret_cast<const f32x4 *>(cz + h * kKB + 16 + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const __bf16 h0 = f2bf(c0[e]), h1 = f2bf(c1[e]);
+                    const __bf16 l0 = f2bf(c0[e] - (float)h0), l1 = f2bf(c1[e] - (float)h1);
+                    zf[e] = r == 0 ? h0 : (r == 1 ? l0 : f2bf(0.f));
+                    zf[4 + e] = r == 0 ? h1 : (r == 1 ? l1 : f2bf(0.f));
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int tile = w + 4 * u;
+                if (tile >= NT) break;
+                const int ta = tile % NA, tb = tile / NA;
+                const bf16x8 af = tb < NA ? tr_frag<D>(Yt, h, tb, r, g) : zf;
+                acc[u] = mfma_bf16(af, tr_frag<D>(Xt, h, ta, r, g), acc[u]);
+            }
+        }
+        __syncthreads();   // before the next chunk's rows overwrite these
+        if (more) {
+            walk_commit<D, KIND, CT, KEYS>(p, Xt, Yt, cum, cz, bh, cn, nn, dir, R);
+            __syncthreads();
+        }
+    }
+}
+
+template <int D, int KIND, int CT>
+__global__ void __launch_bounds__(kWalkThreads) mb_walk_kernel(MbParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int ns = p.causal ? 2 : 4;
+    const int bh = blockIdx.x / ns, s = blockIdx.x % ns;
+    // causal: s = 0 keys from the left, s = 1 queries from the right; else s = 2 dir + (queries)
+    const int dir = p.causal ? s : s >> 1;
+    const bool keys = p.causal ? s == 0 : (s & 1) == 0;
+    if (keys) walk<D, KIND, CT, true>(p, smem, bh, dir);
+    else walk<D, KIND, CT, false>(p, smem, bh, dir);
+}
+
+template <int D, int CT>
+constexpr size_t walk_lds() {
+    return (size_t)2 * CT * D * 2 + (size_t)(2 * CT + 8) * 4;
+}
+
+// ================================ main ===============================================================
+// Four bf16 values of row `row`, channels c .. c + 3 (c a multiple of 4), of a staged tile.
+template <int D>
+__device__ __forceinline__ bf16x4 row4(const __bf16 *tile, int row, int c) {
+    return *reinterpret_cast<const bf16x4 *>(tile + RowTile<D, __bf16>::off(row, c));
+}
+
+template <int D, int CT>
+struct MainLds {
+    static constexpr int TILE = CT * D;                        // bf16 elements per token tile
+    static constexpr size_t TOK = (size_t)4 * TILE * 2;        // phi(q), phi(k), v, dy
+    static constexpr size_t F32 = (size_t)(CT + 4) + 4 * CT + 4 * D;   // cum, 1/den, delta, dA halves, last columns
+    static constexpr size_t BYTES = TOK + F32 * 4;
+    static constexpr int NSF = 2 * CT / D < 4 ? 2 * CT / D : 4;  // states staged at once (value + dy tiles' space)
+};
+
+template <int D, int KIND, int CT>
+__global__ void __launch_bounds__(CT * 4) mb_main_kernel(MbParams p) {
+    using RT = RowTile<D, __bf16>;
+    using ML = MainLds<D, CT>;
+    constexpr int NS = D / 32, NCT = D / 16, SPR = D / 8, NW = CT / 16, NT = CT * 4;
+    extern __shared__ __align__(16) unsigned char smem[];
+    __bf16 *Qt = reinterpret_cast<__bf16 *>(smem);
+    __bf16 *Kt = Qt + ML::TILE, *Vt = Kt + ML::TILE, *Gt = Vt + ML::TILE;
+    float *cum = reinterpret_cast<float *>(Gt + ML::TILE);
+    float *inv = cum + CT + 4, *dl = inv + CT, *dar = dl + CT, *dac = dar + CT, *zst = dac + CT;
+
+    const int bh = blockIdx.x / p.nch, c = blockIdx.x % p.nch;
+    const int n = min(CT, p.L - c * CT);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const size_t row0 = (size_t)bh * p.L + (size_t)c * CT;
+    const bool causal = p.causal != 0;
+
+    // the entering states this chunk needs (none left of the first chunk or right of the last; causal,
+    // not the keys' state from the right nor the queries' from the left)
+    // (a list of 4-bit state indices rather than an array, which a dynamic index would put in scratch)
+    unsigned sts = 0;
+    int nst = 0;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const bool right = st >= 2, keys = (st & 1) == 0;
+        if (!((right ? c == p.nch - 1 : c == 0) || (causal && keys == right))) sts |= (unsigned)st << (4 * nst++);
+    }
+    auto st_at = [&](int k) { return (int)((sts >> (4 * k)) & 15u); };
+
+    // ---- stage the chunk: phi(q), phi(k), v, dy as bf16 rows (zero past n); 1/den and delta per row
+    {
+        constexpr int NIT = CT * SPR / NT;
+        bf16x8 rq[NIT], rk[NIT], rv[NIT], rg[NIT], ry[NIT];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int sl = it * NT + tid;
+            const int row = sl / SPR, cs = (sl % SPR) * 8;
+            const size_t gi = (row0 + min(row, n - 1)) * D + cs;
+            rq[it] = __builtin_bit_cast(bf16x8, ld16(p.q + gi));
+            rk[it] = __builtin_bit_cast(bf16x8, ld16(p.k + gi));
+            rv[it] = __builtin_bit_cast(bf16x8, ld16(p.v + gi));
+            rg[it] = __builtin_bit_cast(bf16x8, ld16(p.dy + gi));
+            ry[it] = __builtin_bit_cast(bf16x8, ld16(p.y + gi));
+        }
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int sl = it * NT + tid;
+            const int row = sl / SPR, cs = (sl % SPR) * 8;
+            const bool ok = row < n;
+            float fq[8], fk[8], ssq = 0.f, ssk = 0.f, part = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                fq[e] = phi_pre<KIND>((float)rq[it][e]);
+                fk[e] = phi_pre<KIND>((float)rk[it][e]);
+                ssq += fq[e] * fq[e];
+                ssk += fk[e] * fk[e];
+                part += (float)rg[it][e] * (float)ry[it][e];
+            }
+            float sq = ok ? 1.f : 0.f, sk = sq;
+            if constexpr (KIND == kMaskS) {
+                sq *= inv_norm(group_sum<SPR>(ssq));
+                sk *= inv_norm(group_sum<SPR>(ssk));
+            }
+            part = group_sum<SPR>(part);
+            bf16x8 oq, ok8, ov, og;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                oq[e] = f2bf(fq[e] * sq);
+                ok8[e] = f2bf(fk[e] * sk);
+                ov[e] = ok ? rv[it][e] : f2bf(0.f);
+                og[e] = ok ? rg[it][e] : f2bf(0.f);
+            }
+            const int at = RT::off(row, cs);
+            *reinterpret_cast<bf16x8 *>(Qt + at) = oq;
+            *reinterpret_cast<bf16x8 *>(Kt + at) = ok8;
+            *reinterpret_cast<bf16x8 *>(Vt + at) = ov;
+            *reinterpret_cast<bf16x8 *>(Gt + at) = og;
+            if (sl % SPR == 0) {
+                const float iv = ok ? 1.f / p.den[row0 + row] : 0.f;
+                inv[row] = iv;
+                dl[row] = part * iv;
+            }
+        }
+    }
+    if (w == 0) chunk_cum<KIND, CT>(cum, p.ll, KIND == kMaskS ? p.ll + row0 : nullptr, bh % p.H, n, lane);
+    for (int t = tid; t < 2 * CT; t += NT) dar[t] = 0.f;
+    for (int t = tid; t < nst * D; t += NT) {
+        const int st = st_at(t / D);
+        zst[st * D + t % D] = p.stz[(((size_t)bh * p.nch + c) * 4 + st) * D + t % D];
+    }
+    __syncthreads();
+    const float tot = cum[CT];
+
+    // ---- query tile w against the chunk's keys: dphi(Q)^T (channel 16 ct + 4 g + e, query 16 w + r)
+    const int i_me = 16 * w + r;   // this lane's query row and key row
+    bf16x8 qf[NS], df[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        qf[st] = rows_frag<D>(Qt, w >> 1, w & 1, st, r, g);
+        df[st] = rows_frag<D>(Gt, w >> 1, w & 1, st, r, g);
+    }
+    const float inv_me = inv[i_me], dl_me = dl[i_me], cum_me = cum[i_me];
+    f32x4 aq[NCT], ak[NCT], av[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) aq[ct] = ak[ct] = av[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float rowterm = 0.f, colterm = 0.f;
+#pragma unroll 1
+    for (int h = 0; h < CT / kKB; ++h) {
+        if (causal && h * kKB > 16 * w + 15) break;   // every key after every query of the tile
+        f32x4 sacc[2], dpacc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                sacc[t] = mfma_bf16(rows_frag<D>(Kt, h, t, st, r, g), qf[st], sacc[t]);
+                dpacc[t] = mfma_bf16(rows_frag<D>(Vt, h, t, st, r, g), df[st], dpacc[t]);
+            }
+        }
+        // element (t, e): key j = 32 h + 16 t + 4 g + e, query i_me
+        bf16x8 dsf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const f32x4 cj = *reinterpret_cast<const f32x4 *>(cum + h * kKB + 16 * t + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = h * kKB + 16 * t + 4 * g + e;
+                float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(cum_me - cj[e])) : 1.f;
+                if (causal && j > i_me) m = 0.f;
+                const float dp = dpacc[t][e] * inv_me - dl_me;
+                const float wv = dp * (sacc[t][e] * m);
+                rowterm += j < i_me ? wv : (j > i_me ? -wv : 0.f);
+                dsf[4 * t + e] = f2bf(dp * m);
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) aq[ct] = mfma_bf16(tr_frag<D>(Kt, h, ct, r, g), dsf, aq[ct]);
+    }
+
+    // ---- key tile w against the chunk's queries: dV^T and dphi(K)^T (channel 16 ct + 4 g + e, key 16 w + r)
+    bf16x8 kf[NS], vf[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        kf[st] = rows_frag<D>(Kt, w >> 1, w & 1, st, r, g);
+        vf[st] = rows_frag<D>(Vt, w >> 1, w & 1, st, r, g);
+    }
+#pragma unroll 1
+    for (int h = 0; h < CT / kKB; ++h) {
+        if (causal && h * kKB + kKB - 1 < 16 * w) continue;   // every query before every key of the tile
+        f32x4 sacc[2], dpacc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                sacc[t] = mfma_bf16(rows_frag<D>(Qt, h, t, st, r, g), kf[st], sacc[t]);
+                dpacc[t] = mfma_bf16(rows_frag<D>(Gt, h, t, st, r, g), vf[st], dpacc[t]);
+            }
+        }
+        // element (t, e): query i = 32 h + 16 t + 4 g + e, key i_me
+        bf16x8 pf, dsf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ib = h * kKB + 16 * t + 4 * g;
+            const f32x4 iv = *reinterpret_cast<const f32x4 *>(inv + ib);
+            const f32x4 dv4 = *reinterpret_cast<const f32x4 *>(dl + ib);
+            const f32x4 ci = *reinterpret_cast<const f32x4 *>(cum + ib);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = ib + e;
+                float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(ci[e] - cum_me)) : 1.f;
+                if (causal && i_me > i) m = 0.f;
+                const float pm = sacc[t][e] * m;
+                const float dp = dpacc[t][e] * iv[e] - dv4[e];
+                const float wv = dp * pm;
+                colterm += i < i_me ? wv : (i > i_me ? -wv : 0.f);
+                pf[4 * t + e] = f2bf(pm * iv[e]);
+                dsf[4 * t + e] = f2bf(dp * m);
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            av[ct] = mfma_bf16(tr_frag<D>(Gt, h, ct, r, g), pf, av[ct]);
+            ak[ct] = mfma_bf16(tr_frag<D>(Qt, h, ct, r, g), dsf, ak[ct]);
+        }
+    }
+
+    // ---- the entering states, staged NSF at a time into the value and dy tiles' space as bf16 d x d
+    // row tiles.  phi(q) and phi(k) of this lane's rows at channels 32 hh + 16 t + 4 g + e serve both as
+    // the transposed-slot operand of dv and as the output layout's channels 16 ct + 4 g + e, ct = 2 hh + t.
+    bf16x8 qT[NS], kT[NS];
+#pragma unroll
+    for (int hh = 0; hh < NS; ++hh) {
+        const bf16x4 q0 = row4<D>(Qt, i_me, 32 * hh + 4 * g), q1 = row4<D>(Qt, i_me, 32 * hh + 16 + 4 * g);
+        const bf16x4 k0 = row4<D>(Kt, i_me, 32 * hh + 4 * g), k1 = row4<D>(Kt, i_me, 32 * hh + 16 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qT[hh][e] = q0[e];
+            qT[hh][4 + e] = q1[e];
+            kT[hh][e] = k0[e];
+            kT[hh][4 + e] = k1[e];
+        }
+    }
+    __syncthreads();   // every wave is done with the value and dy tiles
+    __bf16 *Sb = Vt;
+#pragma unroll 1
+    for (int k0 = 0; k0 < nst; k0 += ML::NSF) {
+        const int kn = min(ML::NSF, nst - k0);
+        for (int k = 0; k < kn; ++k)
+            stage_rows<D, __bf16>(Sb + k * D * D, p.st + (((size_t)bh * p.nch + c) * 4 + st_at(k0 + k)) * D * D, 0, D, D,
+                                  w, NW, lane);
+        wait_vm_all();
+        __syncthreads();
+#pragma unroll 1
+        for (int k = 0; k < kn; ++k) {
+            const int st = st_at(k0 + k);
+            const bool right = st >= 2, keys = (st & 1) == 0;
+            const float sgn = right ? -1.f : 1.f;
+            const float f = KIND == kMaskLit ? 1.f : fast_exp2(right ? tot - cum_me : cum_me);
+            const __bf16 *S = Sb + k * D * D;
+            const float *z = zst + st * D;
+            float part = 0.f;
+            if (keys) {
+                // dphi(q) += f (F dy / den - F_d delta): F rows as A, dy of the query row as B
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st2 = 0; st2 < NS; ++st2) o = mfma_bf16(rows_frag<D>(S, ct >> 1, ct & 1, st2, r, g), df[st2], o);
+                    const f32x4 zc = *reinterpret_cast<const f32x4 *>(z + 16 * ct + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float oe = o[e] * inv_me - zc[e] * dl_me;
+                        aq[ct][e] += f * oe;
+                        part += (float)qT[ct >> 1][4 * (ct & 1) + e] * oe;
+                    }
+                }
+                rowterm += sgn * f * part;
+            } else {
+                // dphi(k) += f (G v + G_d): G rows as A, v of the key row as B; dv += f G^T phi(k):
+                // G read transposed as A, phi(k) in the transposed slots as B
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    f32x4 o = {0.f, 0.f, 0.f, 0.f}, ov = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st2 = 0; st2 < NS; ++st2) {
+                        o = mfma_bf16(rows_frag<D>(S, ct >> 1, ct & 1, st2, r, g), vf[st2], o);
+                        ov = mfma_bf16(tr_frag<D>(S, st2, ct, r, g), kT[st2], ov);
+                    }
+                    const f32x4 zc = *reinterpret_cast<const f32x4 *>(z + 16 * ct + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float oe = o[e] + zc[e];
+                        ak[ct][e] += f * oe;
+                        av[ct][e] += f * ov[e];
+                        part += (float)kT[ct >> 1][4 * (ct & 1) + e] * oe;
+                    }
+                }
+                colterm += sgn * f * part;
+            }
+        }
+        __syncthreads();   // before the next states overwrite these
+    }
+
+    // ---- phi's Jacobian and the stores (this lane: row 16 w + r, channels 16 ct + 4 g .. + 3)
+    rowterm += __shfl_xor(rowterm, 16, 64);
+    rowterm += __shfl_xor(rowterm, 32, 64);
+    colterm += __shfl_xor(colterm, 16, 64);
+    colterm += __shfl_xor(colterm, 32, 64);
+    if (i_me >= n) return;
+    const size_t rowg = row0 + i_me;
+    const bool gb = p.g_bf16 != 0;
+    if constexpr (KIND != kMaskD) {
+        float xq[NCT][4], xk[NCT][4];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(p.q + rowg * D + 16 * ct + 4 * g);
+            const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(p.k + rowg * D + 16 * ct + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xq[ct][e] = (float)q4[e];
+                xk[ct][e] = (float)k4[e];
+            }
+        }
+        phi_backward<D, KIND>(xq, aq);
+        phi_backward<D, KIND>(xk, ak);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const size_t off = rowg * D + 16 * ct + 4 * g;
+        store4(p.dq, gb, off, aq[ct]);
+        store4(p.dk, gb, off, ak[ct]);
+        store4(p.dv, gb, off, av[ct]);
+    }
+    if constexpr (KIND != kMaskLit) {
+        if (g == 0) {
+            p.da_row[rowg] = rowterm;
+            p.da_col[rowg] = colterm;
+        }
+    }
+}
+
+// ================================ host side ===========================================================
+template <typename K>
+void allow_lds(K *kernel, size_t lds) {
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+}
+
+struct MbLayout {
+    size_t st, stz, da, bytes;   // byte offsets into the workspace
+};
+
+MbLayout mb_layout(int B, int H, int L, int d, int C) {
+    const size_t bh = (size_t)B * H, nch = (size_t)((L + C - 1) / C);
+    MbLayout w;
+    w.st = 0;
+    w.stz = w.st + bh * nch * 4 * (size_t)d * d * 2;
+    w.da = w.stz + bh * nch * 4 * (size_t)d * 4;
+    w.bytes = w.da + 2 * (((bh * L) + 3) / 4) * 4 * 4;
+    return w;
+}
+
+size_t mb_main_lds(int d, int C) {
+    const size_t f32 = (size_t)(C + 4) + 4 * (size_t)C + 4 * (size_t)d;
+    return (size_t)4 * C * d * 2 + f32 * 4;
+}
+
+template <int D, int KIND, int CT>
+hipError_t launch_mb_t(const BwdArgs &a, hipStream_t stream) {
+    const MbLayout w = mb_layout(a.B, a.H, a.L, a.d, CT);
+    unsigned char *ws = reinterpret_cast<unsigned char *>(a.workspace);
+    MbParams p;
+    p.q = reinterpret_cast<const __bf16 *>(a.q);
+    p.k = reinterpret_cast<const __bf16 *>(a.k);
+    p.v = reinterpret_cast<const __bf16 *>(a.v);
+    p.y = reinterpret_cast<const __bf16 *>(a.y);
+    p.dy = reinterpret_cast<const __bf16 *>(a.dy);
+    p.den = a.den;
+    p.ll = a.log_lambda;
+    p.H = a.H;
+    p.L = a.L;
+    p.nch = (a.L + CT - 1) / CT;
+    p.causal = a.causal ? 1 : 0;
+    p.dq = a.dq;
+    p.dk = a.dk;
+    p.dv = a.dv;
+    p.g_bf16 = a.g_bf16 ? 1 : 0;
+    p.st = reinterpret_cast<__bf16 *>(ws + w.st);
+    p.stz = reinterpret_cast<float *>(ws + w.stz);
+    const size_t n = (size_t)a.B * a.H * a.L;
+    p.da_row = reinterpret_cast<float *>(ws + w.da);
+    p.da_col = p.da_row + ((n + 3) / 4) * 4;
+    if (p.nch > 1) {
+        constexpr size_t lw = walk_lds<D, CT>();
+        allow_lds(&mb_walk_kernel<D, KIND, CT>, lw);
+        hipLaunchKernelGGL((mb_walk_kernel<D, KIND, CT>), dim3(a.B * a.H * (a.causal ? 2 : 4)), dim3(kWalkThreads), lw,
+                           stream, p);
+    }
+    constexpr size_t lm = MainLds<D, CT>::BYTES;
+    allow_lds(&mb_main_kernel<D, KIND, CT>, lm);
+    hipLaunchKernelGGL((mb_main_kernel<D, KIND, CT>), dim3(a.B * a.H * p.nch), dim3(CT * 4), lm, stream, p);
+    if (KIND != kMaskLit) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_dll(KIND, p.da_row, p.da_col, a.dll, a.B, a.H, a.L, stream);
+    }
+    return hipGetLastError();
+}
+
+template <int D, int KIND>
+hipError_t launch_mb_c(const BwdArgs &a, hipStream_t stream) {
+    if (a.C == 64) return launch_mb_t<D, KIND, 64>(a, stream);
+    if constexpr (D != 128) return launch_mb_t<D, KIND, 128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_mb_kind(const BwdArgs &a, hipStream_t stream) {
+    switch (a.kind) {
+    case kMaskLit: return launch_mb_c<D, kMaskLit>(a, stream);
+    case kMaskD: return launch_mb_c<D, kMaskD>(a, stream);
+    default: return launch_mb_c<D, kMaskS>(a, stream);
+    }
+}
+
+}  // namespace
+
+Plan plan_chunk_bwd_mfma(const BwdArgs &a) {
+    Plan p;
+    const bool dims = a.d == 32 || a.d == 64 || a.d == 128;
+    const bool cs = a.C == 64 || (a.C == 128 && a.d != 128);
+    p.ok = dims && cs && mb_main_lds(a.d, a.C) <= kLdsPerWorkgroup;
+    p.workspace = p.ok ? mb_layout(a.B, a.H, a.L, a.d, a.C).bytes : 0;
+    return p;
+}
+
+hipError_t launch_chunk_bwd_mfma(const BwdArgs &a, hipStream_t stream) {
+    switch (a.d) {
+    case 32: return launch_mb_kind<32>(a, stream);
+    case 64: return launch_mb_kind<64>(a, stream);
+    default: return launch_mb_kind<128>(a, stream);
+    }
+}
+
+}  // namespace lion

@@ -66,6 +66,7 @@ Plan plan_full(const AttnArgs &a);
 Plan plan_selectivity(const SelArgs &a);
 Plan plan_full_bwd(const BwdArgs &a);
 Plan plan_chunk_bwd(const BwdArgs &a);
+Plan plan_chunk_bwd_mfma(const BwdArgs &a);   // chunks of 64 and 128 (bf16 matrix cores)
 Plan plan_chunk(const AttnArgs &a);
 Plan plan_chunk2(const AttnArgs &a);
 Plan plan_birnn(const AttnArgs &a);
@@ -75,6 +76,7 @@ Plan plan_birnn(const AttnArgs &a);
 hipError_t launch_full(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_full_bwd(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream);
+hipError_t launch_chunk_bwd_mfma(const BwdArgs &a, hipStream_t stream);
 // dlog(lambda) from the two halves of dA ([B, H, L] each): LION-S a reverse prefix sum per (batch,
 // head), LION-D sum_t t dA_t per head over the batch.  kind is 1 (D) or 2 (S).
 hipError_t launch_dll(int kind, float *da_row, float *da_col, float *dll, int B, int H, int L, hipStream_t stream);
