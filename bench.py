@@ -46,7 +46,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
 VALU_FP32_PEAK_TFLOPS = 157.3   # fp32 vector
 CSRC = os.path.join(ROOT, "bidirectional_linear_attention_lion_amd", "csrc")
 KERNEL_FILES = {"full": "lion_full.hip", "chunk": "lion_chunk.hip", "birnn": "lion_birnn.hip",
-                "full_bwd": "lion_full_bwd.hip", "chunk_bwd": "lion_chunk_bwd.hip", "selectivity": "lion_selectivity.hip",
+                "full_bwd": "lion_full_bwd.hip", "chunk_bwd": "lion_chunk_bwd_mfma.hip", "selectivity": "lion_selectivity.hip",
                 "full2": "lion_full.hip", "chunk2": "lion_chunk2.hip"}
 SEL_WIDTH = 1024   # layer-input width of the selectivity prologue (the BERT-Large-shaped recipe)
 FORWARD_FORMS = ("full", "chunk", "birnn", "full2", "chunk2")
@@ -54,12 +54,12 @@ FORWARD_FORMS = ("full", "chunk", "birnn", "full2", "chunk2")
 
 def split_form(key: str, default_c: int = 64):
     """Form key -> (form, C): ``chunk128`` -> ("chunk", 128), ``chunk_bwd32``, ``chunk2_128`` (two orders);
-    chunkwise keys without a size take default_c (chunk_bwd: 32)."""
+    chunkwise keys without a size take default_c (chunk_bwd: 64)."""
     for form, pat in (("chunk2", r"chunk2(?:_(\d+))?"), ("chunk_bwd", r"chunk_bwd(\d*)"), ("chunk", r"chunk(\d*)")):
         m = re.fullmatch(pat, key)
         if m:
             c = m.group(1)
-            return form, int(c) if c else (32 if form == "chunk_bwd" else default_c)
+            return form, int(c) if c else (64 if form == "chunk_bwd" else default_c)
     if key in ("full", "full2", "full_bwd", "birnn", "selectivity"):
         return key, default_c
     raise SystemExit(f"bench.py: unknown form key {key!r}")
@@ -98,8 +98,9 @@ def parse_args():
                     help="comma-separated form keys (default: the workload's forms, the chunkwise form at each of "
                          "its chunk sizes; the 4097-token workload adds the full form as a reference): full, "
                          "chunk<C>, birnn; full_bwd (the full form's backward pass, bf16 gradients; y, den and a "
-                         "random dy prepared beforehand), chunk_bwd<C> (the same gradients computed chunkwise, C "
-                         "<= 64, default 32), selectivity (the LION-S prologue: log lambda from a [B, L, 1024] "
+                         "random dy prepared beforehand), chunk_bwd<C> (the same gradients computed chunkwise; C = 16, "
+                         "32 on fp32 matrix cores, 64, 128 on bf16 ones; default 64), selectivity (the LION-S "
+                         "prologue: log lambda from a [B, L, 1024] "
                          "layer input, keys scaled), full2 / chunk2 (the masks of the raster and the "
                          "column-major patch order averaged; image workloads, L = 1 + n^2; the chunkwise one is keyed "
                          "chunk2_<C>)")
@@ -229,11 +230,17 @@ def algorithmic(form: str, wl, C: int, causal: bool = False):
     return nbytes, flops
 
 
+def fp32_form(form: str, C: int) -> bool:
+    """Forms whose products run in fp32 (the RNN form's vector ALUs; the chunkwise backward's fp32 matrix
+    cores for chunks of 16 and 32), priced against the fp32 peak."""
+    return form == "birnn" or (form == "chunk_bwd" and C < 64)
+
+
 def bound_of(form: str, wl, C: int, causal: bool = False) -> str:
-    """The roof that binds a form on a workload: the RNN form is fp32 vector-ALU work; the full and
-    chunk forms are matrix-core work, bound by HBM below the bf16 ridge (peak flops / peak bytes) and
-    by the matrix cores above it."""
-    if form in ("birnn", "chunk_bwd"):
+    """The roof that binds a form on a workload: fp32 work (fp32_form) is priced on the fp32 peak; the
+    bf16 matrix-core forms are bound by HBM below the bf16 ridge (peak flops / peak bytes) and by the
+    matrix cores above it."""
+    if fp32_form(form, C):
         return "alu"
     nbytes, flops = algorithmic(form, wl, C, causal)
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -469,7 +476,7 @@ def main():
             "bound": bound,
             "frac_of_roof": (gbps if bound == "hbm" else tflops) / pk,
             "frac_hbm": gbps / HBM_PEAK_GBS,
-            "frac_mfma_bf16": tflops / MFMA_BF16_PEAK_TFLOPS if f not in ("birnn", "chunk_bwd") else None,
+            "frac_mfma_bf16": None if fp32_form(f, C) else tflops / MFMA_BF16_PEAK_TFLOPS,
             "memory": memory_bytes(f, wl, C, ws_bytes[key]),
             "launch_us": spread[key],
         }

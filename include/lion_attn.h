@@ -211,11 +211,13 @@ LION_API int lion_attn_full_bwd(const void *q, const void *k, const void *v, con
  * construction over phi(q) and [dy / den, -delta]), so the work grows as L C d + L d^2 rather than
  * L^2 d.  Sources: as for lion_attn_full_bwd, and the chunkwise form of lion_attn_chunk (reply
  * "4: Practicality of Recurrent Inference"; blog "LION Part IV - Results", "LION Chunk").
- *   C          16, 32 or 64 (at most 32 when d = 128); other values are LION_ERR_UNSUPPORTED.
+ *   C          16 or 32 (fp32 matrix-core products, fp32 states), 64 or 128 (bf16 matrix-core products
+ *              with fp32 sums, as the full form's backward; 128 needs d <= 64); other values are
+ *              LION_ERR_UNSUPPORTED.
  *   every other argument as for lion_attn_full_bwd; y and den may come from any forward form.
- *   workspace  >= lion_attn_workspace_bytes(LION_FORM_CHUNK_BWD, ..., C, ...) bytes: four fp32
- *              d x (d+1) states (rows padded to d + 4) per chunk and (batch, head), plus 8 B H L;
- *              contents on entry do not matter.
+ *   workspace  >= lion_attn_workspace_bytes(LION_FORM_CHUNK_BWD, ..., C, ...) bytes: four states per
+ *              chunk and (batch, head) -- C <= 32: fp32 d x (d+1) (rows padded to d + 4); C >= 64: a
+ *              bf16 d x d block and an fp32 last column -- plus 8 B H L; contents on entry do not matter.
  * Errors as for the forward entry points. */
 LION_API int lion_attn_chunk_bwd(const void *q, const void *k, const void *v, const float *log_lambda, int mask_kind,
                                  int C, int B, int H, int L, int d, int dtype, const void *y, const float *den,

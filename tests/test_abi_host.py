@@ -210,19 +210,27 @@ def test_chunk_bwd_invalid_arguments(name, kw):
 def test_chunk_bwd_unsupported_and_workspace():
     assert cbwd(dt=0) == UNSUPPORTED                 # fp32 inputs
     assert cbwd(d=16) == UNSUPPORTED
-    for C in (8, 128, 256, 0):
+    for C in (8, 256, 0):
         assert cbwd(C=C) == UNSUPPORTED
-    assert cbwd(C=64, d=128) == UNSUPPORTED          # LDS: at most 32 tokens per chunk at d = 128
-    assert lion.lion_attn_workspace_bytes(lion.FORM_CHUNK_BWD, 2, 3, 17, 128, 64, 1) == SIZE_MAX
+    assert cbwd(C=128, d=128) == UNSUPPORTED         # chunks of 128 need d <= 64
+    assert lion.lion_attn_workspace_bytes(lion.FORM_CHUNK_BWD, 2, 3, 17, 128, 128, 1) == SIZE_MAX
     assert lion.lion_attn_workspace_bytes(lion.FORM_CHUNK_BWD, 2, 3, 17, 64, 64, 0) == SIZE_MAX
-    # four d x (d+1) fp32 states (rows padded to d + 4) per chunk and (batch, head), two dA halves
-    B, H, L, d, C = 2, 3, 150, 64, 32
-    nch = (L + C - 1) // C
-    want = 4 * (4 * B * H * nch * d * (d + 4) + 2 * ((B * H * L + 3) // 4) * 4)
-    need = lion.lion_attn_workspace_bytes(lion.FORM_CHUNK_BWD, B, H, L, d, C, 1)
-    assert need == want
-    assert cbwd(C=C, B=B, H=H, L=L, ws=None, wsb=need) == WORKSPACE
-    assert cbwd(C=C, B=B, H=H, L=L, ws=P, wsb=need - 1) == WORKSPACE
+    B, H, L, d = 2, 3, 150, 64
+    da = 4 * 2 * ((B * H * L + 3) // 4) * 4          # the two dA halves
+    # chunks of 16 and 32: four d x (d+1) fp32 states (rows padded to d + 4) per chunk and (batch, head)
+    for C in (16, 32):
+        nch = (L + C - 1) // C
+        want = 4 * 4 * B * H * nch * d * (d + 4) + da
+        need = lion.lion_attn_workspace_bytes(lion.FORM_CHUNK_BWD, B, H, L, d, C, 1)
+        assert need == want
+        assert cbwd(C=C, B=B, H=H, L=L, ws=None, wsb=need) == WORKSPACE
+        assert cbwd(C=C, B=B, H=H, L=L, ws=P, wsb=need - 1) == WORKSPACE
+    # chunks of 64 and 128: four bf16 d x d blocks and four fp32 last columns per chunk
+    for C in (64, 128):
+        nch = (L + C - 1) // C
+        want = B * H * nch * 4 * (2 * d * d + 4 * d) + da
+        assert lion.lion_attn_workspace_bytes(lion.FORM_CHUNK_BWD, B, H, L, d, C, 1) == want
+        assert cbwd(C=C, B=B, H=H, L=L, ws=P, wsb=want - 1) == WORKSPACE
 
 
 def chunk2(order=P, C=64, ws=P, wsb=1 << 40, **kw):

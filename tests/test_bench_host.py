@@ -45,7 +45,8 @@ def test_algorithmic_chunk_bwd():
     nbytes, flops = bench.algorithmic("chunk_bwd", wl, 32)
     assert nbytes == 8 * bh * L * d * 2 + 4 * bh * L + 4 * 12
     assert flops == bh * (10 * L * 32 * d + 8 * L * 32 + L * 20 * d * d)
-    assert bench.bound_of("chunk_bwd", wl, 64) == "alu"
+    assert bench.bound_of("chunk_bwd", wl, 32) == "alu"         # fp32 matrix cores
+    assert bench.bound_of("chunk_bwd", wl, 64) != "alu"         # bf16 matrix cores
 
 
 def test_algorithmic_causal_counts_the_lower_triangle():
@@ -92,7 +93,7 @@ def test_more_than_one_gpu_is_refused():
 def test_form_keys_and_default_forms():
     assert bench.split_form("chunk128") == ("chunk", 128)
     assert bench.split_form("chunk", 64) == ("chunk", 64)
-    assert bench.split_form("chunk_bwd") == ("chunk_bwd", 32)
+    assert bench.split_form("chunk_bwd") == ("chunk_bwd", 64)
     assert bench.split_form("birnn") == ("birnn", 64)
     with pytest.raises(SystemExit):
         bench.split_form("birnn64")
