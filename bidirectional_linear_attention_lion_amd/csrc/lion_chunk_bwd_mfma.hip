@@ -81,6 +81,14 @@ __device__ __forceinline__ void chunk_cum(float *cum, const float *ll, const flo
     }
 }
 
+// x's bits where ok, else zero (a select on whole 32-bit words: a select on bf16 elements compiles to
+// branches)
+__device__ __forceinline__ u32x4 keep_if(bf16x8 x, bool ok) {
+    const u32x4 b = __builtin_bit_cast(u32x4, x);
+    const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+    return b & m;
+}
+
 // ================================ walk ===============================================================
 template <int D, int CT, bool KEYS>
 struct WalkRegs {
@@ -90,6 +98,8 @@ struct WalkRegs {
     float den[KEYS ? 1 : NIT];
 };
 
+// Rows past n load row n - 1 (walk_commit zeroes them): no branch around the loads, so the compiler can
+// count the loads in flight and wait for one chunk's without waiting for the next one's.
 template <int D, int CT, bool KEYS>
 __device__ __forceinline__ void walk_load(const MbParams &p, int bh, int c, int n, WalkRegs<D, CT, KEYS> &R) {
     using WR = WalkRegs<D, CT, KEYS>;
@@ -98,18 +108,16 @@ __device__ __forceinline__ void walk_load(const MbParams &p, int bh, int c, int 
 #pragma unroll
     for (int it = 0; it < WR::NIT; ++it) {
         const int sl = it * kWalkThreads + tid;
-        const int row = sl / WR::SPR, cs = (sl % WR::SPR) * 8;
-        if (row < n) {
-            const size_t g = (row0 + row) * D + cs;
-            if constexpr (KEYS) {
-                R.x[it] = __builtin_bit_cast(bf16x8, ld16(p.k + g));
-                R.y[it] = __builtin_bit_cast(bf16x8, ld16(p.v + g));
-            } else {
-                R.x[it] = __builtin_bit_cast(bf16x8, ld16(p.q + g));
-                R.y[it] = __builtin_bit_cast(bf16x8, ld16(p.dy + g));
-                R.z[it] = __builtin_bit_cast(bf16x8, ld16(p.y + g));
-                R.den[it] = p.den[row0 + row];
-            }
+        const int row = min(sl / WR::SPR, n - 1), cs = (sl % WR::SPR) * 8;
+        const size_t g = (row0 + row) * D + cs;
+        if constexpr (KEYS) {
+            R.x[it] = __builtin_bit_cast(bf16x8, ld16(p.k + g));
+            R.y[it] = __builtin_bit_cast(bf16x8, ld16(p.v + g));
+        } else {
+            R.x[it] = __builtin_bit_cast(bf16x8, ld16(p.q + g));
+            R.y[it] = __builtin_bit_cast(bf16x8, ld16(p.dy + g));
+            R.z[it] = __builtin_bit_cast(bf16x8, ld16(p.y + g));
+            R.den[it] = p.den[row0 + row];
         }
     }
 }
@@ -124,7 +132,7 @@ __device__ __forceinline__ void walk_commit(const MbParams &p, __bf16 *Xt, __bf1
     using RT = RowTile<D, __bf16>;
     constexpr int SPR = WR::SPR;
     const int tid = threadIdx.x;
-    if (tid < 64)
+    if (uniform(tid >> 6) == 0)
         chunk_cum<KIND, CT>(cum, p.ll, KIND == kMaskS ? p.ll + (size_t)bh * p.L + (size_t)c * CT : nullptr, bh % p.H, n,
                             tid);
     __syncthreads();
@@ -134,34 +142,44 @@ __device__ __forceinline__ void walk_commit(const MbParams &p, __bf16 *Xt, __bf1
         const int sl = it * kWalkThreads + tid;
         const int row = sl / SPR, cs = (sl % SPR) * 8;
         const bool ok = row < n;
+        // rows past n hold row n - 1's values (finite): computed alike, zeroed through the scale
         float fx[8], ss = 0.f, part = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            fx[e] = ok ? phi_pre<KIND>((float)R.x[it][e]) : 0.f;
+            fx[e] = phi_pre<KIND>((float)R.x[it][e]);
             ss += fx[e] * fx[e];
-            if constexpr (!KEYS) part += ok ? (float)R.y[it][e] * (float)R.z[it][e] : 0.f;
+            if constexpr (!KEYS) part += (float)R.y[it][e] * (float)R.z[it][e];
         }
-        float scl = 1.f;
-        if constexpr (KIND == kMaskS) scl = inv_norm(group_sum<SPR>(ss));
+        float scl = ok ? 1.f : 0.f;
+        if constexpr (KIND == kMaskS) scl *= inv_norm(group_sum<SPR>(ss));
         if constexpr (KIND != kMaskLit) scl *= fast_exp2(dir == 0 ? tot - cum[row] : cum[row]);
         if constexpr (!KEYS) {
             part = group_sum<SPR>(part);
-            if (ok) scl *= __builtin_amdgcn_rcpf(R.den[it]);
+            scl *= __builtin_amdgcn_rcpf(R.den[it]);
             if (sl % SPR == 0) cz[row] = ok ? -part : 0.f;
         }
-        bf16x8 xo, yo;
+        bf16x8 xo;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            xo[e] = f2bf(fx[e] * scl);
-            yo[e] = ok ? R.y[it][e] : f2bf(0.f);
-        }
+        for (int e = 0; e < 8; ++e) xo[e] = f2bf(fx[e] * scl);
         *reinterpret_cast<bf16x8 *>(Xt + RT::off(row, cs)) = xo;
-        *reinterpret_cast<bf16x8 *>(Yt + RT::off(row, cs)) = yo;
+        *reinterpret_cast<u32x4 *>(Yt + RT::off(row, cs)) = keep_if(R.y[it], ok);
     }
 }
 
 // State tiles: 16 x 16 tiles (tb, ta) of S^T, tb < NA + 1 (the last one holds the last column in its
-// first two rows), ta < NA; wave w takes tiles w, w + 4, ... with ta = tile % NA, tb = tile / NA.
+// first two rows), ta < NA; wave w takes tiles w, w + 4, ... with ta = tile % NA, tb = tile / NA, which for
+// NA a multiple of 4 is ta = w + 4 (u % (NA / 4)), tb = u / (NA / 4): tb then is known at compile time.
+template <int NA>
+__device__ __forceinline__ void walk_tile(int w, int u, int &ta, int &tb) {
+    if constexpr (NA % 4 == 0) {
+        ta = w + 4 * (u % (NA / 4));
+        tb = u / (NA / 4);
+    } else {
+        ta = (w + 4 * u) % NA;
+        tb = (w + 4 * u) / NA;
+    }
+}
+
 template <int D, int KIND, int CT, bool KEYS>
 __device__ void walk(const MbParams &p, unsigned char *smem, int bh, int dir) {
     using RT = RowTile<D, __bf16>;
@@ -170,26 +188,28 @@ __device__ void walk(const MbParams &p, unsigned char *smem, int bh, int dir) {
     __bf16 *Yt = Xt + CT * D;
     float *cum = reinterpret_cast<float *>(Yt + CT * D);
     float *cz = cum + CT + 4;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int st = 2 * dir + (KEYS ? 0 : 1);
     f32x4 acc[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    WalkRegs<D, CT, KEYS> R;
-    {
-        const int c = dir == 0 ? 0 : p.nch - 1;
-        const int n = min(CT, p.L - c * CT);
-        walk_load<D, CT, KEYS>(p, bh, c, n, R);
-        walk_commit<D, KIND, CT, KEYS>(p, Xt, Yt, cum, cz, bh, c, n, dir, R);
-        __syncthreads();
-    }
-#pragma unroll 1
-    for (int step = 0; step < p.nch; ++step) {
-        const int c = dir == 0 ? step : p.nch - 1 - step;
-        const int cn = dir == 0 ? c + 1 : c - 1;
-        const int nn = min(CT, p.L - cn * CT);
-        const bool more = step + 1 < p.nch;
-        if (more) walk_load<D, CT, KEYS>(p, bh, cn, nn, R);   // in flight while this chunk is summed
+    // Two chunks of loads in flight: the rows of the chunk after next are issued while this chunk is
+    // summed, into the register set the next chunk's rows have just left (the loop takes two steps per
+    // iteration so each set stays a fixed set of registers).
+    WalkRegs<D, CT, KEYS> RA, RB;
+    auto chunk_of = [&](int step) { return dir == 0 ? step : p.nch - 1 - step; };
+    auto rows_of = [&](int step) { return min(CT, p.L - chunk_of(step) * CT); };
+    walk_load<D, CT, KEYS>(p, bh, chunk_of(0), rows_of(0), RA);
+    walk_commit<D, KIND, CT, KEYS>(p, Xt, Yt, cum, cz, bh, chunk_of(0), rows_of(0), dir, RA);
+    __syncthreads();
+    walk_load<D, CT, KEYS>(p, bh, chunk_of(min(1, p.nch - 1)), rows_of(min(1, p.nch - 1)), RA);
+    // one chunk: R1 holds (or is receiving) the next chunk's rows, R2 takes the chunk after next
+    auto one_step = [&](int step, WalkRegs<D, CT, KEYS> &R1, WalkRegs<D, CT, KEYS> &R2) {
+        const int c = chunk_of(step);
+        {   // unconditionally (past the end: the last chunk again, unused), for the same reason as above
+            const int s2 = min(step + 2, p.nch - 1);
+            walk_load<D, CT, KEYS>(p, bh, chunk_of(s2), rows_of(s2), R2);
+        }
         // the state entering chunk c is the running sum so far
         const size_t so = ((size_t)bh * p.nch + c) * 4 + st;
         __bf16 *sd = p.st + so * D * D;
@@ -197,15 +217,18 @@ __device__ void walk(const MbParams &p, unsigned char *smem, int bh, int dir) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int tile = w + 4 * u;
-            if (tile >= NT) break;
-            const int ta = tile % NA, tb = tile / NA, a = 16 * ta + r;
+            if (NT % 4 != 0 && tile >= NT) break;
+            int ta, tb;
+            walk_tile<NA>(w, u, ta, tb);
+            const int a = 16 * ta + r;
             if (tb < NA) {
                 bf16x4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = f2bf(acc[u][e]);
                 *reinterpret_cast<bf16x4 *>(sd + a * D + 16 * tb + 4 * g) = o;
-            } else if (g == 0) {
-                zd[a] = acc[u][0] + acc[u][1];
+            } else {
+                // hi + lo in lane r of group 0; the row's four lanes store the same value
+                zd[a] = __shfl(acc[u][0] + acc[u][1], r, 64);
             }
         }
         // decay across the chunk, then add its tokens: S^T[b][a] += sum_j Y_j[b] X'_j[a]
@@ -223,28 +246,34 @@ __device__ void walk(const MbParams &p, unsigned char *smem, int bh, int dir) {
             } else {
                 const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cz + h * kKB + 4 * g);
                 const f32x4 c1 = *reinterpret_cast<const f32x4 *>(cz + h * kKB + 16 + 4 * g);
+                // selected in fp32: lane r = 0 rounds c (the hi part), r = 1 the rest (the lo part)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const __bf16 h0 = f2bf(c0[e]), h1 = f2bf(c1[e]);
-                    const __bf16 l0 = f2bf(c0[e] - (float)h0), l1 = f2bf(c1[e] - (float)h1);
-                    zf[e] = r == 0 ? h0 : (r == 1 ? l0 : f2bf(0.f));
-                    zf[4 + e] = r == 0 ? h1 : (r == 1 ? l1 : f2bf(0.f));
+                    const float r0 = c0[e] - (float)f2bf(c0[e]), r1 = c1[e] - (float)f2bf(c1[e]);
+                    zf[e] = f2bf(r == 0 ? c0[e] : (r == 1 ? r0 : 0.f));
+                    zf[4 + e] = f2bf(r == 0 ? c1[e] : (r == 1 ? r1 : 0.f));
                 }
             }
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 const int tile = w + 4 * u;
-                if (tile >= NT) break;
-                const int ta = tile % NA, tb = tile / NA;
+                if (NT % 4 != 0 && tile >= NT) break;
+                int ta, tb;
+                walk_tile<NA>(w, u, ta, tb);
                 const bf16x8 af = tb < NA ? tr_frag<D>(Yt, h, tb, r, g) : zf;
                 acc[u] = mfma_bf16(af, tr_frag<D>(Xt, h, ta, r, g), acc[u]);
             }
         }
         __syncthreads();   // before the next chunk's rows overwrite these
-        if (more) {
-            walk_commit<D, KIND, CT, KEYS>(p, Xt, Yt, cum, cz, bh, cn, nn, dir, R);
+        if (step + 1 < p.nch) {
+            walk_commit<D, KIND, CT, KEYS>(p, Xt, Yt, cum, cz, bh, chunk_of(step + 1), rows_of(step + 1), dir, R1);
             __syncthreads();
         }
+    };
+#pragma unroll 1
+    for (int step = 0; step < p.nch; step += 2) {
+        one_step(step, RA, RB);
+        if (step + 1 < p.nch) one_step(step + 1, RB, RA);
     }
 }
 
@@ -282,7 +311,7 @@ struct MainLds {
 };
 
 template <int D, int KIND, int CT>
-__global__ void __launch_bounds__(CT * 4) mb_main_kernel(MbParams p) {
+__global__ void __launch_bounds__(CT * 4) __attribute__((amdgpu_waves_per_eu(3))) mb_main_kernel(MbParams p) {
     using RT = RowTile<D, __bf16>;
     using ML = MainLds<D, CT>;
     constexpr int NS = D / 32, NCT = D / 16, SPR = D / 8, NW = CT / 16, NT = CT * 4;
@@ -345,19 +374,17 @@ __global__ void __launch_bounds__(CT * 4) mb_main_kernel(MbParams p) {
                 sk *= inv_norm(group_sum<SPR>(ssk));
             }
             part = group_sum<SPR>(part);
-            bf16x8 oq, ok8, ov, og;
+            bf16x8 oq, ok8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 oq[e] = f2bf(fq[e] * sq);
                 ok8[e] = f2bf(fk[e] * sk);
-                ov[e] = ok ? rv[it][e] : f2bf(0.f);
-                og[e] = ok ? rg[it][e] : f2bf(0.f);
             }
             const int at = RT::off(row, cs);
             *reinterpret_cast<bf16x8 *>(Qt + at) = oq;
             *reinterpret_cast<bf16x8 *>(Kt + at) = ok8;
-            *reinterpret_cast<bf16x8 *>(Vt + at) = ov;
-            *reinterpret_cast<bf16x8 *>(Gt + at) = og;
+            *reinterpret_cast<u32x4 *>(Vt + at) = keep_if(rv[it], ok);
+            *reinterpret_cast<u32x4 *>(Gt + at) = keep_if(rg[it], ok);
             if (sl % SPR == 0) {
                 const float iv = ok ? 1.f / p.den[row0 + row] : 0.f;
                 inv[row] = iv;
