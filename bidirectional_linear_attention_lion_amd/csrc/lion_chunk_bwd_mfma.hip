@@ -96,11 +96,12 @@ struct WalkRegs {
     static constexpr int NIT = CT * SPR / kWalkThreads;   // slots per thread
     bf16x8 x[NIT], y[NIT], z[KEYS ? 1 : NIT];             // keys: k, v; queries: q, dy, y
     float den[KEYS ? 1 : NIT];
+    float ll[CT / 64];                                    // LION-S: tokens R lane + k of the chunk
 };
 
 // Rows past n load row n - 1 (walk_commit zeroes them): no branch around the loads, so the compiler can
 // count the loads in flight and wait for one chunk's without waiting for the next one's.
-template <int D, int CT, bool KEYS>
+template <int D, int KIND, int CT, bool KEYS>
 __device__ __forceinline__ void walk_load(const MbParams &p, int bh, int c, int n, WalkRegs<D, CT, KEYS> &R) {
     using WR = WalkRegs<D, CT, KEYS>;
     const int tid = threadIdx.x;
@@ -120,23 +121,56 @@ __device__ __forceinline__ void walk_load(const MbParams &p, int bh, int c, int 
             R.den[it] = p.den[row0 + row];
         }
     }
+    if constexpr (KIND == kMaskS) {
+        constexpr int RL = CT / 64;
+#pragma unroll
+        for (int k = 0; k < RL; ++k) R.ll[k] = p.ll[row0 + min((tid & 63) * RL + k, n - 1)];
+    }
 }
 
-// The chunk's rows into the LDS tiles: Xt = w phi(x) (/ den for queries), Yt = v or dy (rows at or past n
-// zero), cz = the last column's entries (queries: -dy.y; keys: unused).  Two barriers inside: the prefix
-// sums first (wave 0), then the rows.
+// LION-S: the chunk's inclusive prefix sums of log(lambda) in log2 units (cum[t], repeating the last one
+// past n) and its total (cum[CT]) from the decays walk_load left in registers; run by one whole wave.
+template <int D, int CT, bool KEYS>
+__device__ __forceinline__ void walk_scan(float *cum, const WalkRegs<D, CT, KEYS> &R, int n, int lane) {
+    constexpr int RL = CT / 64;
+    double x[RL], s = 0.0;
+#pragma unroll
+    for (int k = 0; k < RL; ++k) {
+        s += lane * RL + k < n ? (double)R.ll[k] : 0.0;
+        x[k] = s;
+    }
+    double incl = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double up = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += up;
+    }
+    const double excl = incl - s;
+#pragma unroll
+    for (int k = 0; k < RL; ++k) cum[lane * RL + k] = (float)((excl + x[k]) * 1.4426950408889634);
+    const double tot = __shfl(incl, 63, 64);
+    if (lane == 0) cum[CT] = (float)(tot * 1.4426950408889634);
+}
+
+// Prefix sum at row t of a chunk of n rows (log2 units): LION-D in closed form from lg = log2(lambda_h),
+// LION-S from the scanned table.
+template <int KIND, int CT>
+__device__ __forceinline__ float walk_cum(const float *cum, float lg, int t, int n) {
+    if constexpr (KIND == kMaskD) return (float)(min(t, n - 1) + 1) * lg;
+    else if constexpr (KIND == kMaskS) return cum[min(t, CT)];
+    else return 0.f;
+}
+
+// The chunk's rows into one buffer of LDS tiles: Xt = w phi(x) (/ den for queries), Yt = v or dy (rows
+// at or past n zero), cz = the last column's entries (queries: -dy.y; keys: unused).  No barrier inside.
 template <int D, int KIND, int CT, bool KEYS>
-__device__ __forceinline__ void walk_commit(const MbParams &p, __bf16 *Xt, __bf16 *Yt, float *cum, float *cz, int bh,
-                                            int c, int n, int dir, const WalkRegs<D, CT, KEYS> &R) {
+__device__ __forceinline__ void walk_commit(__bf16 *Xt, __bf16 *Yt, const float *cum, float *cz, int n, int dir,
+                                            float lg, const WalkRegs<D, CT, KEYS> &R) {
     using WR = WalkRegs<D, CT, KEYS>;
     using RT = RowTile<D, __bf16>;
     constexpr int SPR = WR::SPR;
     const int tid = threadIdx.x;
-    if (uniform(tid >> 6) == 0)
-        chunk_cum<KIND, CT>(cum, p.ll, KIND == kMaskS ? p.ll + (size_t)bh * p.L + (size_t)c * CT : nullptr, bh % p.H, n,
-                            tid);
-    __syncthreads();
-    const float tot = cum[CT];
+    const float tot = KIND == kMaskD ? (float)n * lg : walk_cum<KIND, CT>(cum, lg, CT, n + 1);
 #pragma unroll
     for (int it = 0; it < WR::NIT; ++it) {
         const int sl = it * kWalkThreads + tid;
@@ -152,7 +186,10 @@ __device__ __forceinline__ void walk_commit(const MbParams &p, __bf16 *Xt, __bf1
         }
         float scl = ok ? 1.f : 0.f;
         if constexpr (KIND == kMaskS) scl *= inv_norm(group_sum<SPR>(ss));
-        if constexpr (KIND != kMaskLit) scl *= fast_exp2(dir == 0 ? tot - cum[row] : cum[row]);
+        if constexpr (KIND != kMaskLit) {
+            const float cr = walk_cum<KIND, CT>(cum, lg, row, n);
+            scl *= fast_exp2(dir == 0 ? tot - cr : cr);
+        }
         if constexpr (!KEYS) {
             part = group_sum<SPR>(part);
             scl *= __builtin_amdgcn_rcpf(R.den[it]);
@@ -180,35 +217,53 @@ __device__ __forceinline__ void walk_tile(int w, int u, int &ta, int &tb) {
     }
 }
 
+template <int D, int CT>
+struct WalkLds {
+    static constexpr int TILE = CT * D;                              // bf16 elements per tile
+    static constexpr int CUM = CT + 4, CZ = CT;                      // floats per buffer
+    static constexpr size_t BYTES = (size_t)4 * TILE * 2 + (size_t)2 * (CUM + CZ) * 4;
+};
+
+// The staged tiles, prefix sums and last-column entries are double-buffered: chunk s is summed from
+// buffer s & 1 while chunk s + 1 is staged into the other, so a step needs one barrier (two for LION-S,
+// whose prefix sums are scanned by one wave first).
 template <int D, int KIND, int CT, bool KEYS>
 __device__ void walk(const MbParams &p, unsigned char *smem, int bh, int dir) {
-    using RT = RowTile<D, __bf16>;
+    using WL = WalkLds<D, CT>;
     constexpr int NA = D / 16, NT = NA * (NA + 1), NU = (NT + 3) / 4;
-    __bf16 *Xt = reinterpret_cast<__bf16 *>(smem);
-    __bf16 *Yt = Xt + CT * D;
-    float *cum = reinterpret_cast<float *>(Yt + CT * D);
-    float *cz = cum + CT + 4;
+    __bf16 *Xt0 = reinterpret_cast<__bf16 *>(smem);
+    float *cum0 = reinterpret_cast<float *>(Xt0 + 4 * WL::TILE);
+    auto Xt = [&](int b) { return Xt0 + 2 * b * WL::TILE; };
+    auto Yt = [&](int b) { return Xt0 + (2 * b + 1) * WL::TILE; };
+    auto cum = [&](int b) { return cum0 + b * (WL::CUM + WL::CZ); };
+    auto cz = [&](int b) { return cum0 + b * (WL::CUM + WL::CZ) + WL::CUM; };
     const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int st = 2 * dir + (KEYS ? 0 : 1);
+    const float lg = KIND == kMaskD ? p.ll[bh % p.H] * kLog2e : 0.f;
     f32x4 acc[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     // Two chunks of loads in flight: the rows of the chunk after next are issued while this chunk is
     // summed, into the register set the next chunk's rows have just left (the loop takes two steps per
-    // iteration so each set stays a fixed set of registers).
+    // iteration so each set, and each buffer, stays fixed).
     WalkRegs<D, CT, KEYS> RA, RB;
     auto chunk_of = [&](int step) { return dir == 0 ? step : p.nch - 1 - step; };
     auto rows_of = [&](int step) { return min(CT, p.L - chunk_of(step) * CT); };
-    walk_load<D, CT, KEYS>(p, bh, chunk_of(0), rows_of(0), RA);
-    walk_commit<D, KIND, CT, KEYS>(p, Xt, Yt, cum, cz, bh, chunk_of(0), rows_of(0), dir, RA);
+    walk_load<D, KIND, CT, KEYS>(p, bh, chunk_of(0), rows_of(0), RA);
+    if constexpr (KIND == kMaskS) {
+        if (w == 0) walk_scan<D, CT, KEYS>(cum(0), RA, rows_of(0), lane);
+        __syncthreads();
+    }
+    walk_commit<D, KIND, CT, KEYS>(Xt(0), Yt(0), cum(0), cz(0), rows_of(0), dir, lg, RA);
     __syncthreads();
-    walk_load<D, CT, KEYS>(p, bh, chunk_of(min(1, p.nch - 1)), rows_of(min(1, p.nch - 1)), RA);
-    // one chunk: R1 holds (or is receiving) the next chunk's rows, R2 takes the chunk after next
-    auto one_step = [&](int step, WalkRegs<D, CT, KEYS> &R1, WalkRegs<D, CT, KEYS> &R2) {
-        const int c = chunk_of(step);
+    walk_load<D, KIND, CT, KEYS>(p, bh, chunk_of(min(1, p.nch - 1)), rows_of(min(1, p.nch - 1)), RA);
+    // one chunk, summed from buffer b: R1 holds (or is receiving) the next chunk's rows, R2 takes the
+    // chunk after next
+    auto one_step = [&](int step, int b, WalkRegs<D, CT, KEYS> &R1, WalkRegs<D, CT, KEYS> &R2) {
+        const int c = chunk_of(step), n = rows_of(step);
         {   // unconditionally (past the end: the last chunk again, unused), for the same reason as above
             const int s2 = min(step + 2, p.nch - 1);
-            walk_load<D, CT, KEYS>(p, bh, chunk_of(s2), rows_of(s2), R2);
+            walk_load<D, KIND, CT, KEYS>(p, bh, chunk_of(s2), rows_of(s2), R2);
         }
         // the state entering chunk c is the running sum so far
         const size_t so = ((size_t)bh * p.nch + c) * 4 + st;
@@ -232,9 +287,12 @@ __device__ void walk(const MbParams &p, unsigned char *smem, int bh, int dir) {
             }
         }
         // decay across the chunk, then add its tokens: S^T[b][a] += sum_j Y_j[b] X'_j[a]
-        const float dec = KIND == kMaskLit ? 1.f : fast_exp2(cum[CT]);
+        const float dec = KIND == kMaskD ? fast_exp2((float)n * lg)
+                                         : KIND == kMaskS ? fast_exp2(cum(b)[CT]) : 1.f;
 #pragma unroll
         for (int u = 0; u < NU; ++u) acc[u] *= dec;
+        const __bf16 *xb = Xt(b), *yb = Yt(b);
+        const float *czb = cz(b);
 #pragma unroll
         for (int h = 0; h < CT / kKB; ++h) {
             // the last column's tile: row 0 the hi part, row 1 the lo part (keys: 1), at the tokens of
@@ -244,8 +302,8 @@ __device__ void walk(const MbParams &p, unsigned char *smem, int bh, int dir) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) zf[e] = f2bf(r == 0 ? 1.f : 0.f);
             } else {
-                const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cz + h * kKB + 4 * g);
-                const f32x4 c1 = *reinterpret_cast<const f32x4 *>(cz + h * kKB + 16 + 4 * g);
+                const f32x4 c0 = *reinterpret_cast<const f32x4 *>(czb + h * kKB + 4 * g);
+                const f32x4 c1 = *reinterpret_cast<const f32x4 *>(czb + h * kKB + 16 + 4 * g);
                 // selected in fp32: lane r = 0 rounds c (the hi part), r = 1 the rest (the lo part)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -260,20 +318,26 @@ __device__ void walk(const MbParams &p, unsigned char *smem, int bh, int dir) {
                 if (NT % 4 != 0 && tile >= NT) break;
                 int ta, tb;
                 walk_tile<NA>(w, u, ta, tb);
-                const bf16x8 af = tb < NA ? tr_frag<D>(Yt, h, tb, r, g) : zf;
-                acc[u] = mfma_bf16(af, tr_frag<D>(Xt, h, ta, r, g), acc[u]);
+                const bf16x8 af = tb < NA ? tr_frag<D>(yb, h, tb, r, g) : zf;
+                acc[u] = mfma_bf16(af, tr_frag<D>(xb, h, ta, r, g), acc[u]);
             }
         }
-        __syncthreads();   // before the next chunk's rows overwrite these
+        // stage the next chunk into the other buffer (its last readers finished before the previous
+        // step's barrier)
         if (step + 1 < p.nch) {
-            walk_commit<D, KIND, CT, KEYS>(p, Xt, Yt, cum, cz, bh, chunk_of(step + 1), rows_of(step + 1), dir, R1);
-            __syncthreads();
+            const int nb = b ^ 1, n1 = rows_of(step + 1);
+            if constexpr (KIND == kMaskS) {
+                if (w == 0) walk_scan<D, CT, KEYS>(cum(nb), R1, n1, lane);
+                __syncthreads();
+            }
+            walk_commit<D, KIND, CT, KEYS>(Xt(nb), Yt(nb), cum(nb), cz(nb), n1, dir, lg, R1);
         }
+        __syncthreads();   // the next chunk's buffer is written; this one's readers are done
     };
 #pragma unroll 1
     for (int step = 0; step < p.nch; step += 2) {
-        one_step(step, RA, RB);
-        if (step + 1 < p.nch) one_step(step + 1, RB, RA);
+        one_step(step, 0, RA, RB);
+        if (step + 1 < p.nch) one_step(step + 1, 1, RB, RA);
     }
 }
 
@@ -287,11 +351,6 @@ __global__ void __launch_bounds__(kWalkThreads) mb_walk_kernel(MbParams p) {
     const bool keys = p.causal ? s == 0 : (s & 1) == 0;
     if (keys) walk<D, KIND, CT, true>(p, smem, bh, dir);
     else walk<D, KIND, CT, false>(p, smem, bh, dir);
-}
-
-template <int D, int CT>
-constexpr size_t walk_lds() {
-    return (size_t)2 * CT * D * 2 + (size_t)(2 * CT + 8) * 4;
 }
 
 // ================================ main ===============================================================
@@ -663,7 +722,7 @@ hipError_t launch_mb_t(const BwdArgs &a, hipStream_t stream) {
     p.da_row = reinterpret_cast<float *>(ws + w.da);
     p.da_col = p.da_row + ((n + 3) / 4) * 4;
     if (p.nch > 1) {
-        constexpr size_t lw = walk_lds<D, CT>();
+        constexpr size_t lw = WalkLds<D, CT>::BYTES;
         allow_lds(&mb_walk_kernel<D, KIND, CT>, lw);
         hipLaunchKernelGGL((mb_walk_kernel<D, KIND, CT>), dim3(a.B * a.H * (a.causal ? 2 : 4)), dim3(kWalkThreads), lw,
                            stream, p);
