@@ -369,11 +369,15 @@ struct MainLds {
     static constexpr int NSF = 2 * CT / D < 4 ? 2 * CT / D : 4;  // states staged at once (value + dy tiles' space)
 };
 
+// The workgroup has 2 C / 16 waves: waves [0, C / 16) take the query side of query tile w (dphi(q) and
+// the row half of dA), waves [C / 16, 2 C / 16) the key side of key tile w - C / 16 (dphi(k), dv and the
+// column half).  Each side keeps only its own accumulators, and the two run as separate code paths
+// (with the same barriers), so a wave's registers hold one side's work.
 template <int D, int KIND, int CT>
-__global__ void __launch_bounds__(CT * 4) __attribute__((amdgpu_waves_per_eu(3))) mb_main_kernel(MbParams p) {
+__global__ void __launch_bounds__(CT * 8) mb_main_kernel(MbParams p) {
     using RT = RowTile<D, __bf16>;
     using ML = MainLds<D, CT>;
-    constexpr int NS = D / 32, NCT = D / 16, SPR = D / 8, NW = CT / 16, NT = CT * 4;
+    constexpr int NS = D / 32, NCT = D / 16, SPR = D / 8, NW = CT / 16, NWG = 2 * NW, NT = 64 * NWG;
     extern __shared__ __align__(16) unsigned char smem[];
     __bf16 *Qt = reinterpret_cast<__bf16 *>(smem);
     __bf16 *Kt = Qt + ML::TILE, *Vt = Kt + ML::TILE, *Gt = Vt + ML::TILE;
@@ -382,7 +386,8 @@ __global__ void __launch_bounds__(CT * 4) __attribute__((amdgpu_waves_per_eu(3))
 
     const int bh = blockIdx.x / p.nch, c = blockIdx.x % p.nch;
     const int n = min(CT, p.L - c * CT);
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const int tw = w % NW;           // this wave's 16-row tile
     const size_t row0 = (size_t)bh * p.L + (size_t)c * CT;
     const bool causal = p.causal != 0;
 
@@ -400,11 +405,11 @@ __global__ void __launch_bounds__(CT * 4) __attribute__((amdgpu_waves_per_eu(3))
 
     // ---- stage the chunk: phi(q), phi(k), v, dy as bf16 rows (zero past n); 1/den and delta per row
     {
-        constexpr int NIT = CT * SPR / NT;
+        constexpr int NSL = CT * SPR, NIT = (NSL + NT - 1) / NT;
         bf16x8 rq[NIT], rk[NIT], rv[NIT], rg[NIT], ry[NIT];
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int sl = it * NT + tid;
+            const int sl = min(it * NT + tid, NSL - 1);
             const int row = sl / SPR, cs = (sl % SPR) * 8;
             const size_t gi = (row0 + min(row, n - 1)) * D + cs;
             rq[it] = __builtin_bit_cast(bf16x8, ld16(p.q + gi));
@@ -415,8 +420,8 @@ __global__ void __launch_bounds__(CT * 4) __attribute__((amdgpu_waves_per_eu(3))
         }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int sl = it * NT + tid;
-            const int row = sl / SPR, cs = (sl % SPR) * 8;
+            const int sl = it * NT + tid;   // slots past NSL (d = 32) repeat the last one and store nothing
+            const int row = min(sl, NSL - 1) / SPR, cs = (sl % SPR) * 8;
             const bool ok = row < n;
             float fq[8], fk[8], ssq = 0.f, ssk = 0.f, part = 0.f;
 #pragma unroll
@@ -439,15 +444,17 @@ __global__ void __launch_bounds__(CT * 4) __attribute__((amdgpu_waves_per_eu(3))
                 oq[e] = f2bf(fq[e] * sq);
                 ok8[e] = f2bf(fk[e] * sk);
             }
-            const int at = RT::off(row, cs);
-            *reinterpret_cast<bf16x8 *>(Qt + at) = oq;
-            *reinterpret_cast<bf16x8 *>(Kt + at) = ok8;
-            *reinterpret_cast<u32x4 *>(Vt + at) = keep_if(rv[it], ok);
-            *reinterpret_cast<u32x4 *>(Gt + at) = keep_if(rg[it], ok);
-            if (sl % SPR == 0) {
-                const float iv = ok ? 1.f / p.den[row0 + row] : 0.f;
-                inv[row] = iv;
-                dl[row] = part * iv;
+            if (NSL % NT == 0 || sl < NSL) {
+                const int at = RT::off(row, cs);
+                *reinterpret_cast<bf16x8 *>(Qt + at) = oq;
+                *reinterpret_cast<bf16x8 *>(Kt + at) = ok8;
+                *reinterpret_cast<u32x4 *>(Vt + at) = keep_if(rv[it], ok);
+                *reinterpret_cast<u32x4 *>(Gt + at) = keep_if(rg[it], ok);
+                if (sl % SPR == 0) {
+                    const float iv = ok ? 1.f / p.den[row0 + row] : 0.f;
+                    inv[row] = iv;
+                    dl[row] = part * iv;
+                }
             }
         }
     }
@@ -459,213 +466,228 @@ __global__ void __launch_bounds__(CT * 4) __attribute__((amdgpu_waves_per_eu(3))
     }
     __syncthreads();
     const float tot = cum[CT];
+    const int i_me = 16 * tw + r;   // this lane's row of the tile
+    const float cum_me = cum[i_me];
 
-    // ---- query tile w against the chunk's keys: dphi(Q)^T (channel 16 ct + 4 g + e, query 16 w + r)
-    const int i_me = 16 * w + r;   // this lane's query row and key row
-    bf16x8 qf[NS], df[NS];
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-        qf[st] = rows_frag<D>(Qt, w >> 1, w & 1, st, r, g);
-        df[st] = rows_frag<D>(Gt, w >> 1, w & 1, st, r, g);
-    }
-    const float inv_me = inv[i_me], dl_me = dl[i_me], cum_me = cum[i_me];
-    f32x4 aq[NCT], ak[NCT], av[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) aq[ct] = ak[ct] = av[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rowterm = 0.f, colterm = 0.f;
+    // The entering states, staged NSF at a time into the value and dy tiles' space as bf16 d x d row
+    // tiles; apply(S, z, st) runs for each (both sides pass through the same barriers).
+    auto rounds = [&](auto &&apply) {
+        __syncthreads();   // every wave is done with the value and dy tiles
+        __bf16 *Sb = Vt;
 #pragma unroll 1
-    for (int h = 0; h < CT / kKB; ++h) {
-        if (causal && h * kKB > 16 * w + 15) break;   // every key after every query of the tile
-        f32x4 sacc[2], dpacc[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                sacc[t] = mfma_bf16(rows_frag<D>(Kt, h, t, st, r, g), qf[st], sacc[t]);
-                dpacc[t] = mfma_bf16(rows_frag<D>(Vt, h, t, st, r, g), df[st], dpacc[t]);
-            }
-        }
-        // element (t, e): key j = 32 h + 16 t + 4 g + e, query i_me
-        bf16x8 dsf;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const f32x4 cj = *reinterpret_cast<const f32x4 *>(cum + h * kKB + 16 * t + 4 * g);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = h * kKB + 16 * t + 4 * g + e;
-                float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(cum_me - cj[e])) : 1.f;
-                if (causal && j > i_me) m = 0.f;
-                const float dp = dpacc[t][e] * inv_me - dl_me;
-                const float wv = dp * (sacc[t][e] * m);
-                rowterm += j < i_me ? wv : (j > i_me ? -wv : 0.f);
-                dsf[4 * t + e] = f2bf(dp * m);
-            }
-        }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) aq[ct] = mfma_bf16(tr_frag<D>(Kt, h, ct, r, g), dsf, aq[ct]);
-    }
-
-    // ---- key tile w against the chunk's queries: dV^T and dphi(K)^T (channel 16 ct + 4 g + e, key 16 w + r)
-    bf16x8 kf[NS], vf[NS];
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-        kf[st] = rows_frag<D>(Kt, w >> 1, w & 1, st, r, g);
-        vf[st] = rows_frag<D>(Vt, w >> 1, w & 1, st, r, g);
-    }
+        for (int k0 = 0; k0 < nst; k0 += ML::NSF) {
+            const int kn = min(ML::NSF, nst - k0);
+            for (int k = 0; k < kn; ++k)
+                stage_rows<D, __bf16>(Sb + k * D * D, p.st + (((size_t)bh * p.nch + c) * 4 + st_at(k0 + k)) * D * D, 0,
+                                      D, D, w, NWG, lane);
+            wait_vm_all();
+            __syncthreads();
 #pragma unroll 1
-    for (int h = 0; h < CT / kKB; ++h) {
-        if (causal && h * kKB + kKB - 1 < 16 * w) continue;   // every query before every key of the tile
-        f32x4 sacc[2], dpacc[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                sacc[t] = mfma_bf16(rows_frag<D>(Qt, h, t, st, r, g), kf[st], sacc[t]);
-                dpacc[t] = mfma_bf16(rows_frag<D>(Gt, h, t, st, r, g), vf[st], dpacc[t]);
+            for (int k = 0; k < kn; ++k) {
+                const int st = st_at(k0 + k);
+                apply(Sb + k * D * D, zst + st * D, st);
             }
+            __syncthreads();   // before the next states overwrite these
         }
-        // element (t, e): query i = 32 h + 16 t + 4 g + e, key i_me
-        bf16x8 pf, dsf;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int ib = h * kKB + 16 * t + 4 * g;
-            const f32x4 iv = *reinterpret_cast<const f32x4 *>(inv + ib);
-            const f32x4 dv4 = *reinterpret_cast<const f32x4 *>(dl + ib);
-            const f32x4 ci = *reinterpret_cast<const f32x4 *>(cum + ib);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = ib + e;
-                float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(ci[e] - cum_me)) : 1.f;
-                if (causal && i_me > i) m = 0.f;
-                const float pm = sacc[t][e] * m;
-                const float dp = dpacc[t][e] * iv[e] - dv4[e];
-                const float wv = dp * pm;
-                colterm += i < i_me ? wv : (i > i_me ? -wv : 0.f);
-                pf[4 * t + e] = f2bf(pm * iv[e]);
-                dsf[4 * t + e] = f2bf(dp * m);
-            }
-        }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            av[ct] = mfma_bf16(tr_frag<D>(Gt, h, ct, r, g), pf, av[ct]);
-            ak[ct] = mfma_bf16(tr_frag<D>(Qt, h, ct, r, g), dsf, ak[ct]);
-        }
-    }
-
-    // ---- the entering states, staged NSF at a time into the value and dy tiles' space as bf16 d x d
-    // row tiles.  phi(q) and phi(k) of this lane's rows at channels 32 hh + 16 t + 4 g + e serve both as
-    // the transposed-slot operand of dv and as the output layout's channels 16 ct + 4 g + e, ct = 2 hh + t.
-    bf16x8 qT[NS], kT[NS];
-#pragma unroll
-    for (int hh = 0; hh < NS; ++hh) {
-        const bf16x4 q0 = row4<D>(Qt, i_me, 32 * hh + 4 * g), q1 = row4<D>(Qt, i_me, 32 * hh + 16 + 4 * g);
-        const bf16x4 k0 = row4<D>(Kt, i_me, 32 * hh + 4 * g), k1 = row4<D>(Kt, i_me, 32 * hh + 16 + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            qT[hh][e] = q0[e];
-            qT[hh][4 + e] = q1[e];
-            kT[hh][e] = k0[e];
-            kT[hh][4 + e] = k1[e];
-        }
-    }
-    __syncthreads();   // every wave is done with the value and dy tiles
-    __bf16 *Sb = Vt;
-#pragma unroll 1
-    for (int k0 = 0; k0 < nst; k0 += ML::NSF) {
-        const int kn = min(ML::NSF, nst - k0);
-        for (int k = 0; k < kn; ++k)
-            stage_rows<D, __bf16>(Sb + k * D * D, p.st + (((size_t)bh * p.nch + c) * 4 + st_at(k0 + k)) * D * D, 0, D, D,
-                                  w, NW, lane);
-        wait_vm_all();
-        __syncthreads();
-#pragma unroll 1
-        for (int k = 0; k < kn; ++k) {
-            const int st = st_at(k0 + k);
-            const bool right = st >= 2, keys = (st & 1) == 0;
-            const float sgn = right ? -1.f : 1.f;
-            const float f = KIND == kMaskLit ? 1.f : fast_exp2(right ? tot - cum_me : cum_me);
-            const __bf16 *S = Sb + k * D * D;
-            const float *z = zst + st * D;
-            float part = 0.f;
-            if (keys) {
-                // dphi(q) += f (F dy / den - F_d delta): F rows as A, dy of the query row as B
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int st2 = 0; st2 < NS; ++st2) o = mfma_bf16(rows_frag<D>(S, ct >> 1, ct & 1, st2, r, g), df[st2], o);
-                    const f32x4 zc = *reinterpret_cast<const f32x4 *>(z + 16 * ct + 4 * g);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float oe = o[e] * inv_me - zc[e] * dl_me;
-                        aq[ct][e] += f * oe;
-                        part += (float)qT[ct >> 1][4 * (ct & 1) + e] * oe;
-                    }
-                }
-                rowterm += sgn * f * part;
-            } else {
-                // dphi(k) += f (G v + G_d): G rows as A, v of the key row as B; dv += f G^T phi(k):
-                // G read transposed as A, phi(k) in the transposed slots as B
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    f32x4 o = {0.f, 0.f, 0.f, 0.f}, ov = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int st2 = 0; st2 < NS; ++st2) {
-                        o = mfma_bf16(rows_frag<D>(S, ct >> 1, ct & 1, st2, r, g), vf[st2], o);
-                        ov = mfma_bf16(tr_frag<D>(S, st2, ct, r, g), kT[st2], ov);
-                    }
-                    const f32x4 zc = *reinterpret_cast<const f32x4 *>(z + 16 * ct + 4 * g);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float oe = o[e] + zc[e];
-                        ak[ct][e] += f * oe;
-                        av[ct][e] += f * ov[e];
-                        part += (float)kT[ct >> 1][4 * (ct & 1) + e] * oe;
-                    }
-                }
-                colterm += sgn * f * part;
-            }
-        }
-        __syncthreads();   // before the next states overwrite these
-    }
-
-    // ---- phi's Jacobian and the stores (this lane: row 16 w + r, channels 16 ct + 4 g .. + 3)
-    rowterm += __shfl_xor(rowterm, 16, 64);
-    rowterm += __shfl_xor(rowterm, 32, 64);
-    colterm += __shfl_xor(colterm, 16, 64);
-    colterm += __shfl_xor(colterm, 32, 64);
-    if (i_me >= n) return;
+    };
     const size_t rowg = row0 + i_me;
     const bool gb = p.g_bf16 != 0;
-    if constexpr (KIND != kMaskD) {
-        float xq[NCT][4], xk[NCT][4];
+
+    if (w < NW) {
+        // ---- query side: dphi(Q)^T (channel 16 ct + 4 g + e, query i_me) against the chunk's keys
+        bf16x8 qf[NS], df[NS];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(p.q + rowg * D + 16 * ct + 4 * g);
-            const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(p.k + rowg * D + 16 * ct + 4 * g);
+        for (int st = 0; st < NS; ++st) {
+            qf[st] = rows_frag<D>(Qt, tw >> 1, tw & 1, st, r, g);
+            df[st] = rows_frag<D>(Gt, tw >> 1, tw & 1, st, r, g);
+        }
+        const float inv_me = inv[i_me], dl_me = dl[i_me];
+        f32x4 aq[NCT];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xq[ct][e] = (float)q4[e];
-                xk[ct][e] = (float)k4[e];
+        for (int ct = 0; ct < NCT; ++ct) aq[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float rowterm = 0.f;
+#pragma unroll 1
+        for (int h = 0; h < CT / kKB; ++h) {
+            if (causal && h * kKB > 16 * tw + 15) break;   // every key after every query of the tile
+            f32x4 sacc[2], dpacc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    sacc[t] = mfma_bf16(rows_frag<D>(Kt, h, t, st, r, g), qf[st], sacc[t]);
+                    dpacc[t] = mfma_bf16(rows_frag<D>(Vt, h, t, st, r, g), df[st], dpacc[t]);
+                }
+            }
+            // element (t, e): key j = 32 h + 16 t + 4 g + e, query i_me
+            bf16x8 dsf;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const f32x4 cj = *reinterpret_cast<const f32x4 *>(cum + h * kKB + 16 * t + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = h * kKB + 16 * t + 4 * g + e;
+                    float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(cum_me - cj[e])) : 1.f;
+                    if (causal && j > i_me) m = 0.f;
+                    const float dp = dpacc[t][e] * inv_me - dl_me;
+                    const float wv = dp * (sacc[t][e] * m);
+                    rowterm += j < i_me ? wv : (j > i_me ? -wv : 0.f);
+                    dsf[4 * t + e] = f2bf(dp * m);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) aq[ct] = mfma_bf16(tr_frag<D>(Kt, h, ct, r, g), dsf, aq[ct]);
+        }
+        // the keys' states: dphi(q) += f (F dy / den - F_d delta), F rows as A and dy of the query row as
+        // B; the row half of dA takes phi(q) . that (phi(q) at the output layout's channels)
+        rounds([&](const __bf16 *S, const float *z, int st) {
+            if (st & 1) return;   // a queries' state: the key side's
+            const bool right = st >= 2;
+            const float f = KIND == kMaskLit ? 1.f : fast_exp2(right ? tot - cum_me : cum_me);
+            float part = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st2 = 0; st2 < NS; ++st2) o = mfma_bf16(rows_frag<D>(S, ct >> 1, ct & 1, st2, r, g), df[st2], o);
+                const f32x4 zc = *reinterpret_cast<const f32x4 *>(z + 16 * ct + 4 * g);
+                const bf16x4 q4 = row4<D>(Qt, i_me, 16 * ct + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float oe = o[e] * inv_me - zc[e] * dl_me;
+                    aq[ct][e] += f * oe;
+                    part += (float)q4[e] * oe;
+                }
+            }
+            rowterm += (right ? -f : f) * part;
+        });
+        rowterm += __shfl_xor(rowterm, 16, 64);
+        rowterm += __shfl_xor(rowterm, 32, 64);
+        if (i_me >= n) return;
+        if constexpr (KIND != kMaskD) {
+            float xq[NCT][4];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(p.q + rowg * D + 16 * ct + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xq[ct][e] = (float)q4[e];
+            }
+            phi_backward<D, KIND>(xq, aq);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) store4(p.dq, gb, rowg * D + 16 * ct + 4 * g, aq[ct]);
+        if constexpr (KIND != kMaskLit)
+            if (g == 0) p.da_row[rowg] = rowterm;
+    } else {
+        // ---- key side: dV^T and dphi(K)^T (channel 16 ct + 4 g + e, key i_me) against the chunk's queries
+        bf16x8 kf[NS], vf[NS];
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            kf[st] = rows_frag<D>(Kt, tw >> 1, tw & 1, st, r, g);
+            vf[st] = rows_frag<D>(Vt, tw >> 1, tw & 1, st, r, g);
+        }
+        f32x4 ak[NCT], av[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) ak[ct] = av[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float colterm = 0.f;
+#pragma unroll 1
+        for (int h = 0; h < CT / kKB; ++h) {
+            if (causal && h * kKB + kKB - 1 < 16 * tw) continue;   // every query before every key of the tile
+            f32x4 sacc[2], dpacc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    sacc[t] = mfma_bf16(rows_frag<D>(Qt, h, t, st, r, g), kf[st], sacc[t]);
+                    dpacc[t] = mfma_bf16(rows_frag<D>(Gt, h, t, st, r, g), vf[st], dpacc[t]);
+                }
+            }
+            // element (t, e): query i = 32 h + 16 t + 4 g + e, key i_me
+            bf16x8 pf, dsf;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int ib = h * kKB + 16 * t + 4 * g;
+                const f32x4 iv = *reinterpret_cast<const f32x4 *>(inv + ib);
+                const f32x4 dv4 = *reinterpret_cast<const f32x4 *>(dl + ib);
+                const f32x4 ci = *reinterpret_cast<const f32x4 *>(cum + ib);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = ib + e;
+                    float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(ci[e] - cum_me)) : 1.f;
+                    if (causal && i_me > i) m = 0.f;
+                    const float pm = sacc[t][e] * m;
+                    const float dp = dpacc[t][e] * iv[e] - dv4[e];
+                    const float wv = dp * pm;
+                    colterm += i < i_me ? wv : (i > i_me ? -wv : 0.f);
+                    pf[4 * t + e] = f2bf(pm * iv[e]);
+                    dsf[4 * t + e] = f2bf(dp * m);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                av[ct] = mfma_bf16(tr_frag<D>(Gt, h, ct, r, g), pf, av[ct]);
+                ak[ct] = mfma_bf16(tr_frag<D>(Qt, h, ct, r, g), dsf, ak[ct]);
             }
         }
-        phi_backward<D, KIND>(xq, aq);
-        phi_backward<D, KIND>(xk, ak);
-    }
+        // phi(k) of the key row at channels 32 hh + 16 t + 4 g + e: the transposed-slot B operand of dv
+        // and, with ct = 2 hh + t, the output layout's channels 16 ct + 4 g + e
+        bf16x8 kT[NS];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const size_t off = rowg * D + 16 * ct + 4 * g;
-        store4(p.dq, gb, off, aq[ct]);
-        store4(p.dk, gb, off, ak[ct]);
-        store4(p.dv, gb, off, av[ct]);
-    }
-    if constexpr (KIND != kMaskLit) {
-        if (g == 0) {
-            p.da_row[rowg] = rowterm;
-            p.da_col[rowg] = colterm;
+        for (int hh = 0; hh < NS; ++hh) {
+            const bf16x4 k0 = row4<D>(Kt, i_me, 32 * hh + 4 * g), k1 = row4<D>(Kt, i_me, 32 * hh + 16 + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kT[hh][e] = k0[e];
+                kT[hh][4 + e] = k1[e];
+            }
         }
+        // the queries' states: dphi(k) += f (G v + G_d), G rows as A and v of the key row as B; dv += f G^T
+        // phi(k), G read transposed as A; the column half of dA takes phi(k) . (G v + G_d)
+        rounds([&](const __bf16 *S, const float *z, int st) {
+            if (!(st & 1)) return;   // a keys' state: the query side's
+            const bool right = st >= 2;
+            const float f = KIND == kMaskLit ? 1.f : fast_exp2(right ? tot - cum_me : cum_me);
+            float part = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                f32x4 o = {0.f, 0.f, 0.f, 0.f}, ov = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st2 = 0; st2 < NS; ++st2) {
+                    o = mfma_bf16(rows_frag<D>(S, ct >> 1, ct & 1, st2, r, g), vf[st2], o);
+                    ov = mfma_bf16(tr_frag<D>(S, st2, ct, r, g), kT[st2], ov);
+                }
+                const f32x4 zc = *reinterpret_cast<const f32x4 *>(z + 16 * ct + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float oe = o[e] + zc[e];
+                    ak[ct][e] += f * oe;
+                    av[ct][e] += f * ov[e];
+                    part += (float)kT[ct >> 1][4 * (ct & 1) + e] * oe;
+                }
+            }
+            colterm += (right ? -f : f) * part;
+        });
+        colterm += __shfl_xor(colterm, 16, 64);
+        colterm += __shfl_xor(colterm, 32, 64);
+        if (i_me >= n) return;
+        if constexpr (KIND != kMaskD) {
+            float xk[NCT][4];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(p.k + rowg * D + 16 * ct + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xk[ct][e] = (float)k4[e];
+            }
+            phi_backward<D, KIND>(xk, ak);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            store4(p.dk, gb, rowg * D + 16 * ct + 4 * g, ak[ct]);
+            store4(p.dv, gb, rowg * D + 16 * ct + 4 * g, av[ct]);
+        }
+        if constexpr (KIND != kMaskLit)
+            if (g == 0) p.da_col[rowg] = colterm;
     }
 }
 
@@ -729,7 +751,7 @@ hipError_t launch_mb_t(const BwdArgs &a, hipStream_t stream) {
     }
     constexpr size_t lm = MainLds<D, CT>::BYTES;
     allow_lds(&mb_main_kernel<D, KIND, CT>, lm);
-    hipLaunchKernelGGL((mb_main_kernel<D, KIND, CT>), dim3(a.B * a.H * p.nch), dim3(CT * 4), lm, stream, p);
+    hipLaunchKernelGGL((mb_main_kernel<D, KIND, CT>), dim3(a.B * a.H * p.nch), dim3(CT * 8), lm, stream, p);
     if (KIND != kMaskLit) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
