@@ -46,7 +46,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
 VALU_FP32_PEAK_TFLOPS = 157.3   # fp32 vector
 CSRC = os.path.join(ROOT, "bidirectional_linear_attention_lion_amd", "csrc")
 KERNEL_FILES = {"full": "lion_full.hip", "chunk": "lion_chunk.hip", "birnn": "lion_birnn.hip",
-                "full_bwd": "lion_full_bwd.hip", "chunk_bwd": "lion_chunk_bwd_mfma.hip", "selectivity": "lion_selectivity.hip",
+                "full_bwd": ("lion_full_bwd.hip", "lion_bwd_tiles.h"),
+                "chunk_bwd": ("lion_chunk_bwd_mfma.hip", "lion_bwd_tiles.h"), "selectivity": "lion_selectivity.hip",
                 "full2": "lion_full.hip", "chunk2": "lion_chunk2.hip"}
 SEL_WIDTH = 1024   # layer-input width of the selectivity prologue (the BERT-Large-shaped recipe)
 FORWARD_FORMS = ("full", "chunk", "birnn", "full2", "chunk2")
@@ -168,8 +169,10 @@ def host_seconds_per_call(call, forms, start):
 
 
 def kernel_hash(form: str) -> str:
+    """Hash of the sources a form's kernels are built from (its own files, then the shared headers)."""
+    own = KERNEL_FILES[form]
     h = hashlib.sha256()
-    for f in (KERNEL_FILES[form], "lion_device.h", "lion_mask.h", "lion_stage.h"):
+    for f in ((own,) if isinstance(own, str) else own) + ("lion_device.h", "lion_mask.h", "lion_stage.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
