@@ -67,3 +67,13 @@ def test_chunk_bwd_many_pairs(kind):
     # 256 (batch, head) pairs, 1024 walks and 1280 chunk workgroups in flight at once
     run_case(16, 16, 150, 64, kind, seed=4500, C=32)
     run_case(16, 16, 100, 64, kind, causal=True, positive=False, seed=4501, C=32)
+    # the bf16 kernels: 3 and 2 chunks per pair, ragged last chunks
+    run_case(16, 16, 150, 64, kind, positive=False, seed=4502, C=64)
+    run_case(16, 16, 200, 64, kind, causal=True, seed=4503, C=128)
+
+
+def test_chunk_bwd_bf16_small_heads_causal():
+    # d = 32 on the bf16 kernels, causal, chunks of 64 and 128
+    for kind in (lin.LIT, lin.D, lin.S):
+        run_case(1, 2, 300, 32, kind, causal=True, positive=False, seed=4700 + kind, C=128)
+        run_case(1, 2, 300, 32, kind, causal=True, seed=4710 + kind, C=64)
