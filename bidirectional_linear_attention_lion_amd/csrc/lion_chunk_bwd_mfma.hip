@@ -16,11 +16,12 @@
 //         S^T <- e^{tot} S^T + Y^T X' with Y = v or dy (the last column, 1 or -dy.y, enters as a 17th
 //         row tile holding it as a bf16 hi/lo pair).  The state entering each chunk is written as bf16
 //         d x d rows plus its last column in fp32.
-//   main: a workgroup of C / 16 waves per chunk; wave w owns query tile w and key tile w.  The pair part
-//         is the full form's backward restricted to the chunk: S^T and dP^T against the chunk's keys,
-//         then dphi(Q)^T += phi(K)^T dS^T; S and dP against its queries, then dV^T += dY^T (P / den) and
-//         dphi(K)^T += phi(Q)^T dS.  The entering states, staged into the space of the value and dy
-//         tiles, then add (f the weight from the chunk's near end to the token)
+//   main: a workgroup of 2 C / 16 waves per chunk: C / 16 query-side waves (one 16-row query tile each)
+//         and C / 16 key-side waves.  The pair part is the full form's backward restricted to the chunk:
+//         S^T and dP^T against the chunk's keys, then dphi(Q)^T += phi(K)^T dS^T on the query side; S and
+//         dP against its queries, then dV^T += dY^T (P / den) and dphi(K)^T += phi(Q)^T dS on the key
+//         side.  The entering states, staged into the space of the value and dy tiles, then add (f the
+//         weight from the chunk's near end to the token)
 //           dphi(q_i) += f_i (F dy_i / den_i - F_d delta_i),   dphi(k_j) += f_j (G v_j + G_d),
 //           dv_j += f_j G^T phi(k_j)
 //         and the dA halves phi(q_i).(that) and phi(k_j).(that), plus from the left, minus from the right.
