@@ -46,8 +46,6 @@ def _dev(bits):
 
 def run_case(B, H, L, d, kind, causal=False, positive=True, seed=0, eps=1e-6, tag="", C=None):
     """One case through the C ABI against the oracle; C given: the chunkwise backward with chunks of C."""
-    import torch
-    import bidirectional_linear_attention_lion_amd as lion
     rng = np.random.default_rng(seed)
     shape = (B, H, L, d)
     qb, q = _bf16(rng, shape, positive)
@@ -55,42 +53,60 @@ def run_case(B, H, L, d, kind, causal=False, positive=True, seed=0, eps=1e-6, ta
     vb, v = _bf16(rng, shape)
     gb, dy = _bf16(rng, shape)
     ll32 = lin.random_inputs(B, H, L, d, kind, dtype="bf16", seed=seed + 1).log_lambda
+    form = "bwd" if C is None else f"chunk_bwd C{C}"
+    label = (f"B{B} H{H} L{L} d{d} kind={lin.KIND_NAME[kind]}{' causal' if causal else ''} "
+             f"{'positive' if positive else 'signed'} {tag}")
+    return run_inputs((qb, kb, vb, gb), (q, k, v, dy), ll32, kind, causal, eps, (C,), label)[form]
+
+
+def run_inputs(bits, vals, ll32, kind, causal, eps, Cs, label):
+    """The forward and the backward passes through the C ABI on given bf16 inputs (bit patterns and their
+    exact values: q, k, v, dy), each held to the condition-aware gate against one oracle evaluation.
+    Cs lists the passes: None the full form's backward, an integer the chunkwise one with chunks of it.
+    Returns {form: literal errors}."""
+    import torch
+    import bidirectional_linear_attention_lion_amd as lion
+    qb, kb, vb, gb = bits
+    q, k, v, dy = vals
+    B, H, L, d = q.shape
     ll = None if ll32 is None else torch.from_numpy(ll32).cuda()
     mk = kind | (lion.CAUSAL if causal else 0)
     qd, kd, vd, gd = _dev(qb), _dev(kb), _dev(vb), _dev(gb)
     den = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
     y = lion.lion_attn_full(qd, kd, vd, ll, mk, eps, den_out=den)
-    if C is None:
-        dq, dk, dv, dll = lion.lion_attn_full_bwd(qd, kd, vd, ll, mk, y, den, gd, grad_dtype=torch.float32)
-    else:
-        dq, dk, dv, dll = lion.lion_attn_chunk_bwd(qd, kd, vd, ll, mk, C, y, den, gd, grad_dtype=torch.float32)
-    torch.cuda.synchronize()
-    got = {"dq": dq, "dk": dk, "dv": dv, "dll": dll}
+    got_all = {}
+    for C in Cs:
+        if C is None:
+            out = lion.lion_attn_full_bwd(qd, kd, vd, ll, mk, y, den, gd, grad_dtype=torch.float32)
+        else:
+            out = lion.lion_attn_chunk_bwd(qd, kd, vd, ll, mk, C, y, den, gd, grad_dtype=torch.float32)
+        torch.cuda.synchronize()
+        got_all["bwd" if C is None else f"chunk_bwd C{C}"] = dict(zip(("dq", "dk", "dv", "dll"), out))
     res = oracle.full_bwd(q, k, v, None if ll32 is None else ll32.astype(np.float64),
                           kind | (oracle.CAUSAL if causal else 0), eps, dy, want_abs=True)
     names = ("dq", "dk", "dv", "dll")
     ref, absc = dict(zip(names, res[:4])), dict(zip(names, res[4:]))
-    errs, gates = {}, {}
-    for name in names:
-        if ref[name] is None:
-            continue
-        g = got[name].cpu().numpy().astype(np.float64).reshape(ref[name].shape)
-        assert np.all(np.isfinite(g)), f"{name}: non-finite gradients"
-        rms = float(np.sqrt(np.mean(ref[name] ** 2)))
-        err = np.abs(g - ref[name])
-        errs[name] = float(np.max(err)) / max(rms, 1e-300)
-        bound = BWD_TOL * rms + BWD_C * BWD_U * absc[name]
-        # a zero bound (an exactly zero gradient, e.g. dlog(lambda) at L = 1) admits only a zero error
-        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
-        gates[name] = float(np.max(ratio))
-    form = "bwd" if C is None else f"chunk_bwd C{C}"
-    report(f"[{form}] B{B} H{H} L{L} d{d} kind={lin.KIND_NAME[kind]}{' causal' if causal else ''} "
-           f"{'positive' if positive else 'signed'} {tag}: literal "
-           + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + " | gate "
-           + " ".join(f"{n}={e:.3f}" for n, e in gates.items()))
-    for name, gv in gates.items():
-        assert gv <= 1.0, f"{name}: condition-aware gate {gv:.3f} > 1 (L={L}, kind={kind}, causal={causal})"
-    return errs
+    out_errs = {}
+    for form, got in got_all.items():
+        errs, gates = {}, {}
+        for name in names:
+            if ref[name] is None:
+                continue
+            g = got[name].cpu().numpy().astype(np.float64).reshape(ref[name].shape)
+            assert np.all(np.isfinite(g)), f"{form} {name}: non-finite gradients"
+            rms = float(np.sqrt(np.mean(ref[name] ** 2)))
+            err = np.abs(g - ref[name])
+            errs[name] = float(np.max(err)) / max(rms, 1e-300)
+            bound = BWD_TOL * rms + BWD_C * BWD_U * absc[name]
+            # a zero bound (an exactly zero gradient, e.g. dlog(lambda) at L = 1) admits only a zero error
+            ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+            gates[name] = float(np.max(ratio))
+        report(f"[{form}] {label}: literal " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + " | gate "
+               + " ".join(f"{n}={e:.3f}" for n, e in gates.items()))
+        for name, gv in gates.items():
+            assert gv <= 1.0, f"{form} {name}: condition-aware gate {gv:.3f} > 1 ({label})"
+        out_errs[form] = errs
+    return out_errs
 
 
 CASES_L = [1, 17, 64, 100, 197, 300, 600]
