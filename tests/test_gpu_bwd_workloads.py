@@ -2,9 +2,9 @@
 
 For each bf16 workload, the inputs of its recipe (q, k, v ~ N(0, 1) rounded to bf16 and its decay
 recipe; fewer batch entries and heads, full length and head dimension) and a seeded incoming gradient
-dy go through the full form's backward and the chunkwise one (chunks of 64, and 128 on the long
-sequence), each held to the condition-aware gate of ``tests.test_gpu_bwd`` against one fp64 oracle
-evaluation.  The report lines are those of the parity report's backward rows at workload shapes.
+dy go through the full form's backward and the chunkwise one (chunks of 64; on the longer sequences
+also 128, and 32 -- the fp32 path -- on the longest), each held to the condition-aware gate of
+``tests.test_gpu_bwd`` against one fp64 oracle evaluation.  The report lines are those of the parity report's backward rows at workload shapes.
 """
 from __future__ import annotations
 
@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 # (workload, batch entries, heads, chunkwise chunk sizes)
 CASES = [("vit_tiny_lit", 2, 3, (64,)), ("vit_base_d", 2, 2, (64,)), ("bert_large_s", 1, 2, (64, 128)),
-         ("hires_d", 1, 2, (64, 128))]
+         ("hires_d", 1, 2, (32, 64, 128))]
 
 
 @pytest.mark.parametrize("name,B,H,Cs", CASES, ids=[c[0] for c in CASES])
