@@ -21,7 +21,10 @@
 //         column index, then dV^T += dY^T (P / den) and dphi(K)^T += phi(Q)^T dS, and the column half
 //         of dA.
 //   dlog(lambda): LION-S a reverse prefix sum of dA per (batch, head); LION-D sum_t t dA_t over every
-//         batch entry of a head.
+//         batch entry of a head (per-(batch, head) sums first, then a head's batch entries).
+// In both gradient kernels a sub-block that lies wholly on one side of a wave's rows forms the mask as
+// a row factor times a column factor (both at most 1) instead of one exponential per score, as the
+// forward does.
 // Causal variant: M_ij = 0 for j > i (a constant), so those pairs are skipped or zeroed.
 #include <type_traits>
 
@@ -53,8 +56,6 @@ struct BwdParams {
     int causal;
 };
 
-// ================================ dq ==================================================================
-// TT query tiles per wave: the key/value fragments a sub-block reads from LDS serve all of them.
 // Lane i (< 8) of the lane's 16-lane row (DPP row_newbcast; a multiply that uses it takes it as a DPP
 // operand).
 __device__ __forceinline__ float bwd_bcast16(float x, int i) {
@@ -67,6 +68,8 @@ __device__ __forceinline__ float bwd_bcast16(float x, int i) {
     }
 }
 
+// ================================ dq ==================================================================
+// TT query tiles per wave: the key/value fragments a sub-block reads from LDS serve all of them.
 template <int D, int KIND, int TT>
 __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdParams p) {
     using T = __bf16;
