@@ -569,15 +569,22 @@ __global__ void __launch_bounds__(kDllThreads) bwd_dll_d_rows_kernel(BwdParams p
     }
 }
 
-__global__ void __launch_bounds__(64) bwd_dll_d_kernel(BwdParams p, int B) {
-    const int h = blockIdx.x * 64 + threadIdx.x;
-    if (h >= p.H) return;
+__global__ void __launch_bounds__(kDllThreads) bwd_dll_d_kernel(BwdParams p, int B) {
+    // one workgroup per head; its threads take the batch entries' partials in parallel
+    __shared__ double sh[kDllThreads];
+    const int tid = threadIdx.x, h = blockIdx.x;
     double s = 0.0;
-    for (int b = 0; b < B; ++b) {
+    for (int b = tid; b < B; b += kDllThreads) {
         const size_t base = ((size_t)b * p.H + h) * p.L;
         s += (double)p.da_row[base] + (double)p.da_col[base];
     }
-    p.dll[h] = (float)s;
+    sh[tid] = s;
+    __syncthreads();
+    for (int o = kDllThreads / 2; o > 0; o >>= 1) {
+        if (tid < o) sh[tid] += sh[tid + o];
+        __syncthreads();
+    }
+    if (tid == 0) p.dll[h] = (float)sh[0];
 }
 
 // ================================ host side ===========================================================
@@ -702,7 +709,7 @@ hipError_t launch_dll(int kind, float *da_row, float *da_col, float *dll, int B,
         hipLaunchKernelGGL(bwd_dll_s_kernel, dim3(B * H), dim3(kDllThreads), 0, stream, p);
     else {
         hipLaunchKernelGGL(bwd_dll_d_rows_kernel, dim3(B * H), dim3(kDllThreads), 0, stream, p);
-        hipLaunchKernelGGL(bwd_dll_d_kernel, dim3((H + 63) / 64), dim3(64), 0, stream, p, B);
+        hipLaunchKernelGGL(bwd_dll_d_kernel, dim3(H), dim3(kDllThreads), 0, stream, p, B);
     }
     return hipGetLastError();
 }
