@@ -15,6 +15,20 @@ namespace lion {
 
 constexpr int kKB = 32;   // rows per sub-block (two 16-row halves)
 
+// Lane i (< 8) of the lane's 16-lane row (DPP row_newbcast; a multiply that uses it takes it as a DPP
+// operand).  The separable mask's column factors travel this way: lane r < 8 of a row computes the
+// factor of sub-block position 16 (r / 4) + 4 g + r % 4, the position slot 4 t + e of every lane of the
+// row needs.
+__device__ __forceinline__ float bwd_bcast16(float x, int i) {
+    switch (i) {
+#define LION_RB(I) \
+    case I: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + I, 0xF, 0xF, false));
+    LION_RB(0) LION_RB(1) LION_RB(2) LION_RB(3) LION_RB(4) LION_RB(5) LION_RB(6) LION_RB(7)
+#undef LION_RB
+    default: return x;
+    }
+}
+
 // phi over the rows of a staged tile, in place; rows at or past `row_end` become zero rows.
 template <int D, int KIND>
 __device__ __forceinline__ void phi_stage(__bf16 *tile, int rows, int row_end, int tid, int nt) {

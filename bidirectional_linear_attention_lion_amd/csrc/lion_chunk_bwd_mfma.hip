@@ -507,9 +507,23 @@ __global__ void __launch_bounds__(CT * 8) mb_main_kernel(MbParams p) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) aq[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         float rowterm = 0.f;
+        // Separable mask for key sub-blocks wholly before or after the tile's rows (first row r0, last
+        // rl; the prefix sums decrease along the chunk): M_ij = exp2(c_i - c_r0) exp2(c_r0 - c_j) for keys
+        // before, exp2(c_rl - c_i) exp2(c_j - c_rl) for keys after, every factor at most 1; the key's factor
+        // comes by DPP row broadcast.  The sub-block the tile sits in keeps one exponential per score.
+        const float e_first = uniform(cum[16 * tw]), e_last = uniform(cum[16 * tw + 15]);
+        const float rowf_b = KIND != kMaskLit ? fast_exp2(cum_me - e_first) : 1.f;
+        const float rowf_a = KIND != kMaskLit ? fast_exp2(e_last - cum_me) : 1.f;
 #pragma unroll 1
         for (int h = 0; h < CT / kKB; ++h) {
             if (causal && h * kKB > 16 * tw + 15) break;   // every key after every query of the tile
+            // 0: overlap, 1: every key before the tile's rows, 2: every key after them (wave-uniform)
+            const int region = h * kKB + kKB - 1 < 16 * tw ? 1 : h * kKB > 16 * tw + 15 ? 2 : 0;
+            float cl = 1.f;
+            if (KIND != kMaskLit && region != 0) {
+                const float ej = cum[h * kKB + 16 * ((r >> 2) & 1) + 4 * g + (r & 3)];
+                cl = fast_exp2(region == 1 ? e_first - ej : ej - e_last);
+            }
             f32x4 sacc[2], dpacc[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -522,19 +536,34 @@ __global__ void __launch_bounds__(CT * 8) mb_main_kernel(MbParams p) {
             }
             // element (t, e): key j = 32 h + 16 t + 4 g + e, query i_me
             bf16x8 dsf;
+            if (region == 0) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const f32x4 cj = *reinterpret_cast<const f32x4 *>(cum + h * kKB + 16 * t + 4 * g);
+                for (int t = 0; t < 2; ++t) {
+                    const f32x4 cj = *reinterpret_cast<const f32x4 *>(cum + h * kKB + 16 * t + 4 * g);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = h * kKB + 16 * t + 4 * g + e;
-                    float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(cum_me - cj[e])) : 1.f;
-                    if (causal && j > i_me) m = 0.f;
-                    const float dp = dpacc[t][e] * inv_me - dl_me;
-                    const float wv = dp * (sacc[t][e] * m);
-                    rowterm += j < i_me ? wv : (j > i_me ? -wv : 0.f);
-                    dsf[4 * t + e] = f2bf(dp * m);
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = h * kKB + 16 * t + 4 * g + e;
+                        float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(cum_me - cj[e])) : 1.f;
+                        if (causal && j > i_me) m = 0.f;
+                        const float dp = dpacc[t][e] * inv_me - dl_me;
+                        const float wv = dp * (sacc[t][e] * m);
+                        rowterm += j < i_me ? wv : (j > i_me ? -wv : 0.f);
+                        dsf[4 * t + e] = f2bf(dp * m);
+                    }
                 }
+            } else {
+                const float rowf = region == 1 ? rowf_b : rowf_a;
+                float wsum = 0.f;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float m = KIND != kMaskLit ? bwd_bcast16(cl, 4 * t + e) * rowf : 1.f;
+                        const float dp = dpacc[t][e] * inv_me - dl_me;
+                        wsum += dp * (sacc[t][e] * m);
+                        dsf[4 * t + e] = f2bf(dp * m);
+                    }
+                rowterm += region == 1 ? wsum : -wsum;
             }
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) aq[ct] = mfma_bf16(tr_frag<D>(Kt, h, ct, r, g), dsf, aq[ct]);
@@ -591,9 +620,22 @@ __global__ void __launch_bounds__(CT * 8) mb_main_kernel(MbParams p) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) ak[ct] = av[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         float colterm = 0.f;
+        // Separable mask for query sub-blocks wholly before or after the tile's keys (first key k0, last
+        // kl): M_ij = exp2(c_j - c_k0) exp2(c_k0 - c_i) for queries before, exp2(c_kl - c_j) exp2(c_i - c_kl)
+        // for queries after; the query's factor comes by DPP row broadcast.
+        const float e_first = uniform(cum[16 * tw]), e_last = uniform(cum[16 * tw + 15]);
+        const float keyf_b = KIND != kMaskLit ? fast_exp2(cum_me - e_first) : 1.f;
+        const float keyf_a = KIND != kMaskLit ? fast_exp2(e_last - cum_me) : 1.f;
 #pragma unroll 1
         for (int h = 0; h < CT / kKB; ++h) {
             if (causal && h * kKB + kKB - 1 < 16 * tw) continue;   // every query before every key of the tile
+            // 0: overlap, 1: every query before the tile's keys, 2: every query after them (wave-uniform)
+            const int region = h * kKB + kKB - 1 < 16 * tw ? 1 : h * kKB > 16 * tw + 15 ? 2 : 0;
+            float cl = 1.f;
+            if (KIND != kMaskLit && region != 0) {
+                const float ei = cum[h * kKB + 16 * ((r >> 2) & 1) + 4 * g + (r & 3)];
+                cl = fast_exp2(region == 1 ? e_first - ei : ei - e_last);
+            }
             f32x4 sacc[2], dpacc[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -606,25 +648,40 @@ __global__ void __launch_bounds__(CT * 8) mb_main_kernel(MbParams p) {
             }
             // element (t, e): query i = 32 h + 16 t + 4 g + e, key i_me
             bf16x8 pf, dsf;
+            const float keyf = region == 1 ? keyf_b : keyf_a;
+            float wsum = 0.f;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int ib = h * kKB + 16 * t + 4 * g;
                 const f32x4 iv = *reinterpret_cast<const f32x4 *>(inv + ib);
                 const f32x4 dv4 = *reinterpret_cast<const f32x4 *>(dl + ib);
-                const f32x4 ci = *reinterpret_cast<const f32x4 *>(cum + ib);
+                if (region == 0) {
+                    const f32x4 ci = *reinterpret_cast<const f32x4 *>(cum + ib);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = ib + e;
-                    float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(ci[e] - cum_me)) : 1.f;
-                    if (causal && i_me > i) m = 0.f;
-                    const float pm = sacc[t][e] * m;
-                    const float dp = dpacc[t][e] * iv[e] - dv4[e];
-                    const float wv = dp * pm;
-                    colterm += i < i_me ? wv : (i > i_me ? -wv : 0.f);
-                    pf[4 * t + e] = f2bf(pm * iv[e]);
-                    dsf[4 * t + e] = f2bf(dp * m);
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = ib + e;
+                        float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(ci[e] - cum_me)) : 1.f;
+                        if (causal && i_me > i) m = 0.f;
+                        const float pm = sacc[t][e] * m;
+                        const float dp = dpacc[t][e] * iv[e] - dv4[e];
+                        const float wv = dp * pm;
+                        colterm += i < i_me ? wv : (i > i_me ? -wv : 0.f);
+                        pf[4 * t + e] = f2bf(pm * iv[e]);
+                        dsf[4 * t + e] = f2bf(dp * m);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float m = KIND != kMaskLit ? bwd_bcast16(cl, 4 * t + e) * keyf : 1.f;
+                        const float pm = sacc[t][e] * m;
+                        const float dp = dpacc[t][e] * iv[e] - dv4[e];
+                        wsum += dp * pm;
+                        pf[4 * t + e] = f2bf(pm * iv[e]);
+                        dsf[4 * t + e] = f2bf(dp * m);
+                    }
                 }
             }
+            if (region != 0) colterm += region == 1 ? wsum : -wsum;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 av[ct] = mfma_bf16(tr_frag<D>(Gt, h, ct, r, g), pf, av[ct]);

@@ -56,18 +56,6 @@ struct BwdParams {
     int causal;
 };
 
-// Lane i (< 8) of the lane's 16-lane row (DPP row_newbcast; a multiply that uses it takes it as a DPP
-// operand).
-__device__ __forceinline__ float bwd_bcast16(float x, int i) {
-    switch (i) {
-#define LION_RB(I) \
-    case I: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + I, 0xF, 0xF, false));
-    LION_RB(0) LION_RB(1) LION_RB(2) LION_RB(3) LION_RB(4) LION_RB(5) LION_RB(6) LION_RB(7)
-#undef LION_RB
-    default: return x;
-    }
-}
-
 // ================================ dq ==================================================================
 // TT query tiles per wave: the key/value fragments a sub-block reads from LDS serve all of them.
 template <int D, int KIND, int TT>
