@@ -46,7 +46,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
 VALU_FP32_PEAK_TFLOPS = 157.3   # fp32 vector
 CSRC = os.path.join(ROOT, "bidirectional_linear_attention_lion_amd", "csrc")
 KERNEL_FILES = {"full": "lion_full.hip", "chunk": "lion_chunk.hip", "birnn": "lion_birnn.hip",
-                "full_bwd": ("lion_full_bwd.hip", "lion_bwd_tiles.h"),
+                "full_bwd": ("lion_full_bwd.hip", "lion_chunk_bwd_mfma.hip", "lion_bwd_tiles.h"),
                 "chunk_bwd": ("lion_chunk_bwd_mfma.hip", "lion_bwd_tiles.h"), "selectivity": "lion_selectivity.hip",
                 "full2": "lion_full.hip", "chunk2": "lion_chunk2.hip"}
 SEL_WIDTH = 1024   # layer-input width of the selectivity prologue (the BERT-Large-shaped recipe)

@@ -40,7 +40,7 @@ constexpr int kWalkThreads = 256;
 struct MbParams {
     const __bf16 *q, *k, *v, *y, *dy;
     const float *den, *ll;
-    int H, L, nch, causal;
+    int H, L, nch, causal, nbh;   // nbh: B H
     void *dq, *dk, *dv;
     int g_bf16;
     __bf16 *st;                // [B H][nch][4][D][D]: key-left, query-left, key-right, query-right
@@ -361,34 +361,49 @@ __device__ __forceinline__ bf16x4 row4(const __bf16 *tile, int row, int c) {
     return *reinterpret_cast<const bf16x4 *>(tile + RowTile<D, __bf16>::off(row, c));
 }
 
-template <int D, int CT>
+// Tiles per wave (two at C = 256, which would otherwise need 32 waves) and threads per workgroup.
+constexpr int main_tpw(int ct) { return ct > 128 ? 2 : 1; }
+constexpr int main_threads(int ct) { return ct * 8 / main_tpw(ct); }
+
+template <int D, int CT, bool SPLIT = false>
 struct MainLds {
     static constexpr int TILE = CT * D;                        // bf16 elements per token tile
-    static constexpr size_t TOK = (size_t)4 * TILE * 2;        // phi(q), phi(k), v, dy
-    static constexpr size_t F32 = (size_t)(CT + 4) + 4 * CT + 4 * D;   // cum, 1/den, delta, dA halves, last columns
+    static constexpr size_t TOK = (size_t)(SPLIT ? 2 : 4) * TILE * 2;   // phi(q), phi(k), v, dy (one side's two)
+    static constexpr size_t F32 = (size_t)(CT + 4) + 2 * CT + 4 * D;   // cum, 1/den, delta, last columns
     static constexpr size_t BYTES = TOK + F32 * 4;
     static constexpr int NSF = 2 * CT / D < 4 ? 2 * CT / D : 4;  // states staged at once (value + dy tiles' space)
 };
 
-// The workgroup has 2 C / 16 waves: waves [0, C / 16) take the query side of query tile w (dphi(q) and
-// the row half of dA), waves [C / 16, 2 C / 16) the key side of key tile w - C / 16 (dphi(k), dv and the
-// column half).  Each side keeps only its own accumulators, and the two run as separate code paths
-// (with the same barriers), so a wave's registers hold one side's work.
-template <int D, int KIND, int CT>
-__global__ void __launch_bounds__(CT * 8) mb_main_kernel(MbParams p) {
+// The workgroup has 2 C / 16 waves (C / 16 at C = 256, each wave taking two tiles, one from each end, in
+// turn): the first half take the query side of their query tiles (dphi(q) and the row half of dA), the
+// second half the key side of their key tiles (dphi(k), dv and the column half).  Each side keeps only
+// its own accumulators, and the two run as separate code paths (with the same barriers), so a wave's
+// registers hold one side's work.
+// SPLIT (a lone chunk, no states): the two sides go to two workgroups of C / 16 waves, blocks b and b + 8
+// of each 16 (one XCD, so the second read of the rows hits its L2); each stages only the two tiles its
+// side reads across (keys and values for the query side, queries and dy for the key side) and loads the
+// fragments of its own rows from memory, so two such workgroups share a compute unit.
+template <int D, int KIND, int CT, bool SPLIT = false>
+__global__ void __launch_bounds__(SPLIT ? main_threads(CT) / 2 : main_threads(CT))
+    __attribute__((amdgpu_waves_per_eu(SPLIT ? 4 : 1))) mb_main_kernel(MbParams p) {
     using RT = RowTile<D, __bf16>;
-    using ML = MainLds<D, CT>;
-    constexpr int NS = D / 32, NCT = D / 16, SPR = D / 8, NW = CT / 16, NWG = 2 * NW, NT = 64 * NWG;
+    using ML = MainLds<D, CT, SPLIT>;
+    constexpr int NS = D / 32, NCT = D / 16, SPR = D / 8, NW = CT / 16, TPW = main_tpw(CT), NQW = NW / TPW;
+    constexpr int NWG = SPLIT ? NQW : 2 * NQW, NT = 64 * NWG;
     extern __shared__ __align__(16) unsigned char smem[];
+    // (split: the query side's phi(k), v tiles and the key side's phi(q), dy tiles share the space)
     __bf16 *Qt = reinterpret_cast<__bf16 *>(smem);
-    __bf16 *Kt = Qt + ML::TILE, *Vt = Kt + ML::TILE, *Gt = Vt + ML::TILE;
+    __bf16 *Kt = SPLIT ? Qt : Qt + ML::TILE, *Vt = Kt + ML::TILE, *Gt = SPLIT ? Vt : Vt + ML::TILE;
     float *cum = reinterpret_cast<float *>(Gt + ML::TILE);
-    float *inv = cum + CT + 4, *dl = inv + CT, *dar = dl + CT, *dac = dar + CT, *zst = dac + CT;
+    float *inv = cum + CT + 4, *dl = inv + CT, *zst = dl + CT;
 
-    const int bh = blockIdx.x / p.nch, c = blockIdx.x % p.nch;
+    const int bid = blockIdx.x;
+    const int bh = SPLIT ? (bid >> 4) * 8 + (bid & 7) : bid / p.nch, c = SPLIT ? 0 : bid % p.nch;
+    if (SPLIT && bh >= p.nbh) return;   // the grid is rounded up to whole groups of 16 (workgroup-uniform)
     const int n = min(CT, p.L - c * CT);
     const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 4, r = lane & 15;
-    const int tw = w % NW;           // this wave's 16-row tile
+    const int wq = w % NQW;          // this wave's tiles: wq and, with two per wave, NW - 1 - wq
+    const bool qside = SPLIT ? ((bid >> 3) & 1) == 0 : w < NQW;   // wave-uniform
     const size_t row0 = (size_t)bh * p.L + (size_t)c * CT;
     const bool causal = p.causal != 0;
 
@@ -413,9 +428,11 @@ __global__ void __launch_bounds__(CT * 8) mb_main_kernel(MbParams p) {
             const int sl = min(it * NT + tid, NSL - 1);
             const int row = sl / SPR, cs = (sl % SPR) * 8;
             const size_t gi = (row0 + min(row, n - 1)) * D + cs;
-            rq[it] = __builtin_bit_cast(bf16x8, ld16(p.q + gi));
-            rk[it] = __builtin_bit_cast(bf16x8, ld16(p.k + gi));
-            rv[it] = __builtin_bit_cast(bf16x8, ld16(p.v + gi));
+            if (!SPLIT || !qside) rq[it] = __builtin_bit_cast(bf16x8, ld16(p.q + gi));
+            if (!SPLIT || qside) {
+                rk[it] = __builtin_bit_cast(bf16x8, ld16(p.k + gi));
+                rv[it] = __builtin_bit_cast(bf16x8, ld16(p.v + gi));
+            }
             rg[it] = __builtin_bit_cast(bf16x8, ld16(p.dy + gi));
             ry[it] = __builtin_bit_cast(bf16x8, ld16(p.y + gi));
         }
@@ -427,8 +444,8 @@ __global__ void __launch_bounds__(CT * 8) mb_main_kernel(MbParams p) {
             float fq[8], fk[8], ssq = 0.f, ssk = 0.f, part = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                fq[e] = phi_pre<KIND>((float)rq[it][e]);
-                fk[e] = phi_pre<KIND>((float)rk[it][e]);
+                fq[e] = !SPLIT || !qside ? phi_pre<KIND>((float)rq[it][e]) : 0.f;
+                fk[e] = !SPLIT || qside ? phi_pre<KIND>((float)rk[it][e]) : 0.f;
                 ssq += fq[e] * fq[e];
                 ssk += fk[e] * fk[e];
                 part += (float)rg[it][e] * (float)ry[it][e];
@@ -447,10 +464,14 @@ __global__ void __launch_bounds__(CT * 8) mb_main_kernel(MbParams p) {
             }
             if (NSL % NT == 0 || sl < NSL) {
                 const int at = RT::off(row, cs);
-                *reinterpret_cast<bf16x8 *>(Qt + at) = oq;
-                *reinterpret_cast<bf16x8 *>(Kt + at) = ok8;
-                *reinterpret_cast<u32x4 *>(Vt + at) = keep_if(rv[it], ok);
-                *reinterpret_cast<u32x4 *>(Gt + at) = keep_if(rg[it], ok);
+                if (!SPLIT || !qside) {
+                    *reinterpret_cast<bf16x8 *>(Qt + at) = oq;
+                    *reinterpret_cast<u32x4 *>(Gt + at) = keep_if(rg[it], ok);
+                }
+                if (!SPLIT || qside) {
+                    *reinterpret_cast<bf16x8 *>(Kt + at) = ok8;
+                    *reinterpret_cast<u32x4 *>(Vt + at) = keep_if(rv[it], ok);
+                }
                 if (sl % SPR == 0) {
                     const float iv = ok ? 1.f / p.den[row0 + row] : 0.f;
                     inv[row] = iv;
@@ -460,19 +481,17 @@ __global__ void __launch_bounds__(CT * 8) mb_main_kernel(MbParams p) {
         }
     }
     if (w == 0) chunk_cum<KIND, CT>(cum, p.ll, KIND == kMaskS ? p.ll + row0 : nullptr, bh % p.H, n, lane);
-    for (int t = tid; t < 2 * CT; t += NT) dar[t] = 0.f;
     for (int t = tid; t < nst * D; t += NT) {
         const int st = st_at(t / D);
         zst[st * D + t % D] = p.stz[(((size_t)bh * p.nch + c) * 4 + st) * D + t % D];
     }
     __syncthreads();
     const float tot = cum[CT];
-    const int i_me = 16 * tw + r;   // this lane's row of the tile
-    const float cum_me = cum[i_me];
 
     // The entering states, staged NSF at a time into the value and dy tiles' space as bf16 d x d row
     // tiles; apply(S, z, st) runs for each (both sides pass through the same barriers).
     auto rounds = [&](auto &&apply) {
+        if (SPLIT || nst == 0) return;   // a lone chunk (workgroup-uniform)
         __syncthreads();   // every wave is done with the value and dy tiles
         __bf16 *Sb = Vt;
 #pragma unroll 1
@@ -491,261 +510,319 @@ __global__ void __launch_bounds__(CT * 8) mb_main_kernel(MbParams p) {
             __syncthreads();   // before the next states overwrite these
         }
     };
-    const size_t rowg = row0 + i_me;
     const bool gb = p.g_bf16 != 0;
 
-    if (w < NW) {
-        // ---- query side: dphi(Q)^T (channel 16 ct + 4 g + e, query i_me) against the chunk's keys
-        bf16x8 qf[NS], df[NS];
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-            qf[st] = rows_frag<D>(Qt, tw >> 1, tw & 1, st, r, g);
-            df[st] = rows_frag<D>(Gt, tw >> 1, tw & 1, st, r, g);
-        }
-        const float inv_me = inv[i_me], dl_me = dl[i_me];
-        f32x4 aq[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) aq[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float rowterm = 0.f;
-        // Separable mask for key sub-blocks wholly before or after the tile's rows (first row r0, last
-        // rl; the prefix sums decrease along the chunk): M_ij = exp2(c_i - c_r0) exp2(c_r0 - c_j) for keys
-        // before, exp2(c_rl - c_i) exp2(c_j - c_rl) for keys after, every factor at most 1; the key's factor
-        // comes by DPP row broadcast.  The sub-block the tile sits in keeps one exponential per score.
-        const float e_first = uniform(cum[16 * tw]), e_last = uniform(cum[16 * tw + 15]);
-        const float rowf_b = KIND != kMaskLit ? fast_exp2(cum_me - e_first) : 1.f;
-        const float rowf_a = KIND != kMaskLit ? fast_exp2(e_last - cum_me) : 1.f;
+    if (qside) {
 #pragma unroll 1
-        for (int h = 0; h < CT / kKB; ++h) {
-            if (causal && h * kKB > 16 * tw + 15) break;   // every key after every query of the tile
-            // 0: overlap, 1: every key before the tile's rows, 2: every key after them (wave-uniform)
-            const int region = h * kKB + kKB - 1 < 16 * tw ? 1 : h * kKB > 16 * tw + 15 ? 2 : 0;
-            float cl = 1.f;
-            if (KIND != kMaskLit && region != 0) {
-                const float ej = cum[h * kKB + 16 * ((r >> 2) & 1) + 4 * g + (r & 3)];
-                cl = fast_exp2(region == 1 ? e_first - ej : ej - e_last);
-            }
-            f32x4 sacc[2], dpacc[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < TPW; ++kt) {
+            const int tw = kt == 0 ? wq : NW - 1 - wq;   // tiles paired from both ends: the causal pair counts balance
+            const int i_me = 16 * tw + r;   // this lane's row of the tile
+            const float cum_me = cum[i_me];
+            const size_t rowg = row0 + i_me;
+            const bool live = 16 * tw < n;   // wave-uniform; a tile wholly past the chunk's end computes nothing
+            // ---- query side: dphi(Q)^T (channel 16 ct + 4 g + e, query i_me) against the chunk's keys
+            bf16x8 qf[NS], df[NS];
+            if constexpr (SPLIT) {
+                const size_t rc = row0 + min(i_me, n - 1);
+                row_frags<D, KIND, true>(p.q + rc * D, i_me < n, qf);
+                row_frags<D, KIND, false>(p.dy + rc * D, i_me < n, df);
+            } else {
 #pragma unroll
                 for (int st = 0; st < NS; ++st) {
-                    sacc[t] = mfma_bf16(rows_frag<D>(Kt, h, t, st, r, g), qf[st], sacc[t]);
-                    dpacc[t] = mfma_bf16(rows_frag<D>(Vt, h, t, st, r, g), df[st], dpacc[t]);
+                    qf[st] = rows_frag<D>(Qt, tw >> 1, tw & 1, st, r, g);
+                    df[st] = rows_frag<D>(Gt, tw >> 1, tw & 1, st, r, g);
                 }
             }
-            // element (t, e): key j = 32 h + 16 t + 4 g + e, query i_me
-            bf16x8 dsf;
-            if (region == 0) {
+            const float inv_me = inv[i_me], dl_me = dl[i_me];
+            f32x4 aq[NCT];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) aq[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            float rowterm = 0.f;
+            // Separable mask for key sub-blocks wholly before or after the tile's rows (first row r0, last
+            // rl; the prefix sums decrease along the chunk): M_ij = exp2(c_i - c_r0) exp2(c_r0 - c_j) for keys
+            // before, exp2(c_rl - c_i) exp2(c_j - c_rl) for keys after, every factor at most 1; the key's factor
+            // comes by DPP row broadcast.  The sub-block the tile sits in keeps one exponential per score.
+            const float e_first = uniform(cum[16 * tw]), e_last = uniform(cum[16 * tw + 15]);
+            const float rowf_b = KIND != kMaskLit ? fast_exp2(cum_me - e_first) : 1.f;
+            const float rowf_a = KIND != kMaskLit ? fast_exp2(e_last - cum_me) : 1.f;
+#pragma unroll 1
+            for (int h = 0; h < CT / kKB; ++h) {
+                    if (!live || h * kKB >= n) break;   // keys past the chunk's end are zero rows
+                if (causal && h * kKB > 16 * tw + 15) break;   // every key after every query of the tile
+                // 0: overlap, 1: every key before the tile's rows, 2: every key after them (wave-uniform)
+                const int region = h * kKB + kKB - 1 < 16 * tw ? 1 : h * kKB > 16 * tw + 15 ? 2 : 0;
+                float cl = 1.f;
+                if (KIND != kMaskLit && region != 0) {
+                    const float ej = cum[h * kKB + 16 * ((r >> 2) & 1) + 4 * g + (r & 3)];
+                    cl = fast_exp2(region == 1 ? e_first - ej : ej - e_last);
+                }
+                f32x4 sacc[2], dpacc[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const f32x4 cj = *reinterpret_cast<const f32x4 *>(cum + h * kKB + 16 * t + 4 * g);
+                    sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int j = h * kKB + 16 * t + 4 * g + e;
-                        float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(cum_me - cj[e])) : 1.f;
-                        if (causal && j > i_me) m = 0.f;
-                        const float dp = dpacc[t][e] * inv_me - dl_me;
-                        const float wv = dp * (sacc[t][e] * m);
-                        rowterm += j < i_me ? wv : (j > i_me ? -wv : 0.f);
-                        dsf[4 * t + e] = f2bf(dp * m);
+                    for (int st = 0; st < NS; ++st) {
+                        sacc[t] = mfma_bf16(rows_frag<D>(Kt, h, t, st, r, g), qf[st], sacc[t]);
+                        dpacc[t] = mfma_bf16(rows_frag<D>(Vt, h, t, st, r, g), df[st], dpacc[t]);
                     }
                 }
-            } else {
-                const float rowf = region == 1 ? rowf_b : rowf_a;
-                float wsum = 0.f;
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float m = KIND != kMaskLit ? bwd_bcast16(cl, 4 * t + e) * rowf : 1.f;
-                        const float dp = dpacc[t][e] * inv_me - dl_me;
-                        wsum += dp * (sacc[t][e] * m);
-                        dsf[4 * t + e] = f2bf(dp * m);
-                    }
-                rowterm += region == 1 ? wsum : -wsum;
-            }
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) aq[ct] = mfma_bf16(tr_frag<D>(Kt, h, ct, r, g), dsf, aq[ct]);
-        }
-        // the keys' states: dphi(q) += f (F dy / den - F_d delta), F rows as A and dy of the query row as
-        // B; the row half of dA takes phi(q) . that (phi(q) at the output layout's channels)
-        rounds([&](const __bf16 *S, const float *z, int st) {
-            if (st & 1) return;   // a queries' state: the key side's
-            const bool right = st >= 2;
-            const float f = KIND == kMaskLit ? 1.f : fast_exp2(right ? tot - cum_me : cum_me);
-            float part = 0.f;
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int st2 = 0; st2 < NS; ++st2) o = mfma_bf16(rows_frag<D>(S, ct >> 1, ct & 1, st2, r, g), df[st2], o);
-                const f32x4 zc = *reinterpret_cast<const f32x4 *>(z + 16 * ct + 4 * g);
-                const bf16x4 q4 = row4<D>(Qt, i_me, 16 * ct + 4 * g);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float oe = o[e] * inv_me - zc[e] * dl_me;
-                    aq[ct][e] += f * oe;
-                    part += (float)q4[e] * oe;
-                }
-            }
-            rowterm += (right ? -f : f) * part;
-        });
-        rowterm += __shfl_xor(rowterm, 16, 64);
-        rowterm += __shfl_xor(rowterm, 32, 64);
-        if (i_me >= n) return;
-        if constexpr (KIND != kMaskD) {
-            float xq[NCT][4];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(p.q + rowg * D + 16 * ct + 4 * g);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) xq[ct][e] = (float)q4[e];
-            }
-            phi_backward<D, KIND>(xq, aq);
-        }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) store4(p.dq, gb, rowg * D + 16 * ct + 4 * g, aq[ct]);
-        if constexpr (KIND != kMaskLit)
-            if (g == 0) p.da_row[rowg] = rowterm;
-    } else {
-        // ---- key side: dV^T and dphi(K)^T (channel 16 ct + 4 g + e, key i_me) against the chunk's queries
-        bf16x8 kf[NS], vf[NS];
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-            kf[st] = rows_frag<D>(Kt, tw >> 1, tw & 1, st, r, g);
-            vf[st] = rows_frag<D>(Vt, tw >> 1, tw & 1, st, r, g);
-        }
-        f32x4 ak[NCT], av[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) ak[ct] = av[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float colterm = 0.f;
-        // Separable mask for query sub-blocks wholly before or after the tile's keys (first key k0, last
-        // kl): M_ij = exp2(c_j - c_k0) exp2(c_k0 - c_i) for queries before, exp2(c_kl - c_j) exp2(c_i - c_kl)
-        // for queries after; the query's factor comes by DPP row broadcast.
-        const float e_first = uniform(cum[16 * tw]), e_last = uniform(cum[16 * tw + 15]);
-        const float keyf_b = KIND != kMaskLit ? fast_exp2(cum_me - e_first) : 1.f;
-        const float keyf_a = KIND != kMaskLit ? fast_exp2(e_last - cum_me) : 1.f;
-#pragma unroll 1
-        for (int h = 0; h < CT / kKB; ++h) {
-            if (causal && h * kKB + kKB - 1 < 16 * tw) continue;   // every query before every key of the tile
-            // 0: overlap, 1: every query before the tile's keys, 2: every query after them (wave-uniform)
-            const int region = h * kKB + kKB - 1 < 16 * tw ? 1 : h * kKB > 16 * tw + 15 ? 2 : 0;
-            float cl = 1.f;
-            if (KIND != kMaskLit && region != 0) {
-                const float ei = cum[h * kKB + 16 * ((r >> 2) & 1) + 4 * g + (r & 3)];
-                cl = fast_exp2(region == 1 ? e_first - ei : ei - e_last);
-            }
-            f32x4 sacc[2], dpacc[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int st = 0; st < NS; ++st) {
-                    sacc[t] = mfma_bf16(rows_frag<D>(Qt, h, t, st, r, g), kf[st], sacc[t]);
-                    dpacc[t] = mfma_bf16(rows_frag<D>(Gt, h, t, st, r, g), vf[st], dpacc[t]);
-                }
-            }
-            // element (t, e): query i = 32 h + 16 t + 4 g + e, key i_me
-            bf16x8 pf, dsf;
-            const float keyf = region == 1 ? keyf_b : keyf_a;
-            float wsum = 0.f;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int ib = h * kKB + 16 * t + 4 * g;
-                const f32x4 iv = *reinterpret_cast<const f32x4 *>(inv + ib);
-                const f32x4 dv4 = *reinterpret_cast<const f32x4 *>(dl + ib);
+                // element (t, e): key j = 32 h + 16 t + 4 g + e, query i_me
+                bf16x8 dsf;
                 if (region == 0) {
-                    const f32x4 ci = *reinterpret_cast<const f32x4 *>(cum + ib);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = ib + e;
-                        float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(ci[e] - cum_me)) : 1.f;
-                        if (causal && i_me > i) m = 0.f;
-                        const float pm = sacc[t][e] * m;
-                        const float dp = dpacc[t][e] * iv[e] - dv4[e];
-                        const float wv = dp * pm;
-                        colterm += i < i_me ? wv : (i > i_me ? -wv : 0.f);
-                        pf[4 * t + e] = f2bf(pm * iv[e]);
-                        dsf[4 * t + e] = f2bf(dp * m);
+                    for (int t = 0; t < 2; ++t) {
+                        const f32x4 cj = *reinterpret_cast<const f32x4 *>(cum + h * kKB + 16 * t + 4 * g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int j = h * kKB + 16 * t + 4 * g + e;
+                            float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(cum_me - cj[e])) : 1.f;
+                            if (causal && j > i_me) m = 0.f;
+                            const float dp = dpacc[t][e] * inv_me - dl_me;
+                            const float wv = dp * (sacc[t][e] * m);
+                            rowterm += j < i_me ? wv : (j > i_me ? -wv : 0.f);
+                            dsf[4 * t + e] = f2bf(dp * m);
+                        }
                     }
                 } else {
+                    const float rowf = region == 1 ? rowf_b : rowf_a;
+                    float wsum = 0.f;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float m = KIND != kMaskLit ? bwd_bcast16(cl, 4 * t + e) * rowf : 1.f;
+                            const float dp = dpacc[t][e] * inv_me - dl_me;
+                            wsum += dp * (sacc[t][e] * m);
+                            dsf[4 * t + e] = f2bf(dp * m);
+                        }
+                    rowterm += region == 1 ? wsum : -wsum;
+                }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) aq[ct] = mfma_bf16(tr_frag<D>(Kt, h, ct, r, g), dsf, aq[ct]);
+            }
+            // the keys' states: dphi(q) += f (F dy / den - F_d delta), F rows as A and dy of the query row as
+            // B; the row half of dA takes phi(q) . that (phi(q) at the output layout's channels)
+            rounds([&](const __bf16 *S, const float *z, int st) {
+                if (st & 1) return;   // a queries' state: the key side's
+                const bool right = st >= 2;
+                const float f = KIND == kMaskLit ? 1.f : fast_exp2(right ? tot - cum_me : cum_me);
+                float part = 0.f;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st2 = 0; st2 < NS; ++st2) o = mfma_bf16(rows_frag<D>(S, ct >> 1, ct & 1, st2, r, g), df[st2], o);
+                    const f32x4 zc = *reinterpret_cast<const f32x4 *>(z + 16 * ct + 4 * g);
+                    const bf16x4 q4 = row4<D>(Qt, i_me, 16 * ct + 4 * g);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float m = KIND != kMaskLit ? bwd_bcast16(cl, 4 * t + e) * keyf : 1.f;
-                        const float pm = sacc[t][e] * m;
-                        const float dp = dpacc[t][e] * iv[e] - dv4[e];
-                        wsum += dp * pm;
-                        pf[4 * t + e] = f2bf(pm * iv[e]);
-                        dsf[4 * t + e] = f2bf(dp * m);
+                        const float oe = o[e] * inv_me - zc[e] * dl_me;
+                        aq[ct][e] += f * oe;
+                        part += (float)q4[e] * oe;
+                    }
+                }
+                rowterm += (right ? -f : f) * part;
+            });
+            rowterm += __shfl_xor(rowterm, 16, 64);
+            rowterm += __shfl_xor(rowterm, 32, 64);
+            if (i_me < n) {
+                if constexpr (KIND != kMaskD) {
+                    float xq[NCT][4];
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(p.q + rowg * D + 16 * ct + 4 * g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) xq[ct][e] = (float)q4[e];
+                    }
+                    phi_backward<D, KIND>(xq, aq);
+                }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) store4(p.dq, gb, rowg * D + 16 * ct + 4 * g, aq[ct]);
+                if constexpr (KIND != kMaskLit)
+                    if (g == 0) p.da_row[rowg] = rowterm;
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int kt = 0; kt < TPW; ++kt) {
+            const int tw = kt == 0 ? wq : NW - 1 - wq;   // as the query side
+            const int i_me = 16 * tw + r;   // this lane's row of the tile
+            const float cum_me = cum[i_me];
+            const size_t rowg = row0 + i_me;
+            const bool live = 16 * tw < n;   // wave-uniform; a tile wholly past the chunk's end computes nothing
+            // ---- key side: dV^T and dphi(K)^T (channel 16 ct + 4 g + e, key i_me) against the chunk's queries
+            bf16x8 kf[NS], vf[NS];
+            if constexpr (SPLIT) {
+                const size_t rc = row0 + min(i_me, n - 1);
+                row_frags<D, KIND, true>(p.k + rc * D, i_me < n, kf);
+                row_frags<D, KIND, false>(p.v + rc * D, i_me < n, vf);
+            } else {
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    kf[st] = rows_frag<D>(Kt, tw >> 1, tw & 1, st, r, g);
+                    vf[st] = rows_frag<D>(Vt, tw >> 1, tw & 1, st, r, g);
+                }
+            }
+            f32x4 ak[NCT], av[NCT];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) ak[ct] = av[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            float colterm = 0.f;
+            // Separable mask for query sub-blocks wholly before or after the tile's keys (first key k0, last
+            // kl): M_ij = exp2(c_j - c_k0) exp2(c_k0 - c_i) for queries before, exp2(c_kl - c_j) exp2(c_i - c_kl)
+            // for queries after; the query's factor comes by DPP row broadcast.
+            const float e_first = uniform(cum[16 * tw]), e_last = uniform(cum[16 * tw + 15]);
+            const float keyf_b = KIND != kMaskLit ? fast_exp2(cum_me - e_first) : 1.f;
+            const float keyf_a = KIND != kMaskLit ? fast_exp2(e_last - cum_me) : 1.f;
+#pragma unroll 1
+            for (int h = 0; h < CT / kKB; ++h) {
+                    if (!live || h * kKB >= n) break;   // queries past the chunk's end are zero rows
+                if (causal && h * kKB + kKB - 1 < 16 * tw) continue;   // every query before every key of the tile
+                // 0: overlap, 1: every query before the tile's keys, 2: every query after them (wave-uniform)
+                const int region = h * kKB + kKB - 1 < 16 * tw ? 1 : h * kKB > 16 * tw + 15 ? 2 : 0;
+                float cl = 1.f;
+                if (KIND != kMaskLit && region != 0) {
+                    const float ei = cum[h * kKB + 16 * ((r >> 2) & 1) + 4 * g + (r & 3)];
+                    cl = fast_exp2(region == 1 ? e_first - ei : ei - e_last);
+                }
+                f32x4 sacc[2], dpacc[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    sacc[t] = dpacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < NS; ++st) {
+                        sacc[t] = mfma_bf16(rows_frag<D>(Qt, h, t, st, r, g), kf[st], sacc[t]);
+                        dpacc[t] = mfma_bf16(rows_frag<D>(Gt, h, t, st, r, g), vf[st], dpacc[t]);
+                    }
+                }
+                // element (t, e): query i = 32 h + 16 t + 4 g + e, key i_me
+                bf16x8 pf, dsf;
+                const float keyf = region == 1 ? keyf_b : keyf_a;
+                float wsum = 0.f;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int ib = h * kKB + 16 * t + 4 * g;
+                    const f32x4 iv = *reinterpret_cast<const f32x4 *>(inv + ib);
+                    const f32x4 dv4 = *reinterpret_cast<const f32x4 *>(dl + ib);
+                    if (region == 0) {
+                        const f32x4 ci = *reinterpret_cast<const f32x4 *>(cum + ib);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = ib + e;
+                            float m = KIND != kMaskLit ? fast_exp2(-__builtin_fabsf(ci[e] - cum_me)) : 1.f;
+                            if (causal && i_me > i) m = 0.f;
+                            const float pm = sacc[t][e] * m;
+                            const float dp = dpacc[t][e] * iv[e] - dv4[e];
+                            const float wv = dp * pm;
+                            colterm += i < i_me ? wv : (i > i_me ? -wv : 0.f);
+                            pf[4 * t + e] = f2bf(pm * iv[e]);
+                            dsf[4 * t + e] = f2bf(dp * m);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float m = KIND != kMaskLit ? bwd_bcast16(cl, 4 * t + e) * keyf : 1.f;
+                            const float pm = sacc[t][e] * m;
+                            const float dp = dpacc[t][e] * iv[e] - dv4[e];
+                            wsum += dp * pm;
+                            pf[4 * t + e] = f2bf(pm * iv[e]);
+                            dsf[4 * t + e] = f2bf(dp * m);
+                        }
+                    }
+                }
+                if (region != 0) colterm += region == 1 ? wsum : -wsum;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    av[ct] = mfma_bf16(tr_frag<D>(Gt, h, ct, r, g), pf, av[ct]);
+                    ak[ct] = mfma_bf16(tr_frag<D>(Qt, h, ct, r, g), dsf, ak[ct]);
+                }
+            }
+            // phi(k) of the key row at channels 32 hh + 16 t + 4 g + e: the transposed-slot B operand of dv
+            // and, with ct = 2 hh + t, the output layout's channels 16 ct + 4 g + e
+            bf16x8 kT[NS];
+            if constexpr (SPLIT) {
+                // from memory: phi, and LION-S's normalisation over the row's four lane groups
+                const __bf16 *kr = p.k + (row0 + min(i_me, n - 1)) * D;
+                float x[NS][8], ss = 0.f;
+#pragma unroll
+                for (int hh = 0; hh < NS; ++hh) {
+                    const bf16x4 k0 = *reinterpret_cast<const bf16x4 *>(kr + 32 * hh + 4 * g);
+                    const bf16x4 k1 = *reinterpret_cast<const bf16x4 *>(kr + 32 * hh + 16 + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[hh][e] = phi_pre<KIND>((float)k0[e]);
+                        x[hh][4 + e] = phi_pre<KIND>((float)k1[e]);
+                        ss += x[hh][e] * x[hh][e] + x[hh][4 + e] * x[hh][4 + e];
+                    }
+                }
+                float sc = i_me < n ? 1.f : 0.f;
+                if constexpr (KIND == kMaskS) {
+                    ss += __shfl_xor(ss, 16, 64);
+                    ss += __shfl_xor(ss, 32, 64);
+                    sc *= inv_norm(ss);
+                }
+#pragma unroll
+                for (int hh = 0; hh < NS; ++hh)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kT[hh][e] = f2bf(x[hh][e] * sc);
+            } else {
+#pragma unroll
+                for (int hh = 0; hh < NS; ++hh) {
+                    const bf16x4 k0 = row4<D>(Kt, i_me, 32 * hh + 4 * g), k1 = row4<D>(Kt, i_me, 32 * hh + 16 + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        kT[hh][e] = k0[e];
+                        kT[hh][4 + e] = k1[e];
                     }
                 }
             }
-            if (region != 0) colterm += region == 1 ? wsum : -wsum;
+            // the queries' states: dphi(k) += f (G v + G_d), G rows as A and v of the key row as B; dv += f G^T
+            // phi(k), G read transposed as A; the column half of dA takes phi(k) . (G v + G_d)
+            rounds([&](const __bf16 *S, const float *z, int st) {
+                if (!(st & 1)) return;   // a keys' state: the query side's
+                const bool right = st >= 2;
+                const float f = KIND == kMaskLit ? 1.f : fast_exp2(right ? tot - cum_me : cum_me);
+                float part = 0.f;
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                av[ct] = mfma_bf16(tr_frag<D>(Gt, h, ct, r, g), pf, av[ct]);
-                ak[ct] = mfma_bf16(tr_frag<D>(Qt, h, ct, r, g), dsf, ak[ct]);
-            }
-        }
-        // phi(k) of the key row at channels 32 hh + 16 t + 4 g + e: the transposed-slot B operand of dv
-        // and, with ct = 2 hh + t, the output layout's channels 16 ct + 4 g + e
-        bf16x8 kT[NS];
+                for (int ct = 0; ct < NCT; ++ct) {
+                    f32x4 o = {0.f, 0.f, 0.f, 0.f}, ov = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int hh = 0; hh < NS; ++hh) {
-            const bf16x4 k0 = row4<D>(Kt, i_me, 32 * hh + 4 * g), k1 = row4<D>(Kt, i_me, 32 * hh + 16 + 4 * g);
+                    for (int st2 = 0; st2 < NS; ++st2) {
+                        o = mfma_bf16(rows_frag<D>(S, ct >> 1, ct & 1, st2, r, g), vf[st2], o);
+                        ov = mfma_bf16(tr_frag<D>(S, st2, ct, r, g), kT[st2], ov);
+                    }
+                    const f32x4 zc = *reinterpret_cast<const f32x4 *>(z + 16 * ct + 4 * g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kT[hh][e] = k0[e];
-                kT[hh][4 + e] = k1[e];
-            }
-        }
-        // the queries' states: dphi(k) += f (G v + G_d), G rows as A and v of the key row as B; dv += f G^T
-        // phi(k), G read transposed as A; the column half of dA takes phi(k) . (G v + G_d)
-        rounds([&](const __bf16 *S, const float *z, int st) {
-            if (!(st & 1)) return;   // a keys' state: the query side's
-            const bool right = st >= 2;
-            const float f = KIND == kMaskLit ? 1.f : fast_exp2(right ? tot - cum_me : cum_me);
-            float part = 0.f;
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                f32x4 o = {0.f, 0.f, 0.f, 0.f}, ov = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int st2 = 0; st2 < NS; ++st2) {
-                    o = mfma_bf16(rows_frag<D>(S, ct >> 1, ct & 1, st2, r, g), vf[st2], o);
-                    ov = mfma_bf16(tr_frag<D>(S, st2, ct, r, g), kT[st2], ov);
+                    for (int e = 0; e < 4; ++e) {
+                        const float oe = o[e] + zc[e];
+                        ak[ct][e] += f * oe;
+                        av[ct][e] += f * ov[e];
+                        part += (float)kT[ct >> 1][4 * (ct & 1) + e] * oe;
+                    }
                 }
-                const f32x4 zc = *reinterpret_cast<const f32x4 *>(z + 16 * ct + 4 * g);
+                colterm += (right ? -f : f) * part;
+            });
+            colterm += __shfl_xor(colterm, 16, 64);
+            colterm += __shfl_xor(colterm, 32, 64);
+            if (i_me < n) {
+                if constexpr (KIND != kMaskD) {
+                    float xk[NCT][4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float oe = o[e] + zc[e];
-                    ak[ct][e] += f * oe;
-                    av[ct][e] += f * ov[e];
-                    part += (float)kT[ct >> 1][4 * (ct & 1) + e] * oe;
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(p.k + rowg * D + 16 * ct + 4 * g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) xk[ct][e] = (float)k4[e];
+                    }
+                    phi_backward<D, KIND>(xk, ak);
                 }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    store4(p.dk, gb, rowg * D + 16 * ct + 4 * g, ak[ct]);
+                    store4(p.dv, gb, rowg * D + 16 * ct + 4 * g, av[ct]);
+                }
+                if constexpr (KIND != kMaskLit)
+                    if (g == 0) p.da_col[rowg] = colterm;
             }
-            colterm += (right ? -f : f) * part;
-        });
-        colterm += __shfl_xor(colterm, 16, 64);
-        colterm += __shfl_xor(colterm, 32, 64);
-        if (i_me >= n) return;
-        if constexpr (KIND != kMaskD) {
-            float xk[NCT][4];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(p.k + rowg * D + 16 * ct + 4 * g);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) xk[ct][e] = (float)k4[e];
-            }
-            phi_backward<D, KIND>(xk, ak);
         }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            store4(p.dk, gb, rowg * D + 16 * ct + 4 * g, ak[ct]);
-            store4(p.dv, gb, rowg * D + 16 * ct + 4 * g, av[ct]);
-        }
-        if constexpr (KIND != kMaskLit)
-            if (g == 0) p.da_col[rowg] = colterm;
     }
 }
 
@@ -772,15 +849,12 @@ MbLayout mb_layout(int B, int H, int L, int d, int C) {
 }
 
 size_t mb_main_lds(int d, int C) {
-    const size_t f32 = (size_t)(C + 4) + 4 * (size_t)C + 4 * (size_t)d;
+    const size_t f32 = (size_t)(C + 4) + 2 * (size_t)C + 4 * (size_t)d;
     return (size_t)4 * C * d * 2 + f32 * 4;
 }
 
-template <int D, int KIND, int CT>
-hipError_t launch_mb_t(const BwdArgs &a, hipStream_t stream) {
-    const MbLayout w = mb_layout(a.B, a.H, a.L, a.d, CT);
-    unsigned char *ws = reinterpret_cast<unsigned char *>(a.workspace);
-    MbParams p;
+MbParams mb_params(const BwdArgs &a, int C) {
+    MbParams p{};
     p.q = reinterpret_cast<const __bf16 *>(a.q);
     p.k = reinterpret_cast<const __bf16 *>(a.k);
     p.v = reinterpret_cast<const __bf16 *>(a.v);
@@ -790,12 +864,36 @@ hipError_t launch_mb_t(const BwdArgs &a, hipStream_t stream) {
     p.ll = a.log_lambda;
     p.H = a.H;
     p.L = a.L;
-    p.nch = (a.L + CT - 1) / CT;
+    p.nch = (a.L + C - 1) / C;
     p.causal = a.causal ? 1 : 0;
     p.dq = a.dq;
     p.dk = a.dk;
     p.dv = a.dv;
     p.g_bf16 = a.g_bf16 ? 1 : 0;
+    p.nbh = a.B * a.H;
+    return p;
+}
+
+template <int D, int KIND, int CT, bool SPLIT = false>
+hipError_t launch_main_dll(const MbParams &p, const BwdArgs &a, hipStream_t stream) {
+    constexpr size_t lm = MainLds<D, CT, SPLIT>::BYTES;
+    allow_lds(&mb_main_kernel<D, KIND, CT, SPLIT>, lm);
+    const int grid = SPLIT ? 16 * ((a.B * a.H + 7) / 8) : a.B * a.H * p.nch;
+    const int nt = SPLIT ? main_threads(CT) / 2 : main_threads(CT);
+    hipLaunchKernelGGL((mb_main_kernel<D, KIND, CT, SPLIT>), dim3(grid), dim3(nt), lm, stream, p);
+    if (KIND != kMaskLit) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_dll(KIND, p.da_row, p.da_col, a.dll, a.B, a.H, a.L, stream);
+    }
+    return hipGetLastError();
+}
+
+template <int D, int KIND, int CT>
+hipError_t launch_mb_t(const BwdArgs &a, hipStream_t stream) {
+    const MbLayout w = mb_layout(a.B, a.H, a.L, a.d, CT);
+    unsigned char *ws = reinterpret_cast<unsigned char *>(a.workspace);
+    MbParams p = mb_params(a, CT);
     p.st = reinterpret_cast<__bf16 *>(ws + w.st);
     p.stz = reinterpret_cast<float *>(ws + w.stz);
     const size_t n = (size_t)a.B * a.H * a.L;
@@ -807,15 +905,40 @@ hipError_t launch_mb_t(const BwdArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((mb_walk_kernel<D, KIND, CT>), dim3(a.B * a.H * (a.causal ? 2 : 4)), dim3(kWalkThreads), lw,
                            stream, p);
     }
-    constexpr size_t lm = MainLds<D, CT>::BYTES;
-    allow_lds(&mb_main_kernel<D, KIND, CT>, lm);
-    hipLaunchKernelGGL((mb_main_kernel<D, KIND, CT>), dim3(a.B * a.H * p.nch), dim3(CT * 8), lm, stream, p);
-    if (KIND != kMaskLit) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return launch_dll(KIND, p.da_row, p.da_col, a.dll, a.B, a.H, a.L, stream);
+    return launch_main_dll<D, KIND, CT>(p, a, stream);
+}
+
+// The whole sequence as one chunk (no walk, no states); with at least one (batch, head) per compute unit
+// the two sides go to workgroups of their own (fewer (batch, head) pairs leave compute units idle, and
+// then one workgroup per pair, all four tiles staged once, is faster).  The dA halves go to the full
+// form's workspace (3 B H L floats, of which the last two thirds).
+constexpr size_t kSplitMinPairs = 256;
+
+template <int D, int KIND, int CT>
+hipError_t launch_single_c(const MbParams &p, const BwdArgs &a, hipStream_t stream) {
+    if ((size_t)a.B * a.H >= kSplitMinPairs) return launch_main_dll<D, KIND, CT, true>(p, a, stream);
+    return launch_main_dll<D, KIND, CT, false>(p, a, stream);
+}
+
+template <int D, int KIND>
+hipError_t launch_single_t(const BwdArgs &a, hipStream_t stream) {
+    const int C = a.L <= 64 ? 64 : a.L <= 128 ? 128 : 256;
+    MbParams p = mb_params(a, C);
+    const size_t n = (size_t)a.B * a.H * a.L;
+    p.da_row = reinterpret_cast<float *>(a.workspace) + n;
+    p.da_col = p.da_row + n;
+    if (C == 64) return launch_single_c<D, KIND, 64>(p, a, stream);
+    if (C == 128) return launch_single_c<D, KIND, 128>(p, a, stream);
+    return launch_single_c<D, KIND, 256>(p, a, stream);
+}
+
+template <int D>
+hipError_t launch_single_kind(const BwdArgs &a, hipStream_t stream) {
+    switch (a.kind) {
+    case kMaskLit: return launch_single_t<D, kMaskLit>(a, stream);
+    case kMaskD: return launch_single_t<D, kMaskD>(a, stream);
+    default: return launch_single_t<D, kMaskS>(a, stream);
     }
-    return hipGetLastError();
 }
 
 template <int D, int KIND>
@@ -843,6 +966,12 @@ Plan plan_chunk_bwd_mfma(const BwdArgs &a) {
     p.ok = dims && cs && mb_main_lds(a.d, a.C) <= kLdsPerWorkgroup;
     p.workspace = p.ok ? mb_layout(a.B, a.H, a.L, a.d, a.C).bytes : 0;
     return p;
+}
+
+bool single_chunk_bwd_ok(const BwdArgs &a) { return (a.d == 32 || a.d == 64) && a.L >= 1 && a.L <= 256; }
+
+hipError_t launch_single_chunk_bwd(const BwdArgs &a, hipStream_t stream) {
+    return a.d == 32 ? launch_single_kind<32>(a, stream) : launch_single_kind<64>(a, stream);
 }
 
 hipError_t launch_chunk_bwd_mfma(const BwdArgs &a, hipStream_t stream) {

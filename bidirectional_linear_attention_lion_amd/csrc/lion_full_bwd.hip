@@ -703,6 +703,7 @@ hipError_t launch_dll(int kind, float *da_row, float *da_col, float *dll, int B,
 }
 
 hipError_t launch_full_bwd(const BwdArgs &a, hipStream_t stream) {
+    if (single_chunk_bwd_ok(a)) return launch_single_chunk_bwd(a, stream);
     switch (a.d) {
     case 32: return dispatch_kind<32>(a, stream);
     case 64: return dispatch_kind<64>(a, stream);

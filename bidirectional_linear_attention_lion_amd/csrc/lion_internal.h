@@ -77,6 +77,10 @@ hipError_t launch_full(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_full_bwd(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_chunk_bwd_mfma(const BwdArgs &a, hipStream_t stream);
+// The full form's backward as one chunk of the chunkwise main kernel (d of 32 or 64, L <= 256; the
+// full form's workspace).
+bool single_chunk_bwd_ok(const BwdArgs &a);
+hipError_t launch_single_chunk_bwd(const BwdArgs &a, hipStream_t stream);
 // dlog(lambda) from the two halves of dA ([B, H, L] each): LION-S a reverse prefix sum per (batch,
 // head), LION-D sum_t t dA_t per head over the batch.  kind is 1 (D) or 2 (S).
 hipError_t launch_dll(int kind, float *da_row, float *da_col, float *dll, int B, int H, int L, hipStream_t stream);

@@ -126,6 +126,15 @@ def test_bwd_head_dims(d):
 
 
 @pytest.mark.parametrize("kind", [lin.LIT, lin.D, lin.S])
+def test_bwd_sides_apart(kind):
+    # at least 256 (batch, head) pairs and L <= 256: the query and key sides of a pair run in workgroups
+    # of their own (B H = 272 leaves the last group of 16 workgroups partly empty)
+    for B, H, L, d, causal in ((64, 4, 197, 64, False), (32, 8, 256, 64, True), (128, 2, 37, 32, False),
+                               (256, 1, 1, 64, False), (16, 17, 100, 64, False), (64, 4, 129, 32, True)):
+        run_case(B, H, L, d, kind, causal=causal, positive=False, seed=5000 + L, tag="sides apart")
+
+
+@pytest.mark.parametrize("kind", [lin.LIT, lin.D, lin.S])
 def test_bwd_signed(kind):
     for L in (64, 197, 512):
         run_case(2, 3, L, 64, kind, positive=False, seed=3000 + L)
