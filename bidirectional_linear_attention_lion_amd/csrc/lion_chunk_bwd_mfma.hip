@@ -1,5 +1,6 @@
 // lion_chunk_bwd_mfma.hip -- backward pass of the chunkwise form for chunks of 64 and 128 tokens, every
-// product on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16).
+// product on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16); and the full form's backward for a
+// sequence of at most 256 tokens (d <= 64), which is one chunk of up to 256 (no walk, no states).
 //
 // The gradients and their chunkwise split are those of lion_chunk_bwd.hip (the chain rule of the
 // attention form, OpenReview abstract and reply "Concern 1", Theorem 3.3 Eq. 25, organised like the

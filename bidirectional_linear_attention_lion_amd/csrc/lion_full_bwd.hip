@@ -26,6 +26,9 @@
 // a row factor times a column factor (both at most 1) instead of one exponential per score, as the
 // forward does.
 // Causal variant: M_ij = 0 for j > i (a constant), so those pairs are skipped or zeroed.
+// A sequence of at most 256 tokens with d <= 64 takes another route (launch_full_bwd): it is one chunk
+// of the chunkwise backward's main kernel (lion_chunk_bwd_mfma.hip), which stages the whole sequence
+// once and forms both sides' products there, with no states.
 #include <type_traits>
 
 #include "lion_device.h"
