@@ -47,6 +47,7 @@ struct MbParams {
     __bf16 *st;                // [B H][nch][4][D][D]: key-left, query-left, key-right, query-right
     float *stz;                // [B H][nch][4][D]: the states' last column
     float *da_row, *da_col;    // [B H L]
+    float *dll_part;           // LION-D lone chunk: [B H][2 halves][hi, lo] of sum_t t dA_t, or null
 };
 
 // Inclusive prefix sums of the chunk's log decays in log2 units relative to the chunk start (cum[t],
@@ -512,6 +513,9 @@ __global__ void __launch_bounds__(SPLIT ? main_threads(CT) / 2 : main_threads(CT
         }
     };
     const bool gb = p.g_bf16 != 0;
+    // LION-D with dll_part: this lane's share of sum_t t dA_t (a lone chunk, so t is the tile row)
+    const bool fuse_dll = KIND == kMaskD && p.dll_part != nullptr;   // workgroup-uniform
+    double tsum = 0.0;
 
     if (qside) {
 #pragma unroll 1
@@ -639,8 +643,12 @@ __global__ void __launch_bounds__(SPLIT ? main_threads(CT) / 2 : main_threads(CT
                 }
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) store4(p.dq, gb, rowg * D + 16 * ct + 4 * g, aq[ct]);
-                if constexpr (KIND != kMaskLit)
-                    if (g == 0) p.da_row[rowg] = rowterm;
+                if constexpr (KIND != kMaskLit) {
+                    if (g == 0) {
+                        if (fuse_dll) tsum += (double)i_me * (double)rowterm;
+                        else p.da_row[rowg] = rowterm;
+                    }
+                }
             }
         }
     } else {
@@ -820,8 +828,31 @@ __global__ void __launch_bounds__(SPLIT ? main_threads(CT) / 2 : main_threads(CT
                     store4(p.dk, gb, rowg * D + 16 * ct + 4 * g, ak[ct]);
                     store4(p.dv, gb, rowg * D + 16 * ct + 4 * g, av[ct]);
                 }
-                if constexpr (KIND != kMaskLit)
-                    if (g == 0) p.da_col[rowg] = colterm;
+                if constexpr (KIND != kMaskLit) {
+                    if (g == 0) {
+                        if (fuse_dll) tsum += (double)i_me * (double)colterm;
+                        else p.da_col[rowg] = colterm;
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (KIND == kMaskD) {
+        if (fuse_dll) {
+            // each side's waves add their shares in fp64 (the states' last-column space is free: no
+            // states) and the side's first wave leaves the sum as a hi/lo float pair
+            double *red = reinterpret_cast<double *>(zst);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o, 64);
+            if (lane == 0) red[w] = tsum;
+            __syncthreads();
+            if (lane == 0 && (w == 0 || (!SPLIT && w == NQW))) {
+                double sum = 0.0;
+                for (int k = 0; k < NQW; ++k) sum += red[w + k];
+                const float hi = (float)sum;
+                float *dst = p.dll_part + ((size_t)bh * 2 + (qside ? 0 : 1)) * 2;
+                dst[0] = hi;
+                dst[1] = (float)(sum - (double)hi);
             }
         }
     }
@@ -885,6 +916,7 @@ hipError_t launch_main_dll(const MbParams &p, const BwdArgs &a, hipStream_t stre
     if (KIND != kMaskLit) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (p.dll_part != nullptr) return launch_dll_parts(p.dll_part, a.dll, a.B, a.H, stream);
         return launch_dll(KIND, p.da_row, p.da_col, a.dll, a.B, a.H, a.L, stream);
     }
     return hipGetLastError();
@@ -928,6 +960,8 @@ hipError_t launch_single_t(const BwdArgs &a, hipStream_t stream) {
     const size_t n = (size_t)a.B * a.H * a.L;
     p.da_row = reinterpret_cast<float *>(a.workspace) + n;
     p.da_col = p.da_row + n;
+    // LION-D, L >= 4: the token sums of dA are formed in the kernel, into the first third (4 B H floats)
+    if (KIND == kMaskD && a.L >= 4) p.dll_part = reinterpret_cast<float *>(a.workspace);
     if (C == 64) return launch_single_c<D, KIND, 64>(p, a, stream);
     if (C == 128) return launch_single_c<D, KIND, 128>(p, a, stream);
     return launch_single_c<D, KIND, 256>(p, a, stream);

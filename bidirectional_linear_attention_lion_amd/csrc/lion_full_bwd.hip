@@ -578,6 +578,25 @@ __global__ void __launch_bounds__(kDllThreads) bwd_dll_d_kernel(BwdParams p, int
     if (tid == 0) p.dll[h] = (float)sh[0];
 }
 
+// LION-D from partials already summed over the tokens: four floats per (batch, head), two hi/lo pairs
+// (one per half of dA); one workgroup per head adds its B entries.
+__global__ void __launch_bounds__(kDllThreads) bwd_dll_d_parts_kernel(const float *part, float *dll, int B, int H) {
+    __shared__ double sh[kDllThreads];
+    const int tid = threadIdx.x, h = blockIdx.x;
+    double s = 0.0;
+    for (int b = tid; b < B; b += kDllThreads) {
+        const float *q = part + ((size_t)b * H + h) * 4;
+        s += ((double)q[0] + (double)q[1]) + ((double)q[2] + (double)q[3]);
+    }
+    sh[tid] = s;
+    __syncthreads();
+    for (int o = kDllThreads / 2; o > 0; o >>= 1) {
+        if (tid < o) sh[tid] += sh[tid + o];
+        __syncthreads();
+    }
+    if (tid == 0) dll[h] = (float)sh[0];
+}
+
 // ================================ host side ===========================================================
 struct BwdShape {
     int tt, nw, nsb, sk, nbuf;
@@ -702,6 +721,11 @@ hipError_t launch_dll(int kind, float *da_row, float *da_col, float *dll, int B,
         hipLaunchKernelGGL(bwd_dll_d_rows_kernel, dim3(B * H), dim3(kDllThreads), 0, stream, p);
         hipLaunchKernelGGL(bwd_dll_d_kernel, dim3(H), dim3(kDllThreads), 0, stream, p, B);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_dll_parts(const float *part, float *dll, int B, int H, hipStream_t stream) {
+    hipLaunchKernelGGL(bwd_dll_d_parts_kernel, dim3(H), dim3(kDllThreads), 0, stream, part, dll, B, H);
     return hipGetLastError();
 }
 

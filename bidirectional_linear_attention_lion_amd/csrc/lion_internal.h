@@ -84,6 +84,8 @@ hipError_t launch_single_chunk_bwd(const BwdArgs &a, hipStream_t stream);
 // dlog(lambda) from the two halves of dA ([B, H, L] each): LION-S a reverse prefix sum per (batch,
 // head), LION-D sum_t t dA_t per head over the batch.  kind is 1 (D) or 2 (S).
 hipError_t launch_dll(int kind, float *da_row, float *da_col, float *dll, int B, int H, int L, hipStream_t stream);
+// LION-D dlog(lambda) from per-(batch, head) token sums: part is fp32 [B, H, 4], two hi/lo pairs each.
+hipError_t launch_dll_parts(const float *part, float *dll, int B, int H, hipStream_t stream);
 hipError_t launch_selectivity(const SelArgs &a, hipStream_t stream);
 hipError_t launch_chunk(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_chunk2(const AttnArgs &a, hipStream_t stream);
