@@ -552,7 +552,7 @@ __global__ void __launch_bounds__(SPLIT ? main_threads(CT) / 2 : main_threads(CT
             const float rowf_a = KIND != kMaskLit ? fast_exp2(e_last - cum_me) : 1.f;
 #pragma unroll 1
             for (int h = 0; h < CT / kKB; ++h) {
-                    if (!live || h * kKB >= n) break;   // keys past the chunk's end are zero rows
+                if (!live || h * kKB >= n) break;   // keys past the chunk's end are zero rows
                 if (causal && h * kKB > 16 * tw + 15) break;   // every key after every query of the tile
                 // 0: overlap, 1: every key before the tile's rows, 2: every key after them (wave-uniform)
                 const int region = h * kKB + kKB - 1 < 16 * tw ? 1 : h * kKB > 16 * tw + 15 ? 2 : 0;
@@ -684,7 +684,7 @@ __global__ void __launch_bounds__(SPLIT ? main_threads(CT) / 2 : main_threads(CT
             const float keyf_a = KIND != kMaskLit ? fast_exp2(e_last - cum_me) : 1.f;
 #pragma unroll 1
             for (int h = 0; h < CT / kKB; ++h) {
-                    if (!live || h * kKB >= n) break;   // queries past the chunk's end are zero rows
+                if (!live || h * kKB >= n) break;   // queries past the chunk's end are zero rows
                 if (causal && h * kKB + kKB - 1 < 16 * tw) continue;   // every query before every key of the tile
                 // 0: overlap, 1: every query before the tile's keys, 2: every query after them (wave-uniform)
                 const int region = h * kKB + kKB - 1 < 16 * tw ? 1 : h * kKB > 16 * tw + 15 ? 2 : 0;
