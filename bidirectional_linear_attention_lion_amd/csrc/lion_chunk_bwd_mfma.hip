@@ -941,15 +941,18 @@ hipError_t launch_mb_t(const BwdArgs &a, hipStream_t stream) {
     return launch_main_dll<D, KIND, CT>(p, a, stream);
 }
 
-// The whole sequence as one chunk (no walk, no states); with at least one (batch, head) per compute unit
-// the two sides go to workgroups of their own (fewer (batch, head) pairs leave compute units idle, and
-// then one workgroup per pair, all four tiles staged once, is faster).  The dA halves go to the full
-// form's workspace (3 B H L floats, of which the last two thirds).
-constexpr size_t kSplitMinPairs = 256;
+// The whole sequence as one chunk (no walk, no states).  The two sides go to workgroups of their own
+// (two per compute unit) unless one workgroup per (batch, head) fills a single round of the 256 compute
+// units while the split would put two on some of them (128 < B H <= 256); LION-D's heavier mask work
+// makes the split pay there as well.  The dA halves go to the full form's workspace (3 B H L floats, of
+// which the last two thirds).
+constexpr size_t kComputeUnits = 256;
 
 template <int D, int KIND, int CT>
 hipError_t launch_single_c(const MbParams &p, const BwdArgs &a, hipStream_t stream) {
-    if ((size_t)a.B * a.H >= kSplitMinPairs) return launch_main_dll<D, KIND, CT, true>(p, a, stream);
+    const size_t pairs = (size_t)a.B * a.H;
+    const bool one_round = pairs > kComputeUnits / 2 && pairs <= kComputeUnits;
+    if (KIND == kMaskD || !one_round) return launch_main_dll<D, KIND, CT, true>(p, a, stream);
     return launch_main_dll<D, KIND, CT, false>(p, a, stream);
 }
 

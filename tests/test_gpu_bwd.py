@@ -127,11 +127,21 @@ def test_bwd_head_dims(d):
 
 @pytest.mark.parametrize("kind", [lin.LIT, lin.D, lin.S])
 def test_bwd_sides_apart(kind):
-    # at least 256 (batch, head) pairs and L <= 256: the query and key sides of a pair run in workgroups
-    # of their own (B H = 272 leaves the last group of 16 workgroups partly empty)
-    for B, H, L, d, causal in ((64, 4, 197, 64, False), (32, 8, 256, 64, True), (128, 2, 37, 32, False),
-                               (256, 1, 1, 64, False), (16, 17, 100, 64, False), (64, 4, 129, 32, True)):
+    # L <= 256, more than 256 (batch, head) pairs: the query and key sides of a pair run in workgroups of
+    # their own (B H = 272 leaves the last group of 16 workgroups partly empty); the small cases of the
+    # tests above take the same route
+    for B, H, L, d, causal in ((64, 5, 197, 64, False), (32, 9, 256, 64, True), (128, 3, 37, 32, False),
+                               (257, 1, 1, 64, False), (16, 17, 100, 64, False), (64, 5, 129, 32, True)):
         run_case(B, H, L, d, kind, causal=causal, positive=False, seed=5000 + L, tag="sides apart")
+
+
+@pytest.mark.parametrize("kind", [lin.LIT, lin.S])
+def test_bwd_one_workgroup_per_pair(kind):
+    # L <= 256 and 128 < B H <= 256, LION-LIT or LION-S: one workgroup per (batch, head) with all four
+    # tiles (chunks of 64, 128 and 256; two tiles per wave at 256)
+    for B, H, L, d, causal in ((64, 3, 197, 64, False), (32, 8, 256, 64, True), (129, 1, 37, 32, False),
+                               (200, 1, 1, 64, False), (16, 16, 100, 64, False), (43, 3, 129, 32, True)):
+        run_case(B, H, L, d, kind, causal=causal, positive=False, seed=6000 + L, tag="one workgroup per pair")
 
 
 @pytest.mark.parametrize("kind", [lin.LIT, lin.D, lin.S])
